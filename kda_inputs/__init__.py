@@ -1,0 +1,112 @@
+"""Seeded synthetic inputs for the KDA mixer (shared by tests, smoke check and bench).
+
+This module only draws random numbers and shapes them into the workloads' value
+distributions; it contains none of the mixer's arithmetic (no convolution, norm or
+recurrence).  Both the oracle side and the GPU side consume the same tensors.
+
+Workloads (one KDA layer of the released model: 96 heads x head_dim 128, short
+conv kernel 4 -- "Kimi-K3 model atlas -- self.layers", linear_attn_config):
+
+* raw q, k, v ~ N(0, 1)
+* log-decay g = -exp(a_h) * softplus(z), a_h ~ U(lo, hi) drawn once per head (like
+  the per-head ``A_log``), z ~ N(0, 1) per element (one decay per channel, the
+  full-rank gate)
+* beta = sigmoid(b), b ~ N(0, sigma_b^2)
+* conv filters ~ N(0, 0.25) (std 0.5), float32, layout [3 (q,k,v), H*D, 4]
+* S0 ~ N(0, 0.01) (std 0.1) float32 where the workload has an initial state
+* decode: conv history ~ N(0, 1) in the I/O dtype
+
+The second parameter of every N(., .) is a variance.  bf16 tensors are rounded
+from float32 with round-to-nearest-even (torch's conversion).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, replace
+
+import torch
+import torch.nn.functional as F
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    B: int
+    T: int
+    H: int
+    D: int
+    io: str            # "bf16" | "fp32"
+    chunk: int         # 0 for decode
+    a_lo: float
+    a_hi: float
+    b_std: float
+    s0_std: float      # 0 => no initial state (S0 = NULL)
+    decode: bool = False
+    conv_state_std: float = 0.0   # 0 => no conv history (zeros)
+
+    @property
+    def tokens(self) -> int:
+        return self.B * self.T
+
+    def scaled(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+
+WORKLOADS = {
+    "tiny-fp32": Workload("tiny-fp32", B=1, T=64, H=2, D=16, io="fp32", chunk=16,
+                          a_lo=-1.0, a_hi=1.0, b_std=1.0, s0_std=0.0),
+    "prefill-4k": Workload("prefill-4k", B=1, T=4096, H=96, D=128, io="bf16", chunk=64,
+                           a_lo=-1.0, a_hi=1.0, b_std=1.0, s0_std=0.0),
+    "prefill-b4-8k-s0": Workload("prefill-b4-8k-s0", B=4, T=8192, H=96, D=128, io="bf16",
+                                 chunk=64, a_lo=-3.0, a_hi=2.0, b_std=math.sqrt(2.0),
+                                 s0_std=0.1),
+    "decode-b256": Workload("decode-b256", B=256, T=1, H=96, D=128, io="bf16", chunk=0,
+                            a_lo=-1.0, a_hi=1.0, b_std=1.0, s0_std=0.1, decode=True,
+                            conv_state_std=1.0),
+    "prefill-64k": Workload("prefill-64k", B=1, T=65536, H=96, D=128, io="bf16", chunk=64,
+                            a_lo=-3.0, a_hi=2.0, b_std=math.sqrt(2.0), s0_std=0.1),
+}
+# The same five workloads by position (0: tiny parity case ... 4: long context).
+ORDER = ["tiny-fp32", "prefill-4k", "prefill-b4-8k-s0", "decode-b256", "prefill-64k"]
+
+DTYPES = {"bf16": torch.bfloat16, "fp32": torch.float32}
+
+
+def make_inputs(w: Workload, seed: int = 0, device: str | torch.device = "cpu") -> dict:
+    """Draw one set of inputs for workload ``w`` on ``device``.
+
+    Returns a dict of tensors: q, k, v, g [B,T,H,D] (decode: [B,H,D]) in the I/O
+    dtype; beta [B,T,H] (decode [B,H]); conv_w [3,H*D,4] fp32; S0 [B,H,D,D] fp32 or
+    None; conv_state [B,3,3,H*D] in the I/O dtype or None.
+    """
+    device = torch.device(device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    io = DTYPES[w.io]
+    B, T, H, D = w.B, w.T, w.H, w.D
+    shape = (B, H, D) if w.decode else (B, T, H, D)
+    bshape = (B, H) if w.decode else (B, T, H)
+
+    def randn(*s, std=1.0):
+        x = torch.randn(*s, generator=gen, device=device, dtype=torch.float32)
+        return x.mul_(std) if std != 1.0 else x
+
+    q = randn(*shape).to(io)
+    k = randn(*shape).to(io)
+    v = randn(*shape).to(io)
+    a = torch.empty(H, device=device, dtype=torch.float32).uniform_(w.a_lo, w.a_hi, generator=gen)
+    z = randn(*shape)
+    g = F.softplus(z).mul_(-torch.exp(a).view(*([1] * (len(shape) - 2)), H, 1)).to(io)
+    del z
+    beta = torch.sigmoid(randn(*bshape, std=w.b_std)).to(io)
+    conv_w = randn(3, H * D, 4, std=0.5)
+    S0 = randn(B, H, D, D, std=w.s0_std) if w.s0_std > 0 else None
+    conv_state = randn(B, 3, 3, H * D, std=w.conv_state_std).to(io) if w.conv_state_std > 0 else None
+    return dict(q=q, k=k, v=v, g=g, beta=beta, conv_w=conv_w, S0=S0, conv_state=conv_state)
+
+
+def to_numpy(t):
+    """float64 NumPy copy of a tensor (exact for bf16/fp32 values), or None."""
+    if t is None:
+        return None
+    return t.detach().to("cpu", torch.float64).numpy()

@@ -1,0 +1,18 @@
+"""fp64 CPU oracle for the KDA token mixer (test infrastructure only).
+
+Importable only by the tests, the smoke check and the CPU-baseline leg of the
+benchmark.  The GPU library never imports it.
+"""
+from .kda_oracle import (  # noqa: F401
+    CONV_K,
+    L2_EPS,
+    conv_norm_reference,
+    conv_tail,
+    gated_delta_step,
+    kda_reference,
+    kda_reference_decode_step,
+    kda_reference_heads,
+    l2_normalize,
+    short_conv,
+    silu,
+)

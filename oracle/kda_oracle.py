@@ -1,0 +1,248 @@
+"""Plain fp64 CPU oracle for the Kimi Delta Attention (KDA) token mixer.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check in
+``__graft_entry__`` and the CPU-baseline leg of ``bench.py`` may import this
+module.  The GPU library never calls it, and it shares no code with the GPU
+library: it is a slow, obviously-correct statement of what the mixer computes.
+
+Sources (web pages; cited by title and section):
+
+* "Kimi-K3 model atlas -- self.layers": 69 of the 93 layers are KDA layers whose
+  state between calls has a fixed size; the released ``linear_attn_config`` sets
+  ``num_heads 96``, ``head_dim 128``, ``short_conv_kernel_size 4`` and a full-rank
+  (per-channel) gate.
+* "MaxText PR 5548 (Kimi-K3 config, schema, param mapping)", review item 2: the
+  KDA tensors ``{q,k,v}_conv1d.weight`` have shape ``[12288, 1, 4]`` and are kept
+  in float32, like ``A_log`` and ``dt_bias`` (one decay per channel).
+* "Kimi-K3 atlas -- MoE input (decode)", ``KimiRMSNorm``: norm computed in float32
+  with ``eps = 1e-6``; used here only through the identity that ties the L2 norm
+  of q and k to that RMSNorm (see ``l2_normalize``).
+
+The pages name the mixer and its parameters but do not print its equations.
+The definition implemented here is the channel-wise gated delta rule:
+
+    S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T,
+    o_t = scale * S_t^T q_t,        alpha_t = exp(g_t)  (one decay per key channel)
+
+preceded by a causal depthwise short convolution (kernel 4) and SiLU on q, k, v
+and a per-head L2 normalisation of q and k.  Readings where the pages are silent
+(tap order, eps placement, scale, decay axis, ...) are listed in the module-level
+constants and in the project design notes; every function says which it uses.
+
+Every function here is pinned by tests that do not re-type it: closed forms,
+brute-force matrix products, an independent chunked rewrite, invariants and a
+hand-worked example.  No function here is "parity unpinned".
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# Reading: the L2 norm of q and k divides by sqrt(sum(x^2) + eps) with eps inside
+# the root.  eps = 1e-6 is the value the pages fix for KimiRMSNorm ("Kimi-K3 atlas
+# -- MoE input (decode)", RMSNorm excerpt); the pages give no eps for the L2 norm.
+L2_EPS = 1e-6
+# Released config, linear_attn_config.short_conv_kernel_size ("Kimi-K3 model
+# atlas -- self.layers", config.json).
+CONV_K = 4
+
+
+def silu(x: np.ndarray) -> np.ndarray:
+    """SiLU(x) = x * sigmoid(x) = x / (1 + exp(-x)), elementwise, fp64."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / (1.0 + np.exp(-x))
+
+
+def short_conv(x: np.ndarray, w: np.ndarray, history: np.ndarray | None = None) -> np.ndarray:
+    """Causal depthwise convolution over time, no bias.
+
+    x:       [T, C] raw inputs of one sequence (fp64)
+    w:       [C, K] one K-tap filter per channel; this is the ``[C, 1, K]`` layout
+             of the stored ``*_conv1d.weight`` tensors (MaxText PR 5548, review
+             item 2) with the singleton middle axis dropped.
+    history: [K-1, C] the K-1 raw inputs that precede x, oldest first, or None
+             for zeros.
+
+    Reading of the tap order (the pages give only the weight shape): the layout is
+    a cross-correlation with K-1 inputs of left padding, so
+        y[t, c] = sum_{tau=0}^{K-1} w[c, tau] * x[t - (K-1) + tau, c],
+    i.e. the last tap w[c, K-1] multiplies the current input.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    T, C = x.shape
+    K = w.shape[1]
+    if history is None:
+        history = np.zeros((K - 1, C))
+    xe = np.concatenate([np.asarray(history, dtype=np.float64), x], axis=0)  # [K-1+T, C]
+    y = np.zeros((T, C))
+    for tau in range(K):
+        y += w[:, tau][None, :] * xe[tau:tau + T, :]
+    return y
+
+
+def conv_tail(x: np.ndarray, history: np.ndarray | None, K: int = CONV_K) -> np.ndarray:
+    """The K-1 most recent raw inputs after consuming x ([T, C]), oldest first.
+
+    This is the convolution's carried state: feeding it back as ``history`` lets a
+    later call continue the same sequence.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    C = x.shape[1]
+    if history is None:
+        history = np.zeros((K - 1, C))
+    xe = np.concatenate([np.asarray(history, dtype=np.float64), x], axis=0)
+    return xe[xe.shape[0] - (K - 1):, :].copy()
+
+
+def l2_normalize(x: np.ndarray, eps: float = L2_EPS) -> np.ndarray:
+    """x / sqrt(sum_c x_c^2 + eps) over the last axis (one head's channels).
+
+    Reading (pages silent on the L2 norm's eps): eps inside the square root, added
+    to the sum of squares.  With eps' = d * eps this equals KimiRMSNorm with unit
+    weight divided by sqrt(d), which is how the tests tie it to the pages'
+    RMSNorm definition.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt((x * x).sum(axis=-1, keepdims=True) + eps)
+
+
+def gated_delta_step(S, q, k, v, g, beta, scale=1.0):
+    """One step of the channel-wise gated delta rule for a batch of heads.
+
+    S: [..., dk, dv] state before the step; q, k, g: [..., dk]; v: [..., dv];
+    beta: [...].  The decay alpha = exp(g) scales the rows of S (the key axis),
+    the reading that matches Diag(alpha) left-multiplying the dk x dv state.
+
+    Written in the rank-one form that the definition expands to:
+        S_bar = Diag(alpha) S
+        u     = beta * (v - S_bar^T k)
+        S'    = S_bar + k u^T            ( = (I - beta k k^T) S_bar + beta k v^T )
+        o     = scale * S'^T q           (output reads the updated state)
+    """
+    alpha = np.exp(g)
+    S_bar = alpha[..., :, None] * S
+    r = np.einsum("...cv,...c->...v", S_bar, k)
+    u = beta[..., None] * (v - r)
+    S_new = S_bar + k[..., :, None] * u[..., None, :]
+    o = scale * np.einsum("...cv,...c->...v", S_new, q)
+    return S_new, o
+
+
+def _check_decay(g):
+    if not np.all(np.isfinite(g)):
+        raise ValueError("log-decay g must be finite")
+    if np.any(g > 0):
+        raise ValueError("log-decay g must be <= 0 (decay factors in (0, 1])")
+
+
+def kda_reference(q, k, v, g, beta, conv_w=None, conv_state=None, S0=None,
+                  scale=1.0, l2norm_qk=True, eps=L2_EPS):
+    """The full KDA mixer over a batch of sequences, sequentially in time, fp64.
+
+    q, k, v, g: [B, T, H, D] (raw q, k, v before the convolution; g is the
+                per-channel log-decay, finite and <= 0)
+    beta:       [B, T, H]
+    conv_w:     [3, H*D, K] float32 filters for q, k, v in that order, or None to
+                skip the convolution and SiLU (inputs used as given)
+    conv_state: [B, 3, K-1, H*D] raw inputs preceding t = 0, or None for zeros
+    S0:         [B, H, D, D] initial state, or None for zeros
+    Returns (o [B, T, H, D], S_T [B, H, D, D], tail [B, 3, K-1, H*D] or None).
+
+    Steps: (1) short causal conv per channel and SiLU on q, k, v; (2) L2 norm of q
+    and k per head; (3) the gated delta rule step by step from S0.
+    """
+    q, k, v, g = (np.asarray(a, dtype=np.float64) for a in (q, k, v, g))
+    beta = np.asarray(beta, dtype=np.float64)
+    B, T, H, D = q.shape
+    _check_decay(g)
+    tail = None
+    if conv_w is not None:
+        conv_w = np.asarray(conv_w, dtype=np.float64)
+        K = conv_w.shape[2]
+        outs = []
+        tails = np.zeros((B, 3, K - 1, H * D))
+        for i, x in enumerate((q, k, v)):
+            y = np.empty_like(x)
+            for b in range(B):
+                hist = None if conv_state is None else np.asarray(conv_state[b, i], dtype=np.float64)
+                xb = x[b].reshape(T, H * D)
+                y[b] = silu(short_conv(xb, conv_w[i], hist)).reshape(T, H, D)
+                tails[b, i] = conv_tail(xb, hist, K)
+            outs.append(y)
+        q, k, v = outs
+        tail = tails
+    if l2norm_qk:
+        q = l2_normalize(q, eps)
+        k = l2_normalize(k, eps)
+    S = np.zeros((B, H, D, D)) if S0 is None else np.array(S0, dtype=np.float64)
+    o = np.empty((B, T, H, D))
+    for t in range(T):
+        S, o[:, t] = gated_delta_step(S, q[:, t], k[:, t], v[:, t], g[:, t], beta[:, t], scale)
+    return o, S, tail
+
+
+def kda_reference_decode_step(q, k, v, g, beta, S, conv_w=None, conv_state=None,
+                              scale=1.0, l2norm_qk=True, eps=L2_EPS):
+    """One autoregressive KDA step for B sequences: the mixer at T = 1.
+
+    q, k, v, g: [B, H, D] raw inputs of the new token; beta [B, H];
+    S [B, H, D, D] cached state; conv_state [B, 3, K-1, H*D] cached raw inputs.
+    Returns (o [B, H, D], S_new, conv_state_new).
+    """
+    o, S_new, tail = kda_reference(
+        np.asarray(q)[:, None], np.asarray(k)[:, None], np.asarray(v)[:, None],
+        np.asarray(g)[:, None], np.asarray(beta)[:, None],
+        conv_w=conv_w, conv_state=conv_state, S0=S, scale=scale,
+        l2norm_qk=l2norm_qk, eps=eps)
+    return o[:, 0], S_new, tail
+
+
+def conv_norm_reference(q, k, v, conv_w, conv_state=None, l2norm_qk=True, eps=L2_EPS):
+    """Only the pre-recurrence part: conv + SiLU on q, k, v, then L2 of q and k.
+
+    Same inputs as ``kda_reference``; returns (q_hat, k_hat, v_hat, tail).
+    """
+    q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
+    B, T, H, D = q.shape
+    conv_w = np.asarray(conv_w, dtype=np.float64)
+    K = conv_w.shape[2]
+    outs = []
+    tails = np.zeros((B, 3, K - 1, H * D))
+    for i, x in enumerate((q, k, v)):
+        y = np.empty_like(x)
+        for b in range(B):
+            hist = None if conv_state is None else np.asarray(conv_state[b, i], dtype=np.float64)
+            xb = x[b].reshape(T, H * D)
+            y[b] = silu(short_conv(xb, conv_w[i], hist)).reshape(T, H, D)
+            tails[b, i] = conv_tail(xb, hist, K)
+        outs.append(y)
+    qh, kh, vh = outs
+    if l2norm_qk:
+        qh = l2_normalize(qh, eps)
+        kh = l2_normalize(kh, eps)
+    return qh, kh, vh, tails
+
+
+def kda_reference_heads(q, k, v, g, beta, heads, conv_w=None, conv_state=None, S0=None,
+                        scale=1.0, l2norm_qk=True, eps=L2_EPS):
+    """``kda_reference`` restricted to a list of (b, h) pairs.
+
+    Heads are independent (their state, decay and filters are per head/channel),
+    so the result for a listed head equals the full call's.  Inputs are the full
+    arrays; only the listed slices are read.  Returns a list of (o [T, D], S_T
+    [D, D]) in the order of ``heads``.
+    """
+    out = []
+    D = q.shape[3]
+    for (b, h) in heads:
+        sl = slice(h * D, (h + 1) * D)
+        cw = None if conv_w is None else np.asarray(conv_w)[:, sl, :]
+        cs = None if conv_state is None else np.asarray(conv_state)[b:b + 1, :, :, sl]
+        s0 = None if S0 is None else np.asarray(S0)[b:b + 1, h:h + 1]
+        o, S, _ = kda_reference(
+            np.asarray(q)[b:b + 1, :, h:h + 1], np.asarray(k)[b:b + 1, :, h:h + 1],
+            np.asarray(v)[b:b + 1, :, h:h + 1], np.asarray(g)[b:b + 1, :, h:h + 1],
+            np.asarray(beta)[b:b + 1, :, h:h + 1], conv_w=cw, conv_state=cs, S0=s0,
+            scale=scale, l2norm_qk=l2norm_qk, eps=eps)
+        out.append((o[0, :, 0], S[0, 0]))
+    return out

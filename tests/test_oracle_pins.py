@@ -1,0 +1,337 @@
+"""Pins for the fp64 oracle: values fixed by hand, closed forms, brute force,
+invariants and an independent chunked rewrite.  CPU only.
+
+Each pin targets a plausible slip in the oracle: the hand example and the
+brute-force matrix form catch a wrong sign, a transposed state, decay on the wrong
+axis, a misplaced beta or reading S_{t-1} for the output; the impulse test catches
+a reversed tap order; the split tests catch a mishandled conv history or state
+hand-over; the norm identity catches eps in the wrong place.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+from scipy.special import expit
+
+from oracle import (conv_norm_reference, conv_tail, gated_delta_step, kda_reference,
+                    kda_reference_decode_step, kda_reference_heads, l2_normalize,
+                    short_conv, silu)
+from chunked_form import chunk_quantities, chunked_head
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rand_case(rng, B=1, T=9, H=2, D=4, strong=False, s0=True):
+    q = rng.standard_normal((B, T, H, D))
+    k = rng.standard_normal((B, T, H, D))
+    v = rng.standard_normal((B, T, H, D))
+    scale = 3.0 if strong else 0.5
+    g = -scale * np.log1p(np.exp(rng.standard_normal((B, T, H, D))))
+    beta = expit(rng.standard_normal((B, T, H)))
+    conv_w = 0.5 * rng.standard_normal((3, H * D, 4))
+    S0 = 0.1 * rng.standard_normal((B, H, D, D)) if s0 else None
+    return q, k, v, g, beta, conv_w, S0
+
+
+# ---------------------------------------------------------------- P1 hand example
+def test_hand_example_t1():
+    d = json.load(open(os.path.join(GOLDEN, "hand_t1.json")))
+    f = lambda x: np.array(x, dtype=np.float64)
+    q, k, v, g = (f(d[n]).reshape(1, 1, 1, 2) for n in ("q", "k", "v", "g"))
+    beta = np.full((1, 1, 1), d["beta"])
+    S0 = f(d["S0"]).reshape(1, 1, 2, 2)
+    o, S, tail = kda_reference(q, k, v, g, beta, conv_w=None, S0=S0, l2norm_qk=False)
+    assert tail is None
+    np.testing.assert_allclose(S[0, 0], f(d["S1"]), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(o[0, 0, 0], f(d["o"]), rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------- brute force: the matrix form
+def test_rank_one_step_equals_matrix_form():
+    rng = np.random.default_rng(1)
+    dk, dv = 5, 3
+    S = rng.standard_normal((dk, dv))
+    for _ in range(6):
+        q, k, g = rng.standard_normal(dk), rng.standard_normal(dk), -np.abs(rng.standard_normal(dk))
+        v = rng.standard_normal(dv)
+        beta = float(expit(rng.standard_normal()))
+        S_mat = (np.eye(dk) - beta * np.outer(k, k)) @ np.diag(np.exp(g)) @ S + beta * np.outer(k, v)
+        o_mat = S_mat.T @ q
+        S_new, o = gated_delta_step(S, q, k, v, g, np.float64(beta))
+        np.testing.assert_allclose(S_new, S_mat, rtol=1e-13, atol=1e-13)
+        np.testing.assert_allclose(o, o_mat, rtol=1e-13, atol=1e-13)
+        S = S_new
+
+
+def test_full_mixer_brute_force_tiny():
+    """Conv + SiLU + L2 + recurrence, each step written with explicit matrices."""
+    rng = np.random.default_rng(2)
+    B, T, H, D = 1, 5, 1, 3
+    q, k, v, g, beta, conv_w, S0 = rand_case(rng, B, T, H, D)
+    o, S, tail = kda_reference(q, k, v, g, beta, conv_w=conv_w, S0=S0)
+    # brute force: build each conv output as an explicit dot over the 4-tap window
+    xs = []
+    for i, x in enumerate((q, k, v)):
+        xe = np.concatenate([np.zeros((3, D)), x[0, :, 0]], axis=0)
+        y = np.array([[np.dot(conv_w[i, c], xe[t:t + 4, c]) for c in range(D)] for t in range(T)])
+        xs.append(y * expit(y))
+    qh, kh, vh = xs
+    qh = qh / np.sqrt((qh ** 2).sum(1, keepdims=True) + 1e-6)
+    kh = kh / np.sqrt((kh ** 2).sum(1, keepdims=True) + 1e-6)
+    Sm = S0[0, 0].copy()
+    for t in range(T):
+        b = beta[0, t, 0]
+        Sm = (np.eye(D) - b * np.outer(kh[t], kh[t])) @ np.diag(np.exp(g[0, t, 0])) @ Sm + b * np.outer(kh[t], vh[t])
+        np.testing.assert_allclose(o[0, t, 0], Sm.T @ qh[t], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(S[0, 0], Sm, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------------------- closed forms
+def test_beta0_alpha1_keeps_state():
+    """P2: beta = 0 and g = 0 leave S0 untouched and o_t = S0^T q_t."""
+    rng = np.random.default_rng(3)
+    q, k, v, _, _, _, S0 = rand_case(rng, B=2, T=7, H=2, D=4)
+    g = np.zeros_like(q)
+    beta = np.zeros(q.shape[:3])
+    o, S, _ = kda_reference(q, k, v, g, beta, S0=S0, l2norm_qk=False)
+    np.testing.assert_array_equal(S, S0)
+    for b in range(2):
+        for h in range(2):
+            np.testing.assert_allclose(o[b, :, h], q[b, :, h] @ S0[b, h], rtol=1e-13, atol=1e-13)
+
+
+def test_orthonormal_keys_linear_attention():
+    """P3: g = 0, S0 = 0, mutually orthonormal keys => S_T = sum_t beta_t k_t v_t^T
+    and o_t = sum_{j<=t} beta_j (k_j . q_t) v_j (plain causal linear attention)."""
+    rng = np.random.default_rng(4)
+    D, T = 6, 5
+    Qm, _ = np.linalg.qr(rng.standard_normal((D, D)))
+    k = Qm[:, :T].T.reshape(1, T, 1, D)
+    q = rng.standard_normal((1, T, 1, D))
+    v = rng.standard_normal((1, T, 1, D))
+    beta = expit(rng.standard_normal((1, T, 1)))
+    o, S, _ = kda_reference(q, k, v, np.zeros_like(q), beta, l2norm_qk=False)
+    expect = sum(beta[0, t, 0] * np.outer(k[0, t, 0], v[0, t, 0]) for t in range(T))
+    np.testing.assert_allclose(S[0, 0], expect, rtol=1e-12, atol=1e-12)
+    for t in range(T):
+        ot = sum(beta[0, j, 0] * np.dot(k[0, j, 0], q[0, t, 0]) * v[0, j, 0] for j in range(t + 1))
+        np.testing.assert_allclose(o[0, t, 0], ot, rtol=1e-12, atol=1e-12)
+    # beta = 1 gives exactly sum k v^T
+    o1, S1, _ = kda_reference(q, k, v, np.zeros_like(q), np.ones((1, T, 1)), l2norm_qk=False)
+    np.testing.assert_allclose(S1[0, 0], k[0, :, 0].T @ v[0, :, 0], rtol=1e-12, atol=1e-12)
+
+
+def test_alpha0_resets_state():
+    """P4: g = -1000 (alpha = 0) forgets S0: S_t = beta_t k_t v_t^T,
+    o_t = beta_t (k_t . q_t) v_t, whatever S0 is."""
+    rng = np.random.default_rng(5)
+    q, k, v, _, beta, _, S0 = rand_case(rng, B=1, T=6, H=1, D=4)
+    g = np.full_like(q, -1000.0)
+    o, S, _ = kda_reference(q, k, v, g, beta, S0=S0, l2norm_qk=False)
+    T = q.shape[1]
+    for t in range(T):
+        b = beta[0, t, 0]
+        np.testing.assert_allclose(o[0, t, 0], b * np.dot(k[0, t, 0], q[0, t, 0]) * v[0, t, 0],
+                                   rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(S[0, 0], beta[0, -1, 0] * np.outer(k[0, -1, 0], v[0, -1, 0]),
+                               rtol=1e-12, atol=1e-12)
+
+
+def test_retrieval_invariant():
+    """P5: S_t^T k_t = (1 - beta |k|^2) S_bar^T k_t + beta |k|^2 v_t, with
+    S_bar = Diag(exp g_t) S_{t-1}; unit keys and beta = 1 read back v_t exactly."""
+    rng = np.random.default_rng(6)
+    D = 5
+    S = rng.standard_normal((D, D))
+    for _ in range(5):
+        q, k, v = rng.standard_normal(D), rng.standard_normal(D), rng.standard_normal(D)
+        g = -np.abs(rng.standard_normal(D))
+        beta = np.float64(expit(rng.standard_normal()))
+        S_new, _ = gated_delta_step(S, q, k, v, g, beta)
+        S_bar = np.diag(np.exp(g)) @ S
+        kk = k @ k
+        np.testing.assert_allclose(S_new.T @ k, (1 - beta * kk) * (S_bar.T @ k) + beta * kk * v,
+                                   rtol=1e-12, atol=1e-12)
+        ku = k / np.linalg.norm(k)
+        S_one, _ = gated_delta_step(S, q, ku, v, g, np.float64(1.0))
+        np.testing.assert_allclose(S_one.T @ ku, v, rtol=1e-12, atol=1e-12)
+        S = S_new
+
+
+# ----------------------------------------------- P6/P7: chunked == sequential
+@pytest.mark.parametrize("C", [7, 16, 64])
+@pytest.mark.parametrize("strong", [False, True])
+def test_chunked_equals_sequential(C, strong):
+    rng = np.random.default_rng(7 + C)
+    T, D = 150, 8
+    q, k, v, g, beta, _, S0 = rand_case(rng, B=1, T=T, H=1, D=D, strong=strong)
+    q = l2_normalize(q)
+    k = l2_normalize(k)
+    o, S, _ = kda_reference(q, k, v, g, beta, S0=S0, l2norm_qk=False)
+    oc, Sc = chunked_head(q[0, :, 0], k[0, :, 0], v[0, :, 0], g[0, :, 0], beta[0, :, 0], S0[0, 0], C)
+    np.testing.assert_allclose(oc, o[0, :, 0], rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(Sc, S[0, 0], rtol=1e-11, atol=1e-12)
+
+
+def test_chunk_affine_state_map():
+    """P7: one chunk maps S0 to M S0 + N with M = Diag(Lam_C) - Ktil^T W, N = Ktil^T Ut."""
+    rng = np.random.default_rng(8)
+    C, D = 16, 6
+    q, k, v, g, beta, _, _ = rand_case(rng, B=1, T=C, H=1, D=D)
+    k = l2_normalize(k)
+    m = chunk_quantities(q[0, :, 0], k[0, :, 0], v[0, :, 0], g[0, :, 0], beta[0, :, 0])
+    M = np.diag(m["LamC"]) - m["Ktil"].T @ m["W"]
+    N = m["Ktil"].T @ m["Ut"]
+    for seed in range(3):
+        S0 = np.random.default_rng(seed).standard_normal((1, 1, D, D))
+        _, S, _ = kda_reference(q, k, v, g, beta, S0=S0, l2norm_qk=False)
+        np.testing.assert_allclose(S[0, 0], M @ S0[0, 0] + N, rtol=1e-11, atol=1e-12)
+
+
+# ------------------------------------------------------- P8: splitting time
+@pytest.mark.parametrize("t0", [1, 2, 3, 17])
+def test_time_split_and_decode(t0):
+    rng = np.random.default_rng(9)
+    B, T, H, D = 2, 24, 2, 4
+    q, k, v, g, beta, conv_w, S0 = rand_case(rng, B, T, H, D)
+    o, S, tail = kda_reference(q, k, v, g, beta, conv_w=conv_w, S0=S0)
+    a = slice(0, t0)
+    b = slice(t0, T)
+    o1, S1, tail1 = kda_reference(q[:, a], k[:, a], v[:, a], g[:, a], beta[:, a], conv_w=conv_w, S0=S0)
+    o2, S2, tail2 = kda_reference(q[:, b], k[:, b], v[:, b], g[:, b], beta[:, b], conv_w=conv_w,
+                                  conv_state=tail1, S0=S1)
+    np.testing.assert_allclose(np.concatenate([o1, o2], 1), o, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(S2, S, rtol=1e-12, atol=1e-12)
+    np.testing.assert_array_equal(tail2, tail)
+    # token-by-token decode reaches the same result
+    Sd, cs = S0.copy(), None
+    for t in range(T):
+        od, Sd, cs = kda_reference_decode_step(q[:, t], k[:, t], v[:, t], g[:, t], beta[:, t], Sd,
+                                               conv_w=conv_w, conv_state=cs)
+        np.testing.assert_allclose(od, o[:, t], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(Sd, S, rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------ P9: value columns are independent
+def test_value_column_independence():
+    rng = np.random.default_rng(10)
+    B, T, H, D = 1, 12, 2, 4
+    q, k, v, g, beta, conv_w, S0 = rand_case(rng, B, T, H, D)
+    o, S, _ = kda_reference(q, k, v, g, beta, conv_w=conv_w, S0=S0)
+    v2 = v.copy()
+    v2[..., 1] += 3.0
+    S02 = S0.copy()
+    S02[..., 1] -= 1.0
+    o2, S2, _ = kda_reference(q, k, v2, g, beta, conv_w=conv_w, S0=S02)
+    keep = [0, 2, 3]
+    np.testing.assert_array_equal(o2[..., keep], o[..., keep])
+    np.testing.assert_array_equal(S2[..., keep], S[..., keep])
+    assert not np.allclose(o2[..., 1], o[..., 1])
+
+
+def test_heads_are_independent():
+    rng = np.random.default_rng(11)
+    B, T, H, D = 2, 10, 3, 4
+    q, k, v, g, beta, conv_w, S0 = rand_case(rng, B, T, H, D)
+    conv_state = rng.standard_normal((B, 3, 3, H * D))
+    o, S, _ = kda_reference(q, k, v, g, beta, conv_w=conv_w, conv_state=conv_state, S0=S0)
+    heads = [(1, 2), (0, 0), (1, 1)]
+    for (b, h), (oh, Sh) in zip(heads, kda_reference_heads(q, k, v, g, beta, heads, conv_w=conv_w,
+                                                            conv_state=conv_state, S0=S0)):
+        np.testing.assert_array_equal(oh, o[b, :, h])
+        np.testing.assert_array_equal(Sh, S[b, h])
+
+
+# ----------------------------------------- P10: the pages' RMSNorm identity
+def kimi_rmsnorm(x, eps=1e-6):
+    """KimiRMSNorm with unit weight as printed on "Kimi-K3 atlas -- MoE input
+    (decode)": x * rsqrt(mean(x^2) + eps), in float32 there (fp64 here)."""
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+
+
+def test_l2_norm_matches_rmsnorm_identity():
+    rng = np.random.default_rng(12)
+    for d in (16, 128):
+        x = rng.standard_normal((50, d)) * np.exp(rng.uniform(-4, 2, size=(50, 1)))
+        eps = 1e-6
+        np.testing.assert_allclose(l2_normalize(x, d * eps), kimi_rmsnorm(x, eps) / np.sqrt(d),
+                                   rtol=1e-13, atol=0)
+        # closed form of the norm: |l2(x)| = sqrt(|x|^2 / (|x|^2 + eps)) = 1 - O(eps/|x|^2)
+        n2 = (x * x).sum(-1)
+        nrm = np.linalg.norm(l2_normalize(x, eps), axis=-1)
+        np.testing.assert_allclose(nrm, np.sqrt(n2 / (n2 + eps)), rtol=1e-14, atol=0)
+        assert np.all(np.abs(nrm - 1) <= eps / n2)
+    np.testing.assert_array_equal(l2_normalize(np.zeros((2, 8))), np.zeros((2, 8)))
+
+
+# -------------------------------------------------------- P11: convolution
+def test_conv_identity_taps_and_impulse():
+    rng = np.random.default_rng(13)
+    T, C = 11, 5
+    x = rng.standard_normal((T, C))
+    w_id = np.zeros((C, 4))
+    w_id[:, 3] = 1.0
+    np.testing.assert_array_equal(short_conv(x, w_id), x)
+    w = rng.standard_normal((C, 4))
+    imp = np.zeros((T, C))
+    imp[4, :] = 1.0
+    y = short_conv(imp, w)
+    for m in range(4):
+        np.testing.assert_array_equal(y[4 + m], w[:, 3 - m])
+    assert np.all(y[:4] == 0) and np.all(y[8:] == 0)
+
+
+def test_conv_matches_numpy_convolve_with_history():
+    rng = np.random.default_rng(14)
+    T, C = 13, 6
+    x = rng.standard_normal((T, C))
+    hist = rng.standard_normal((3, C))
+    w = rng.standard_normal((C, 4))
+    y = short_conv(x, w, hist)
+    for c in range(C):
+        full = np.convolve(np.concatenate([hist[:, c], x[:, c]]), w[c, ::-1])
+        np.testing.assert_allclose(y[:, c], full[3:3 + T], rtol=1e-13, atol=1e-13)
+    np.testing.assert_array_equal(conv_tail(x, hist), x[-3:])
+    np.testing.assert_array_equal(conv_tail(x[:2], hist), np.concatenate([hist[2:], x[:2]]))
+
+
+# ------------------------------------------------------------- P12: SiLU
+def test_silu_textbook():
+    x = np.linspace(-30, 30, 601)
+    np.testing.assert_allclose(silu(x), x * expit(x), rtol=1e-14, atol=1e-300)
+    assert silu(np.array([0.0]))[0] == 0.0
+
+
+def test_conv_norm_reference_is_the_mixer_front():
+    """The split-out conv/norm stage feeds the recurrence exactly."""
+    rng = np.random.default_rng(15)
+    q, k, v, g, beta, conv_w, S0 = rand_case(rng, 1, 6, 2, 4)
+    qh, kh, vh, tail = conv_norm_reference(q, k, v, conv_w)
+    o1, S1, t1 = kda_reference(q, k, v, g, beta, conv_w=conv_w, S0=S0)
+    o2, S2, _ = kda_reference(qh, kh, vh, g, beta, conv_w=None, S0=S0, l2norm_qk=False)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(S1, S2)
+    np.testing.assert_array_equal(tail, t1)
+
+
+# ------------------------------------------------------- preconditions
+def test_decay_preconditions():
+    rng = np.random.default_rng(16)
+    q, k, v, g, beta, _, _ = rand_case(rng, 1, 3, 1, 2)
+    with pytest.raises(ValueError):
+        kda_reference(q, k, v, np.abs(g) + 0.1, beta)
+    g2 = g.copy()
+    g2[0, 0, 0, 0] = np.nan
+    with pytest.raises(ValueError):
+        kda_reference(q, k, v, g2, beta)
+
+
+def test_empty_sequence_is_identity():
+    rng = np.random.default_rng(17)
+    q, k, v, g, beta, conv_w, S0 = rand_case(rng, 1, 0, 2, 4)
+    hist = rng.standard_normal((1, 3, 3, 8))
+    o, S, tail = kda_reference(q, k, v, g, beta, conv_w=conv_w, conv_state=hist, S0=S0)
+    assert o.shape == (1, 0, 2, 4)
+    np.testing.assert_array_equal(S, S0)
+    np.testing.assert_array_equal(tail, hist)
