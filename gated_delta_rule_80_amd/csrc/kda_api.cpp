@@ -1,0 +1,344 @@
+// Host side of libkda: argument validation (host-only, no HIP calls), workspace
+// sizing and the launch sequence on the caller's stream.  See include/kda.h.
+#include "kda.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <initializer_list>
+
+#include "kda_launch.h"
+#include "kda_layout.h"
+
+namespace {
+
+using kda::record_layout;
+
+struct Span {
+  uintptr_t lo = 0, hi = 0;  // [lo, hi); empty when lo == hi
+};
+
+Span span(const void* p, size_t bytes) {
+  Span s;
+  if (p != nullptr && bytes > 0) {
+    s.lo = reinterpret_cast<uintptr_t>(p);
+    s.hi = s.lo + bytes;
+  }
+  return s;
+}
+bool overlaps(Span a, Span b) { return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi; }
+bool same_or_disjoint(Span a, Span b) { return (a.lo == b.lo && a.hi == b.hi) || !overlaps(a, b); }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool supported_d(int D) { return D == 16 || D == 32 || D == 64 || D == 128; }
+bool supported_chunk(int C) { return C == 16 || C == 32 || C == 64; }
+size_t esize(int io) { return io == KDA_FP32 ? 4 : 2; }
+
+// a * b * c * d without overflow past 2^62; returns false on overflow.
+bool mul_ok(size_t& out, std::initializer_list<size_t> xs) {
+  size_t acc = 1;
+  for (size_t x : xs) {
+    if (x != 0 && acc > (size_t(1) << 62) / x) return false;
+    acc *= x;
+  }
+  out = acc;
+  return true;
+}
+
+kda_status hip_status(hipError_t e) { return e == hipSuccess ? KDA_OK : KDA_ERR_HIP; }
+
+struct PrefillSizes {
+  size_t x;      // bytes of one [B][T][H][D] tensor
+  size_t bta;    // bytes of beta
+  size_t state;  // bytes of S0 / S_T
+  size_t cw;     // bytes of conv_w
+  size_t cst;    // bytes of a conv state
+  int NT;
+};
+
+kda_status prefill_sizes(const kda_prefill_args* a, PrefillSizes& s) {
+  const size_t es = esize(a->io);
+  size_t tok;
+  if (!mul_ok(tok, {(size_t)a->B, (size_t)a->T})) return KDA_ERR_SHAPE;
+  if (!mul_ok(s.x, {tok, (size_t)a->H, (size_t)a->D, es})) return KDA_ERR_SHAPE;
+  if (!mul_ok(s.bta, {tok, (size_t)a->H, es})) return KDA_ERR_SHAPE;
+  if (!mul_ok(s.state, {(size_t)a->B, (size_t)a->H, (size_t)a->D, (size_t)a->D, 4})) return KDA_ERR_SHAPE;
+  const size_t ck = a->conv_k > 0 ? (size_t)a->conv_k : 0;
+  if (!mul_ok(s.cw, {3, (size_t)a->H, (size_t)a->D, ck, 4})) return KDA_ERR_SHAPE;
+  if (!mul_ok(s.cst, {(size_t)a->B, 3, ck > 0 ? ck - 1 : 0, (size_t)a->H, (size_t)a->D, es}))
+    return KDA_ERR_SHAPE;
+  s.NT = a->chunk > 0 ? (a->T + a->chunk - 1) / a->chunk : 0;
+  // one workgroup per (b, h, chunk) must fit a 1-D grid
+  size_t wgs;
+  if (!mul_ok(wgs, {(size_t)a->B, (size_t)a->H, (size_t)(s.NT > 0 ? s.NT : 1)}) ||
+      wgs > 0x7fffffffu)
+    return KDA_ERR_SHAPE;
+  return KDA_OK;
+}
+
+size_t record_bytes(int io, int D, int C) { return record_layout(C, D, esize(io)).bytes; }
+
+// Choice of the value-column block of the state walk: narrower blocks give more
+// parallel walks when B * H is small.
+int state_vblock(int B, int H, int D) {
+  if (D < 64) return D;
+  const long walks64 = (long)B * H * (D / 64);
+  return walks64 < 240 ? 32 : 64;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char* kda_status_str(int status) {
+  switch (status) {
+    case KDA_OK: return "ok";
+    case KDA_ERR_NULL: return "required pointer is NULL";
+    case KDA_ERR_SHAPE: return "invalid or overflowing size";
+    case KDA_ERR_DTYPE: return "invalid dtype";
+    case KDA_ERR_ALIGN: return "device pointer not 16-byte aligned";
+    case KDA_ERR_ALIAS: return "output overlaps an input";
+    case KDA_ERR_UNSUPPORTED: return "unsupported mode";
+    case KDA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case KDA_ERR_HIP: return "HIP runtime error";
+    case KDA_ERR_VALUE: return "scalar argument out of range";
+  }
+  return "unknown status";
+}
+
+kda_status kda_validate_prefill(const kda_prefill_args* a) {
+  if (a == nullptr) return KDA_ERR_NULL;
+  if (a->io != KDA_BF16 && a->io != KDA_FP32) return KDA_ERR_DTYPE;
+  if (a->B < 1 || a->T < 0 || a->H < 1 || a->D < 1 || a->chunk < 1 || a->conv_k < 0)
+    return KDA_ERR_SHAPE;
+  if (!supported_d(a->D) || !supported_chunk(a->chunk) || (a->conv_k != 0 && a->conv_k != 4))
+    return KDA_ERR_UNSUPPORTED;
+  if (a->io == KDA_FP32 && a->D == 128 && a->chunk == 64) return KDA_ERR_UNSUPPORTED;
+  if ((a->flags & ~KDA_FLAG_L2NORM_QK) != 0) return KDA_ERR_VALUE;
+  if (!std::isfinite(a->l2_eps) || a->l2_eps < 0.f || !std::isfinite(a->scale)) return KDA_ERR_VALUE;
+  PrefillSizes s;
+  if (kda_status e = prefill_sizes(a, s); e != KDA_OK) return e;
+  const bool need_x = a->T > 0;
+  if (need_x && (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->o)) return KDA_ERR_NULL;
+  if (!a->S_T) return KDA_ERR_NULL;
+  if (a->conv_k > 0 && !a->conv_w) return KDA_ERR_NULL;
+  if (a->conv_k == 0 && (a->conv_w || a->conv_state_in || a->conv_state_out)) return KDA_ERR_NULL;
+  for (const void* p : std::initializer_list<const void*>{a->q, a->k, a->v, a->g, a->beta, (const void*)a->conv_w, a->conv_state_in,
+                        (const void*)a->S0, a->o, (const void*)a->S_T, (const void*)a->conv_state_out})
+    if (p && !aligned16(p)) return KDA_ERR_ALIGN;
+  const Span q = span(a->q, s.x), k = span(a->k, s.x), v = span(a->v, s.x), g = span(a->g, s.x);
+  const Span bt = span(a->beta, s.bta), cw = span(a->conv_w, s.cw);
+  const Span ci = span(a->conv_state_in, s.cst), co = span(a->conv_state_out, s.cst);
+  const Span s0 = span(a->S0, s.state), st = span(a->S_T, s.state), o = span(a->o, s.x);
+  for (Span in : {q, k, v, g, bt, cw, ci, s0, st, co})
+    if (overlaps(o, in)) return KDA_ERR_ALIAS;
+  for (Span in : {q, k, v, g, bt, cw, ci, co})
+    if (overlaps(st, in)) return KDA_ERR_ALIAS;
+  if (!same_or_disjoint(st, s0)) return KDA_ERR_ALIAS;
+  for (Span in : {q, k, v, g, bt, cw, s0})
+    if (overlaps(co, in)) return KDA_ERR_ALIAS;
+  if (!same_or_disjoint(co, ci)) return KDA_ERR_ALIAS;
+  return KDA_OK;
+}
+
+size_t kda_prefill_workspace_bytes(const kda_prefill_args* a) {
+  if (kda_validate_prefill(a) != KDA_OK) return 0;
+  const int NT = (a->T + a->chunk - 1) / a->chunk;
+  size_t n;
+  if (!mul_ok(n, {(size_t)a->B, (size_t)a->H, (size_t)NT, record_bytes(a->io, a->D, a->chunk)}))
+    return 0;
+  return n;
+}
+
+static kda_status check_workspace(const kda_prefill_args* a, void* ws, size_t ws_bytes) {
+  const size_t need = kda_prefill_workspace_bytes(a);
+  if (need == 0) return KDA_OK;
+  if (ws == nullptr || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0 || ws_bytes < need)
+    return KDA_ERR_WORKSPACE;
+  PrefillSizes s;
+  prefill_sizes(a, s);
+  const Span w = span(ws, need);
+  for (Span x : {span(a->q, s.x), span(a->k, s.x), span(a->v, s.x), span(a->g, s.x),
+                 span(a->beta, s.bta), span(a->conv_w, s.cw), span(a->conv_state_in, s.cst),
+                 span(a->S0, s.state), span(a->o, s.x), span(a->S_T, s.state),
+                 span(a->conv_state_out, s.cst)})
+    if (overlaps(w, x)) return KDA_ERR_ALIAS;
+  return KDA_OK;
+}
+
+static kda_status run_stage(const kda_prefill_args* a, void* ws, int stage, hipStream_t st) {
+  const bool fp32 = a->io == KDA_FP32;
+  const int NT = (a->T + a->chunk - 1) / a->chunk;
+  switch (stage) {
+    case KDA_STAGE_PREP: {
+      if (a->T == 0) return KDA_OK;
+      kda::PrepParams p{};
+      p.q = a->q; p.k = a->k; p.v = a->v; p.g = a->g; p.beta = a->beta;
+      p.conv_w = a->conv_k > 0 ? a->conv_w : nullptr;
+      p.conv_state_in = a->conv_k > 0 ? a->conv_state_in : nullptr;
+      p.ws = static_cast<char*>(ws);
+      p.B = a->B; p.T = a->T; p.H = a->H; p.NT = NT;
+      p.conv_k = a->conv_k;
+      p.l2 = (a->flags & KDA_FLAG_L2NORM_QK) ? 1 : 0;
+      p.eps = a->l2_eps;
+      p.scale = a->scale;
+      return hip_status(kda::launch_prep(p, a->D, a->chunk, fp32, st));
+    }
+    case KDA_STAGE_STATE: {
+      if (a->T == 0) {
+        if (a->S_T == a->S0) return KDA_OK;
+        const size_t n = (size_t)a->B * a->H * a->D * a->D;
+        return hip_status(kda::launch_copy_state(a->S0, a->S_T, n, st));
+      }
+      kda::StateParams p{};
+      p.ws = static_cast<const char*>(ws);
+      p.S0 = a->S0; p.S_T = a->S_T; p.o = a->o;
+      p.B = a->B; p.T = a->T; p.H = a->H; p.NT = NT;
+      return hip_status(
+          kda::launch_state(p, a->D, a->chunk, fp32, state_vblock(a->B, a->H, a->D), st));
+    }
+    case KDA_STAGE_CONV_TAIL: {
+      if (a->conv_k == 0 || a->conv_state_out == nullptr) return KDA_OK;
+      kda::TailParams p{};
+      p.x[0] = a->q; p.x[1] = a->k; p.x[2] = a->v;
+      p.conv_state_in = a->conv_state_in;
+      p.conv_state_out = a->conv_state_out;
+      p.B = a->B; p.T = a->T; p.HD = a->H * a->D;
+      return hip_status(kda::launch_conv_tail(p, fp32, st));
+    }
+  }
+  return KDA_ERR_VALUE;
+}
+
+kda_status kda_prefill_stage(const kda_prefill_args* a, void* ws, size_t ws_bytes, int stage,
+                             void* stream) {
+  if (kda_status e = kda_validate_prefill(a); e != KDA_OK) return e;
+  if (stage < KDA_STAGE_PREP || stage > KDA_STAGE_CONV_TAIL) return KDA_ERR_VALUE;
+  if (kda_status e = check_workspace(a, ws, ws_bytes); e != KDA_OK) return e;
+  return run_stage(a, ws, stage, static_cast<hipStream_t>(stream));
+}
+
+kda_status kda_prefill(const kda_prefill_args* a, void* ws, size_t ws_bytes, void* stream) {
+  if (kda_status e = kda_validate_prefill(a); e != KDA_OK) return e;
+  if (kda_status e = check_workspace(a, ws, ws_bytes); e != KDA_OK) return e;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  for (int stage = KDA_STAGE_PREP; stage <= KDA_STAGE_CONV_TAIL; ++stage)
+    if (kda_status e = run_stage(a, ws, stage, st); e != KDA_OK) return e;
+  return KDA_OK;
+}
+
+// ------------------------------------------------------------------ conv_norm
+kda_status kda_validate_conv_norm(const kda_conv_norm_args* a) {
+  if (a == nullptr) return KDA_ERR_NULL;
+  if (a->io != KDA_BF16 && a->io != KDA_FP32) return KDA_ERR_DTYPE;
+  if (a->B < 1 || a->T < 0 || a->H < 1 || a->D < 1 || a->conv_k < 0) return KDA_ERR_SHAPE;
+  if (!supported_d(a->D) || a->conv_k != 4) return KDA_ERR_UNSUPPORTED;
+  if ((a->flags & ~KDA_FLAG_L2NORM_QK) != 0) return KDA_ERR_VALUE;
+  if (!std::isfinite(a->l2_eps) || a->l2_eps < 0.f) return KDA_ERR_VALUE;
+  const size_t es = esize(a->io);
+  size_t x, cw, cst;
+  if (!mul_ok(x, {(size_t)a->B, (size_t)a->T, (size_t)a->H, (size_t)a->D, es}) ||
+      !mul_ok(cw, {3, (size_t)a->H, (size_t)a->D, 4, 4}) ||
+      !mul_ok(cst, {(size_t)a->B, 3, 3, (size_t)a->H, (size_t)a->D, es}))
+    return KDA_ERR_SHAPE;
+  if ((size_t)a->B * a->H * ((a->T + 63) / 64 + 1) > 0x7fffffffu) return KDA_ERR_SHAPE;
+  if (a->T > 0 && (!a->q || !a->k || !a->v || !a->q_out || !a->k_out || !a->v_out))
+    return KDA_ERR_NULL;
+  if (!a->conv_w) return KDA_ERR_NULL;
+  for (const void* p : std::initializer_list<const void*>{a->q, a->k, a->v, (const void*)a->conv_w, a->conv_state_in, a->q_out,
+                        a->k_out, a->v_out, a->conv_state_out})
+    if (p && !aligned16(p)) return KDA_ERR_ALIGN;
+  const Span q = span(a->q, x), k = span(a->k, x), v = span(a->v, x), w = span(a->conv_w, cw);
+  const Span ci = span(a->conv_state_in, cst), co = span(a->conv_state_out, cst);
+  const Span oq = span(a->q_out, x), ok = span(a->k_out, x), ov = span(a->v_out, x);
+  for (Span out : {oq, ok, ov})
+    for (Span in : {q, k, v, w, ci, co})
+      if (overlaps(out, in)) return KDA_ERR_ALIAS;
+  if (overlaps(oq, ok) || overlaps(oq, ov) || overlaps(ok, ov)) return KDA_ERR_ALIAS;
+  for (Span in : {q, k, v, w})
+    if (overlaps(co, in)) return KDA_ERR_ALIAS;
+  if (!same_or_disjoint(co, ci)) return KDA_ERR_ALIAS;
+  return KDA_OK;
+}
+
+kda_status kda_conv_norm(const kda_conv_norm_args* a, void* stream) {
+  if (kda_status e = kda_validate_conv_norm(a); e != KDA_OK) return e;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool fp32 = a->io == KDA_FP32;
+  if (a->T > 0) {
+    kda::ConvNormParams p{};
+    p.q = a->q; p.k = a->k; p.v = a->v;
+    p.conv_w = a->conv_w;
+    p.conv_state_in = a->conv_state_in;
+    p.q_out = a->q_out; p.k_out = a->k_out; p.v_out = a->v_out;
+    p.B = a->B; p.T = a->T; p.H = a->H;
+    p.l2 = (a->flags & KDA_FLAG_L2NORM_QK) ? 1 : 0;
+    p.eps = a->l2_eps;
+    if (kda_status e = hip_status(kda::launch_conv_norm(p, a->D, fp32, st)); e != KDA_OK) return e;
+  }
+  if (a->conv_state_out != nullptr) {
+    kda::TailParams p{};
+    p.x[0] = a->q; p.x[1] = a->k; p.x[2] = a->v;
+    p.conv_state_in = a->conv_state_in;
+    p.conv_state_out = a->conv_state_out;
+    p.B = a->B; p.T = a->T; p.HD = a->H * a->D;
+    return hip_status(kda::launch_conv_tail(p, fp32, st));
+  }
+  return KDA_OK;
+}
+
+// --------------------------------------------------------------------- decode
+kda_status kda_validate_decode(const kda_decode_args* a) {
+  if (a == nullptr) return KDA_ERR_NULL;
+  if (a->io != KDA_BF16 && a->io != KDA_FP32) return KDA_ERR_DTYPE;
+  if (a->B < 1 || a->H < 1 || a->D < 1 || a->conv_k < 0) return KDA_ERR_SHAPE;
+  if (!supported_d(a->D) || (a->conv_k != 0 && a->conv_k != 4)) return KDA_ERR_UNSUPPORTED;
+  if ((a->flags & ~KDA_FLAG_L2NORM_QK) != 0) return KDA_ERR_VALUE;
+  if (!std::isfinite(a->l2_eps) || a->l2_eps < 0.f || !std::isfinite(a->scale)) return KDA_ERR_VALUE;
+  const size_t es = esize(a->io);
+  const size_t ck = a->conv_k > 0 ? (size_t)a->conv_k : 0;
+  size_t x, bt, st, cw, cst;
+  if (!mul_ok(x, {(size_t)a->B, (size_t)a->H, (size_t)a->D, es}) ||
+      !mul_ok(bt, {(size_t)a->B, (size_t)a->H, es}) ||
+      !mul_ok(st, {(size_t)a->B, (size_t)a->H, (size_t)a->D, (size_t)a->D, 4}) ||
+      !mul_ok(cw, {3, (size_t)a->H, (size_t)a->D, ck, 4}) ||
+      !mul_ok(cst, {(size_t)a->B, 3, ck > 0 ? ck - 1 : 0, (size_t)a->H, (size_t)a->D, es}))
+    return KDA_ERR_SHAPE;
+  if ((size_t)a->B * a->H > 0x7fffffffu) return KDA_ERR_SHAPE;
+  if (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->S || !a->o) return KDA_ERR_NULL;
+  if (a->conv_k > 0 && (!a->conv_w || !a->conv_state)) return KDA_ERR_NULL;
+  if (a->conv_k == 0 && (a->conv_w || a->conv_state)) return KDA_ERR_NULL;
+  for (const void* p : std::initializer_list<const void*>{a->q, a->k, a->v, a->g, a->beta, (const void*)a->conv_w,
+                        (const void*)a->conv_state, (const void*)a->S, a->o})
+    if (p && !aligned16(p)) return KDA_ERR_ALIGN;
+  const Span q = span(a->q, x), k = span(a->k, x), v = span(a->v, x), g = span(a->g, x);
+  const Span b = span(a->beta, bt), w = span(a->conv_w, cw), cs = span(a->conv_state, cst);
+  const Span S = span(a->S, st), o = span(a->o, x);
+  for (Span in : {q, k, v, g, b, w, cs, S})
+    if (overlaps(o, in)) return KDA_ERR_ALIAS;
+  for (Span in : {q, k, v, g, b, w, cs})
+    if (overlaps(S, in)) return KDA_ERR_ALIAS;
+  for (Span in : {q, k, v, g, b, w})
+    if (overlaps(cs, in)) return KDA_ERR_ALIAS;
+  return KDA_OK;
+}
+
+kda_status kda_decode_step(const kda_decode_args* a, void* stream) {
+  if (kda_status e = kda_validate_decode(a); e != KDA_OK) return e;
+  kda::DecodeParams p{};
+  p.q = a->q; p.k = a->k; p.v = a->v; p.g = a->g; p.beta = a->beta;
+  p.conv_w = a->conv_k > 0 ? a->conv_w : nullptr;
+  p.conv_state = a->conv_state;
+  p.S = a->S;
+  p.o = a->o;
+  p.B = a->B; p.H = a->H;
+  p.conv_k = a->conv_k;
+  p.l2 = (a->flags & KDA_FLAG_L2NORM_QK) ? 1 : 0;
+  p.eps = a->l2_eps;
+  p.scale = a->scale;
+  return hip_status(kda::launch_decode(p, a->D, a->io == KDA_FP32, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

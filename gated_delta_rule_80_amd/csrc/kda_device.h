@@ -1,0 +1,170 @@
+// Device helpers for the KDA kernels on gfx950 (CDNA4): element conversions,
+// 16x16 matrix-core tiles and small wave utilities.
+//
+// Matrix-core tile convention used everywhere (wave64, 16 x 16 output tile):
+//   operand rows:  lane l supplies row (l % 16) of the A operand and column
+//                  (l % 16) of the B operand, with a run of consecutive k values
+//                  chosen by the lane group g = l / 16.  A and B use the same
+//                  (g, slot) -> k assignment, so the contraction is over the full
+//                  k range whatever order the hardware walks it in.
+//   accumulator:   lane l holds column (l % 16), rows 4*(l/16) + 0..3.
+// Both operands are read "along k": A as rows of A, B as rows of B^T.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- conversions
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }
+
+template <typename E> __device__ __forceinline__ E from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }  // RNE
+
+// Load 8 consecutive elements (16-byte aligned for bf16, 32-byte for fp32) as floats.
+__device__ __forceinline__ void load8(const __bf16* p, float* out) {
+  bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) out[i] = (float)v[i];
+}
+__device__ __forceinline__ void load8(const float* p, float* out) {
+  f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { out[i] = a[i]; out[4 + i] = b[i]; }
+}
+__device__ __forceinline__ void store8(__bf16* p, const float* in) {
+  bf16x8 v;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = (__bf16)in[i];
+  *reinterpret_cast<bf16x8*>(p) = v;
+}
+__device__ __forceinline__ void store8(float* p, const float* in) {
+  f32x4 a, b;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { a[i] = in[i]; b[i] = in[4 + i]; }
+  *reinterpret_cast<f32x4*>(p) = a;
+  *reinterpret_cast<f32x4*>(p + 4) = b;
+}
+// 4 consecutive elements (8-byte aligned bf16 / 16-byte aligned fp32)
+__device__ __forceinline__ void store4(__bf16* p, float a, float b, float c, float d) {
+  bf16x4 v;
+  v[0] = (__bf16)a; v[1] = (__bf16)b; v[2] = (__bf16)c; v[3] = (__bf16)d;
+  *reinterpret_cast<bf16x4*>(p) = v;
+}
+__device__ __forceinline__ void store4(float* p, float a, float b, float c, float d) {
+  f32x4 v;
+  v[0] = a; v[1] = b; v[2] = c; v[3] = d;
+  *reinterpret_cast<f32x4*>(p) = v;
+}
+__device__ __forceinline__ void load4(const __bf16* p, float* out) {
+  bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+  out[0] = (float)v[0]; out[1] = (float)v[1]; out[2] = (float)v[2]; out[3] = (float)v[3];
+}
+__device__ __forceinline__ void load4(const float* p, float* out) {
+  f32x4 v = *reinterpret_cast<const f32x4*>(p);
+  out[0] = v[0]; out[1] = v[1]; out[2] = v[2]; out[3] = v[3];
+}
+
+// ------------------------------------------------------------ matrix-core tiles
+// acc(16x16) += A(16 x K) * B(K x 16) where A is given by its rows (A + m*lda, k
+// contiguous) and B by the rows of B^T (Bt + n*ldb, k contiguous).  K is a
+// compile-time multiple of 16 (bf16) or 4 (fp32).  Pointers may be LDS or global.
+template <int K>
+__device__ __forceinline__ void mma_rows(f32x4& acc, const __bf16* A, int lda, const __bf16* Bt,
+                                         int ldb, int lane) {
+  const int r = lane & 15, g = lane >> 4;
+  static_assert(K % 16 == 0, "bf16 tiles need K % 16 == 0");
+  if constexpr (K % 32 == 0) {
+#pragma unroll
+    for (int k0 = 0; k0 < K; k0 += 32) {
+      bf16x8 a = *reinterpret_cast<const bf16x8*>(A + r * lda + k0 + 8 * g);
+      bf16x8 b = *reinterpret_cast<const bf16x8*>(Bt + r * ldb + k0 + 8 * g);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int k0 = 0; k0 < K; k0 += 16) {
+      s16x4 a = *reinterpret_cast<const s16x4*>(A + r * lda + k0 + 4 * g);
+      s16x4 b = *reinterpret_cast<const s16x4*>(Bt + r * ldb + k0 + 4 * g);
+      acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, acc, 0, 0, 0);
+    }
+  }
+}
+template <int K>
+__device__ __forceinline__ void mma_rows(f32x4& acc, const float* A, int lda, const float* Bt,
+                                         int ldb, int lane) {
+  const int r = lane & 15, g = lane >> 4;
+  static_assert(K % 4 == 0, "fp32 tiles need K % 4 == 0");
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += 4) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A[r * lda + k0 + g], Bt[r * ldb + k0 + g], acc, 0,
+                                               0, 0);
+  }
+}
+
+// Same as mma_rows but only over k in [0, kmax) rounded up to the instruction
+// depth (kmax is a runtime bound used for causal skipping; entries past the true
+// bound must be zero in memory or masked by the caller).
+template <int K>
+__device__ __forceinline__ void mma_rows_upto(f32x4& acc, const __bf16* A, int lda,
+                                              const __bf16* Bt, int ldb, int lane, int kmax) {
+  const int r = lane & 15, g = lane >> 4;
+  if constexpr (K % 32 == 0) {
+#pragma unroll
+    for (int k0 = 0; k0 < K; k0 += 32) {
+      if (k0 < kmax) {
+        bf16x8 a = *reinterpret_cast<const bf16x8*>(A + r * lda + k0 + 8 * g);
+        bf16x8 b = *reinterpret_cast<const bf16x8*>(Bt + r * ldb + k0 + 8 * g);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k0 = 0; k0 < K; k0 += 16) {
+      if (k0 < kmax) {
+        s16x4 a = *reinterpret_cast<const s16x4*>(A + r * lda + k0 + 4 * g);
+        s16x4 b = *reinterpret_cast<const s16x4*>(Bt + r * ldb + k0 + 4 * g);
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, acc, 0, 0, 0);
+      }
+    }
+  }
+}
+template <int K>
+__device__ __forceinline__ void mma_rows_upto(f32x4& acc, const float* A, int lda, const float* Bt,
+                                              int ldb, int lane, int kmax) {
+  const int r = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += 4) {
+    if (k0 < kmax)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A[r * lda + k0 + g], Bt[r * ldb + k0 + g], acc, 0,
+                                                 0, 0);
+  }
+}
+
+// Instruction depth along k for an element type (used for causal bounds).
+template <typename E> struct KStep;
+template <> struct KStep<__bf16> { static constexpr int value = 32; };
+template <> struct KStep<float> { static constexpr int value = 4; };
+
+// ------------------------------------------------------------ small math
+__device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
+
+// xor-butterfly sum over groups of `W` consecutive lanes (W a power of two <= 64)
+template <int W>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+  for (int m = 1; m < W; m <<= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+
+}  // namespace kda

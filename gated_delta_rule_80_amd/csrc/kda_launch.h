@@ -1,0 +1,16 @@
+// Kernel launchers (defined next to their kernels, called by the host runtime).
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include "kda_layout.h"
+
+namespace kda {
+
+hipError_t launch_prep(const PrepParams& p, int D, int C, bool fp32, hipStream_t st);
+hipError_t launch_state(const StateParams& p, int D, int C, bool fp32, int vb, hipStream_t st);
+hipError_t launch_conv_norm(const ConvNormParams& p, int D, bool fp32, hipStream_t st);
+hipError_t launch_conv_tail(const TailParams& p, bool fp32, hipStream_t st);
+hipError_t launch_copy_state(const float* src, float* dst, size_t n, hipStream_t st);
+hipError_t launch_decode(const DecodeParams& p, int D, bool fp32, hipStream_t st);
+
+}  // namespace kda

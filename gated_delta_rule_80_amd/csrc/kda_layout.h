@@ -1,0 +1,101 @@
+// Workspace layout and kernel parameter blocks shared by the host runtime and
+// the kernels.  No HIP types here: the host side includes it from plain C++.
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+constexpr size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// One workspace record per (sequence, head, chunk) holds what the chunk
+// preparation hands to the state walk, in element type E (bf16 or fp32):
+//   W      [C][D]  row-major   T diag(beta) (K * Lambda)
+//   QL     [C][D]  row-major   scale * Q * Lambda
+//   KT     [D][C]  row-major   (K * exp(Gamma_C - Gamma))^T
+//   U      [C][D]  fragment order: tile (t/16, v/16) of 64 lanes x 4 values
+//                  T diag(beta) V (the state-free part of the new values)
+//   P      [C][C]  row-major   scale * (Q K^T masked, with relative decay), j <= i
+//   LC     [D]     float32     exp(Gamma_C), the chunk's total decay
+struct RecordLayout {
+  size_t w, ql, kt, u, p;  // element offsets
+  size_t lc_bytes;         // byte offset of LC
+  size_t bytes;            // record size (256-byte multiple)
+};
+
+constexpr RecordLayout record_layout(int C, int D, size_t esize) {
+  RecordLayout r{};
+  const size_t cd = (size_t)C * D;
+  r.w = 0;
+  r.ql = cd;
+  r.kt = 2 * cd;
+  r.u = 3 * cd;
+  r.p = 4 * cd;
+  r.lc_bytes = round_up((4 * cd + (size_t)C * C) * esize, 16);
+  r.bytes = round_up(r.lc_bytes + 4 * (size_t)D, 256);
+  return r;
+}
+
+struct PrepParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* g;
+  const void* beta;
+  const float* conv_w;        // NULL when conv_k == 0
+  const void* conv_state_in;  // may be NULL
+  char* ws;
+  int B, T, H, NT;
+  int conv_k;
+  int l2;
+  float eps;
+  float scale;
+};
+
+struct StateParams {
+  const char* ws;
+  const float* S0;  // may be NULL
+  float* S_T;
+  void* o;
+  int B, T, H, NT;
+};
+
+struct ConvNormParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* conv_w;
+  const void* conv_state_in;
+  void* q_out;
+  void* k_out;
+  void* v_out;
+  int B, T, H;
+  int l2;
+  float eps;
+};
+
+struct TailParams {
+  const void* x[3];           // q, k, v raw inputs [B][T][H*D]
+  const void* conv_state_in;  // may be NULL
+  void* conv_state_out;
+  int B, T, HD;
+};
+
+struct DecodeParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* g;
+  const void* beta;
+  const float* conv_w;  // NULL when conv_k == 0
+  void* conv_state;
+  float* S;
+  void* o;
+  int B, H;
+  int conv_k;
+  int l2;
+  float eps;
+  float scale;
+};
+
+}  // namespace kda

@@ -1,0 +1,190 @@
+/*
+ * kda.h -- C ABI of libkda, the Kimi Delta Attention (KDA) token mixer for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The mixer (the token mixer of 69 of the 93 layers of Kimi-K3, with a state of
+ * fixed size per head: "Kimi-K3 model atlas -- self.layers"; geometry from the
+ * released config's linear_attn_config: num_heads 96, head_dim 128,
+ * short_conv_kernel_size 4, full-rank gate) computes, per sequence b and head h:
+ *
+ *   1. causal depthwise conv over time, kernel K = conv_k (no bias), then SiLU,
+ *      on q, k and v separately:  y[t,c] = SiLU( sum_tau w[c,tau] x[t-(K-1)+tau, c] )
+ *      (filters stored per channel as [H*D, 1, K] float32: "MaxText PR 5548",
+ *      review item 2; the last tap multiplies the current token);
+ *   2. L2 normalisation of q and k over the head's D channels:
+ *      x / sqrt(sum x^2 + l2_eps)   (l2_eps defaults to 1e-6, the eps the pages
+ *      fix for KimiRMSNorm: "Kimi-K3 atlas -- MoE input (decode)");
+ *   3. the channel-wise gated delta rule with a D x D float32 state,
+ *      S_t = (I - beta_t k_t k_t^T) Diag(exp(g_t)) S_{t-1} + beta_t k_t v_t^T,
+ *      o_t = scale * S_t^T q_t   (decay per key channel; the output reads S_t).
+ *
+ * Conventions for every entry point
+ *   - Ownership: the caller owns every buffer.  The library never allocates or
+ *     frees device memory and keeps no global mutable state (reentrant; any
+ *     number of streams).  Scratch memory is the caller's workspace.
+ *   - Pointers named "device" are device (HBM) addresses; they must be 16-byte
+ *     aligned.  Argument structs themselves live in host memory.
+ *   - Asynchrony: compute entry points enqueue kernels on `stream` (a
+ *     hipStream_t passed as void*, NULL = the default stream) and return.  Launch
+ *     failures are reported as KDA_ERR_HIP; faults during execution surface at
+ *     the caller's next synchronisation.
+ *   - All-or-nothing: every argument is validated on the host before anything is
+ *     enqueued; on any error nothing is launched and outputs are untouched.
+ *     Validation never calls into the HIP runtime and never reads device memory.
+ *   - Unsupported modes return KDA_ERR_UNSUPPORTED instead of computing a wrong
+ *     result (packed/variable-length batches, D outside {16,32,64,128},
+ *     conv_k outside {0,4}, chunk outside {16,32,64}, fp32 I/O with D = 128 and
+ *     chunk = 64).
+ *   - Device values are not checked: g must be finite and <= 0, inputs finite.
+ *
+ * Layouts (row-major, innermost last; dtype = `io` unless stated):
+ *   q, k, v, g, o   [B][T][H][D]        (decode: [B][H][D])
+ *   beta            [B][T][H]           (decode: [B][H])
+ *   conv_w          [3][H*D][conv_k]    float32, filters of q, k, v in that order
+ *   conv state      [B][3][conv_k-1][H*D]  raw (pre-conv) inputs, oldest first
+ *   S0, S_T, S      [B][H][D][D]        float32, row = key channel, col = value channel
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+typedef enum kda_status {
+  KDA_OK = 0,
+  KDA_ERR_NULL = 1,        /* a required pointer is NULL (or conv_w given with conv_k = 0) */
+  KDA_ERR_SHAPE = 2,       /* a size is negative, zero where it must not be, or overflows */
+  KDA_ERR_DTYPE = 3,       /* io is not a kda_dtype */
+  KDA_ERR_ALIGN = 4,       /* a device pointer is not 16-byte aligned */
+  KDA_ERR_ALIAS = 5,       /* an output overlaps an input it may not overlap */
+  KDA_ERR_UNSUPPORTED = 6, /* valid request outside what this build implements */
+  KDA_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than the query says */
+  KDA_ERR_HIP = 8,         /* the HIP runtime refused a launch */
+  KDA_ERR_VALUE = 9        /* a scalar argument is out of range (eps, scale, flags, stage) */
+} kda_status;
+
+typedef enum kda_dtype {
+  KDA_BF16 = 0, /* bfloat16 I/O, bf16 matrix-core products with float32 accumulation */
+  KDA_FP32 = 1  /* float32 I/O and float32 arithmetic throughout */
+} kda_dtype;
+
+/* flags */
+#define KDA_FLAG_L2NORM_QK (1u << 0) /* apply step 2 (the released model does) */
+#define KDA_FLAGS_DEFAULT KDA_FLAG_L2NORM_QK
+
+/* ------------------------------------------------------------------ prefill */
+/* Whole-sequence forward of the mixer for B equal-length sequences.
+ *
+ * The recurrence is evaluated in chunks of `chunk` tokens: per chunk a cumulative
+ * log-decay, the masked intra-chunk key products, a unit-lower-triangular solve
+ * (the WY/UT form of the delta rule), then a serial walk over chunks that carries
+ * the D x D state.  The chunk length changes rounding only, not the result.
+ */
+typedef struct kda_prefill_args {
+  int32_t B, T, H, D;   /* batch, tokens (>= 0), heads, head_dim (keys and values) */
+  int32_t chunk;        /* 16 | 32 | 64 (64 recommended for D = 128) */
+  int32_t conv_k;       /* 4, or 0 = inputs are already convolved + activated */
+  uint32_t flags;       /* KDA_FLAG_* */
+  float l2_eps;         /* >= 0, finite; 1e-6 in the released model */
+  float scale;          /* finite; output scale (1.0 in the released model) */
+  int32_t io;           /* kda_dtype of q, k, v, g, beta, o, conv states */
+  const void* q;        /* device [B][T][H][D] raw queries */
+  const void* k;        /* device [B][T][H][D] raw keys */
+  const void* v;        /* device [B][T][H][D] raw values */
+  const void* g;        /* device [B][T][H][D] log-decay per key channel (finite, <= 0) */
+  const void* beta;     /* device [B][T][H] write strength */
+  const float* conv_w;  /* device [3][H*D][conv_k] float32; NULL iff conv_k == 0 */
+  const void* conv_state_in;  /* device [B][3][conv_k-1][H*D] or NULL (= zeros) */
+  const float* S0;      /* device [B][H][D][D] initial state or NULL (= zeros) */
+  void* o;              /* device [B][T][H][D] output; may not overlap any input */
+  float* S_T;           /* device [B][H][D][D] final state; may equal S0 (in place) */
+  void* conv_state_out; /* device [B][3][conv_k-1][H*D] or NULL; may equal conv_state_in */
+} kda_prefill_args;
+
+/* Host-only check of every argument; returns the first error found. */
+kda_status kda_validate_prefill(const kda_prefill_args* a);
+
+/* Bytes of device workspace kda_prefill needs for these sizes (0 if invalid). */
+size_t kda_prefill_workspace_bytes(const kda_prefill_args* a);
+
+/* Enqueue the whole forward on `stream`.  ws: device workspace of at least
+ * kda_prefill_workspace_bytes(a) bytes, 256-byte aligned, not shared with a call
+ * that may run concurrently.  T == 0 copies S0 (or zeros) to S_T and the conv
+ * state through. */
+kda_status kda_prefill(const kda_prefill_args* a, void* ws, size_t ws_bytes, void* stream);
+
+/* The stages kda_prefill enqueues, one at a time, for profiling:
+ *   0 = chunk preparation (conv + SiLU + L2, cumulative decay, intra-chunk
+ *       products, triangular solve; writes the workspace),
+ *   1 = state walk over chunks with the output (reads the workspace; writes o, S_T),
+ *   2 = conv-state hand-over (writes conv_state_out).
+ * Running 0, 1, 2 in order on one stream is exactly kda_prefill (T > 0). */
+#define KDA_STAGE_PREP 0
+#define KDA_STAGE_STATE 1
+#define KDA_STAGE_CONV_TAIL 2
+kda_status kda_prefill_stage(const kda_prefill_args* a, void* ws, size_t ws_bytes, int stage,
+                             void* stream);
+
+/* ---------------------------------------------------------------- conv_norm */
+/* Step 1 and 2 alone: writes the convolved, activated (and for q, k normalised)
+ * inputs, as the recurrence consumes them.  Same layouts and rules as prefill. */
+typedef struct kda_conv_norm_args {
+  int32_t B, T, H, D;
+  int32_t conv_k;       /* 4 (0 is rejected: nothing to do) */
+  uint32_t flags;
+  float l2_eps;
+  int32_t io;
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* conv_w;        /* device [3][H*D][conv_k] */
+  const void* conv_state_in;  /* device or NULL */
+  void* q_out;                /* device [B][T][H][D] */
+  void* k_out;
+  void* v_out;
+  void* conv_state_out;       /* device or NULL; may equal conv_state_in */
+} kda_conv_norm_args;
+
+kda_status kda_validate_conv_norm(const kda_conv_norm_args* a);
+kda_status kda_conv_norm(const kda_conv_norm_args* a, void* stream);
+
+/* ------------------------------------------------------------------- decode */
+/* One autoregressive step for B sequences (T = 1): conv ring shift, SiLU, L2,
+ * then the state update and output, the state read and written once, in place.
+ * This is the cached-state decode that MaxText's KDA lacks ("MaxText PR 5550",
+ * Known limitations). */
+typedef struct kda_decode_args {
+  int32_t B, H, D;
+  int32_t conv_k;       /* 4 or 0 */
+  uint32_t flags;
+  float l2_eps;
+  float scale;
+  int32_t io;
+  const void* q;        /* device [B][H][D] raw */
+  const void* k;
+  const void* v;
+  const void* g;        /* device [B][H][D] log-decay (finite, <= 0) */
+  const void* beta;     /* device [B][H] */
+  const float* conv_w;  /* device [3][H*D][conv_k]; NULL iff conv_k == 0 */
+  void* conv_state;     /* device [B][3][conv_k-1][H*D] in/out; required iff conv_k > 0 */
+  float* S;             /* device [B][H][D][D] in/out, updated in place */
+  void* o;              /* device [B][H][D]; may not overlap any input */
+} kda_decode_args;
+
+kda_status kda_validate_decode(const kda_decode_args* a);
+kda_status kda_decode_step(const kda_decode_args* a, void* stream);
+
+/* ------------------------------------------------------------------- misc */
+const char* kda_status_str(int status);
+int kda_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDA_H_ */

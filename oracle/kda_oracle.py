@@ -121,10 +121,10 @@ def gated_delta_step(S, q, k, v, g, beta, scale=1.0):
     """
     alpha = np.exp(g)
     S_bar = alpha[..., :, None] * S
-    r = np.einsum("...cv,...c->...v", S_bar, k)
+    r = np.matmul(k[..., None, :], S_bar)[..., 0, :]          # S_bar^T k
     u = beta[..., None] * (v - r)
     S_new = S_bar + k[..., :, None] * u[..., None, :]
-    o = scale * np.einsum("...cv,...c->...v", S_new, q)
+    o = scale * np.matmul(q[..., None, :], S_new)[..., 0, :]  # S'^T q
     return S_new, o
 
 

@@ -1,0 +1,238 @@
+"""The C ABI on the CPU: the library loads, exports what include/kda.h declares,
+and every invalid argument is rejected by host-only validation with its own
+status code.  Pointers here are fake, 16-byte aligned addresses: validation must
+never dereference them or call into the HIP runtime."""
+import ctypes
+
+import pytest
+
+import gated_delta_rule_80_amd as kda
+from gated_delta_rule_80_amd import _lib
+
+OK, NULL, SHAPE, DTYPE, ALIGN, ALIAS, UNSUP, WS, HIP, VALUE = range(10)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return kda.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = kda.declared_functions()
+    assert {"kda_prefill", "kda_decode_step", "kda_conv_norm", "kda_prefill_stage",
+            "kda_prefill_workspace_bytes", "kda_validate_prefill", "kda_validate_decode",
+            "kda_validate_conv_norm", "kda_status_str", "kda_abi_version"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.kda_abi_version() == 1
+    for s in range(10):
+        assert kda.kda_status_str(s) and kda.kda_status_str(s) != "unknown status"
+
+
+class Fake:
+    """Disjoint fake device buffers (never dereferenced)."""
+
+    def __init__(self):
+        self.next = 0x7F0000000000
+
+    def __call__(self, nbytes=1 << 32):
+        p = self.next
+        self.next += ((nbytes + 4095) // 4096 + 1) * 4096
+        return p
+
+
+def prefill(**kw):
+    f = Fake()
+    a = _lib.PrefillArgs()
+    a.B, a.T, a.H, a.D, a.chunk, a.conv_k = 2, 100, 4, 128, 64, 4
+    a.flags, a.l2_eps, a.scale, a.io = 1, 1e-6, 1.0, _lib.KDA_BF16
+    for n in ("q", "k", "v", "g", "beta", "conv_w", "conv_state_in", "S0", "o", "S_T",
+              "conv_state_out"):
+        setattr(a, n, f())
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def decode(**kw):
+    f = Fake()
+    a = _lib.DecodeArgs()
+    a.B, a.H, a.D, a.conv_k, a.flags, a.l2_eps, a.scale, a.io = 8, 4, 128, 4, 1, 1e-6, 1.0, 0
+    for n in ("q", "k", "v", "g", "beta", "conv_w", "conv_state", "S", "o"):
+        setattr(a, n, f())
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def conv_norm(**kw):
+    f = Fake()
+    a = _lib.ConvNormArgs()
+    a.B, a.T, a.H, a.D, a.conv_k, a.flags, a.l2_eps, a.io = 2, 50, 4, 64, 4, 1, 1e-6, 0
+    for n in ("q", "k", "v", "conv_w", "conv_state_in", "q_out", "k_out", "v_out",
+              "conv_state_out"):
+        setattr(a, n, f())
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def vp(a):
+    return kda.kda_validate_prefill(a)
+
+
+def test_prefill_valid_and_workspace(lib):
+    a = prefill()
+    assert vp(a) == OK
+    ws = kda.kda_prefill_workspace_bytes(a)
+    # 2 x 4 heads x 2 chunks x one 256-byte-aligned record per chunk
+    assert ws > 0 and ws % 256 == 0 and ws % (2 * 4 * 2) == 0
+    a.io = _lib.KDA_FP32
+    a.chunk = 32
+    assert vp(a) == OK
+    assert kda.kda_prefill_workspace_bytes(prefill(B=0)) == 0
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("io", 7, DTYPE),
+    ("B", 0, SHAPE), ("H", 0, SHAPE), ("T", -1, SHAPE), ("D", 0, SHAPE), ("chunk", 0, SHAPE),
+    ("D", 96, UNSUP), ("D", 256, UNSUP), ("chunk", 48, UNSUP), ("chunk", 128, UNSUP),
+    ("conv_k", 3, UNSUP), ("flags", 2, VALUE), ("l2_eps", -1.0, VALUE),
+    ("l2_eps", float("nan"), VALUE), ("scale", float("inf"), VALUE),
+    ("q", None, NULL), ("k", None, NULL), ("v", None, NULL), ("g", None, NULL),
+    ("beta", None, NULL), ("o", None, NULL), ("S_T", None, NULL), ("conv_w", None, NULL),
+])
+def test_prefill_rejects(lib, field, value, code):
+    assert vp(prefill(**{field: value})) == code
+
+
+def test_prefill_fp32_d128_c64_unsupported(lib):
+    assert vp(prefill(io=_lib.KDA_FP32, D=128, chunk=64)) == UNSUP
+
+
+def test_prefill_conv_k0_rules(lib):
+    assert vp(prefill(conv_k=0)) == NULL  # filters given without a conv
+    assert vp(prefill(conv_k=0, conv_w=None, conv_state_in=None, conv_state_out=None)) == OK
+
+
+def test_prefill_optional_pointers(lib):
+    assert vp(prefill(S0=None)) == OK
+    assert vp(prefill(conv_state_in=None, conv_state_out=None)) == OK
+    # empty sequences need no input pointers, only the state output
+    assert vp(prefill(T=0, q=None, k=None, v=None, g=None, beta=None, o=None)) == OK
+    assert kda.kda_prefill_workspace_bytes(prefill(T=0)) == 0
+
+
+@pytest.mark.parametrize("field", ["q", "k", "v", "g", "beta", "conv_w", "conv_state_in", "S0",
+                                   "o", "S_T", "conv_state_out"])
+def test_prefill_alignment(lib, field):
+    a = prefill()
+    setattr(a, field, getattr(a, field) + 8)
+    assert vp(a) == ALIGN
+
+
+def test_prefill_aliasing(lib):
+    a = prefill()
+    a.o = a.q
+    assert vp(a) == ALIAS
+    a = prefill()
+    a.o = a.S_T
+    assert vp(a) == ALIAS
+    a = prefill()
+    a.S_T = a.S0  # in place is allowed
+    assert vp(a) == OK
+    a = prefill()
+    a.S_T = a.S0 + 256  # partial overlap is not
+    assert vp(a) == ALIAS
+    a = prefill()
+    a.conv_state_out = a.conv_state_in
+    assert vp(a) == OK
+    a = prefill()
+    a.conv_state_out = a.conv_state_in + 1024
+    assert vp(a) == ALIAS
+    a = prefill()
+    a.S_T = a.k + 4096
+    assert vp(a) == ALIAS
+    a = prefill()
+    a.o = a.g + 16  # overlap inside the range
+    assert vp(a) == ALIAS
+
+
+def test_prefill_workspace_errors(lib):
+    a = prefill()
+    need = kda.kda_prefill_workspace_bytes(a)
+    # NULL workspace / too small / misaligned: refused before any launch
+    assert lib.kda_prefill(ctypes.byref(a), None, need, None) == WS
+    assert lib.kda_prefill(ctypes.byref(a), ctypes.c_void_p(0x100000000000), need - 1, None) == WS
+    assert lib.kda_prefill(ctypes.byref(a), ctypes.c_void_p(0x100000000010), need, None) == WS
+    # workspace overlapping an output
+    assert lib.kda_prefill(ctypes.byref(a), ctypes.c_void_p(a.o), need, None) == ALIAS
+    # invalid stage number
+    assert lib.kda_prefill_stage(ctypes.byref(a), ctypes.c_void_p(0x100000000000), need, 3,
+                                 None) == VALUE
+    # invalid args are reported before the workspace
+    b = prefill(io=9)
+    assert lib.kda_prefill(ctypes.byref(b), None, 0, None) == DTYPE
+
+
+def test_prefill_size_overflow(lib):
+    assert vp(prefill(B=1 << 30, T=1 << 30)) == SHAPE
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("io", -1, DTYPE), ("B", 0, SHAPE), ("H", -2, SHAPE), ("D", 48, UNSUP), ("conv_k", 2, UNSUP),
+    ("flags", 4, VALUE), ("l2_eps", float("inf"), VALUE), ("scale", float("nan"), VALUE),
+    ("q", None, NULL), ("S", None, NULL), ("o", None, NULL), ("conv_state", None, NULL),
+    ("conv_w", None, NULL),
+])
+def test_decode_rejects(lib, field, value, code):
+    assert kda.kda_validate_decode(decode(**{field: value})) == code
+
+
+def test_decode_valid_and_alias(lib):
+    assert kda.kda_validate_decode(decode()) == OK
+    assert kda.kda_validate_decode(decode(conv_k=0, conv_w=None, conv_state=None)) == OK
+    a = decode()
+    a.o = a.S + 64
+    assert kda.kda_validate_decode(a) == ALIAS
+    a = decode()
+    a.S = a.q
+    assert kda.kda_validate_decode(a) == ALIAS
+    a = decode()
+    a.conv_state = a.v
+    assert kda.kda_validate_decode(a) == ALIAS
+    a = decode()
+    a.beta += 4
+    assert kda.kda_validate_decode(a) == ALIGN
+
+
+def test_conv_norm_validation(lib):
+    assert kda.kda_validate_conv_norm(conv_norm()) == OK
+    assert kda.kda_validate_conv_norm(conv_norm(conv_k=0)) == UNSUP
+    assert kda.kda_validate_conv_norm(conv_norm(D=24)) == UNSUP
+    assert kda.kda_validate_conv_norm(conv_norm(io=3)) == DTYPE
+    assert kda.kda_validate_conv_norm(conv_norm(q_out=None)) == NULL
+    a = conv_norm()
+    a.k_out = a.q_out
+    assert kda.kda_validate_conv_norm(a) == ALIAS
+    a = conv_norm()
+    a.v_out = a.v
+    assert kda.kda_validate_conv_norm(a) == ALIAS
+    a = conv_norm()
+    a.conv_state_out = a.conv_state_in
+    assert kda.kda_validate_conv_norm(a) == OK
+
+
+def test_errors_before_launch_never_touch_hip(lib):
+    """A rejected call returns its code from the entry point itself (no device)."""
+    a = prefill(D=96)
+    assert lib.kda_prefill(ctypes.byref(a), None, 0, None) == UNSUP
+    d = decode(B=0)
+    assert lib.kda_decode_step(ctypes.byref(d), None) == SHAPE
+    c = conv_norm(conv_k=0)
+    assert lib.kda_conv_norm(ctypes.byref(c), None) == UNSUP
+
+
+def test_binding_raises_without_library(tmp_path):
+    with pytest.raises(RuntimeError, match="missing"):
+        _lib.load(str(tmp_path / "nope.so"))

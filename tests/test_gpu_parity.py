@@ -1,0 +1,261 @@
+"""Parity of the HIP path (called through the C ABI) with the fp64 oracle.
+
+Tolerance (relative L2 over the whole tensor, separately for o and S_T): 2e-2
+for bf16 inputs, 1e-4 for fp32 inputs.  The conv state hand-over is a copy of
+raw inputs and must match exactly."""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_80_amd as kda
+from kda_inputs import WORKLOADS, make_inputs, to_numpy
+from kda_testutil import (TOL, cuda, gpu_prefill, make, oracle_heads, oracle_prefill, rel_l2,
+                          small)
+from oracle import conv_norm_reference, kda_reference_decode_step
+
+pytestmark = pytest.mark.gpu
+
+
+def check_prefill(w, chunk, seed=0, **kw):
+    inp = make(w, seed)
+    o, S, tail = gpu_prefill(inp, chunk, **kw)
+    ro, rS, rtail = oracle_prefill(inp, **{k: v for k, v in kw.items() if k in ("scale",)})
+    tol = TOL[w.io]
+    eo, eS = rel_l2(o, ro), rel_l2(S, rS)
+    print(f"{w.name} chunk={chunk}: rel_l2 o={eo:.2e} S_T={eS:.2e}", flush=True)
+    assert np.isfinite(o).all() and np.isfinite(S).all()
+    assert eo <= tol, eo
+    assert eS <= tol, eS
+    if rtail is not None and tail is not None:
+        np.testing.assert_array_equal(tail, rtail)
+    return inp, o, S
+
+
+def test_tiny_fp32_workload():
+    w = WORKLOADS["tiny-fp32"]
+    check_prefill(w, w.chunk)
+
+
+def test_bf16_multitile_ragged_with_state():
+    w = small(B=2, T=200, H=3, D=128, io="bf16", chunk=64, strong=True, s0=True, conv_state=True)
+    check_prefill(w, 64)
+
+
+@pytest.mark.parametrize("io,D,chunk", [
+    (io, D, C) for io in ("fp32", "bf16") for D in (16, 32, 64, 128) for C in (16, 32, 64)
+    if not (io == "fp32" and D == 128 and C == 64)])
+def test_dims_and_chunks(io, D, chunk):
+    w = small(B=2, T=77, H=2, D=D, io=io, chunk=chunk, s0=True, conv_state=True)
+    check_prefill(w, chunk, seed=D + chunk)
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 15, 16, 17, 63, 64, 65, 129])
+@pytest.mark.parametrize("io,D,chunk", [("bf16", 128, 64), ("fp32", 16, 16), ("fp32", 64, 32)])
+def test_sequence_length_edges(T, io, D, chunk):
+    w = small(B=1, T=T, H=2, D=D, io=io, chunk=chunk, s0=True, conv_state=True)
+    check_prefill(w, chunk, seed=T)
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_chunk_size_invariance_bf16(chunk):
+    w = small(B=1, T=300, H=2, D=128, io="bf16", chunk=chunk, strong=True, s0=True)
+    check_prefill(w, chunk, seed=5)
+
+
+def test_scale_and_no_l2():
+    w = small(B=1, T=70, H=2, D=32, io="fp32", chunk=32, s0=True)
+    inp = make(w, 1)
+    from oracle import kda_reference
+    n = {k: to_numpy(v) for k, v in inp.items()}
+    for scale, l2 in ((0.0883883, True), (1.0, False)):
+        if not l2:
+            # unnormalised keys: keep beta*|k|^2 small so the recurrence stays contractive
+            inp = dict(inp, q=inp["q"] * 0.1, k=inp["k"] * 0.1)
+            n = {k: to_numpy(v) for k, v in inp.items()}
+        o, S, _ = gpu_prefill(inp, 32, scale=scale, l2norm_qk=l2)
+        ro, rS, _ = kda_reference(n["q"], n["k"], n["v"], n["g"], n["beta"], conv_w=n["conv_w"],
+                                  S0=n["S0"], scale=scale, l2norm_qk=l2)
+        assert rel_l2(o, ro) <= 1e-4 and rel_l2(S, rS) <= 1e-4
+
+
+def test_no_conv_mode():
+    w = small(B=2, T=90, H=2, D=64, io="fp32", chunk=32, s0=True)
+    inp = make(w, 2)
+    inp["conv_w"] = None
+    o, S, tail = gpu_prefill(inp, 32)
+    ro, rS, _ = oracle_prefill(inp)
+    assert tail is None
+    assert rel_l2(o, ro) <= 1e-4 and rel_l2(S, rS) <= 1e-4
+
+
+def test_empty_sequence():
+    w = small(B=2, T=0, H=2, D=64, io="bf16", chunk=64, s0=True, conv_state=True)
+    inp = make(w, 3)
+    o, S, tail = gpu_prefill(inp, 64)
+    assert o.shape == (2, 0, 2, 64)
+    np.testing.assert_array_equal(S, inp["S0"].numpy())
+    np.testing.assert_array_equal(tail, inp["conv_state"].float().numpy())
+    # without S0 the final state is zeros
+    inp["S0"] = None
+    _, S2, _ = gpu_prefill(inp, 64)
+    assert (S2 == 0).all()
+
+
+def test_in_place_state_and_conv_state():
+    w = small(B=2, T=150, H=2, D=128, io="bf16", chunk=64, s0=True, conv_state=True)
+    inp = make(w, 4)
+    o_ref, S_ref, tail_ref = gpu_prefill(inp, 64)
+    c = cuda(inp)
+    S = c["S0"].clone()
+    cs = c["conv_state"].clone()
+    o, S_out, cs_out = kda.kda_prefill(c["q"], c["k"], c["v"], c["g"], c["beta"], c["conv_w"], cs,
+                                       S, chunk=64, S_T=S, conv_state_out=cs)
+    torch.cuda.synchronize()
+    assert S_out.data_ptr() == S.data_ptr() and cs_out.data_ptr() == cs.data_ptr()
+    np.testing.assert_array_equal(S.cpu().numpy(), S_ref)
+    np.testing.assert_array_equal(cs.float().cpu().numpy(), tail_ref)
+    np.testing.assert_array_equal(o.float().cpu().numpy(), o_ref)
+
+
+def test_stages_compose_to_prefill():
+    w = small(B=1, T=130, H=3, D=128, io="bf16", chunk=64, s0=True, conv_state=True)
+    inp = cuda(make(w, 5))
+    o1, S1, t1 = kda.kda_prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                 inp["conv_w"], inp["conv_state"], inp["S0"], chunk=64)
+    o2, S2, t2 = torch.empty_like(o1), torch.empty_like(S1), torch.empty_like(t1)
+    a = kda.prefill_args(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["conv_w"],
+                         inp["conv_state"], inp["S0"], o2, S2, t2, chunk=64)
+    ws = torch.empty(kda.kda_prefill_workspace_bytes(a), dtype=torch.uint8, device="cuda")
+    for stage in (0, 1, 2):
+        kda.kda_prefill_stage(a, ws, stage)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(S1, S2) and torch.equal(t1, t2)
+
+
+@pytest.mark.parametrize("t0", [1, 3, 64, 100])
+def test_split_prefill_hands_over_state(t0):
+    w = small(B=2, T=180, H=2, D=128, io="bf16", chunk=64, strong=True, s0=True, conv_state=True)
+    inp = make(w, 6)
+    ro, rS, rtail = oracle_prefill(inp)
+    c = cuda(inp)
+    a, b = slice(0, t0), slice(t0, None)
+    part = lambda x, s: x[:, s].contiguous()
+    o1, S1, t1 = kda.kda_prefill(*(part(c[n], a) for n in ("q", "k", "v", "g", "beta")),
+                                 c["conv_w"], c["conv_state"], c["S0"], chunk=64)
+    o2, S2, t2 = kda.kda_prefill(*(part(c[n], b) for n in ("q", "k", "v", "g", "beta")),
+                                 c["conv_w"], t1, S1, chunk=64)
+    o = torch.cat([o1, o2], 1).float().cpu().numpy()
+    assert rel_l2(o, ro) <= 2e-2
+    assert rel_l2(S2.cpu().numpy(), rS) <= 2e-2
+    np.testing.assert_array_equal(t2.float().cpu().numpy(), rtail)
+
+
+def test_prefill_equals_decode_steps():
+    w = small(B=2, T=40, H=3, D=64, io="fp32", chunk=16, s0=True, conv_state=True)
+    inp = make(w, 7)
+    o_ref, S_ref, tail_ref = gpu_prefill(inp, 16)
+    c = cuda(inp)
+    S = c["S0"].clone()
+    cs = c["conv_state"].clone()
+    outs = []
+    for t in range(w.T):
+        outs.append(kda.kda_decode_step(c["q"][:, t].contiguous(), c["k"][:, t].contiguous(),
+                                        c["v"][:, t].contiguous(), c["g"][:, t].contiguous(),
+                                        c["beta"][:, t].contiguous(), S, c["conv_w"], cs))
+    torch.cuda.synchronize()
+    o = torch.stack(outs, 1).cpu().numpy()
+    assert rel_l2(o, o_ref) <= 1e-4
+    assert rel_l2(S.cpu().numpy(), S_ref) <= 1e-4
+    np.testing.assert_array_equal(cs.cpu().numpy(), tail_ref)
+
+
+@pytest.mark.parametrize("io,D", [("fp32", 16), ("fp32", 32), ("fp32", 64), ("fp32", 128),
+                                  ("bf16", 16), ("bf16", 64), ("bf16", 128)])
+def test_decode_vs_oracle(io, D):
+    w = WORKLOADS["decode-b256"].scaled(B=5, H=3, D=D, io=io)
+    inp = make_inputs(w, seed=D)
+    n = {k: to_numpy(v) for k, v in inp.items()}
+    ro, rS, rcs = kda_reference_decode_step(n["q"], n["k"], n["v"], n["g"], n["beta"], n["S0"],
+                                            conv_w=n["conv_w"], conv_state=n["conv_state"])
+    c = cuda(inp)
+    S = c["S0"].clone()
+    cs = c["conv_state"].clone()
+    o = kda.kda_decode_step(c["q"], c["k"], c["v"], c["g"], c["beta"], S, c["conv_w"], cs)
+    torch.cuda.synchronize()
+    tol = TOL[io]
+    assert rel_l2(o.float().cpu().numpy(), ro) <= tol
+    assert rel_l2(S.cpu().numpy(), rS) <= tol
+    np.testing.assert_array_equal(cs.float().cpu().numpy(), rcs)
+
+
+def test_decode_without_conv():
+    w = WORKLOADS["decode-b256"].scaled(B=4, H=2, D=32, io="fp32", conv_state_std=0.0)
+    inp = make_inputs(w, seed=11)
+    n = {k: to_numpy(v) for k, v in inp.items()}
+    ro, rS, _ = kda_reference_decode_step(n["q"], n["k"], n["v"], n["g"], n["beta"], n["S0"])
+    c = cuda(inp)
+    S = c["S0"].clone()
+    o = kda.kda_decode_step(c["q"], c["k"], c["v"], c["g"], c["beta"], S)
+    torch.cuda.synchronize()
+    assert rel_l2(o.cpu().numpy(), ro) <= 1e-4 and rel_l2(S.cpu().numpy(), rS) <= 1e-4
+
+
+@pytest.mark.parametrize("io,D", [("fp32", 16), ("bf16", 128), ("fp32", 64)])
+def test_conv_norm_vs_oracle(io, D):
+    w = small(B=2, T=133, H=3, D=D, io=io, conv_state=True)
+    inp = make(w, 12)
+    c = cuda(inp)
+    qh, kh, vh, tail = kda.kda_conv_norm(c["q"], c["k"], c["v"], c["conv_w"], c["conv_state"])
+    torch.cuda.synchronize()
+    rq, rk, rv, rtail = conv_norm_reference(to_numpy(inp["q"]), to_numpy(inp["k"]),
+                                            to_numpy(inp["v"]), to_numpy(inp["conv_w"]),
+                                            to_numpy(inp["conv_state"]))
+    tol = 1e-5 if io == "fp32" else 8e-3  # bf16 output rounding only
+    for x, r in ((qh, rq), (kh, rk), (vh, rv)):
+        assert rel_l2(x.float().cpu().numpy(), r) <= tol
+    np.testing.assert_array_equal(tail.float().cpu().numpy(), rtail)
+
+
+def test_alpha0_reset_and_beta0_identity():
+    w = small(B=1, T=96, H=2, D=128, io="bf16", chunk=64, s0=True)
+    inp = make(w, 13)
+    inp["g"] = torch.full_like(inp["g"], -1000.0)
+    o, S, _ = gpu_prefill(inp, 64)
+    ro, rS, _ = oracle_prefill(inp)
+    assert np.isfinite(o).all() and rel_l2(o, ro) <= 2e-2 and rel_l2(S, rS) <= 2e-2
+    inp = make(w, 14)
+    inp["g"] = torch.zeros_like(inp["g"])
+    inp["beta"] = torch.zeros_like(inp["beta"])
+    o, S, _ = gpu_prefill(inp, 64)
+    ro, rS, _ = oracle_prefill(inp)
+    np.testing.assert_allclose(S, inp["S0"].numpy(), rtol=0, atol=0)  # nothing written, no decay
+    assert rel_l2(o, ro) <= 2e-2
+
+
+def test_head_and_batch_permutation_equivariance():
+    w = small(B=3, T=100, H=4, D=64, io="bf16", chunk=32, s0=True, conv_state=True)
+    inp = make(w, 15)
+    o, S, tail = gpu_prefill(inp, 32)
+    hp = torch.tensor([2, 0, 3, 1])
+    bp = torch.tensor([1, 2, 0])
+    D = w.D
+    chan = (hp[:, None] * D + torch.arange(D)[None, :]).reshape(-1)
+    perm = dict(inp)
+    for n in ("q", "k", "v", "g"):
+        perm[n] = inp[n][bp][:, :, hp].contiguous()
+    perm["beta"] = inp["beta"][bp][:, :, hp].contiguous()
+    perm["conv_w"] = inp["conv_w"][:, chan].contiguous()
+    perm["conv_state"] = inp["conv_state"][bp][..., chan].contiguous()
+    perm["S0"] = inp["S0"][bp][:, hp].contiguous()
+    o2, S2, tail2 = gpu_prefill(perm, 32)
+    np.testing.assert_array_equal(o2, o[bp.numpy()][:, :, hp.numpy()])
+    np.testing.assert_array_equal(S2, S[bp.numpy()][:, hp.numpy()])
+
+
+def test_strong_decay_finite():
+    w = WORKLOADS["prefill-b4-8k-s0"].scaled(B=1, T=1024, H=8)
+    inp = make(w, 16)
+    o, S, _ = gpu_prefill(inp, 64)
+    assert np.isfinite(o).all() and np.isfinite(S).all()
+    for (b, h), (ro, rS) in zip([(0, 0), (0, 5)], oracle_heads(inp, [(0, 0), (0, 5)])):
+        assert rel_l2(o[b, :, h], ro) <= 2e-2 and rel_l2(S[b, h], rS) <= 2e-2
