@@ -29,6 +29,7 @@ if ROOT not in sys.path:
 HBM_PEAK = 8.0e12          # B/s
 BF16_PEAK = 2.5e15         # flop/s, dense
 KERNEL_SOURCES = ["gated_delta_rule_80_amd/csrc/kda_prep.hip",
+                  "gated_delta_rule_80_amd/csrc/kda_prep_exact.hip",
                   "gated_delta_rule_80_amd/csrc/kda_state.hip",
                   "gated_delta_rule_80_amd/csrc/kda_decode.hip",
                   "gated_delta_rule_80_amd/csrc/kda_convnorm.h",
@@ -164,6 +165,9 @@ def main(argv=None) -> int:
     ap.add_argument("--decode-workload", default="decode-b256")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing (0 = skip)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run the library's plain state-copy kernel (kda_prefill with T=0) "
+                         "on this many MiB, to calibrate HBM byte counters")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print("bench.py measures one GPU: the KDA mixer shards over (sequence, head) with no "
@@ -212,7 +216,7 @@ def main(argv=None) -> int:
     tokens_per_s = w.B * w.T / (ms / 1e3)
 
     nb = prefill_bytes(w)
-    names = ["kda_chunk_prep", "kda_chunk_state", "kda_conv_tail"]
+    names = ["kda_chunk_prep_kernel", "kda_chunk_state_kernel", "kda_conv_tail_kernel"]
     dom = 0 if stage_ms[0] >= stage_ms[1] else 1
     dom_bytes = nb["prep"] if dom == 0 else nb["state"]
     achieved = dom_bytes / (stage_ms[dom] / 1e3)
@@ -257,6 +261,22 @@ def main(argv=None) -> int:
                            "algorithmic_bytes": dbytes}}
     del dinp, S, cs, od
     torch.cuda.empty_cache()
+
+    if args.calib_copy_mib > 0:
+        # kda_prefill with T = 0 copies S0 to S_T with one plain copy kernel
+        # (kda_copy_state_kernel): exactly n bytes read and n bytes written.
+        nb_state = 128 * 128 * 4
+        nbh = max(1, args.calib_copy_mib * (1 << 20) // nb_state)
+        src = torch.randn(nbh, 1, 128, 128, device=dev)
+        dst = torch.empty_like(src)
+        z = torch.empty(nbh, 0, 1, 128, dtype=torch.bfloat16, device=dev)
+        ca = kda.prefill_args(z, z, z, z, z[..., 0], None, None, src, None, dst, None, chunk=64)
+        for _ in range(3):
+            kda.kda_prefill_raw(ca, None, stream)
+        torch.cuda.synchronize()
+        print(f"calibration copy: {nbh * nb_state} bytes read and written per launch",
+              file=sys.stderr, flush=True)
+        del src, dst
 
     cpu = None
     if args.cpu_budget > 0:

@@ -22,7 +22,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkda.so")
 
-SOURCES = ["kda_api.cpp", "kda_prep.hip", "kda_state.hip", "kda_decode.hip"]
+SOURCES = ["kda_api.cpp", "kda_prep.hip", "kda_prep_exact.hip", "kda_state.hip",
+           "kda_decode.hip"]
 ARCH = "gfx950"
 
 

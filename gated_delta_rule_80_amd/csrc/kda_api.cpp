@@ -76,7 +76,10 @@ kda_status prefill_sizes(const kda_prefill_args* a, PrefillSizes& s) {
   return KDA_OK;
 }
 
-size_t record_bytes(int io, int D, int C) { return record_layout(C, D, esize(io)).bytes; }
+kda::WorkspaceLayout ws_layout(const kda_prefill_args* a) {
+  const size_t NT = (size_t)((a->T + a->chunk - 1) / a->chunk);
+  return kda::workspace_layout((size_t)a->B * a->H * NT, a->chunk, a->D, esize(a->io));
+}
 
 // Choice of the value-column block of the state walk: narrower blocks give more
 // parallel walks when B * H is small.
@@ -145,11 +148,12 @@ kda_status kda_validate_prefill(const kda_prefill_args* a) {
 
 size_t kda_prefill_workspace_bytes(const kda_prefill_args* a) {
   if (kda_validate_prefill(a) != KDA_OK) return 0;
+  if (a->T == 0) return 0;
   const int NT = (a->T + a->chunk - 1) / a->chunk;
   size_t n;
-  if (!mul_ok(n, {(size_t)a->B, (size_t)a->H, (size_t)NT, record_bytes(a->io, a->D, a->chunk)}))
-    return 0;
-  return n;
+  const size_t rec = record_layout(a->chunk, a->D, esize(a->io)).bytes;
+  if (!mul_ok(n, {(size_t)a->B, (size_t)a->H, (size_t)NT, rec})) return 0;
+  return ws_layout(a).bytes;
 }
 
 static kda_status check_workspace(const kda_prefill_args* a, void* ws, size_t ws_bytes) {
@@ -178,7 +182,10 @@ static kda_status run_stage(const kda_prefill_args* a, void* ws, int stage, hipS
       p.q = a->q; p.k = a->k; p.v = a->v; p.g = a->g; p.beta = a->beta;
       p.conv_w = a->conv_k > 0 ? a->conv_w : nullptr;
       p.conv_state_in = a->conv_k > 0 ? a->conv_state_in : nullptr;
-      p.ws = static_cast<char*>(ws);
+      const kda::WorkspaceLayout wl = ws_layout(a);
+      p.ws = static_cast<char*>(ws) + wl.records;
+      p.fb_count = static_cast<unsigned*>(ws);
+      p.fb_list = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + wl.list);
       p.B = a->B; p.T = a->T; p.H = a->H; p.NT = NT;
       p.conv_k = a->conv_k;
       p.l2 = (a->flags & KDA_FLAG_L2NORM_QK) ? 1 : 0;
@@ -193,7 +200,7 @@ static kda_status run_stage(const kda_prefill_args* a, void* ws, int stage, hipS
         return hip_status(kda::launch_copy_state(a->S0, a->S_T, n, st));
       }
       kda::StateParams p{};
-      p.ws = static_cast<const char*>(ws);
+      p.ws = static_cast<const char*>(ws) + ws_layout(a).records;
       p.S0 = a->S0; p.S_T = a->S_T; p.o = a->o;
       p.B = a->B; p.T = a->T; p.H = a->H; p.NT = NT;
       return hip_status(

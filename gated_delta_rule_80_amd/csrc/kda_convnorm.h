@@ -1,5 +1,5 @@
 // Short causal convolution + SiLU + per-head L2 norm for one thread's tile of
-// 4 consecutive tokens x 8 consecutive channels of one head.
+// TOK consecutive tokens x 8 consecutive channels of one head.
 //
 // The filters are stored per channel as [H*D][K] float32, the [C, 1, K] layout of
 // the released q/k/v_conv1d weights ("MaxText PR 5548", review item 2), and
@@ -12,15 +12,22 @@
 
 namespace kda {
 
-// Raw inputs of tensor `x` (one of q, k, v) for tokens t in [t_first - 3, t_first + 3],
+constexpr float kLog2e = 1.4426950408889634f;
+
+// SiLU(x) = x * sigmoid(x) with the hardware exp2 and reciprocal (about 1 ulp each).
+__device__ __forceinline__ float silu_fast(float x) {
+  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-kLog2e * x));
+}
+
+// Raw inputs of tensor `x` (one of q, k, v) for tokens t in [t_first - 3, t_first + TOK),
 // channels [ch, ch + 8).  Tokens < 0 read the carried state, tokens >= T read 0.
-template <typename IO>
+template <int TOK, typename IO>
 __device__ __forceinline__ void load_window(const IO* x, const IO* state, int tensor, int b,
                                             int T, int H, int D, int h, int ch, int t_first,
-                                            float (&win)[7][8]) {
+                                            float (&win)[TOK + 3][8]) {
   const size_t HD = (size_t)H * D;
 #pragma unroll
-  for (int m = 0; m < 7; ++m) {
+  for (int m = 0; m < TOK + 3; ++m) {
     const int t = t_first - 3 + m;
     if (t >= 0 && t < T) {
       load8(x + ((size_t)b * T + t) * HD + (size_t)h * D + ch, win[m]);
@@ -34,24 +41,23 @@ __device__ __forceinline__ void load_window(const IO* x, const IO* state, int te
   }
 }
 
-// Computes conv + SiLU for 4 tokens x 8 channels of one tensor.  With conv_w ==
-// NULL (conv_k == 0) the raw inputs are passed through.  Outputs of tokens >= T
-// are zero.
-template <typename IO>
+// conv + SiLU for TOK tokens x 8 channels of one tensor.  With conv_w == NULL
+// (conv_k == 0) the raw inputs are passed through.  Outputs of tokens >= T are 0.
+template <int TOK, typename IO>
 __device__ __forceinline__ void conv_silu_tile(const IO* x, const IO* state, const float* conv_w,
                                                int tensor, int b, int T, int H, int D, int h,
                                                int ch, int t_first, bool active,
-                                               float (&y)[4][8]) {
+                                               float (&y)[TOK][8]) {
   if (!active) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < TOK; ++m)
 #pragma unroll
       for (int c = 0; c < 8; ++c) y[m][c] = 0.f;
     return;
   }
   if (conv_w == nullptr) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
+    for (int m = 0; m < TOK; ++m) {
       const int t = t_first + m;
       if (t < T) {
         load8(x + ((size_t)b * T + t) * ((size_t)H * D) + (size_t)h * D + ch, y[m]);
@@ -62,21 +68,21 @@ __device__ __forceinline__ void conv_silu_tile(const IO* x, const IO* state, con
     }
     return;
   }
-  float win[7][8];
-  load_window<IO>(x, state, tensor, b, T, H, D, h, ch, t_first, win);
+  float win[TOK + 3][8];
+  load_window<TOK, IO>(x, state, tensor, b, T, H, D, h, ch, t_first, win);
   const size_t HD = (size_t)H * D;
   const float* wt = conv_w + ((size_t)tensor * HD + (size_t)h * D + ch) * 4;
 #pragma unroll
   for (int c = 0; c < 8; ++c) {
     const f32x4 w = *reinterpret_cast<const f32x4*>(wt + 4 * c);
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
+    for (int m = 0; m < TOK; ++m) {
       // output token t_first + m uses window rows m .. m + 3 (inputs t - 3 .. t)
       float acc = w[0] * win[m][c];
       acc = fmaf(w[1], win[m + 1][c], acc);
       acc = fmaf(w[2], win[m + 2][c], acc);
       acc = fmaf(w[3], win[m + 3][c], acc);
-      y[m][c] = (t_first + m < T) ? silu(acc) : 0.f;
+      y[m][c] = (t_first + m < T) ? silu_fast(acc) : 0.f;
     }
   }
 }
@@ -85,19 +91,19 @@ __device__ __forceinline__ void conv_silu_tile(const IO* x, const IO* state, con
 // lanes (the channels of one token row) must call this together: the L2 sums are
 // reduced across that group.  On return q is normalised and multiplied by
 // `scale`, k normalised, v convolved; qk[m] = <q_m, k_m> of the returned values.
-template <int D, typename IO>
+template <int TOK, int D, typename IO>
 __device__ __forceinline__ void conv_norm_tile(const IO* q, const IO* k, const IO* v,
                                                const IO* state, const float* conv_w, int b, int T,
                                                int H, int h, int ch, int t_first, bool active,
                                                bool l2, float eps, float scale,
-                                               float (&yq)[4][8], float (&yk)[4][8],
-                                               float (&yv)[4][8], float (&qk)[4]) {
-  conv_silu_tile<IO>(q, state, conv_w, 0, b, T, H, D, h, ch, t_first, active, yq);
-  conv_silu_tile<IO>(k, state, conv_w, 1, b, T, H, D, h, ch, t_first, active, yk);
-  conv_silu_tile<IO>(v, state, conv_w, 2, b, T, H, D, h, ch, t_first, active, yv);
+                                               float (&yq)[TOK][8], float (&yk)[TOK][8],
+                                               float (&yv)[TOK][8], float (&qk)[TOK]) {
+  conv_silu_tile<TOK, IO>(q, state, conv_w, 0, b, T, H, D, h, ch, t_first, active, yq);
+  conv_silu_tile<TOK, IO>(k, state, conv_w, 1, b, T, H, D, h, ch, t_first, active, yk);
+  conv_silu_tile<TOK, IO>(v, state, conv_w, 2, b, T, H, D, h, ch, t_first, active, yv);
   constexpr int G = D / 8;  // lanes sharing one token row
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
+  for (int m = 0; m < TOK; ++m) {
     float sq = 0.f, sk = 0.f;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {

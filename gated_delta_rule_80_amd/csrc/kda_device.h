@@ -13,6 +13,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace kda {
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -65,6 +67,16 @@ __device__ __forceinline__ void store4(float* p, float a, float b, float c, floa
   f32x4 v;
   v[0] = a; v[1] = b; v[2] = c; v[3] = d;
   *reinterpret_cast<f32x4*>(p) = v;
+}
+// 2 consecutive elements (4-byte aligned bf16 / 8-byte aligned fp32)
+__device__ __forceinline__ void store2(__bf16* p, float a, float b) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 v;
+  v[0] = (__bf16)a; v[1] = (__bf16)b;
+  *reinterpret_cast<bf16x2*>(p) = v;
+}
+__device__ __forceinline__ void store2(float* p, float a, float b) {
+  *reinterpret_cast<float2*>(p) = make_float2(a, b);
 }
 __device__ __forceinline__ void load4(const __bf16* p, float* out) {
   bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
@@ -149,6 +161,75 @@ __device__ __forceinline__ void mma_rows_upto(f32x4& acc, const float* A, int ld
       acc = __builtin_amdgcn_mfma_f32_16x16x4f32(A[r * lda + k0 + g], Bt[r * ldb + k0 + g], acc, 0,
                                                  0, 0);
   }
+}
+
+// One lane's share of a 16-row matrix-core operand over a compile-time depth K,
+// read "along k" from row (base + (l % 16) * ld).  The same registers serve as
+// the A operand (rows of A) or the B operand (rows of B^T).
+template <typename E, int K> struct RowFrag;
+
+template <int K> struct RowFrag<__bf16, K> {
+  static constexpr bool X32 = (K % 32) == 0;
+  static constexpr int STEP = X32 ? 32 : 16;
+  static constexpr int PER = X32 ? 8 : 4;  // elements per lane per step
+  static constexpr int N = K / STEP;
+  static_assert(K % 16 == 0, "bf16 operands need K % 16 == 0");
+  using V = typename std::conditional<X32, bf16x8, bf16x4>::type;
+  V v[N];
+  // row: pointer to this lane's row (row 0 of the tile + (lane % 16) * ld)
+  __device__ __forceinline__ void load(const __bf16* row, int g) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = *reinterpret_cast<const V*>(row + i * STEP + PER * g);
+  }
+  // zero every element whose k index exceeds kmax (causal mask)
+  __device__ __forceinline__ void mask_above(int kmax, int g) {
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+#pragma unroll
+      for (int e = 0; e < PER; ++e)
+        if (i * STEP + PER * g + e > kmax) v[i][e] = (__bf16)0.f;
+  }
+};
+
+template <int K> struct RowFrag<float, K> {
+  static constexpr int STEP = 4;
+  static constexpr int N = K / 4;
+  static_assert(K % 4 == 0, "fp32 operands need K % 4 == 0");
+  float v[N];
+  __device__ __forceinline__ void load(const float* row, int g) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = row[4 * i + g];
+  }
+  __device__ __forceinline__ void mask_above(int kmax, int g) {
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if (4 * i + g > kmax) v[i] = 0.f;
+  }
+};
+
+// acc += A * B over the first `steps` k-steps (all by default)
+template <int K>
+__device__ __forceinline__ void mma(f32x4& acc, const RowFrag<__bf16, K>& a,
+                                    const RowFrag<__bf16, K>& b, int steps = RowFrag<__bf16, K>::N) {
+#pragma unroll
+  for (int i = 0; i < RowFrag<__bf16, K>::N; ++i) {
+    if (i < steps) {
+      if constexpr (RowFrag<__bf16, K>::X32) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v[i], b.v[i], acc, 0, 0, 0);
+      } else {
+        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a.v[i]),
+                                                        __builtin_bit_cast(s16x4, b.v[i]), acc,
+                                                        0, 0, 0);
+      }
+    }
+  }
+}
+template <int K>
+__device__ __forceinline__ void mma(f32x4& acc, const RowFrag<float, K>& a,
+                                    const RowFrag<float, K>& b, int steps = RowFrag<float, K>::N) {
+#pragma unroll
+  for (int i = 0; i < RowFrag<float, K>::N; ++i)
+    if (i < steps) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[i], b.v[i], acc, 0, 0, 0);
 }
 
 // Instruction depth along k for an element type (used for causal bounds).

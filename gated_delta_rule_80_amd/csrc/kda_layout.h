@@ -36,6 +36,23 @@ constexpr RecordLayout record_layout(int C, int D, size_t esize) {
   return r;
 }
 
+// Workspace: a 256-byte header whose first word counts the chunks the fast
+// preparation handed to the exact one, the list of those chunk indices, then one
+// record per (sequence, head, chunk).
+struct WorkspaceLayout {
+  size_t list;     // byte offset of the fallback list (uint32 per chunk)
+  size_t records;  // byte offset of the first record
+  size_t bytes;    // total
+};
+
+constexpr WorkspaceLayout workspace_layout(size_t nrec, int C, int D, size_t esize) {
+  WorkspaceLayout w{};
+  w.list = 256;
+  w.records = round_up(w.list + 4 * nrec, 256);
+  w.bytes = w.records + nrec * record_layout(C, D, esize).bytes;
+  return w;
+}
+
 struct PrepParams {
   const void* q;
   const void* k;
@@ -44,7 +61,9 @@ struct PrepParams {
   const void* beta;
   const float* conv_w;        // NULL when conv_k == 0
   const void* conv_state_in;  // may be NULL
-  char* ws;
+  char* ws;                 // first record
+  unsigned* fb_count;       // chunks handed to the exact preparation
+  unsigned* fb_list;        // their record indices
   int B, T, H, NT;
   int conv_k;
   int l2;

@@ -1,6 +1,6 @@
-// Chunk preparation for the KDA prefill: one workgroup per (sequence, head,
-// chunk of C tokens).  Everything here is independent across chunks; the serial
-// dependence on the state is left to the state walk.
+// Chunk preparation for the KDA prefill: one workgroup of 512 threads per
+// (sequence, head, chunk of C tokens).  Everything here is independent across
+// chunks; the serial dependence on the state is left to the state walk.
 //
 // Per chunk (Gamma = chunk-local cumulative sum of the log-decay g, per channel;
 // Lambda = exp(Gamma); all decays act on the key channels):
@@ -10,19 +10,20 @@
 //      P_ij = scale * sum_c q_ic k_jc exp(Gamma_ic - Gamma_jc)  (j <= i)
 //   4. T = (I + A)^-1 (unit lower triangular)
 //   5. W = T diag(beta) (K * Lambda),  U~ = T diag(beta) V
-// The triangular structure is the WY/UT form of a product of generalised
-// Householder factors (I - beta k k^T), which is what the delta rule composes.
+// The triangular structure is the WY/UT form of the product of the generalised
+// Householder factors (I - beta k k^T) that the delta rule composes.
 //
-// Step 3 without overflow: exp(Gamma_i - Gamma_j) with j < i is <= 1, but the
-// split exp(Gamma_i) * exp(-Gamma_j) needed to make it a matrix product overflows
-// fp32 for strong decays.  The pairs (i, j) are therefore grouped by the level of
-// a binary hierarchy over the chunk at which i and j first fall into different
-// halves.  At level l (segments of 2^(l+1) tokens) a pair splits as
-// "j in the upper half, i in the lower half" and is factored about the last
-// token r of the upper half:  exp(Gamma_i - Gamma_r) * exp(Gamma_r - Gamma_j),
-// both factors <= 1.  Levels >= 4 give whole 16x16 tiles; levels 0..3 live inside
-// the diagonal tiles and are masked per element.  Every pair j < i is covered by
-// exactly one level.
+// Step 3 as matrix products over 16-token blocks p (all factors per channel):
+//   a_i = exp(Gamma_i - G_p)   for i in block p, G_p = Gamma just before block p  (<= 1)
+//   b_j = exp(G_{q+1} - Gamma_j) for j in block q, G_{q+1} = Gamma at its last token (<= 1)
+//   blocks p > q:  exp(Gamma_i - Gamma_j) = a_i * exp(G_p - G_{q+1}) * b_j, every factor <= 1,
+//                  so no factor overflows and an underflowed factor means a negligible term;
+//   block p = p:   exp(Gamma_i - Gamma_j) = a_i / a_j = a_i * b_j * exp(G_p - G_{p+1}),
+//                  representable while the block's decay span G_p - G_{p+1} stays below
+//                  ~80 nats; a channel above that uses its block's midpoint as the
+//                  reference instead (both factors within exp(+-span/2)).
+// A chunk with a span too large even for that (> ~166 nats in 16 tokens) is listed
+// in the workspace and recomputed by the exact preparation kernel.
 #include "kda_convnorm.h"
 #include "kda_device.h"
 #include "kda_launch.h"
@@ -30,50 +31,68 @@
 
 namespace kda {
 
-constexpr int kPrepThreads = 256;
-
-__host__ __device__ constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
-
-// Level at which 16-row blocks R > Q of a chunk separate (>= 4).
-__device__ __forceinline__ int tile_level(int R, int Q) { return 4 + 31 - __clz(R ^ Q); }
+constexpr int kFastThreads = 512;
+constexpr float kSafeSpan2 = 112.f;   // log2 units (~78 nats): boundary references
+constexpr float kFatalSpan2 = 240.f;  // log2 units (~166 nats): midpoint references
 
 template <int D, int C, typename E>
-struct PrepSmem {
+struct FastSmem {
   static constexpr int PE = 16 / (int)sizeof(E);  // 16-byte row padding, in elements
-  static constexpr int LQ = D + PE;               // rows of q, k, X, Y
-  static constexpr int LG = D + 4;                // rows of Gamma (floats)
-  static constexpr int LT = C + PE;               // rows of (beta K Lambda)^T, (beta V)^T, T
-  static constexpr int LA = C + 4;                // rows of A and T (floats)
-  static constexpr int NB = C / 16;
-
-  E q[C * LQ];       // normalised, scaled q (later: T in E precision)
-  E k[C * LQ];       // normalised k
-  float gam[C * LG]; // Gamma
-  E klt[D * LT];     // (diag(beta) K Lambda)^T
-  E vt[D * LT];      // (diag(beta) V)^T
-  // region reused by phase: segment totals -> level operands X, Y -> A, T, scratch
-  static constexpr int R1_LEVELS = 2 * C * LQ * (int)sizeof(E);
-  // T in E precision lives in q's space when it fits (C <= D), else after the solve scratch
-  static constexpr bool TB_IN_Q = C <= D;
+  static constexpr int LQ = D + PE;               // operand rows (k = channel)
+  static constexpr int LT = C + PE;               // transposed rows (k = token)
+  static constexpr int LA = C + 4;                // A and T rows (floats)
+  static constexpr int NB = C / 16;               // 16-token blocks
+  static constexpr int NPAIR = (NB - 1) * (NB - 2) / 2 > 0 ? (NB - 1) * (NB - 2) / 2 : 1;
+  // operand arrays, 6 x [C][LQ] in E:
+  //   RA = beta k a, RP = q a (rows i);  CB = k b (rows j, blocks below the diagonal);
+  //   CD = k / a (rows j, diagonal); RAd, RPd (rows i, diagonal; equal RA, RP on
+  //   channels that use the block-start reference).
+  // The same region holds the segment totals first and A, T, scratch, T in E last.
+  static constexpr int OPS = 6 * C * LQ * (int)sizeof(E);
   static constexpr int TB_OFF = (2 * C * LA + 4 * 16 * 17) * 4;
-  static constexpr int R1_SOLVE = TB_OFF + (TB_IN_Q ? 0 : C * LT * (int)sizeof(E));
-  static constexpr int R1_TOT = (C / 4) * D * 4;
-  static constexpr int R1 = R1_LEVELS > R1_SOLVE ? (R1_LEVELS > R1_TOT ? R1_LEVELS : R1_TOT)
-                                                 : (R1_SOLVE > R1_TOT ? R1_SOLVE : R1_TOT);
+  static constexpr int SOLVE = TB_OFF + C * LT * (int)sizeof(E);
+  static constexpr int R1 = OPS > SOLVE ? OPS : SOLVE;
   alignas(16) char r1[R1];
-  float beta[C];
-  float pd[C];  // diagonal of P
+  alignas(16) E klt[D * LT];           // (diag(beta) K Lambda)^T
+  alignas(16) E vt[D * LT];            // (diag(beta) V)^T
+  alignas(16) float gb[(NB + 1) * D];  // log2 decay at block boundaries: gb[p] = Gamma before block p
+  alignas(16) float esp[NB * D];       // exp(G_p - G_{p+1}) for channels on the block-start reference
+  alignas(16) float eb[NB * D];        // exp(G_p)
+  alignas(16) float ec[NB * D];        // exp(Gamma_C - G_{p+1})
+  alignas(16) float mpq[NPAIR * D];    // exp(G_p - G_{q+1}) for block pairs p - q >= 2
+  int fatal;
 };
 
+__device__ __forceinline__ int pair_index(int R, int Q) {
+  // pairs (R, Q) with R - Q >= 2 in the order (2,0), (3,0), (3,1), (4,0), ...
+  return (R - 2) * (R - 1) / 2 + Q;
+}
+
+// Multiply the operand fragment element-wise by a per-k factor f[k] (k = channel).
+template <int K>
+__device__ __forceinline__ void scale_k(RowFrag<__bf16, K>& fr, const float* f, int g) {
+  using FR = RowFrag<__bf16, K>;
+#pragma unroll
+  for (int i = 0; i < FR::N; ++i)
+#pragma unroll
+    for (int e = 0; e < FR::PER; ++e)
+      fr.v[i][e] = (__bf16)((float)fr.v[i][e] * f[i * FR::STEP + FR::PER * g + e]);
+}
+template <int K>
+__device__ __forceinline__ void scale_k(RowFrag<float, K>& fr, const float* f, int g) {
+#pragma unroll
+  for (int i = 0; i < RowFrag<float, K>::N; ++i) fr.v[i] *= f[4 * i + g];
+}
+
 template <int D, int C, typename IO, typename E>
-__global__ __launch_bounds__(kPrepThreads) void kda_chunk_prep_kernel(PrepParams p) {
-  using SM = PrepSmem<D, C, E>;
+__global__ __launch_bounds__(kFastThreads) void kda_chunk_prep_kernel(PrepParams p) {
+  using SM = FastSmem<D, C, E>;
   __shared__ SM sm;
-  constexpr int LQ = SM::LQ, LG = SM::LG, LT = SM::LT, LA = SM::LA, NB = SM::NB;
-  constexpr int NOCT = D / 8;         // 8-channel groups per token row
-  constexpr int NSEG = C / 4;         // 4-token segments
-  constexpr int ITEMS = NSEG * NOCT;  // <= 256
-  static_assert(ITEMS <= kPrepThreads, "tile does not fit one pass");
+  constexpr int LQ = SM::LQ, LT = SM::LT, LA = SM::LA, NB = SM::NB;
+  constexpr int NOCT = D / 8;          // 8-channel groups per token row
+  constexpr int NSEG = C / 2;          // 2-token segments
+  constexpr int ITEMS = NSEG * NOCT;   // <= 512
+  static_assert(ITEMS <= kFastThreads, "tile does not fit one pass");
   constexpr RecordLayout RL = record_layout(C, D, sizeof(E));
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -90,190 +109,207 @@ __global__ __launch_bounds__(kPrepThreads) void kda_chunk_prep_kernel(PrepParams
   E* gU = reinterpret_cast<E*>(recp) + RL.u;
   E* gP = reinterpret_cast<E*>(recp) + RL.p;
   float* gLC = reinterpret_cast<float*>(recp + RL.lc_bytes);
-
-  const IO* q = static_cast<const IO*>(p.q);
-  const IO* k = static_cast<const IO*>(p.k);
-  const IO* v = static_cast<const IO*>(p.v);
-  const IO* gg = static_cast<const IO*>(p.g);
-  const IO* bb = static_cast<const IO*>(p.beta);
-  const IO* cs = static_cast<const IO*>(p.conv_state_in);
+  E* RA = reinterpret_cast<E*>(sm.r1);
+  E* RP = RA + C * LQ;
+  E* CB = RP + C * LQ;
+  E* CD = CB + C * LQ;
+  E* RAd = CD + C * LQ;
+  E* RPd = RAd + C * LQ;
 
   // ---------------------------------------------------------------- phase 1
   const bool active = tid < ITEMS;
-  const int s = active ? tid / NOCT : 0;
+  const int s = active ? tid / NOCT : 0;  // 2-token segment
   const int j = tid % NOCT;
   const int ch = 8 * j;
-  const int tf = t0 + 4 * s;  // first token of this thread's segment
-  float yq[4][8], yk[4][8], yv[4][8], qk[4];
-  conv_norm_tile<D, IO>(q, k, v, cs, p.conv_w, b, p.T, p.H, h, ch, tf, active, p.l2 != 0, p.eps,
-                        p.scale, yq, yk, yv, qk);
-  float gl[4][8], bt[4];
+  const int pb = s / 8;                   // 16-token block of this segment
+  const int tf = t0 + 2 * s;
+  float yq[2][8], yk[2][8], yv[2][8], qk[2];
+  conv_norm_tile<2, D, IO>(static_cast<const IO*>(p.q), static_cast<const IO*>(p.k),
+                           static_cast<const IO*>(p.v), static_cast<const IO*>(p.conv_state_in),
+                           p.conv_w, b, p.T, p.H, h, ch, tf, active, p.l2 != 0, p.eps, p.scale,
+                           yq, yk, yv, qk);
+  float g2[2][8], bt[2];
   const size_t HD = (size_t)p.H * D;
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
+  for (int m = 0; m < 2; ++m) {
     const int t = tf + m;
     if (active && t < p.T) {
-      load8(gg + ((size_t)b * p.T + t) * HD + (size_t)h * D + ch, gl[m]);
-      bt[m] = to_f32(bb[((size_t)b * p.T + t) * p.H + h]);
+      load8(static_cast<const IO*>(p.g) + ((size_t)b * p.T + t) * HD + (size_t)h * D + ch, g2[m]);
+      bt[m] = to_f32(static_cast<const IO*>(p.beta)[((size_t)b * p.T + t) * p.H + h]);
     } else {
 #pragma unroll
-      for (int c = 0; c < 8; ++c) gl[m][c] = 0.f;
+      for (int c = 0; c < 8; ++c) g2[m][c] = 0.f;
       bt[m] = 0.f;
     }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) g2[m][c] *= kLog2e;  // decay in log2 units from here on
   }
-  // cumulative log-decay: within the segment, then across segments
 #pragma unroll
-  for (int m = 1; m < 4; ++m)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) gl[m][c] += gl[m - 1][c];
-  float* tot = reinterpret_cast<float*>(sm.r1);  // [NSEG][D]
-  if (active) store8(tot + s * D + ch, gl[3]);
+  for (int c = 0; c < 8; ++c) g2[1][c] += g2[0][c];
+  float* tot = reinterpret_cast<float*>(RAd);  // [NSEG][D] segment totals, later exclusive prefixes
+  static_assert(NSEG * D * 4 <= 2 * C * LQ * (int)sizeof(E), "segment totals fit RAd/RPd");
+  if (tid == 0) sm.fatal = 0;
+  if (active) store8(tot + s * D + ch, g2[1]);
   __syncthreads();
-  float pre[8], gC[8];
-#pragma unroll
-  for (int c = 0; c < 8; ++c) pre[c] = gC[c] = 0.f;
-  if (active) {
+  // one thread per channel: exclusive scan over segments and the per-block factors
+  if (tid < D) {
+    const int c = tid;
+    float acc = 0.f;
+    sm.gb[c] = 0.f;
     for (int s2 = 0; s2 < NSEG; ++s2) {
-      float t8[8];
-      load8(tot + s2 * D + ch, t8);
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        if (s2 < s) pre[c] += t8[c];
-        gC[c] += t8[c];
-      }
+      const float v = tot[s2 * D + c];
+      tot[s2 * D + c] = acc;
+      acc += v;
+      if ((s2 & 7) == 7) sm.gb[((s2 + 1) >> 3) * D + c] = acc;
     }
+    gLC[c] = __builtin_amdgcn_exp2f(acc);
+    bool fatal = false;
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      const float g0 = sm.gb[q * D + c], g1 = sm.gb[(q + 1) * D + c];
+      const float span = g0 - g1;
+      sm.esp[q * D + c] = span <= kSafeSpan2 ? __builtin_amdgcn_exp2f(span) : 0.f;
+      sm.eb[q * D + c] = __builtin_amdgcn_exp2f(g0);
+      sm.ec[q * D + c] = __builtin_amdgcn_exp2f(acc - g1);
+      fatal |= span > kFatalSpan2;
+    }
+#pragma unroll
+    for (int R = 2; R < NB; ++R)
+#pragma unroll
+      for (int Q = 0; Q + 2 <= R; ++Q)
+        sm.mpq[pair_index(R, Q) * D + c] =
+            __builtin_amdgcn_exp2f(sm.gb[R * D + c] - sm.gb[(Q + 1) * D + c]);
+    if (fatal) atomicOr(&sm.fatal, 1);
   }
-#pragma unroll
-  for (int m = 0; m < 4; ++m)
-#pragma unroll
-    for (int c = 0; c < 8; ++c) gl[m][c] += pre[c];
+  __syncthreads();
+  if (sm.fatal) {
+    // decays too strong for the factoring: the exact preparation redoes this chunk
+    if (tid == 0) {
+      const unsigned slot = atomicAdd(p.fb_count, 1u);
+      p.fb_list[slot] = (unsigned)rec;
+    }
+    return;
+  }
+  float rad[2][8], rpd[2][8];
   if (active) {
-    float lamC[8], ktl[4][8];
+    float pre[8], gp[8], gq[8], esp[8], eb[8], ec[8];
+    load8(tot + s * D + ch, pre);
+    load8(&sm.gb[pb * D + ch], gp);
+    load8(&sm.gb[(pb + 1) * D + ch], gq);
+    load8(&sm.esp[pb * D + ch], esp);
+    load8(&sm.eb[pb * D + ch], eb);
+    load8(&sm.ec[pb * D + ch], ec);
+    bool any_wide = false;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) lamC[c] = __expf(gC[c]);
+    for (int c = 0; c < 8; ++c) any_wide |= (gp[c] - gq[c]) > kSafeSpan2;
+    float kt[2][8];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int tl = 4 * s + m;
-      float lam[8], ql[8];
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        lam[c] = __expf(gl[m][c]);
-        ql[c] = yq[m][c] * lam[c];
-        ktl[m][c] = yk[m][c] * __expf(gC[c] - gl[m][c]);
-      }
-      store8(&sm.q[tl * LQ + ch], yq[m]);
-      store8(&sm.k[tl * LQ + ch], yk[m]);
-      store8(&sm.gam[tl * LG + ch], gl[m]);
-      store8(gQL + (size_t)tl * D + ch, ql);
+    for (int m = 0; m < 2; ++m) {
+      const int tl = 2 * s + m;
+      float ra[8], rp[8], cb[8], cd[8], ql[8];
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        sm.klt[(ch + c) * LT + tl] = from_f32<E>(bt[m] * yk[m][c] * lam[c]);
+        const float gam = g2[m][c] + pre[c];
+        const float a = __builtin_amdgcn_exp2f(gam - gp[c]);
+        const float bb = __builtin_amdgcn_exp2f(gq[c] - gam);
+        const float bk = bt[m] * yk[m][c];
+        ra[c] = bk * a;
+        rp[c] = yq[m][c] * a;
+        cb[c] = yk[m][c] * bb;
+        cd[c] = cb[c] * esp[c];
+        ql[c] = rp[c] * eb[c];
+        kt[m][c] = cb[c] * ec[c];
+        rad[m][c] = ra[c];
+        rpd[m][c] = rp[c];
+        sm.klt[(ch + c) * LT + tl] = from_f32<E>(ra[c] * eb[c]);
         sm.vt[(ch + c) * LT + tl] = from_f32<E>(bt[m] * yv[m][c]);
       }
-      if (j == 0) {
-        sm.beta[tl] = bt[m];
-        sm.pd[tl] = qk[m];
+      if (any_wide) {
+        // channels whose block span is too wide for exp(+span): midpoint reference
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          if (gp[c] - gq[c] > kSafeSpan2) {
+            const float gam = g2[m][c] + pre[c];
+            const float mid = 0.5f * (gp[c] + gq[c]);
+            const float ad = __builtin_amdgcn_exp2f(gam - mid);
+            rad[m][c] = bt[m] * yk[m][c] * ad;
+            rpd[m][c] = yq[m][c] * ad;
+            cd[c] = yk[m][c] * __builtin_amdgcn_exp2f(mid - gam);
+          }
+        }
       }
+      store8(RA + tl * LQ + ch, ra);
+      store8(RP + tl * LQ + ch, rp);
+      store8(CB + tl * LQ + ch, cb);
+      store8(CD + tl * LQ + ch, cd);
+      store8(gQL + (size_t)tl * D + ch, ql);
     }
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
-      store4(gKT + (size_t)(ch + c) * C + 4 * s, ktl[0][c], ktl[1][c], ktl[2][c], ktl[3][c]);
-    if (s == 0) {
-      *reinterpret_cast<f32x4*>(gLC + ch) = f32x4{lamC[0], lamC[1], lamC[2], lamC[3]};
-      *reinterpret_cast<f32x4*>(gLC + ch + 4) = f32x4{lamC[4], lamC[5], lamC[6], lamC[7]};
+    for (int c = 0; c < 8; ++c) store2(gKT + (size_t)(ch + c) * C + 2 * s, kt[0][c], kt[1][c]);
+  }
+  __syncthreads();  // every read of the segment prefixes is done
+  if (active) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      store8(RAd + (2 * s + m) * LQ + ch, rad[m]);
+      store8(RPd + (2 * s + m) * LQ + ch, rpd[m]);
     }
   }
   __syncthreads();
 
   // ---------------------------------------------------------------- phase 2
-  // Tiles of A^T / P^T owned by this wave: all (R, Q) with R >= Q, round robin.
+  // A^T / P^T tiles (rows j, columns i), lower block triangle, round robin over waves
   constexpr int NTILE = NB * (NB + 1) / 2;
-  constexpr int TPW = (NTILE + 3) / 4;
+  constexpr int NW = kFastThreads / 64;
+  constexpr int TPW = (NTILE + NW - 1) / NW;
   f32x4 accA[TPW], accP[TPW];
   int tR[TPW], tQ[TPW];
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
+    int idx = wave + NW * i, R = 0;
+    while (idx > R) { idx -= R + 1; ++R; }
+    tR[i] = (wave + NW * i < NTILE) ? R : -1;
+    tQ[i] = idx;
     accA[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     accP[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    int idx = wave + 4 * i, R = 0;
-    while (idx > R) { idx -= R + 1; ++R; }  // idx-th lower tile in row-major order
-    tR[i] = (wave + 4 * i < NTILE) ? R : -1;
-    tQ[i] = idx;
-  }
-  E* X = reinterpret_cast<E*>(sm.r1);  // [C][LQ] row-role beta*k*f or col-role k*f
-  E* Y = X + C * LQ;                   // [C][LQ] row-role q*f
-  constexpr int LOGC = ilog2(C);
-  for (int lev = LOGC - 1; lev >= 0; --lev) {
-    const int L = 1 << lev;
-    for (int it = tid; it < C * NOCT; it += kPrepThreads) {
-      const int t = it / NOCT, c0 = 8 * (it % NOCT);
-      const bool lower = (t >> lev) & 1;
-      const int ref = lower ? ((t & ~(L - 1)) - 1) : (t | (L - 1));
-      float gt[8], gr[8], kk[8], f[8];
-      load8(&sm.gam[t * LG + c0], gt);
-      load8(&sm.gam[ref * LG + c0], gr);
-      load8(&sm.k[t * LQ + c0], kk);
-      if (lower) {
-        float qq[8], xr[8];
-        load8(&sm.q[t * LQ + c0], qq);
-        const float bta = sm.beta[t];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          f[c] = __expf(gt[c] - gr[c]);
-          xr[c] = bta * kk[c] * f[c];
-          qq[c] *= f[c];
-        }
-        store8(X + t * LQ + c0, xr);
-        store8(Y + t * LQ + c0, qq);
-      } else {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) kk[c] *= __expf(gr[c] - gt[c]);
-        store8(X + t * LQ + c0, kk);
-      }
+    if (tR[i] < 0) continue;
+    const int R0 = tR[i], Q0 = tQ[i];
+    RowFrag<E, D> cf, fa, fp;
+    if (R0 != Q0) {
+      cf.load(CB + (16 * Q0 + r) * LQ, g4);
+      if (R0 - Q0 >= 2) scale_k<D>(cf, &sm.mpq[pair_index(R0, Q0) * D], g4);
+      fa.load(RA + (16 * R0 + r) * LQ, g4);
+      fp.load(RP + (16 * R0 + r) * LQ, g4);
+    } else {
+      cf.load(CD + (16 * Q0 + r) * LQ, g4);
+      fa.load(RAd + (16 * R0 + r) * LQ, g4);
+      fp.load(RPd + (16 * R0 + r) * LQ, g4);
     }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      const int R = tR[i], Q = tQ[i];
-      if (R < 0) continue;
-      if (R != Q) {
-        if (tile_level(R, Q) != lev) continue;
-        // transposed tiles: rows j (upper half, column role), columns i (row role)
-        mma_rows<D>(accA[i], X + 16 * Q * LQ, LQ, X + 16 * R * LQ, LQ, lane);
-        mma_rows<D>(accP[i], X + 16 * Q * LQ, LQ, Y + 16 * R * LQ, LQ, lane);
-      } else if (lev < 4) {
-        f32x4 ta = {0.f, 0.f, 0.f, 0.f}, tp = {0.f, 0.f, 0.f, 0.f};
-        mma_rows<D>(ta, X + 16 * R * LQ, LQ, X + 16 * R * LQ, LQ, lane);
-        mma_rows<D>(tp, X + 16 * R * LQ, LQ, Y + 16 * R * LQ, LQ, lane);
-        const int ii = 16 * R + r;  // column = i
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int jj = 16 * R + 4 * g4 + e;  // row = j
-          const bool ok = ((ii >> (lev + 1)) == (jj >> (lev + 1))) && ((ii >> lev) & 1) &&
-                          !((jj >> lev) & 1);
-          accA[i][e] += ok ? ta[e] : 0.f;
-          accP[i][e] += ok ? tp[e] : 0.f;
-        }
-      }
-    }
-    __syncthreads();
+    mma<D>(accA[i], cf, fa);
+    mma<D>(accP[i], cf, fp);
   }
+  __syncthreads();  // operands are dead from here on
 
   // ---------------------------------------------------------------- phase 3
   float* sA = reinterpret_cast<float*>(sm.r1);  // [C][LA]
   float* sT = sA + C * LA;                      // [C][LA]
-  float* scr = sT + C * LA;                     // [4 waves][16][17]
-  for (int it = tid; it < C * LA; it += kPrepThreads) sT[it] = 0.f;
+  float* scr = sT + C * LA;                     // [4][16][17]
+  for (int it = tid; it < C * LA; it += kFastThreads) sT[it] = 0.f;
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
     const int R = tR[i], Q = tQ[i];
     if (R < 0) continue;
     const int ii = 16 * R + r;
     const int jj = 16 * Q + 4 * g4;
-    *reinterpret_cast<f32x4*>(&sA[ii * LA + jj]) = accA[i];
-    float pv[4];
+    float av[4], pv[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) pv[e] = (jj + e == ii) ? sm.pd[ii] : accP[i][e];
+    for (int e = 0; e < 4; ++e) {
+      const bool lowA = (R != Q) || (jj + e < ii);
+      const bool lowP = (R != Q) || (jj + e <= ii);
+      av[e] = lowA ? accA[i][e] : 0.f;
+      pv[e] = lowP ? accP[i][e] : 0.f;
+    }
+    *reinterpret_cast<f32x4*>(&sA[ii * LA + jj]) = f32x4{av[0], av[1], av[2], av[3]};
     store4(gP + (size_t)ii * C + jj, pv[0], pv[1], pv[2], pv[3]);
   }
   __syncthreads();
@@ -281,8 +317,8 @@ __global__ __launch_bounds__(kPrepThreads) void kda_chunk_prep_kernel(PrepParams
   // ---------------------------------------------------------------- phase 4
   // diagonal 16x16 blocks by forward substitution, one column per thread
   if (tid < C) {
-    const int pb = tid >> 4, col = tid & 15;
-    const float* Ab = sA + (16 * pb) * LA + 16 * pb;
+    const int pq = tid >> 4, col = tid & 15;
+    const float* Ab = sA + (16 * pq) * LA + 16 * pq;
     float x[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -292,20 +328,20 @@ __global__ __launch_bounds__(kPrepThreads) void kda_chunk_prep_kernel(PrepParams
       x[i] = acc;
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sT[(16 * pb + i) * LA + 16 * pb + col] = x[i];
+    for (int i = 0; i < 16; ++i) sT[(16 * pq + i) * LA + 16 * pq + col] = x[i];
   }
   __syncthreads();
   // off-diagonal blocks, block row by block row:
   //   T_pq = -T_pp * sum_{r=q}^{p-1} A_pr T_rq
-  for (int pb = 1; pb < NB; ++pb) {
+  for (int pr = 1; pr < NB; ++pr) {
     const int qb = wave;
-    float* xs = scr + wave * 16 * 17;
-    if (qb < pb) {
+    float* xs = scr + (wave & 3) * 16 * 17;
+    if (qb < pr) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int rb = qb; rb < pb; ++rb) {
+      for (int rb = qb; rb < pr; ++rb) {
 #pragma unroll
         for (int k0 = 0; k0 < 16; k0 += 4) {
-          const float a = sA[(16 * pb + r) * LA + 16 * rb + k0 + g4];
+          const float a = sA[(16 * pr + r) * LA + 16 * rb + k0 + g4];
           const float bv = sT[(16 * rb + k0 + g4) * LA + 16 * qb + r];
           acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv, acc, 0, 0, 0);
         }
@@ -314,16 +350,16 @@ __global__ __launch_bounds__(kPrepThreads) void kda_chunk_prep_kernel(PrepParams
       for (int e = 0; e < 4; ++e) xs[(4 * g4 + e) * 17 + r] = acc[e];
     }
     __syncthreads();
-    if (qb < pb) {
+    if (qb < pr) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k0 = 0; k0 < 16; k0 += 4) {
-        const float a = sT[(16 * pb + r) * LA + 16 * pb + k0 + g4];
+        const float a = sT[(16 * pr + r) * LA + 16 * pr + k0 + g4];
         const float bv = xs[(k0 + g4) * 17 + r];
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv, acc, 0, 0, 0);
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sT[(16 * pb + 4 * g4 + e) * LA + 16 * qb + r] = -acc[e];
+      for (int e = 0; e < 4; ++e) sT[(16 * pr + 4 * g4 + e) * LA + 16 * qb + r] = -acc[e];
     }
     __syncthreads();
   }
@@ -334,8 +370,8 @@ __global__ __launch_bounds__(kPrepThreads) void kda_chunk_prep_kernel(PrepParams
     Tb = reinterpret_cast<const E*>(sT);
     LTB = LA;
   } else {
-    E* tb = SM::TB_IN_Q ? sm.q : reinterpret_cast<E*>(sm.r1 + SM::TB_OFF);  // q no longer needed
-    for (int it = tid; it < C * C; it += kPrepThreads) {
+    E* tb = reinterpret_cast<E*>(sm.r1 + SM::TB_OFF);
+    for (int it = tid; it < C * C; it += kFastThreads) {
       const int i = it / C, jj = it % C;
       tb[i * LT + jj] = from_f32<E>(sT[i * LA + jj]);
     }
@@ -347,7 +383,7 @@ __global__ __launch_bounds__(kPrepThreads) void kda_chunk_prep_kernel(PrepParams
   // ---------------------------------------------------------------- phase 5
   // W^T tiles (c, i): A = (beta K Lambda)^T rows c, B^T = T rows i (j <= i)
   constexpr int NWT = (D / 16) * NB;
-  for (int tt = wave; tt < NWT; tt += 4) {
+  for (int tt = wave; tt < NWT; tt += NW) {
     const int Ct = tt / NB, It = tt % NB;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     mma_rows_upto<C>(acc, sm.klt + 16 * Ct * LT, LT, Tb + 16 * It * LTB, LTB, lane, 16 * It + 16);
@@ -355,7 +391,7 @@ __global__ __launch_bounds__(kPrepThreads) void kda_chunk_prep_kernel(PrepParams
     store4(gW + (size_t)i * D + c, acc[0], acc[1], acc[2], acc[3]);
   }
   // U~ tiles (i, v): A = T rows i, B^T = (beta V)^T rows v; stored in fragment order
-  for (int tt = wave; tt < NWT; tt += 4) {
+  for (int tt = wave; tt < NWT; tt += NW) {
     const int It = tt / (D / 16), Vt = tt % (D / 16);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     mma_rows_upto<C>(acc, Tb + 16 * It * LTB, LTB, sm.vt + 16 * Vt * LT, LT, lane, 16 * It + 16);
@@ -377,10 +413,10 @@ __global__ __launch_bounds__(256) void kda_conv_norm_kernel(ConvNormParams p) {
   const int tf = blk * TOK + 4 * s;
   const bool active = tf < p.T;
   float yq[4][8], yk[4][8], yv[4][8], qk[4];
-  conv_norm_tile<D, IO>(static_cast<const IO*>(p.q), static_cast<const IO*>(p.k),
-                        static_cast<const IO*>(p.v), static_cast<const IO*>(p.conv_state_in),
-                        p.conv_w, b, p.T, p.H, h, 8 * j, tf, active, p.l2 != 0, p.eps, 1.0f, yq,
-                        yk, yv, qk);
+  conv_norm_tile<4, D, IO>(static_cast<const IO*>(p.q), static_cast<const IO*>(p.k),
+                           static_cast<const IO*>(p.v), static_cast<const IO*>(p.conv_state_in),
+                           p.conv_w, b, p.T, p.H, h, 8 * j, tf, active, p.l2 != 0, p.eps, 1.0f,
+                           yq, yk, yv, qk);
   if (!active) return;
   const size_t HD = (size_t)p.H * D;
   IO* oq = static_cast<IO*>(p.q_out);
@@ -434,11 +470,16 @@ __global__ __launch_bounds__(256) void kda_copy_state_kernel(const float* src, f
   if (idx < n) dst[idx] = src ? src[idx] : 0.f;
 }
 
+// Clears the count of chunks handed to the exact preparation.
+__global__ void kda_reset_count_kernel(unsigned* count) {
+  if (threadIdx.x == 0) *count = 0u;
+}
+
 // ------------------------------------------------------------------ launchers
 template <int D, int C, typename IO, typename E>
 static hipError_t launch_prep_t(const PrepParams& p, hipStream_t st) {
   const unsigned grid = (unsigned)((size_t)p.B * p.H * p.NT);
-  hipLaunchKernelGGL((kda_chunk_prep_kernel<D, C, IO, E>), dim3(grid), dim3(kPrepThreads), 0, st,
+  hipLaunchKernelGGL((kda_chunk_prep_kernel<D, C, IO, E>), dim3(grid), dim3(kFastThreads), 0, st,
                      p);
   return hipGetLastError();
 }
@@ -467,8 +508,15 @@ static hipError_t launch_prep_d(const PrepParams& p, int D, int C, hipStream_t s
 }
 
 hipError_t launch_prep(const PrepParams& p, int D, int C, bool fp32, hipStream_t st) {
-  return fp32 ? launch_prep_d<float, float>(p, D, C, st)
-              : launch_prep_d<__bf16, __bf16>(p, D, C, st);
+  hipLaunchKernelGGL(kda_reset_count_kernel, dim3(1), dim3(64), 0, st, p.fb_count);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  const hipError_t e = fp32 ? launch_prep_d<float, float>(p, D, C, st)
+                            : launch_prep_d<__bf16, __bf16>(p, D, C, st);
+  if (e != hipSuccess) return e;
+  // the exact preparation of the listed chunks (exits at once when none is listed)
+  const size_t nrec = (size_t)p.B * p.H * p.NT;
+  const unsigned grid = (unsigned)(nrec < 512 ? nrec : 512);
+  return launch_prep_exact(p, D, C, fp32, grid, st);
 }
 
 template <int D, typename IO>

@@ -6,10 +6,15 @@
 // Per chunk, with S the D x VB float32 state block at the chunk start and the
 // chunk record written by the preparation kernel:
 //   U      = U~ - W S                         (the chunk's corrected new values)
-//   O      = (scale Q Lambda) S + P U         (inter-chunk + intra-chunk output)
+//   O^T    = S^T (scale Q Lambda)^T + U^T P^T (inter-chunk + intra-chunk output)
 //   S_next = Diag(Lambda_C) S + Ktil^T U      (Ktil = K exp(Gamma_C - Gamma))
 // S stays in float32 matrix-core accumulators for the whole walk; a copy in the
-// operand element type is staged in LDS for the products that read it.
+// operand element type is staged in LDS for the products that read it.  The
+// output is formed transposed so each lane holds 4 consecutive value columns of
+// one token, which it stores contiguously.
+//
+// The chunk record of chunk n+1 is loaded into registers while chunk n is being
+// computed, so the serial walk does not wait on memory latency.
 #include "kda_device.h"
 #include "kda_launch.h"
 #include "kda_layout.h"
@@ -18,54 +23,15 @@ namespace kda {
 
 constexpr int kStateThreads = 256;
 
-// acc += P(rows i0..i0+15, k) * B(k, 16 cols), P read from global row-major with
-// the causal mask j <= i applied in registers; only k < i0 + 16 is visited.
-template <int C>
-__device__ __forceinline__ void mma_causal(f32x4& acc, const __bf16* P, int i0, const __bf16* Bt,
-                                           int ldb, int lane) {
-  const int r = lane & 15, g = lane >> 4;
-  const int i = i0 + r;
-  if constexpr (C % 32 == 0) {
-#pragma unroll
-    for (int k0 = 0; k0 < C; k0 += 32) {
-      if (k0 < i0 + 16) {
-        bf16x8 a = *reinterpret_cast<const bf16x8*>(P + (size_t)i * C + k0 + 8 * g);
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (k0 + 8 * g + e > i) a[e] = (__bf16)0.f;
-        bf16x8 b = *reinterpret_cast<const bf16x8*>(Bt + r * ldb + k0 + 8 * g);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
-      }
-    }
-  } else {
-#pragma unroll
-    for (int k0 = 0; k0 < C; k0 += 16) {
-      if (k0 < i0 + 16) {
-        bf16x4 a = *reinterpret_cast<const bf16x4*>(P + (size_t)i * C + k0 + 4 * g);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (k0 + 4 * g + e > i) a[e] = (__bf16)0.f;
-        s16x4 as = __builtin_bit_cast(s16x4, a);
-        s16x4 bs = *reinterpret_cast<const s16x4*>(Bt + r * ldb + k0 + 4 * g);
-        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(as, bs, acc, 0, 0, 0);
-      }
-    }
-  }
-}
-template <int C>
-__device__ __forceinline__ void mma_causal(f32x4& acc, const float* P, int i0, const float* Bt,
-                                           int ldb, int lane) {
-  const int r = lane & 15, g = lane >> 4;
-  const int i = i0 + r;
-#pragma unroll
-  for (int k0 = 0; k0 < C; k0 += 4) {
-    if (k0 < i0 + 16) {
-      const int kk = k0 + g;
-      const float a = (kk <= i) ? P[(size_t)i * C + kk] : 0.f;
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, Bt[r * ldb + kk], acc, 0, 0, 0);
-    }
-  }
-}
+template <typename E, int D, int C, int NCTW, int NU>
+struct ChunkRegs {
+  RowFrag<E, D> w;         // W rows of this wave's t-tile
+  RowFrag<E, D> ql;        // scale Q Lambda rows of this wave's t-tile
+  RowFrag<E, C> p;         // P rows of this wave's t-tile (causally masked)
+  RowFrag<E, C> kt[NCTW];  // Ktil^T rows of this wave's c-tiles
+  f32x4 ut[NU];            // U~ fragments of this wave's (t-tile, v-tile) units
+  f32x4 lc[NCTW];          // Lambda_C for the 4 rows this lane holds per c-tile
+};
 
 template <int D, int C, int VB, typename IO, typename E>
 __global__ __launch_bounds__(kStateThreads) void kda_chunk_state_kernel(StateParams p) {
@@ -73,11 +39,14 @@ __global__ __launch_bounds__(kStateThreads) void kda_chunk_state_kernel(StatePar
   constexpr int LS = D + PE;  // sS row stride: row = value column v, k = key channel c
   constexpr int LU = C + PE;  // sU row stride: row = value column v, k = token t
   constexpr int NV = D / VB;
-  constexpr int VT = VB / 16;
-  constexpr int T1 = (C / 16) * VT;  // U / O tiles (t-tile, v-tile)
-  constexpr int T3 = (D / 16) * VT;  // state tiles (c-tile, v-tile)
-  constexpr int P1 = (T1 + 3) / 4;
-  constexpr int P3 = (T3 + 3) / 4;
+  constexpr int VT = VB / 16;   // v-tiles
+  constexpr int RT = C / 16;    // t-tiles
+  constexpr int CT = D / 16;    // c-tiles
+  static_assert(4 % RT == 0 || RT == 4, "t-tiles must divide the 4 waves");
+  constexpr int NU = (RT * VT + 3) / 4;      // (t-tile, v-tile) units per wave (upper bound)
+  constexpr int NS = (CT * VT + 3) / 4;      // (c-tile, v-tile) units per wave (upper bound)
+  constexpr int CTW = CT < 4 ? CT : 4;       // c-tile stride between a wave's units
+  constexpr int NCTW = CT > 4 ? CT / 4 : 1;  // distinct c-tiles per wave
   constexpr RecordLayout RL = record_layout(C, D, sizeof(E));
   __shared__ __attribute__((aligned(16))) E sS[VB * LS];
   __shared__ __attribute__((aligned(16))) E sU[VB * LU];
@@ -99,15 +68,52 @@ __global__ __launch_bounds__(kStateThreads) void kda_chunk_state_kernel(StatePar
   const int h = bh % p.H, b = bh / p.H;
   const int vb0 = vblk * VB;
 
+  // this wave's tiles
+  const int R = wave % RT;               // t-tile of every (t, v) unit of this wave
+  const bool has_u = wave < RT * VT;     // any (t, v) unit at all
+  const int i_row = 16 * R + r;          // row of P / W / QL this lane reads
+  const int csteps = (16 * R + 16 + RowFrag<E, C>::STEP - 1) / RowFrag<E, C>::STEP;
+
+  auto load_chunk = [&](int n, ChunkRegs<E, D, C, NCTW, NU>& cr) {
+    const char* recp = p.ws + ((size_t)bh * p.NT + n) * RL.bytes;
+    const E* W = reinterpret_cast<const E*>(recp) + RL.w;
+    const E* QL = reinterpret_cast<const E*>(recp) + RL.ql;
+    const E* KT = reinterpret_cast<const E*>(recp) + RL.kt;
+    const E* Ut = reinterpret_cast<const E*>(recp) + RL.u;
+    const E* P = reinterpret_cast<const E*>(recp) + RL.p;
+    const float* LC = reinterpret_cast<const float*>(recp + RL.lc_bytes);
+    if (has_u) {
+      cr.w.load(W + (size_t)i_row * D, g4);
+      cr.ql.load(QL + (size_t)i_row * D, g4);
+      cr.p.load(P + (size_t)i_row * C, g4);
+    }
+#pragma unroll
+    for (int j = 0; j < NCTW; ++j) {
+      const int Ct = (wave % CTW) + 4 * j;
+      cr.kt[j].load(KT + (size_t)(16 * Ct + r) * C, g4);
+      cr.lc[j] = *reinterpret_cast<const f32x4*>(LC + 16 * Ct + 4 * g4);
+    }
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+      const int u = wave + 4 * i;
+      if (u < RT * VT) {
+        const int Vt = u / RT;
+        float t4[4];
+        load4(Ut + ((size_t)(R * (D / 16) + vb0 / 16 + Vt) * 64 + lane) * 4, t4);
+        cr.ut[i] = f32x4{t4[0], t4[1], t4[2], t4[3]};
+      }
+    }
+  };
+
   // ---- initial state
-  f32x4 accS[P3];
+  f32x4 accS[NS];
   const size_t sbase = (size_t)bh * D * D;
 #pragma unroll
-  for (int i = 0; i < P3; ++i) {
-    const int tt = wave + 4 * i;
+  for (int i = 0; i < NS; ++i) {
+    const int u = wave + 4 * i;
     accS[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (tt < T3 && p.S0 != nullptr) {
-      const int Ct = tt / VT, Vt = tt % VT;
+    if (u < CT * VT && p.S0 != nullptr) {
+      const int Ct = u % CT, Vt = u / CT;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         accS[i][e] = p.S0[sbase + (size_t)(16 * Ct + 4 * g4 + e) * D + vb0 + 16 * Vt + r];
@@ -115,10 +121,10 @@ __global__ __launch_bounds__(kStateThreads) void kda_chunk_state_kernel(StatePar
   }
   auto stage_state = [&]() {
 #pragma unroll
-    for (int i = 0; i < P3; ++i) {
-      const int tt = wave + 4 * i;
-      if (tt < T3) {
-        const int Ct = tt / VT, Vt = tt % VT;
+    for (int i = 0; i < NS; ++i) {
+      const int u = wave + 4 * i;
+      if (u < CT * VT) {
+        const int Ct = u % CT, Vt = u / CT;
         store4(&sS[(16 * Vt + r) * LS + 16 * Ct + 4 * g4], accS[i][0], accS[i][1], accS[i][2],
                accS[i][3]);
       }
@@ -128,70 +134,69 @@ __global__ __launch_bounds__(kStateThreads) void kda_chunk_state_kernel(StatePar
 
   IO* o = static_cast<IO*>(p.o);
   const size_t HD = (size_t)p.H * D;
+  ChunkRegs<E, D, C, NCTW, NU> cur, nxt;
+  load_chunk(0, cur);
   for (int n = 0; n < p.NT; ++n) {
-    const char* recp = p.ws + ((size_t)bh * p.NT + n) * RL.bytes;
-    const E* W = reinterpret_cast<const E*>(recp) + RL.w;
-    const E* QL = reinterpret_cast<const E*>(recp) + RL.ql;
-    const E* KT = reinterpret_cast<const E*>(recp) + RL.kt;
-    const E* Ut = reinterpret_cast<const E*>(recp) + RL.u;
-    const E* P = reinterpret_cast<const E*>(recp) + RL.p;
-    const float* LC = reinterpret_cast<const float*>(recp + RL.lc_bytes);
+    if (n + 1 < p.NT) load_chunk(n + 1, nxt);
+    if (has_u) cur.p.mask_above(i_row, g4);
     __syncthreads();  // sS holds this chunk's starting state; sU is free
-    f32x4 accO[P1];
-    // ---- U = U~ - W S,  O = QL S
+    // ---- U = U~ - W S  and  O^T = S^T QL^T
+    f32x4 accO[NU];
 #pragma unroll
-    for (int i = 0; i < P1; ++i) {
-      const int tt = wave + 4 * i;
+    for (int i = 0; i < NU; ++i) {
+      const int u = wave + 4 * i;
       accO[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (tt < T1) {
-        const int R = tt / VT, Vt = tt % VT;
+      if (u < RT * VT) {
+        const int Vt = u / RT;
+        RowFrag<E, D> sf;
+        sf.load(sS + (16 * Vt + r) * LS, g4);
         f32x4 ws = {0.f, 0.f, 0.f, 0.f};
-        mma_rows<D>(ws, W + (size_t)16 * R * D, D, sS + 16 * Vt * LS, LS, lane);
-        mma_rows<D>(accO[i], QL + (size_t)16 * R * D, D, sS + 16 * Vt * LS, LS, lane);
-        float u[4];
-        load4(Ut + ((size_t)(R * (D / 16) + vb0 / 16 + Vt) * 64 + lane) * 4, u);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) u[e] -= ws[e];
-        store4(&sU[(16 * Vt + r) * LU + 16 * R + 4 * g4], u[0], u[1], u[2], u[3]);
+        mma<D>(ws, cur.w, sf);        // (t, v) tile of W S
+        mma<D>(accO[i], sf, cur.ql);  // (v, t) tile of S^T QL^T
+        store4(&sU[(16 * Vt + r) * LU + 16 * R + 4 * g4], cur.ut[i][0] - ws[0],
+               cur.ut[i][1] - ws[1], cur.ut[i][2] - ws[2], cur.ut[i][3] - ws[3]);
       }
     }
     __syncthreads();  // sU complete; every read of sS for this chunk is done
-    // ---- O += P U, write O
+    // ---- O^T += U^T P^T (j <= i), store O
 #pragma unroll
-    for (int i = 0; i < P1; ++i) {
-      const int tt = wave + 4 * i;
-      if (tt < T1) {
-        const int R = tt / VT, Vt = tt % VT;
-        mma_causal<C>(accO[i], P, 16 * R, sU + 16 * Vt * LU, LU, lane);
-        const int v = vb0 + 16 * Vt + r;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int t = n * C + 16 * R + 4 * g4 + e;
-          if (t < p.T) o[((size_t)b * p.T + t) * HD + (size_t)h * D + v] = from_f32<IO>(accO[i][e]);
-        }
+    for (int i = 0; i < NU; ++i) {
+      const int u = wave + 4 * i;
+      if (u < RT * VT) {
+        const int Vt = u / RT;
+        RowFrag<E, C> uf;
+        uf.load(sU + (16 * Vt + r) * LU, g4);
+        mma<C>(accO[i], uf, cur.p, csteps);
+        const int t = n * C + 16 * R + r;
+        if (t < p.T)
+          store4(o + ((size_t)b * p.T + t) * HD + (size_t)h * D + vb0 + 16 * Vt + 4 * g4,
+                 accO[i][0], accO[i][1], accO[i][2], accO[i][3]);
       }
     }
     // ---- S = Diag(Lambda_C) S + Ktil^T U
 #pragma unroll
-    for (int i = 0; i < P3; ++i) {
-      const int tt = wave + 4 * i;
-      if (tt < T3) {
-        const int Ct = tt / VT, Vt = tt % VT;
-        const f32x4 lc = *reinterpret_cast<const f32x4*>(LC + 16 * Ct + 4 * g4);
+    for (int i = 0; i < NS; ++i) {
+      const int u = wave + 4 * i;
+      if (u < CT * VT) {
+        const int Vt = u / CT;
+        const int j = i % NCTW;  // this unit's c-tile is (wave % CTW) + 4 * j
+        RowFrag<E, C> uf;
+        uf.load(sU + (16 * Vt + r) * LU, g4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) accS[i][e] *= lc[e];
-        mma_rows<C>(accS[i], KT + (size_t)16 * Ct * C, C, sU + 16 * Vt * LU, LU, lane);
+        for (int e = 0; e < 4; ++e) accS[i][e] *= cur.lc[j][e];
+        mma<C>(accS[i], cur.kt[j], uf);
       }
     }
     stage_state();
+    cur = nxt;
   }
   // ---- final state
   if (p.S_T != nullptr) {
 #pragma unroll
-    for (int i = 0; i < P3; ++i) {
-      const int tt = wave + 4 * i;
-      if (tt < T3) {
-        const int Ct = tt / VT, Vt = tt % VT;
+    for (int i = 0; i < NS; ++i) {
+      const int u = wave + 4 * i;
+      if (u < CT * VT) {
+        const int Ct = u % CT, Vt = u / CT;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           p.S_T[sbase + (size_t)(16 * Ct + 4 * g4 + e) * D + vb0 + 16 * Vt + r] = accS[i][e];

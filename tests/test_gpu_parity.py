@@ -259,3 +259,35 @@ def test_strong_decay_finite():
     assert np.isfinite(o).all() and np.isfinite(S).all()
     for (b, h), (ro, rS) in zip([(0, 0), (0, 5)], oracle_heads(inp, [(0, 0), (0, 5)])):
         assert rel_l2(o[b, :, h], ro) <= 2e-2 and rel_l2(S[b, h], rS) <= 2e-2
+
+
+@pytest.mark.parametrize("gval,desc", [(-6.0, "wide block spans: midpoint reference"),
+                                       (-12.0, "spans beyond the factoring: exact fallback"),
+                                       (-40.0, "extreme per-step decay")])
+def test_strong_decay_channel_paths(gval, desc):
+    """Channels whose 16-token decay span exceeds what the block-start factoring
+    can represent take the midpoint reference (about 80-166 nats) or send their
+    chunk to the exact preparation (beyond that).  Only some channels of some
+    chunks are made strong so both paths meet ordinary ones in one call."""
+    w = small(B=2, T=200, H=2, D=128, io="bf16", chunk=64, s0=True, conv_state=True)
+    inp = make(w, 21)
+    g = inp["g"].float()
+    g[0, 64:128, 0, ::3] = gval     # second chunk of (b=0, h=0), every third channel
+    g[1, :40, 1, 5:9] = gval        # first chunk of (b=1, h=1), four channels
+    inp["g"] = g.to(inp["g"].dtype)
+    o, S, _ = gpu_prefill(inp, 64)
+    ro, rS, _ = oracle_prefill(inp)
+    eo, eS = rel_l2(o, ro), rel_l2(S, rS)
+    print(f"{desc}: o={eo:.2e} S={eS:.2e}", flush=True)
+    assert np.isfinite(o).all() and np.isfinite(S).all()
+    assert eo <= 2e-2 and eS <= 2e-2
+
+
+def test_fallback_all_chunks_fp32():
+    """Every chunk too strong for the factoring: the exact path alone, fp32."""
+    w = small(B=1, T=100, H=2, D=64, io="fp32", chunk=32, s0=True)
+    inp = make(w, 22)
+    inp["g"] = torch.full_like(inp["g"], -15.0)
+    o, S, _ = gpu_prefill(inp, 32)
+    ro, rS, _ = oracle_prefill(inp)
+    assert rel_l2(o, ro) <= 1e-4 and rel_l2(S, rS) <= 1e-4
