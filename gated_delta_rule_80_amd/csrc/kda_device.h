@@ -232,10 +232,47 @@ __device__ __forceinline__ void mma(f32x4& acc, const RowFrag<float, K>& a,
     if (i < steps) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[i], b.v[i], acc, 0, 0, 0);
 }
 
+// ------------------------------------------------- swizzled LDS matrix images
+// A row-major matrix of K elements per row stored in LDS with its 16-byte chunks
+// permuted within each row: chunk c of row `row` sits at position c ^ (row % RC),
+// RC = chunks per row.  Sixteen lanes reading the same k range of 16 different
+// rows then hit distinct banks.
+template <typename E, int K>
+struct Swz {
+  static constexpr int EPC = 16 / (int)sizeof(E);  // elements per chunk
+  static constexpr int RC = K / EPC;               // chunks per row (power of two)
+  static_assert(RC >= 1 && (RC & (RC - 1)) == 0, "rows must hold a power-of-two chunk count");
+  // element offset of element k of `row`
+  __device__ __forceinline__ static int at(int row, int k) {
+    return row * K + (((k / EPC) ^ (row & (RC - 1))) * EPC) + (k % EPC);
+  }
+};
+
+// Load this lane's fragment of row `row` from a swizzled LDS image.
+template <int K>
+__device__ __forceinline__ void load_swz(RowFrag<__bf16, K>& f, const __bf16* img, int row, int g) {
+  using FR = RowFrag<__bf16, K>;
+#pragma unroll
+  for (int i = 0; i < FR::N; ++i)
+    f.v[i] = *reinterpret_cast<const typename FR::V*>(img + Swz<__bf16, K>::at(row, i * FR::STEP + FR::PER * g));
+}
+template <int K>
+__device__ __forceinline__ void load_swz(RowFrag<float, K>& f, const float* img, int row, int g) {
+#pragma unroll
+  for (int i = 0; i < RowFrag<float, K>::N; ++i) f.v[i] = img[Swz<float, K>::at(row, 4 * i + g)];
+}
+
 // Instruction depth along k for an element type (used for causal bounds).
 template <typename E> struct KStep;
 template <> struct KStep<__bf16> { static constexpr int value = 32; };
 template <> struct KStep<float> { static constexpr int value = 4; };
+
+// Workgroup barrier ordering LDS accesses only: waits for this wave's LDS
+// operations, not for its outstanding global-memory operations (including
+// global-to-LDS copies into a buffer nobody touches until a later full barrier).
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 // ------------------------------------------------------------ small math
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }

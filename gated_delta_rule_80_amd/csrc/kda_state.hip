@@ -13,8 +13,11 @@
 // output is formed transposed so each lane holds 4 consecutive value columns of
 // one token, which it stores contiguously.
 //
-// The chunk record of chunk n+1 is loaded into registers while chunk n is being
-// computed, so the serial walk does not wait on memory latency.
+// The chunk record is copied into LDS by the asynchronous global-to-LDS loads of
+// gfx950 (16 bytes per lane straight into LDS, no registers involved).  Each
+// chunk's fragments are read from LDS into registers at the start of its step,
+// after which the copy of the next chunk is issued and runs under the step's
+// arithmetic.
 #include "kda_device.h"
 #include "kda_launch.h"
 #include "kda_layout.h"
@@ -23,19 +26,42 @@ namespace kda {
 
 constexpr int kStateThreads = 256;
 
-template <typename E, int D, int C, int NCTW, int NU>
-struct ChunkRegs {
-  RowFrag<E, D> w;         // W rows of this wave's t-tile
-  RowFrag<E, D> ql;        // scale Q Lambda rows of this wave's t-tile
-  RowFrag<E, C> p;         // P rows of this wave's t-tile (causally masked)
-  RowFrag<E, C> kt[NCTW];  // Ktil^T rows of this wave's c-tiles
-  f32x4 ut[NU];            // U~ fragments of this wave's (t-tile, v-tile) units
-  f32x4 lc[NCTW];          // Lambda_C for the 4 rows this lane holds per c-tile
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+// 4 consecutive elements kept raw until used
+template <typename E> struct Raw4;
+template <> struct Raw4<__bf16> {
+  bf16x4 v;
+  __device__ __forceinline__ void load(const __bf16* p) { v = *reinterpret_cast<const bf16x4*>(p); }
+  __device__ __forceinline__ float operator[](int i) const { return (float)v[i]; }
+};
+template <> struct Raw4<float> {
+  f32x4 v;
+  __device__ __forceinline__ void load(const float* p) { v = *reinterpret_cast<const f32x4*>(p); }
+  __device__ __forceinline__ float operator[](int i) const { return v[i]; }
+};
+
+// The LDS image of the part of one chunk record a workgroup reads.  Byte offsets;
+// every part is a whole number of 16-byte chunks.
+template <int D, int C, int VB, typename E>
+struct RecImage {
+  static constexpr int ES = (int)sizeof(E);
+  static constexpr int W = 0;                          // [C][D] swizzled
+  static constexpr int QL = W + C * D * ES;            // [C][D] swizzled
+  static constexpr int KT = QL + C * D * ES;           // [D][C] swizzled
+  static constexpr int P = KT + D * C * ES;            // [C][C] swizzled
+  static constexpr int U = P + C * C * ES;             // (C/16) x (VB/16) fragment tiles
+  static constexpr int LC = U + C * VB * ES;           // [D] float
+  static constexpr int BYTES = LC + D * 4;
+  static constexpr int CHUNKS = BYTES / 16;
+  static_assert(BYTES % 16 == 0, "record image is whole 16-byte chunks");
 };
 
 template <int D, int C, int VB, typename IO, typename E>
-__global__ __launch_bounds__(kStateThreads) void kda_chunk_state_kernel(StateParams p) {
+__global__ __launch_bounds__(kStateThreads, 2) void kda_chunk_state_kernel(StateParams p) {
   constexpr int PE = 16 / (int)sizeof(E);
+  constexpr int ES = (int)sizeof(E);
   constexpr int LS = D + PE;  // sS row stride: row = value column v, k = key channel c
   constexpr int LU = C + PE;  // sU row stride: row = value column v, k = token t
   constexpr int NV = D / VB;
@@ -47,7 +73,11 @@ __global__ __launch_bounds__(kStateThreads) void kda_chunk_state_kernel(StatePar
   constexpr int NS = (CT * VT + 3) / 4;      // (c-tile, v-tile) units per wave (upper bound)
   constexpr int CTW = CT < 4 ? CT : 4;       // c-tile stride between a wave's units
   constexpr int NCTW = CT > 4 ? CT / 4 : 1;  // distinct c-tiles per wave
+  constexpr bool FULL_U = (RT * VT) % 4 == 0;
+  constexpr bool FULL_S = (CT * VT) % 4 == 0;
   constexpr RecordLayout RL = record_layout(C, D, sizeof(E));
+  using IMG = RecImage<D, C, VB, E>;
+  __shared__ __attribute__((aligned(16))) char img[IMG::BYTES];
   __shared__ __attribute__((aligned(16))) E sS[VB * LS];
   __shared__ __attribute__((aligned(16))) E sU[VB * LU];
 
@@ -69,39 +99,55 @@ __global__ __launch_bounds__(kStateThreads) void kda_chunk_state_kernel(StatePar
   const int vb0 = vblk * VB;
 
   // this wave's tiles
-  const int R = wave % RT;               // t-tile of every (t, v) unit of this wave
-  const bool has_u = wave < RT * VT;     // any (t, v) unit at all
-  const int i_row = 16 * R + r;          // row of P / W / QL this lane reads
+  const int R = wave % RT;                      // t-tile of every (t, v) unit of this wave
+  const bool has_u = FULL_U || wave < RT * VT;  // any (t, v) unit at all
+  const int i_row = 16 * R + r;                 // row of P / W / QL this lane reads
   const int csteps = (16 * R + 16 + RowFrag<E, C>::STEP - 1) / RowFrag<E, C>::STEP;
 
-  auto load_chunk = [&](int n, ChunkRegs<E, D, C, NCTW, NU>& cr) {
+  // ---- asynchronous copy of a chunk's record image into LDS.  Thread tid moves
+  // 16-byte chunk it * 256 + tid of the image; its source offset inside the
+  // record is the same for every chunk, so it is computed once.
+  constexpr int ITERS = (IMG::CHUNKS + kStateThreads - 1) / kStateThreads;
+  uint32_t src_off[ITERS];
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    constexpr int RCD = D * ES / 16;           // chunks per row of W, QL
+    constexpr int RCC = C * ES / 16;           // chunks per row of KT, P
+    constexpr int UPIECE = VT * 64 * 4 * ES / 16;  // chunks of U~ per t-tile: VT tiles x 64 lanes x 4
+    const int idx = it * kStateThreads + tid;
+    const int byte = idx * 16;
+    size_t off;
+    if (byte < IMG::KT) {
+      // W or QL: rows of RCD chunks, stored swizzled
+      const bool isql = byte >= IMG::QL;
+      const int ci = idx - (isql ? IMG::QL / 16 : 0);
+      const int row = ci / RCD, cs = ci % RCD;
+      off = (size_t)(isql ? RL.ql : RL.w) * ES + (size_t)(row * RCD + (cs ^ (row & (RCD - 1)))) * 16;
+    } else if (byte < IMG::U) {
+      // KT or P: rows of RCC chunks, stored swizzled
+      const bool isp = byte >= IMG::P;
+      const int ci = idx - (isp ? IMG::P : IMG::KT) / 16;
+      const int row = ci / RCC, cs = ci % RCC;
+      off = (size_t)(isp ? RL.p : RL.kt) * ES + (size_t)(row * RCC + (cs ^ (row & (RCC - 1)))) * 16;
+    } else if (byte < IMG::LC) {
+      // U~ tiles of this value block, one contiguous piece per t-tile
+      const int ci = idx - IMG::U / 16;
+      const int tt = ci / UPIECE, w = ci % UPIECE;
+      off = (size_t)RL.u * ES + ((size_t)(tt * (D / 16) + vb0 / 16) * 64 * 4) * ES + (size_t)w * 16;
+    } else {
+      off = RL.lc_bytes + (size_t)(idx - IMG::LC / 16) * 16;
+    }
+    src_off[it] = (uint32_t)off;
+  }
+  auto issue_copy = [&](int n) {
     const char* recp = p.ws + ((size_t)bh * p.NT + n) * RL.bytes;
-    const E* W = reinterpret_cast<const E*>(recp) + RL.w;
-    const E* QL = reinterpret_cast<const E*>(recp) + RL.ql;
-    const E* KT = reinterpret_cast<const E*>(recp) + RL.kt;
-    const E* Ut = reinterpret_cast<const E*>(recp) + RL.u;
-    const E* P = reinterpret_cast<const E*>(recp) + RL.p;
-    const float* LC = reinterpret_cast<const float*>(recp + RL.lc_bytes);
-    if (has_u) {
-      cr.w.load(W + (size_t)i_row * D, g4);
-      cr.ql.load(QL + (size_t)i_row * D, g4);
-      cr.p.load(P + (size_t)i_row * C, g4);
-    }
 #pragma unroll
-    for (int j = 0; j < NCTW; ++j) {
-      const int Ct = (wave % CTW) + 4 * j;
-      cr.kt[j].load(KT + (size_t)(16 * Ct + r) * C, g4);
-      cr.lc[j] = *reinterpret_cast<const f32x4*>(LC + 16 * Ct + 4 * g4);
-    }
-#pragma unroll
-    for (int i = 0; i < NU; ++i) {
-      const int u = wave + 4 * i;
-      if (u < RT * VT) {
-        const int Vt = u / RT;
-        float t4[4];
-        load4(Ut + ((size_t)(R * (D / 16) + vb0 / 16 + Vt) * 64 + lane) * 4, t4);
-        cr.ut[i] = f32x4{t4[0], t4[1], t4[2], t4[3]};
-      }
+    for (int it = 0; it < ITERS; ++it) {
+      // this wave's 64 lanes fill img + (it * 256 + 64 * wave) * 16 onwards, 16 bytes per lane
+      if (it * kStateThreads + tid < IMG::CHUNKS)
+        __builtin_amdgcn_global_load_lds(
+            (const glb_void_t*)(recp + src_off[it]),
+            (lds_void_t*)(img + (size_t)(it * kStateThreads + 64 * wave) * 16), 16, 0, 0);
     }
   };
 
@@ -112,7 +158,7 @@ __global__ __launch_bounds__(kStateThreads) void kda_chunk_state_kernel(StatePar
   for (int i = 0; i < NS; ++i) {
     const int u = wave + 4 * i;
     accS[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (u < CT * VT && p.S0 != nullptr) {
+    if ((FULL_S || u < CT * VT) && p.S0 != nullptr) {
       const int Ct = u % CT, Vt = u / CT;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
@@ -123,7 +169,7 @@ __global__ __launch_bounds__(kStateThreads) void kda_chunk_state_kernel(StatePar
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       const int u = wave + 4 * i;
-      if (u < CT * VT) {
+      if (FULL_S || u < CT * VT) {
         const int Ct = u % CT, Vt = u / CT;
         store4(&sS[(16 * Vt + r) * LS + 16 * Ct + 4 * g4], accS[i][0], accS[i][1], accS[i][2],
                accS[i][3]);
@@ -134,39 +180,70 @@ __global__ __launch_bounds__(kStateThreads) void kda_chunk_state_kernel(StatePar
 
   IO* o = static_cast<IO*>(p.o);
   const size_t HD = (size_t)p.H * D;
-  ChunkRegs<E, D, C, NCTW, NU> cur, nxt;
-  load_chunk(0, cur);
+  const E* iW = reinterpret_cast<const E*>(img + IMG::W);
+  const E* iQL = reinterpret_cast<const E*>(img + IMG::QL);
+  const E* iKT = reinterpret_cast<const E*>(img + IMG::KT);
+  const E* iP = reinterpret_cast<const E*>(img + IMG::P);
+  const E* iU = reinterpret_cast<const E*>(img + IMG::U);
+  const float* iLC = reinterpret_cast<const float*>(img + IMG::LC);
+
+  issue_copy(0);
   for (int n = 0; n < p.NT; ++n) {
-    if (n + 1 < p.NT) load_chunk(n + 1, nxt);
-    if (has_u) cur.p.mask_above(i_row, g4);
-    __syncthreads();  // sS holds this chunk's starting state; sU is free
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies (and stores) have landed
+    __syncthreads();                // the whole image of chunk n and the state are in LDS
+    // ---- this chunk's fragments, from the image into registers
+    RowFrag<E, D> fw, fql;
+    RowFrag<E, C> fp;
+    RowFrag<E, C> fkt[NCTW];
+    Raw4<E> fu[NU];
+    f32x4 flc[NCTW];
+    if (has_u) {
+      load_swz<D>(fw, iW, i_row, g4);
+      load_swz<D>(fql, iQL, i_row, g4);
+      load_swz<C>(fp, iP, i_row, g4);
+    }
+#pragma unroll
+    for (int j = 0; j < NCTW; ++j) {
+      const int Ct = (wave % CTW) + 4 * j;
+      load_swz<C>(fkt[j], iKT, 16 * Ct + r, g4);
+      flc[j] = *reinterpret_cast<const f32x4*>(iLC + 16 * Ct + 4 * g4);
+    }
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+      const int u = wave + 4 * i;
+      if (FULL_U || u < RT * VT) fu[i].load(iU + ((size_t)(R * VT + u / RT) * 64 + lane) * 4);
+    }
+    __syncthreads();  // every wave holds its fragments: the image may be overwritten
+    if (n + 1 < p.NT) issue_copy(n + 1);
+    if (has_u) fp.mask_above(i_row, g4);
+
     // ---- U = U~ - W S  and  O^T = S^T QL^T
     f32x4 accO[NU];
 #pragma unroll
     for (int i = 0; i < NU; ++i) {
       const int u = wave + 4 * i;
       accO[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (u < RT * VT) {
+      if (FULL_U || u < RT * VT) {
         const int Vt = u / RT;
         RowFrag<E, D> sf;
         sf.load(sS + (16 * Vt + r) * LS, g4);
         f32x4 ws = {0.f, 0.f, 0.f, 0.f};
-        mma<D>(ws, cur.w, sf);        // (t, v) tile of W S
-        mma<D>(accO[i], sf, cur.ql);  // (v, t) tile of S^T QL^T
-        store4(&sU[(16 * Vt + r) * LU + 16 * R + 4 * g4], cur.ut[i][0] - ws[0],
-               cur.ut[i][1] - ws[1], cur.ut[i][2] - ws[2], cur.ut[i][3] - ws[3]);
+        mma<D>(ws, fw, sf);        // (t, v) tile of W S
+        mma<D>(accO[i], sf, fql);  // (v, t) tile of S^T QL^T
+        store4(&sU[(16 * Vt + r) * LU + 16 * R + 4 * g4], fu[i][0] - ws[0], fu[i][1] - ws[1],
+               fu[i][2] - ws[2], fu[i][3] - ws[3]);
       }
     }
-    __syncthreads();  // sU complete; every read of sS for this chunk is done
+    lds_barrier();  // sU complete; every read of sS for this chunk is done
     // ---- O^T += U^T P^T (j <= i), store O
 #pragma unroll
     for (int i = 0; i < NU; ++i) {
       const int u = wave + 4 * i;
-      if (u < RT * VT) {
+      if (FULL_U || u < RT * VT) {
         const int Vt = u / RT;
         RowFrag<E, C> uf;
         uf.load(sU + (16 * Vt + r) * LU, g4);
-        mma<C>(accO[i], uf, cur.p, csteps);
+        mma<C>(accO[i], uf, fp, csteps);
         const int t = n * C + 16 * R + r;
         if (t < p.T)
           store4(o + ((size_t)b * p.T + t) * HD + (size_t)h * D + vb0 + 16 * Vt + 4 * g4,
@@ -177,25 +254,24 @@ __global__ __launch_bounds__(kStateThreads) void kda_chunk_state_kernel(StatePar
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       const int u = wave + 4 * i;
-      if (u < CT * VT) {
+      if (FULL_S || u < CT * VT) {
         const int Vt = u / CT;
         const int j = i % NCTW;  // this unit's c-tile is (wave % CTW) + 4 * j
         RowFrag<E, C> uf;
         uf.load(sU + (16 * Vt + r) * LU, g4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) accS[i][e] *= cur.lc[j][e];
-        mma<C>(accS[i], cur.kt[j], uf);
+        for (int e = 0; e < 4; ++e) accS[i][e] *= flc[j][e];
+        mma<C>(accS[i], fkt[j], uf);
       }
     }
     stage_state();
-    cur = nxt;
   }
   // ---- final state
   if (p.S_T != nullptr) {
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       const int u = wave + 4 * i;
-      if (u < CT * VT) {
+      if (FULL_S || u < CT * VT) {
         const int Ct = u % CT, Vt = u / CT;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
