@@ -19,88 +19,126 @@ __device__ __forceinline__ float silu_fast(float x) {
   return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-kLog2e * x));
 }
 
-// Raw inputs of tensor `x` (one of q, k, v) for tokens t in [t_first - 3, t_first + TOK),
-// channels [ch, ch + 8).  Tokens < 0 read the carried state, tokens >= T read 0.
-template <int TOK, typename IO>
-__device__ __forceinline__ void load_window(const IO* x, const IO* state, int tensor, int b,
-                                            int T, int H, int D, int h, int ch, int t_first,
-                                            float (&win)[TOK + 3][8]) {
-  const size_t HD = (size_t)H * D;
-#pragma unroll
-  for (int m = 0; m < TOK + 3; ++m) {
-    const int t = t_first - 3 + m;
-    if (t >= 0 && t < T) {
-      load8(x + ((size_t)b * T + t) * HD + (size_t)h * D + ch, win[m]);
-    } else if (t < 0 && state != nullptr) {
-      // state layout [B][3 tensors][3 taps][H*D], oldest tap first
-      load8(state + (((size_t)b * 3 + tensor) * 3 + (3 + t)) * HD + (size_t)h * D + ch, win[m]);
-    } else {
-#pragma unroll
-      for (int c = 0; c < 8; ++c) win[m][c] = 0.f;
+// 8 consecutive elements kept unconverted while their load is in flight.
+template <typename IO> struct Raw8;
+template <> struct Raw8<__bf16> {
+  bf16x8 v;
+  __device__ __forceinline__ void load(const __bf16* p) { v = *reinterpret_cast<const bf16x8*>(p); }
+  __device__ __forceinline__ float operator[](int c) const { return (float)v[c]; }
+};
+template <> struct Raw8<float> {
+  f32x4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const f32x4*>(p);
+    b = *reinterpret_cast<const f32x4*>(p + 4);
+  }
+  __device__ __forceinline__ float operator[](int c) const { return c < 4 ? a[c] : b[c - 4]; }
+};
+
+// Filters of head h, [3 tensors][D channels][4 taps] float32 (3*D entries of 16
+// bytes), copied to LDS `dst` with the direct global-to-LDS path.  Called by all
+// NT threads of the block; the copy is complete after the caller's next
+// s_waitcnt vmcnt(0) and barrier.
+template <int D, int NT>
+__device__ __forceinline__ void stage_filters(const float* conv_w, int H, int h, float* dst, int tid) {
+  constexpr int N = 3 * D;
+  const int lane = tid & 63;
+  for (int base = tid - lane; base < N; base += NT) {  // wave-uniform
+    const int e = base + lane;
+    if (e < N) {
+      const int x = e / D, c = e % D;
+      __builtin_amdgcn_global_load_lds(
+          (const glb_void_t*)(conv_w + ((size_t)x * H * D + (size_t)h * D + c) * 4),
+          (lds_void_t*)(dst + 4 * base), 16, 0, 0);
     }
   }
 }
 
-// conv + SiLU for TOK tokens x 8 channels of one tensor.  With conv_w == NULL
-// (conv_k == 0) the raw inputs are passed through.  Outputs of tokens >= T are 0.
+// Raw rows of q, k, v (x = 0, 1, 2) for one thread's tile of TOK tokens from
+// t_first, channels [ch, ch + 8) of head h.  With the convolution, row m holds
+// token t_first - 3 + m (TOK + 3 rows); tokens < 0 read the carried state
+// ([B][3 tensors][3 taps][H*D], oldest tap first).  Without it, row 3 + m holds
+// token t_first + m.  Rows that read nothing (tokens >= T, or < 0 with no state)
+// load a valid row and are zeroed by front_compute, so every load is issued
+// unconditionally and all of them are in flight together.  Needs T > 0.
 template <int TOK, typename IO>
-__device__ __forceinline__ void conv_silu_tile(const IO* x, const IO* state, const float* conv_w,
-                                               int tensor, int b, int T, int H, int D, int h,
-                                               int ch, int t_first, bool active,
-                                               float (&y)[TOK][8]) {
-  if (!active) {
+__device__ __forceinline__ void front_load(const IO* q, const IO* k, const IO* v, const IO* state,
+                                           bool conv, int b, int T, int H, int D, int h, int ch,
+                                           int t_first, Raw8<IO> (&win)[3][TOK + 3]) {
+  const size_t HD = (size_t)H * D;
+  const size_t row0 = (size_t)b * T * HD + (size_t)h * D + ch;
+  const IO* src[3] = {q, k, v};
+  if (conv) {
 #pragma unroll
-    for (int m = 0; m < TOK; ++m)
+    for (int x = 0; x < 3; ++x) {
+      const IO* srow = state == nullptr ? src[x] + row0
+                                        : state + ((size_t)b * 3 + x) * 3 * HD + (size_t)h * D + ch;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) y[m][c] = 0.f;
-    return;
-  }
-  if (conv_w == nullptr) {
-#pragma unroll
-    for (int m = 0; m < TOK; ++m) {
-      const int t = t_first + m;
-      if (t < T) {
-        load8(x + ((size_t)b * T + t) * ((size_t)H * D) + (size_t)h * D + ch, y[m]);
-      } else {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) y[m][c] = 0.f;
+      for (int m = 0; m < TOK + 3; ++m) {
+        const int t = t_first - 3 + m;
+        const bool in_seq = t >= 0 && t < T;
+        const bool in_state = t < 0 && state != nullptr;
+        const IO* ptr = in_seq ? src[x] + row0 + (size_t)t * HD
+                               : (in_state ? srow + (size_t)(3 + t) * HD : src[x] + row0);
+        win[x][m].load(ptr);
       }
     }
-    return;
-  }
-  float win[TOK + 3][8];
-  load_window<TOK, IO>(x, state, tensor, b, T, H, D, h, ch, t_first, win);
-  const size_t HD = (size_t)H * D;
-  const float* wt = conv_w + ((size_t)tensor * HD + (size_t)h * D + ch) * 4;
+  } else {
 #pragma unroll
-  for (int c = 0; c < 8; ++c) {
-    const f32x4 w = *reinterpret_cast<const f32x4*>(wt + 4 * c);
+    for (int x = 0; x < 3; ++x)
 #pragma unroll
-    for (int m = 0; m < TOK; ++m) {
-      // output token t_first + m uses window rows m .. m + 3 (inputs t - 3 .. t)
-      float acc = w[0] * win[m][c];
-      acc = fmaf(w[1], win[m + 1][c], acc);
-      acc = fmaf(w[2], win[m + 2][c], acc);
-      acc = fmaf(w[3], win[m + 3][c], acc);
-      y[m][c] = (t_first + m < T) ? silu_fast(acc) : 0.f;
-    }
+      for (int m = 0; m < TOK; ++m) {
+        const int t = t_first + m;
+        win[x][3 + m].load(src[x] + row0 + (size_t)(t < T ? t : T - 1) * HD);
+      }
   }
 }
 
-// Full front end for q, k, v of one tile.  All lanes of a group of D/8 consecutive
-// lanes (the channels of one token row) must call this together: the L2 sums are
-// reduced across that group.  On return q is normalised and multiplied by
-// `scale`, k normalised, v convolved; qk[m] = <q_m, k_m> of the returned values.
+// conv + SiLU + L2 norm of the rows front_load fetched.  `filt` is the head's
+// [3][D][4] filter block (LDS or global; unused without the convolution).  All
+// lanes of a group of D/8 consecutive lanes (the channels of one token row) must
+// call this together: the L2 sums are reduced across that group.  On return q is
+// normalised and multiplied by `scale`, k normalised, v convolved; qk[m] =
+// <q_m, k_m> of the returned values.  Tokens >= T and inactive lanes give zeros.
 template <int TOK, int D, typename IO>
-__device__ __forceinline__ void conv_norm_tile(const IO* q, const IO* k, const IO* v,
-                                               const IO* state, const float* conv_w, int b, int T,
-                                               int H, int h, int ch, int t_first, bool active,
-                                               bool l2, float eps, float scale,
-                                               float (&yq)[TOK][8], float (&yk)[TOK][8],
-                                               float (&yv)[TOK][8], float (&qk)[TOK]) {
-  conv_silu_tile<TOK, IO>(q, state, conv_w, 0, b, T, H, D, h, ch, t_first, active, yq);
-  conv_silu_tile<TOK, IO>(k, state, conv_w, 1, b, T, H, D, h, ch, t_first, active, yk);
-  conv_silu_tile<TOK, IO>(v, state, conv_w, 2, b, T, H, D, h, ch, t_first, active, yv);
+__device__ __forceinline__ void front_compute(const Raw8<IO> (&win)[3][TOK + 3], const float* filt,
+                                              bool conv, bool has_state, int ch, int t_first,
+                                              int T, bool active, bool l2, float eps, float scale,
+                                              float (&yq)[TOK][8], float (&yk)[TOK][8],
+                                              float (&yv)[TOK][8], float (&qk)[TOK]) {
+  float (*y[3])[8] = {yq, yk, yv};
+#pragma unroll
+  for (int x = 0; x < 3; ++x) {
+    if (conv) {
+      float rows[TOK + 3][8];
+#pragma unroll
+      for (int m = 0; m < TOK + 3; ++m) {
+        const int t = t_first - 3 + m;
+        const bool ok = (t >= 0 && t < T) || (t < 0 && has_state);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) rows[m][c] = ok ? win[x][m][c] : 0.f;
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const f32x4 w = *reinterpret_cast<const f32x4*>(filt + ((size_t)x * D + ch + c) * 4);
+#pragma unroll
+        for (int m = 0; m < TOK; ++m) {
+          // output token t_first + m uses rows m .. m + 3 (inputs t - 3 .. t)
+          float acc = w[0] * rows[m][c];
+          acc = fmaf(w[1], rows[m + 1][c], acc);
+          acc = fmaf(w[2], rows[m + 2][c], acc);
+          acc = fmaf(w[3], rows[m + 3][c], acc);
+          y[x][m][c] = (active && t_first + m < T) ? silu_fast(acc) : 0.f;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < TOK; ++m)
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          y[x][m][c] = (active && t_first + m < T) ? win[x][3 + m][c] : 0.f;
+    }
+  }
   constexpr int G = D / 8;  // lanes sharing one token row
 #pragma unroll
   for (int m = 0; m < TOK; ++m) {

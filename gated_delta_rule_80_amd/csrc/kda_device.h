@@ -24,6 +24,10 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
+// Address-space-qualified pointers for the direct global-to-LDS copy builtin.
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
 // ---------------------------------------------------------------- conversions
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ float to_f32(__bf16 x) { return (float)x; }

@@ -37,29 +37,42 @@ constexpr float kFatalSpan2 = 240.f;  // log2 units (~166 nats): midpoint refere
 
 template <int D, int C, typename E>
 struct FastSmem {
-  static constexpr int PE = 16 / (int)sizeof(E);  // 16-byte row padding, in elements
-  static constexpr int LQ = D + PE;               // operand rows (k = channel)
-  static constexpr int LT = C + PE;               // transposed rows (k = token)
-  static constexpr int LA = C + 4;                // A and T rows (floats)
-  static constexpr int NB = C / 16;               // 16-token blocks
+  static constexpr int ES = (int)sizeof(E);
+  static constexpr int PE = 16 / ES;               // 16-byte row padding, in elements
+  static constexpr int KP = D >= 64 ? 2 : 1;       // passes over halves of the channels
+  static constexpr int DH = D / KP;                // channels per pass
+  static constexpr int LQ = DH + PE;               // operand rows (k = channel)
+  static constexpr int LT = C + PE;                // rows of T in E (k = token)
+  static constexpr int LA = C + 4;                 // A and T rows (floats)
+  static constexpr int NB = C / 16;                // 16-token blocks
   static constexpr int NPAIR = (NB - 1) * (NB - 2) / 2 > 0 ? (NB - 1) * (NB - 2) / 2 : 1;
-  // operand arrays, 6 x [C][LQ] in E:
-  //   RA = beta k a, RP = q a (rows i);  CB = k b (rows j, blocks below the diagonal);
-  //   CD = k / a (rows j, diagonal); RAd, RPd (rows i, diagonal; equal RA, RP on
-  //   channels that use the block-start reference).
-  // The same region holds the segment totals first and A, T, scratch, T in E last.
-  static constexpr int OPS = 6 * C * LQ * (int)sizeof(E);
-  static constexpr int TB_OFF = (2 * C * LA + 4 * 16 * 17) * 4;
-  static constexpr int SOLVE = TB_OFF + C * LT * (int)sizeof(E);
-  static constexpr int R1 = OPS > SOLVE ? OPS : SOLVE;
+  // One region, used in turn for:
+  //   the segment totals of the decay scan;
+  //   6 operand arrays [C][LQ] for one channel pass:
+  //     RA = beta k a, RP = q a (rows i);  CB = k b (rows j, blocks below the diagonal);
+  //     CD = k / a (rows j, diagonal); RAd, RPd (rows i, diagonal; equal RA, RP on
+  //     channels on the block-start reference);
+  //   A, T (float), the solve's scratch and T in E;
+  //   (beta K Lambda)^T and (beta V)^T as swizzled [D][C] images, next to T in E.
+  static constexpr int OPS = 6 * C * LQ * ES;
+  static constexpr int TOT = (C / 2) * D * 4;
+  static constexpr int SOLVE = (2 * C * LA + 4 * 16 * 17) * 4;
+  static constexpr int IMGS = 2 * D * C * ES;   // the two transposed images
+  static constexpr int KLT_OFF = 0;              // written after the solve
+  static constexpr int VT_OFF = D * C * ES;
+  // T in E, [C][LT], clear of both the float solve arrays and the images
+  static constexpr int TB_OFF = ((SOLVE > IMGS ? SOLVE : IMGS) + 15) / 16 * 16;
+  static constexpr int TB_BYTES = C * LT * ES;
+  static constexpr int LAST = TB_OFF + TB_BYTES;
+  static constexpr int R1a = OPS > TOT ? OPS : TOT;
+  static constexpr int R1 = R1a > LAST ? R1a : LAST;
   alignas(16) char r1[R1];
-  alignas(16) E klt[D * LT];           // (diag(beta) K Lambda)^T
-  alignas(16) E vt[D * LT];            // (diag(beta) V)^T
   alignas(16) float gb[(NB + 1) * D];  // log2 decay at block boundaries: gb[p] = Gamma before block p
   alignas(16) float esp[NB * D];       // exp(G_p - G_{p+1}) for channels on the block-start reference
   alignas(16) float eb[NB * D];        // exp(G_p)
   alignas(16) float ec[NB * D];        // exp(Gamma_C - G_{p+1})
   alignas(16) float mpq[NPAIR * D];    // exp(G_p - G_{q+1}) for block pairs p - q >= 2
+  alignas(16) float filt[3 * D * 4];   // the head's conv filters [q, k, v][D][4]
   int fatal;
 };
 
@@ -84,15 +97,42 @@ __device__ __forceinline__ void scale_k(RowFrag<float, K>& fr, const float* f, i
   for (int i = 0; i < RowFrag<float, K>::N; ++i) fr.v[i] *= f[4 * i + g];
 }
 
+// Swizzled image of a [rows][C] matrix used as a matrix-core operand along its
+// rows: 16-byte chunk c of row `row` sits at c ^ ((row ^ (row >> 3)) % RC).  Both
+// the transposed stores that build it (consecutive rows 8 apart per lane group)
+// and the fragment reads (16 consecutive rows) spread over the banks.
+template <typename E, int C>
+struct TImg {
+  static constexpr int EPC = 16 / (int)sizeof(E);
+  static constexpr int RC = C / EPC;
+  __device__ __forceinline__ static int at(int row, int k) {
+    return row * C + (((k / EPC) ^ ((row ^ (row >> 3)) & (RC - 1))) * EPC) + (k % EPC);
+  }
+};
+
+template <int K, typename E>
+__device__ __forceinline__ void load_timg(RowFrag<E, K>& f, const E* img, int row, int g) {
+  using FR = RowFrag<E, K>;
+  if constexpr (sizeof(E) == 2) {
+#pragma unroll
+    for (int i = 0; i < FR::N; ++i)
+      f.v[i] = *reinterpret_cast<const typename FR::V*>(img + TImg<E, K>::at(row, i * FR::STEP + FR::PER * g));
+  } else {
+#pragma unroll
+    for (int i = 0; i < FR::N; ++i) f.v[i] = img[TImg<E, K>::at(row, 4 * i + g)];
+  }
+}
+
 template <int D, int C, typename IO, typename E>
-__global__ __launch_bounds__(kFastThreads) void kda_chunk_prep_kernel(PrepParams p) {
+__global__ __launch_bounds__(kFastThreads, 1) void kda_chunk_prep_kernel(PrepParams p) {
   using SM = FastSmem<D, C, E>;
   __shared__ SM sm;
-  constexpr int LQ = SM::LQ, LT = SM::LT, LA = SM::LA, NB = SM::NB;
+  constexpr int LQ = SM::LQ, LT = SM::LT, LA = SM::LA, NB = SM::NB, KP = SM::KP, DH = SM::DH;
   constexpr int NOCT = D / 8;          // 8-channel groups per token row
   constexpr int NSEG = C / 2;          // 2-token segments
   constexpr int ITEMS = NSEG * NOCT;   // <= 512
   static_assert(ITEMS <= kFastThreads, "tile does not fit one pass");
+  static_assert(SM::TOT <= SM::R1, "segment totals fit the region");
   constexpr RecordLayout RL = record_layout(C, D, sizeof(E));
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -123,31 +163,40 @@ __global__ __launch_bounds__(kFastThreads) void kda_chunk_prep_kernel(PrepParams
   const int ch = 8 * j;
   const int pb = s / 8;                   // 16-token block of this segment
   const int tf = t0 + 2 * s;
-  float yq[2][8], yk[2][8], yv[2][8], qk[2];
-  conv_norm_tile<2, D, IO>(static_cast<const IO*>(p.q), static_cast<const IO*>(p.k),
-                           static_cast<const IO*>(p.v), static_cast<const IO*>(p.conv_state_in),
-                           p.conv_w, b, p.T, p.H, h, ch, tf, active, p.l2 != 0, p.eps, p.scale,
-                           yq, yk, yv, qk);
+  const int mypass = j / (NOCT / KP);     // channel pass that stores this thread's operands
+  // every global load of this phase is issued before the first wait: the head's
+  // filters (straight to LDS), the q/k/v windows, g and beta
+  const bool conv = p.conv_w != nullptr;
+  if (conv) stage_filters<D, kFastThreads>(p.conv_w, p.H, h, sm.filt, tid);
+  Raw8<IO> win[3][5];
+  front_load<2, IO>(static_cast<const IO*>(p.q), static_cast<const IO*>(p.k),
+                    static_cast<const IO*>(p.v), static_cast<const IO*>(p.conv_state_in), conv, b,
+                    p.T, p.H, D, h, ch, tf, win);
   float g2[2][8], bt[2];
   const size_t HD = (size_t)p.H * D;
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
+    // clamped token, zeroed past the end below
     const int t = tf + m;
-    if (active && t < p.T) {
-      load8(static_cast<const IO*>(p.g) + ((size_t)b * p.T + t) * HD + (size_t)h * D + ch, g2[m]);
-      bt[m] = to_f32(static_cast<const IO*>(p.beta)[((size_t)b * p.T + t) * p.H + h]);
-    } else {
+    const int tc = t < p.T ? t : p.T - 1;
+    load8(static_cast<const IO*>(p.g) + ((size_t)b * p.T + tc) * HD + (size_t)h * D + ch, g2[m]);
+    bt[m] = to_f32(static_cast<const IO*>(p.beta)[((size_t)b * p.T + tc) * p.H + h]);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();  // filters are in LDS
+  float yq[2][8], yk[2][8], yv[2][8], qk[2];
+  front_compute<2, D, IO>(win, sm.filt, conv, p.conv_state_in != nullptr, ch, tf, p.T, active,
+                          p.l2 != 0, p.eps, p.scale, yq, yk, yv, qk);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) g2[m][c] = 0.f;
-      bt[m] = 0.f;
-    }
+  for (int m = 0; m < 2; ++m) {
+    const bool ok = active && tf + m < p.T;
+    bt[m] = ok ? bt[m] : 0.f;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) g2[m][c] *= kLog2e;  // decay in log2 units from here on
+    for (int c = 0; c < 8; ++c) g2[m][c] = ok ? g2[m][c] * kLog2e : 0.f;  // log2 units from here on
   }
 #pragma unroll
   for (int c = 0; c < 8; ++c) g2[1][c] += g2[0][c];
-  float* tot = reinterpret_cast<float*>(RAd);  // [NSEG][D] segment totals, later exclusive prefixes
-  static_assert(NSEG * D * 4 <= 2 * C * LQ * (int)sizeof(E), "segment totals fit RAd/RPd");
+  float* tot = reinterpret_cast<float*>(sm.r1);  // [NSEG][D] segment totals, then exclusive prefixes
   if (tid == 0) sm.fatal = 0;
   if (active) store8(tot + s * D + ch, g2[1]);
   __syncthreads();
@@ -190,7 +239,10 @@ __global__ __launch_bounds__(kFastThreads) void kda_chunk_prep_kernel(PrepParams
     }
     return;
   }
-  float rad[2][8], rpd[2][8];
+  // operands of this thread's 2 tokens x 8 channels, kept until its channel pass;
+  // (beta K Lambda) and (beta V) kept until the transposed images are built
+  E op[6][2][8];
+  E kv[2][2][8];
   if (active) {
     float pre[8], gp[8], gq[8], esp[8], eb[8], ec[8];
     load8(tot + s * D + ch, pre);
@@ -206,23 +258,25 @@ __global__ __launch_bounds__(kFastThreads) void kda_chunk_prep_kernel(PrepParams
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       const int tl = 2 * s + m;
-      float ra[8], rp[8], cb[8], cd[8], ql[8];
+      float ql[8];
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         const float gam = g2[m][c] + pre[c];
         const float a = __builtin_amdgcn_exp2f(gam - gp[c]);
         const float bb = __builtin_amdgcn_exp2f(gq[c] - gam);
-        const float bk = bt[m] * yk[m][c];
-        ra[c] = bk * a;
-        rp[c] = yq[m][c] * a;
-        cb[c] = yk[m][c] * bb;
-        cd[c] = cb[c] * esp[c];
-        ql[c] = rp[c] * eb[c];
-        kt[m][c] = cb[c] * ec[c];
-        rad[m][c] = ra[c];
-        rpd[m][c] = rp[c];
-        sm.klt[(ch + c) * LT + tl] = from_f32<E>(ra[c] * eb[c]);
-        sm.vt[(ch + c) * LT + tl] = from_f32<E>(bt[m] * yv[m][c]);
+        const float ra = bt[m] * yk[m][c] * a;
+        const float rp = yq[m][c] * a;
+        const float cb = yk[m][c] * bb;
+        op[0][m][c] = from_f32<E>(ra);
+        op[1][m][c] = from_f32<E>(rp);
+        op[2][m][c] = from_f32<E>(cb);
+        op[3][m][c] = from_f32<E>(cb * esp[c]);
+        op[4][m][c] = op[0][m][c];
+        op[5][m][c] = op[1][m][c];
+        ql[c] = rp * eb[c];
+        kt[m][c] = cb * ec[c];
+        kv[0][m][c] = from_f32<E>(ra * eb[c]);
+        kv[1][m][c] = from_f32<E>(bt[m] * yv[m][c]);
       }
       if (any_wide) {
         // channels whose block span is too wide for exp(+span): midpoint reference
@@ -232,33 +286,22 @@ __global__ __launch_bounds__(kFastThreads) void kda_chunk_prep_kernel(PrepParams
             const float gam = g2[m][c] + pre[c];
             const float mid = 0.5f * (gp[c] + gq[c]);
             const float ad = __builtin_amdgcn_exp2f(gam - mid);
-            rad[m][c] = bt[m] * yk[m][c] * ad;
-            rpd[m][c] = yq[m][c] * ad;
-            cd[c] = yk[m][c] * __builtin_amdgcn_exp2f(mid - gam);
+            op[4][m][c] = from_f32<E>(bt[m] * yk[m][c] * ad);
+            op[5][m][c] = from_f32<E>(yq[m][c] * ad);
+            op[3][m][c] = from_f32<E>(yk[m][c] * __builtin_amdgcn_exp2f(mid - gam));
           }
         }
       }
-      store8(RA + tl * LQ + ch, ra);
-      store8(RP + tl * LQ + ch, rp);
-      store8(CB + tl * LQ + ch, cb);
-      store8(CD + tl * LQ + ch, cd);
       store8(gQL + (size_t)tl * D + ch, ql);
     }
 #pragma unroll
     for (int c = 0; c < 8; ++c) store2(gKT + (size_t)(ch + c) * C + 2 * s, kt[0][c], kt[1][c]);
   }
   __syncthreads();  // every read of the segment prefixes is done
-  if (active) {
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      store8(RAd + (2 * s + m) * LQ + ch, rad[m]);
-      store8(RPd + (2 * s + m) * LQ + ch, rpd[m]);
-    }
-  }
-  __syncthreads();
 
   // ---------------------------------------------------------------- phase 2
-  // A^T / P^T tiles (rows j, columns i), lower block triangle, round robin over waves
+  // A^T / P^T tiles (rows j, columns i), lower block triangle, round robin over
+  // waves, accumulated over the channel passes
   constexpr int NTILE = NB * (NB + 1) / 2;
   constexpr int NW = kFastThreads / 64;
   constexpr int TPW = (NTILE + NW - 1) / NW;
@@ -272,23 +315,44 @@ __global__ __launch_bounds__(kFastThreads) void kda_chunk_prep_kernel(PrepParams
     tQ[i] = idx;
     accA[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     accP[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (tR[i] < 0) continue;
-    const int R0 = tR[i], Q0 = tQ[i];
-    RowFrag<E, D> cf, fa, fp;
-    if (R0 != Q0) {
-      cf.load(CB + (16 * Q0 + r) * LQ, g4);
-      if (R0 - Q0 >= 2) scale_k<D>(cf, &sm.mpq[pair_index(R0, Q0) * D], g4);
-      fa.load(RA + (16 * R0 + r) * LQ, g4);
-      fp.load(RP + (16 * R0 + r) * LQ, g4);
-    } else {
-      cf.load(CD + (16 * Q0 + r) * LQ, g4);
-      fa.load(RAd + (16 * R0 + r) * LQ, g4);
-      fp.load(RPd + (16 * R0 + r) * LQ, g4);
-    }
-    mma<D>(accA[i], cf, fa);
-    mma<D>(accP[i], cf, fp);
   }
-  __syncthreads();  // operands are dead from here on
+#pragma unroll
+  for (int kp = 0; kp < KP; ++kp) {
+    if (active && mypass == kp) {
+      const int cl = ch - kp * DH;  // channel inside this pass
+#pragma unroll
+      for (int a = 0; a < 6; ++a) {
+        E* dst = RA + a * C * LQ;
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          float tmp[8];
+#pragma unroll
+          for (int c = 0; c < 8; ++c) tmp[c] = to_f32(op[a][m][c]);
+          store8(dst + (2 * s + m) * LQ + cl, tmp);
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      if (tR[i] < 0) continue;
+      const int R0 = tR[i], Q0 = tQ[i];
+      RowFrag<E, DH> cf, fa, fp;
+      if (R0 != Q0) {
+        cf.load(CB + (16 * Q0 + r) * LQ, g4);
+        if (R0 - Q0 >= 2) scale_k<DH>(cf, &sm.mpq[pair_index(R0, Q0) * D + kp * DH], g4);
+        fa.load(RA + (16 * R0 + r) * LQ, g4);
+        fp.load(RP + (16 * R0 + r) * LQ, g4);
+      } else {
+        cf.load(CD + (16 * Q0 + r) * LQ, g4);
+        fa.load(RAd + (16 * R0 + r) * LQ, g4);
+        fp.load(RPd + (16 * R0 + r) * LQ, g4);
+      }
+      mma<DH>(accA[i], cf, fa);
+      mma<DH>(accP[i], cf, fp);
+    }
+    __syncthreads();  // this pass's operands are dead
+  }
 
   // ---------------------------------------------------------------- phase 3
   float* sA = reinterpret_cast<float*>(sm.r1);  // [C][LA]
@@ -363,67 +427,95 @@ __global__ __launch_bounds__(kFastThreads) void kda_chunk_prep_kernel(PrepParams
     }
     __syncthreads();
   }
-  // T in the matrix-core element type
-  const E* Tb;
-  int LTB;
-  if constexpr (sizeof(E) == 4) {
-    Tb = reinterpret_cast<const E*>(sT);
-    LTB = LA;
-  } else {
-    E* tb = reinterpret_cast<E*>(sm.r1 + SM::TB_OFF);
-    for (int it = tid; it < C * C; it += kFastThreads) {
-      const int i = it / C, jj = it % C;
-      tb[i * LT + jj] = from_f32<E>(sT[i * LA + jj]);
-    }
-    Tb = tb;
-    LTB = LT;
-    __syncthreads();
+  // T in the matrix-core element type, after A / T / scratch
+  E* tb = reinterpret_cast<E*>(sm.r1 + SM::TB_OFF);
+  for (int it = tid; it < C * C; it += kFastThreads) {
+    const int i = it / C, jj = it % C;
+    tb[i * LT + jj] = from_f32<E>(sT[i * LA + jj]);
   }
+  __syncthreads();  // A and T (float) are dead
 
   // ---------------------------------------------------------------- phase 5
-  // W^T tiles (c, i): A = (beta K Lambda)^T rows c, B^T = T rows i (j <= i)
+  // (beta K Lambda)^T and (beta V)^T as swizzled [D][C] images
+  E* klt = reinterpret_cast<E*>(sm.r1 + SM::KLT_OFF);
+  E* vt = reinterpret_cast<E*>(sm.r1 + SM::VT_OFF);
+  static_assert(SM::IMGS <= SM::TB_OFF, "transposed images stay clear of T");
+  if (active) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int row = ch + c;
+      const int at = TImg<E, C>::at(row, 2 * s);
+      if constexpr (sizeof(E) == 2) {
+        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+        *reinterpret_cast<bf16x2*>(klt + at) = bf16x2{kv[0][0][c], kv[0][1][c]};
+        *reinterpret_cast<bf16x2*>(vt + at) = bf16x2{kv[1][0][c], kv[1][1][c]};
+      } else {
+        *reinterpret_cast<float2*>(klt + at) = make_float2(kv[0][0][c], kv[0][1][c]);
+        *reinterpret_cast<float2*>(vt + at) = make_float2(kv[1][0][c], kv[1][1][c]);
+      }
+    }
+  }
+  __syncthreads();
+  // W^T tiles (c, i): A = (beta K Lambda)^T rows c, B = T rows i (j <= i)
   constexpr int NWT = (D / 16) * NB;
+  constexpr int STEPC = RowFrag<E, C>::STEP;
   for (int tt = wave; tt < NWT; tt += NW) {
     const int Ct = tt / NB, It = tt % NB;
+    RowFrag<E, C> fa, fb;
+    load_timg<C>(fa, klt, 16 * Ct + r, g4);
+    fb.load(tb + (16 * It + r) * LT, g4);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    mma_rows_upto<C>(acc, sm.klt + 16 * Ct * LT, LT, Tb + 16 * It * LTB, LTB, lane, 16 * It + 16);
+    mma<C>(acc, fa, fb, (16 * It + 16 + STEPC - 1) / STEPC);
     const int i = 16 * It + r, c = 16 * Ct + 4 * g4;
     store4(gW + (size_t)i * D + c, acc[0], acc[1], acc[2], acc[3]);
   }
-  // U~ tiles (i, v): A = T rows i, B^T = (beta V)^T rows v; stored in fragment order
+  // U~ tiles (i, v): A = T rows i, B = (beta V)^T rows v; stored in fragment order
   for (int tt = wave; tt < NWT; tt += NW) {
     const int It = tt / (D / 16), Vt = tt % (D / 16);
+    RowFrag<E, C> fa, fb;
+    fa.load(tb + (16 * It + r) * LT, g4);
+    load_timg<C>(fb, vt, 16 * Vt + r, g4);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    mma_rows_upto<C>(acc, Tb + 16 * It * LTB, LTB, sm.vt + 16 * Vt * LT, LT, lane, 16 * It + 16);
+    mma<C>(acc, fa, fb, (16 * It + 16 + STEPC - 1) / STEPC);
     store4(gU + ((size_t)(It * (D / 16) + Vt) * 64 + lane) * 4, acc[0], acc[1], acc[2], acc[3]);
   }
 }
 
 // ------------------------------------------------------------ conv_norm alone
+// tokens per thread of the standalone front end (fp32 rows take twice the registers)
+template <typename IO> constexpr int conv_norm_tokens() { return sizeof(IO) == 2 ? 4 : 2; }
+
 template <int D, typename IO>
 __global__ __launch_bounds__(256) void kda_conv_norm_kernel(ConvNormParams p) {
   constexpr int NOCT = D / 8;
-  constexpr int TOK = 256 / NOCT * 4;  // tokens per workgroup
+  constexpr int TT = conv_norm_tokens<IO>();
+  constexpr int TOK = 256 / NOCT * TT;  // tokens per workgroup
+  __shared__ alignas(16) float filt[3 * D * 4];
   const int tid = threadIdx.x;
   const int nblk = (p.T + TOK - 1) / TOK;
   const int blk = blockIdx.x % nblk;
   const int bh = blockIdx.x / nblk;
   const int h = bh % p.H, b = bh / p.H;
   const int s = tid / NOCT, j = tid % NOCT;
-  const int tf = blk * TOK + 4 * s;
+  const int tf = blk * TOK + TT * s;
   const bool active = tf < p.T;
-  float yq[4][8], yk[4][8], yv[4][8], qk[4];
-  conv_norm_tile<4, D, IO>(static_cast<const IO*>(p.q), static_cast<const IO*>(p.k),
-                           static_cast<const IO*>(p.v), static_cast<const IO*>(p.conv_state_in),
-                           p.conv_w, b, p.T, p.H, h, 8 * j, tf, active, p.l2 != 0, p.eps, 1.0f,
-                           yq, yk, yv, qk);
+  stage_filters<D, 256>(p.conv_w, p.H, h, filt, tid);
+  Raw8<IO> win[3][TT + 3];
+  front_load<TT, IO>(static_cast<const IO*>(p.q), static_cast<const IO*>(p.k),
+                     static_cast<const IO*>(p.v), static_cast<const IO*>(p.conv_state_in), true, b,
+                     p.T, p.H, D, h, 8 * j, tf, win);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();  // filters are in LDS
+  float yq[TT][8], yk[TT][8], yv[TT][8], qk[TT];
+  front_compute<TT, D, IO>(win, filt, true, p.conv_state_in != nullptr, 8 * j, tf, p.T, active,
+                           p.l2 != 0, p.eps, 1.0f, yq, yk, yv, qk);
   if (!active) return;
   const size_t HD = (size_t)p.H * D;
   IO* oq = static_cast<IO*>(p.q_out);
   IO* ok = static_cast<IO*>(p.k_out);
   IO* ov = static_cast<IO*>(p.v_out);
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
+  for (int m = 0; m < TT; ++m) {
     const int t = tf + m;
     if (t >= p.T) break;
     const size_t off = ((size_t)b * p.T + t) * HD + (size_t)h * D + 8 * j;
@@ -521,7 +613,7 @@ hipError_t launch_prep(const PrepParams& p, int D, int C, bool fp32, hipStream_t
 
 template <int D, typename IO>
 static hipError_t launch_conv_norm_t(const ConvNormParams& p, hipStream_t st) {
-  constexpr int TOK = 256 / (D / 8) * 4;
+  constexpr int TOK = 256 / (D / 8) * conv_norm_tokens<IO>();
   const int nblk = (p.T + TOK - 1) / TOK;
   const unsigned grid = (unsigned)((size_t)p.B * p.H * nblk);
   hipLaunchKernelGGL((kda_conv_norm_kernel<D, IO>), dim3(grid), dim3(256), 0, st, p);

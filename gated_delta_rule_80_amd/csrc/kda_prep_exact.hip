@@ -65,6 +65,7 @@ struct PrepSmem {
   alignas(16) char r1[R1];
   float beta[C];
   float pd[C];  // diagonal of P
+  alignas(16) float filt[3 * D * 4];  // the head's conv filters [q, k, v][D][4]
 };
 
 template <int D, int C, typename IO, typename E>
@@ -109,22 +110,31 @@ __global__ __launch_bounds__(kPrepThreads) void kda_chunk_prep_exact_kernel(Prep
   const int j = tid % NOCT;
   const int ch = 8 * j;
   const int tf = t0 + 4 * s;  // first token of this thread's segment
-  float yq[4][8], yk[4][8], yv[4][8], qk[4];
-  conv_norm_tile<4, D, IO>(q, k, v, cs, p.conv_w, b, p.T, p.H, h, ch, tf, active, p.l2 != 0, p.eps,
-                        p.scale, yq, yk, yv, qk);
+  // every global load of this phase is issued before the first wait
+  const bool conv = p.conv_w != nullptr;
+  if (conv) stage_filters<D, kPrepThreads>(p.conv_w, p.H, h, sm.filt, tid);
+  Raw8<IO> win[3][7];
+  front_load<4, IO>(q, k, v, cs, conv, b, p.T, p.H, D, h, ch, tf, win);
   float gl[4][8], bt[4];
   const size_t HD = (size_t)p.H * D;
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     const int t = tf + m;
-    if (active && t < p.T) {
-      load8(gg + ((size_t)b * p.T + t) * HD + (size_t)h * D + ch, gl[m]);
-      bt[m] = to_f32(bb[((size_t)b * p.T + t) * p.H + h]);
-    } else {
+    const int tc = t < p.T ? t : p.T - 1;
+    load8(gg + ((size_t)b * p.T + tc) * HD + (size_t)h * D + ch, gl[m]);
+    bt[m] = to_f32(bb[((size_t)b * p.T + tc) * p.H + h]);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();  // filters are in LDS
+  float yq[4][8], yk[4][8], yv[4][8], qk[4];
+  front_compute<4, D, IO>(win, sm.filt, conv, cs != nullptr, ch, tf, p.T, active, p.l2 != 0,
+                          p.eps, p.scale, yq, yk, yv, qk);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) gl[m][c] = 0.f;
-      bt[m] = 0.f;
-    }
+  for (int m = 0; m < 4; ++m) {
+    const bool ok = active && tf + m < p.T;
+    bt[m] = ok ? bt[m] : 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) gl[m][c] = ok ? gl[m][c] : 0.f;
   }
   // cumulative log-decay: within the segment, then across segments
 #pragma unroll

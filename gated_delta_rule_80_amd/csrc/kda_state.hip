@@ -26,9 +26,6 @@ namespace kda {
 
 constexpr int kStateThreads = 256;
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glb_void_t;
-
 // 4 consecutive elements kept raw until used
 template <typename E> struct Raw4;
 template <> struct Raw4<__bf16> {
