@@ -99,8 +99,11 @@ __device__ __forceinline__ void front_load(const IO* q, const IO* k, const IO* v
 // lanes of a group of D/8 consecutive lanes (the channels of one token row) must
 // call this together: the L2 sums are reduced across that group.  On return q is
 // normalised and multiplied by `scale`, k normalised, v convolved; qk[m] =
-// <q_m, k_m> of the returned values.  Tokens >= T and inactive lanes give zeros.
-template <int TOK, int D, typename IO>
+// <q_m, k_m> of the returned values (0 unless WANT_QK).  With MASK, rows that
+// read nothing are zeroed here and tokens >= T and inactive lanes give zeros;
+// without it the rows must already hold zeros where nothing was read, and the
+// outputs of tokens >= T are left as computed (finite).
+template <int TOK, int D, typename IO, bool WANT_QK = true, bool MASK = true>
 __device__ __forceinline__ void front_compute(const Raw8<IO> (&win)[3][TOK + 3], const float* filt,
                                               bool conv, bool has_state, int ch, int t_first,
                                               int T, bool active, bool l2, float eps, float scale,
@@ -114,7 +117,7 @@ __device__ __forceinline__ void front_compute(const Raw8<IO> (&win)[3][TOK + 3],
 #pragma unroll
       for (int m = 0; m < TOK + 3; ++m) {
         const int t = t_first - 3 + m;
-        const bool ok = (t >= 0 && t < T) || (t < 0 && has_state);
+        const bool ok = !MASK || (t >= 0 && t < T) || (t < 0 && has_state);
 #pragma unroll
         for (int c = 0; c < 8; ++c) rows[m][c] = ok ? win[x][m][c] : 0.f;
       }
@@ -128,7 +131,7 @@ __device__ __forceinline__ void front_compute(const Raw8<IO> (&win)[3][TOK + 3],
           acc = fmaf(w[1], rows[m + 1][c], acc);
           acc = fmaf(w[2], rows[m + 2][c], acc);
           acc = fmaf(w[3], rows[m + 3][c], acc);
-          y[x][m][c] = (active && t_first + m < T) ? silu_fast(acc) : 0.f;
+          y[x][m][c] = (!MASK || (active && t_first + m < T)) ? silu_fast(acc) : 0.f;
         }
       }
     } else {
@@ -136,7 +139,7 @@ __device__ __forceinline__ void front_compute(const Raw8<IO> (&win)[3][TOK + 3],
       for (int m = 0; m < TOK; ++m)
 #pragma unroll
         for (int c = 0; c < 8; ++c)
-          y[x][m][c] = (active && t_first + m < T) ? win[x][3 + m][c] : 0.f;
+          y[x][m][c] = (!MASK || (active && t_first + m < T)) ? win[x][3 + m][c] : 0.f;
     }
   }
   constexpr int G = D / 8;  // lanes sharing one token row
@@ -150,8 +153,8 @@ __device__ __forceinline__ void front_compute(const Raw8<IO> (&win)[3][TOK + 3],
     }
     sq = group_sum<G>(sq);
     sk = group_sum<G>(sk);
-    const float rq = (l2 ? 1.0f / sqrtf(sq + eps) : 1.0f) * scale;
-    const float rk = l2 ? 1.0f / sqrtf(sk + eps) : 1.0f;
+    const float rq = (l2 ? __builtin_amdgcn_rsqf(sq + eps) : 1.0f) * scale;
+    const float rk = l2 ? __builtin_amdgcn_rsqf(sk + eps) : 1.0f;
     float d = 0.f;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
@@ -159,7 +162,7 @@ __device__ __forceinline__ void front_compute(const Raw8<IO> (&win)[3][TOK + 3],
       yk[m][c] *= rk;
       d = fmaf(yq[m][c], yk[m][c], d);
     }
-    qk[m] = group_sum<G>(d);
+    qk[m] = WANT_QK ? group_sum<G>(d) : 0.f;
   }
 }
 

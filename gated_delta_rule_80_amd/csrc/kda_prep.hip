@@ -1,6 +1,7 @@
-// Chunk preparation for the KDA prefill: one workgroup of 512 threads per
-// (sequence, head, chunk of C tokens).  Everything here is independent across
-// chunks; the serial dependence on the state is left to the state walk.
+// Chunk preparation for the KDA prefill: persistent workgroups of 512 threads,
+// one (sequence, head, chunk of C tokens) at a time, with the next chunk's inputs
+// copied to LDS while the current one computes.  Everything here is independent
+// across chunks; the serial dependence on the state is left to the state walk.
 //
 // Per chunk (Gamma = chunk-local cumulative sum of the log-decay g, per channel;
 // Lambda = exp(Gamma); all decays act on the key channels):
@@ -13,17 +14,15 @@
 // The triangular structure is the WY/UT form of the product of the generalised
 // Householder factors (I - beta k k^T) that the delta rule composes.
 //
-// Step 3 as matrix products over 16-token blocks p (all factors per channel):
-//   a_i = exp(Gamma_i - G_p)   for i in block p, G_p = Gamma just before block p  (<= 1)
-//   b_j = exp(G_{q+1} - Gamma_j) for j in block q, G_{q+1} = Gamma at its last token (<= 1)
-//   blocks p > q:  exp(Gamma_i - Gamma_j) = a_i * exp(G_p - G_{q+1}) * b_j, every factor <= 1,
-//                  so no factor overflows and an underflowed factor means a negligible term;
-//   block p = p:   exp(Gamma_i - Gamma_j) = a_i / a_j = a_i * b_j * exp(G_p - G_{p+1}),
-//                  representable while the block's decay span G_p - G_{p+1} stays below
-//                  ~80 nats; a channel above that uses its block's midpoint as the
-//                  reference instead (both factors within exp(+-span/2)).
-// A chunk with a span too large even for that (> ~166 nats in 16 tokens) is listed
-// in the workspace and recomputed by the exact preparation kernel.
+// Step 3 as matrix products over 16-token blocks, per channel: with G_p the
+// cumulative decay just before block p and m_p = (G_p + G_{p+1}) / 2 the middle
+// of the block's range,
+//   a_i = exp(Gamma_i - m_p) for i in block p,   b_j = exp(m_q - Gamma_j) for j in block q,
+//   exp(Gamma_i - Gamma_j) = a_i * exp(m_p - m_q) * b_j,
+// where the pair factor is 1 on the diagonal (p = q) and <= 1 below it.  a and b
+// lie within exp(+-s/2) for a block decay span s, so every factor is representable
+// in fp32/bf16 while s stays below ~166 nats; a chunk with a wider block span is
+// listed in the workspace and recomputed by the exact preparation kernel.
 #include "kda_convnorm.h"
 #include "kda_device.h"
 #include "kda_launch.h"
@@ -32,53 +31,142 @@
 namespace kda {
 
 constexpr int kFastThreads = 512;
-constexpr float kSafeSpan2 = 112.f;   // log2 units (~78 nats): boundary references
-constexpr float kFatalSpan2 = 240.f;  // log2 units (~166 nats): midpoint references
+constexpr float kFatalSpan2 = 240.f;  // log2 units (~166 nats): widest block span factored
 
 template <int D, int C, typename E>
 struct FastSmem {
   static constexpr int ES = (int)sizeof(E);
   static constexpr int PE = 16 / ES;               // 16-byte row padding, in elements
-  static constexpr int KP = D >= 64 ? 2 : 1;       // passes over halves of the channels
-  static constexpr int DH = D / KP;                // channels per pass
-  static constexpr int LQ = DH + PE;               // operand rows (k = channel)
+  static constexpr int LQ = D + PE;                // operand rows (k = channel)
   static constexpr int LT = C + PE;                // rows of T in E (k = token)
   static constexpr int LA = C + 4;                 // A and T rows (floats)
   static constexpr int NB = C / 16;                // 16-token blocks
-  static constexpr int NPAIR = (NB - 1) * (NB - 2) / 2 > 0 ? (NB - 1) * (NB - 2) / 2 : 1;
-  // One region, used in turn for:
-  //   the segment totals of the decay scan;
-  //   6 operand arrays [C][LQ] for one channel pass:
-  //     RA = beta k a, RP = q a (rows i);  CB = k b (rows j, blocks below the diagonal);
-  //     CD = k / a (rows j, diagonal); RAd, RPd (rows i, diagonal; equal RA, RP on
-  //     channels on the block-start reference);
+  static constexpr int NPAIR = NB * (NB - 1) / 2 > 0 ? NB * (NB - 1) / 2 : 1;
+  // One region, used in turn for
+  //   the operand arrays [C][LQ]: RA = beta k a (rows i), RP = q a (rows i),
+  //     CB = k b (rows j), with a, b the block-midpoint decay factors;
   //   A, T (float), the solve's scratch and T in E;
   //   (beta K Lambda)^T and (beta V)^T as swizzled [D][C] images, next to T in E.
-  static constexpr int OPS = 6 * C * LQ * ES;
-  static constexpr int TOT = (C / 2) * D * 4;
+  static constexpr int OPS = 3 * C * LQ * ES;
   static constexpr int SOLVE = (2 * C * LA + 4 * 16 * 17) * 4;
-  static constexpr int IMGS = 2 * D * C * ES;   // the two transposed images
-  static constexpr int KLT_OFF = 0;              // written after the solve
+  static constexpr int IMGS = 2 * D * C * ES;
+  static constexpr int KLT_OFF = 0;
   static constexpr int VT_OFF = D * C * ES;
-  // T in E, [C][LT], clear of both the float solve arrays and the images
   static constexpr int TB_OFF = ((SOLVE > IMGS ? SOLVE : IMGS) + 15) / 16 * 16;
-  static constexpr int TB_BYTES = C * LT * ES;
-  static constexpr int LAST = TB_OFF + TB_BYTES;
-  static constexpr int R1a = OPS > TOT ? OPS : TOT;
-  static constexpr int R1 = R1a > LAST ? R1a : LAST;
+  static constexpr int LAST = TB_OFF + C * LT * ES;
+  static constexpr int R1 = OPS > LAST ? OPS : LAST;
   alignas(16) char r1[R1];
-  alignas(16) float gb[(NB + 1) * D];  // log2 decay at block boundaries: gb[p] = Gamma before block p
-  alignas(16) float esp[NB * D];       // exp(G_p - G_{p+1}) for channels on the block-start reference
-  alignas(16) float eb[NB * D];        // exp(G_p)
-  alignas(16) float ec[NB * D];        // exp(Gamma_C - G_{p+1})
-  alignas(16) float mpq[NPAIR * D];    // exp(G_p - G_{q+1}) for block pairs p - q >= 2
-  alignas(16) float filt[3 * D * 4];   // the head's conv filters [q, k, v][D][4]
+  alignas(16) float tot[(C / 2) * D];  // 2-token segment totals, then exclusive prefixes
+  alignas(16) float gb[(NB + 1) * D];  // Gamma at block boundaries: gb[p] = Gamma before block p
+  alignas(16) float mid[NB * D];       // block midpoints (gb[p] + gb[p + 1]) / 2
+  alignas(16) float mpq[NPAIR * D];    // exp(mid[R] - mid[Q]) for blocks R > Q
   int fatal;
 };
 
 __device__ __forceinline__ int pair_index(int R, int Q) {
-  // pairs (R, Q) with R - Q >= 2 in the order (2,0), (3,0), (3,1), (4,0), ...
-  return (R - 2) * (R - 1) / 2 + Q;
+  // pairs R > Q in the order (1,0), (2,0), (2,1), (3,0), ...
+  return R * (R - 1) / 2 + Q;
+}
+
+// Inputs of one chunk, copied to LDS ahead of use with the direct global-to-LDS
+// path (16 bytes per lane): the q/k/v rows of tokens t0 - 3 .. t0 + C - 1 (the
+// conv window; rows before the sequence come from the carried conv state), the
+// g rows, and the head's conv filters.  beta goes through registers.
+template <int D, int C, typename IO>
+struct ChunkStage {
+  static constexpr int CPR = D * (int)sizeof(IO) / 16;  // 16-byte pieces per row
+  static constexpr int XR = C + 3;                      // window rows per tensor
+  static constexpr int NX = 3 * XR * CPR;
+  static constexpr int NG = C * CPR;
+  static constexpr int NF = 3 * D;                      // one piece = 4 taps of a channel
+  alignas(16) IO x[3][XR][D];
+  alignas(16) IO g[C][D];
+  alignas(16) float filt[3][D][4];
+  float beta[C];
+};
+
+// 16 zero bytes: the copy source of every staged piece that reads nothing.
+__device__ __attribute__((aligned(16))) const unsigned kZero16[4] = {0u, 0u, 0u, 0u};
+
+// Issue the copies of chunk `rec`'s inputs into `stg` (all NT threads).  Pieces
+// that read nothing (tokens >= T, tokens < 0 without a carried state) copy
+// zeros.  Complete at the issuing threads' next s_waitcnt vmcnt(0).
+template <int D, int C, typename IO, int NT>
+__device__ __forceinline__ void issue_stage(const PrepParams& p, int rec, ChunkStage<D, C, IO>* stg,
+                                            int tid) {
+  using S = ChunkStage<D, C, IO>;
+  constexpr int CPR = S::CPR, XR = S::XR;
+  constexpr int XP = XR * CPR;  // pieces of one tensor's window
+  constexpr int GP = C * CPR;   // pieces of the g rows
+  constexpr int FP = 3 * D;     // pieces of the filters
+  static_assert((CPR & (CPR - 1)) == 0, "pieces per row is a power of two");
+  const int n = rec % p.NT;
+  const int bh = rec / p.NT;
+  const int h = bh % p.H, b = bh / p.H;
+  const int t0 = n * C;
+  const size_t HD = (size_t)p.H * D;
+  const char* zero = reinterpret_cast<const char*>(kZero16);
+  char* dst = reinterpret_cast<char*>(stg);
+  const int lane = tid & 63, wbase = tid - lane;
+  const IO* xs[3] = {static_cast<const IO*>(p.q), static_cast<const IO*>(p.k),
+                     static_cast<const IO*>(p.v)};
+  const IO* state = static_cast<const IO*>(p.conv_state_in);
+  auto copy = [&](const char* src, int piece0) {
+    __builtin_amdgcn_global_load_lds((const glb_void_t*)src, (lds_void_t*)(dst + 16 * piece0), 16,
+                                     0, 0);
+  };
+#pragma unroll
+  for (int x = 0; x < 3; ++x) {
+    const IO* xrow = xs[x] + (size_t)b * p.T * HD + (size_t)h * D;
+    const IO* srow = state != nullptr ? state + ((size_t)b * 3 + x) * 3 * HD + (size_t)h * D : nullptr;
+#pragma unroll
+    for (int it = 0; it < (XP + NT - 1) / NT; ++it) {
+      const int e = it * NT + tid;
+      if (it * NT + wbase < XP && e < XP) {
+        const int m = e / CPR, pc = e % CPR;
+        const int t = t0 - 3 + m;
+        const char* src = zero;
+        if (t >= 0 && t < p.T) src = reinterpret_cast<const char*>(xrow + (size_t)t * HD) + 16 * pc;
+        else if (t < 0 && srow != nullptr)
+          src = reinterpret_cast<const char*>(srow + (size_t)(3 + t) * HD) + 16 * pc;
+        copy(src, x * XP + it * NT + wbase);
+      }
+    }
+  }
+  {
+    const IO* grow = static_cast<const IO*>(p.g) + (size_t)b * p.T * HD + (size_t)h * D;
+#pragma unroll
+    for (int it = 0; it < (GP + NT - 1) / NT; ++it) {
+      const int e = it * NT + tid;
+      if (it * NT + wbase < GP && e < GP) {
+        const int m = e / CPR, pc = e % CPR;
+        const int t = t0 + m;
+        const char* src = t < p.T ? reinterpret_cast<const char*>(grow + (size_t)t * HD) + 16 * pc : zero;
+        copy(src, 3 * XP + it * NT + wbase);
+      }
+    }
+  }
+  if (p.conv_w != nullptr) {
+#pragma unroll
+    for (int it = 0; it < (FP + NT - 1) / NT; ++it) {
+      const int e = it * NT + tid;
+      if (it * NT + wbase < FP && e < FP) {
+        const int x = e / D, c = e % D;
+        copy(reinterpret_cast<const char*>(p.conv_w + ((size_t)x * HD + (size_t)h * D + c) * 4),
+             3 * XP + GP + it * NT + wbase);
+      }
+    }
+  }
+}
+
+// beta of token t0 + tid of chunk `rec` (0 past the end of the sequence)
+template <typename IO>
+__device__ __forceinline__ float chunk_beta(const PrepParams& p, int rec, int C, int tid) {
+  const int bh = rec / p.NT;
+  const int t = (rec % p.NT) * C + tid;
+  const float v = to_f32(static_cast<const IO*>(p.beta)[((size_t)(bh / p.H) * p.T +
+                                                          (t < p.T ? t : p.T - 1)) * p.H + bh % p.H]);
+  return t < p.T ? v : 0.f;
 }
 
 // Multiply the operand fragment element-wise by a per-k factor f[k] (k = channel).
@@ -123,361 +211,330 @@ __device__ __forceinline__ void load_timg(RowFrag<E, K>& f, const E* img, int ro
   }
 }
 
+// Persistent: workgroup w prepares chunks w, w + gridDim.x, ...; the inputs of
+// the next chunk are copied to LDS while the current one computes.
 template <int D, int C, typename IO, typename E>
 __global__ __launch_bounds__(kFastThreads, 1) void kda_chunk_prep_kernel(PrepParams p) {
   using SM = FastSmem<D, C, E>;
+  using STG = ChunkStage<D, C, IO>;
   __shared__ SM sm;
-  constexpr int LQ = SM::LQ, LT = SM::LT, LA = SM::LA, NB = SM::NB, KP = SM::KP, DH = SM::DH;
+  __shared__ STG stg;
+  constexpr int LQ = SM::LQ, LT = SM::LT, LA = SM::LA, NB = SM::NB;
   constexpr int NOCT = D / 8;          // 8-channel groups per token row
   constexpr int NSEG = C / 2;          // 2-token segments
   constexpr int ITEMS = NSEG * NOCT;   // <= 512
+  constexpr int NW = kFastThreads / 64;
   static_assert(ITEMS <= kFastThreads, "tile does not fit one pass");
-  static_assert(SM::TOT <= SM::R1, "segment totals fit the region");
   constexpr RecordLayout RL = record_layout(C, D, sizeof(E));
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g4 = lane >> 4;
-  const int rec = blockIdx.x;
-  const int n = rec % p.NT;
-  const int bh = rec / p.NT;
-  const int h = bh % p.H, b = bh / p.H;
-  const int t0 = n * C;
-  char* recp = p.ws + (size_t)rec * RL.bytes;
-  E* gW = reinterpret_cast<E*>(recp) + RL.w;
-  E* gQL = reinterpret_cast<E*>(recp) + RL.ql;
-  E* gKT = reinterpret_cast<E*>(recp) + RL.kt;
-  E* gU = reinterpret_cast<E*>(recp) + RL.u;
-  E* gP = reinterpret_cast<E*>(recp) + RL.p;
-  float* gLC = reinterpret_cast<float*>(recp + RL.lc_bytes);
-  E* RA = reinterpret_cast<E*>(sm.r1);
-  E* RP = RA + C * LQ;
-  E* CB = RP + C * LQ;
-  E* CD = CB + C * LQ;
-  E* RAd = CD + C * LQ;
-  E* RPd = RAd + C * LQ;
-
-  // ---------------------------------------------------------------- phase 1
+  const int nrec = p.B * p.H * p.NT;
   const bool active = tid < ITEMS;
   const int s = active ? tid / NOCT : 0;  // 2-token segment
   const int j = tid % NOCT;
   const int ch = 8 * j;
   const int pb = s / 8;                   // 16-token block of this segment
-  const int tf = t0 + 2 * s;
-  const int mypass = j / (NOCT / KP);     // channel pass that stores this thread's operands
-  // every global load of this phase is issued before the first wait: the head's
-  // filters (straight to LDS), the q/k/v windows, g and beta
   const bool conv = p.conv_w != nullptr;
-  if (conv) stage_filters<D, kFastThreads>(p.conv_w, p.H, h, sm.filt, tid);
-  Raw8<IO> win[3][5];
-  front_load<2, IO>(static_cast<const IO*>(p.q), static_cast<const IO*>(p.k),
-                    static_cast<const IO*>(p.v), static_cast<const IO*>(p.conv_state_in), conv, b,
-                    p.T, p.H, D, h, ch, tf, win);
-  float g2[2][8], bt[2];
-  const size_t HD = (size_t)p.H * D;
-#pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    // clamped token, zeroed past the end below
-    const int t = tf + m;
-    const int tc = t < p.T ? t : p.T - 1;
-    load8(static_cast<const IO*>(p.g) + ((size_t)b * p.T + tc) * HD + (size_t)h * D + ch, g2[m]);
-    bt[m] = to_f32(static_cast<const IO*>(p.beta)[((size_t)b * p.T + tc) * p.H + h]);
+  E* RA = reinterpret_cast<E*>(sm.r1);
+  E* RP = RA + C * LQ;
+  E* CB = RP + C * LQ;
+
+  int rec = blockIdx.x;
+  float bnext = 0.f;
+  if (rec < nrec) {
+    issue_stage<D, C, IO, kFastThreads>(p, rec, &stg, tid);
+    if (tid < C) stg.beta[tid] = chunk_beta<IO>(p, rec, C, tid);
   }
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();  // filters are in LDS
-  float yq[2][8], yk[2][8], yv[2][8], qk[2];
-  front_compute<2, D, IO>(win, sm.filt, conv, p.conv_state_in != nullptr, ch, tf, p.T, active,
-                          p.l2 != 0, p.eps, p.scale, yq, yk, yv, qk);
+  for (; rec < nrec; rec += gridDim.x) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // this chunk's inputs are in LDS; the previous chunk is done with LDS
+    const int n = rec % p.NT;
+    const int t0 = n * C;
+    const int tf = t0 + 2 * s;
+    const int next = rec + (int)gridDim.x;
+    char* recp = p.ws + (size_t)rec * RL.bytes;
+    E* gW = reinterpret_cast<E*>(recp) + RL.w;
+    E* gQL = reinterpret_cast<E*>(recp) + RL.ql;
+    E* gKT = reinterpret_cast<E*>(recp) + RL.kt;
+    E* gU = reinterpret_cast<E*>(recp) + RL.u;
+    E* gP = reinterpret_cast<E*>(recp) + RL.p;
+    float* gLC = reinterpret_cast<float*>(recp + RL.lc_bytes);
+
+    // -------------------------------------------------------------- phase 1
+    // conv + SiLU + L2 norm of this thread's 2 tokens x 8 channels
+    Raw8<IO> win[3][5];
 #pragma unroll
-  for (int m = 0; m < 2; ++m) {
-    const bool ok = active && tf + m < p.T;
-    bt[m] = ok ? bt[m] : 0.f;
+    for (int x = 0; x < 3; ++x)
 #pragma unroll
-    for (int c = 0; c < 8; ++c) g2[m][c] = ok ? g2[m][c] * kLog2e : 0.f;  // log2 units from here on
-  }
-#pragma unroll
-  for (int c = 0; c < 8; ++c) g2[1][c] += g2[0][c];
-  float* tot = reinterpret_cast<float*>(sm.r1);  // [NSEG][D] segment totals, then exclusive prefixes
-  if (tid == 0) sm.fatal = 0;
-  if (active) store8(tot + s * D + ch, g2[1]);
-  __syncthreads();
-  // one thread per channel: exclusive scan over segments and the per-block factors
-  if (tid < D) {
-    const int c = tid;
-    float acc = 0.f;
-    sm.gb[c] = 0.f;
-    for (int s2 = 0; s2 < NSEG; ++s2) {
-      const float v = tot[s2 * D + c];
-      tot[s2 * D + c] = acc;
-      acc += v;
-      if ((s2 & 7) == 7) sm.gb[((s2 + 1) >> 3) * D + c] = acc;
-    }
-    gLC[c] = __builtin_amdgcn_exp2f(acc);
-    bool fatal = false;
-#pragma unroll
-    for (int q = 0; q < NB; ++q) {
-      const float g0 = sm.gb[q * D + c], g1 = sm.gb[(q + 1) * D + c];
-      const float span = g0 - g1;
-      sm.esp[q * D + c] = span <= kSafeSpan2 ? __builtin_amdgcn_exp2f(span) : 0.f;
-      sm.eb[q * D + c] = __builtin_amdgcn_exp2f(g0);
-      sm.ec[q * D + c] = __builtin_amdgcn_exp2f(acc - g1);
-      fatal |= span > kFatalSpan2;
-    }
-#pragma unroll
-    for (int R = 2; R < NB; ++R)
-#pragma unroll
-      for (int Q = 0; Q + 2 <= R; ++Q)
-        sm.mpq[pair_index(R, Q) * D + c] =
-            __builtin_amdgcn_exp2f(sm.gb[R * D + c] - sm.gb[(Q + 1) * D + c]);
-    if (fatal) atomicOr(&sm.fatal, 1);
-  }
-  __syncthreads();
-  if (sm.fatal) {
-    // decays too strong for the factoring: the exact preparation redoes this chunk
-    if (tid == 0) {
-      const unsigned slot = atomicAdd(p.fb_count, 1u);
-      p.fb_list[slot] = (unsigned)rec;
-    }
-    return;
-  }
-  // operands of this thread's 2 tokens x 8 channels, kept until its channel pass;
-  // (beta K Lambda) and (beta V) kept until the transposed images are built
-  E op[6][2][8];
-  E kv[2][2][8];
-  if (active) {
-    float pre[8], gp[8], gq[8], esp[8], eb[8], ec[8];
-    load8(tot + s * D + ch, pre);
-    load8(&sm.gb[pb * D + ch], gp);
-    load8(&sm.gb[(pb + 1) * D + ch], gq);
-    load8(&sm.esp[pb * D + ch], esp);
-    load8(&sm.eb[pb * D + ch], eb);
-    load8(&sm.ec[pb * D + ch], ec);
-    bool any_wide = false;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) any_wide |= (gp[c] - gq[c]) > kSafeSpan2;
-    float kt[2][8];
+      for (int mm = 0; mm < 5; ++mm) win[x][mm].load(&stg.x[x][2 * s + mm][ch]);
+    float g2[2][8], bt[2];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      const int tl = 2 * s + m;
-      float ql[8];
+      load8(&stg.g[2 * s + m][ch], g2[m]);
+      bt[m] = stg.beta[2 * s + m];
+    }
+    float yq[2][8], yk[2][8], yv[2][8], qk[2];
+    // staged rows that read nothing hold zeros; tokens past the end have beta = 0
+    // and g = 0, which is all the later phases need of them
+    front_compute<2, D, IO, false, false>(win, &stg.filt[0][0][0], conv, p.conv_state_in != nullptr,
+                                          ch, tf, p.T, active, p.l2 != 0, p.eps, p.scale, yq, yk,
+                                          yv, qk);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        const float gam = g2[m][c] + pre[c];
-        const float a = __builtin_amdgcn_exp2f(gam - gp[c]);
-        const float bb = __builtin_amdgcn_exp2f(gq[c] - gam);
-        const float ra = bt[m] * yk[m][c] * a;
-        const float rp = yq[m][c] * a;
-        const float cb = yk[m][c] * bb;
-        op[0][m][c] = from_f32<E>(ra);
-        op[1][m][c] = from_f32<E>(rp);
-        op[2][m][c] = from_f32<E>(cb);
-        op[3][m][c] = from_f32<E>(cb * esp[c]);
-        op[4][m][c] = op[0][m][c];
-        op[5][m][c] = op[1][m][c];
-        ql[c] = rp * eb[c];
-        kt[m][c] = cb * ec[c];
-        kv[0][m][c] = from_f32<E>(ra * eb[c]);
-        kv[1][m][c] = from_f32<E>(bt[m] * yv[m][c]);
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) g2[m][c] *= kLog2e;  // log2 units from here on
+#pragma unroll
+    for (int c = 0; c < 8; ++c) g2[1][c] += g2[0][c];
+    if (tid == 0) sm.fatal = 0;
+    if (active) store8(sm.tot + s * D + ch, g2[1]);
+    __syncthreads();  // the staged inputs are consumed: start copying the next chunk's
+    if (next < nrec) {
+      issue_stage<D, C, IO, kFastThreads>(p, next, &stg, tid);
+      if (tid < C) bnext = chunk_beta<IO>(p, next, C, tid);
+    }
+    // from here on, barriers wait for LDS only, so the copies stay in flight
+
+    // one thread per channel: exclusive scan over segments, block boundaries,
+    // midpoints and the pair factors
+    if (tid < D) {
+      const int c = tid;
+      float acc = 0.f;
+      float gbl[NB + 1];
+      gbl[0] = 0.f;
+#pragma unroll
+      for (int s2 = 0; s2 < NSEG; ++s2) {
+        const float v = sm.tot[s2 * D + c];
+        sm.tot[s2 * D + c] = acc;
+        acc += v;
+        if ((s2 & 7) == 7) gbl[(s2 + 1) >> 3] = acc;
       }
-      if (any_wide) {
-        // channels whose block span is too wide for exp(+span): midpoint reference
+      gLC[c] = __builtin_amdgcn_exp2f(acc);
+      bool fatal = false;
+      float md[NB];
+#pragma unroll
+      for (int q = 0; q <= NB; ++q) sm.gb[q * D + c] = gbl[q];
+#pragma unroll
+      for (int q = 0; q < NB; ++q) {
+        md[q] = 0.5f * (gbl[q] + gbl[q + 1]);
+        sm.mid[q * D + c] = md[q];
+        fatal |= gbl[q] - gbl[q + 1] > kFatalSpan2;
+      }
+#pragma unroll
+      for (int R = 1; R < NB; ++R)
+#pragma unroll
+        for (int Q = 0; Q < R; ++Q)
+          sm.mpq[pair_index(R, Q) * D + c] = __builtin_amdgcn_exp2f(md[R] - md[Q]);
+      if (fatal) atomicOr(&sm.fatal, 1);
+    }
+    lds_barrier();
+    if (sm.fatal) {
+      // decays too strong for the factoring: the exact preparation redoes this chunk
+      if (tid == 0) {
+        const unsigned slot = atomicAdd(p.fb_count, 1u);
+        p.fb_list[slot] = (unsigned)rec;
+      }
+    } else {
+      // operands: with Gamma_i the cumulative decay and m the midpoint of token
+      // i's block, a_i = exp(Gamma_i - m), b_i = exp(m - Gamma_i)
+      E kv[2][2][8];  // beta K Lambda and beta V, kept for the transposed images
+      if (active) {
+        float pre[8], md[8], gC[8];
+        load8(&sm.tot[s * D + ch], pre);
+        load8(&sm.mid[pb * D + ch], md);
+        load8(&sm.gb[NB * D + ch], gC);
+        float kt[2][8];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const int tl = 2 * s + m;
+          float ra[8], rp[8], cb[8], ql[8];
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            const float gam = g2[m][c] + pre[c];
+            const float a = __builtin_amdgcn_exp2f(gam - md[c]);
+            const float bb = __builtin_amdgcn_exp2f(md[c] - gam);
+            const float lam = __builtin_amdgcn_exp2f(gam);
+            const float bk = bt[m] * yk[m][c];
+            ra[c] = bk * a;
+            rp[c] = yq[m][c] * a;
+            cb[c] = yk[m][c] * bb;
+            ql[c] = yq[m][c] * lam;
+            kt[m][c] = yk[m][c] * __builtin_amdgcn_exp2f(gC[c] - gam);
+            kv[0][m][c] = from_f32<E>(bk * lam);
+            kv[1][m][c] = from_f32<E>(bt[m] * yv[m][c]);
+          }
+          store8(RA + tl * LQ + ch, ra);
+          store8(RP + tl * LQ + ch, rp);
+          store8(CB + tl * LQ + ch, cb);
+          store8(gQL + (size_t)tl * D + ch, ql);
+        }
+#pragma unroll
+        for (int c = 0; c < 8; ++c) store2(gKT + (size_t)(ch + c) * C + 2 * s, kt[0][c], kt[1][c]);
+      }
+      lds_barrier();
+
+      // ------------------------------------------------------------ phase 2
+      // A^T / P^T tiles (rows j, columns i) of the lower block triangle, round
+      // robin over waves; for blocks R > Q the k b rows take the pair factor
+      constexpr int NTILE = NB * (NB + 1) / 2;
+      constexpr int TPW = (NTILE + NW - 1) / NW;
+      f32x4 accA[TPW], accP[TPW];
+      int tR[TPW], tQ[TPW];
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) {
+        int idx = wave + NW * i, R = 0;
+        while (idx > R) { idx -= R + 1; ++R; }
+        tR[i] = (wave + NW * i < NTILE) ? R : -1;
+        tQ[i] = idx;
+        accA[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+        accP[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      // channels in pieces of KC (fp32 fragments take four times the registers)
+      constexpr int KC = sizeof(E) == 2 ? D : (D < 32 ? D : 32);
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) {
+        if (tR[i] < 0) continue;
+        const int R0 = tR[i], Q0 = tQ[i];
+#pragma unroll
+        for (int kc = 0; kc < D; kc += KC) {
+          RowFrag<E, KC> cf, fa, fp;
+          cf.load(CB + (16 * Q0 + r) * LQ + kc, g4);
+          if (R0 != Q0) scale_k<KC>(cf, &sm.mpq[pair_index(R0, Q0) * D + kc], g4);
+          fa.load(RA + (16 * R0 + r) * LQ + kc, g4);
+          fp.load(RP + (16 * R0 + r) * LQ + kc, g4);
+          mma<KC>(accA[i], cf, fa);
+          mma<KC>(accP[i], cf, fp);
+        }
+      }
+      lds_barrier();  // the operands are dead
+
+      // ------------------------------------------------------------ phase 3
+      float* sA = reinterpret_cast<float*>(sm.r1);  // [C][LA]
+      float* sT = sA + C * LA;                      // [C][LA]
+      float* scr = sT + C * LA;                     // [4][16][17]
+      for (int it = tid; it < C * LA; it += kFastThreads) sT[it] = 0.f;
+#pragma unroll
+      for (int i = 0; i < TPW; ++i) {
+        const int R = tR[i], Q = tQ[i];
+        if (R < 0) continue;
+        const int ii = 16 * R + r;
+        const int jj = 16 * Q + 4 * g4;
+        float av[4], pv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool lowA = (R != Q) || (jj + e < ii);
+          const bool lowP = (R != Q) || (jj + e <= ii);
+          av[e] = lowA ? accA[i][e] : 0.f;
+          pv[e] = lowP ? accP[i][e] : 0.f;
+        }
+        *reinterpret_cast<f32x4*>(&sA[ii * LA + jj]) = f32x4{av[0], av[1], av[2], av[3]};
+        store4(gP + (size_t)ii * C + jj, pv[0], pv[1], pv[2], pv[3]);
+      }
+      lds_barrier();
+
+      // ------------------------------------------------------------ phase 4
+      // T = (I + A)^-1: diagonal 16x16 blocks by forward substitution, one
+      // column per thread
+      if (tid < C) {
+        const int pq = tid >> 4, col = tid & 15;
+        const float* Ab = sA + (16 * pq) * LA + 16 * pq;
+        float x[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float acc = (i == col) ? 1.f : 0.f;
+#pragma unroll
+          for (int jj = 0; jj < i; ++jj) acc = fmaf(-Ab[i * LA + jj], x[jj], acc);
+          x[i] = acc;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sT[(16 * pq + i) * LA + 16 * pq + col] = x[i];
+      }
+      lds_barrier();
+      // off-diagonal blocks, block row by block row:
+      //   T_pq = -T_pp * sum_{r=q}^{p-1} A_pr T_rq
+      for (int pr = 1; pr < NB; ++pr) {
+        const int qb = wave;
+        float* xs = scr + (wave & 3) * 16 * 17;
+        if (qb < pr) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          for (int rb = qb; rb < pr; ++rb) {
+#pragma unroll
+            for (int k0 = 0; k0 < 16; k0 += 4) {
+              const float a = sA[(16 * pr + r) * LA + 16 * rb + k0 + g4];
+              const float bv = sT[(16 * rb + k0 + g4) * LA + 16 * qb + r];
+              acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv, acc, 0, 0, 0);
+            }
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) xs[(4 * g4 + e) * 17 + r] = acc[e];
+        }
+        lds_barrier();
+        if (qb < pr) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int k0 = 0; k0 < 16; k0 += 4) {
+            const float a = sT[(16 * pr + r) * LA + 16 * pr + k0 + g4];
+            const float bv = xs[(k0 + g4) * 17 + r];
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv, acc, 0, 0, 0);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sT[(16 * pr + 4 * g4 + e) * LA + 16 * qb + r] = -acc[e];
+        }
+        lds_barrier();
+      }
+      // T in the matrix-core element type, after A / T / scratch
+      E* tb = reinterpret_cast<E*>(sm.r1 + SM::TB_OFF);
+      for (int it = tid; it < C * C; it += kFastThreads) {
+        const int i = it / C, jj = it % C;
+        tb[i * LT + jj] = from_f32<E>(sT[i * LA + jj]);
+      }
+      lds_barrier();  // A and T (float) are dead
+
+      // ------------------------------------------------------------ phase 5
+      // (beta K Lambda)^T and (beta V)^T as swizzled [D][C] images
+      E* klt = reinterpret_cast<E*>(sm.r1 + SM::KLT_OFF);
+      E* vt = reinterpret_cast<E*>(sm.r1 + SM::VT_OFF);
+      static_assert(SM::IMGS <= SM::TB_OFF, "transposed images stay clear of T");
+      if (active) {
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-          if (gp[c] - gq[c] > kSafeSpan2) {
-            const float gam = g2[m][c] + pre[c];
-            const float mid = 0.5f * (gp[c] + gq[c]);
-            const float ad = __builtin_amdgcn_exp2f(gam - mid);
-            op[4][m][c] = from_f32<E>(bt[m] * yk[m][c] * ad);
-            op[5][m][c] = from_f32<E>(yq[m][c] * ad);
-            op[3][m][c] = from_f32<E>(yk[m][c] * __builtin_amdgcn_exp2f(mid - gam));
+          const int at = TImg<E, C>::at(ch + c, 2 * s);
+          if constexpr (sizeof(E) == 2) {
+            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+            *reinterpret_cast<bf16x2*>(klt + at) = bf16x2{kv[0][0][c], kv[0][1][c]};
+            *reinterpret_cast<bf16x2*>(vt + at) = bf16x2{kv[1][0][c], kv[1][1][c]};
+          } else {
+            *reinterpret_cast<float2*>(klt + at) = make_float2(kv[0][0][c], kv[0][1][c]);
+            *reinterpret_cast<float2*>(vt + at) = make_float2(kv[1][0][c], kv[1][1][c]);
           }
         }
       }
-      store8(gQL + (size_t)tl * D + ch, ql);
-    }
-#pragma unroll
-    for (int c = 0; c < 8; ++c) store2(gKT + (size_t)(ch + c) * C + 2 * s, kt[0][c], kt[1][c]);
-  }
-  __syncthreads();  // every read of the segment prefixes is done
-
-  // ---------------------------------------------------------------- phase 2
-  // A^T / P^T tiles (rows j, columns i), lower block triangle, round robin over
-  // waves, accumulated over the channel passes
-  constexpr int NTILE = NB * (NB + 1) / 2;
-  constexpr int NW = kFastThreads / 64;
-  constexpr int TPW = (NTILE + NW - 1) / NW;
-  f32x4 accA[TPW], accP[TPW];
-  int tR[TPW], tQ[TPW];
-#pragma unroll
-  for (int i = 0; i < TPW; ++i) {
-    int idx = wave + NW * i, R = 0;
-    while (idx > R) { idx -= R + 1; ++R; }
-    tR[i] = (wave + NW * i < NTILE) ? R : -1;
-    tQ[i] = idx;
-    accA[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    accP[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-#pragma unroll
-  for (int kp = 0; kp < KP; ++kp) {
-    if (active && mypass == kp) {
-      const int cl = ch - kp * DH;  // channel inside this pass
-#pragma unroll
-      for (int a = 0; a < 6; ++a) {
-        E* dst = RA + a * C * LQ;
-#pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          float tmp[8];
-#pragma unroll
-          for (int c = 0; c < 8; ++c) tmp[c] = to_f32(op[a][m][c]);
-          store8(dst + (2 * s + m) * LQ + cl, tmp);
-        }
+      lds_barrier();
+      // W^T tiles (c, i): A = (beta K Lambda)^T rows c, B = T rows i (j <= i)
+      constexpr int NWT = (D / 16) * NB;
+      constexpr int STEPC = RowFrag<E, C>::STEP;
+      for (int tt = wave; tt < NWT; tt += NW) {
+        const int Ct = tt / NB, It = tt % NB;
+        RowFrag<E, C> fa, fb;
+        load_timg<C>(fa, klt, 16 * Ct + r, g4);
+        fb.load(tb + (16 * It + r) * LT, g4);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        mma<C>(acc, fa, fb, (16 * It + 16 + STEPC - 1) / STEPC);
+        const int i = 16 * It + r, c = 16 * Ct + 4 * g4;
+        store4(gW + (size_t)i * D + c, acc[0], acc[1], acc[2], acc[3]);
+      }
+      // U~ tiles (i, v): A = T rows i, B = (beta V)^T rows v; stored in fragment order
+      for (int tt = wave; tt < NWT; tt += NW) {
+        const int It = tt / (D / 16), Vt = tt % (D / 16);
+        RowFrag<E, C> fa, fb;
+        fa.load(tb + (16 * It + r) * LT, g4);
+        load_timg<C>(fb, vt, 16 * Vt + r, g4);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        mma<C>(acc, fa, fb, (16 * It + 16 + STEPC - 1) / STEPC);
+        store4(gU + ((size_t)(It * (D / 16) + Vt) * 64 + lane) * 4, acc[0], acc[1], acc[2], acc[3]);
       }
     }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      if (tR[i] < 0) continue;
-      const int R0 = tR[i], Q0 = tQ[i];
-      RowFrag<E, DH> cf, fa, fp;
-      if (R0 != Q0) {
-        cf.load(CB + (16 * Q0 + r) * LQ, g4);
-        if (R0 - Q0 >= 2) scale_k<DH>(cf, &sm.mpq[pair_index(R0, Q0) * D + kp * DH], g4);
-        fa.load(RA + (16 * R0 + r) * LQ, g4);
-        fp.load(RP + (16 * R0 + r) * LQ, g4);
-      } else {
-        cf.load(CD + (16 * Q0 + r) * LQ, g4);
-        fa.load(RAd + (16 * R0 + r) * LQ, g4);
-        fp.load(RPd + (16 * R0 + r) * LQ, g4);
-      }
-      mma<DH>(accA[i], cf, fa);
-      mma<DH>(accP[i], cf, fp);
-    }
-    __syncthreads();  // this pass's operands are dead
-  }
-
-  // ---------------------------------------------------------------- phase 3
-  float* sA = reinterpret_cast<float*>(sm.r1);  // [C][LA]
-  float* sT = sA + C * LA;                      // [C][LA]
-  float* scr = sT + C * LA;                     // [4][16][17]
-  for (int it = tid; it < C * LA; it += kFastThreads) sT[it] = 0.f;
-#pragma unroll
-  for (int i = 0; i < TPW; ++i) {
-    const int R = tR[i], Q = tQ[i];
-    if (R < 0) continue;
-    const int ii = 16 * R + r;
-    const int jj = 16 * Q + 4 * g4;
-    float av[4], pv[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const bool lowA = (R != Q) || (jj + e < ii);
-      const bool lowP = (R != Q) || (jj + e <= ii);
-      av[e] = lowA ? accA[i][e] : 0.f;
-      pv[e] = lowP ? accP[i][e] : 0.f;
-    }
-    *reinterpret_cast<f32x4*>(&sA[ii * LA + jj]) = f32x4{av[0], av[1], av[2], av[3]};
-    store4(gP + (size_t)ii * C + jj, pv[0], pv[1], pv[2], pv[3]);
-  }
-  __syncthreads();
-
-  // ---------------------------------------------------------------- phase 4
-  // diagonal 16x16 blocks by forward substitution, one column per thread
-  if (tid < C) {
-    const int pq = tid >> 4, col = tid & 15;
-    const float* Ab = sA + (16 * pq) * LA + 16 * pq;
-    float x[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      float acc = (i == col) ? 1.f : 0.f;
-#pragma unroll
-      for (int jj = 0; jj < i; ++jj) acc = fmaf(-Ab[i * LA + jj], x[jj], acc);
-      x[i] = acc;
-    }
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sT[(16 * pq + i) * LA + 16 * pq + col] = x[i];
-  }
-  __syncthreads();
-  // off-diagonal blocks, block row by block row:
-  //   T_pq = -T_pp * sum_{r=q}^{p-1} A_pr T_rq
-  for (int pr = 1; pr < NB; ++pr) {
-    const int qb = wave;
-    float* xs = scr + (wave & 3) * 16 * 17;
-    if (qb < pr) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int rb = qb; rb < pr; ++rb) {
-#pragma unroll
-        for (int k0 = 0; k0 < 16; k0 += 4) {
-          const float a = sA[(16 * pr + r) * LA + 16 * rb + k0 + g4];
-          const float bv = sT[(16 * rb + k0 + g4) * LA + 16 * qb + r];
-          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv, acc, 0, 0, 0);
-        }
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) xs[(4 * g4 + e) * 17 + r] = acc[e];
-    }
-    __syncthreads();
-    if (qb < pr) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int k0 = 0; k0 < 16; k0 += 4) {
-        const float a = sT[(16 * pr + r) * LA + 16 * pr + k0 + g4];
-        const float bv = xs[(k0 + g4) * 17 + r];
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv, acc, 0, 0, 0);
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sT[(16 * pr + 4 * g4 + e) * LA + 16 * qb + r] = -acc[e];
-    }
-    __syncthreads();
-  }
-  // T in the matrix-core element type, after A / T / scratch
-  E* tb = reinterpret_cast<E*>(sm.r1 + SM::TB_OFF);
-  for (int it = tid; it < C * C; it += kFastThreads) {
-    const int i = it / C, jj = it % C;
-    tb[i * LT + jj] = from_f32<E>(sT[i * LA + jj]);
-  }
-  __syncthreads();  // A and T (float) are dead
-
-  // ---------------------------------------------------------------- phase 5
-  // (beta K Lambda)^T and (beta V)^T as swizzled [D][C] images
-  E* klt = reinterpret_cast<E*>(sm.r1 + SM::KLT_OFF);
-  E* vt = reinterpret_cast<E*>(sm.r1 + SM::VT_OFF);
-  static_assert(SM::IMGS <= SM::TB_OFF, "transposed images stay clear of T");
-  if (active) {
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int row = ch + c;
-      const int at = TImg<E, C>::at(row, 2 * s);
-      if constexpr (sizeof(E) == 2) {
-        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-        *reinterpret_cast<bf16x2*>(klt + at) = bf16x2{kv[0][0][c], kv[0][1][c]};
-        *reinterpret_cast<bf16x2*>(vt + at) = bf16x2{kv[1][0][c], kv[1][1][c]};
-      } else {
-        *reinterpret_cast<float2*>(klt + at) = make_float2(kv[0][0][c], kv[0][1][c]);
-        *reinterpret_cast<float2*>(vt + at) = make_float2(kv[1][0][c], kv[1][1][c]);
-      }
-    }
-  }
-  __syncthreads();
-  // W^T tiles (c, i): A = (beta K Lambda)^T rows c, B = T rows i (j <= i)
-  constexpr int NWT = (D / 16) * NB;
-  constexpr int STEPC = RowFrag<E, C>::STEP;
-  for (int tt = wave; tt < NWT; tt += NW) {
-    const int Ct = tt / NB, It = tt % NB;
-    RowFrag<E, C> fa, fb;
-    load_timg<C>(fa, klt, 16 * Ct + r, g4);
-    fb.load(tb + (16 * It + r) * LT, g4);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    mma<C>(acc, fa, fb, (16 * It + 16 + STEPC - 1) / STEPC);
-    const int i = 16 * It + r, c = 16 * Ct + 4 * g4;
-    store4(gW + (size_t)i * D + c, acc[0], acc[1], acc[2], acc[3]);
-  }
-  // U~ tiles (i, v): A = T rows i, B = (beta V)^T rows v; stored in fragment order
-  for (int tt = wave; tt < NWT; tt += NW) {
-    const int It = tt / (D / 16), Vt = tt % (D / 16);
-    RowFrag<E, C> fa, fb;
-    fa.load(tb + (16 * It + r) * LT, g4);
-    load_timg<C>(fb, vt, 16 * Vt + r, g4);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    mma<C>(acc, fa, fb, (16 * It + 16 + STEPC - 1) / STEPC);
-    store4(gU + ((size_t)(It * (D / 16) + Vt) * 64 + lane) * 4, acc[0], acc[1], acc[2], acc[3]);
+    if (next < nrec && tid < C) stg.beta[tid] = bnext;
   }
 }
 
@@ -568,9 +625,39 @@ __global__ void kda_reset_count_kernel(unsigned* count) {
 }
 
 // ------------------------------------------------------------------ launchers
+// Resident workgroups of a persistent kernel on the current device: compute
+// units x workgroups per unit, taken once per device and kernel.
+template <typename K>
+static hipError_t resident_blocks(K kernel, int threads, unsigned* out) {
+  constexpr int kMaxDev = 64;
+  static int cache[kMaxDev];
+  int dev = 0;
+  if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return e;
+  if (dev >= 0 && dev < kMaxDev && cache[dev] > 0) {
+    *out = (unsigned)cache[dev];
+    return hipSuccess;
+  }
+  int cus = 0, per_cu = 0;
+  if (hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+      e != hipSuccess)
+    return e;
+  if (hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0);
+      e != hipSuccess)
+    return e;
+  const int n = cus * (per_cu > 0 ? per_cu : 1);
+  if (dev >= 0 && dev < kMaxDev) cache[dev] = n;
+  *out = (unsigned)n;
+  return hipSuccess;
+}
+
 template <int D, int C, typename IO, typename E>
 static hipError_t launch_prep_t(const PrepParams& p, hipStream_t st) {
-  const unsigned grid = (unsigned)((size_t)p.B * p.H * p.NT);
+  const size_t nrec = (size_t)p.B * p.H * p.NT;
+  unsigned grid = 0;
+  if (hipError_t e = resident_blocks(kda_chunk_prep_kernel<D, C, IO, E>, kFastThreads, &grid);
+      e != hipSuccess)
+    return e;
+  if (nrec < grid) grid = (unsigned)nrec;
   hipLaunchKernelGGL((kda_chunk_prep_kernel<D, C, IO, E>), dim3(grid), dim3(kFastThreads), 0, st,
                      p);
   return hipGetLastError();
