@@ -1,7 +1,6 @@
-// Chunk preparation for the KDA prefill: persistent workgroups of 512 threads,
-// one (sequence, head, chunk of C tokens) at a time, with the next chunk's inputs
-// copied to LDS while the current one computes.  Everything here is independent
-// across chunks; the serial dependence on the state is left to the state walk.
+// Chunk preparation for the KDA prefill: one workgroup per (sequence, head,
+// chunk of C tokens).  Everything here is independent across chunks; the serial
+// dependence on the state is left to the state walk.
 //
 // Per chunk (Gamma = chunk-local cumulative sum of the log-decay g, per channel;
 // Lambda = exp(Gamma); all decays act on the key channels):
@@ -30,10 +29,26 @@
 
 namespace kda {
 
-constexpr int kFastThreads = 512;
 constexpr float kFatalSpan2 = 240.f;  // log2 units (~166 nats): widest block span factored
 
-template <int D, int C, typename E>
+// Threads per workgroup: 256 for bf16 (two workgroups share a compute unit, so
+// one's loads overlap the other's arithmetic), 512 for fp32 (whose rows take
+// twice the registers, so each thread holds half as many tokens).
+template <typename E> constexpr int fast_threads() { return sizeof(E) == 2 ? 256 : 512; }
+
+// Work split of the front end: each thread takes TOK consecutive tokens x 8
+// channels of the chunk.
+template <int D, int C, int NTH>
+struct FastTile {
+  static constexpr int NOCT = D / 8;  // 8-channel groups per token row
+  static constexpr int TOK = C * NOCT / NTH > 0 ? C * NOCT / NTH : 1;
+  static constexpr int NSEG = C / TOK;  // token segments
+  static constexpr int ITEMS = NSEG * NOCT;
+  static_assert(ITEMS <= NTH, "tile does not fit one pass");
+  static_assert(16 % TOK == 0, "a segment stays inside one 16-token block");
+};
+
+template <int D, int C, typename E, int NSEG>
 struct FastSmem {
   static constexpr int ES = (int)sizeof(E);
   static constexpr int PE = 16 / ES;               // 16-byte row padding, in elements
@@ -56,117 +71,17 @@ struct FastSmem {
   static constexpr int LAST = TB_OFF + C * LT * ES;
   static constexpr int R1 = OPS > LAST ? OPS : LAST;
   alignas(16) char r1[R1];
-  alignas(16) float tot[(C / 2) * D];  // 2-token segment totals, then exclusive prefixes
+  alignas(16) float tot[NSEG * D];     // segment totals, then exclusive prefixes
   alignas(16) float gb[(NB + 1) * D];  // Gamma at block boundaries: gb[p] = Gamma before block p
   alignas(16) float mid[NB * D];       // block midpoints (gb[p] + gb[p + 1]) / 2
   alignas(16) float mpq[NPAIR * D];    // exp(mid[R] - mid[Q]) for blocks R > Q
+  alignas(16) float filt[3 * D * 4];   // the head's conv filters [q, k, v][D][4]
   int fatal;
 };
 
 __device__ __forceinline__ int pair_index(int R, int Q) {
   // pairs R > Q in the order (1,0), (2,0), (2,1), (3,0), ...
   return R * (R - 1) / 2 + Q;
-}
-
-// Inputs of one chunk, copied to LDS ahead of use with the direct global-to-LDS
-// path (16 bytes per lane): the q/k/v rows of tokens t0 - 3 .. t0 + C - 1 (the
-// conv window; rows before the sequence come from the carried conv state), the
-// g rows, and the head's conv filters.  beta goes through registers.
-template <int D, int C, typename IO>
-struct ChunkStage {
-  static constexpr int CPR = D * (int)sizeof(IO) / 16;  // 16-byte pieces per row
-  static constexpr int XR = C + 3;                      // window rows per tensor
-  static constexpr int NX = 3 * XR * CPR;
-  static constexpr int NG = C * CPR;
-  static constexpr int NF = 3 * D;                      // one piece = 4 taps of a channel
-  alignas(16) IO x[3][XR][D];
-  alignas(16) IO g[C][D];
-  alignas(16) float filt[3][D][4];
-  float beta[C];
-};
-
-// 16 zero bytes: the copy source of every staged piece that reads nothing.
-__device__ __attribute__((aligned(16))) const unsigned kZero16[4] = {0u, 0u, 0u, 0u};
-
-// Issue the copies of chunk `rec`'s inputs into `stg` (all NT threads).  Pieces
-// that read nothing (tokens >= T, tokens < 0 without a carried state) copy
-// zeros.  Complete at the issuing threads' next s_waitcnt vmcnt(0).
-template <int D, int C, typename IO, int NT>
-__device__ __forceinline__ void issue_stage(const PrepParams& p, int rec, ChunkStage<D, C, IO>* stg,
-                                            int tid) {
-  using S = ChunkStage<D, C, IO>;
-  constexpr int CPR = S::CPR, XR = S::XR;
-  constexpr int XP = XR * CPR;  // pieces of one tensor's window
-  constexpr int GP = C * CPR;   // pieces of the g rows
-  constexpr int FP = 3 * D;     // pieces of the filters
-  static_assert((CPR & (CPR - 1)) == 0, "pieces per row is a power of two");
-  const int n = rec % p.NT;
-  const int bh = rec / p.NT;
-  const int h = bh % p.H, b = bh / p.H;
-  const int t0 = n * C;
-  const size_t HD = (size_t)p.H * D;
-  const char* zero = reinterpret_cast<const char*>(kZero16);
-  char* dst = reinterpret_cast<char*>(stg);
-  const int lane = tid & 63, wbase = tid - lane;
-  const IO* xs[3] = {static_cast<const IO*>(p.q), static_cast<const IO*>(p.k),
-                     static_cast<const IO*>(p.v)};
-  const IO* state = static_cast<const IO*>(p.conv_state_in);
-  auto copy = [&](const char* src, int piece0) {
-    __builtin_amdgcn_global_load_lds((const glb_void_t*)src, (lds_void_t*)(dst + 16 * piece0), 16,
-                                     0, 0);
-  };
-#pragma unroll
-  for (int x = 0; x < 3; ++x) {
-    const IO* xrow = xs[x] + (size_t)b * p.T * HD + (size_t)h * D;
-    const IO* srow = state != nullptr ? state + ((size_t)b * 3 + x) * 3 * HD + (size_t)h * D : nullptr;
-#pragma unroll
-    for (int it = 0; it < (XP + NT - 1) / NT; ++it) {
-      const int e = it * NT + tid;
-      if (it * NT + wbase < XP && e < XP) {
-        const int m = e / CPR, pc = e % CPR;
-        const int t = t0 - 3 + m;
-        const char* src = zero;
-        if (t >= 0 && t < p.T) src = reinterpret_cast<const char*>(xrow + (size_t)t * HD) + 16 * pc;
-        else if (t < 0 && srow != nullptr)
-          src = reinterpret_cast<const char*>(srow + (size_t)(3 + t) * HD) + 16 * pc;
-        copy(src, x * XP + it * NT + wbase);
-      }
-    }
-  }
-  {
-    const IO* grow = static_cast<const IO*>(p.g) + (size_t)b * p.T * HD + (size_t)h * D;
-#pragma unroll
-    for (int it = 0; it < (GP + NT - 1) / NT; ++it) {
-      const int e = it * NT + tid;
-      if (it * NT + wbase < GP && e < GP) {
-        const int m = e / CPR, pc = e % CPR;
-        const int t = t0 + m;
-        const char* src = t < p.T ? reinterpret_cast<const char*>(grow + (size_t)t * HD) + 16 * pc : zero;
-        copy(src, 3 * XP + it * NT + wbase);
-      }
-    }
-  }
-  if (p.conv_w != nullptr) {
-#pragma unroll
-    for (int it = 0; it < (FP + NT - 1) / NT; ++it) {
-      const int e = it * NT + tid;
-      if (it * NT + wbase < FP && e < FP) {
-        const int x = e / D, c = e % D;
-        copy(reinterpret_cast<const char*>(p.conv_w + ((size_t)x * HD + (size_t)h * D + c) * 4),
-             3 * XP + GP + it * NT + wbase);
-      }
-    }
-  }
-}
-
-// beta of token t0 + tid of chunk `rec` (0 past the end of the sequence)
-template <typename IO>
-__device__ __forceinline__ float chunk_beta(const PrepParams& p, int rec, int C, int tid) {
-  const int bh = rec / p.NT;
-  const int t = (rec % p.NT) * C + tid;
-  const float v = to_f32(static_cast<const IO*>(p.beta)[((size_t)(bh / p.H) * p.T +
-                                                          (t < p.T ? t : p.T - 1)) * p.H + bh % p.H]);
-  return t < p.T ? v : 0.f;
 }
 
 // Multiply the operand fragment element-wise by a per-k factor f[k] (k = channel).
@@ -211,330 +126,342 @@ __device__ __forceinline__ void load_timg(RowFrag<E, K>& f, const E* img, int ro
   }
 }
 
-// Persistent: workgroup w prepares chunks w, w + gridDim.x, ...; the inputs of
-// the next chunk are copied to LDS while the current one computes.
+// TOK consecutive elements of one image row (TOK * sizeof(E) <= 16 bytes, inside
+// one 16-byte chunk)
+template <int TOK, typename E>
+__device__ __forceinline__ void store_run(E* dst, const E (&v)[TOK]) {
+  if constexpr (TOK * sizeof(E) == 16) {
+    typedef E run_t __attribute__((ext_vector_type(TOK)));
+    run_t x;
+#pragma unroll
+    for (int i = 0; i < TOK; ++i) x[i] = v[i];
+    *reinterpret_cast<run_t*>(dst) = x;
+  } else if constexpr (TOK * sizeof(E) == 8 || TOK * sizeof(E) == 4) {
+    typedef E run_t __attribute__((ext_vector_type(TOK)));
+    run_t x;
+#pragma unroll
+    for (int i = 0; i < TOK; ++i) x[i] = v[i];
+    *reinterpret_cast<run_t*>(dst) = x;
+  } else {
+#pragma unroll
+    for (int i = 0; i < TOK; ++i) dst[i] = v[i];
+  }
+}
+
+// One workgroup per (sequence, head, chunk).
 template <int D, int C, typename IO, typename E>
-__global__ __launch_bounds__(kFastThreads, 1) void kda_chunk_prep_kernel(PrepParams p) {
-  using SM = FastSmem<D, C, E>;
-  using STG = ChunkStage<D, C, IO>;
+__global__ __launch_bounds__(fast_threads<E>()) void kda_chunk_prep_kernel(PrepParams p) {
+  constexpr int NTH = fast_threads<E>();
+  using TL = FastTile<D, C, NTH>;
+  constexpr int NOCT = TL::NOCT, TOK = TL::TOK, NSEG = TL::NSEG, ITEMS = TL::ITEMS;
+  using SM = FastSmem<D, C, E, NSEG>;
   __shared__ SM sm;
-  __shared__ STG stg;
   constexpr int LQ = SM::LQ, LT = SM::LT, LA = SM::LA, NB = SM::NB;
-  constexpr int NOCT = D / 8;          // 8-channel groups per token row
-  constexpr int NSEG = C / 2;          // 2-token segments
-  constexpr int ITEMS = NSEG * NOCT;   // <= 512
-  constexpr int NW = kFastThreads / 64;
-  static_assert(ITEMS <= kFastThreads, "tile does not fit one pass");
+  constexpr int NW = NTH / 64;
   constexpr RecordLayout RL = record_layout(C, D, sizeof(E));
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g4 = lane >> 4;
-  const int nrec = p.B * p.H * p.NT;
-  const bool active = tid < ITEMS;
-  const int s = active ? tid / NOCT : 0;  // 2-token segment
-  const int j = tid % NOCT;
-  const int ch = 8 * j;
-  const int pb = s / 8;                   // 16-token block of this segment
-  const bool conv = p.conv_w != nullptr;
+  const int rec = blockIdx.x;
+  const int n = rec % p.NT;
+  const int bh = rec / p.NT;
+  const int h = bh % p.H, b = bh / p.H;
+  const int t0 = n * C;
+  char* recp = p.ws + (size_t)rec * RL.bytes;
+  E* gW = reinterpret_cast<E*>(recp) + RL.w;
+  E* gQL = reinterpret_cast<E*>(recp) + RL.ql;
+  E* gKT = reinterpret_cast<E*>(recp) + RL.kt;
+  E* gU = reinterpret_cast<E*>(recp) + RL.u;
+  E* gP = reinterpret_cast<E*>(recp) + RL.p;
+  float* gLC = reinterpret_cast<float*>(recp + RL.lc_bytes);
   E* RA = reinterpret_cast<E*>(sm.r1);
   E* RP = RA + C * LQ;
   E* CB = RP + C * LQ;
 
-  int rec = blockIdx.x;
-  float bnext = 0.f;
-  if (rec < nrec) {
-    issue_stage<D, C, IO, kFastThreads>(p, rec, &stg, tid);
-    if (tid < C) stg.beta[tid] = chunk_beta<IO>(p, rec, C, tid);
+  // ---------------------------------------------------------------- phase 1
+  const bool active = tid < ITEMS;
+  const int s = active ? tid / NOCT : 0;  // token segment
+  const int j = tid % NOCT;
+  const int ch = 8 * j;
+  const int pb = (TOK * s) / 16;          // 16-token block of this segment
+  const int tf = t0 + TOK * s;
+  // every global load of this phase is issued before the first wait: the head's
+  // filters (straight to LDS), the q/k/v windows, g and beta
+  const bool conv = p.conv_w != nullptr;
+  if (conv) stage_filters<D, NTH>(p.conv_w, p.H, h, sm.filt, tid);
+  Raw8<IO> win[3][TOK + 3];
+  front_load<TOK, IO>(static_cast<const IO*>(p.q), static_cast<const IO*>(p.k),
+                      static_cast<const IO*>(p.v), static_cast<const IO*>(p.conv_state_in), conv,
+                      b, p.T, p.H, D, h, ch, tf, win);
+  Raw8<IO> graw[TOK];
+  IO braw[TOK];
+  const size_t HD = (size_t)p.H * D;
+#pragma unroll
+  for (int m = 0; m < TOK; ++m) {
+    // clamped token, zeroed past the end below
+    const int t = tf + m < p.T ? tf + m : p.T - 1;
+    graw[m].load(static_cast<const IO*>(p.g) + ((size_t)b * p.T + t) * HD + (size_t)h * D + ch);
+    braw[m] = static_cast<const IO*>(p.beta)[((size_t)b * p.T + t) * p.H + h];
   }
-  for (; rec < nrec; rec += gridDim.x) {
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();  // this chunk's inputs are in LDS; the previous chunk is done with LDS
-    const int n = rec % p.NT;
-    const int t0 = n * C;
-    const int tf = t0 + 2 * s;
-    const int next = rec + (int)gridDim.x;
-    char* recp = p.ws + (size_t)rec * RL.bytes;
-    E* gW = reinterpret_cast<E*>(recp) + RL.w;
-    E* gQL = reinterpret_cast<E*>(recp) + RL.ql;
-    E* gKT = reinterpret_cast<E*>(recp) + RL.kt;
-    E* gU = reinterpret_cast<E*>(recp) + RL.u;
-    E* gP = reinterpret_cast<E*>(recp) + RL.p;
-    float* gLC = reinterpret_cast<float*>(recp + RL.lc_bytes);
-
-    // -------------------------------------------------------------- phase 1
-    // conv + SiLU + L2 norm of this thread's 2 tokens x 8 channels
-    Raw8<IO> win[3][5];
+  if (tid == 0) sm.fatal = 0;
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();  // filters are in LDS
+  float yq[TOK][8], yk[TOK][8], yv[TOK][8], qk[TOK];
+  front_compute<TOK, D, IO, false>(win, sm.filt, conv, p.conv_state_in != nullptr, ch, tf, p.T,
+                                   active, p.l2 != 0, p.eps, p.scale, yq, yk, yv, qk);
+  // cumulative log2-decay within the segment; beta and g are 0 past the end
+  float gc[TOK][8], bt[TOK];
 #pragma unroll
-    for (int x = 0; x < 3; ++x)
+  for (int m = 0; m < TOK; ++m) {
+    const bool ok = active && tf + m < p.T;
+    bt[m] = ok ? to_f32(braw[m]) : 0.f;
 #pragma unroll
-      for (int mm = 0; mm < 5; ++mm) win[x][mm].load(&stg.x[x][2 * s + mm][ch]);
-    float g2[2][8], bt[2];
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      load8(&stg.g[2 * s + m][ch], g2[m]);
-      bt[m] = stg.beta[2 * s + m];
+    for (int c = 0; c < 8; ++c) {
+      const float gv = ok ? graw[m][c] * kLog2e : 0.f;
+      gc[m][c] = m == 0 ? gv : gc[m - 1][c] + gv;
     }
-    float yq[2][8], yk[2][8], yv[2][8], qk[2];
-    // staged rows that read nothing hold zeros; tokens past the end have beta = 0
-    // and g = 0, which is all the later phases need of them
-    front_compute<2, D, IO, false, false>(win, &stg.filt[0][0][0], conv, p.conv_state_in != nullptr,
-                                          ch, tf, p.T, active, p.l2 != 0, p.eps, p.scale, yq, yk,
-                                          yv, qk);
+  }
+  if (active) store8(sm.tot + s * D + ch, gc[TOK - 1]);
+  __syncthreads();
+  // one thread per channel: exclusive scan over segments, block boundaries,
+  // midpoints and the pair factors
+  if (tid < D) {
+    const int c = tid;
+    constexpr int SPB = 16 / TOK;  // segments per block
+    float acc = 0.f;
+    float gbl[NB + 1];
+    gbl[0] = 0.f;
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int c = 0; c < 8; ++c) g2[m][c] *= kLog2e;  // log2 units from here on
-#pragma unroll
-    for (int c = 0; c < 8; ++c) g2[1][c] += g2[0][c];
-    if (tid == 0) sm.fatal = 0;
-    if (active) store8(sm.tot + s * D + ch, g2[1]);
-    __syncthreads();  // the staged inputs are consumed: start copying the next chunk's
-    if (next < nrec) {
-      issue_stage<D, C, IO, kFastThreads>(p, next, &stg, tid);
-      if (tid < C) bnext = chunk_beta<IO>(p, next, C, tid);
+    for (int s2 = 0; s2 < NSEG; ++s2) {
+      const float v = sm.tot[s2 * D + c];
+      sm.tot[s2 * D + c] = acc;
+      acc += v;
+      if ((s2 + 1) % SPB == 0) gbl[(s2 + 1) / SPB] = acc;
     }
-    // from here on, barriers wait for LDS only, so the copies stay in flight
-
-    // one thread per channel: exclusive scan over segments, block boundaries,
-    // midpoints and the pair factors
-    if (tid < D) {
-      const int c = tid;
-      float acc = 0.f;
-      float gbl[NB + 1];
-      gbl[0] = 0.f;
+    gLC[c] = __builtin_amdgcn_exp2f(acc);
+    bool fatal = false;
+    float md[NB];
 #pragma unroll
-      for (int s2 = 0; s2 < NSEG; ++s2) {
-        const float v = sm.tot[s2 * D + c];
-        sm.tot[s2 * D + c] = acc;
-        acc += v;
-        if ((s2 & 7) == 7) gbl[(s2 + 1) >> 3] = acc;
-      }
-      gLC[c] = __builtin_amdgcn_exp2f(acc);
-      bool fatal = false;
-      float md[NB];
+    for (int q = 0; q <= NB; ++q) sm.gb[q * D + c] = gbl[q];
 #pragma unroll
-      for (int q = 0; q <= NB; ++q) sm.gb[q * D + c] = gbl[q];
-#pragma unroll
-      for (int q = 0; q < NB; ++q) {
-        md[q] = 0.5f * (gbl[q] + gbl[q + 1]);
-        sm.mid[q * D + c] = md[q];
-        fatal |= gbl[q] - gbl[q + 1] > kFatalSpan2;
-      }
-#pragma unroll
-      for (int R = 1; R < NB; ++R)
-#pragma unroll
-        for (int Q = 0; Q < R; ++Q)
-          sm.mpq[pair_index(R, Q) * D + c] = __builtin_amdgcn_exp2f(md[R] - md[Q]);
-      if (fatal) atomicOr(&sm.fatal, 1);
+    for (int q = 0; q < NB; ++q) {
+      md[q] = 0.5f * (gbl[q] + gbl[q + 1]);
+      sm.mid[q * D + c] = md[q];
+      fatal |= gbl[q] - gbl[q + 1] > kFatalSpan2;
     }
-    lds_barrier();
-    if (sm.fatal) {
-      // decays too strong for the factoring: the exact preparation redoes this chunk
-      if (tid == 0) {
-        const unsigned slot = atomicAdd(p.fb_count, 1u);
-        p.fb_list[slot] = (unsigned)rec;
-      }
-    } else {
-      // operands: with Gamma_i the cumulative decay and m the midpoint of token
-      // i's block, a_i = exp(Gamma_i - m), b_i = exp(m - Gamma_i)
-      E kv[2][2][8];  // beta K Lambda and beta V, kept for the transposed images
-      if (active) {
-        float pre[8], md[8], gC[8];
-        load8(&sm.tot[s * D + ch], pre);
-        load8(&sm.mid[pb * D + ch], md);
-        load8(&sm.gb[NB * D + ch], gC);
-        float kt[2][8];
 #pragma unroll
-        for (int m = 0; m < 2; ++m) {
-          const int tl = 2 * s + m;
-          float ra[8], rp[8], cb[8], ql[8];
+    for (int R = 1; R < NB; ++R)
 #pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            const float gam = g2[m][c] + pre[c];
-            const float a = __builtin_amdgcn_exp2f(gam - md[c]);
-            const float bb = __builtin_amdgcn_exp2f(md[c] - gam);
-            const float lam = __builtin_amdgcn_exp2f(gam);
-            const float bk = bt[m] * yk[m][c];
-            ra[c] = bk * a;
-            rp[c] = yq[m][c] * a;
-            cb[c] = yk[m][c] * bb;
-            ql[c] = yq[m][c] * lam;
-            kt[m][c] = yk[m][c] * __builtin_amdgcn_exp2f(gC[c] - gam);
-            kv[0][m][c] = from_f32<E>(bk * lam);
-            kv[1][m][c] = from_f32<E>(bt[m] * yv[m][c]);
-          }
-          store8(RA + tl * LQ + ch, ra);
-          store8(RP + tl * LQ + ch, rp);
-          store8(CB + tl * LQ + ch, cb);
-          store8(gQL + (size_t)tl * D + ch, ql);
-        }
-#pragma unroll
-        for (int c = 0; c < 8; ++c) store2(gKT + (size_t)(ch + c) * C + 2 * s, kt[0][c], kt[1][c]);
-      }
-      lds_barrier();
-
-      // ------------------------------------------------------------ phase 2
-      // A^T / P^T tiles (rows j, columns i) of the lower block triangle, round
-      // robin over waves; for blocks R > Q the k b rows take the pair factor
-      constexpr int NTILE = NB * (NB + 1) / 2;
-      constexpr int TPW = (NTILE + NW - 1) / NW;
-      f32x4 accA[TPW], accP[TPW];
-      int tR[TPW], tQ[TPW];
-#pragma unroll
-      for (int i = 0; i < TPW; ++i) {
-        int idx = wave + NW * i, R = 0;
-        while (idx > R) { idx -= R + 1; ++R; }
-        tR[i] = (wave + NW * i < NTILE) ? R : -1;
-        tQ[i] = idx;
-        accA[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-        accP[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-      // channels in pieces of KC (fp32 fragments take four times the registers)
-      constexpr int KC = sizeof(E) == 2 ? D : (D < 32 ? D : 32);
-#pragma unroll
-      for (int i = 0; i < TPW; ++i) {
-        if (tR[i] < 0) continue;
-        const int R0 = tR[i], Q0 = tQ[i];
-#pragma unroll
-        for (int kc = 0; kc < D; kc += KC) {
-          RowFrag<E, KC> cf, fa, fp;
-          cf.load(CB + (16 * Q0 + r) * LQ + kc, g4);
-          if (R0 != Q0) scale_k<KC>(cf, &sm.mpq[pair_index(R0, Q0) * D + kc], g4);
-          fa.load(RA + (16 * R0 + r) * LQ + kc, g4);
-          fp.load(RP + (16 * R0 + r) * LQ + kc, g4);
-          mma<KC>(accA[i], cf, fa);
-          mma<KC>(accP[i], cf, fp);
-        }
-      }
-      lds_barrier();  // the operands are dead
-
-      // ------------------------------------------------------------ phase 3
-      float* sA = reinterpret_cast<float*>(sm.r1);  // [C][LA]
-      float* sT = sA + C * LA;                      // [C][LA]
-      float* scr = sT + C * LA;                     // [4][16][17]
-      for (int it = tid; it < C * LA; it += kFastThreads) sT[it] = 0.f;
-#pragma unroll
-      for (int i = 0; i < TPW; ++i) {
-        const int R = tR[i], Q = tQ[i];
-        if (R < 0) continue;
-        const int ii = 16 * R + r;
-        const int jj = 16 * Q + 4 * g4;
-        float av[4], pv[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool lowA = (R != Q) || (jj + e < ii);
-          const bool lowP = (R != Q) || (jj + e <= ii);
-          av[e] = lowA ? accA[i][e] : 0.f;
-          pv[e] = lowP ? accP[i][e] : 0.f;
-        }
-        *reinterpret_cast<f32x4*>(&sA[ii * LA + jj]) = f32x4{av[0], av[1], av[2], av[3]};
-        store4(gP + (size_t)ii * C + jj, pv[0], pv[1], pv[2], pv[3]);
-      }
-      lds_barrier();
-
-      // ------------------------------------------------------------ phase 4
-      // T = (I + A)^-1: diagonal 16x16 blocks by forward substitution, one
-      // column per thread
-      if (tid < C) {
-        const int pq = tid >> 4, col = tid & 15;
-        const float* Ab = sA + (16 * pq) * LA + 16 * pq;
-        float x[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float acc = (i == col) ? 1.f : 0.f;
-#pragma unroll
-          for (int jj = 0; jj < i; ++jj) acc = fmaf(-Ab[i * LA + jj], x[jj], acc);
-          x[i] = acc;
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sT[(16 * pq + i) * LA + 16 * pq + col] = x[i];
-      }
-      lds_barrier();
-      // off-diagonal blocks, block row by block row:
-      //   T_pq = -T_pp * sum_{r=q}^{p-1} A_pr T_rq
-      for (int pr = 1; pr < NB; ++pr) {
-        const int qb = wave;
-        float* xs = scr + (wave & 3) * 16 * 17;
-        if (qb < pr) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-          for (int rb = qb; rb < pr; ++rb) {
-#pragma unroll
-            for (int k0 = 0; k0 < 16; k0 += 4) {
-              const float a = sA[(16 * pr + r) * LA + 16 * rb + k0 + g4];
-              const float bv = sT[(16 * rb + k0 + g4) * LA + 16 * qb + r];
-              acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv, acc, 0, 0, 0);
-            }
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) xs[(4 * g4 + e) * 17 + r] = acc[e];
-        }
-        lds_barrier();
-        if (qb < pr) {
-          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int k0 = 0; k0 < 16; k0 += 4) {
-            const float a = sT[(16 * pr + r) * LA + 16 * pr + k0 + g4];
-            const float bv = xs[(k0 + g4) * 17 + r];
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv, acc, 0, 0, 0);
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) sT[(16 * pr + 4 * g4 + e) * LA + 16 * qb + r] = -acc[e];
-        }
-        lds_barrier();
-      }
-      // T in the matrix-core element type, after A / T / scratch
-      E* tb = reinterpret_cast<E*>(sm.r1 + SM::TB_OFF);
-      for (int it = tid; it < C * C; it += kFastThreads) {
-        const int i = it / C, jj = it % C;
-        tb[i * LT + jj] = from_f32<E>(sT[i * LA + jj]);
-      }
-      lds_barrier();  // A and T (float) are dead
-
-      // ------------------------------------------------------------ phase 5
-      // (beta K Lambda)^T and (beta V)^T as swizzled [D][C] images
-      E* klt = reinterpret_cast<E*>(sm.r1 + SM::KLT_OFF);
-      E* vt = reinterpret_cast<E*>(sm.r1 + SM::VT_OFF);
-      static_assert(SM::IMGS <= SM::TB_OFF, "transposed images stay clear of T");
-      if (active) {
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          const int at = TImg<E, C>::at(ch + c, 2 * s);
-          if constexpr (sizeof(E) == 2) {
-            typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-            *reinterpret_cast<bf16x2*>(klt + at) = bf16x2{kv[0][0][c], kv[0][1][c]};
-            *reinterpret_cast<bf16x2*>(vt + at) = bf16x2{kv[1][0][c], kv[1][1][c]};
-          } else {
-            *reinterpret_cast<float2*>(klt + at) = make_float2(kv[0][0][c], kv[0][1][c]);
-            *reinterpret_cast<float2*>(vt + at) = make_float2(kv[1][0][c], kv[1][1][c]);
-          }
-        }
-      }
-      lds_barrier();
-      // W^T tiles (c, i): A = (beta K Lambda)^T rows c, B = T rows i (j <= i)
-      constexpr int NWT = (D / 16) * NB;
-      constexpr int STEPC = RowFrag<E, C>::STEP;
-      for (int tt = wave; tt < NWT; tt += NW) {
-        const int Ct = tt / NB, It = tt % NB;
-        RowFrag<E, C> fa, fb;
-        load_timg<C>(fa, klt, 16 * Ct + r, g4);
-        fb.load(tb + (16 * It + r) * LT, g4);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        mma<C>(acc, fa, fb, (16 * It + 16 + STEPC - 1) / STEPC);
-        const int i = 16 * It + r, c = 16 * Ct + 4 * g4;
-        store4(gW + (size_t)i * D + c, acc[0], acc[1], acc[2], acc[3]);
-      }
-      // U~ tiles (i, v): A = T rows i, B = (beta V)^T rows v; stored in fragment order
-      for (int tt = wave; tt < NWT; tt += NW) {
-        const int It = tt / (D / 16), Vt = tt % (D / 16);
-        RowFrag<E, C> fa, fb;
-        fa.load(tb + (16 * It + r) * LT, g4);
-        load_timg<C>(fb, vt, 16 * Vt + r, g4);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        mma<C>(acc, fa, fb, (16 * It + 16 + STEPC - 1) / STEPC);
-        store4(gU + ((size_t)(It * (D / 16) + Vt) * 64 + lane) * 4, acc[0], acc[1], acc[2], acc[3]);
-      }
+      for (int Q = 0; Q < R; ++Q)
+        sm.mpq[pair_index(R, Q) * D + c] = __builtin_amdgcn_exp2f(md[R] - md[Q]);
+    if (fatal) atomicOr(&sm.fatal, 1);
+  }
+  __syncthreads();
+  if (sm.fatal) {
+    // decays too strong for the factoring: the exact preparation redoes this chunk
+    if (tid == 0) {
+      const unsigned slot = atomicAdd(p.fb_count, 1u);
+      p.fb_list[slot] = (unsigned)rec;
     }
-    if (next < nrec && tid < C) stg.beta[tid] = bnext;
+    return;
+  }
+  // operands: with Gamma_i the cumulative decay and m the midpoint of token
+  // i's block, a_i = exp(Gamma_i - m), b_i = exp(m - Gamma_i)
+  E kv[2][8][TOK];  // beta K Lambda and beta V, kept for the transposed images
+  if (active) {
+    float pre[8], md[8], gC[8];
+    load8(&sm.tot[s * D + ch], pre);
+    load8(&sm.mid[pb * D + ch], md);
+    load8(&sm.gb[NB * D + ch], gC);
+    float kt[8][TOK];
+#pragma unroll
+    for (int m = 0; m < TOK; ++m) {
+      const int tl = TOK * s + m;
+      float ra[8], rp[8], cb[8], ql[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float gam = gc[m][c] + pre[c];
+        const float a = __builtin_amdgcn_exp2f(gam - md[c]);
+        const float bb = __builtin_amdgcn_exp2f(md[c] - gam);
+        const float lam = __builtin_amdgcn_exp2f(gam);
+        const float bk = bt[m] * yk[m][c];
+        ra[c] = bk * a;
+        rp[c] = yq[m][c] * a;
+        cb[c] = yk[m][c] * bb;
+        ql[c] = yq[m][c] * lam;
+        kt[c][m] = yk[m][c] * __builtin_amdgcn_exp2f(gC[c] - gam);
+        kv[0][c][m] = from_f32<E>(bk * lam);
+        kv[1][c][m] = from_f32<E>(bt[m] * yv[m][c]);
+      }
+      store8(RA + tl * LQ + ch, ra);
+      store8(RP + tl * LQ + ch, rp);
+      store8(CB + tl * LQ + ch, cb);
+      store8(gQL + (size_t)tl * D + ch, ql);
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      E run[TOK];
+#pragma unroll
+      for (int m = 0; m < TOK; ++m) run[m] = from_f32<E>(kt[c][m]);
+      store_run<TOK>(gKT + (size_t)(ch + c) * C + TOK * s, run);
+    }
+  }
+  __syncthreads();
+
+  // ---------------------------------------------------------------- phase 2
+  // A^T / P^T tiles (rows j, columns i) of the lower block triangle, round robin
+  // over waves; for blocks R > Q the k b rows take the pair factor.  Channels go
+  // in pieces of KC (fp32 fragments take four times the registers).
+  constexpr int NTILE = NB * (NB + 1) / 2;
+  constexpr int TPW = (NTILE + NW - 1) / NW;
+  constexpr int KC = sizeof(E) == 2 ? D : (D < 32 ? D : 32);
+  f32x4 accA[TPW], accP[TPW];
+  int tR[TPW], tQ[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    int idx = wave + NW * i, R = 0;
+    while (idx > R) { idx -= R + 1; ++R; }
+    tR[i] = (wave + NW * i < NTILE) ? R : -1;
+    tQ[i] = idx;
+    accA[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    accP[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    if (tR[i] < 0) continue;
+    const int R0 = tR[i], Q0 = tQ[i];
+#pragma unroll
+    for (int kc = 0; kc < D; kc += KC) {
+      RowFrag<E, KC> cf, fa, fp;
+      cf.load(CB + (16 * Q0 + r) * LQ + kc, g4);
+      if (R0 != Q0) scale_k<KC>(cf, &sm.mpq[pair_index(R0, Q0) * D + kc], g4);
+      fa.load(RA + (16 * R0 + r) * LQ + kc, g4);
+      fp.load(RP + (16 * R0 + r) * LQ + kc, g4);
+      mma<KC>(accA[i], cf, fa);
+      mma<KC>(accP[i], cf, fp);
+    }
+  }
+  __syncthreads();  // the operands are dead
+
+  // ---------------------------------------------------------------- phase 3
+  float* sA = reinterpret_cast<float*>(sm.r1);  // [C][LA]
+  float* sT = sA + C * LA;                      // [C][LA]
+  float* scr = sT + C * LA;                     // [4][16][17]
+  for (int it = tid; it < C * LA; it += NTH) sT[it] = 0.f;
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int R = tR[i], Q = tQ[i];
+    if (R < 0) continue;
+    const int ii = 16 * R + r;
+    const int jj = 16 * Q + 4 * g4;
+    float av[4], pv[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool lowA = (R != Q) || (jj + e < ii);
+      const bool lowP = (R != Q) || (jj + e <= ii);
+      av[e] = lowA ? accA[i][e] : 0.f;
+      pv[e] = lowP ? accP[i][e] : 0.f;
+    }
+    *reinterpret_cast<f32x4*>(&sA[ii * LA + jj]) = f32x4{av[0], av[1], av[2], av[3]};
+    store4(gP + (size_t)ii * C + jj, pv[0], pv[1], pv[2], pv[3]);
+  }
+  __syncthreads();
+
+  // ---------------------------------------------------------------- phase 4
+  // T = (I + A)^-1: diagonal 16x16 blocks by forward substitution, one column
+  // per thread
+  if (tid < C) {
+    const int pq = tid >> 4, col = tid & 15;
+    const float* Ab = sA + (16 * pq) * LA + 16 * pq;
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float acc = (i == col) ? 1.f : 0.f;
+#pragma unroll
+      for (int jj = 0; jj < i; ++jj) acc = fmaf(-Ab[i * LA + jj], x[jj], acc);
+      x[i] = acc;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sT[(16 * pq + i) * LA + 16 * pq + col] = x[i];
+  }
+  __syncthreads();
+  // off-diagonal blocks, block row by block row (wave qb computes block column qb):
+  //   T_pq = -T_pp * sum_{r=q}^{p-1} A_pr T_rq
+  static_assert(NB - 1 <= NW, "a wave per block column");
+  for (int pr = 1; pr < NB; ++pr) {
+    const int qb = wave;
+    float* xs = scr + (wave & 3) * 16 * 17;
+    if (qb < pr) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int rb = qb; rb < pr; ++rb) {
+#pragma unroll
+        for (int k0 = 0; k0 < 16; k0 += 4) {
+          const float a = sA[(16 * pr + r) * LA + 16 * rb + k0 + g4];
+          const float bv = sT[(16 * rb + k0 + g4) * LA + 16 * qb + r];
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv, acc, 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) xs[(4 * g4 + e) * 17 + r] = acc[e];
+    }
+    __syncthreads();
+    if (qb < pr) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k0 = 0; k0 < 16; k0 += 4) {
+        const float a = sT[(16 * pr + r) * LA + 16 * pr + k0 + g4];
+        const float bv = xs[(k0 + g4) * 17 + r];
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv, acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sT[(16 * pr + 4 * g4 + e) * LA + 16 * qb + r] = -acc[e];
+    }
+    __syncthreads();
+  }
+  // T in the matrix-core element type, after A / T / scratch
+  E* tb = reinterpret_cast<E*>(sm.r1 + SM::TB_OFF);
+  for (int it = tid; it < C * C; it += NTH) {
+    const int i = it / C, jj = it % C;
+    tb[i * LT + jj] = from_f32<E>(sT[i * LA + jj]);
+  }
+  __syncthreads();  // A and T (float) are dead
+
+  // ---------------------------------------------------------------- phase 5
+  // (beta K Lambda)^T and (beta V)^T as swizzled [D][C] images
+  E* klt = reinterpret_cast<E*>(sm.r1 + SM::KLT_OFF);
+  E* vt = reinterpret_cast<E*>(sm.r1 + SM::VT_OFF);
+  static_assert(SM::IMGS <= SM::TB_OFF, "transposed images stay clear of T");
+  if (active) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int at = TImg<E, C>::at(ch + c, TOK * s);
+      store_run<TOK>(klt + at, kv[0][c]);
+      store_run<TOK>(vt + at, kv[1][c]);
+    }
+  }
+  __syncthreads();
+  // W^T tiles (c, i): A = (beta K Lambda)^T rows c, B = T rows i (j <= i)
+  constexpr int NWT = (D / 16) * NB;
+  constexpr int STEPC = RowFrag<E, C>::STEP;
+  for (int tt = wave; tt < NWT; tt += NW) {
+    const int Ct = tt / NB, It = tt % NB;
+    RowFrag<E, C> fa, fb;
+    load_timg<C>(fa, klt, 16 * Ct + r, g4);
+    fb.load(tb + (16 * It + r) * LT, g4);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    mma<C>(acc, fa, fb, (16 * It + 16 + STEPC - 1) / STEPC);
+    const int i = 16 * It + r, c = 16 * Ct + 4 * g4;
+    store4(gW + (size_t)i * D + c, acc[0], acc[1], acc[2], acc[3]);
+  }
+  // U~ tiles (i, v): A = T rows i, B = (beta V)^T rows v; stored in fragment order
+  for (int tt = wave; tt < NWT; tt += NW) {
+    const int It = tt / (D / 16), Vt = tt % (D / 16);
+    RowFrag<E, C> fa, fb;
+    fa.load(tb + (16 * It + r) * LT, g4);
+    load_timg<C>(fb, vt, 16 * Vt + r, g4);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    mma<C>(acc, fa, fb, (16 * It + 16 + STEPC - 1) / STEPC);
+    store4(gU + ((size_t)(It * (D / 16) + Vt) * 64 + lane) * 4, acc[0], acc[1], acc[2], acc[3]);
   }
 }
 
@@ -625,41 +552,11 @@ __global__ void kda_reset_count_kernel(unsigned* count) {
 }
 
 // ------------------------------------------------------------------ launchers
-// Resident workgroups of a persistent kernel on the current device: compute
-// units x workgroups per unit, taken once per device and kernel.
-template <typename K>
-static hipError_t resident_blocks(K kernel, int threads, unsigned* out) {
-  constexpr int kMaxDev = 64;
-  static int cache[kMaxDev];
-  int dev = 0;
-  if (hipError_t e = hipGetDevice(&dev); e != hipSuccess) return e;
-  if (dev >= 0 && dev < kMaxDev && cache[dev] > 0) {
-    *out = (unsigned)cache[dev];
-    return hipSuccess;
-  }
-  int cus = 0, per_cu = 0;
-  if (hipError_t e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-      e != hipSuccess)
-    return e;
-  if (hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0);
-      e != hipSuccess)
-    return e;
-  const int n = cus * (per_cu > 0 ? per_cu : 1);
-  if (dev >= 0 && dev < kMaxDev) cache[dev] = n;
-  *out = (unsigned)n;
-  return hipSuccess;
-}
-
 template <int D, int C, typename IO, typename E>
 static hipError_t launch_prep_t(const PrepParams& p, hipStream_t st) {
-  const size_t nrec = (size_t)p.B * p.H * p.NT;
-  unsigned grid = 0;
-  if (hipError_t e = resident_blocks(kda_chunk_prep_kernel<D, C, IO, E>, kFastThreads, &grid);
-      e != hipSuccess)
-    return e;
-  if (nrec < grid) grid = (unsigned)nrec;
-  hipLaunchKernelGGL((kda_chunk_prep_kernel<D, C, IO, E>), dim3(grid), dim3(kFastThreads), 0, st,
-                     p);
+  const unsigned grid = (unsigned)((size_t)p.B * p.H * p.NT);
+  hipLaunchKernelGGL((kda_chunk_prep_kernel<D, C, IO, E>), dim3(grid), dim3(fast_threads<E>()), 0,
+                     st, p);
   return hipGetLastError();
 }
 
