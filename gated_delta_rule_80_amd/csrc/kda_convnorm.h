@@ -54,13 +54,23 @@ __device__ __forceinline__ void stage_filters(const float* conv_w, int H, int h,
   }
 }
 
+// 32 zero bytes: the load source of every row that reads nothing.  A plain
+// global variable (never written), so a choice between it and an input row is
+// still a global address and the loads stay global loads.
+static __device__ __attribute__((aligned(16))) float kZeroRow[8];
+
+template <typename IO>
+__device__ __forceinline__ const IO* zero_row() {
+  return reinterpret_cast<const IO*>(kZeroRow);
+}
+
 // Raw rows of q, k, v (x = 0, 1, 2) for one thread's tile of TOK tokens from
 // t_first, channels [ch, ch + 8) of head h.  With the convolution, row m holds
 // token t_first - 3 + m (TOK + 3 rows); tokens < 0 read the carried state
 // ([B][3 tensors][3 taps][H*D], oldest tap first).  Without it, row 3 + m holds
 // token t_first + m.  Rows that read nothing (tokens >= T, or < 0 with no state)
-// load a valid row and are zeroed by front_compute, so every load is issued
-// unconditionally and all of them are in flight together.  Needs T > 0.
+// read zeros, so every load is issued unconditionally and all of them are in
+// flight together.
 template <int TOK, typename IO>
 __device__ __forceinline__ void front_load(const IO* q, const IO* k, const IO* v, const IO* state,
                                            bool conv, int b, int T, int H, int D, int h, int ch,
@@ -71,15 +81,14 @@ __device__ __forceinline__ void front_load(const IO* q, const IO* k, const IO* v
   if (conv) {
 #pragma unroll
     for (int x = 0; x < 3; ++x) {
-      const IO* srow = state == nullptr ? src[x] + row0
+      const IO* srow = state == nullptr ? nullptr
                                         : state + ((size_t)b * 3 + x) * 3 * HD + (size_t)h * D + ch;
 #pragma unroll
       for (int m = 0; m < TOK + 3; ++m) {
         const int t = t_first - 3 + m;
-        const bool in_seq = t >= 0 && t < T;
-        const bool in_state = t < 0 && state != nullptr;
-        const IO* ptr = in_seq ? src[x] + row0 + (size_t)t * HD
-                               : (in_state ? srow + (size_t)(3 + t) * HD : src[x] + row0);
+        const IO* ptr = zero_row<IO>();
+        if (t >= 0 && t < T) ptr = src[x] + row0 + (size_t)t * HD;
+        else if (t < 0 && srow != nullptr) ptr = srow + (size_t)(3 + t) * HD;
         win[x][m].load(ptr);
       }
     }
@@ -89,7 +98,7 @@ __device__ __forceinline__ void front_load(const IO* q, const IO* k, const IO* v
 #pragma unroll
       for (int m = 0; m < TOK; ++m) {
         const int t = t_first + m;
-        win[x][3 + m].load(src[x] + row0 + (size_t)(t < T ? t : T - 1) * HD);
+        win[x][3 + m].load(t < T ? src[x] + row0 + (size_t)t * HD : zero_row<IO>());
       }
   }
 }
@@ -99,13 +108,12 @@ __device__ __forceinline__ void front_load(const IO* q, const IO* k, const IO* v
 // lanes of a group of D/8 consecutive lanes (the channels of one token row) must
 // call this together: the L2 sums are reduced across that group.  On return q is
 // normalised and multiplied by `scale`, k normalised, v convolved; qk[m] =
-// <q_m, k_m> of the returned values (0 unless WANT_QK).  With MASK, rows that
-// read nothing are zeroed here and tokens >= T and inactive lanes give zeros;
-// without it the rows must already hold zeros where nothing was read, and the
-// outputs of tokens >= T are left as computed (finite).
+// <q_m, k_m> of the returned values (0 unless WANT_QK).  With MASK, tokens >= T
+// and inactive lanes give zeros; without it their outputs are left as computed
+// (finite).
 template <int TOK, int D, typename IO, bool WANT_QK = true, bool MASK = true>
 __device__ __forceinline__ void front_compute(const Raw8<IO> (&win)[3][TOK + 3], const float* filt,
-                                              bool conv, bool has_state, int ch, int t_first,
+                                              bool conv, int ch, int t_first,
                                               int T, bool active, bool l2, float eps, float scale,
                                               float (&yq)[TOK][8], float (&yk)[TOK][8],
                                               float (&yv)[TOK][8], float (&qk)[TOK]) {
@@ -115,12 +123,9 @@ __device__ __forceinline__ void front_compute(const Raw8<IO> (&win)[3][TOK + 3],
     if (conv) {
       float rows[TOK + 3][8];
 #pragma unroll
-      for (int m = 0; m < TOK + 3; ++m) {
-        const int t = t_first - 3 + m;
-        const bool ok = !MASK || (t >= 0 && t < T) || (t < 0 && has_state);
+      for (int m = 0; m < TOK + 3; ++m)
 #pragma unroll
-        for (int c = 0; c < 8; ++c) rows[m][c] = ok ? win[x][m][c] : 0.f;
-      }
+        for (int c = 0; c < 8; ++c) rows[m][c] = win[x][m][c];
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         const f32x4 w = *reinterpret_cast<const f32x4*>(filt + ((size_t)x * D + ch + c) * 4);

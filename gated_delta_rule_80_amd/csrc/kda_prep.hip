@@ -72,9 +72,12 @@ struct FastSmem {
   static constexpr int R1 = OPS > LAST ? OPS : LAST;
   alignas(16) char r1[R1];
   alignas(16) float tot[NSEG * D];     // segment totals, then exclusive prefixes
-  alignas(16) float gb[(NB + 1) * D];  // Gamma at block boundaries: gb[p] = Gamma before block p
-  alignas(16) float mid[NB * D];       // block midpoints (gb[p] + gb[p + 1]) / 2
-  alignas(16) float mpq[NPAIR * D];    // exp(mid[R] - mid[Q]) for blocks R > Q
+  // per block p and channel, with G_p the cumulative decay before block p and
+  // m_p = (G_p + G_{p+1}) / 2:
+  alignas(16) float mid[NB * D];       // m_p
+  alignas(16) float emid[NB * D];      // exp(m_p)
+  alignas(16) float ecm[NB * D];       // exp(Gamma_C - m_p)
+  alignas(16) float mpq[NPAIR * D];    // exp(m_R - m_Q) for blocks R > Q
   alignas(16) float filt[3 * D * 4];   // the head's conv filters [q, k, v][D][4]
   int fatal;
 };
@@ -198,26 +201,28 @@ __global__ __launch_bounds__(fast_threads<E>()) void kda_chunk_prep_kernel(PrepP
   const size_t HD = (size_t)p.H * D;
 #pragma unroll
   for (int m = 0; m < TOK; ++m) {
-    // clamped token, zeroed past the end below
+    // past the end: g reads zeros, beta is zeroed below
     const int t = tf + m < p.T ? tf + m : p.T - 1;
-    graw[m].load(static_cast<const IO*>(p.g) + ((size_t)b * p.T + t) * HD + (size_t)h * D + ch);
+    graw[m].load(tf + m < p.T ? static_cast<const IO*>(p.g) + ((size_t)b * p.T + t) * HD +
+                                    (size_t)h * D + ch
+                              : zero_row<IO>());
     braw[m] = static_cast<const IO*>(p.beta)[((size_t)b * p.T + t) * p.H + h];
   }
   if (tid == 0) sm.fatal = 0;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();  // filters are in LDS
   float yq[TOK][8], yk[TOK][8], yv[TOK][8], qk[TOK];
-  front_compute<TOK, D, IO, false>(win, sm.filt, conv, p.conv_state_in != nullptr, ch, tf, p.T,
-                                   active, p.l2 != 0, p.eps, p.scale, yq, yk, yv, qk);
-  // cumulative log2-decay within the segment; beta and g are 0 past the end
+  front_compute<TOK, D, IO, false, false>(win, sm.filt, conv, ch, tf, p.T, active, p.l2 != 0,
+                                          p.eps, p.scale, yq, yk, yv, qk);
+  // cumulative log2-decay within the segment.  Past the end of the sequence g
+  // and beta are 0, which is all the later phases need of those tokens.
   float gc[TOK][8], bt[TOK];
 #pragma unroll
   for (int m = 0; m < TOK; ++m) {
-    const bool ok = active && tf + m < p.T;
-    bt[m] = ok ? to_f32(braw[m]) : 0.f;
+    bt[m] = tf + m < p.T ? to_f32(braw[m]) : 0.f;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const float gv = ok ? graw[m][c] * kLog2e : 0.f;
+      const float gv = graw[m][c] * kLog2e;
       gc[m][c] = m == 0 ? gv : gc[m - 1][c] + gv;
     }
   }
@@ -242,11 +247,11 @@ __global__ __launch_bounds__(fast_threads<E>()) void kda_chunk_prep_kernel(PrepP
     bool fatal = false;
     float md[NB];
 #pragma unroll
-    for (int q = 0; q <= NB; ++q) sm.gb[q * D + c] = gbl[q];
-#pragma unroll
     for (int q = 0; q < NB; ++q) {
       md[q] = 0.5f * (gbl[q] + gbl[q + 1]);
       sm.mid[q * D + c] = md[q];
+      sm.emid[q * D + c] = __builtin_amdgcn_exp2f(md[q]);
+      sm.ecm[q * D + c] = __builtin_amdgcn_exp2f(acc - md[q]);
       fatal |= gbl[q] - gbl[q + 1] > kFatalSpan2;
     }
 #pragma unroll
@@ -266,13 +271,17 @@ __global__ __launch_bounds__(fast_threads<E>()) void kda_chunk_prep_kernel(PrepP
     return;
   }
   // operands: with Gamma_i the cumulative decay and m the midpoint of token
-  // i's block, a_i = exp(Gamma_i - m), b_i = exp(m - Gamma_i)
+  // i's block, a_i = exp(Gamma_i - m), b_i = exp(m - Gamma_i), and
+  //   Lambda_i = a_i exp(m),   exp(Gamma_C - Gamma_i) = b_i exp(Gamma_C - m).
+  // (Where exp(m) or exp(Gamma_C - m) underflows, the true value is below
+  // exp(s/2) times that, far under the rounding of the other terms.)
   E kv[2][8][TOK];  // beta K Lambda and beta V, kept for the transposed images
   if (active) {
-    float pre[8], md[8], gC[8];
+    float pre[8], md[8], em[8], ec[8];
     load8(&sm.tot[s * D + ch], pre);
     load8(&sm.mid[pb * D + ch], md);
-    load8(&sm.gb[NB * D + ch], gC);
+    load8(&sm.emid[pb * D + ch], em);
+    load8(&sm.ecm[pb * D + ch], ec);
     float kt[8][TOK];
 #pragma unroll
     for (int m = 0; m < TOK; ++m) {
@@ -283,13 +292,13 @@ __global__ __launch_bounds__(fast_threads<E>()) void kda_chunk_prep_kernel(PrepP
         const float gam = gc[m][c] + pre[c];
         const float a = __builtin_amdgcn_exp2f(gam - md[c]);
         const float bb = __builtin_amdgcn_exp2f(md[c] - gam);
-        const float lam = __builtin_amdgcn_exp2f(gam);
+        const float lam = a * em[c];
         const float bk = bt[m] * yk[m][c];
         ra[c] = bk * a;
         rp[c] = yq[m][c] * a;
         cb[c] = yk[m][c] * bb;
         ql[c] = yq[m][c] * lam;
-        kt[c][m] = yk[m][c] * __builtin_amdgcn_exp2f(gC[c] - gam);
+        kt[c][m] = yk[m][c] * (bb * ec[c]);
         kv[0][c][m] = from_f32<E>(bk * lam);
         kv[1][c][m] = from_f32<E>(bt[m] * yv[m][c]);
       }
@@ -491,8 +500,8 @@ __global__ __launch_bounds__(256) void kda_conv_norm_kernel(ConvNormParams p) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();  // filters are in LDS
   float yq[TT][8], yk[TT][8], yv[TT][8], qk[TT];
-  front_compute<TT, D, IO>(win, filt, true, p.conv_state_in != nullptr, 8 * j, tf, p.T, active,
-                           p.l2 != 0, p.eps, 1.0f, yq, yk, yv, qk);
+  front_compute<TT, D, IO>(win, filt, true, 8 * j, tf, p.T, active, p.l2 != 0, p.eps, 1.0f, yq,
+                           yk, yv, qk);
   if (!active) return;
   const size_t HD = (size_t)p.H * D;
   IO* oq = static_cast<IO*>(p.q_out);

@@ -127,8 +127,8 @@ __global__ __launch_bounds__(kPrepThreads) void kda_chunk_prep_exact_kernel(Prep
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();  // filters are in LDS
   float yq[4][8], yk[4][8], yv[4][8], qk[4];
-  front_compute<4, D, IO>(win, sm.filt, conv, cs != nullptr, ch, tf, p.T, active, p.l2 != 0,
-                          p.eps, p.scale, yq, yk, yv, qk);
+  front_compute<4, D, IO>(win, sm.filt, conv, ch, tf, p.T, active, p.l2 != 0, p.eps, p.scale, yq,
+                          yk, yv, qk);
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     const bool ok = active && tf + m < p.T;
