@@ -81,12 +81,19 @@ kda::WorkspaceLayout ws_layout(const kda_prefill_args* a) {
   return kda::workspace_layout((size_t)a->B * a->H * NT, a->chunk, a->D, esize(a->io));
 }
 
-// Choice of the value-column block of the state walk: narrower blocks give more
-// parallel walks when B * H is small.
-int state_vblock(int B, int H, int D) {
-  if (D < 64) return D;
+// Value columns per state-walk workgroup and its thread count.  Every workgroup
+// streams the chunk's W, Q Lambda, Ktil^T and P whatever its value block, so
+// wider blocks read less per column; with bf16 at D = 128, 64 columns on 512
+// threads measured fastest at B * H = 96 and 384.  Narrower blocks give more
+// parallel walks elsewhere.
+struct StateCfg {
+  int vb, threads;
+};
+StateCfg state_config(int B, int H, int D, bool fp32) {
+  if (D < 64) return {D, 256};
+  if (D == 128 && !fp32) return {64, 512};
   const long walks64 = (long)B * H * (D / 64);
-  return walks64 < 240 ? 32 : 64;
+  return {walks64 < 240 ? 32 : 64, 256};
 }
 
 }  // namespace
@@ -204,7 +211,8 @@ static kda_status run_stage(const kda_prefill_args* a, void* ws, int stage, hipS
       p.S0 = a->S0; p.S_T = a->S_T; p.o = a->o;
       p.B = a->B; p.T = a->T; p.H = a->H; p.NT = NT;
       return hip_status(
-          kda::launch_state(p, a->D, a->chunk, fp32, state_vblock(a->B, a->H, a->D), st));
+          kda::launch_state(p, a->D, a->chunk, fp32, state_config(a->B, a->H, a->D, fp32).vb,
+                            state_config(a->B, a->H, a->D, fp32).threads, st));
     }
     case KDA_STAGE_CONV_TAIL: {
       if (a->conv_k == 0 || a->conv_state_out == nullptr) return KDA_OK;

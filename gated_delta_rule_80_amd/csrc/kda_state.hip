@@ -1,7 +1,8 @@
-// State walk of the KDA prefill: one workgroup per (sequence, head, block of VB
-// value columns), walking the chunks of the sequence in order.  Value columns of
-// the state evolve independently (every product below is column-wise in v), so
-// splitting them across workgroups is exact and gives B*H*(D/VB) parallel walks.
+// State walk of the KDA prefill: one workgroup (4 or 8 waves) per (sequence,
+// head, block of VB value columns), walking the chunks of the sequence in order.
+// Value columns of the state evolve independently (every product below is
+// column-wise in v), so splitting them across workgroups is exact and gives
+// B*H*(D/VB) parallel walks.
 //
 // Per chunk, with S the D x VB float32 state block at the chunk start and the
 // chunk record written by the preparation kernel:
@@ -24,7 +25,6 @@
 
 namespace kda {
 
-constexpr int kStateThreads = 256;
 
 // 4 consecutive elements kept raw until used
 template <typename E> struct Raw4;
@@ -55,8 +55,9 @@ struct RecImage {
   static_assert(BYTES % 16 == 0, "record image is whole 16-byte chunks");
 };
 
-template <int D, int C, int VB, typename IO, typename E>
-__global__ __launch_bounds__(kStateThreads, 2) void kda_chunk_state_kernel(StateParams p) {
+template <int D, int C, int VB, typename IO, typename E, int NT>
+__global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void kda_chunk_state_kernel(StateParams p) {
+  constexpr int NW = NT / 64;  // waves
   constexpr int PE = 16 / (int)sizeof(E);
   constexpr int ES = (int)sizeof(E);
   constexpr int LS = D + PE;  // sS row stride: row = value column v, k = key channel c
@@ -65,13 +66,14 @@ __global__ __launch_bounds__(kStateThreads, 2) void kda_chunk_state_kernel(State
   constexpr int VT = VB / 16;   // v-tiles
   constexpr int RT = C / 16;    // t-tiles
   constexpr int CT = D / 16;    // c-tiles
-  static_assert(4 % RT == 0 || RT == 4, "t-tiles must divide the 4 waves");
-  constexpr int NU = (RT * VT + 3) / 4;      // (t-tile, v-tile) units per wave (upper bound)
-  constexpr int NS = (CT * VT + 3) / 4;      // (c-tile, v-tile) units per wave (upper bound)
-  constexpr int CTW = CT < 4 ? CT : 4;       // c-tile stride between a wave's units
-  constexpr int NCTW = CT > 4 ? CT / 4 : 1;  // distinct c-tiles per wave
-  constexpr bool FULL_U = (RT * VT) % 4 == 0;
-  constexpr bool FULL_S = (CT * VT) % 4 == 0;
+  static_assert(NW % RT == 0, "every unit of a wave has the same t-tile");
+  static_assert(CT <= NW || CT % NW == 0, "every unit of a wave has one of NCTW c-tiles");
+  constexpr int NU = (RT * VT + NW - 1) / NW;  // (t-tile, v-tile) units per wave (upper bound)
+  constexpr int NS = (CT * VT + NW - 1) / NW;  // (c-tile, v-tile) units per wave (upper bound)
+  constexpr int CTW = CT < NW ? CT : NW;       // c-tile stride between a wave's units
+  constexpr int NCTW = CT > NW ? CT / NW : 1;  // distinct c-tiles per wave
+  constexpr bool FULL_U = (RT * VT) % NW == 0;
+  constexpr bool FULL_S = (CT * VT) % NW == 0;
   constexpr RecordLayout RL = record_layout(C, D, sizeof(E));
   using IMG = RecImage<D, C, VB, E>;
   __shared__ __attribute__((aligned(16))) char img[IMG::BYTES];
@@ -104,14 +106,14 @@ __global__ __launch_bounds__(kStateThreads, 2) void kda_chunk_state_kernel(State
   // ---- asynchronous copy of a chunk's record image into LDS.  Thread tid moves
   // 16-byte chunk it * 256 + tid of the image; its source offset inside the
   // record is the same for every chunk, so it is computed once.
-  constexpr int ITERS = (IMG::CHUNKS + kStateThreads - 1) / kStateThreads;
+  constexpr int ITERS = (IMG::CHUNKS + NT - 1) / NT;
   uint32_t src_off[ITERS];
 #pragma unroll
   for (int it = 0; it < ITERS; ++it) {
     constexpr int RCD = D * ES / 16;           // chunks per row of W, QL
     constexpr int RCC = C * ES / 16;           // chunks per row of KT, P
     constexpr int UPIECE = VT * 64 * 4 * ES / 16;  // chunks of U~ per t-tile: VT tiles x 64 lanes x 4
-    const int idx = it * kStateThreads + tid;
+    const int idx = it * NT + tid;
     const int byte = idx * 16;
     size_t off;
     if (byte < IMG::KT) {
@@ -140,11 +142,11 @@ __global__ __launch_bounds__(kStateThreads, 2) void kda_chunk_state_kernel(State
     const char* recp = p.ws + ((size_t)bh * p.NT + n) * RL.bytes;
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
-      // this wave's 64 lanes fill img + (it * 256 + 64 * wave) * 16 onwards, 16 bytes per lane
-      if (it * kStateThreads + tid < IMG::CHUNKS)
+      // this wave's 64 lanes fill img + (it * NT + 64 * wave) * 16 onwards, 16 bytes per lane
+      if (it * NT + tid < IMG::CHUNKS)
         __builtin_amdgcn_global_load_lds(
             (const glb_void_t*)(recp + src_off[it]),
-            (lds_void_t*)(img + (size_t)(it * kStateThreads + 64 * wave) * 16), 16, 0, 0);
+            (lds_void_t*)(img + (size_t)(it * NT + 64 * wave) * 16), 16, 0, 0);
     }
   };
 
@@ -153,7 +155,7 @@ __global__ __launch_bounds__(kStateThreads, 2) void kda_chunk_state_kernel(State
   const size_t sbase = (size_t)bh * D * D;
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
-    const int u = wave + 4 * i;
+    const int u = wave + NW * i;
     accS[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     if ((FULL_S || u < CT * VT) && p.S0 != nullptr) {
       const int Ct = u % CT, Vt = u / CT;
@@ -165,7 +167,7 @@ __global__ __launch_bounds__(kStateThreads, 2) void kda_chunk_state_kernel(State
   auto stage_state = [&]() {
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
-      const int u = wave + 4 * i;
+      const int u = wave + NW * i;
       if (FULL_S || u < CT * VT) {
         const int Ct = u % CT, Vt = u / CT;
         store4(&sS[(16 * Vt + r) * LS + 16 * Ct + 4 * g4], accS[i][0], accS[i][1], accS[i][2],
@@ -184,10 +186,28 @@ __global__ __launch_bounds__(kStateThreads, 2) void kda_chunk_state_kernel(State
   const E* iU = reinterpret_cast<const E*>(img + IMG::U);
   const float* iLC = reinterpret_cast<const float*>(img + IMG::LC);
 
+  // The output of chunk n is stored during step n + 1, right after the copy of
+  // chunk n + 2 is issued, so the stores retire while step n + 1 computes instead
+  // of delaying the wait for the next copy.
+  f32x4 pendO[NU];
+  auto store_out = [&](int nn) {
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+      const int u = wave + NW * i;
+      if (FULL_U || u < RT * VT) {
+        const int Vt = u / RT;
+        const int t = nn * C + 16 * R + r;
+        if (t < p.T)
+          store4(o + ((size_t)b * p.T + t) * HD + (size_t)h * D + vb0 + 16 * Vt + 4 * g4,
+                 pendO[i][0], pendO[i][1], pendO[i][2], pendO[i][3]);
+      }
+    }
+  };
+
   issue_copy(0);
   for (int n = 0; n < p.NT; ++n) {
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies (and stores) have landed
-    __syncthreads();                // the whole image of chunk n and the state are in LDS
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of chunk n (and older stores) are done
+    lds_barrier();                  // the whole image of chunk n and the state are in LDS
     // ---- this chunk's fragments, from the image into registers
     RowFrag<E, D> fw, fql;
     RowFrag<E, C> fp;
@@ -201,24 +221,25 @@ __global__ __launch_bounds__(kStateThreads, 2) void kda_chunk_state_kernel(State
     }
 #pragma unroll
     for (int j = 0; j < NCTW; ++j) {
-      const int Ct = (wave % CTW) + 4 * j;
+      const int Ct = (wave % CTW) + CTW * j;
       load_swz<C>(fkt[j], iKT, 16 * Ct + r, g4);
       flc[j] = *reinterpret_cast<const f32x4*>(iLC + 16 * Ct + 4 * g4);
     }
 #pragma unroll
     for (int i = 0; i < NU; ++i) {
-      const int u = wave + 4 * i;
+      const int u = wave + NW * i;
       if (FULL_U || u < RT * VT) fu[i].load(iU + ((size_t)(R * VT + u / RT) * 64 + lane) * 4);
     }
-    __syncthreads();  // every wave holds its fragments: the image may be overwritten
+    lds_barrier();  // every wave holds its fragments: the image may be overwritten
     if (n + 1 < p.NT) issue_copy(n + 1);
+    if (n > 0) store_out(n - 1);
     if (has_u) fp.mask_above(i_row, g4);
 
     // ---- U = U~ - W S  and  O^T = S^T QL^T
     f32x4 accO[NU];
 #pragma unroll
     for (int i = 0; i < NU; ++i) {
-      const int u = wave + 4 * i;
+      const int u = wave + NW * i;
       accO[i] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (FULL_U || u < RT * VT) {
         const int Vt = u / RT;
@@ -235,25 +256,22 @@ __global__ __launch_bounds__(kStateThreads, 2) void kda_chunk_state_kernel(State
     // ---- O^T += U^T P^T (j <= i), store O
 #pragma unroll
     for (int i = 0; i < NU; ++i) {
-      const int u = wave + 4 * i;
+      const int u = wave + NW * i;
       if (FULL_U || u < RT * VT) {
         const int Vt = u / RT;
         RowFrag<E, C> uf;
         uf.load(sU + (16 * Vt + r) * LU, g4);
         mma<C>(accO[i], uf, fp, csteps);
-        const int t = n * C + 16 * R + r;
-        if (t < p.T)
-          store4(o + ((size_t)b * p.T + t) * HD + (size_t)h * D + vb0 + 16 * Vt + 4 * g4,
-                 accO[i][0], accO[i][1], accO[i][2], accO[i][3]);
+        pendO[i] = accO[i];
       }
     }
     // ---- S = Diag(Lambda_C) S + Ktil^T U
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
-      const int u = wave + 4 * i;
+      const int u = wave + NW * i;
       if (FULL_S || u < CT * VT) {
         const int Vt = u / CT;
-        const int j = i % NCTW;  // this unit's c-tile is (wave % CTW) + 4 * j
+        const int j = i % NCTW;  // this unit's c-tile is (wave % CTW) + CTW * j
         RowFrag<E, C> uf;
         uf.load(sU + (16 * Vt + r) * LU, g4);
 #pragma unroll
@@ -263,11 +281,12 @@ __global__ __launch_bounds__(kStateThreads, 2) void kda_chunk_state_kernel(State
     }
     stage_state();
   }
+  if (p.NT > 0) store_out(p.NT - 1);
   // ---- final state
   if (p.S_T != nullptr) {
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
-      const int u = wave + 4 * i;
+      const int u = wave + NW * i;
       if (FULL_S || u < CT * VT) {
         const int Ct = u % CT, Vt = u / CT;
 #pragma unroll
@@ -279,47 +298,58 @@ __global__ __launch_bounds__(kStateThreads, 2) void kda_chunk_state_kernel(State
 }
 
 template <int D, int C, typename IO, typename E>
-static hipError_t launch_state_t(const StateParams& p, int vb, hipStream_t st) {
+static hipError_t launch_state_t(const StateParams& p, int vb, int threads, hipStream_t st) {
+  // vb value columns per workgroup (32 or 64, or D when D < 64); 512 threads only
+  // with D = 128 and vb = 64
+  const size_t BH = (size_t)p.B * p.H;
+  if constexpr (D == 128) {
+    if (vb == 64 && threads == 512) {
+      hipLaunchKernelGGL((kda_chunk_state_kernel<D, C, 64, IO, E, 512>), dim3((unsigned)(BH * 2)),
+                         dim3(512), 0, st, p);
+      return hipGetLastError();
+    }
+  }
+  if (threads != 256) return hipErrorInvalidValue;
   constexpr int VBmax = D >= 64 ? 64 : D;
   if (vb == 32 && D >= 32) {
     constexpr int VB = D >= 32 ? 32 : D;
-    const unsigned grid = (unsigned)((size_t)p.B * p.H * (D / VB));
-    hipLaunchKernelGGL((kda_chunk_state_kernel<D, C, VB, IO, E>), dim3(grid),
-                       dim3(kStateThreads), 0, st, p);
+    hipLaunchKernelGGL((kda_chunk_state_kernel<D, C, VB, IO, E, 256>), dim3((unsigned)(BH * (D / VB))),
+                       dim3(256), 0, st, p);
   } else {
-    const unsigned grid = (unsigned)((size_t)p.B * p.H * (D / VBmax));
-    hipLaunchKernelGGL((kda_chunk_state_kernel<D, C, VBmax, IO, E>), dim3(grid),
-                       dim3(kStateThreads), 0, st, p);
+    hipLaunchKernelGGL((kda_chunk_state_kernel<D, C, VBmax, IO, E, 256>),
+                       dim3((unsigned)(BH * (D / VBmax))), dim3(256), 0, st, p);
   }
   return hipGetLastError();
 }
 
 template <int D, typename IO, typename E>
-static hipError_t launch_state_c(const StateParams& p, int C, int vb, hipStream_t st) {
+static hipError_t launch_state_c(const StateParams& p, int C, int vb, int threads, hipStream_t st) {
   switch (C) {
-    case 16: return launch_state_t<D, 16, IO, E>(p, vb, st);
-    case 32: return launch_state_t<D, 32, IO, E>(p, vb, st);
+    case 16: return launch_state_t<D, 16, IO, E>(p, vb, threads, st);
+    case 32: return launch_state_t<D, 32, IO, E>(p, vb, threads, st);
     case 64:
       if constexpr (sizeof(E) == 4 && D == 128) return hipErrorInvalidValue;
-      else return launch_state_t<D, 64, IO, E>(p, vb, st);
+      else return launch_state_t<D, 64, IO, E>(p, vb, threads, st);
   }
   return hipErrorInvalidValue;
 }
 
 template <typename IO, typename E>
-static hipError_t launch_state_d(const StateParams& p, int D, int C, int vb, hipStream_t st) {
+static hipError_t launch_state_d(const StateParams& p, int D, int C, int vb, int threads,
+                                 hipStream_t st) {
   switch (D) {
-    case 16: return launch_state_c<16, IO, E>(p, C, vb, st);
-    case 32: return launch_state_c<32, IO, E>(p, C, vb, st);
-    case 64: return launch_state_c<64, IO, E>(p, C, vb, st);
-    case 128: return launch_state_c<128, IO, E>(p, C, vb, st);
+    case 16: return launch_state_c<16, IO, E>(p, C, vb, threads, st);
+    case 32: return launch_state_c<32, IO, E>(p, C, vb, threads, st);
+    case 64: return launch_state_c<64, IO, E>(p, C, vb, threads, st);
+    case 128: return launch_state_c<128, IO, E>(p, C, vb, threads, st);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_state(const StateParams& p, int D, int C, bool fp32, int vb, hipStream_t st) {
-  return fp32 ? launch_state_d<float, float>(p, D, C, vb, st)
-              : launch_state_d<__bf16, __bf16>(p, D, C, vb, st);
+hipError_t launch_state(const StateParams& p, int D, int C, bool fp32, int vb, int threads,
+                        hipStream_t st) {
+  return fp32 ? launch_state_d<float, float>(p, D, C, vb, threads, st)
+              : launch_state_d<__bf16, __bf16>(p, D, C, vb, threads, st);
 }
 
 }  // namespace kda
