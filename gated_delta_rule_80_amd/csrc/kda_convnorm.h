@@ -19,11 +19,38 @@ __device__ __forceinline__ float silu_fast(float x) {
   return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-kLog2e * x));
 }
 
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t BufRes;
+
+// Buffer resource over `bytes` bytes from `base` (raw, no stride).  Loads through
+// it are range checked: an access at or past `bytes` -- a negative 32-bit offset
+// included -- returns zeros.  The third word selects 32-bit data format, as
+// untyped loads need on gfx9.
+// base and bytes must be the same in every lane; they are moved to scalar
+// registers explicitly (a resource computed in vector registers would otherwise
+// be legalised with a loop over lanes).
+__device__ __forceinline__ BufRes make_buf(const void* base, unsigned bytes) {
+  const unsigned long long a = reinterpret_cast<unsigned long long>(base);
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)a);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
+  void* sbase = reinterpret_cast<void*>(((unsigned long long)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(sbase, (short)0,
+                                           (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
 // 8 consecutive elements kept unconverted while their load is in flight.
 template <typename IO> struct Raw8;
 template <> struct Raw8<__bf16> {
   bf16x8 v;
   __device__ __forceinline__ void load(const __bf16* p) { v = *reinterpret_cast<const bf16x8*>(p); }
+  // range-checked load (zeros where voff is outside the buffer); offsets in bytes
+  __device__ __forceinline__ void load(BufRes r, int voff, int soff) {
+    v = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+  }
+  // bitwise or (one of the two is all zeros)
+  __device__ __forceinline__ void merge(const Raw8& o) {
+    v = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, v) | __builtin_bit_cast(u32x4, o.v));
+  }
   __device__ __forceinline__ float operator[](int c) const { return (float)v[c]; }
 };
 template <> struct Raw8<float> {
@@ -31,6 +58,14 @@ template <> struct Raw8<float> {
   __device__ __forceinline__ void load(const float* p) {
     a = *reinterpret_cast<const f32x4*>(p);
     b = *reinterpret_cast<const f32x4*>(p + 4);
+  }
+  __device__ __forceinline__ void load(BufRes r, int voff, int soff) {
+    a = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+    b = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16, soff, 0));
+  }
+  __device__ __forceinline__ void merge(const Raw8& o) {
+    a = __builtin_bit_cast(f32x4, __builtin_bit_cast(u32x4, a) | __builtin_bit_cast(u32x4, o.a));
+    b = __builtin_bit_cast(f32x4, __builtin_bit_cast(u32x4, b) | __builtin_bit_cast(u32x4, o.b));
   }
   __device__ __forceinline__ float operator[](int c) const { return c < 4 ? a[c] : b[c - 4]; }
 };
@@ -54,52 +89,59 @@ __device__ __forceinline__ void stage_filters(const float* conv_w, int H, int h,
   }
 }
 
-// 32 zero bytes: the load source of every row that reads nothing.  A plain
-// global variable (never written), so a choice between it and an input row is
-// still a global address and the loads stay global loads.
-static __device__ __attribute__((aligned(16))) float kZeroRow[8];
-
-template <typename IO>
-__device__ __forceinline__ const IO* zero_row() {
-  return reinterpret_cast<const IO*>(kZeroRow);
-}
-
 // Raw rows of q, k, v (x = 0, 1, 2) for one thread's tile of TOK tokens from
-// t_first, channels [ch, ch + 8) of head h.  With the convolution, row m holds
-// token t_first - 3 + m (TOK + 3 rows); tokens < 0 read the carried state
+// t_first, channels [ch, ch + 8) of head h.  The workgroup's threads together
+// cover tokens [t_base, t_base + n_tok) (the same values for all of them).  With the convolution, row m holds token
+// t_first - 3 + m (TOK + 3 rows); tokens < 0 read the carried state
 // ([B][3 tensors][3 taps][H*D], oldest tap first).  Without it, row 3 + m holds
-// token t_first + m.  Rows that read nothing (tokens >= T, or < 0 with no state)
-// read zeros, so every load is issued unconditionally and all of them are in
-// flight together.
+// token t_first + m.  Rows that read nothing (tokens >= T, or < 0 with no
+// state) read zeros: every row goes through a range-checked buffer load whose
+// range ends at the sequence's last row (or the state's last tap; the check is
+// on the per-lane offset, where rows before the range wrap to huge values), so
+// all loads are issued unconditionally with 32-bit offset arithmetic.  Needs
+// T > 0 and (n_tok + 3) * H * D * sizeof(IO) < 2 GiB.
 template <int TOK, typename IO>
 __device__ __forceinline__ void front_load(const IO* q, const IO* k, const IO* v, const IO* state,
                                            bool conv, int b, int T, int H, int D, int h, int ch,
-                                           int t_first, Raw8<IO> (&win)[3][TOK + 3]) {
-  const size_t HD = (size_t)H * D;
-  const size_t row0 = (size_t)b * T * HD + (size_t)h * D + ch;
-  const IO* src[3] = {q, k, v};
-  if (conv) {
+                                           int t_base, int n_tok, int t_first,
+                                           Raw8<IO> (&win)[3][TOK + 3]) {
+  constexpr int ES = (int)sizeof(IO);
+  const long HD = (long)H * D;
+  // rows [r0, r1) of this sequence and head: from the first row any thread reads
+  // to the last one that exists
+  const int r0 = conv ? (t_base - 3 > 0 ? t_base - 3 : 0) : t_base;
+  const int r1 = t_base + n_tok < T ? t_base + n_tok : T;
+  const unsigned bytes = (unsigned)(((long)(r1 - 1 - r0) * HD + D) * ES);
+  const int row_b = (int)(HD * ES);
+  const int t0 = conv ? t_first - 3 : t_first;  // token of row (conv ? 0 : 3)
+  const int voff = (t0 - r0) * row_b + ch * ES;  // negative rows fall out of range
+#pragma unroll
+  for (int x = 0; x < 3; ++x) {
+    const IO* src = x == 0 ? q : (x == 1 ? k : v);
+    const BufRes rx = make_buf(src + ((long)b * T + r0) * HD + (long)h * D, bytes);
+    if (conv) {
+#pragma unroll
+      for (int m = 0; m < TOK + 3; ++m) win[x][m].load(rx, voff + m * row_b, 0);
+    } else {
+#pragma unroll
+      for (int m = 0; m < TOK; ++m) win[x][3 + m].load(rx, voff + m * row_b, 0);
+    }
+  }
+  if (conv && state != nullptr && t_base < 3) {
+    // the first rows of the sequence: taps before token 0 come from the state,
+    // whose 3 rows sit at "tokens" -3 .. -1 (rows past them fall out of range)
+    const unsigned sbytes = (unsigned)((2 * HD + D) * ES);
+    const int svoff = (t_first - 3 + 3) * row_b + ch * ES;  // token t_first - 3 is state row t_first
 #pragma unroll
     for (int x = 0; x < 3; ++x) {
-      const IO* srow = state == nullptr ? nullptr
-                                        : state + ((size_t)b * 3 + x) * 3 * HD + (size_t)h * D + ch;
+      const BufRes rs = make_buf(state + ((long)b * 3 + x) * 3 * HD + (long)h * D, sbytes);
 #pragma unroll
-      for (int m = 0; m < TOK + 3; ++m) {
-        const int t = t_first - 3 + m;
-        const IO* ptr = zero_row<IO>();
-        if (t >= 0 && t < T) ptr = src[x] + row0 + (size_t)t * HD;
-        else if (t < 0 && srow != nullptr) ptr = srow + (size_t)(3 + t) * HD;
-        win[x][m].load(ptr);
+      for (int m = 0; m < 3; ++m) {
+        Raw8<IO> sv;
+        sv.load(rs, svoff + m * row_b, 0);
+        win[x][m].merge(sv);
       }
     }
-  } else {
-#pragma unroll
-    for (int x = 0; x < 3; ++x)
-#pragma unroll
-      for (int m = 0; m < TOK; ++m) {
-        const int t = t_first + m;
-        win[x][3 + m].load(t < T ? src[x] + row0 + (size_t)t * HD : zero_row<IO>());
-      }
   }
 }
 

@@ -92,6 +92,17 @@ __device__ __forceinline__ void load4(const float* p, float* out) {
 }
 
 // ------------------------------------------------------------ matrix-core tiles
+// A 16-deep bf16 product step (4 k-values per lane) issued as the 32-deep
+// instruction with the other 4 k-slots zero on both sides.  Every bf16 product
+// then uses one instruction shape, so dependent accumulation chains never mix
+// shapes.
+__device__ __forceinline__ f32x4 mfma_bf16_k16(bf16x4 a, bf16x4 b, f32x4 acc) {
+  const bf16x4 z = {(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
+  const bf16x8 a8 = __builtin_shufflevector(a, z, 0, 1, 2, 3, 4, 5, 6, 7);
+  const bf16x8 b8 = __builtin_shufflevector(b, z, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, b8, acc, 0, 0, 0);
+}
+
 // acc(16x16) += A(16 x K) * B(K x 16) where A is given by its rows (A + m*lda, k
 // contiguous) and B by the rows of B^T (Bt + n*ldb, k contiguous).  K is a
 // compile-time multiple of 16 (bf16) or 4 (fp32).  Pointers may be LDS or global.
@@ -110,9 +121,9 @@ __device__ __forceinline__ void mma_rows(f32x4& acc, const __bf16* A, int lda, c
   } else {
 #pragma unroll
     for (int k0 = 0; k0 < K; k0 += 16) {
-      s16x4 a = *reinterpret_cast<const s16x4*>(A + r * lda + k0 + 4 * g);
-      s16x4 b = *reinterpret_cast<const s16x4*>(Bt + r * ldb + k0 + 4 * g);
-      acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, acc, 0, 0, 0);
+      bf16x4 a = *reinterpret_cast<const bf16x4*>(A + r * lda + k0 + 4 * g);
+      bf16x4 b = *reinterpret_cast<const bf16x4*>(Bt + r * ldb + k0 + 4 * g);
+      acc = mfma_bf16_k16(a, b, acc);
     }
   }
 }
@@ -148,9 +159,9 @@ __device__ __forceinline__ void mma_rows_upto(f32x4& acc, const __bf16* A, int l
 #pragma unroll
     for (int k0 = 0; k0 < K; k0 += 16) {
       if (k0 < kmax) {
-        s16x4 a = *reinterpret_cast<const s16x4*>(A + r * lda + k0 + 4 * g);
-        s16x4 b = *reinterpret_cast<const s16x4*>(Bt + r * ldb + k0 + 4 * g);
-        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, acc, 0, 0, 0);
+        bf16x4 a = *reinterpret_cast<const bf16x4*>(A + r * lda + k0 + 4 * g);
+        bf16x4 b = *reinterpret_cast<const bf16x4*>(Bt + r * ldb + k0 + 4 * g);
+        acc = mfma_bf16_k16(a, b, acc);
       }
     }
   }
@@ -221,9 +232,7 @@ __device__ __forceinline__ void mma(f32x4& acc, const RowFrag<__bf16, K>& a,
       if constexpr (RowFrag<__bf16, K>::X32) {
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v[i], b.v[i], acc, 0, 0, 0);
       } else {
-        acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a.v[i]),
-                                                        __builtin_bit_cast(s16x4, b.v[i]), acc,
-                                                        0, 0, 0);
+        acc = mfma_bf16_k16(a.v[i], b.v[i], acc);
       }
     }
   }

@@ -195,18 +195,31 @@ __global__ __launch_bounds__(fast_threads<E>()) void kda_chunk_prep_kernel(PrepP
   Raw8<IO> win[3][TOK + 3];
   front_load<TOK, IO>(static_cast<const IO*>(p.q), static_cast<const IO*>(p.k),
                       static_cast<const IO*>(p.v), static_cast<const IO*>(p.conv_state_in), conv,
-                      b, p.T, p.H, D, h, ch, tf, win);
+                      b, p.T, p.H, D, h, ch, t0, C, tf, win);
+  // g rows and beta of tokens [t0, t0 + C): range-checked loads read zeros past
+  // the end of the sequence
   Raw8<IO> graw[TOK];
-  IO braw[TOK];
-  const size_t HD = (size_t)p.H * D;
+  float braw[TOK];
+  {
+    constexpr int ES = (int)sizeof(IO);
+    const int nt = p.T - t0 < C ? p.T - t0 : C;
+    const long HD = (long)p.H * D;
+    const BufRes rg = make_buf(static_cast<const IO*>(p.g) + ((long)b * p.T + t0) * HD + (long)h * D,
+                               (unsigned)(((long)(nt - 1) * HD + D) * ES));
+    const BufRes rb = make_buf(static_cast<const IO*>(p.beta) + ((long)b * p.T + t0) * p.H + h,
+                               (unsigned)(((long)(nt - 1) * p.H + 1) * ES));
+    const int gv = (TOK * s) * (int)(HD * ES) + ch * ES;
+    const int bv = (TOK * s) * p.H * ES;
 #pragma unroll
-  for (int m = 0; m < TOK; ++m) {
-    // past the end: g reads zeros, beta is zeroed below
-    const int t = tf + m < p.T ? tf + m : p.T - 1;
-    graw[m].load(tf + m < p.T ? static_cast<const IO*>(p.g) + ((size_t)b * p.T + t) * HD +
-                                    (size_t)h * D + ch
-                              : zero_row<IO>());
-    braw[m] = static_cast<const IO*>(p.beta)[((size_t)b * p.T + t) * p.H + h];
+    for (int m = 0; m < TOK; ++m) {
+      graw[m].load(rg, gv + m * (int)(HD * ES), 0);
+      if constexpr (ES == 2)
+        braw[m] = __builtin_bit_cast(__bf16, (unsigned short)__builtin_amdgcn_raw_buffer_load_b16(
+                                                 rb, bv + m * p.H * ES, 0, 0));
+      else
+        braw[m] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                rb, bv + m * p.H * ES, 0, 0));
+    }
   }
   if (tid == 0) sm.fatal = 0;
   __builtin_amdgcn_s_waitcnt(0);
@@ -219,7 +232,7 @@ __global__ __launch_bounds__(fast_threads<E>()) void kda_chunk_prep_kernel(PrepP
   float gc[TOK][8], bt[TOK];
 #pragma unroll
   for (int m = 0; m < TOK; ++m) {
-    bt[m] = tf + m < p.T ? to_f32(braw[m]) : 0.f;
+    bt[m] = braw[m];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
       const float gv = graw[m][c] * kLog2e;
@@ -496,7 +509,7 @@ __global__ __launch_bounds__(256) void kda_conv_norm_kernel(ConvNormParams p) {
   Raw8<IO> win[3][TT + 3];
   front_load<TT, IO>(static_cast<const IO*>(p.q), static_cast<const IO*>(p.k),
                      static_cast<const IO*>(p.v), static_cast<const IO*>(p.conv_state_in), true, b,
-                     p.T, p.H, D, h, 8 * j, tf, win);
+                     p.T, p.H, D, h, 8 * j, blk * TOK, TOK, tf, win);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();  // filters are in LDS
   float yq[TT][8], yk[TT][8], yv[TT][8], qk[TT];

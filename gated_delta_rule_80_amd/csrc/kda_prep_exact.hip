@@ -114,7 +114,7 @@ __global__ __launch_bounds__(kPrepThreads) void kda_chunk_prep_exact_kernel(Prep
   const bool conv = p.conv_w != nullptr;
   if (conv) stage_filters<D, kPrepThreads>(p.conv_w, p.H, h, sm.filt, tid);
   Raw8<IO> win[3][7];
-  front_load<4, IO>(q, k, v, cs, conv, b, p.T, p.H, D, h, ch, tf, win);
+  front_load<4, IO>(q, k, v, cs, conv, b, p.T, p.H, D, h, ch, t0, C, tf, win);
   float gl[4][8], bt[4];
   const size_t HD = (size_t)p.H * D;
 #pragma unroll
