@@ -70,21 +70,38 @@ template <> struct Raw8<float> {
   __device__ __forceinline__ float operator[](int c) const { return c < 4 ? a[c] : b[c - 4]; }
 };
 
-// Filters of head h, [3 tensors][D channels][4 taps] float32 (3*D entries of 16
-// bytes), copied to LDS `dst` with the direct global-to-LDS path.  Called by all
-// NT threads of the block; the copy is complete after the caller's next
-// s_waitcnt vmcnt(0) and barrier.
+// Filters of head h as [3 tensors][4 taps][D channels] float32 in LDS (taps
+// outermost, so the 8 channels a thread reads for one tap are 32 contiguous
+// bytes and 8 consecutive channel groups fall in distinct banks).  The global
+// layout is [3][H*D][4].  load_filters issues the global loads of this
+// thread's entries (call it before the other loads so those stay in flight);
+// store_filters writes them transposed.  All NT threads call both; the copy is
+// visible after the caller's next barrier.
 template <int D, int NT>
-__device__ __forceinline__ void stage_filters(const float* conv_w, int H, int h, float* dst, int tid) {
-  constexpr int N = 3 * D;
-  const int lane = tid & 63;
-  for (int base = tid - lane; base < N; base += NT) {  // wave-uniform
-    const int e = base + lane;
-    if (e < N) {
-      const int x = e / D, c = e % D;
-      __builtin_amdgcn_global_load_lds(
-          (const glb_void_t*)(conv_w + ((size_t)x * H * D + (size_t)h * D + c) * 4),
-          (lds_void_t*)(dst + 4 * base), 16, 0, 0);
+struct FilterRegs {
+  static constexpr int N = (3 * D + NT - 1) / NT;
+  f32x4 w[N];
+};
+template <int D, int NT>
+__device__ __forceinline__ void load_filters(const float* conv_w, int H, int h, int tid,
+                                             FilterRegs<D, NT>& f) {
+#pragma unroll
+  for (int i = 0; i < FilterRegs<D, NT>::N; ++i) {
+    const int e = tid + NT * i;
+    const int x = e / D, c = e % D;
+    if (e < 3 * D)
+      f.w[i] = *reinterpret_cast<const f32x4*>(conv_w + ((size_t)x * H * D + (size_t)h * D + c) * 4);
+  }
+}
+template <int D, int NT>
+__device__ __forceinline__ void store_filters(const FilterRegs<D, NT>& f, float* dst, int tid) {
+#pragma unroll
+  for (int i = 0; i < FilterRegs<D, NT>::N; ++i) {
+    const int e = tid + NT * i;
+    const int x = e / D, c = e % D;
+    if (e < 3 * D) {
+#pragma unroll
+      for (int tau = 0; tau < 4; ++tau) dst[(x * 4 + tau) * D + c] = f.w[i][tau];
     }
   }
 }
@@ -146,7 +163,8 @@ __device__ __forceinline__ void front_load(const IO* q, const IO* k, const IO* v
 }
 
 // conv + SiLU + L2 norm of the rows front_load fetched.  `filt` is the head's
-// [3][D][4] filter block (LDS or global; unused without the convolution).  All
+// [3][4][D] filter block written by store_filters (unused without the
+// convolution).  All
 // lanes of a group of D/8 consecutive lanes (the channels of one token row) must
 // call this together: the L2 sums are reduced across that group.  On return q is
 // normalised and multiplied by `scale`, k normalised, v convolved; qk[m] =
@@ -168,16 +186,26 @@ __device__ __forceinline__ void front_compute(const Raw8<IO> (&win)[3][TOK + 3],
       for (int m = 0; m < TOK + 3; ++m)
 #pragma unroll
         for (int c = 0; c < 8; ++c) rows[m][c] = win[x][m][c];
+      float w[4][8];
+#pragma unroll
+      for (int tau = 0; tau < 4; ++tau) {
+        const f32x4 lo = *reinterpret_cast<const f32x4*>(filt + (x * 4 + tau) * D + ch);
+        const f32x4 hi = *reinterpret_cast<const f32x4*>(filt + (x * 4 + tau) * D + ch + 4);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          w[tau][c] = lo[c];
+          w[tau][c + 4] = hi[c];
+        }
+      }
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        const f32x4 w = *reinterpret_cast<const f32x4*>(filt + ((size_t)x * D + ch + c) * 4);
 #pragma unroll
         for (int m = 0; m < TOK; ++m) {
           // output token t_first + m uses rows m .. m + 3 (inputs t - 3 .. t)
-          float acc = w[0] * rows[m][c];
-          acc = fmaf(w[1], rows[m + 1][c], acc);
-          acc = fmaf(w[2], rows[m + 2][c], acc);
-          acc = fmaf(w[3], rows[m + 3][c], acc);
+          float acc = w[0][c] * rows[m][c];
+          acc = fmaf(w[1][c], rows[m + 1][c], acc);
+          acc = fmaf(w[2][c], rows[m + 2][c], acc);
+          acc = fmaf(w[3][c], rows[m + 3][c], acc);
           y[x][m][c] = (!MASK || (active && t_first + m < T)) ? silu_fast(acc) : 0.f;
         }
       }

@@ -299,11 +299,28 @@ __device__ __forceinline__ void wait_vmcnt() {
 // ------------------------------------------------------------ small math
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
 
-// xor-butterfly sum over groups of `W` consecutive lanes (W a power of two <= 64)
+// x from another lane of the same 16-lane row by a DPP lane pattern (all lanes
+// active)
+template <int CTRL>
+__device__ __forceinline__ float dpp_get(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF,
+                                                            0xF, false));
+}
+
+// Sum over groups of `W` consecutive lanes (W a power of two <= 64), every lane
+// of a group receiving the group's sum.  Groups of up to 16 lanes use DPP lane
+// patterns inside a row, each pairing lanes from different halves of the
+// current partial group: swap neighbours, swap pairs (quad_perm), mirror the 8
+// lanes of a half row, mirror the row.  Wider groups add xor-shuffles.
 template <int W>
 __device__ __forceinline__ float group_sum(float x) {
+  static_assert(W >= 1 && W <= 64 && (W & (W - 1)) == 0, "power-of-two group");
+  if constexpr (W >= 2) x += dpp_get<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+  if constexpr (W >= 4) x += dpp_get<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+  if constexpr (W >= 8) x += dpp_get<0x141>(x);  // row_half_mirror
+  if constexpr (W >= 16) x += dpp_get<0x140>(x); // row_mirror
 #pragma unroll
-  for (int m = 1; m < W; m <<= 1) x += __shfl_xor(x, m, 64);
+  for (int m = 16; m < W; m <<= 1) x += __shfl_xor(x, m, 64);
   return x;
 }
 

@@ -78,7 +78,7 @@ struct FastSmem {
   alignas(16) float emid[NB * D];      // exp(m_p)
   alignas(16) float ecm[NB * D];       // exp(Gamma_C - m_p)
   alignas(16) float mpq[NPAIR * D];    // exp(m_R - m_Q) for blocks R > Q
-  alignas(16) float filt[3 * D * 4];   // the head's conv filters [q, k, v][D][4]
+  alignas(16) float filt[3 * 4 * D];   // the head's conv filters [q, k, v][tap][D]
   int fatal;
 };
 
@@ -165,11 +165,16 @@ __global__ __launch_bounds__(fast_threads<E>()) void kda_chunk_prep_kernel(PrepP
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g4 = lane >> 4;
-  const int rec = blockIdx.x;
-  const int n = rec % p.NT;
-  const int bh = rec / p.NT;
+  // Chunk-major order: the workgroups running at the same time cover every head
+  // of a few consecutive chunks, so together they read whole token rows of q, k,
+  // v, g (all heads of a token are adjacent in memory).  Records stay in
+  // (sequence, head, chunk) order for the state walk.
+  const int BH = p.B * p.H;
+  const int n = blockIdx.x / BH;
+  const int bh = blockIdx.x % BH;
   const int h = bh % p.H, b = bh / p.H;
   const int t0 = n * C;
+  const int rec = bh * p.NT + n;
   char* recp = p.ws + (size_t)rec * RL.bytes;
   E* gW = reinterpret_cast<E*>(recp) + RL.w;
   E* gQL = reinterpret_cast<E*>(recp) + RL.ql;
@@ -189,9 +194,10 @@ __global__ __launch_bounds__(fast_threads<E>()) void kda_chunk_prep_kernel(PrepP
   const int pb = (TOK * s) / 16;          // 16-token block of this segment
   const int tf = t0 + TOK * s;
   // every global load of this phase is issued before the first wait: the head's
-  // filters (straight to LDS), the q/k/v windows, g and beta
+  // filters, the q/k/v windows, g and beta
   const bool conv = p.conv_w != nullptr;
-  if (conv) stage_filters<D, NTH>(p.conv_w, p.H, h, sm.filt, tid);
+  FilterRegs<D, NTH> fr;
+  if (conv) load_filters<D, NTH>(p.conv_w, p.H, h, tid, fr);
   Raw8<IO> win[3][TOK + 3];
   front_load<TOK, IO>(static_cast<const IO*>(p.q), static_cast<const IO*>(p.k),
                       static_cast<const IO*>(p.v), static_cast<const IO*>(p.conv_state_in), conv,
@@ -222,7 +228,8 @@ __global__ __launch_bounds__(fast_threads<E>()) void kda_chunk_prep_kernel(PrepP
     }
   }
   if (tid == 0) sm.fatal = 0;
-  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_sched_barrier(0);  // the loads above are all issued first
+  if (conv) store_filters<D, NTH>(fr, sm.filt, tid);
   __syncthreads();  // filters are in LDS
   float yq[TOK][8], yk[TOK][8], yv[TOK][8], qk[TOK];
   front_compute<TOK, D, IO, false, false>(win, sm.filt, conv, ch, tf, p.T, active, p.l2 != 0,
@@ -462,28 +469,43 @@ __global__ __launch_bounds__(fast_threads<E>()) void kda_chunk_prep_kernel(PrepP
     }
   }
   __syncthreads();
-  // W^T tiles (c, i): A = (beta K Lambda)^T rows c, B = T rows i (j <= i)
-  constexpr int NWT = (D / 16) * NB;
+  // W^T tiles (c, i) = (beta K Lambda)^T T^T and U~ tiles (i, v) = T (beta V): the
+  // NW / NB waves of token tile It split its 2 D/16 tiles; the T rows of the
+  // token tile are loaded once per wave, and the causal k-steps stop at the
+  // tile's diagonal
   constexpr int STEPC = RowFrag<E, C>::STEP;
-  for (int tt = wave; tt < NWT; tt += NW) {
-    const int Ct = tt / NB, It = tt % NB;
-    RowFrag<E, C> fa, fb;
-    load_timg<C>(fa, klt, 16 * Ct + r, g4);
-    fb.load(tb + (16 * It + r) * LT, g4);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    mma<C>(acc, fa, fb, (16 * It + 16 + STEPC - 1) / STEPC);
-    const int i = 16 * It + r, c = 16 * Ct + 4 * g4;
-    store4(gW + (size_t)i * D + c, acc[0], acc[1], acc[2], acc[3]);
-  }
-  // U~ tiles (i, v): A = T rows i, B = (beta V)^T rows v; stored in fragment order
-  for (int tt = wave; tt < NWT; tt += NW) {
-    const int It = tt / (D / 16), Vt = tt % (D / 16);
-    RowFrag<E, C> fa, fb;
-    fa.load(tb + (16 * It + r) * LT, g4);
-    load_timg<C>(fb, vt, 16 * Vt + r, g4);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    mma<C>(acc, fa, fb, (16 * It + 16 + STEPC - 1) / STEPC);
-    store4(gU + ((size_t)(It * (D / 16) + Vt) * 64 + lane) * 4, acc[0], acc[1], acc[2], acc[3]);
+  constexpr int WPI = NW / NB;        // waves per token tile
+  constexpr int DT = D / 16;          // channel (or value) tiles
+  static_assert(NW % NB == 0, "waves split evenly over the token tiles");
+  {
+    const int It = wave % NB, sub = wave / NB;
+    const int steps = (16 * It + 16 + STEPC - 1) / STEPC;
+    RowFrag<E, C> ft;
+    ft.load(tb + (16 * It + r) * LT, g4);
+    E* wrow = gW + (size_t)(16 * It + r) * D + 4 * g4;
+#pragma unroll
+    for (int q = 0; q < (DT + WPI - 1) / WPI; ++q) {
+      const int Ct = sub + WPI * q;
+      if (DT % WPI == 0 || Ct < DT) {
+        RowFrag<E, C> fa;
+        load_timg<C>(fa, klt, 16 * Ct + r, g4);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        mma<C>(acc, fa, ft, steps);
+        store4(wrow + 16 * Ct, acc[0], acc[1], acc[2], acc[3]);
+      }
+    }
+    E* urow = gU + ((size_t)It * DT * 64 + lane) * 4;
+#pragma unroll
+    for (int q = 0; q < (DT + WPI - 1) / WPI; ++q) {
+      const int Vt = sub + WPI * q;
+      if (DT % WPI == 0 || Vt < DT) {
+        RowFrag<E, C> fb;
+        load_timg<C>(fb, vt, 16 * Vt + r, g4);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        mma<C>(acc, ft, fb, steps);
+        store4(urow + (size_t)Vt * 64 * 4, acc[0], acc[1], acc[2], acc[3]);
+      }
+    }
   }
 }
 
@@ -496,7 +518,7 @@ __global__ __launch_bounds__(256) void kda_conv_norm_kernel(ConvNormParams p) {
   constexpr int NOCT = D / 8;
   constexpr int TT = conv_norm_tokens<IO>();
   constexpr int TOK = 256 / NOCT * TT;  // tokens per workgroup
-  __shared__ alignas(16) float filt[3 * D * 4];
+  __shared__ alignas(16) float filt[3 * 4 * D];
   const int tid = threadIdx.x;
   const int nblk = (p.T + TOK - 1) / TOK;
   const int blk = blockIdx.x % nblk;
@@ -505,12 +527,14 @@ __global__ __launch_bounds__(256) void kda_conv_norm_kernel(ConvNormParams p) {
   const int s = tid / NOCT, j = tid % NOCT;
   const int tf = blk * TOK + TT * s;
   const bool active = tf < p.T;
-  stage_filters<D, 256>(p.conv_w, p.H, h, filt, tid);
+  FilterRegs<D, 256> fr;
+  load_filters<D, 256>(p.conv_w, p.H, h, tid, fr);
   Raw8<IO> win[3][TT + 3];
   front_load<TT, IO>(static_cast<const IO*>(p.q), static_cast<const IO*>(p.k),
                      static_cast<const IO*>(p.v), static_cast<const IO*>(p.conv_state_in), true, b,
                      p.T, p.H, D, h, 8 * j, blk * TOK, TOK, tf, win);
-  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_sched_barrier(0);
+  store_filters<D, 256>(fr, filt, tid);
   __syncthreads();  // filters are in LDS
   float yq[TT][8], yk[TT][8], yv[TT][8], qk[TT];
   front_compute<TT, D, IO>(win, filt, true, 8 * j, tf, p.T, active, p.l2 != 0, p.eps, 1.0f, yq,

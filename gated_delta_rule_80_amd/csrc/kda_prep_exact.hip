@@ -65,7 +65,7 @@ struct PrepSmem {
   alignas(16) char r1[R1];
   float beta[C];
   float pd[C];  // diagonal of P
-  alignas(16) float filt[3 * D * 4];  // the head's conv filters [q, k, v][D][4]
+  alignas(16) float filt[3 * 4 * D];  // the head's conv filters [q, k, v][tap][D]
 };
 
 template <int D, int C, typename IO, typename E>
@@ -112,7 +112,8 @@ __global__ __launch_bounds__(kPrepThreads) void kda_chunk_prep_exact_kernel(Prep
   const int tf = t0 + 4 * s;  // first token of this thread's segment
   // every global load of this phase is issued before the first wait
   const bool conv = p.conv_w != nullptr;
-  if (conv) stage_filters<D, kPrepThreads>(p.conv_w, p.H, h, sm.filt, tid);
+  FilterRegs<D, kPrepThreads> fr;
+  if (conv) load_filters<D, kPrepThreads>(p.conv_w, p.H, h, tid, fr);
   Raw8<IO> win[3][7];
   front_load<4, IO>(q, k, v, cs, conv, b, p.T, p.H, D, h, ch, t0, C, tf, win);
   float gl[4][8], bt[4];
@@ -124,7 +125,8 @@ __global__ __launch_bounds__(kPrepThreads) void kda_chunk_prep_exact_kernel(Prep
     load8(gg + ((size_t)b * p.T + tc) * HD + (size_t)h * D + ch, gl[m]);
     bt[m] = to_f32(bb[((size_t)b * p.T + tc) * p.H + h]);
   }
-  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_sched_barrier(0);
+  if (conv) store_filters<D, kPrepThreads>(fr, sm.filt, tid);
   __syncthreads();  // filters are in LDS
   float yq[4][8], yk[4][8], yv[4][8], qk[4];
   front_compute<4, D, IO>(win, sm.filt, conv, ch, tf, p.T, active, p.l2 != 0, p.eps, p.scale, yq,
