@@ -18,6 +18,15 @@ conv kernel 4 -- "Kimi-K3 model atlas -- self.layers", linear_attn_config):
 
 The second parameter of every N(., .) is a variance.  bf16 tensors are rounded
 from float32 with round-to-nearest-even (torch's conversion).
+
+Optional stages (``make_stage_inputs``, drawn from a generator of their own so the
+tensors above do not change):
+
+* output gate pre-activation ~ N(0, 1) in the I/O dtype; output-norm gain
+  1 + N(0, 0.01) float32, one per value channel
+* raw decay projection f ~ N(0, 1) in the I/O dtype, A_log ~ U(lo, hi) per head
+  and dt_bias ~ N(0, 0.25) per channel, both float32; beta logits
+  ~ N(0, sigma_b^2) in the I/O dtype
 """
 from __future__ import annotations
 
@@ -103,6 +112,32 @@ def make_inputs(w: Workload, seed: int = 0, device: str | torch.device = "cpu") 
     S0 = randn(B, H, D, D, std=w.s0_std) if w.s0_std > 0 else None
     conv_state = randn(B, 3, 3, H * D, std=w.conv_state_std).to(io) if w.conv_state_std > 0 else None
     return dict(q=q, k=k, v=v, g=g, beta=beta, conv_w=conv_w, S0=S0, conv_state=conv_state)
+
+
+def make_stage_inputs(w: Workload, seed: int = 0, device: str | torch.device = "cpu") -> dict:
+    """Inputs of the optional stages for workload ``w``: o_gate and f [B,T,H,D]
+    (decode [B,H,D]) and b_logit [B,T,H] (decode [B,H]) in the I/O dtype; o_norm_w
+    [D], A_log [H] and dt_bias [H*D] float32."""
+    device = torch.device(device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed) * 1000003 + 17)
+    io = DTYPES[w.io]
+    B, T, H, D = w.B, w.T, w.H, w.D
+    shape = (B, H, D) if w.decode else (B, T, H, D)
+    bshape = (B, H) if w.decode else (B, T, H)
+
+    def randn(*s, std=1.0):
+        x = torch.randn(*s, generator=gen, device=device, dtype=torch.float32)
+        return x.mul_(std) if std != 1.0 else x
+
+    o_gate = randn(*shape).to(io)
+    o_norm_w = randn(D, std=0.1).add_(1.0)
+    f = randn(*shape).to(io)
+    A_log = torch.empty(H, device=device, dtype=torch.float32).uniform_(w.a_lo, w.a_hi, generator=gen)
+    dt_bias = randn(H * D, std=0.5)
+    b_logit = randn(*bshape, std=w.b_std).to(io)
+    return dict(o_gate=o_gate, o_norm_w=o_norm_w, f=f, A_log=A_log, dt_bias=dt_bias,
+                b_logit=b_logit)
 
 
 def to_numpy(t):

@@ -6,13 +6,19 @@ benchmark.  The GPU library never imports it.
 from .kda_oracle import (  # noqa: F401
     CONV_K,
     L2_EPS,
+    RMS_EPS,
     conv_norm_reference,
     conv_tail,
     gated_delta_step,
+    kda_gate,
     kda_reference,
     kda_reference_decode_step,
     kda_reference_heads,
     l2_normalize,
+    output_gate_norm,
+    rms_norm,
     short_conv,
+    sigmoid,
     silu,
+    softplus,
 )

@@ -14,9 +14,14 @@ Sources (web pages; cited by title and section):
 * "MaxText PR 5548 (Kimi-K3 config, schema, param mapping)", review item 2: the
   KDA tensors ``{q,k,v}_conv1d.weight`` have shape ``[12288, 1, 4]`` and are kept
   in float32, like ``A_log`` and ``dt_bias`` (one decay per channel).
-* "Kimi-K3 atlas -- MoE input (decode)", ``KimiRMSNorm``: norm computed in float32
-  with ``eps = 1e-6``; used here only through the identity that ties the L2 norm
-  of q and k to that RMSNorm (see ``l2_normalize``).
+* "Kimi-K3 atlas -- MoE input (decode)", ``KimiRMSNorm``: x / sqrt(mean(x^2) + eps)
+  times a per-feature gain, computed in float32 with ``eps = 1e-6``.  Used for the
+  identity that ties the L2 norm of q and k to that RMSNorm (see
+  ``l2_normalize``) and for the optional output norm (``output_gate_norm``).
+* "MaxText PR 5548", review item 2: each KDA layer has an ``o_norm.weight`` of
+  shape [128] (one gain per value channel of a head, float32) and a ``g_proj``;
+  "MaxText PR 5543", What, item 1: an MLA attention output gated by
+  ``g_proj`` is multiplied by the sigmoid of it.
 
 The pages name the mixer and its parameters but do not print its equations.
 The definition implemented here is the channel-wise gated delta rule:
@@ -44,6 +49,9 @@ L2_EPS = 1e-6
 # Released config, linear_attn_config.short_conv_kernel_size ("Kimi-K3 model
 # atlas -- self.layers", config.json).
 CONV_K = 4
+# eps of the optional output RMSNorm: KimiRMSNorm's default ("Kimi-K3 atlas --
+# MoE input (decode)", RMSNorm excerpt).
+RMS_EPS = 1e-6
 
 
 def silu(x: np.ndarray) -> np.ndarray:
@@ -106,6 +114,76 @@ def l2_normalize(x: np.ndarray, eps: float = L2_EPS) -> np.ndarray:
     return x / np.sqrt((x * x).sum(axis=-1, keepdims=True) + eps)
 
 
+def sigmoid(x: np.ndarray) -> np.ndarray:
+    """The logistic function 1 / (1 + exp(-x)), elementwise, fp64."""
+    x = np.asarray(x, dtype=np.float64)
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def rms_norm(x: np.ndarray, w: np.ndarray | None = None, eps: float = RMS_EPS) -> np.ndarray:
+    """KimiRMSNorm over the last axis: x / sqrt(mean_c x_c^2 + eps), times the gain w.
+
+    ("Kimi-K3 atlas -- MoE input (decode)", RMSNorm excerpt: the mean of squares,
+    eps inside the root, one gain per feature.)  The excerpt rounds the normalised
+    value to the activation dtype before the gain; here everything is fp64 and the
+    GPU rounds once at the end, a difference of one rounding that the parity
+    tolerance covers.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    y = x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    return y if w is None else y * np.asarray(w, dtype=np.float64)
+
+
+def output_gate_norm(o: np.ndarray, o_norm_w: np.ndarray | None = None,
+                     gate: np.ndarray | None = None, eps: float = RMS_EPS) -> np.ndarray:
+    """The optional output stage of a head: RMSNorm with the o_norm gain, then the
+    sigmoid output gate.
+
+    o:        [..., D] mixer output of one head per row
+    o_norm_w: [D] gain shared by the heads (the layer's o_norm.weight has shape
+              [head_dim]), or None to skip the norm
+    gate:     [..., D] gate pre-activation (the g_proj output), or None to skip
+    Reading: norm first, then gate, the order of a gated RMSNorm whose gain is
+    o_norm.weight; the pages give the sigmoid gate for the MLA output and no
+    formula for KDA's, so the sigmoid is taken by analogy ("MaxText PR 5543",
+    What, item 1).
+    """
+    y = np.asarray(o, dtype=np.float64)
+    if o_norm_w is not None:
+        y = rms_norm(y, o_norm_w, eps)
+    if gate is not None:
+        y = y * sigmoid(gate)
+    return y
+
+
+def softplus(x: np.ndarray) -> np.ndarray:
+    """softplus(x) = ln(1 + e^x), elementwise, fp64 (as log(e^0 + e^x), which does
+    not overflow for large x)."""
+    return np.logaddexp(0.0, np.asarray(x, dtype=np.float64))
+
+
+def kda_gate(f: np.ndarray, A_log: np.ndarray, dt_bias: np.ndarray) -> np.ndarray:
+    """Per-channel log-decay from the gate projection: g = -exp(A_log[h]) * softplus(f + dt_bias).
+
+    f:       [..., H, D] gate projection output (the full-rank gate: one value per
+             key channel)
+    A_log:   [H] float32, one per head; dt_bias: [H*D] float32, one per channel
+             ("MaxText PR 5548", review item 2, and the A_log slicing notes: A_log
+             is [num_heads], dt_bias [12288], both kept in float32 to avoid decay
+             drift over long contexts).
+    Reading: the pages give the parameters and their shapes, not the formula; this
+    is the plainest form they support (a positive rate exp(A_log) per head times a
+    softplus of the biased projection, so g <= 0 always).  The config's
+    gate_lower_bound (-5.0, "Kimi-K3 model atlas -- self.layers") is not applied:
+    the pages do not say how.
+    """
+    f = np.asarray(f, dtype=np.float64)
+    H, D = f.shape[-2], f.shape[-1]
+    rate = np.exp(np.asarray(A_log, dtype=np.float64)).reshape(H, 1)
+    bias = np.asarray(dt_bias, dtype=np.float64).reshape(H, D)
+    return -rate * softplus(f + bias)
+
+
 def gated_delta_step(S, q, k, v, g, beta, scale=1.0):
     """One step of the channel-wise gated delta rule for a batch of heads.
 
@@ -136,7 +214,8 @@ def _check_decay(g):
 
 
 def kda_reference(q, k, v, g, beta, conv_w=None, conv_state=None, S0=None,
-                  scale=1.0, l2norm_qk=True, eps=L2_EPS):
+                  scale=1.0, l2norm_qk=True, eps=L2_EPS, o_norm_w=None, o_gate=None,
+                  o_norm_eps=RMS_EPS, A_log=None, dt_bias=None, beta_sigmoid=False):
     """The full KDA mixer over a batch of sequences, sequentially in time, fp64.
 
     q, k, v, g: [B, T, H, D] (raw q, k, v before the convolution; g is the
@@ -146,14 +225,24 @@ def kda_reference(q, k, v, g, beta, conv_w=None, conv_state=None, S0=None,
                 skip the convolution and SiLU (inputs used as given)
     conv_state: [B, 3, K-1, H*D] raw inputs preceding t = 0, or None for zeros
     S0:         [B, H, D, D] initial state, or None for zeros
+    o_norm_w, o_gate: the optional output stage (``output_gate_norm``); o_gate is
+                [B, T, H, D]
+    A_log, dt_bias: if given, g holds the gate projection output f and the decay
+                is ``kda_gate(f, A_log, dt_bias)``
+    beta_sigmoid: if true, beta holds logits and the write strength is sigmoid(beta)
     Returns (o [B, T, H, D], S_T [B, H, D, D], tail [B, 3, K-1, H*D] or None).
 
     Steps: (1) short causal conv per channel and SiLU on q, k, v; (2) L2 norm of q
-    and k per head; (3) the gated delta rule step by step from S0.
+    and k per head; (3) the gated delta rule step by step from S0; (4) if asked,
+    the output RMSNorm and sigmoid gate per head.
     """
     q, k, v, g = (np.asarray(a, dtype=np.float64) for a in (q, k, v, g))
     beta = np.asarray(beta, dtype=np.float64)
     B, T, H, D = q.shape
+    if A_log is not None:
+        g = kda_gate(g, A_log, dt_bias)
+    if beta_sigmoid:
+        beta = sigmoid(beta)
     _check_decay(g)
     tail = None
     if conv_w is not None:
@@ -178,22 +267,29 @@ def kda_reference(q, k, v, g, beta, conv_w=None, conv_state=None, S0=None,
     o = np.empty((B, T, H, D))
     for t in range(T):
         S, o[:, t] = gated_delta_step(S, q[:, t], k[:, t], v[:, t], g[:, t], beta[:, t], scale)
+    if o_norm_w is not None or o_gate is not None:
+        o = output_gate_norm(o, o_norm_w, o_gate, o_norm_eps)
     return o, S, tail
 
 
 def kda_reference_decode_step(q, k, v, g, beta, S, conv_w=None, conv_state=None,
-                              scale=1.0, l2norm_qk=True, eps=L2_EPS):
+                              scale=1.0, l2norm_qk=True, eps=L2_EPS, o_norm_w=None,
+                              o_gate=None, o_norm_eps=RMS_EPS, A_log=None, dt_bias=None,
+                              beta_sigmoid=False):
     """One autoregressive KDA step for B sequences: the mixer at T = 1.
 
     q, k, v, g: [B, H, D] raw inputs of the new token; beta [B, H];
-    S [B, H, D, D] cached state; conv_state [B, 3, K-1, H*D] cached raw inputs.
+    S [B, H, D, D] cached state; conv_state [B, 3, K-1, H*D] cached raw inputs;
+    o_gate [B, H, D] or None.
     Returns (o [B, H, D], S_new, conv_state_new).
     """
     o, S_new, tail = kda_reference(
         np.asarray(q)[:, None], np.asarray(k)[:, None], np.asarray(v)[:, None],
         np.asarray(g)[:, None], np.asarray(beta)[:, None],
         conv_w=conv_w, conv_state=conv_state, S0=S, scale=scale,
-        l2norm_qk=l2norm_qk, eps=eps)
+        l2norm_qk=l2norm_qk, eps=eps, o_norm_w=o_norm_w,
+        o_gate=None if o_gate is None else np.asarray(o_gate)[:, None], o_norm_eps=o_norm_eps,
+        A_log=A_log, dt_bias=dt_bias, beta_sigmoid=beta_sigmoid)
     return o[:, 0], S_new, tail
 
 
@@ -224,7 +320,8 @@ def conv_norm_reference(q, k, v, conv_w, conv_state=None, l2norm_qk=True, eps=L2
 
 
 def kda_reference_heads(q, k, v, g, beta, heads, conv_w=None, conv_state=None, S0=None,
-                        scale=1.0, l2norm_qk=True, eps=L2_EPS):
+                        scale=1.0, l2norm_qk=True, eps=L2_EPS, o_norm_w=None, o_gate=None,
+                        o_norm_eps=RMS_EPS, A_log=None, dt_bias=None, beta_sigmoid=False):
     """``kda_reference`` restricted to a list of (b, h) pairs.
 
     Heads are independent (their state, decay and filters are per head/channel),
@@ -239,10 +336,15 @@ def kda_reference_heads(q, k, v, g, beta, heads, conv_w=None, conv_state=None, S
         cw = None if conv_w is None else np.asarray(conv_w)[:, sl, :]
         cs = None if conv_state is None else np.asarray(conv_state)[b:b + 1, :, :, sl]
         s0 = None if S0 is None else np.asarray(S0)[b:b + 1, h:h + 1]
+        og = None if o_gate is None else np.asarray(o_gate)[b:b + 1, :, h:h + 1]
         o, S, _ = kda_reference(
             np.asarray(q)[b:b + 1, :, h:h + 1], np.asarray(k)[b:b + 1, :, h:h + 1],
             np.asarray(v)[b:b + 1, :, h:h + 1], np.asarray(g)[b:b + 1, :, h:h + 1],
             np.asarray(beta)[b:b + 1, :, h:h + 1], conv_w=cw, conv_state=cs, S0=s0,
-            scale=scale, l2norm_qk=l2norm_qk, eps=eps)
+            scale=scale, l2norm_qk=l2norm_qk, eps=eps, o_norm_w=o_norm_w, o_gate=og,
+            o_norm_eps=o_norm_eps,
+            A_log=None if A_log is None else np.asarray(A_log)[h:h + 1],
+            dt_bias=None if dt_bias is None else np.asarray(dt_bias)[sl],
+            beta_sigmoid=beta_sigmoid)
         out.append((o[0, :, 0], S[0, 0]))
     return out

@@ -16,7 +16,8 @@ from scipy.special import expit
 
 from oracle import (conv_norm_reference, conv_tail, gated_delta_step, kda_reference,
                     kda_reference_decode_step, kda_reference_heads, l2_normalize,
-                    short_conv, silu)
+                    kda_gate, output_gate_norm, rms_norm, short_conv, sigmoid, silu,
+                    softplus)
 from chunked_form import chunk_quantities, chunked_head
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -335,3 +336,170 @@ def test_empty_sequence_is_identity():
     assert o.shape == (1, 0, 2, 4)
     np.testing.assert_array_equal(S, S0)
     np.testing.assert_array_equal(tail, hist)
+
+
+# ------------------------------------------------- output RMSNorm and sigmoid gate
+def test_output_gate_norm_hand_example():
+    d = json.load(open(os.path.join(GOLDEN, "hand_gate_norm.json")))
+    f = lambda x: np.array(x, dtype=np.float64)
+    out = output_gate_norm(f(d["o"]), f(d["w"]), f(d["gate"]), eps=d["eps"])
+    np.testing.assert_allclose(out, f(d["out"]), rtol=0, atol=1e-14)
+    # the same worked numbers in closed form
+    np.testing.assert_allclose(out, [3 * np.sqrt(2) / 10, 6 * np.sqrt(2) / 5], rtol=0, atol=1e-14)
+
+
+def test_rms_norm_closed_forms():
+    """Constant and one-hot rows: catches a sum taken for the mean (a factor D) and
+    eps outside the root."""
+    D, eps = 8, 1e-3
+    c = -1.7
+    np.testing.assert_allclose(rms_norm(np.full(D, c), eps=eps), np.full(D, c / np.sqrt(c * c + eps)),
+                               rtol=1e-15, atol=0)
+    x = np.zeros(D)
+    x[5] = c
+    want = np.zeros(D)
+    want[5] = c / np.sqrt(c * c / D + eps)
+    np.testing.assert_allclose(rms_norm(x, eps=eps), want, rtol=1e-15, atol=0)
+    # with eps = 0 the result has mean square exactly 1 and keeps the direction
+    y = rms_norm(np.random.default_rng(3).standard_normal((4, D)), eps=0.0)
+    np.testing.assert_allclose(np.mean(y * y, axis=-1), 1.0, rtol=1e-14)
+
+
+def test_rms_norm_and_l2_norm_identity():
+    """RMSNorm_eps(x; gain 1) / sqrt(D) = x / sqrt(sum x^2 + D eps): the output norm
+    against the (independently pinned) L2 norm of q and k."""
+    rng = np.random.default_rng(4)
+    for D in (2, 16, 128):
+        x = rng.standard_normal((3, 5, D))
+        eps = 1e-6
+        np.testing.assert_allclose(rms_norm(x, eps=eps) / np.sqrt(D), l2_normalize(x, D * eps),
+                                   rtol=1e-13, atol=0)
+
+
+def test_rms_norm_gain_is_per_channel():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((6, 4))
+    w = np.array([0.5, -2.0, 0.0, 3.0])
+    np.testing.assert_allclose(rms_norm(x, w), rms_norm(x) * w[None], rtol=1e-15, atol=0)
+    assert np.all(rms_norm(x, w)[:, 2] == 0.0)
+
+
+def test_sigmoid_values():
+    np.testing.assert_allclose(sigmoid(np.log([3.0, 1.0 / 3.0, 1.0])), [0.75, 0.25, 0.5],
+                               rtol=0, atol=1e-15)
+    x = np.linspace(-30, 30, 61)
+    np.testing.assert_allclose(sigmoid(x) + sigmoid(-x), 1.0, rtol=0, atol=1e-15)
+    np.testing.assert_allclose(sigmoid(x), expit(x), rtol=1e-14, atol=0)
+
+
+def test_zero_gate_halves_the_output():
+    """A gate pre-activation of zero gives exactly half the ungated output (the
+    property "MaxText PR 5543" states for its sigmoid gate with zero g_proj)."""
+    rng = np.random.default_rng(6)
+    o = rng.standard_normal((2, 7, 3, 16))
+    w = 1.0 + 0.1 * rng.standard_normal(16)
+    np.testing.assert_array_equal(output_gate_norm(o, w, np.zeros_like(o)), 0.5 * output_gate_norm(o, w))
+    np.testing.assert_array_equal(output_gate_norm(o, None, np.zeros_like(o)), 0.5 * o)
+    np.testing.assert_array_equal(output_gate_norm(o), o)
+
+
+def test_output_stage_in_the_mixer_is_per_head():
+    """The mixer with the output stage equals the plain mixer followed by the stage
+    on each head's row; each head normalises over its own D channels only."""
+    rng = np.random.default_rng(7)
+    q, k, v, g, beta, conv_w, S0 = rand_case(rng, B=2, T=11, H=3, D=4)
+    gate = rng.standard_normal(q.shape)
+    w = rng.standard_normal(4)
+    o0, S_plain, _ = kda_reference(q, k, v, g, beta, conv_w=conv_w, S0=S0)
+    o1, S1, _ = kda_reference(q, k, v, g, beta, conv_w=conv_w, S0=S0, o_norm_w=w, o_gate=gate)
+    np.testing.assert_array_equal(S1, S_plain)  # the state never sees the output stage
+    for b in range(2):
+        for t in range(11):
+            for h in range(3):
+                r = o0[b, t, h]
+                want = r / np.sqrt(np.mean(r * r) + 1e-6) * w / (1 + np.exp(-gate[b, t, h]))
+                np.testing.assert_allclose(o1[b, t, h], want, rtol=1e-13, atol=1e-15)
+    # the sampled-head and decode entry points carry the stage the same way
+    (oh, _), = kda_reference_heads(q, k, v, g, beta, [(1, 2)], conv_w=conv_w, S0=S0,
+                                   o_norm_w=w, o_gate=gate)
+    np.testing.assert_allclose(oh, o1[1, :, 2], rtol=1e-13, atol=1e-15)
+    od, _, _ = kda_reference_decode_step(q[:, 0], k[:, 0], v[:, 0], g[:, 0], beta[:, 0], S0,
+                                         conv_w=conv_w, o_norm_w=w, o_gate=gate[:, 0])
+    o_first, _, _ = kda_reference(q[:, :1], k[:, :1], v[:, :1], g[:, :1], beta[:, :1],
+                                  conv_w=conv_w, S0=S0, o_norm_w=w, o_gate=gate[:, :1])
+    np.testing.assert_allclose(od, o_first[:, 0], rtol=1e-13, atol=1e-15)
+
+
+# ------------------------------------------------- decay and beta from raw projections
+def test_gate_activation_hand_example():
+    d = json.load(open(os.path.join(GOLDEN, "hand_gate_act.json")))
+    f = lambda x: np.array(x, dtype=np.float64)
+    g = kda_gate(f(d["f"]), f(d["A_log"]), f(d["dt_bias"]))
+    np.testing.assert_allclose(g, f(d["g"]), rtol=0, atol=1e-14)
+    np.testing.assert_allclose(sigmoid(f(d["b"])), f(d["beta"]), rtol=0, atol=1e-15)
+
+
+def test_softplus_closed_forms():
+    np.testing.assert_allclose(softplus(0.0), np.log(2.0), rtol=1e-15)
+    np.testing.assert_allclose(softplus(np.log(np.e - 1.0)), 1.0, rtol=1e-15)
+    x = np.linspace(-20, 20, 81)
+    np.testing.assert_allclose(softplus(x) - softplus(-x), x, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(softplus(x), np.log1p(np.exp(x)), rtol=1e-14)
+    assert softplus(800.0) == 800.0 and np.isfinite(softplus(-800.0))
+
+
+def test_gate_activation_axes():
+    """A_log indexes heads and dt_bias indexes channels h*D + c: catches a swapped
+    or transposed parameter."""
+    H, D = 3, 4
+    A_log = np.log(np.array([1.0, 2.0, 4.0]))
+    f = np.zeros((2, 5, H, D))
+    g = kda_gate(f, A_log, np.zeros(H * D))
+    for h in range(H):
+        np.testing.assert_allclose(g[..., h, :], -(2.0 ** h) * np.log(2.0), rtol=1e-15)
+    bias = np.zeros(H * D)
+    bias[2 * D + 1] = np.log(np.e - 1.0)  # head 2, channel 1 only
+    g = kda_gate(f, A_log, bias)
+    np.testing.assert_allclose(g[..., 2, 1], -4.0, rtol=1e-15)
+    np.testing.assert_allclose(g[..., 1, 1], -2.0 * np.log(2.0), rtol=1e-15)
+    np.testing.assert_allclose(g[..., 2, 0], -4.0 * np.log(2.0), rtol=1e-15)
+
+
+def test_gate_activation_is_a_valid_decay():
+    rng = np.random.default_rng(8)
+    g = kda_gate(4 * rng.standard_normal((2, 50, 3, 8)), rng.uniform(-3, 2, 3),
+                 rng.standard_normal(24))
+    assert np.all(np.isfinite(g)) and np.all(g <= 0)
+    # more negative projections decay less (softplus is increasing)
+    f = np.linspace(-5, 5, 11).reshape(1, 11, 1, 1) * np.ones((1, 11, 1, 2))
+    g = kda_gate(f, np.zeros(1), np.zeros(2))
+    assert np.all(np.diff(g[0, :, 0, 0]) < 0)
+
+
+def test_raw_projection_inputs_in_the_mixer():
+    """The mixer fed raw projections equals the mixer fed the activated values, for
+    every entry point."""
+    rng = np.random.default_rng(9)
+    q, k, v, _, _, conv_w, S0 = rand_case(rng, B=2, T=7, H=3, D=4)
+    f = rng.standard_normal(q.shape)
+    A_log = rng.uniform(-1, 1, 3)
+    dt_bias = 0.5 * rng.standard_normal(12)
+    blog = rng.standard_normal(q.shape[:3])
+    g = kda_gate(f, A_log, dt_bias)
+    beta = sigmoid(blog)
+    o0, S0_, _ = kda_reference(q, k, v, g, beta, conv_w=conv_w, S0=S0)
+    o1, S1, _ = kda_reference(q, k, v, f, blog, conv_w=conv_w, S0=S0, A_log=A_log,
+                              dt_bias=dt_bias, beta_sigmoid=True)
+    np.testing.assert_allclose(o1, o0, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(S1, S0_, rtol=1e-13, atol=1e-14)
+    (oh, Sh), = kda_reference_heads(q, k, v, f, blog, [(1, 2)], conv_w=conv_w, S0=S0,
+                                    A_log=A_log, dt_bias=dt_bias, beta_sigmoid=True)
+    np.testing.assert_allclose(oh, o0[1, :, 2], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(Sh, S0_[1, 2], rtol=1e-13, atol=1e-14)
+    od, Sd, _ = kda_reference_decode_step(q[:, 0], k[:, 0], v[:, 0], f[:, 0], blog[:, 0], S0,
+                                          conv_w=conv_w, A_log=A_log, dt_bias=dt_bias,
+                                          beta_sigmoid=True)
+    o_first, S_first, _ = kda_reference(q[:, :1], k[:, :1], v[:, :1], g[:, :1], beta[:, :1],
+                                        conv_w=conv_w, S0=S0)
+    np.testing.assert_allclose(od, o_first[:, 0], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(Sd, S_first, rtol=1e-13, atol=1e-14)
