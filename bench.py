@@ -5,7 +5,9 @@
 A step is one kda_prefill over the workload (conv + SiLU + L2, chunk preparation,
 state walk with output, conv-state hand-over), inputs resident in HBM.  The
 decode step (B=256 sequences, in-place state) is timed in the same run and
-reported beside it.  Prints one JSON line.
+reported beside it.  A second leg ("stages") times the same prefill and decode
+steps with the optional stages on: decay and write strength from raw
+projections, output RMSNorm and sigmoid gate.  Prints one JSON line.
 
 Roofline figures use algorithmic bytes (each tensor the kernel must read or
 write, once) divided by the kernel's mean duration from HIP events recorded on
@@ -28,6 +30,8 @@ if ROOT not in sys.path:
 
 HBM_PEAK = 8.0e12          # B/s
 BF16_PEAK = 2.5e15         # flop/s, dense
+STAGE_NAMES = ["kda_chunk_prep_kernel", "kda_chunk_state_kernel", "kda_conv_tail_kernel",
+               "kda_out_stage_kernel"]
 KERNEL_SOURCES = ["gated_delta_rule_80_amd/csrc/kda_prep.hip",
                   "gated_delta_rule_80_amd/csrc/kda_prep_exact.hip",
                   "gated_delta_rule_80_amd/csrc/kda_state.hip",
@@ -81,6 +85,16 @@ def decode_bytes(w) -> int:
     x = w.B * w.H * w.D * es
     return (2 * w.B * w.H * w.D * w.D * 4 + 5 * x + w.B * w.H * es
             + 2 * w.B * 3 * 3 * w.H * w.D * es + 3 * w.H * w.D * 16)
+
+
+def stage_bytes(w) -> dict:
+    """Extra algorithmic bytes of the optional stages: the gate pre-activation read
+    once in the fused minimum; the separate output pass reads o and the gate and
+    writes o.  (f and the beta logits replace g and beta byte for byte.)"""
+    es = esize(w.io)
+    x = w.B * w.T * w.H * w.D * es
+    params = (w.H + 2 * w.H * w.D + w.D) * 4  # A_log, dt_bias (and its use), o_norm_w
+    return {"path_extra": x + params, "out_pass": 3 * x + w.D * 4}
 
 
 def traffic_for(kernel: str):
@@ -156,6 +170,99 @@ def _warm(_):
     return 0
 
 
+def time_prefill(kda, torch, a, ws, stream, steps, warmup):
+    """Mean ms per kda_prefill (run stage by stage) and per stage, from HIP events
+    on the launch stream."""
+    n = len(STAGE_NAMES)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        for s in range(n):
+            kda.kda_prefill_stage(a, ws, s, stream)
+            if ev is not None:
+                ev[s + 1].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 1)] for _ in range(steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(steps):
+        step(evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms = t_start.elapsed_time(t_end) / steps
+    stage_ms = [sum(e[s].elapsed_time(e[s + 1]) for e in evs) / steps for s in range(n)]
+    return ms, stage_ms
+
+
+def stages_leg(kda, torch, w, wd, args, stream, dev, plain_ms, plain_dms):
+    """Prefill and decode with every optional stage on (same workloads and seeds)."""
+    from kda_inputs import make_inputs, make_stage_inputs
+    inp = make_inputs(w, seed=args.seed, device=dev)
+    st = make_stage_inputs(w, seed=args.seed, device=dev)
+    o = torch.empty_like(inp["q"])
+    S_T = torch.empty(w.B, w.H, w.D, w.D, dtype=torch.float32, device=dev)
+    cso = torch.empty(w.B, 3, 3, w.H * w.D, dtype=inp["q"].dtype, device=dev)
+    a = kda.prefill_args(inp["q"], inp["k"], inp["v"], st["f"], st["b_logit"], inp["conv_w"],
+                         inp["conv_state"], inp["S0"], o, S_T, cso, chunk=w.chunk,
+                         A_log=st["A_log"], dt_bias=st["dt_bias"], beta_logits=True,
+                         o_norm_w=st["o_norm_w"], o_gate=st["o_gate"])
+    ws = torch.empty(kda.kda_prefill_workspace_bytes(a), dtype=torch.uint8, device=dev)
+    ms, stage_ms = time_prefill(kda, torch, a, ws, stream, args.steps, args.warmup)
+    sb = stage_bytes(w)
+    path_bytes = prefill_bytes(w)["path"] + sb["path_extra"]
+    out_ms = stage_ms[3]
+    out = None
+    if out_ms > 0.001:
+        out = {"bound": "hbm", "kernel": STAGE_NAMES[3], "algorithmic_bytes": sb["out_pass"],
+               "achieved": sb["out_pass"] / (out_ms / 1e3) / 1e9, "peak": HBM_PEAK / 1e9,
+               "unit": "GB/s", "frac": sb["out_pass"] / (out_ms / 1e3) / HBM_PEAK,
+               "traffic": traffic_for(STAGE_NAMES[3]), "mean_launch_ms": out_ms}
+    prefill = {"workload": w.name, "ms_per_step": ms, "tokens_per_s": w.B * w.T / (ms / 1e3),
+               "extra_ms_vs_plain": ms - plain_ms,
+               "output_stage_in_walk": out_ms <= 0.001,
+               "stage_ms": {STAGE_NAMES[i]: stage_ms[i] for i in range(len(STAGE_NAMES))},
+               "path_hbm_frac": path_bytes / (ms / 1e3) / HBM_PEAK, "out_pass_roofline": out}
+    del ws, inp, st, o, S_T, cso
+    torch.cuda.empty_cache()
+
+    dinp = make_inputs(wd, seed=args.seed + 1, device=dev)
+    dst = make_stage_inputs(wd, seed=args.seed + 1, device=dev)
+    S = dinp["S0"]
+    od = torch.empty_like(dinp["q"])
+    da = kda.decode_args(dinp["q"], dinp["k"], dinp["v"], dst["f"], dst["b_logit"], S, od,
+                         dinp["conv_w"], dinp["conv_state"], A_log=dst["A_log"],
+                         dt_bias=dst["dt_bias"], beta_logits=True, o_norm_w=dst["o_norm_w"],
+                         o_gate=dst["o_gate"])
+    for _ in range(args.warmup):
+        kda.kda_decode_raw(da, stream)
+    torch.cuda.synchronize()
+    d0 = torch.cuda.Event(enable_timing=True)
+    d1 = torch.cuda.Event(enable_timing=True)
+    d0.record(stream)
+    for _ in range(args.steps):
+        kda.kda_decode_raw(da, stream)
+    d1.record(stream)
+    torch.cuda.synchronize()
+    dms = d0.elapsed_time(d1) / args.steps
+    dbytes = decode_bytes(wd) + wd.B * wd.H * wd.D * esize(wd.io) + (wd.H + wd.H * wd.D + wd.D) * 4
+    decode = {"workload": wd.name, "ms_per_step": dms, "seq_per_s": wd.B / (dms / 1e3),
+              "extra_ms_vs_plain": dms - plain_dms,
+              "roofline": {"bound": "hbm", "kernel": "kda_decode_kernel",
+                           "achieved": dbytes / (dms / 1e3) / 1e9, "peak": HBM_PEAK / 1e9,
+                           "unit": "GB/s", "frac": dbytes / (dms / 1e3) / HBM_PEAK,
+                           "algorithmic_bytes": dbytes}}
+    del dinp, dst, S, od
+    torch.cuda.empty_cache()
+    return {"what": "raw-projection decay and beta, output RMSNorm + sigmoid gate",
+            "prefill": prefill, "decode": decode}
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -165,6 +272,8 @@ def main(argv=None) -> int:
     ap.add_argument("--decode-workload", default="decode-b256")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing (0 = skip)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-stages", action="store_true",
+                    help="skip the leg with the optional stages (raw projections, output norm + gate)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run the library's plain state-copy kernel (kda_prefill with T=0) "
                          "on this many MiB, to calibrate HBM byte counters")
@@ -191,32 +300,11 @@ def main(argv=None) -> int:
     ws = torch.empty(kda.kda_prefill_workspace_bytes(a), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        for s in range(3):
-            kda.kda_prefill_stage(a, ws, s, stream)
-            if ev is not None:
-                ev[s + 1].record(stream)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for i in range(args.steps):
-        step(evs[i])
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    ms = t_start.elapsed_time(t_end) / args.steps
-    stage_ms = [sum(e[s].elapsed_time(e[s + 1]) for e in evs) / args.steps for s in range(3)]
+    ms, stage_ms = time_prefill(kda, torch, a, ws, stream, args.steps, args.warmup)
     tokens_per_s = w.B * w.T / (ms / 1e3)
 
     nb = prefill_bytes(w)
-    names = ["kda_chunk_prep_kernel", "kda_chunk_state_kernel", "kda_conv_tail_kernel"]
+    names = STAGE_NAMES
     dom = 0 if stage_ms[0] >= stage_ms[1] else 1
     dom_bytes = nb["prep"] if dom == 0 else nb["state"]
     achieved = dom_bytes / (stage_ms[dom] / 1e3)
@@ -229,6 +317,7 @@ def main(argv=None) -> int:
             "hbm_frac": nb["path"] / (ms / 1e3) / HBM_PEAK,
             "mfma_frac_useful": flops / (ms / 1e3) / BF16_PEAK,
             "stage_ms": {names[i]: stage_ms[i] for i in range(3)}}
+    plain_ms = ms
     del ws, inp, o, S_T, cso
     torch.cuda.empty_cache()
 
@@ -262,6 +351,10 @@ def main(argv=None) -> int:
     del dinp, S, cs, od
     torch.cuda.empty_cache()
 
+    stages = None
+    if not args.no_stages:
+        stages = stages_leg(kda, torch, w, wd, args, stream, dev, plain_ms, dms)
+
     if args.calib_copy_mib > 0:
         # kda_prefill with T = 0 copies S0 to S_T with one plain copy kernel
         # (kda_copy_state_kernel): exactly n bytes read and n bytes written.
@@ -291,7 +384,8 @@ def main(argv=None) -> int:
         "vs_baseline": None, "dtype": w.io, "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "D": w.D, "chunk": w.chunk,
                    "io": w.io, "state": "fp32"},
-        "roofline": roofline, "path": path, "decode": decode, "cpu_baseline": cpu,
+        "roofline": roofline, "path": path, "decode": decode, "stages": stages,
+        "cpu_baseline": cpu,
         "source_hash": source_hash(),
     }
     print(json.dumps(line), flush=True)

@@ -22,7 +22,10 @@ KDA_OK = 0
 KDA_BF16 = 0
 KDA_FP32 = 1
 KDA_FLAG_L2NORM_QK = 1
-KDA_STAGE_PREP, KDA_STAGE_STATE, KDA_STAGE_CONV_TAIL = 0, 1, 2
+KDA_FLAG_BETA_LOGITS = 2
+ABI_VERSION = 2
+KDA_STAGE_PREP, KDA_STAGE_STATE, KDA_STAGE_CONV_TAIL, KDA_STAGE_OUTPUT = 0, 1, 2, 3
+NUM_STAGES = 4
 STATUS_NAMES = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE",
                 4: "KDA_ERR_ALIGN", 5: "KDA_ERR_ALIAS", 6: "KDA_ERR_UNSUPPORTED",
                 7: "KDA_ERR_WORKSPACE", 8: "KDA_ERR_HIP", 9: "KDA_ERR_VALUE"}
@@ -37,7 +40,9 @@ class PrefillArgs(ctypes.Structure):
                 ("io", ctypes.c_int32),
                 ("q", _vp), ("k", _vp), ("v", _vp), ("g", _vp), ("beta", _vp), ("conv_w", _vp),
                 ("conv_state_in", _vp), ("S0", _vp), ("o", _vp), ("S_T", _vp),
-                ("conv_state_out", _vp)]
+                ("conv_state_out", _vp),
+                ("A_log", _vp), ("dt_bias", _vp), ("o_norm_w", _vp), ("o_norm_eps", ctypes.c_float),
+                ("o_gate", _vp)]
 
 
 class ConvNormArgs(ctypes.Structure):
@@ -53,7 +58,9 @@ class DecodeArgs(ctypes.Structure):
                 ("conv_k", ctypes.c_int32), ("flags", ctypes.c_uint32), ("l2_eps", ctypes.c_float),
                 ("scale", ctypes.c_float), ("io", ctypes.c_int32),
                 ("q", _vp), ("k", _vp), ("v", _vp), ("g", _vp), ("beta", _vp), ("conv_w", _vp),
-                ("conv_state", _vp), ("S", _vp), ("o", _vp)]
+                ("conv_state", _vp), ("S", _vp), ("o", _vp),
+                ("A_log", _vp), ("dt_bias", _vp), ("o_norm_w", _vp), ("o_norm_eps", ctypes.c_float),
+                ("o_gate", _vp)]
 
 
 class KdaError(RuntimeError):
@@ -103,7 +110,7 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.kda_validate_decode.argtypes = [P(DecodeArgs)]
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [P(DecodeArgs), _vp]
-    if lib.kda_abi_version() != 1:
+    if lib.kda_abi_version() != ABI_VERSION:
         raise RuntimeError("libkda ABI version mismatch")
     if path is None:
         _lib = lib
@@ -157,9 +164,19 @@ def _check(status: int, where: str):
         raise KdaError(status, where)
 
 
+def _flags(l2norm_qk: bool, beta_logits: bool) -> int:
+    return (KDA_FLAG_L2NORM_QK if l2norm_qk else 0) | (KDA_FLAG_BETA_LOGITS if beta_logits else 0)
+
+
+def _stages(a, A_log, dt_bias, o_norm_w, o_norm_eps, o_gate):
+    a.A_log, a.dt_bias, a.o_norm_w, a.o_gate = _ptr(A_log), _ptr(dt_bias), _ptr(o_norm_w), _ptr(o_gate)
+    a.o_norm_eps = o_norm_eps
+
+
 def prefill_args(q, k, v, g, beta, conv_w=None, conv_state_in=None, S0=None, o=None, S_T=None,
                  conv_state_out=None, *, chunk=64, scale=1.0, l2norm_qk=True, eps=1e-6,
-                 conv_k=None, B=None, T=None, H=None, D=None, io=None) -> PrefillArgs:
+                 conv_k=None, B=None, T=None, H=None, D=None, io=None, A_log=None, dt_bias=None,
+                 beta_logits=False, o_norm_w=None, o_norm_eps=1e-6, o_gate=None) -> PrefillArgs:
     """Fill kda_prefill_args from tensors (shapes from q unless given explicitly)."""
     a = PrefillArgs()
     if q is not None and not isinstance(q, int):
@@ -172,13 +189,14 @@ def prefill_args(q, k, v, g, beta, conv_w=None, conv_state_in=None, S0=None, o=N
                           H0 if H is None else H, D0 if D is None else D)
     a.chunk = chunk
     a.conv_k = (4 if conv_w is not None else 0) if conv_k is None else conv_k
-    a.flags = KDA_FLAG_L2NORM_QK if l2norm_qk else 0
+    a.flags = _flags(l2norm_qk, beta_logits)
     a.l2_eps = eps
     a.scale = scale
     a.io = io0 if io is None else io
     a.q, a.k, a.v, a.g, a.beta = _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta)
     a.conv_w, a.conv_state_in, a.S0 = _ptr(conv_w), _ptr(conv_state_in), _ptr(S0)
     a.o, a.S_T, a.conv_state_out = _ptr(o), _ptr(S_T), _ptr(conv_state_out)
+    _stages(a, A_log, dt_bias, o_norm_w, o_norm_eps, o_gate)
     return a
 
 
@@ -201,12 +219,16 @@ def _workspace(args: PrefillArgs, device, workspace=None):
 
 def kda_prefill(q, k, v, g, beta, conv_w=None, conv_state=None, S0=None, *, chunk=64, scale=1.0,
                 l2norm_qk=True, eps=1e-6, o=None, S_T=None, conv_state_out=None, workspace=None,
-                stream=None):
+                stream=None, A_log=None, dt_bias=None, beta_logits=False, o_norm_w=None,
+                o_norm_eps=1e-6, o_gate=None):
     """Whole-sequence KDA forward.  Returns (o, S_T, conv_state_out).
 
     q, k, v, g: [B, T, H, D] (bf16 or fp32, same dtype); beta [B, T, H];
     conv_w [3, H*D, 4] fp32 or None (no conv); conv_state [B, 3, 3, H*D] or None;
     S0 [B, H, D, D] fp32 or None.  Outputs are allocated unless given.
+    Optional stages: A_log [H] and dt_bias [H*D] fp32 (g then holds the raw gate
+    projection), beta_logits (beta holds logits), o_norm_w [D] fp32 and o_gate
+    [B, T, H, D] for the output RMSNorm and sigmoid gate.
     """
     B, T, H, D = q.shape
     dev = q.device
@@ -217,7 +239,9 @@ def kda_prefill(q, k, v, g, beta, conv_w=None, conv_state=None, S0=None, *, chun
     if conv_state_out is None and conv_w is not None:
         conv_state_out = torch.empty(B, 3, 3, H * D, dtype=q.dtype, device=dev)
     a = prefill_args(q, k, v, g, beta, conv_w, conv_state, S0, o, S_T, conv_state_out, chunk=chunk,
-                     scale=scale, l2norm_qk=l2norm_qk, eps=eps)
+                     scale=scale, l2norm_qk=l2norm_qk, eps=eps, A_log=A_log, dt_bias=dt_bias,
+                     beta_logits=beta_logits, o_norm_w=o_norm_w, o_norm_eps=o_norm_eps,
+                     o_gate=o_gate)
     _check(kda_validate_prefill(a), "kda_prefill")
     ws, need = _workspace(a, dev, workspace)
     _check(load().kda_prefill(ctypes.byref(a), _ptr(ws) if ws is not None else None, need if
@@ -227,7 +251,8 @@ def kda_prefill(q, k, v, g, beta, conv_w=None, conv_state=None, S0=None, *, chun
 
 
 def kda_prefill_stage(args: PrefillArgs, workspace, stage: int, stream=None):
-    """Enqueue one stage of kda_prefill (0 prep, 1 state walk, 2 conv hand-over)."""
+    """Enqueue one stage of kda_prefill (0 prep, 1 state walk, 2 conv hand-over,
+    3 separate output-stage pass)."""
     ws = _ptr(workspace) if workspace is not None else None
     nbytes = workspace.numel() if workspace is not None else 0
     _check(load().kda_prefill_stage(ctypes.byref(args), ws, nbytes, int(stage), _stream(stream)),
@@ -274,16 +299,18 @@ def kda_conv_norm(q, k, v, conv_w, conv_state=None, *, l2norm_qk=True, eps=1e-6,
 
 
 def decode_args(q, k, v, g, beta, S, o, conv_w=None, conv_state=None, *, scale=1.0,
-                l2norm_qk=True, eps=1e-6) -> DecodeArgs:
+                l2norm_qk=True, eps=1e-6, A_log=None, dt_bias=None, beta_logits=False,
+                o_norm_w=None, o_norm_eps=1e-6, o_gate=None) -> DecodeArgs:
     a = DecodeArgs()
     a.B, a.H, a.D = q.shape
     a.conv_k = 4 if conv_w is not None else 0
-    a.flags = KDA_FLAG_L2NORM_QK if l2norm_qk else 0
+    a.flags = _flags(l2norm_qk, beta_logits)
     a.l2_eps = eps
     a.scale = scale
     a.io = _io_of(q)
     a.q, a.k, a.v, a.g, a.beta = _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta)
     a.conv_w, a.conv_state, a.S, a.o = _ptr(conv_w), _ptr(conv_state), _ptr(S), _ptr(o)
+    _stages(a, A_log, dt_bias, o_norm_w, o_norm_eps, o_gate)
     return a
 
 
@@ -292,15 +319,18 @@ def kda_validate_decode(args: DecodeArgs) -> int:
 
 
 def kda_decode_step(q, k, v, g, beta, S, conv_w=None, conv_state=None, *, scale=1.0,
-                    l2norm_qk=True, eps=1e-6, o=None, stream=None):
+                    l2norm_qk=True, eps=1e-6, o=None, stream=None, A_log=None, dt_bias=None,
+                    beta_logits=False, o_norm_w=None, o_norm_eps=1e-6, o_gate=None):
     """One decode step; S [B,H,D,D] fp32 and conv_state [B,3,3,H*D] are updated in place.
 
-    q, k, v, g: [B, H, D]; beta [B, H].  Returns o [B, H, D].
+    q, k, v, g: [B, H, D]; beta [B, H].  Returns o [B, H, D].  Optional stages as
+    in kda_prefill (o_gate [B, H, D]).
     """
     if o is None:
         o = torch.empty_like(q)
     a = decode_args(q, k, v, g, beta, S, o, conv_w, conv_state, scale=scale, l2norm_qk=l2norm_qk,
-                    eps=eps)
+                    eps=eps, A_log=A_log, dt_bias=dt_bias, beta_logits=beta_logits,
+                    o_norm_w=o_norm_w, o_norm_eps=o_norm_eps, o_gate=o_gate)
     _check(load().kda_decode_step(ctypes.byref(a), _stream(stream)), "kda_decode_step")
     return o
 

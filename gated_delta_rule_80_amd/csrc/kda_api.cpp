@@ -86,14 +86,34 @@ kda::WorkspaceLayout ws_layout(const kda_prefill_args* a) {
 // wider blocks read less per column; with bf16 at D = 128, 64 columns on 512
 // threads measured fastest at B * H = 96 and 384.  Narrower blocks give more
 // parallel walks elsewhere.
+//
+// With the output stage (gn) the walk applies it itself when one workgroup holds
+// all D value columns (D <= 64: fused); at D = 128 o is finished by a separate
+// in-place pass.  (A whole-row walk for bf16 at D = 128, 1024 threads, measured
+// slower than the 64-column walk plus that pass at B * H = 96 and 384.)
 struct StateCfg {
   int vb, threads;
+  bool fused;
 };
-StateCfg state_config(int B, int H, int D, bool fp32) {
-  if (D < 64) return {D, 256};
-  if (D == 128 && !fp32) return {64, 512};
+StateCfg state_config(int B, int H, int D, bool fp32, bool gn) {
+  if (D < 64) return {D, 256, gn};
+  if (gn && D == 64) return {64, 256, true};
+  if (D == 128 && !fp32) return {64, 512, false};
   const long walks64 = (long)B * H * (D / 64);
-  return {walks64 < 240 ? 32 : 64, 256};
+  return {walks64 < 240 ? 32 : 64, 256, false};
+}
+
+constexpr uint32_t kKnownFlags = KDA_FLAG_L2NORM_QK | KDA_FLAG_BETA_LOGITS;
+
+// Checks shared by prefill and decode for the optional stages' pointers and
+// scalars (their overlaps are checked with the other buffers).
+kda_status validate_stages(const float* A_log, const float* dt_bias, const float* o_norm_w,
+                           float o_norm_eps, const void* o_gate) {
+  if ((A_log == nullptr) != (dt_bias == nullptr)) return KDA_ERR_NULL;
+  if (o_norm_w != nullptr && (!std::isfinite(o_norm_eps) || o_norm_eps < 0.f)) return KDA_ERR_VALUE;
+  for (const void* p : {(const void*)A_log, (const void*)dt_bias, (const void*)o_norm_w, o_gate})
+    if (p && !aligned16(p)) return KDA_ERR_ALIGN;
+  return KDA_OK;
 }
 
 }  // namespace
@@ -126,10 +146,13 @@ kda_status kda_validate_prefill(const kda_prefill_args* a) {
   if (!supported_d(a->D) || !supported_chunk(a->chunk) || (a->conv_k != 0 && a->conv_k != 4))
     return KDA_ERR_UNSUPPORTED;
   if (a->io == KDA_FP32 && a->D == 128 && a->chunk == 64) return KDA_ERR_UNSUPPORTED;
-  if ((a->flags & ~KDA_FLAG_L2NORM_QK) != 0) return KDA_ERR_VALUE;
+  if ((a->flags & ~kKnownFlags) != 0) return KDA_ERR_VALUE;
   if (!std::isfinite(a->l2_eps) || a->l2_eps < 0.f || !std::isfinite(a->scale)) return KDA_ERR_VALUE;
   PrefillSizes s;
   if (kda_status e = prefill_sizes(a, s); e != KDA_OK) return e;
+  if (kda_status e = validate_stages(a->A_log, a->dt_bias, a->o_norm_w, a->o_norm_eps, a->o_gate);
+      e != KDA_OK)
+    return e;
   const bool need_x = a->T > 0;
   if (need_x && (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->o)) return KDA_ERR_NULL;
   if (!a->S_T) return KDA_ERR_NULL;
@@ -142,12 +165,14 @@ kda_status kda_validate_prefill(const kda_prefill_args* a) {
   const Span bt = span(a->beta, s.bta), cw = span(a->conv_w, s.cw);
   const Span ci = span(a->conv_state_in, s.cst), co = span(a->conv_state_out, s.cst);
   const Span s0 = span(a->S0, s.state), st = span(a->S_T, s.state), o = span(a->o, s.x);
-  for (Span in : {q, k, v, g, bt, cw, ci, s0, st, co})
+  const Span al = span(a->A_log, (size_t)a->H * 4), db = span(a->dt_bias, (size_t)a->H * a->D * 4);
+  const Span nw = span(a->o_norm_w, (size_t)a->D * 4), og = span(a->o_gate, s.x);
+  for (Span in : {q, k, v, g, bt, cw, ci, s0, st, co, al, db, nw, og})
     if (overlaps(o, in)) return KDA_ERR_ALIAS;
-  for (Span in : {q, k, v, g, bt, cw, ci, co})
+  for (Span in : {q, k, v, g, bt, cw, ci, co, al, db, nw, og})
     if (overlaps(st, in)) return KDA_ERR_ALIAS;
   if (!same_or_disjoint(st, s0)) return KDA_ERR_ALIAS;
-  for (Span in : {q, k, v, g, bt, cw, s0})
+  for (Span in : {q, k, v, g, bt, cw, s0, al, db, nw, og})
     if (overlaps(co, in)) return KDA_ERR_ALIAS;
   if (!same_or_disjoint(co, ci)) return KDA_ERR_ALIAS;
   return KDA_OK;
@@ -174,7 +199,9 @@ static kda_status check_workspace(const kda_prefill_args* a, void* ws, size_t ws
   for (Span x : {span(a->q, s.x), span(a->k, s.x), span(a->v, s.x), span(a->g, s.x),
                  span(a->beta, s.bta), span(a->conv_w, s.cw), span(a->conv_state_in, s.cst),
                  span(a->S0, s.state), span(a->o, s.x), span(a->S_T, s.state),
-                 span(a->conv_state_out, s.cst)})
+                 span(a->conv_state_out, s.cst), span(a->A_log, (size_t)a->H * 4),
+                 span(a->dt_bias, (size_t)a->H * a->D * 4), span(a->o_norm_w, (size_t)a->D * 4),
+                 span(a->o_gate, s.x)})
     if (overlaps(w, x)) return KDA_ERR_ALIAS;
   return KDA_OK;
 }
@@ -198,6 +225,9 @@ static kda_status run_stage(const kda_prefill_args* a, void* ws, int stage, hipS
       p.l2 = (a->flags & KDA_FLAG_L2NORM_QK) ? 1 : 0;
       p.eps = a->l2_eps;
       p.scale = a->scale;
+      p.A_log = a->A_log;
+      p.dt_bias = a->dt_bias;
+      p.beta_logits = (a->flags & KDA_FLAG_BETA_LOGITS) ? 1 : 0;
       return hip_status(kda::launch_prep(p, a->D, a->chunk, fp32, st));
     }
     case KDA_STAGE_STATE: {
@@ -206,13 +236,28 @@ static kda_status run_stage(const kda_prefill_args* a, void* ws, int stage, hipS
         const size_t n = (size_t)a->B * a->H * a->D * a->D;
         return hip_status(kda::launch_copy_state(a->S0, a->S_T, n, st));
       }
+      const bool gn = a->o_norm_w != nullptr || a->o_gate != nullptr;
+      const StateCfg cfg = state_config(a->B, a->H, a->D, fp32, gn);
       kda::StateParams p{};
       p.ws = static_cast<const char*>(ws) + ws_layout(a).records;
       p.S0 = a->S0; p.S_T = a->S_T; p.o = a->o;
       p.B = a->B; p.T = a->T; p.H = a->H; p.NT = NT;
-      return hip_status(
-          kda::launch_state(p, a->D, a->chunk, fp32, state_config(a->B, a->H, a->D, fp32).vb,
-                            state_config(a->B, a->H, a->D, fp32).threads, st));
+      p.o_gate = a->o_gate;
+      p.o_norm_w = a->o_norm_w;
+      p.o_norm_eps = a->o_norm_eps;
+      return hip_status(kda::launch_state(p, a->D, a->chunk, fp32, cfg.vb, cfg.threads, cfg.fused,
+                                          st));
+    }
+    case KDA_STAGE_OUTPUT: {
+      const bool gn = a->o_norm_w != nullptr || a->o_gate != nullptr;
+      if (a->T == 0 || !gn || state_config(a->B, a->H, a->D, fp32, gn).fused) return KDA_OK;
+      kda::OutStageParams q{};
+      q.o = a->o;
+      q.o_gate = a->o_gate;
+      q.o_norm_w = a->o_norm_w;
+      q.o_norm_eps = a->o_norm_eps;
+      q.rows = (long)a->B * a->T * a->H;
+      return hip_status(kda::launch_out_stage(q, a->D, fp32, st));
     }
     case KDA_STAGE_CONV_TAIL: {
       if (a->conv_k == 0 || a->conv_state_out == nullptr) return KDA_OK;
@@ -230,7 +275,7 @@ static kda_status run_stage(const kda_prefill_args* a, void* ws, int stage, hipS
 kda_status kda_prefill_stage(const kda_prefill_args* a, void* ws, size_t ws_bytes, int stage,
                              void* stream) {
   if (kda_status e = kda_validate_prefill(a); e != KDA_OK) return e;
-  if (stage < KDA_STAGE_PREP || stage > KDA_STAGE_CONV_TAIL) return KDA_ERR_VALUE;
+  if (stage < KDA_STAGE_PREP || stage > KDA_STAGE_OUTPUT) return KDA_ERR_VALUE;
   if (kda_status e = check_workspace(a, ws, ws_bytes); e != KDA_OK) return e;
   return run_stage(a, ws, stage, static_cast<hipStream_t>(stream));
 }
@@ -239,7 +284,7 @@ kda_status kda_prefill(const kda_prefill_args* a, void* ws, size_t ws_bytes, voi
   if (kda_status e = kda_validate_prefill(a); e != KDA_OK) return e;
   if (kda_status e = check_workspace(a, ws, ws_bytes); e != KDA_OK) return e;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  for (int stage = KDA_STAGE_PREP; stage <= KDA_STAGE_CONV_TAIL; ++stage)
+  for (int stage = KDA_STAGE_PREP; stage <= KDA_STAGE_OUTPUT; ++stage)
     if (kda_status e = run_stage(a, ws, stage, st); e != KDA_OK) return e;
   return KDA_OK;
 }
@@ -310,8 +355,11 @@ kda_status kda_validate_decode(const kda_decode_args* a) {
   if (a->io != KDA_BF16 && a->io != KDA_FP32) return KDA_ERR_DTYPE;
   if (a->B < 1 || a->H < 1 || a->D < 1 || a->conv_k < 0) return KDA_ERR_SHAPE;
   if (!supported_d(a->D) || (a->conv_k != 0 && a->conv_k != 4)) return KDA_ERR_UNSUPPORTED;
-  if ((a->flags & ~KDA_FLAG_L2NORM_QK) != 0) return KDA_ERR_VALUE;
+  if ((a->flags & ~kKnownFlags) != 0) return KDA_ERR_VALUE;
   if (!std::isfinite(a->l2_eps) || a->l2_eps < 0.f || !std::isfinite(a->scale)) return KDA_ERR_VALUE;
+  if (kda_status e = validate_stages(a->A_log, a->dt_bias, a->o_norm_w, a->o_norm_eps, a->o_gate);
+      e != KDA_OK)
+    return e;
   const size_t es = esize(a->io);
   const size_t ck = a->conv_k > 0 ? (size_t)a->conv_k : 0;
   size_t x, bt, st, cw, cst;
@@ -331,11 +379,13 @@ kda_status kda_validate_decode(const kda_decode_args* a) {
   const Span q = span(a->q, x), k = span(a->k, x), v = span(a->v, x), g = span(a->g, x);
   const Span b = span(a->beta, bt), w = span(a->conv_w, cw), cs = span(a->conv_state, cst);
   const Span S = span(a->S, st), o = span(a->o, x);
-  for (Span in : {q, k, v, g, b, w, cs, S})
+  const Span al = span(a->A_log, (size_t)a->H * 4), db = span(a->dt_bias, (size_t)a->H * a->D * 4);
+  const Span nw = span(a->o_norm_w, (size_t)a->D * 4), og = span(a->o_gate, x);
+  for (Span in : {q, k, v, g, b, w, cs, S, al, db, nw, og})
     if (overlaps(o, in)) return KDA_ERR_ALIAS;
-  for (Span in : {q, k, v, g, b, w, cs})
+  for (Span in : {q, k, v, g, b, w, cs, al, db, nw, og})
     if (overlaps(S, in)) return KDA_ERR_ALIAS;
-  for (Span in : {q, k, v, g, b, w})
+  for (Span in : {q, k, v, g, b, w, al, db, nw, og})
     if (overlaps(cs, in)) return KDA_ERR_ALIAS;
   return KDA_OK;
 }
@@ -353,6 +403,12 @@ kda_status kda_decode_step(const kda_decode_args* a, void* stream) {
   p.l2 = (a->flags & KDA_FLAG_L2NORM_QK) ? 1 : 0;
   p.eps = a->l2_eps;
   p.scale = a->scale;
+  p.A_log = a->A_log;
+  p.dt_bias = a->dt_bias;
+  p.beta_logits = (a->flags & KDA_FLAG_BETA_LOGITS) ? 1 : 0;
+  p.o_gate = a->o_gate;
+  p.o_norm_w = a->o_norm_w;
+  p.o_norm_eps = a->o_norm_eps;
   return hip_status(kda::launch_decode(p, a->D, a->io == KDA_FP32, static_cast<hipStream_t>(stream)));
 }
 

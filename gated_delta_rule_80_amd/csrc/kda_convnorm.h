@@ -19,6 +19,19 @@ __device__ __forceinline__ float silu_fast(float x) {
   return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-kLog2e * x));
 }
 
+// sigmoid(x) the same way
+__device__ __forceinline__ float sigmoid_fast(float x) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-kLog2e * x));
+}
+
+// softplus(x) * log2(e) = max(x, 0) log2(e) + log2(1 + 2^(-|x| log2(e))), with the
+// hardware base-2 exp and log.  Where 2^(-|x| log2 e) < 2^-24 the second term
+// rounds to 0 (an absolute error below 1e-7).
+__device__ __forceinline__ float softplus_log2(float x) {
+  const float e = __builtin_amdgcn_exp2f(-kLog2e * fabsf(x));
+  return fmaf(fmaxf(x, 0.0f), kLog2e, __builtin_amdgcn_logf(1.0f + e));
+}
+
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __amdgpu_buffer_rsrc_t BufRes;
 

@@ -8,6 +8,9 @@
 //   u = beta (v - r_k);  o = r_q + (k . q) u  ( = S_new^T q );  S_new = S_bar + k u^T
 // The two reductions over the key channels share one pass: each thread owns a
 // few state rows x 4 value columns and partial sums are combined through LDS.
+// Optional stages: g and beta from raw projections (-exp(A_log) softplus(f +
+// dt_bias), sigmoid(b)), and o <- RMSNorm(o) * gain * sigmoid(gate) over the
+// head's D values, which this workgroup holds whole.
 #include "kda_device.h"
 #include "kda_launch.h"
 #include "kda_layout.h"
@@ -30,6 +33,7 @@ __global__ __launch_bounds__(DecodeShape<D>::NTH) void kda_decode_kernel(DecodeP
   static_assert(R >= 1 && CG * R == D, "decode tiling");
   __shared__ float sq[D], sk[D], sv[D], sa[D], su[D];
   __shared__ float red[3][NW];
+  __shared__ float ored[NW];
   __shared__ f32x4 part[2][CG][VG];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -78,7 +82,9 @@ __global__ __launch_bounds__(DecodeShape<D>::NTH) void kda_decode_kernel(DecodeP
     yq = y[0];
     yk = y[1];
     yv = y[2];
-    sa[c] = __expf(to_f32(static_cast<const IO*>(p.g)[xo]));
+    float gc = to_f32(static_cast<const IO*>(p.g)[xo]);
+    if (p.A_log != nullptr) gc = gate_decay(gc, p.dt_bias[(size_t)h * D + c], -__expf(p.A_log[h]));
+    sa[c] = __expf(gc);
   }
   // ---- L2 norms and <q, k> over the head's D channels
   float s_qq = group_sum<64>(yq * yq), s_kk = group_sum<64>(yk * yk), s_qk = group_sum<64>(yq * yk);
@@ -103,7 +109,8 @@ __global__ __launch_bounds__(DecodeShape<D>::NTH) void kda_decode_kernel(DecodeP
     sk[tid] = yk * rk;
     sv[tid] = yv;
   }
-  const float beta = to_f32(static_cast<const IO*>(p.beta)[bh]);
+  float beta = to_f32(static_cast<const IO*>(p.beta)[bh]);
+  if (p.beta_logits) beta = sigmoid(beta);
   __syncthreads();
 
   // ---- one sweep: decay the rows, partial S_bar^T k and S_bar^T q
@@ -122,6 +129,7 @@ __global__ __launch_bounds__(DecodeShape<D>::NTH) void kda_decode_kernel(DecodeP
   part[0][cg][vg] = pk;
   part[1][cg][vg] = pq;
   __syncthreads();
+  float ov = 0.f;
   if (tid < D) {
     const int v = tid;
     float rk_v = 0.f, rq_v = 0.f;
@@ -132,7 +140,21 @@ __global__ __launch_bounds__(DecodeShape<D>::NTH) void kda_decode_kernel(DecodeP
     }
     const float u = beta * (sv[v] - rk_v);
     su[v] = u;
-    static_cast<IO*>(p.o)[(size_t)bh * D + v] = from_f32<IO>(rq_v + kq * u);
+    ov = rq_v + kq * u;
+  }
+  if (p.o_norm_w != nullptr) {
+    // mean square of the head's D outputs (threads >= D contribute zeros)
+    const float ss = group_sum<64>(ov * ov);
+    if (lane == 0) ored[wave] = ss;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) tot += ored[w];
+    if (tid < D) ov *= p.o_norm_w[tid] / sqrtf(tot * (1.0f / D) + p.o_norm_eps);
+  }
+  if (tid < D) {
+    if (p.o_gate != nullptr) ov *= sigmoid(to_f32(static_cast<const IO*>(p.o_gate)[(size_t)bh * D + tid]));
+    static_cast<IO*>(p.o)[(size_t)bh * D + tid] = from_f32<IO>(ov);
   }
   __syncthreads();
   // ---- S_new = S_bar + k u^T, streamed back

@@ -298,6 +298,18 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // ------------------------------------------------------------ small math
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
+__device__ __forceinline__ float sigmoid(float x) { return 1.0f / (1.0f + __expf(-x)); }
+// ln(1 + e^x) as max(x, 0) + ln(1 + e^-|x|) with the hardware exp and log: no
+// overflow; where e^-|x| < 2^-24 the second term rounds to 0, an absolute error
+// below 6e-8 (the decay of such a channel is below 1e-7 per token anyway).
+__device__ __forceinline__ float softplus(float x) {
+  return fmaxf(x, 0.0f) + __logf(1.0f + __expf(-fabsf(x)));
+}
+// Log-decay of one key channel from the raw gate projection f: -exp(A_log[h]) *
+// softplus(f + dt_bias[c]); `neg_rate` is -exp(A_log[h]) (times any unit change).
+__device__ __forceinline__ float gate_decay(float f, float bias, float neg_rate) {
+  return neg_rate * softplus(f + bias);
+}
 
 // x from another lane of the same 16-lane row by a DPP lane pattern (all lanes
 // active)

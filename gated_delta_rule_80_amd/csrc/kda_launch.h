@@ -9,8 +9,9 @@ namespace kda {
 hipError_t launch_prep(const PrepParams& p, int D, int C, bool fp32, hipStream_t st);
 hipError_t launch_prep_exact(const PrepParams& p, int D, int C, bool fp32, unsigned grid,
                              hipStream_t st);
-hipError_t launch_state(const StateParams& p, int D, int C, bool fp32, int vb, int threads,
+hipError_t launch_state(const StateParams& p, int D, int C, bool fp32, int vb, int threads, bool gn,
                         hipStream_t st);
+hipError_t launch_out_stage(const OutStageParams& p, int D, bool fp32, hipStream_t st);
 hipError_t launch_conv_norm(const ConvNormParams& p, int D, bool fp32, hipStream_t st);
 hipError_t launch_conv_tail(const TailParams& p, bool fp32, hipStream_t st);
 hipError_t launch_copy_state(const float* src, float* dst, size_t n, hipStream_t st);

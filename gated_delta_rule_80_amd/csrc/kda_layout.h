@@ -69,6 +69,9 @@ struct PrepParams {
   int l2;
   float eps;
   float scale;
+  const float* A_log;    // [H]: g holds the raw gate projection (with dt_bias), or NULL
+  const float* dt_bias;  // [H*D]
+  int beta_logits;       // beta holds logits
 };
 
 struct StateParams {
@@ -77,6 +80,20 @@ struct StateParams {
   float* S_T;
   void* o;
   int B, T, H, NT;
+  // output stage, applied in the walk only by the kernels built for it
+  const void* o_gate;     // [B][T][H][D] or NULL
+  const float* o_norm_w;  // [D] or NULL
+  float o_norm_eps;
+};
+
+// The output stage on its own, in place on o: RMSNorm with gain and/or the
+// sigmoid gate, one row of D values per (token, head).
+struct OutStageParams {
+  void* o;
+  const void* o_gate;     // or NULL
+  const float* o_norm_w;  // or NULL
+  float o_norm_eps;
+  long rows;
 };
 
 struct ConvNormParams {
@@ -115,6 +132,12 @@ struct DecodeParams {
   int l2;
   float eps;
   float scale;
+  const float* A_log;     // as in PrepParams
+  const float* dt_bias;
+  int beta_logits;
+  const void* o_gate;     // [B][H][D] or NULL
+  const float* o_norm_w;  // [D] or NULL
+  float o_norm_eps;
 };
 
 }  // namespace kda

@@ -206,9 +206,19 @@ __global__ __launch_bounds__(fast_threads<E>()) void kda_chunk_prep_kernel(PrepP
   // the end of the sequence
   Raw8<IO> graw[TOK];
   float braw[TOK];
+  const int nt = p.T - t0 < C ? p.T - t0 : C;  // tokens of the sequence in this chunk
+  // raw gate projection: this thread's 8 channel biases and minus the head's rate
+  const bool gact = p.A_log != nullptr;
+  f32x4 gb0 = {0.f, 0.f, 0.f, 0.f}, gb1 = gb0;
+  float gneg = 0.f;
+  if (gact) {
+    const f32x4* bp = reinterpret_cast<const f32x4*>(p.dt_bias + (size_t)h * D + ch);
+    gb0 = bp[0];
+    gb1 = bp[1];
+    gneg = -__expf(p.A_log[h]);
+  }
   {
     constexpr int ES = (int)sizeof(IO);
-    const int nt = p.T - t0 < C ? p.T - t0 : C;
     const long HD = (long)p.H * D;
     const BufRes rg = make_buf(static_cast<const IO*>(p.g) + ((long)b * p.T + t0) * HD + (long)h * D,
                                (unsigned)(((long)(nt - 1) * HD + D) * ES));
@@ -235,14 +245,21 @@ __global__ __launch_bounds__(fast_threads<E>()) void kda_chunk_prep_kernel(PrepP
   front_compute<TOK, D, IO, false, false>(win, sm.filt, conv, ch, tf, p.T, active, p.l2 != 0,
                                           p.eps, p.scale, yq, yk, yv, qk);
   // cumulative log2-decay within the segment.  Past the end of the sequence g
-  // and beta are 0, which is all the later phases need of those tokens.
+  // and beta are 0 (the range-checked loads give zeros; the activations of raw
+  // projections are masked there), which is all the later phases need of those
+  // tokens.
   float gc[TOK][8], bt[TOK];
 #pragma unroll
   for (int m = 0; m < TOK; ++m) {
-    bt[m] = braw[m];
+    const bool in_seq = TOK * s + m < nt;
+    bt[m] = p.beta_logits ? (in_seq ? sigmoid_fast(braw[m]) : 0.f) : braw[m];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const float gv = graw[m][c] * kLog2e;
+      float gv;  // log2 units
+      if (gact)
+        gv = in_seq ? gneg * softplus_log2(graw[m][c] + (c < 4 ? gb0[c] : gb1[c - 4])) : 0.f;
+      else
+        gv = graw[m][c] * kLog2e;
       gc[m][c] = m == 0 ? gv : gc[m - 1][c] + gv;
     }
   }

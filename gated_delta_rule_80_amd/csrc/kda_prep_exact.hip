@@ -131,12 +131,20 @@ __global__ __launch_bounds__(kPrepThreads) void kda_chunk_prep_exact_kernel(Prep
   float yq[4][8], yk[4][8], yv[4][8], qk[4];
   front_compute<4, D, IO>(win, sm.filt, conv, ch, tf, p.T, active, p.l2 != 0, p.eps, p.scale, yq,
                           yk, yv, qk);
+  // raw projections -> decay and write strength (float32); zero past the end
+  const bool gact = p.A_log != nullptr;
+  float gbias[8], gneg = 0.f;
+  if (gact) {
+    load8(p.dt_bias + (size_t)h * D + ch, gbias);
+    gneg = -__expf(p.A_log[h]);
+  }
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     const bool ok = active && tf + m < p.T;
-    bt[m] = ok ? bt[m] : 0.f;
+    bt[m] = ok ? (p.beta_logits ? sigmoid(bt[m]) : bt[m]) : 0.f;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) gl[m][c] = ok ? gl[m][c] : 0.f;
+    for (int c = 0; c < 8; ++c)
+      gl[m][c] = ok ? (gact ? gate_decay(gl[m][c], gbias[c], gneg) : gl[m][c]) : 0.f;
   }
   // cumulative log-decay: within the segment, then across segments
 #pragma unroll

@@ -55,8 +55,12 @@ struct RecImage {
   static_assert(BYTES % 16 == 0, "record image is whole 16-byte chunks");
 };
 
-template <int D, int C, int VB, typename IO, typename E, int NT>
+// GN: apply the output stage (RMSNorm with gain over the head's D values, sigmoid
+// gate) before storing o.  Only with VB == D, where one workgroup holds every
+// value column of its tokens.
+template <int D, int C, int VB, typename IO, typename E, int NT, bool GN>
 __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void kda_chunk_state_kernel(StateParams p) {
+  static_assert(!GN || VB == D, "the output stage needs whole rows");
   constexpr int NW = NT / 64;  // waves
   constexpr int PE = 16 / (int)sizeof(E);
   constexpr int ES = (int)sizeof(E);
@@ -190,16 +194,91 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void kda_chunk_state_kernel(
   // chunk n + 2 is issued, so the stores retire while step n + 1 computes instead
   // of delaying the wait for the next copy.
   f32x4 pendO[NU];
+  // Output stage (GN): lane (r, g4) of a unit holds token 16 R + r and value rows
+  // 16 Vt + 4 g4 + e.  Each wave leaves its per-token sums of squares in ored;
+  // the waves of one t-tile are those with wave % RT == R.  The gate rows of
+  // chunk n are copied into buffer n % 2 of sgate at the start of step n, with
+  // the record copy of chunk n + 1 (the same wait covers both), and read at the
+  // store of chunk n in step n + 1.  A buffer holds [C][D] in 16-byte pieces,
+  // piece c of row t at c ^ (t % GRP) (conflict-free reads of 16 rows at one
+  // column).
+  constexpr int GRP = D * (int)sizeof(IO) / 16;  // 16-byte pieces per gate row
+  constexpr int GCH = C * GRP;                   // pieces per chunk
+  __shared__ float ored[GN ? NW * 16 : 1];
+  __shared__ __attribute__((aligned(16))) float onw[GN ? D : 1];  // norm gain (1 without norm)
+  __shared__ __attribute__((aligned(16))) char sgate[GN ? 2 * GCH * 16 : 16];
+  const bool has_norm = GN && p.o_norm_w != nullptr;
+  const bool has_gate = GN && p.o_gate != nullptr;
+  if constexpr (GN) {
+    // visible to every wave after the loop's first barrier
+    for (int c = tid; c < D; c += NT) onw[c] = has_norm ? p.o_norm_w[c] : 1.0f;
+  }
+  auto load_gate = [&](int nn) {
+    if constexpr (GN) {
+      if (!has_gate) return;
+      const char* src = static_cast<const char*>(p.o_gate) +
+                        (((size_t)b * p.T + (size_t)nn * C) * HD + (size_t)h * D) * sizeof(IO);
+#pragma unroll
+      for (int it = 0; it < (GCH + NT - 1) / NT; ++it) {
+        const int idx = it * NT + tid;
+        const int tt = idx / GRP, cs = idx % GRP;
+        // lanes of one wave fill 64 consecutive pieces from sgate + (it * NT + 64 * wave) * 16
+        if (idx < GCH && nn * C + tt < p.T)
+          __builtin_amdgcn_global_load_lds(
+              (const glb_void_t*)(src + (size_t)tt * HD * sizeof(IO) + (size_t)((cs ^ (tt % GRP)) * 16)),
+              (lds_void_t*)(sgate + (size_t)((nn & 1) * GCH + it * NT + 64 * wave) * 16), 16, 0, 0);
+      }
+    }
+  };
+  auto gate_at = [&](int nn, int tt, int v) {  // 4 gate values of chunk nn, row tt, columns v ..
+    const int piece = v * (int)sizeof(IO) / 16, off = v * (int)sizeof(IO) % 16;
+    Raw4<IO> gv;
+    gv.load(reinterpret_cast<const IO*>(sgate + ((nn & 1) * GCH + tt * GRP + (piece ^ (tt % GRP))) * 16 + off));
+    return gv;
+  };
+  auto row_sums = [&]() {
+    if constexpr (GN) {
+      float ss = 0.f;
+#pragma unroll
+      for (int i = 0; i < NU; ++i)
+        if (FULL_U || wave + NW * i < RT * VT)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ss = fmaf(pendO[i][e], pendO[i][e], ss);
+      ss += __shfl_xor(ss, 16, 64);
+      ss += __shfl_xor(ss, 32, 64);
+      if (g4 == 0) ored[wave * 16 + r] = ss;
+    }
+  };
   auto store_out = [&](int nn) {
+    float rs = 1.f;
+    if constexpr (GN) {
+      if (has_norm) {
+        float tot = 0.f;
+#pragma unroll
+        for (int w = R; w < NW; w += RT) tot += ored[w * 16 + r];
+        rs = 1.0f / sqrtf(tot * (1.0f / D) + p.o_norm_eps);
+      }
+    }
 #pragma unroll
     for (int i = 0; i < NU; ++i) {
       const int u = wave + NW * i;
       if (FULL_U || u < RT * VT) {
         const int Vt = u / RT;
         const int t = nn * C + 16 * R + r;
+        f32x4 ov = pendO[i];
+        if constexpr (GN) {
+          const f32x4 w = *reinterpret_cast<const f32x4*>(&onw[16 * Vt + 4 * g4]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ov[e] *= rs * w[e];
+          if (has_gate) {
+            const Raw4<IO> gv = gate_at(nn, 16 * R + r, 16 * Vt + 4 * g4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ov[e] *= sigmoid(gv[e]);
+          }
+        }
         if (t < p.T)
           store4(o + ((size_t)b * p.T + t) * HD + (size_t)h * D + vb0 + 16 * Vt + 4 * g4,
-                 pendO[i][0], pendO[i][1], pendO[i][2], pendO[i][3]);
+                 ov[0], ov[1], ov[2], ov[3]);
       }
     }
   };
@@ -232,6 +311,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void kda_chunk_state_kernel(
     }
     lds_barrier();  // every wave holds its fragments: the image may be overwritten
     if (n + 1 < p.NT) issue_copy(n + 1);
+    load_gate(n);  // buffer n % 2: chunk n - 2's, stored during step n - 1
     if (n > 0) store_out(n - 1);
     if (has_u) fp.mask_above(i_row, g4);
 
@@ -265,6 +345,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void kda_chunk_state_kernel(
         pendO[i] = accO[i];
       }
     }
+    row_sums();
     // ---- S = Diag(Lambda_C) S + Ktil^T U
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
@@ -280,6 +361,10 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void kda_chunk_state_kernel(
       }
     }
     stage_state();
+  }
+  if constexpr (GN) {
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's gate copies
+    lds_barrier();                  // the last chunk's row sums and gate rows
   }
   if (p.NT > 0) store_out(p.NT - 1);
   // ---- final state
@@ -298,58 +383,125 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void kda_chunk_state_kernel(
 }
 
 template <int D, int C, typename IO, typename E>
-static hipError_t launch_state_t(const StateParams& p, int vb, int threads, hipStream_t st) {
+static hipError_t launch_state_t(const StateParams& p, int vb, int threads, bool gn,
+                                 hipStream_t st) {
   // vb value columns per workgroup (32 or 64, or D when D < 64); 512 threads only
-  // with D = 128 and vb = 64
+  // with D = 128 and vb = 64.  gn (output stage in the walk) needs vb == D: 256
+  // threads, D <= 64.
   const size_t BH = (size_t)p.B * p.H;
   if constexpr (D == 128) {
-    if (vb == 64 && threads == 512) {
-      hipLaunchKernelGGL((kda_chunk_state_kernel<D, C, 64, IO, E, 512>), dim3((unsigned)(BH * 2)),
-                         dim3(512), 0, st, p);
+    if (!gn && vb == 64 && threads == 512) {
+      hipLaunchKernelGGL((kda_chunk_state_kernel<D, C, 64, IO, E, 512, false>),
+                         dim3((unsigned)(BH * 2)), dim3(512), 0, st, p);
       return hipGetLastError();
     }
   }
   if (threads != 256) return hipErrorInvalidValue;
+  if (gn) {
+    if constexpr (D <= 64) {
+      if (vb != D) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((kda_chunk_state_kernel<D, C, D, IO, E, 256, true>), dim3((unsigned)BH),
+                         dim3(256), 0, st, p);
+      return hipGetLastError();
+    }
+    return hipErrorInvalidValue;
+  }
   constexpr int VBmax = D >= 64 ? 64 : D;
   if (vb == 32 && D >= 32) {
     constexpr int VB = D >= 32 ? 32 : D;
-    hipLaunchKernelGGL((kda_chunk_state_kernel<D, C, VB, IO, E, 256>), dim3((unsigned)(BH * (D / VB))),
-                       dim3(256), 0, st, p);
+    hipLaunchKernelGGL((kda_chunk_state_kernel<D, C, VB, IO, E, 256, false>),
+                       dim3((unsigned)(BH * (D / VB))), dim3(256), 0, st, p);
   } else {
-    hipLaunchKernelGGL((kda_chunk_state_kernel<D, C, VBmax, IO, E, 256>),
+    hipLaunchKernelGGL((kda_chunk_state_kernel<D, C, VBmax, IO, E, 256, false>),
                        dim3((unsigned)(BH * (D / VBmax))), dim3(256), 0, st, p);
   }
   return hipGetLastError();
 }
 
 template <int D, typename IO, typename E>
-static hipError_t launch_state_c(const StateParams& p, int C, int vb, int threads, hipStream_t st) {
+static hipError_t launch_state_c(const StateParams& p, int C, int vb, int threads, bool gn,
+                                 hipStream_t st) {
   switch (C) {
-    case 16: return launch_state_t<D, 16, IO, E>(p, vb, threads, st);
-    case 32: return launch_state_t<D, 32, IO, E>(p, vb, threads, st);
+    case 16: return launch_state_t<D, 16, IO, E>(p, vb, threads, gn, st);
+    case 32: return launch_state_t<D, 32, IO, E>(p, vb, threads, gn, st);
     case 64:
       if constexpr (sizeof(E) == 4 && D == 128) return hipErrorInvalidValue;
-      else return launch_state_t<D, 64, IO, E>(p, vb, threads, st);
+      else return launch_state_t<D, 64, IO, E>(p, vb, threads, gn, st);
   }
   return hipErrorInvalidValue;
 }
 
 template <typename IO, typename E>
-static hipError_t launch_state_d(const StateParams& p, int D, int C, int vb, int threads,
+static hipError_t launch_state_d(const StateParams& p, int D, int C, int vb, int threads, bool gn,
                                  hipStream_t st) {
   switch (D) {
-    case 16: return launch_state_c<16, IO, E>(p, C, vb, threads, st);
-    case 32: return launch_state_c<32, IO, E>(p, C, vb, threads, st);
-    case 64: return launch_state_c<64, IO, E>(p, C, vb, threads, st);
-    case 128: return launch_state_c<128, IO, E>(p, C, vb, threads, st);
+    case 16: return launch_state_c<16, IO, E>(p, C, vb, threads, gn, st);
+    case 32: return launch_state_c<32, IO, E>(p, C, vb, threads, gn, st);
+    case 64: return launch_state_c<64, IO, E>(p, C, vb, threads, gn, st);
+    case 128: return launch_state_c<128, IO, E>(p, C, vb, threads, gn, st);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_state(const StateParams& p, int D, int C, bool fp32, int vb, int threads,
+hipError_t launch_state(const StateParams& p, int D, int C, bool fp32, int vb, int threads, bool gn,
                         hipStream_t st) {
-  return fp32 ? launch_state_d<float, float>(p, D, C, vb, threads, st)
-              : launch_state_d<__bf16, __bf16>(p, D, C, vb, threads, st);
+  return fp32 ? launch_state_d<float, float>(p, D, C, vb, threads, gn, st)
+              : launch_state_d<__bf16, __bf16>(p, D, C, vb, threads, gn, st);
+}
+
+// The output stage on its own, in place: one row of D values per (token, head),
+// D / 8 threads per row, each with 8 consecutive values.  Used when the state
+// walk splits a head's value columns over workgroups.
+template <int D, typename IO>
+__global__ __launch_bounds__(256) void kda_out_stage_kernel(OutStageParams p) {
+  constexpr int G = D / 8;      // threads per row
+  constexpr int RPW = 256 / G;  // rows per workgroup
+  const long row = (long)blockIdx.x * RPW + threadIdx.x / G;
+  const int j = threadIdx.x % G;
+  const bool ok = row < p.rows;
+  IO* o = static_cast<IO*>(p.o) + row * D + 8 * j;
+  float x[8], gt[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) x[c] = gt[c] = 0.f;
+  if (ok) {
+    load8(o, x);
+    if (p.o_gate != nullptr) load8(static_cast<const IO*>(p.o_gate) + row * D + 8 * j, gt);
+  }
+  if (p.o_norm_w != nullptr) {
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) ss = fmaf(x[c], x[c], ss);
+    ss = group_sum<G>(ss);
+    const float rs = 1.0f / sqrtf(ss * (1.0f / D) + p.o_norm_eps);
+    float w[8];
+    load8(p.o_norm_w + 8 * j, w);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) x[c] *= rs * w[c];
+  }
+  if (p.o_gate != nullptr) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) x[c] *= sigmoid(gt[c]);
+  }
+  if (ok) store8(o, x);
+}
+
+template <typename IO>
+static hipError_t launch_out_stage_t(const OutStageParams& p, int D, hipStream_t st) {
+  const long rpw = 256 / (D / 8);
+  const unsigned grid = (unsigned)((p.rows + rpw - 1) / rpw);
+  switch (D) {
+    case 16: hipLaunchKernelGGL((kda_out_stage_kernel<16, IO>), dim3(grid), dim3(256), 0, st, p); break;
+    case 32: hipLaunchKernelGGL((kda_out_stage_kernel<32, IO>), dim3(grid), dim3(256), 0, st, p); break;
+    case 64: hipLaunchKernelGGL((kda_out_stage_kernel<64, IO>), dim3(grid), dim3(256), 0, st, p); break;
+    case 128: hipLaunchKernelGGL((kda_out_stage_kernel<128, IO>), dim3(grid), dim3(256), 0, st, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_out_stage(const OutStageParams& p, int D, bool fp32, hipStream_t st) {
+  if (p.rows <= 0) return hipSuccess;
+  return fp32 ? launch_out_stage_t<float>(p, D, st) : launch_out_stage_t<__bf16>(p, D, st);
 }
 
 }  // namespace kda

@@ -18,6 +18,21 @@
  *      S_t = (I - beta_t k_t k_t^T) Diag(exp(g_t)) S_{t-1} + beta_t k_t v_t^T,
  *      o_t = scale * S_t^T q_t   (decay per key channel; the output reads S_t).
  *
+ * Optional stages around it, each off unless its pointers are given:
+ *   - decay and write strength from raw projections: g = -exp(A_log[h]) *
+ *     softplus(f + dt_bias[h*D + c]) with f the gate projection, evaluated in
+ *     float32 (A_log [num_heads] and dt_bias [H*D] are kept in float32 because
+ *     bf16 copies drift the decay over long contexts: "MaxText PR 5548", review
+ *     item 2; the softplus form is this library's reading, the pages give only
+ *     the parameters), and beta = sigmoid(b) with flag KDA_FLAG_BETA_LOGITS;
+ *   - the output RMSNorm of each head with the layer's o_norm gain ([head_dim],
+ *     float32: "MaxText PR 5548", review item 2; the norm as KimiRMSNorm:
+ *     "Kimi-K3 atlas -- MoE input (decode)"), then the sigmoid output gate of
+ *     the g_proj output (the gate form of "MaxText PR 5543", What, item 1):
+ *     o <- o / sqrt(mean_c o_c^2 + o_norm_eps) * o_norm_w * sigmoid(o_gate).
+ *     The gate_lower_bound of the released config is not applied (the pages do
+ *     not say how it enters).
+ *
  * Conventions for every entry point
  *   - Ownership: the caller owns every buffer.  The library never allocates or
  *     frees device memory and keeps no global mutable state (reentrant; any
@@ -35,7 +50,8 @@
  *     result (packed/variable-length batches, D outside {16,32,64,128},
  *     conv_k outside {0,4}, chunk outside {16,32,64}, fp32 I/O with D = 128 and
  *     chunk = 64).
- *   - Device values are not checked: g must be finite and <= 0, inputs finite.
+ *   - Device values are not checked: g must be finite and <= 0 (any finite value
+ *     when it holds a raw projection), inputs finite.
  *
  * Layouts (row-major, innermost last; dtype = `io` unless stated):
  *   q, k, v, g, o   [B][T][H][D]        (decode: [B][H][D])
@@ -54,7 +70,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 typedef enum kda_status {
   KDA_OK = 0,
@@ -76,6 +92,7 @@ typedef enum kda_dtype {
 
 /* flags */
 #define KDA_FLAG_L2NORM_QK (1u << 0) /* apply step 2 (the released model does) */
+#define KDA_FLAG_BETA_LOGITS (1u << 1) /* beta holds logits b; the write strength is sigmoid(b) */
 #define KDA_FLAGS_DEFAULT KDA_FLAG_L2NORM_QK
 
 /* ------------------------------------------------------------------ prefill */
@@ -105,6 +122,14 @@ typedef struct kda_prefill_args {
   void* o;              /* device [B][T][H][D] output; may not overlap any input */
   float* S_T;           /* device [B][H][D][D] final state; may equal S0 (in place) */
   void* conv_state_out; /* device [B][3][conv_k-1][H*D] or NULL; may equal conv_state_in */
+  /* optional stages (NULL = off) */
+  const float* A_log;   /* device [H] float32; given iff dt_bias is.  Then g holds the raw
+                           gate projection f and the decay is -exp(A_log[h]) softplus(f + dt_bias) */
+  const float* dt_bias; /* device [H*D] float32 */
+  const float* o_norm_w;/* device [D] float32 gain of the output RMSNorm (shared by the heads) */
+  float o_norm_eps;     /* >= 0, finite; read only with o_norm_w (1e-6 in the released model) */
+  const void* o_gate;   /* device [B][T][H][D] gate pre-activation: o <- o * sigmoid(o_gate),
+                           after the norm if both are given */
 } kda_prefill_args;
 
 /* Host-only check of every argument; returns the first error found. */
@@ -121,13 +146,19 @@ kda_status kda_prefill(const kda_prefill_args* a, void* ws, size_t ws_bytes, voi
 
 /* The stages kda_prefill enqueues, one at a time, for profiling:
  *   0 = chunk preparation (conv + SiLU + L2, cumulative decay, intra-chunk
- *       products, triangular solve; writes the workspace),
- *   1 = state walk over chunks with the output (reads the workspace; writes o, S_T),
- *   2 = conv-state hand-over (writes conv_state_out).
- * Running 0, 1, 2 in order on one stream is exactly kda_prefill (T > 0). */
+ *       products, triangular solve, and the activation of raw projections;
+ *       writes the workspace),
+ *   1 = state walk over chunks with the output (reads the workspace; writes o, S_T;
+ *       applies the output norm and gate itself when one workgroup holds a
+ *       head's whole output row),
+ *   2 = conv-state hand-over (writes conv_state_out),
+ *   3 = the output norm and gate as a separate in-place pass over o, when stage 1
+ *       did not apply them (nothing otherwise).
+ * Running 0, 1, 2, 3 in order on one stream is exactly kda_prefill (T > 0). */
 #define KDA_STAGE_PREP 0
 #define KDA_STAGE_STATE 1
 #define KDA_STAGE_CONV_TAIL 2
+#define KDA_STAGE_OUTPUT 3
 kda_status kda_prefill_stage(const kda_prefill_args* a, void* ws, size_t ws_bytes, int stage,
                              void* stream);
 
@@ -175,6 +206,12 @@ typedef struct kda_decode_args {
   void* conv_state;     /* device [B][3][conv_k-1][H*D] in/out; required iff conv_k > 0 */
   float* S;             /* device [B][H][D][D] in/out, updated in place */
   void* o;              /* device [B][H][D]; may not overlap any input */
+  /* optional stages, as in kda_prefill_args */
+  const float* A_log;   /* device [H] float32; given iff dt_bias is (g then holds f) */
+  const float* dt_bias; /* device [H*D] float32 */
+  const float* o_norm_w;/* device [D] float32 or NULL */
+  float o_norm_eps;
+  const void* o_gate;   /* device [B][H][D] or NULL */
 } kda_decode_args;
 
 kda_status kda_validate_decode(const kda_decode_args* a);

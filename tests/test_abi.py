@@ -24,7 +24,7 @@ def test_exports_every_declared_symbol(lib):
             "kda_validate_conv_norm", "kda_status_str", "kda_abi_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.kda_abi_version() == 1
+    assert lib.kda_abi_version() == 2
     for s in range(10):
         assert kda.kda_status_str(s) and kda.kda_status_str(s) != "unknown status"
 
@@ -97,7 +97,7 @@ def test_prefill_valid_and_workspace(lib):
     ("io", 7, DTYPE),
     ("B", 0, SHAPE), ("H", 0, SHAPE), ("T", -1, SHAPE), ("D", 0, SHAPE), ("chunk", 0, SHAPE),
     ("D", 96, UNSUP), ("D", 256, UNSUP), ("chunk", 48, UNSUP), ("chunk", 128, UNSUP),
-    ("conv_k", 3, UNSUP), ("flags", 2, VALUE), ("l2_eps", -1.0, VALUE),
+    ("conv_k", 3, UNSUP), ("flags", 4, VALUE), ("flags", 1 << 31, VALUE), ("l2_eps", -1.0, VALUE),
     ("l2_eps", float("nan"), VALUE), ("scale", float("inf"), VALUE),
     ("q", None, NULL), ("k", None, NULL), ("v", None, NULL), ("g", None, NULL),
     ("beta", None, NULL), ("o", None, NULL), ("S_T", None, NULL), ("conv_w", None, NULL),
@@ -168,7 +168,9 @@ def test_prefill_workspace_errors(lib):
     # workspace overlapping an output
     assert lib.kda_prefill(ctypes.byref(a), ctypes.c_void_p(a.o), need, None) == ALIAS
     # invalid stage number
-    assert lib.kda_prefill_stage(ctypes.byref(a), ctypes.c_void_p(0x100000000000), need, 3,
+    assert lib.kda_prefill_stage(ctypes.byref(a), ctypes.c_void_p(0x100000000000), need, 4,
+                                 None) == VALUE
+    assert lib.kda_prefill_stage(ctypes.byref(a), ctypes.c_void_p(0x100000000000), need, -1,
                                  None) == VALUE
     # invalid args are reported before the workspace
     b = prefill(io=9)
@@ -236,3 +238,59 @@ def test_errors_before_launch_never_touch_hip(lib):
 def test_binding_raises_without_library(tmp_path):
     with pytest.raises(RuntimeError, match="missing"):
         _lib.load(str(tmp_path / "nope.so"))
+
+
+# ------------------------------------------------------------ optional stages
+def stages(make, **kw):
+    """Valid args with every optional stage on (fake, disjoint buffers)."""
+    f = Fake()
+    f.next = 0x7E0000000000
+    a = make()
+    a.flags = 1 | 2  # L2 norm + beta logits
+    a.A_log, a.dt_bias, a.o_norm_w, a.o_gate = f(), f(), f(), f()
+    a.o_norm_eps = 1e-6
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("make,validate", [(prefill, kda.kda_validate_prefill),
+                                           (decode, kda.kda_validate_decode)])
+def test_stage_arguments(lib, make, validate):
+    assert validate(stages(make)) == OK
+    # each stage alone
+    assert validate(stages(make, A_log=None, dt_bias=None)) == OK
+    assert validate(stages(make, o_norm_w=None)) == OK
+    assert validate(stages(make, o_gate=None)) == OK
+    assert validate(stages(make, flags=1)) == OK
+    # A_log and dt_bias come together
+    assert validate(stages(make, A_log=None)) == NULL
+    assert validate(stages(make, dt_bias=None)) == NULL
+    # eps of the output norm is checked only when the norm is on
+    assert validate(stages(make, o_norm_eps=float("nan"))) == VALUE
+    assert validate(stages(make, o_norm_eps=-1.0)) == VALUE
+    assert validate(stages(make, o_norm_eps=float("nan"), o_norm_w=None)) == OK
+    for field in ("A_log", "dt_bias", "o_norm_w", "o_gate"):
+        a = stages(make)
+        setattr(a, field, getattr(a, field) + 4)
+        assert validate(a) == ALIGN, field
+    # the output may not overlap a stage input, nor may the state
+    for field in ("A_log", "dt_bias", "o_norm_w", "o_gate"):
+        a = stages(make)
+        setattr(a, field, a.o)
+        assert validate(a) == ALIAS, field
+    a = stages(make)
+    a.o_gate = a.S_T if make is prefill else a.S
+    assert validate(a) == ALIAS
+
+
+def test_stage_struct_layout_matches_header():
+    """The ctypes structs end with the optional-stage fields in header order."""
+    text = open(_lib.HEADER_PATH).read()
+    for struct, cls in (("kda_prefill_args", _lib.PrefillArgs), ("kda_decode_args", _lib.DecodeArgs)):
+        body = text[text.index("typedef struct " + struct):]
+        body = body[:body.index("} " + struct)]
+        import re
+        body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+        names = re.findall(r"\b([A-Za-z_][A-Za-z0-9_]*)\s*[,;]", body)
+        assert [n for n, _ in cls._fields_] == names, struct

@@ -126,7 +126,7 @@ def test_stages_compose_to_prefill():
     a = kda.prefill_args(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["conv_w"],
                          inp["conv_state"], inp["S0"], o2, S2, t2, chunk=64)
     ws = torch.empty(kda.kda_prefill_workspace_bytes(a), dtype=torch.uint8, device="cuda")
-    for stage in (0, 1, 2):
+    for stage in (0, 1, 2, 3):
         kda.kda_prefill_stage(a, ws, stage)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(S1, S2) and torch.equal(t1, t2)
