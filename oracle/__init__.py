@@ -14,6 +14,7 @@ from .kda_oracle import (  # noqa: F401
     kda_reference,
     kda_reference_decode_step,
     kda_reference_heads,
+    kda_reference_packed,
     l2_normalize,
     output_gate_norm,
     rms_norm,

@@ -319,6 +319,49 @@ def conv_norm_reference(q, k, v, conv_w, conv_state=None, l2norm_qk=True, eps=L2
     return qh, kh, vh, tails
 
 
+def kda_reference_packed(q, k, v, g, beta, cu_seqlens, conv_w=None, conv_state=None, S0=None,
+                         **kw):
+    """The mixer over packed sequences: sequence i is tokens [cu_seqlens[i],
+    cu_seqlens[i+1]) of a single row of tokens, with its own conv history and
+    initial state; nothing crosses a boundary.
+
+    ("MaxText PR 5550" rejects packed batches for KDA because its layer ignores
+    segment ids, i.e. would let state and conv history flow from one sequence
+    into the next; "Kimi-K3 model atlas -- self.layers", transformer excerpt:
+    the model hands a padding mask to its KDA layers.)
+
+    q, k, v, g: [1, T, H, D]; beta [1, T, H]; cu_seqlens: N + 1 non-decreasing
+    offsets from 0 to T; conv_state [N, 3, K-1, H*D] or None; S0 [N, H, D, D] or
+    None.  Other keyword arguments as ``kda_reference`` (o_gate is [1, T, H, D]).
+    Returns (o [1, T, H, D], S_T [N, H, D, D], tail [N, 3, K-1, H*D] or None).
+    """
+    cu = [int(c) for c in cu_seqlens]
+    N = len(cu) - 1
+    if cu[0] != 0 or cu[-1] != np.asarray(q).shape[1] or any(b < a for a, b in zip(cu, cu[1:])):
+        raise ValueError("cu_seqlens must run from 0 to T without decreasing")
+    B, T, H, D = np.asarray(q).shape
+    if B != 1:
+        raise ValueError("packed sequences share one row of tokens (B = 1)")
+    o = np.zeros((1, T, H, D))
+    S_out = np.zeros((N, H, D, D))
+    tails = None if conv_w is None else np.zeros((N, 3, np.asarray(conv_w).shape[2] - 1, H * D))
+    o_gate = kw.pop("o_gate", None)
+    for i in range(N):
+        a, e = cu[i], cu[i + 1]
+        sl = slice(a, e)
+        cs = None if conv_state is None else np.asarray(conv_state)[i:i + 1]
+        s0 = None if S0 is None else np.asarray(S0)[i:i + 1]
+        og = None if o_gate is None else np.asarray(o_gate)[:, sl]
+        oi, Si, ti = kda_reference(np.asarray(q)[:, sl], np.asarray(k)[:, sl], np.asarray(v)[:, sl],
+                                   np.asarray(g)[:, sl], np.asarray(beta)[:, sl], conv_w=conv_w,
+                                   conv_state=cs, S0=s0, o_gate=og, **kw)
+        o[:, sl] = oi
+        S_out[i] = Si[0]
+        if tails is not None:
+            tails[i] = ti[0]
+    return o, S_out, tails
+
+
 def kda_reference_heads(q, k, v, g, beta, heads, conv_w=None, conv_state=None, S0=None,
                         scale=1.0, l2norm_qk=True, eps=L2_EPS, o_norm_w=None, o_gate=None,
                         o_norm_eps=RMS_EPS, A_log=None, dt_bias=None, beta_sigmoid=False):

@@ -15,7 +15,8 @@ import pytest
 from scipy.special import expit
 
 from oracle import (conv_norm_reference, conv_tail, gated_delta_step, kda_reference,
-                    kda_reference_decode_step, kda_reference_heads, l2_normalize,
+                    kda_reference_decode_step, kda_reference_heads, kda_reference_packed,
+                    l2_normalize,
                     kda_gate, output_gate_norm, rms_norm, short_conv, sigmoid, silu,
                     softplus)
 from chunked_form import chunk_quantities, chunked_head
@@ -503,3 +504,68 @@ def test_raw_projection_inputs_in_the_mixer():
                                         conv_w=conv_w, S0=S0)
     np.testing.assert_allclose(od, o_first[:, 0], rtol=1e-13, atol=1e-14)
     np.testing.assert_allclose(Sd, S_first, rtol=1e-13, atol=1e-14)
+
+
+# ------------------------------------------------------------- packed sequences
+def test_packed_equals_reset_in_one_sequence():
+    """Packing pinned through the alpha = 0 reset (P4): sequences A and B packed
+    give, for B, what one sequence A + B gives when B's first token has g = -1000
+    (the state forgets A) and A ends in three zero raw rows (the conv window of
+    B's first tokens then sees zeros, B's own empty history)."""
+    rng = np.random.default_rng(10)
+    La, Lb, H, D = 9, 7, 2, 4
+    q, k, v, g, beta, conv_w, _ = rand_case(rng, B=1, T=La + Lb, H=H, D=D)
+    for x in (q, k, v):
+        x[:, La - 3:La] = 0.0
+    S0a = 0.1 * rng.standard_normal((1, H, D, D))
+    g_one = g.copy()
+    g_one[:, La] = -1000.0
+    o_one, S_one, _ = kda_reference(q, k, v, g_one, beta, conv_w=conv_w, S0=S0a)
+    S0 = np.concatenate([S0a, np.zeros((1, H, D, D))])
+    o_pk, S_pk, tails = kda_reference_packed(q, k, v, g, beta, [0, La, La + Lb], conv_w=conv_w, S0=S0)
+    np.testing.assert_allclose(o_pk, o_one, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(S_pk[1], S_one[0], rtol=1e-12, atol=1e-13)
+    # the tail of each sequence is its own last three raw rows
+    HD = H * D
+    np.testing.assert_array_equal(tails[1, 0], q[0, La + Lb - 3:].reshape(3, HD))
+    np.testing.assert_array_equal(tails[0, 2], v[0, La - 3:La].reshape(3, HD))
+
+
+def test_packed_empty_and_short_sequences():
+    """Empty sequences hand their state and conv history through unchanged; a
+    sequence shorter than the conv window mixes its history into the tail."""
+    rng = np.random.default_rng(11)
+    cu = [0, 0, 5, 5, 6, 6, 8]
+    N, H, D = len(cu) - 1, 2, 4
+    q, k, v, g, beta, conv_w, _ = rand_case(rng, B=1, T=cu[-1], H=H, D=D)
+    S0 = rng.standard_normal((N, H, D, D))
+    cs = rng.standard_normal((N, 3, 3, H * D))
+    o, S, tails = kda_reference_packed(q, k, v, g, beta, cu, conv_w=conv_w, conv_state=cs, S0=S0)
+    for i in (0, 2, 4):
+        np.testing.assert_array_equal(S[i], S0[i])
+        np.testing.assert_array_equal(tails[i], cs[i])
+    # sequence 3 has one token: its tail is the last two history rows, then that token
+    np.testing.assert_array_equal(tails[3, 1, :2], cs[3, 1, 1:])
+    np.testing.assert_array_equal(tails[3, 1, 2], k[0, 5].reshape(H * D))
+
+
+def test_packed_equal_lengths_match_batch():
+    rng = np.random.default_rng(12)
+    B, L, H, D = 3, 6, 2, 4
+    q, k, v, g, beta, conv_w, S0 = rand_case(rng, B=B, T=L, H=H, D=D)
+    cs = rng.standard_normal((B, 3, 3, H * D))
+    ob, Sb, tb = kda_reference(q, k, v, g, beta, conv_w=conv_w, conv_state=cs, S0=S0)
+    flat = lambda x: x.reshape(1, B * L, *x.shape[2:])
+    op, Sp, tp = kda_reference_packed(flat(q), flat(k), flat(v), flat(g), flat(beta),
+                                      [0, L, 2 * L, 3 * L], conv_w=conv_w, conv_state=cs, S0=S0)
+    np.testing.assert_allclose(op, flat(ob), rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(Sp, Sb, rtol=1e-13, atol=1e-14)
+    np.testing.assert_array_equal(tp, tb)
+
+
+def test_packed_rejects_bad_offsets():
+    rng = np.random.default_rng(13)
+    q, k, v, g, beta, _, _ = rand_case(rng, B=1, T=5, H=1, D=4)
+    for cu in ([0, 3, 2, 5], [1, 5], [0, 4], [0, 6]):
+        with pytest.raises(ValueError):
+            kda_reference_packed(q, k, v, g, beta, cu)
