@@ -6,8 +6,9 @@ A step is one kda_prefill over the workload (conv + SiLU + L2, chunk preparation
 state walk with output, conv-state hand-over), inputs resident in HBM.  The
 decode step (B=256 sequences, in-place state) is timed in the same run and
 reported beside it.  A second leg ("stages") times the same prefill and decode
-steps with the optional stages on: decay and write strength from raw
-projections, output RMSNorm and sigmoid gate.  Prints one JSON line.
+steps with the optional stages on (decay and write strength from raw
+projections, output RMSNorm and sigmoid gate) and the prefill's tokens packed as
+sequences of mixed length.  Prints one JSON line.
 
 Roofline figures use algorithmic bytes (each tensor the kernel must read or
 write, once) divided by the kernel's mean duration from HIP events recorded on
@@ -263,6 +264,35 @@ def stages_leg(kda, torch, w, wd, args, stream, dev, plain_ms, plain_dms):
             "prefill": prefill, "decode": decode}
 
 
+# The 4096 tokens of the 4k workload as 8 packed sequences of mixed length.
+PACKED_LENGTHS = [1024, 512, 700, 300, 1000, 60, 400, 100]
+
+
+def packed_leg(kda, torch, w, args, stream, dev, plain_ms):
+    """Prefill over the same number of tokens packed as sequences of mixed length."""
+    from kda_inputs import make_packed_inputs
+    lengths = PACKED_LENGTHS if sum(PACKED_LENGTHS) == w.B * w.T else [w.T] * w.B
+    inp = make_packed_inputs(w, lengths, seed=args.seed, device=dev)
+    N = len(lengths)
+    o = torch.empty_like(inp["q"])
+    S_T = torch.empty(N, w.H, w.D, w.D, dtype=torch.float32, device=dev)
+    cso = torch.empty(N, 3, 3, w.H * w.D, dtype=inp["q"].dtype, device=dev)
+    a = kda.prefill_args(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["conv_w"],
+                         inp["conv_state"], inp["S0"], o, S_T, cso, chunk=w.chunk,
+                         cu_seqlens=inp["cu_seqlens"])
+    ws = torch.empty(kda.kda_prefill_workspace_bytes(a), dtype=torch.uint8, device=dev)
+    ms, stage_ms = time_prefill(kda, torch, a, ws, stream, args.steps, args.warmup)
+    tokens = sum(lengths)
+    nb = prefill_bytes(w)["path"]
+    out = {"workload": f"{w.name} packed as {N} sequences", "lengths": lengths, "ms_per_step": ms,
+           "tokens_per_s": tokens / (ms / 1e3), "ms_vs_unpacked": ms - plain_ms,
+           "stage_ms": {STAGE_NAMES[i]: stage_ms[i] for i in range(len(STAGE_NAMES))},
+           "path_hbm_frac": nb / (ms / 1e3) / HBM_PEAK}
+    del ws, inp, o, S_T, cso
+    torch.cuda.empty_cache()
+    return out
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -273,7 +303,8 @@ def main(argv=None) -> int:
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing (0 = skip)")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-stages", action="store_true",
-                    help="skip the leg with the optional stages (raw projections, output norm + gate)")
+                    help="skip the legs with the optional stages (raw projections, output norm + "
+                         "gate) and with packed sequences")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run the library's plain state-copy kernel (kda_prefill with T=0) "
                          "on this many MiB, to calibrate HBM byte counters")
@@ -354,6 +385,7 @@ def main(argv=None) -> int:
     stages = None
     if not args.no_stages:
         stages = stages_leg(kda, torch, w, wd, args, stream, dev, plain_ms, dms)
+        stages["packed"] = packed_leg(kda, torch, w, args, stream, dev, plain_ms)
 
     if args.calib_copy_mib > 0:
         # kda_prefill with T = 0 copies S0 to S_T with one plain copy kernel

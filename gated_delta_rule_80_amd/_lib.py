@@ -42,7 +42,7 @@ class PrefillArgs(ctypes.Structure):
                 ("conv_state_in", _vp), ("S0", _vp), ("o", _vp), ("S_T", _vp),
                 ("conv_state_out", _vp),
                 ("A_log", _vp), ("dt_bias", _vp), ("o_norm_w", _vp), ("o_norm_eps", ctypes.c_float),
-                ("o_gate", _vp)]
+                ("o_gate", _vp), ("cu_seqlens", _vp), ("n_seqs", ctypes.c_int32)]
 
 
 class ConvNormArgs(ctypes.Structure):
@@ -176,7 +176,8 @@ def _stages(a, A_log, dt_bias, o_norm_w, o_norm_eps, o_gate):
 def prefill_args(q, k, v, g, beta, conv_w=None, conv_state_in=None, S0=None, o=None, S_T=None,
                  conv_state_out=None, *, chunk=64, scale=1.0, l2norm_qk=True, eps=1e-6,
                  conv_k=None, B=None, T=None, H=None, D=None, io=None, A_log=None, dt_bias=None,
-                 beta_logits=False, o_norm_w=None, o_norm_eps=1e-6, o_gate=None) -> PrefillArgs:
+                 beta_logits=False, o_norm_w=None, o_norm_eps=1e-6, o_gate=None,
+                 cu_seqlens=None) -> PrefillArgs:
     """Fill kda_prefill_args from tensors (shapes from q unless given explicitly)."""
     a = PrefillArgs()
     if q is not None and not isinstance(q, int):
@@ -197,6 +198,11 @@ def prefill_args(q, k, v, g, beta, conv_w=None, conv_state_in=None, S0=None, o=N
     a.conv_w, a.conv_state_in, a.S0 = _ptr(conv_w), _ptr(conv_state_in), _ptr(S0)
     a.o, a.S_T, a.conv_state_out = _ptr(o), _ptr(S_T), _ptr(conv_state_out)
     _stages(a, A_log, dt_bias, o_norm_w, o_norm_eps, o_gate)
+    if cu_seqlens is not None:
+        if cu_seqlens.dtype != torch.int32:
+            raise TypeError("cu_seqlens must be int32")
+        a.cu_seqlens = _ptr(cu_seqlens)
+        a.n_seqs = cu_seqlens.numel() - 1
     return a
 
 
@@ -220,7 +226,7 @@ def _workspace(args: PrefillArgs, device, workspace=None):
 def kda_prefill(q, k, v, g, beta, conv_w=None, conv_state=None, S0=None, *, chunk=64, scale=1.0,
                 l2norm_qk=True, eps=1e-6, o=None, S_T=None, conv_state_out=None, workspace=None,
                 stream=None, A_log=None, dt_bias=None, beta_logits=False, o_norm_w=None,
-                o_norm_eps=1e-6, o_gate=None):
+                o_norm_eps=1e-6, o_gate=None, cu_seqlens=None):
     """Whole-sequence KDA forward.  Returns (o, S_T, conv_state_out).
 
     q, k, v, g: [B, T, H, D] (bf16 or fp32, same dtype); beta [B, T, H];
@@ -229,19 +235,22 @@ def kda_prefill(q, k, v, g, beta, conv_w=None, conv_state=None, S0=None, *, chun
     Optional stages: A_log [H] and dt_bias [H*D] fp32 (g then holds the raw gate
     projection), beta_logits (beta holds logits), o_norm_w [D] fp32 and o_gate
     [B, T, H, D] for the output RMSNorm and sigmoid gate.
+    Packed sequences: cu_seqlens int32 [N + 1] on the device with B = 1; then S0,
+    S_T are [N, H, D, D] and the conv states [N, 3, 3, H*D].
     """
     B, T, H, D = q.shape
     dev = q.device
+    NS = B if cu_seqlens is None else cu_seqlens.numel() - 1
     if o is None:
         o = torch.empty_like(q)
     if S_T is None:
-        S_T = torch.empty(B, H, D, D, dtype=torch.float32, device=dev)
+        S_T = torch.empty(NS, H, D, D, dtype=torch.float32, device=dev)
     if conv_state_out is None and conv_w is not None:
-        conv_state_out = torch.empty(B, 3, 3, H * D, dtype=q.dtype, device=dev)
+        conv_state_out = torch.empty(NS, 3, 3, H * D, dtype=q.dtype, device=dev)
     a = prefill_args(q, k, v, g, beta, conv_w, conv_state, S0, o, S_T, conv_state_out, chunk=chunk,
                      scale=scale, l2norm_qk=l2norm_qk, eps=eps, A_log=A_log, dt_bias=dt_bias,
                      beta_logits=beta_logits, o_norm_w=o_norm_w, o_norm_eps=o_norm_eps,
-                     o_gate=o_gate)
+                     o_gate=o_gate, cu_seqlens=cu_seqlens)
     _check(kda_validate_prefill(a), "kda_prefill")
     ws, need = _workspace(a, dev, workspace)
     _check(load().kda_prefill(ctypes.byref(a), _ptr(ws) if ws is not None else None, need if

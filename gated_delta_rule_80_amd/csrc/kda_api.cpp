@@ -53,32 +53,44 @@ struct PrefillSizes {
   size_t state;  // bytes of S0 / S_T
   size_t cw;     // bytes of conv_w
   size_t cst;    // bytes of a conv state
-  int NT;
+  size_t cu;     // bytes of cu_seqlens
+  int NS;        // sequences: B, or n_seqs when packed
+  int NT;        // chunk slots per (sequence, head), or per head when packed
 };
+
+bool packed(const kda_prefill_args* a) { return a->cu_seqlens != nullptr; }
 
 kda_status prefill_sizes(const kda_prefill_args* a, PrefillSizes& s) {
   const size_t es = esize(a->io);
+  s.NS = packed(a) ? a->n_seqs : a->B;
   size_t tok;
   if (!mul_ok(tok, {(size_t)a->B, (size_t)a->T})) return KDA_ERR_SHAPE;
   if (!mul_ok(s.x, {tok, (size_t)a->H, (size_t)a->D, es})) return KDA_ERR_SHAPE;
   if (!mul_ok(s.bta, {tok, (size_t)a->H, es})) return KDA_ERR_SHAPE;
-  if (!mul_ok(s.state, {(size_t)a->B, (size_t)a->H, (size_t)a->D, (size_t)a->D, 4})) return KDA_ERR_SHAPE;
+  if (!mul_ok(s.state, {(size_t)s.NS, (size_t)a->H, (size_t)a->D, (size_t)a->D, 4})) return KDA_ERR_SHAPE;
   const size_t ck = a->conv_k > 0 ? (size_t)a->conv_k : 0;
   if (!mul_ok(s.cw, {3, (size_t)a->H, (size_t)a->D, ck, 4})) return KDA_ERR_SHAPE;
-  if (!mul_ok(s.cst, {(size_t)a->B, 3, ck > 0 ? ck - 1 : 0, (size_t)a->H, (size_t)a->D, es}))
+  if (!mul_ok(s.cst, {(size_t)s.NS, 3, ck > 0 ? ck - 1 : 0, (size_t)a->H, (size_t)a->D, es}))
     return KDA_ERR_SHAPE;
-  s.NT = a->chunk > 0 ? (a->T + a->chunk - 1) / a->chunk : 0;
-  // one workgroup per (b, h, chunk) must fit a 1-D grid
+  s.cu = packed(a) ? ((size_t)a->n_seqs + 1) * 4 : 0;
+  const long nt = a->chunk > 0 ? ((long)a->T + a->chunk - 1) / a->chunk : 0;
+  // packed: every sequence wastes at most one partly filled chunk
+  const long slots = packed(a) ? nt + a->n_seqs : nt;
+  if (slots > 0x7fffffffL) return KDA_ERR_SHAPE;
+  s.NT = (int)slots;
+  // one workgroup per (b, h, chunk) and per state walk must fit a 1-D grid
   size_t wgs;
   if (!mul_ok(wgs, {(size_t)a->B, (size_t)a->H, (size_t)(s.NT > 0 ? s.NT : 1)}) ||
-      wgs > 0x7fffffffu)
+      wgs > 0x7fffffffu || (size_t)s.NS * a->H * 4 > 0x7fffffffu)
     return KDA_ERR_SHAPE;
   return KDA_OK;
 }
 
 kda::WorkspaceLayout ws_layout(const kda_prefill_args* a) {
-  const size_t NT = (size_t)((a->T + a->chunk - 1) / a->chunk);
-  return kda::workspace_layout((size_t)a->B * a->H * NT, a->chunk, a->D, esize(a->io));
+  PrefillSizes s;
+  prefill_sizes(a, s);
+  return kda::workspace_layout((size_t)a->B * a->H * s.NT, a->chunk, a->D, esize(a->io),
+                               packed(a) ? (size_t)a->n_seqs : 0);
 }
 
 // Value columns per state-walk workgroup and its thread count.  Every workgroup
@@ -153,13 +165,15 @@ kda_status kda_validate_prefill(const kda_prefill_args* a) {
   if (kda_status e = validate_stages(a->A_log, a->dt_bias, a->o_norm_w, a->o_norm_eps, a->o_gate);
       e != KDA_OK)
     return e;
+  if (packed(a) ? (a->B != 1 || a->n_seqs < 1) : a->n_seqs != 0) return KDA_ERR_SHAPE;
   const bool need_x = a->T > 0;
   if (need_x && (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->o)) return KDA_ERR_NULL;
   if (!a->S_T) return KDA_ERR_NULL;
   if (a->conv_k > 0 && !a->conv_w) return KDA_ERR_NULL;
   if (a->conv_k == 0 && (a->conv_w || a->conv_state_in || a->conv_state_out)) return KDA_ERR_NULL;
   for (const void* p : std::initializer_list<const void*>{a->q, a->k, a->v, a->g, a->beta, (const void*)a->conv_w, a->conv_state_in,
-                        (const void*)a->S0, a->o, (const void*)a->S_T, (const void*)a->conv_state_out})
+                        (const void*)a->S0, a->o, (const void*)a->S_T, (const void*)a->conv_state_out,
+                        (const void*)a->cu_seqlens})
     if (p && !aligned16(p)) return KDA_ERR_ALIGN;
   const Span q = span(a->q, s.x), k = span(a->k, s.x), v = span(a->v, s.x), g = span(a->g, s.x);
   const Span bt = span(a->beta, s.bta), cw = span(a->conv_w, s.cw);
@@ -167,12 +181,13 @@ kda_status kda_validate_prefill(const kda_prefill_args* a) {
   const Span s0 = span(a->S0, s.state), st = span(a->S_T, s.state), o = span(a->o, s.x);
   const Span al = span(a->A_log, (size_t)a->H * 4), db = span(a->dt_bias, (size_t)a->H * a->D * 4);
   const Span nw = span(a->o_norm_w, (size_t)a->D * 4), og = span(a->o_gate, s.x);
-  for (Span in : {q, k, v, g, bt, cw, ci, s0, st, co, al, db, nw, og})
+  const Span cu = span(a->cu_seqlens, s.cu);
+  for (Span in : {q, k, v, g, bt, cw, ci, s0, st, co, al, db, nw, og, cu})
     if (overlaps(o, in)) return KDA_ERR_ALIAS;
-  for (Span in : {q, k, v, g, bt, cw, ci, co, al, db, nw, og})
+  for (Span in : {q, k, v, g, bt, cw, ci, co, al, db, nw, og, cu})
     if (overlaps(st, in)) return KDA_ERR_ALIAS;
   if (!same_or_disjoint(st, s0)) return KDA_ERR_ALIAS;
-  for (Span in : {q, k, v, g, bt, cw, s0, al, db, nw, og})
+  for (Span in : {q, k, v, g, bt, cw, s0, al, db, nw, og, cu})
     if (overlaps(co, in)) return KDA_ERR_ALIAS;
   if (!same_or_disjoint(co, ci)) return KDA_ERR_ALIAS;
   return KDA_OK;
@@ -181,10 +196,11 @@ kda_status kda_validate_prefill(const kda_prefill_args* a) {
 size_t kda_prefill_workspace_bytes(const kda_prefill_args* a) {
   if (kda_validate_prefill(a) != KDA_OK) return 0;
   if (a->T == 0) return 0;
-  const int NT = (a->T + a->chunk - 1) / a->chunk;
+  PrefillSizes s;
+  prefill_sizes(a, s);
   size_t n;
   const size_t rec = record_layout(a->chunk, a->D, esize(a->io)).bytes;
-  if (!mul_ok(n, {(size_t)a->B, (size_t)a->H, (size_t)NT, rec})) return 0;
+  if (!mul_ok(n, {(size_t)a->B, (size_t)a->H, (size_t)s.NT, rec})) return 0;
   return ws_layout(a).bytes;
 }
 
@@ -201,17 +217,41 @@ static kda_status check_workspace(const kda_prefill_args* a, void* ws, size_t ws
                  span(a->S0, s.state), span(a->o, s.x), span(a->S_T, s.state),
                  span(a->conv_state_out, s.cst), span(a->A_log, (size_t)a->H * 4),
                  span(a->dt_bias, (size_t)a->H * a->D * 4), span(a->o_norm_w, (size_t)a->D * 4),
-                 span(a->o_gate, s.x)})
+                 span(a->o_gate, s.x), span(a->cu_seqlens, s.cu)})
     if (overlaps(w, x)) return KDA_ERR_ALIAS;
   return KDA_OK;
 }
 
+// The packed-sequence tables in the workspace (written by the first stage).
+static kda::SeqTables seq_tables(const kda_prefill_args* a, void* ws) {
+  kda::SeqTables t{};
+  if (!packed(a) || a->T == 0) return t;
+  int* bounds = reinterpret_cast<int*>(static_cast<char*>(ws) + ws_layout(a).seq);
+  t.bounds = bounds;
+  t.cstart = bounds + a->n_seqs + 1;
+  t.n_seqs = a->n_seqs;
+  return t;
+}
+
 static kda_status run_stage(const kda_prefill_args* a, void* ws, int stage, hipStream_t st) {
   const bool fp32 = a->io == KDA_FP32;
-  const int NT = (a->T + a->chunk - 1) / a->chunk;
+  PrefillSizes sz;
+  prefill_sizes(a, sz);
+  const int NT = sz.NT;
+  const kda::SeqTables seqs = seq_tables(a, ws);
   switch (stage) {
     case KDA_STAGE_PREP: {
       if (a->T == 0) return KDA_OK;
+      if (packed(a)) {
+        kda::IndexParams ip{};
+        ip.cu_seqlens = a->cu_seqlens;
+        ip.bounds = const_cast<int*>(seqs.bounds);
+        ip.cstart = const_cast<int*>(seqs.cstart);
+        ip.n_seqs = a->n_seqs;
+        ip.T = a->T;
+        ip.C = a->chunk;
+        if (kda_status e = hip_status(kda::launch_seq_index(ip, st)); e != KDA_OK) return e;
+      }
       kda::PrepParams p{};
       p.q = a->q; p.k = a->k; p.v = a->v; p.g = a->g; p.beta = a->beta;
       p.conv_w = a->conv_k > 0 ? a->conv_w : nullptr;
@@ -228,20 +268,22 @@ static kda_status run_stage(const kda_prefill_args* a, void* ws, int stage, hipS
       p.A_log = a->A_log;
       p.dt_bias = a->dt_bias;
       p.beta_logits = (a->flags & KDA_FLAG_BETA_LOGITS) ? 1 : 0;
+      p.seqs = seqs;
       return hip_status(kda::launch_prep(p, a->D, a->chunk, fp32, st));
     }
     case KDA_STAGE_STATE: {
       if (a->T == 0) {
         if (a->S_T == a->S0) return KDA_OK;
-        const size_t n = (size_t)a->B * a->H * a->D * a->D;
+        const size_t n = (size_t)sz.NS * a->H * a->D * a->D;
         return hip_status(kda::launch_copy_state(a->S0, a->S_T, n, st));
       }
       const bool gn = a->o_norm_w != nullptr || a->o_gate != nullptr;
-      const StateCfg cfg = state_config(a->B, a->H, a->D, fp32, gn);
+      const StateCfg cfg = state_config(sz.NS, a->H, a->D, fp32, gn);
       kda::StateParams p{};
       p.ws = static_cast<const char*>(ws) + ws_layout(a).records;
       p.S0 = a->S0; p.S_T = a->S_T; p.o = a->o;
-      p.B = a->B; p.T = a->T; p.H = a->H; p.NT = NT;
+      p.B = sz.NS; p.T = a->T; p.H = a->H; p.NT = NT;
+      p.seqs = seqs;
       p.o_gate = a->o_gate;
       p.o_norm_w = a->o_norm_w;
       p.o_norm_eps = a->o_norm_eps;
@@ -250,7 +292,7 @@ static kda_status run_stage(const kda_prefill_args* a, void* ws, int stage, hipS
     }
     case KDA_STAGE_OUTPUT: {
       const bool gn = a->o_norm_w != nullptr || a->o_gate != nullptr;
-      if (a->T == 0 || !gn || state_config(a->B, a->H, a->D, fp32, gn).fused) return KDA_OK;
+      if (a->T == 0 || !gn || state_config(sz.NS, a->H, a->D, fp32, gn).fused) return KDA_OK;
       kda::OutStageParams q{};
       q.o = a->o;
       q.o_gate = a->o_gate;
@@ -265,7 +307,8 @@ static kda_status run_stage(const kda_prefill_args* a, void* ws, int stage, hipS
       p.x[0] = a->q; p.x[1] = a->k; p.x[2] = a->v;
       p.conv_state_in = a->conv_state_in;
       p.conv_state_out = a->conv_state_out;
-      p.B = a->B; p.T = a->T; p.HD = a->H * a->D;
+      p.B = sz.NS; p.T = a->T; p.HD = a->H * a->D;
+      p.bounds = seqs.bounds;  // NULL unless packed with T > 0 (T = 0: every sequence is empty)
       return hip_status(kda::launch_conv_tail(p, fp32, st));
     }
   }

@@ -296,6 +296,21 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// ------------------------------------------------------------ packed sequences
+// The sequence that owns chunk slot gc: the largest i < n_seqs with cstart[i] <=
+// gc (an empty sequence owns no slot, so it is skipped).  gc < cstart[n_seqs].
+__device__ __forceinline__ int seq_of_slot(const int* cstart, int n_seqs, int gc) {
+  int lo = 0, hi = n_seqs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cstart[mid] <= gc)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
 // ------------------------------------------------------------ small math
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + __expf(-x)); }
 __device__ __forceinline__ float sigmoid(float x) { return 1.0f / (1.0f + __expf(-x)); }

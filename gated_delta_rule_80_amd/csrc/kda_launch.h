@@ -14,6 +14,7 @@ hipError_t launch_state(const StateParams& p, int D, int C, bool fp32, int vb, i
 hipError_t launch_out_stage(const OutStageParams& p, int D, bool fp32, hipStream_t st);
 hipError_t launch_conv_norm(const ConvNormParams& p, int D, bool fp32, hipStream_t st);
 hipError_t launch_conv_tail(const TailParams& p, bool fp32, hipStream_t st);
+hipError_t launch_seq_index(const IndexParams& p, hipStream_t st);
 hipError_t launch_copy_state(const float* src, float* dst, size_t n, hipStream_t st);
 hipError_t launch_decode(const DecodeParams& p, int D, bool fp32, hipStream_t st);
 

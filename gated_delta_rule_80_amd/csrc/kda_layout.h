@@ -37,21 +37,44 @@ constexpr RecordLayout record_layout(int C, int D, size_t esize) {
 }
 
 // Workspace: a 256-byte header whose first word counts the chunks the fast
-// preparation handed to the exact one, the list of those chunk indices, then one
-// record per (sequence, head, chunk).
+// preparation handed to the exact one, the list of those chunk indices, for
+// packed sequences their clamped token bounds and first chunk indices (int32,
+// n_seqs + 1 each), then one record per (sequence, head, chunk) -- for packed
+// sequences per (head, chunk slot), n_slots = ceil(T / C) + n_seqs slots a head.
 struct WorkspaceLayout {
   size_t list;     // byte offset of the fallback list (uint32 per chunk)
+  size_t seq;      // byte offset of the sequence tables (packed sequences)
   size_t records;  // byte offset of the first record
   size_t bytes;    // total
 };
 
-constexpr WorkspaceLayout workspace_layout(size_t nrec, int C, int D, size_t esize) {
+constexpr WorkspaceLayout workspace_layout(size_t nrec, int C, int D, size_t esize,
+                                           size_t n_seqs = 0) {
   WorkspaceLayout w{};
   w.list = 256;
-  w.records = round_up(w.list + 4 * nrec, 256);
+  w.seq = round_up(w.list + 4 * nrec, 256);
+  w.records = round_up(w.seq + (n_seqs > 0 ? 8 * (n_seqs + 1) : 0), 256);
   w.bytes = w.records + nrec * record_layout(C, D, esize).bytes;
   return w;
 }
+
+// Packed sequences: sequence i is tokens [bounds[i], bounds[i + 1]) and owns
+// chunk slots [cstart[i], cstart[i + 1]) of every head (both tables in the
+// workspace, written by the index kernel from the caller's offsets).
+struct SeqTables {
+  const int* bounds;  // NULL: B equal-length sequences
+  const int* cstart;
+  int n_seqs;
+};
+
+struct IndexParams {
+  const int* cu_seqlens;  // caller's offsets, n_seqs + 1
+  int* bounds;
+  int* cstart;
+  int n_seqs;
+  int T;
+  int C;
+};
 
 struct PrepParams {
   const void* q;
@@ -72,6 +95,7 @@ struct PrepParams {
   const float* A_log;    // [H]: g holds the raw gate projection (with dt_bias), or NULL
   const float* dt_bias;  // [H*D]
   int beta_logits;       // beta holds logits
+  SeqTables seqs;        // packed sequences (then B = 1 and NT = chunk slots per head)
 };
 
 struct StateParams {
@@ -84,6 +108,7 @@ struct StateParams {
   const void* o_gate;     // [B][T][H][D] or NULL
   const float* o_norm_w;  // [D] or NULL
   float o_norm_eps;
+  SeqTables seqs;         // packed sequences (then B = n_seqs, NT = chunk slots per head)
 };
 
 // The output stage on its own, in place on o: RMSNorm with gain and/or the
@@ -115,6 +140,7 @@ struct TailParams {
   const void* conv_state_in;  // may be NULL
   void* conv_state_out;
   int B, T, HD;
+  const int* bounds;          // packed sequences: B = n_seqs, token bounds; else NULL
 };
 
 struct DecodeParams {

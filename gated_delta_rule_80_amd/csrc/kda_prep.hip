@@ -168,13 +168,33 @@ __global__ __launch_bounds__(fast_threads<E>()) void kda_chunk_prep_kernel(PrepP
   // Chunk-major order: the workgroups running at the same time cover every head
   // of a few consecutive chunks, so together they read whole token rows of q, k,
   // v, g (all heads of a token are adjacent in memory).  Records stay in
-  // (sequence, head, chunk) order for the state walk.
-  const int BH = p.B * p.H;
-  const int n = blockIdx.x / BH;
-  const int bh = blockIdx.x % BH;
-  const int h = bh % p.H, b = bh / p.H;
+  // (sequence, head, chunk) order for the state walk.  Packed sequences: slot gc
+  // of head h, a chunk of the sequence owning that slot (slots past the last one
+  // in use have nothing to do).  b is the sequence (conv state), tok0 its first
+  // token row, Tq its length.
+  int n, h, b, rec, Tq;
+  long tok0;
+  if (p.seqs.bounds == nullptr) {
+    const int BH = p.B * p.H;
+    n = blockIdx.x / BH;
+    const int bh = blockIdx.x % BH;
+    h = bh % p.H;
+    b = bh / p.H;
+    rec = bh * p.NT + n;
+    tok0 = (long)b * p.T;
+    Tq = p.T;
+  } else {
+    const int gc = blockIdx.x / p.H;
+    h = blockIdx.x % p.H;
+    if (gc >= p.seqs.cstart[p.seqs.n_seqs]) return;
+    b = seq_of_slot(p.seqs.cstart, p.seqs.n_seqs, gc);
+    n = gc - p.seqs.cstart[b];
+    tok0 = p.seqs.bounds[b];
+    Tq = p.seqs.bounds[b + 1] - p.seqs.bounds[b];
+    rec = h * p.NT + gc;
+    if (n < 0 || (long)n * C >= Tq) return;  // inconsistent tables: touch nothing
+  }
   const int t0 = n * C;
-  const int rec = bh * p.NT + n;
   char* recp = p.ws + (size_t)rec * RL.bytes;
   E* gW = reinterpret_cast<E*>(recp) + RL.w;
   E* gQL = reinterpret_cast<E*>(recp) + RL.ql;
@@ -199,14 +219,19 @@ __global__ __launch_bounds__(fast_threads<E>()) void kda_chunk_prep_kernel(PrepP
   FilterRegs<D, NTH> fr;
   if (conv) load_filters<D, NTH>(p.conv_w, p.H, h, tid, fr);
   Raw8<IO> win[3][TOK + 3];
-  front_load<TOK, IO>(static_cast<const IO*>(p.q), static_cast<const IO*>(p.k),
-                      static_cast<const IO*>(p.v), static_cast<const IO*>(p.conv_state_in), conv,
-                      b, p.T, p.H, D, h, ch, t0, C, tf, win);
+  const long HDl = (long)p.H * D;
+  const IO* cs_in = p.conv_state_in == nullptr
+                        ? nullptr
+                        : static_cast<const IO*>(p.conv_state_in) + (long)b * 9 * HDl;
+  front_load<TOK, IO>(static_cast<const IO*>(p.q) + tok0 * HDl,
+                      static_cast<const IO*>(p.k) + tok0 * HDl,
+                      static_cast<const IO*>(p.v) + tok0 * HDl, cs_in, conv, 0, Tq, p.H, D, h,
+                      ch, t0, C, tf, win);
   // g rows and beta of tokens [t0, t0 + C): range-checked loads read zeros past
   // the end of the sequence
   Raw8<IO> graw[TOK];
   float braw[TOK];
-  const int nt = p.T - t0 < C ? p.T - t0 : C;  // tokens of the sequence in this chunk
+  const int nt = Tq - t0 < C ? Tq - t0 : C;  // tokens of the sequence in this chunk
   // raw gate projection: this thread's 8 channel biases and minus the head's rate
   const bool gact = p.A_log != nullptr;
   f32x4 gb0 = {0.f, 0.f, 0.f, 0.f}, gb1 = gb0;
@@ -220,9 +245,9 @@ __global__ __launch_bounds__(fast_threads<E>()) void kda_chunk_prep_kernel(PrepP
   {
     constexpr int ES = (int)sizeof(IO);
     const long HD = (long)p.H * D;
-    const BufRes rg = make_buf(static_cast<const IO*>(p.g) + ((long)b * p.T + t0) * HD + (long)h * D,
+    const BufRes rg = make_buf(static_cast<const IO*>(p.g) + (tok0 + t0) * HD + (long)h * D,
                                (unsigned)(((long)(nt - 1) * HD + D) * ES));
-    const BufRes rb = make_buf(static_cast<const IO*>(p.beta) + ((long)b * p.T + t0) * p.H + h,
+    const BufRes rb = make_buf(static_cast<const IO*>(p.beta) + (tok0 + t0) * p.H + h,
                                (unsigned)(((long)(nt - 1) * p.H + 1) * ES));
     const int gv = (TOK * s) * (int)(HD * ES) + ch * ES;
     const int bv = (TOK * s) * p.H * ES;
@@ -242,7 +267,7 @@ __global__ __launch_bounds__(fast_threads<E>()) void kda_chunk_prep_kernel(PrepP
   if (conv) store_filters<D, NTH>(fr, sm.filt, tid);
   __syncthreads();  // filters are in LDS
   float yq[TOK][8], yk[TOK][8], yv[TOK][8], qk[TOK];
-  front_compute<TOK, D, IO, false, false>(win, sm.filt, conv, ch, tf, p.T, active, p.l2 != 0,
+  front_compute<TOK, D, IO, false, false>(win, sm.filt, conv, ch, tf, Tq, active, p.l2 != 0,
                                           p.eps, p.scale, yq, yk, yv, qk);
   // cumulative log2-decay within the segment.  Past the end of the sequence g
   // and beta are 0 (the range-checked loads give zeros; the activations of raw
@@ -573,9 +598,10 @@ __global__ __launch_bounds__(256) void kda_conv_norm_kernel(ConvNormParams p) {
 }
 
 // --------------------------------------------------------- conv state hand-over
-// conv_state_out[b][i][tau][c] = raw input at position T - 3 + tau (tau = 0..2),
-// taken from the previous state when that position is < 0.  Each thread reads
-// its three values before writing them, so out may equal in.
+// conv_state_out[b][i][tau][c] = raw input at position T - 3 + tau (tau = 0..2)
+// of sequence b, taken from the previous state when that position is < 0 (T the
+// sequence's length; packed sequences read their bounds).  Each thread reads its
+// three values before writing them, so out may equal in.
 template <typename IO>
 __global__ __launch_bounds__(256) void kda_conv_tail_kernel(TailParams p) {
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
@@ -587,12 +613,14 @@ __global__ __launch_bounds__(256) void kda_conv_tail_kernel(TailParams p) {
   const IO* x = static_cast<const IO*>(p.x[i]);
   const IO* in = static_cast<const IO*>(p.conv_state_in);
   IO* out = static_cast<IO*>(p.conv_state_out);
+  const long tok0 = p.bounds == nullptr ? (long)b * p.T : p.bounds[b];
+  const int Tq = p.bounds == nullptr ? p.T : p.bounds[b + 1] - p.bounds[b];
   IO val[3];
 #pragma unroll
   for (int tau = 0; tau < 3; ++tau) {
-    const int t = p.T - 3 + tau;
+    const int t = Tq - 3 + tau;
     if (t >= 0)
-      val[tau] = x[((size_t)b * p.T + t) * p.HD + c];
+      val[tau] = x[((size_t)tok0 + t) * p.HD + c];
     else if (in != nullptr)
       val[tau] = in[(((size_t)b * 3 + i) * 3 + (3 + t)) * p.HD + c];
     else
@@ -600,6 +628,76 @@ __global__ __launch_bounds__(256) void kda_conv_tail_kernel(TailParams p) {
   }
 #pragma unroll
   for (int tau = 0; tau < 3; ++tau) out[(((size_t)b * 3 + i) * 3 + tau) * p.HD + c] = val[tau];
+}
+
+// ------------------------------------------------------ packed-sequence tables
+// Inclusive scan over the 1024 threads of a workgroup (max or sum); red holds 16
+// ints of scratch.  Every thread must call it.
+template <bool ADD>
+__device__ __forceinline__ int block_scan(int x, int* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x = ADD ? x + y : (y > x ? y : x);
+  }
+  if (lane == 63) red[wave] = x;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < 16 ? red[lane] : (ADD ? 0 : -2147483647 - 1);
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) {
+      const int y = __shfl_up(w, d, 64);
+      if (lane >= d) w = ADD ? w + y : (y > w ? y : w);
+    }
+    if (lane < 16) red[lane] = w;
+  }
+  __syncthreads();
+  if (wave > 0) {
+    const int pre = red[wave - 1];
+    x = ADD ? x + pre : (pre > x ? pre : x);
+  }
+  __syncthreads();  // red may be reused
+  return x;
+}
+
+// Token bounds of the packed sequences, the running maximum of the caller's
+// offsets clamped to [0, T] (so malformed offsets can only give empty or
+// shortened sequences, never an access outside the tensors), and each sequence's
+// first chunk slot, the exclusive running sum of its chunk count (cstart[n_seqs]
+// = slots in use).  One workgroup of 1024 threads, n_seqs + 1 entries in blocks.
+__global__ __launch_bounds__(1024) void kda_seq_index_kernel(IndexParams p) {
+  __shared__ int red[16];
+  __shared__ int carry;
+  const int tid = threadIdx.x;
+  if (tid == 0) carry = 0;
+  __syncthreads();
+  for (int base = 0; base <= p.n_seqs; base += 1024) {
+    const int i = base + tid;
+    int x = 0;
+    if (i <= p.n_seqs) {
+      x = p.cu_seqlens[i];
+      x = x < 0 ? 0 : (x > p.T ? p.T : x);
+    }
+    x = block_scan<false>(x, red);
+    if (x < carry) x = carry;
+    if (i <= p.n_seqs) p.bounds[i] = x;
+    __syncthreads();  // every thread has read carry
+    if (tid == 1023) carry = x;
+    __syncthreads();
+  }
+  // bounds are visible to the whole workgroup after the barrier above
+  if (tid == 0) carry = 0;
+  __syncthreads();
+  for (int base = 0; base <= p.n_seqs; base += 1024) {
+    const int i = base + tid;
+    const int cnt = i < p.n_seqs ? (p.bounds[i + 1] - p.bounds[i] + p.C - 1) / p.C : 0;
+    const int incl = block_scan<true>(cnt, red) + carry;
+    if (i <= p.n_seqs) p.cstart[i] = incl - cnt;
+    __syncthreads();
+    if (tid == 1023) carry = incl;
+    __syncthreads();
+  }
 }
 
 // S_T = S0 (or zeros) for empty sequences.
@@ -693,6 +791,11 @@ hipError_t launch_conv_tail(const TailParams& p, bool fp32, hipStream_t st) {
     hipLaunchKernelGGL((kda_conv_tail_kernel<float>), dim3(grid), dim3(256), 0, st, p);
   else
     hipLaunchKernelGGL((kda_conv_tail_kernel<__bf16>), dim3(grid), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_seq_index(const IndexParams& p, hipStream_t st) {
+  hipLaunchKernelGGL(kda_seq_index_kernel, dim3(1), dim3(1024), 0, st, p);
   return hipGetLastError();
 }
 

@@ -85,9 +85,26 @@ __global__ __launch_bounds__(kPrepThreads) void kda_chunk_prep_exact_kernel(Prep
   for (unsigned li = blockIdx.x; li < nlist; li += gridDim.x) {
   __syncthreads();  // the previous chunk's phase 5 is done with LDS
   const int rec = (int)p.fb_list[li];
-  const int n = rec % p.NT;
-  const int bh = rec / p.NT;
-  const int h = bh % p.H, b = bh / p.H;
+  // b: the sequence (conv state); tok0: its first token row; Tq: its length
+  int n, h, b, Tq;
+  long tok0;
+  if (p.seqs.bounds == nullptr) {
+    n = rec % p.NT;
+    const int bh = rec / p.NT;
+    h = bh % p.H;
+    b = bh / p.H;
+    tok0 = (long)b * p.T;
+    Tq = p.T;
+  } else {
+    // packed sequences: record = head * slots + slot
+    const int gc = rec % p.NT;
+    h = rec / p.NT;
+    b = seq_of_slot(p.seqs.cstart, p.seqs.n_seqs, gc);
+    n = gc - p.seqs.cstart[b];
+    tok0 = p.seqs.bounds[b];
+    Tq = p.seqs.bounds[b + 1] - p.seqs.bounds[b];
+    if (n < 0 || (long)n * C >= Tq) continue;  // inconsistent tables: touch nothing
+  }
   const int t0 = n * C;
   char* recp = p.ws + (size_t)rec * RL.bytes;
   E* gW = reinterpret_cast<E*>(recp) + RL.w;
@@ -97,12 +114,16 @@ __global__ __launch_bounds__(kPrepThreads) void kda_chunk_prep_exact_kernel(Prep
   E* gP = reinterpret_cast<E*>(recp) + RL.p;
   float* gLC = reinterpret_cast<float*>(recp + RL.lc_bytes);
 
-  const IO* q = static_cast<const IO*>(p.q);
-  const IO* k = static_cast<const IO*>(p.k);
-  const IO* v = static_cast<const IO*>(p.v);
-  const IO* gg = static_cast<const IO*>(p.g);
-  const IO* bb = static_cast<const IO*>(p.beta);
-  const IO* cs = static_cast<const IO*>(p.conv_state_in);
+  // the sequence's rows: token t of it is row tok0 + t
+  const long HDl = (long)p.H * D;
+  const IO* q = static_cast<const IO*>(p.q) + tok0 * HDl;
+  const IO* k = static_cast<const IO*>(p.k) + tok0 * HDl;
+  const IO* v = static_cast<const IO*>(p.v) + tok0 * HDl;
+  const IO* gg = static_cast<const IO*>(p.g) + tok0 * HDl;
+  const IO* bb = static_cast<const IO*>(p.beta) + tok0 * p.H;
+  const IO* cs = p.conv_state_in == nullptr
+                     ? nullptr
+                     : static_cast<const IO*>(p.conv_state_in) + (long)b * 9 * HDl;
 
   // ---------------------------------------------------------------- phase 1
   const bool active = tid < ITEMS;
@@ -115,21 +136,21 @@ __global__ __launch_bounds__(kPrepThreads) void kda_chunk_prep_exact_kernel(Prep
   FilterRegs<D, kPrepThreads> fr;
   if (conv) load_filters<D, kPrepThreads>(p.conv_w, p.H, h, tid, fr);
   Raw8<IO> win[3][7];
-  front_load<4, IO>(q, k, v, cs, conv, b, p.T, p.H, D, h, ch, t0, C, tf, win);
+  front_load<4, IO>(q, k, v, cs, conv, 0, Tq, p.H, D, h, ch, t0, C, tf, win);
   float gl[4][8], bt[4];
   const size_t HD = (size_t)p.H * D;
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     const int t = tf + m;
-    const int tc = t < p.T ? t : p.T - 1;
-    load8(gg + ((size_t)b * p.T + tc) * HD + (size_t)h * D + ch, gl[m]);
-    bt[m] = to_f32(bb[((size_t)b * p.T + tc) * p.H + h]);
+    const int tc = t < Tq ? t : Tq - 1;
+    load8(gg + (size_t)tc * HD + (size_t)h * D + ch, gl[m]);
+    bt[m] = to_f32(bb[(size_t)tc * p.H + h]);
   }
   __builtin_amdgcn_sched_barrier(0);
   if (conv) store_filters<D, kPrepThreads>(fr, sm.filt, tid);
   __syncthreads();  // filters are in LDS
   float yq[4][8], yk[4][8], yv[4][8], qk[4];
-  front_compute<4, D, IO>(win, sm.filt, conv, ch, tf, p.T, active, p.l2 != 0, p.eps, p.scale, yq,
+  front_compute<4, D, IO>(win, sm.filt, conv, ch, tf, Tq, active, p.l2 != 0, p.eps, p.scale, yq,
                           yk, yv, qk);
   // raw projections -> decay and write strength (float32); zero past the end
   const bool gact = p.A_log != nullptr;
@@ -140,7 +161,7 @@ __global__ __launch_bounds__(kPrepThreads) void kda_chunk_prep_exact_kernel(Prep
   }
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
-    const bool ok = active && tf + m < p.T;
+    const bool ok = active && tf + m < Tq;
     bt[m] = ok ? (p.beta_logits ? sigmoid(bt[m]) : bt[m]) : 0.f;
 #pragma unroll
     for (int c = 0; c < 8; ++c)

@@ -100,6 +100,27 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void kda_chunk_state_kernel(
   }
   const int h = bh % p.H, b = bh / p.H;
   const int vb0 = vblk * VB;
+  // This walk's tokens and records: sequence b of B equal-length ones, or packed
+  // sequence b (tokens [bounds[b], bounds[b + 1]), chunk slots from cstart[b] of
+  // head h).
+  long tok0;
+  int Tq, nch;
+  size_t rec0;
+  if (p.seqs.bounds == nullptr) {
+    tok0 = (long)b * p.T;
+    Tq = p.T;
+    nch = p.NT;
+    rec0 = (size_t)bh * p.NT;
+  } else {
+    tok0 = p.seqs.bounds[b];
+    Tq = p.seqs.bounds[b + 1] - p.seqs.bounds[b];
+    // slots clamped to this head's NT, so the records read stay in the workspace
+    int c0 = p.seqs.cstart[b], c1 = p.seqs.cstart[b + 1];
+    c0 = c0 < 0 ? 0 : (c0 > p.NT ? p.NT : c0);
+    c1 = c1 < c0 ? c0 : (c1 > p.NT ? p.NT : c1);
+    nch = c1 - c0;
+    rec0 = (size_t)h * p.NT + c0;
+  }
 
   // this wave's tiles
   const int R = wave % RT;                      // t-tile of every (t, v) unit of this wave
@@ -143,7 +164,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void kda_chunk_state_kernel(
     src_off[it] = (uint32_t)off;
   }
   auto issue_copy = [&](int n) {
-    const char* recp = p.ws + ((size_t)bh * p.NT + n) * RL.bytes;
+    const char* recp = p.ws + (rec0 + n) * RL.bytes;
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
       // this wave's 64 lanes fill img + (it * NT + 64 * wave) * 16 onwards, 16 bytes per lane
@@ -217,13 +238,13 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void kda_chunk_state_kernel(
     if constexpr (GN) {
       if (!has_gate) return;
       const char* src = static_cast<const char*>(p.o_gate) +
-                        (((size_t)b * p.T + (size_t)nn * C) * HD + (size_t)h * D) * sizeof(IO);
+                        (((size_t)tok0 + (size_t)nn * C) * HD + (size_t)h * D) * sizeof(IO);
 #pragma unroll
       for (int it = 0; it < (GCH + NT - 1) / NT; ++it) {
         const int idx = it * NT + tid;
         const int tt = idx / GRP, cs = idx % GRP;
         // lanes of one wave fill 64 consecutive pieces from sgate + (it * NT + 64 * wave) * 16
-        if (idx < GCH && nn * C + tt < p.T)
+        if (idx < GCH && nn * C + tt < Tq)
           __builtin_amdgcn_global_load_lds(
               (const glb_void_t*)(src + (size_t)tt * HD * sizeof(IO) + (size_t)((cs ^ (tt % GRP)) * 16)),
               (lds_void_t*)(sgate + (size_t)((nn & 1) * GCH + it * NT + 64 * wave) * 16), 16, 0, 0);
@@ -276,15 +297,15 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void kda_chunk_state_kernel(
             for (int e = 0; e < 4; ++e) ov[e] *= sigmoid(gv[e]);
           }
         }
-        if (t < p.T)
-          store4(o + ((size_t)b * p.T + t) * HD + (size_t)h * D + vb0 + 16 * Vt + 4 * g4,
+        if (t < Tq)
+          store4(o + ((size_t)tok0 + t) * HD + (size_t)h * D + vb0 + 16 * Vt + 4 * g4,
                  ov[0], ov[1], ov[2], ov[3]);
       }
     }
   };
 
-  issue_copy(0);
-  for (int n = 0; n < p.NT; ++n) {
+  if (nch > 0) issue_copy(0);
+  for (int n = 0; n < nch; ++n) {
     __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of chunk n (and older stores) are done
     lds_barrier();                  // the whole image of chunk n and the state are in LDS
     // ---- this chunk's fragments, from the image into registers
@@ -310,7 +331,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void kda_chunk_state_kernel(
       if (FULL_U || u < RT * VT) fu[i].load(iU + ((size_t)(R * VT + u / RT) * 64 + lane) * 4);
     }
     lds_barrier();  // every wave holds its fragments: the image may be overwritten
-    if (n + 1 < p.NT) issue_copy(n + 1);
+    if (n + 1 < nch) issue_copy(n + 1);
     load_gate(n);  // buffer n % 2: chunk n - 2's, stored during step n - 1
     if (n > 0) store_out(n - 1);
     if (has_u) fp.mask_above(i_row, g4);
@@ -366,7 +387,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void kda_chunk_state_kernel(
     __builtin_amdgcn_s_waitcnt(0);  // this wave's gate copies
     lds_barrier();                  // the last chunk's row sums and gate rows
   }
-  if (p.NT > 0) store_out(p.NT - 1);
+  if (nch > 0) store_out(nch - 1);
   // ---- final state
   if (p.S_T != nullptr) {
 #pragma unroll

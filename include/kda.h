@@ -47,9 +47,11 @@
  *     enqueued; on any error nothing is launched and outputs are untouched.
  *     Validation never calls into the HIP runtime and never reads device memory.
  *   - Unsupported modes return KDA_ERR_UNSUPPORTED instead of computing a wrong
- *     result (packed/variable-length batches, D outside {16,32,64,128},
- *     conv_k outside {0,4}, chunk outside {16,32,64}, fp32 I/O with D = 128 and
- *     chunk = 64).
+ *     result (D outside {16,32,64,128}, conv_k outside {0,4}, chunk outside
+ *     {16,32,64}, fp32 I/O with D = 128 and chunk = 64).  Packed variable-length
+ *     sequences are supported by kda_prefill (cu_seqlens; the layers the pages
+ *     describe reject packing because their KDA would let state flow across
+ *     segment boundaries: "MaxText PR 5550").
  *   - Device values are not checked: g must be finite and <= 0 (any finite value
  *     when it holds a raw projection), inputs finite.
  *
@@ -130,6 +132,16 @@ typedef struct kda_prefill_args {
   float o_norm_eps;     /* >= 0, finite; read only with o_norm_w (1e-6 in the released model) */
   const void* o_gate;   /* device [B][T][H][D] gate pre-activation: o <- o * sigmoid(o_gate),
                            after the norm if both are given */
+  /* packed sequences (NULL = B equal-length sequences) */
+  const int32_t* cu_seqlens; /* device [n_seqs + 1] token offsets, 0 = cu[0] <= cu[1] <= ...
+                                <= cu[n_seqs] = T; requires B = 1.  Sequence i is tokens
+                                [cu[i], cu[i+1]) with its own conv history and initial state:
+                                S0, S_T are [n_seqs][H][D][D] and the conv states
+                                [n_seqs][3][conv_k-1][H*D].  Offsets are read on the device
+                                and clamped (running maximum, within [0, T]): malformed ones
+                                give wrong sequences but no access outside the buffers, and
+                                tokens outside every sequence leave o undefined. */
+  int32_t n_seqs;       /* >= 1 with cu_seqlens; must be 0 without */
 } kda_prefill_args;
 
 /* Host-only check of every argument; returns the first error found. */

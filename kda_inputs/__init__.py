@@ -140,6 +140,34 @@ def make_stage_inputs(w: Workload, seed: int = 0, device: str | torch.device = "
                 b_logit=b_logit)
 
 
+def make_packed_inputs(w: Workload, lengths, seed: int = 0,
+                       device: str | torch.device = "cpu") -> dict:
+    """Packed sequences of the given lengths with workload w's value distributions
+    (w.B and w.T are ignored): q, k, v, g [1, T, H, D] and beta [1, T, H] with T =
+    sum(lengths); S0 [N, H, D, D] and conv_state [N, 3, 3, H*D] per sequence (when
+    w has them); cu_seqlens int32 [N + 1], the running sum of the lengths."""
+    lengths = [int(x) for x in lengths]
+    T = sum(lengths)
+    N = len(lengths)
+    base = make_inputs(replace(w, B=1, T=T, s0_std=0.0, conv_state_std=0.0), seed=seed, device=device)
+    device = torch.device(device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed) * 7919 + 5)
+    H, D = w.H, w.D
+    S0 = None
+    if w.s0_std > 0:
+        S0 = torch.randn(N, H, D, D, generator=gen, device=device).mul_(w.s0_std)
+    conv_state = None
+    if w.conv_state_std > 0:
+        conv_state = torch.randn(N, 3, 3, H * D, generator=gen, device=device).mul_(
+            w.conv_state_std).to(DTYPES[w.io])
+    cu = [0]
+    for x in lengths:
+        cu.append(cu[-1] + x)
+    return dict(base, S0=S0, conv_state=conv_state,
+                cu_seqlens=torch.tensor(cu, dtype=torch.int32, device=device))
+
+
 def to_numpy(t):
     """float64 NumPy copy of a tensor (exact for bf16/fp32 values), or None."""
     if t is None:

@@ -294,3 +294,39 @@ def test_stage_struct_layout_matches_header():
         body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
         names = re.findall(r"\b([A-Za-z_][A-Za-z0-9_]*)\s*[,;]", body)
         assert [n for n, _ in cls._fields_] == names, struct
+
+
+# ------------------------------------------------------------ packed sequences
+def test_packed_arguments(lib):
+    f = Fake()
+    f.next = 0x7D0000000000
+    cu = f()
+    a = prefill(B=1, cu_seqlens=cu, n_seqs=5)
+    assert vp(a) == OK
+    assert vp(prefill(B=2, cu_seqlens=cu, n_seqs=5)) == SHAPE  # packed rows share B = 1
+    assert vp(prefill(B=1, cu_seqlens=cu, n_seqs=0)) == SHAPE
+    assert vp(prefill(B=1, n_seqs=3)) == SHAPE                 # n_seqs without offsets
+    assert vp(prefill(B=1, cu_seqlens=cu + 4, n_seqs=5)) == ALIGN
+    b = prefill(B=1, cu_seqlens=cu, n_seqs=5)
+    b.cu_seqlens = b.o
+    assert vp(b) == ALIAS
+    # the workspace holds a head's chunk slots, one more per sequence, and the tables
+    w1 = kda.kda_prefill_workspace_bytes(prefill(B=1, cu_seqlens=cu, n_seqs=1))
+    w9 = kda.kda_prefill_workspace_bytes(prefill(B=1, cu_seqlens=cu, n_seqs=9))
+    plain = kda.kda_prefill_workspace_bytes(prefill(B=1))
+    assert plain < w1 < w9
+    # T = 0 needs no workspace, packed or not
+    assert kda.kda_prefill_workspace_bytes(prefill(B=1, T=0, cu_seqlens=cu, n_seqs=4)) == 0
+
+
+def test_packed_state_sizes_follow_n_seqs(lib):
+    """S_T of a packed call spans n_seqs states: an S_T placed right after S0's
+    n_seqs states is fine, one starting inside them overlaps."""
+    f = Fake()
+    f.next = 0x7C0000000000
+    a = prefill(B=1, cu_seqlens=f(), n_seqs=3)
+    state = 3 * a.H * a.D * a.D * 4
+    a.S_T = a.S0 + state
+    assert vp(a) == OK
+    a.S_T = a.S0 + state - 256
+    assert vp(a) == ALIAS
