@@ -12,6 +12,7 @@ from .kda_oracle import (  # noqa: F401
     gated_delta_step,
     kda_gate,
     kda_reference,
+    kda_reference_backward,
     kda_reference_decode_step,
     kda_reference_heads,
     kda_reference_packed,

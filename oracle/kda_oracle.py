@@ -319,6 +319,121 @@ def conv_norm_reference(q, k, v, conv_w, conv_state=None, l2norm_qk=True, eps=L2
     return qh, kh, vh, tails
 
 
+def kda_reference_backward(q, k, v, g, beta, do, dS_T=None, conv_w=None, conv_state=None,
+                           S0=None, scale=1.0, l2norm_qk=True, eps=L2_EPS):
+    """Gradients of the mixer by reverse-mode differentiation of its sequential
+    definition (``kda_reference``), fp64.
+
+    The scalar differentiated is  L = sum(o * do) + sum(S_T * dS_T)  (dS_T None: 0),
+    i.e. do and dS_T are the upstream gradients of o and S_T.  Inputs as
+    ``kda_reference``.  Returns a dict of gradients with the inputs' shapes: dq, dk,
+    dv (of the raw inputs), dg, dbeta, dS0 (zeros-shaped when S0 is None: the
+    gradient of a zero initial state), dconv_w and dconv_state (None without the
+    convolution).
+
+    Reverse of one step (S_bar = Diag(alpha) S, u = beta (v - S_bar^T k),
+    S' = S_bar + k u^T, o = scale S'^T q), with G the gradient of S':
+        G += scale q do^T;   dq = scale S' do
+        dk += G u;   du = G^T k
+        dv = beta du;   dbeta = du . (v - S_bar^T k)
+        G_bar = G - beta k du^T;   dk -= beta S_bar du
+        dalpha = rowsum(G_bar * S);   dg = alpha * dalpha;   G <- Diag(alpha) G_bar
+    then the front end in reverse: the L2 norm (z = y / n, n = sqrt(|y|^2 + eps):
+    dy = dz / n - y (y . dz) / n^3), SiLU (x sigmoid(x), derivative
+    sigmoid(x) (1 + x (1 - sigmoid(x)))) and the convolution (a correlation, whose
+    adjoint sends dy[t] back to the inputs t-3 .. t and to the filter taps).
+    """
+    q, k, v, g, do = (np.asarray(a, dtype=np.float64) for a in (q, k, v, g, do))
+    beta = np.asarray(beta, dtype=np.float64)
+    B, T, H, D = q.shape
+    _check_decay(g)
+    HD = H * D
+    raw = (q, k, v)
+    pre = ys = None
+    if conv_w is not None:
+        cw = np.asarray(conv_w, dtype=np.float64)
+        K = cw.shape[2]
+        hist = np.zeros((B, 3, K - 1, HD)) if conv_state is None else np.asarray(conv_state, dtype=np.float64)
+        pre = np.empty((3, B, T, HD))
+        for i, x in enumerate(raw):
+            for b in range(B):
+                pre[i, b] = short_conv(x[b].reshape(T, HD), cw[i], hist[b, i])
+        ys = [silu(pre[i]).reshape(B, T, H, D) for i in range(3)]
+    else:
+        ys = [x.copy() for x in raw]
+    yq, yk, yv = ys
+    if l2norm_qk:
+        nq = np.sqrt(np.sum(yq * yq, axis=-1, keepdims=True) + eps)
+        nk = np.sqrt(np.sum(yk * yk, axis=-1, keepdims=True) + eps)
+        qh, kh = yq / nq, yk / nk
+    else:
+        qh, kh = yq, yk
+    vh = yv
+    # forward, keeping the state before each step
+    S = np.zeros((B, H, D, D)) if S0 is None else np.array(S0, dtype=np.float64)
+    S_prev = np.empty((T, B, H, D, D))
+    for t in range(T):
+        S_prev[t] = S
+        S, _ = gated_delta_step(S, qh[:, t], kh[:, t], vh[:, t], g[:, t], beta[:, t], scale)
+    # reverse
+    G = np.zeros((B, H, D, D)) if dS_T is None else np.array(dS_T, dtype=np.float64)
+    dqh, dkh, dvh = np.zeros_like(qh), np.zeros_like(kh), np.zeros_like(vh)
+    dg, dbeta = np.zeros_like(g), np.zeros_like(beta)
+    for t in range(T - 1, -1, -1):
+        qt, kt, vt, bt = qh[:, t], kh[:, t], vh[:, t], beta[:, t]
+        alpha = np.exp(g[:, t])
+        Sp = S_prev[t]
+        S_bar = alpha[..., :, None] * Sp
+        r = np.einsum("bhcv,bhc->bhv", S_bar, kt)
+        u = bt[..., None] * (vt - r)
+        S_new = S_bar + kt[..., :, None] * u[..., None, :]
+        dot = do[:, t]
+        G = G + scale * qt[..., :, None] * dot[..., None, :]
+        dqh[:, t] = scale * np.einsum("bhcv,bhv->bhc", S_new, dot)
+        dk_t = np.einsum("bhcv,bhv->bhc", G, u)
+        du = np.einsum("bhcv,bhc->bhv", G, kt)
+        dvh[:, t] = bt[..., None] * du
+        dbeta[:, t] = np.sum(du * (vt - r), axis=-1)
+        dr = -bt[..., None] * du
+        G_bar = G + kt[..., :, None] * dr[..., None, :]
+        dk_t += np.einsum("bhcv,bhv->bhc", S_bar, dr)
+        dkh[:, t] = dk_t
+        dalpha = np.sum(G_bar * Sp, axis=-1)
+        dg[:, t] = alpha * dalpha
+        G = alpha[..., :, None] * G_bar
+    dS0 = G
+    # front end in reverse
+    if l2norm_qk:
+        dyq = dqh / nq - yq * np.sum(yq * dqh, axis=-1, keepdims=True) / nq ** 3
+        dyk = dkh / nk - yk * np.sum(yk * dkh, axis=-1, keepdims=True) / nk ** 3
+    else:
+        dyq, dyk = dqh, dkh
+    dys = [dyq, dyk, dvh]
+    if conv_w is None:
+        dq_, dk_, dv_ = dys
+        return dict(dq=dq_, dk=dk_, dv=dv_, dg=dg, dbeta=dbeta, dS0=dS0, dconv_w=None,
+                    dconv_state=None)
+    dconv_w = np.zeros_like(cw)
+    dhist = np.zeros_like(hist)
+    dx = []
+    for i in range(3):
+        xs = pre[i]
+        sg = sigmoid(xs)
+        dpre = dys[i].reshape(B, T, HD) * sg * (1.0 + xs * (1.0 - sg))
+        dxi = np.zeros((B, T, HD))
+        for b in range(B):
+            xe = np.concatenate([hist[b, i], raw[i][b].reshape(T, HD)], axis=0)  # [K-1+T, HD]
+            dxe = np.zeros_like(xe)
+            for tau in range(K):
+                dconv_w[i][:, tau] += np.sum(dpre[b] * xe[tau:tau + T], axis=0)
+                dxe[tau:tau + T] += cw[i][:, tau][None, :] * dpre[b]
+            dhist[b, i] = dxe[:K - 1]
+            dxi[b] = dxe[K - 1:]
+        dx.append(dxi.reshape(B, T, H, D))
+    return dict(dq=dx[0], dk=dx[1], dv=dx[2], dg=dg, dbeta=dbeta, dS0=dS0, dconv_w=dconv_w,
+                dconv_state=dhist)
+
+
 def kda_reference_packed(q, k, v, g, beta, cu_seqlens, conv_w=None, conv_state=None, S0=None,
                          **kw):
     """The mixer over packed sequences: sequence i is tokens [cu_seqlens[i],

@@ -15,7 +15,7 @@ import pytest
 from scipy.special import expit
 
 from oracle import (conv_norm_reference, conv_tail, gated_delta_step, kda_reference,
-                    kda_reference_decode_step, kda_reference_heads, kda_reference_packed,
+                    kda_reference_backward, kda_reference_decode_step, kda_reference_heads, kda_reference_packed,
                     l2_normalize,
                     kda_gate, output_gate_norm, rms_norm, short_conv, sigmoid, silu,
                     softplus)
@@ -569,3 +569,83 @@ def test_packed_rejects_bad_offsets():
     for cu in ([0, 3, 2, 5], [1, 5], [0, 4], [0, 6]):
         with pytest.raises(ValueError):
             kda_reference_packed(q, k, v, g, beta, cu)
+
+
+# ------------------------------------------------------------------- backward
+def _loss_and_grads(rng, conv, l2, s0=True, B=2, T=7, H=2, D=4, scale=0.7):
+    q, k, v, g, beta, conv_w, S0 = rand_case(rng, B=B, T=T, H=H, D=D, s0=s0)
+    conv_w = conv_w if conv else None
+    cs = rng.standard_normal((B, 3, 3, H * D)) if conv else None
+    do = rng.standard_normal(q.shape)
+    dST = rng.standard_normal((B, H, D, D))
+
+    def L(q, k, v, g, beta, S0, conv_w, cs):
+        o, S, _ = kda_reference(q, k, v, g, beta, conv_w=conv_w, conv_state=cs, S0=S0,
+                                scale=scale, l2norm_qk=l2)
+        return np.sum(o * do) + np.sum(S * dST)
+
+    gr = kda_reference_backward(q, k, v, g, beta, do, dST, conv_w=conv_w, conv_state=cs, S0=S0,
+                                scale=scale, l2norm_qk=l2)
+    args = dict(q=q, k=k, v=v, g=g, beta=beta, S0=S0, conv_w=conv_w, cs=cs)
+    return L, gr, args
+
+
+@pytest.mark.parametrize("conv,l2", [(True, True), (False, True), (True, False), (False, False)])
+def test_backward_matches_finite_differences(conv, l2):
+    """Directional derivatives of L = sum(o * do) + sum(S_T * dS_T) by central
+    differences of the forward oracle, for every input."""
+    rng = np.random.default_rng(20 + 2 * conv + l2)
+    L, gr, args = _loss_and_grads(rng, conv, l2)
+    names = dict(q="dq", k="dk", v="dv", g="dg", beta="dbeta", S0="dS0", conv_w="dconv_w",
+                 cs="dconv_state")
+    h = 1e-6
+    for n, gn in names.items():
+        if args[n] is None:
+            assert gr[gn] is None
+            continue
+        for _ in range(2):
+            d = rng.standard_normal(args[n].shape)
+            a1, a2 = dict(args), dict(args)
+            a1[n] = args[n] + h * d
+            a2[n] = args[n] - h * d
+            fd = (L(**a1) - L(**a2)) / (2 * h)
+            an = np.sum(gr[gn] * d)
+            assert abs(fd - an) <= 1e-7 * max(1.0, abs(fd)), (n, fd, an)
+
+
+def test_backward_elementwise_tiny():
+    """Every element of every gradient on a tiny case, one central difference each."""
+    rng = np.random.default_rng(30)
+    L, gr, args = _loss_and_grads(rng, True, True, B=1, T=3, H=1, D=2)
+    names = dict(q="dq", k="dk", v="dv", g="dg", beta="dbeta", S0="dS0", conv_w="dconv_w",
+                 cs="dconv_state")
+    h = 1e-6
+    for n, gn in names.items():
+        x = args[n]
+        for idx in np.ndindex(x.shape):
+            a1, a2 = dict(args), dict(args)
+            x1, x2 = x.copy(), x.copy()
+            x1[idx] += h
+            x2[idx] -= h
+            a1[n], a2[n] = x1, x2
+            fd = (L(**a1) - L(**a2)) / (2 * h)
+            assert abs(fd - gr[gn][idx]) <= 1e-7 * max(1.0, abs(fd)), (n, idx, fd, gr[gn][idx])
+
+
+def test_backward_closed_form_without_writes():
+    """beta = 0 and g = 0 (no write, no decay): o_t = scale S0^T q_t, so dq_t = scale
+    S0 do_t, dS0 = scale sum_t q_t do_t^T + dS_T, and dk = dv = 0."""
+    rng = np.random.default_rng(31)
+    B, T, H, D, scale = 1, 5, 2, 3, 0.5
+    q, k, v = (rng.standard_normal((B, T, H, D)) for _ in range(3))
+    g = np.zeros((B, T, H, D))
+    beta = np.zeros((B, T, H))
+    S0 = rng.standard_normal((B, H, D, D))
+    do = rng.standard_normal((B, T, H, D))
+    dST = rng.standard_normal((B, H, D, D))
+    gr = kda_reference_backward(q, k, v, g, beta, do, dST, S0=S0, scale=scale, l2norm_qk=False)
+    np.testing.assert_allclose(gr["dq"], scale * np.einsum("bhcv,bthv->bthc", S0, do), rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(gr["dS0"], scale * np.einsum("bthc,bthv->bhcv", q, do) + dST,
+                               rtol=1e-13, atol=1e-14)
+    np.testing.assert_array_equal(gr["dk"], 0.0)
+    np.testing.assert_array_equal(gr["dv"], 0.0)
