@@ -17,7 +17,12 @@ from ._lib import (  # noqa: F401
     kda_conv_norm,
     kda_decode_raw,
     kda_decode_step,
+    backward_args,
+    kda_backward_workspace_bytes,
     kda_prefill,
+    kda_prefill_backward,
+    kda_prefill_backward_raw,
+    kda_validate_backward,
     kda_prefill_raw,
     kda_prefill_stage,
     kda_prefill_workspace_bytes,

@@ -63,6 +63,12 @@ class DecodeArgs(ctypes.Structure):
                 ("o_gate", _vp)]
 
 
+class BackwardArgs(ctypes.Structure):
+    _fields_ = [("fwd", PrefillArgs), ("dO", _vp), ("dS_T", _vp), ("dq", _vp), ("dk", _vp),
+                ("dv", _vp), ("dg", _vp), ("dbeta", _vp), ("dS0", _vp), ("dconv_w", _vp),
+                ("dconv_state", _vp)]
+
+
 class KdaError(RuntimeError):
     def __init__(self, status: int, where: str):
         self.status = int(status)
@@ -110,6 +116,12 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.kda_validate_decode.argtypes = [P(DecodeArgs)]
     lib.kda_decode_step.restype = ctypes.c_int
     lib.kda_decode_step.argtypes = [P(DecodeArgs), _vp]
+    lib.kda_validate_backward.restype = ctypes.c_int
+    lib.kda_validate_backward.argtypes = [P(BackwardArgs)]
+    lib.kda_backward_workspace_bytes.restype = ctypes.c_size_t
+    lib.kda_backward_workspace_bytes.argtypes = [P(BackwardArgs)]
+    lib.kda_prefill_backward.restype = ctypes.c_int
+    lib.kda_prefill_backward.argtypes = [P(BackwardArgs), _vp, ctypes.c_size_t, _vp]
     if lib.kda_abi_version() != ABI_VERSION:
         raise RuntimeError("libkda ABI version mismatch")
     if path is None:
@@ -346,3 +358,63 @@ def kda_decode_step(q, k, v, g, beta, S, conv_w=None, conv_state=None, *, scale=
 
 def kda_decode_raw(args: DecodeArgs, stream=None):
     _check(load().kda_decode_step(ctypes.byref(args), _stream(stream)), "kda_decode_step")
+
+
+# ------------------------------------------------------------------- backward
+def backward_args(fwd: PrefillArgs, do, dS_T, grads: dict) -> BackwardArgs:
+    a = BackwardArgs()
+    a.fwd = fwd
+    a.dO, a.dS_T = _ptr(do), _ptr(dS_T)
+    for n in ("dq", "dk", "dv", "dg", "dbeta", "dS0", "dconv_w", "dconv_state"):
+        setattr(a, n, _ptr(grads.get(n)))
+    return a
+
+
+def kda_validate_backward(args: BackwardArgs) -> int:
+    return int(load().kda_validate_backward(ctypes.byref(args)))
+
+
+def kda_backward_workspace_bytes(args: BackwardArgs) -> int:
+    return int(load().kda_backward_workspace_bytes(ctypes.byref(args)))
+
+
+def kda_prefill_backward(q, k, v, g, beta, conv_w=None, conv_state=None, S0=None, *, do,
+                         dS_T=None, chunk=64, scale=1.0, l2norm_qk=True, eps=1e-6, workspace=None,
+                         stream=None):
+    """Gradients of L = <o, do> + <S_T, dS_T> (the forward is recomputed).
+
+    Returns (grads, o, S_T): grads is a dict of float32 tensors dq, dk, dv, dg
+    [B, T, H, D], dbeta [B, T, H], dS0 [B, H, D, D], and with the convolution
+    dconv_w [3, H*D, 4] and dconv_state [B, 3, 3, H*D].
+    """
+    B, T, H, D = q.shape
+    dev = q.device
+    f32 = dict(dtype=torch.float32, device=dev)
+    o = torch.empty_like(q)
+    S_T = torch.empty(B, H, D, D, **f32)
+    cso = torch.empty(B, 3, 3, H * D, dtype=q.dtype, device=dev) if conv_w is not None else None
+    fwd = prefill_args(q, k, v, g, beta, conv_w, conv_state, S0, o, S_T, cso, chunk=chunk,
+                       scale=scale, l2norm_qk=l2norm_qk, eps=eps)
+    grads = dict(dq=torch.empty(B, T, H, D, **f32), dk=torch.empty(B, T, H, D, **f32),
+                 dv=torch.empty(B, T, H, D, **f32), dg=torch.empty(B, T, H, D, **f32),
+                 dbeta=torch.empty(B, T, H, **f32), dS0=torch.empty(B, H, D, D, **f32))
+    if conv_w is not None:
+        grads["dconv_w"] = torch.empty(3, H * D, 4, **f32)
+        grads["dconv_state"] = torch.empty(B, 3, 3, H * D, **f32)
+    a = backward_args(fwd, do, dS_T, grads)
+    _check(kda_validate_backward(a), "kda_prefill_backward")
+    need = kda_backward_workspace_bytes(a)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws = _ptr(workspace) if workspace is not None else None
+    nbytes = workspace.numel() if workspace is not None else 0
+    _check(load().kda_prefill_backward(ctypes.byref(a), ws, nbytes, _stream(stream)),
+           "kda_prefill_backward")
+    return grads, o, S_T
+
+
+def kda_prefill_backward_raw(args: BackwardArgs, workspace, stream=None):
+    ws = _ptr(workspace) if workspace is not None else None
+    nbytes = workspace.numel() if workspace is not None else 0
+    _check(load().kda_prefill_backward(ctypes.byref(args), ws, nbytes, _stream(stream)),
+           "kda_prefill_backward")

@@ -233,7 +233,17 @@ static kda::SeqTables seq_tables(const kda_prefill_args* a, void* ws) {
   return t;
 }
 
-static kda_status run_stage(const kda_prefill_args* a, void* ws, int stage, hipStream_t st) {
+// Extra outputs of the forward stages when they run for the backward pass.
+struct BwdFwdOut {
+  float* y;
+  float* gam;
+  float* beta;
+  float* tT;
+  float* ckS;
+};
+
+static kda_status run_stage(const kda_prefill_args* a, void* ws, int stage, hipStream_t st,
+                            const BwdFwdOut* bo = nullptr) {
   const bool fp32 = a->io == KDA_FP32;
   PrefillSizes sz;
   prefill_sizes(a, sz);
@@ -269,6 +279,12 @@ static kda_status run_stage(const kda_prefill_args* a, void* ws, int stage, hipS
       p.dt_bias = a->dt_bias;
       p.beta_logits = (a->flags & KDA_FLAG_BETA_LOGITS) ? 1 : 0;
       p.seqs = seqs;
+      if (bo != nullptr) {
+        p.y_out = bo->y;
+        p.gam_out = bo->gam;
+        p.beta_out = bo->beta;
+        p.t_out = bo->tT;
+      }
       return hip_status(kda::launch_prep(p, a->D, a->chunk, fp32, st));
     }
     case KDA_STAGE_STATE: {
@@ -287,6 +303,7 @@ static kda_status run_stage(const kda_prefill_args* a, void* ws, int stage, hipS
       p.o_gate = a->o_gate;
       p.o_norm_w = a->o_norm_w;
       p.o_norm_eps = a->o_norm_eps;
+      p.ckpt = bo != nullptr ? bo->ckS : nullptr;
       return hip_status(kda::launch_state(p, a->D, a->chunk, fp32, cfg.vb, cfg.threads, cfg.fused,
                                           st));
     }
@@ -453,6 +470,198 @@ kda_status kda_decode_step(const kda_decode_args* a, void* stream) {
   p.o_norm_w = a->o_norm_w;
   p.o_norm_eps = a->o_norm_eps;
   return hip_status(kda::launch_decode(p, a->D, a->io == KDA_FP32, static_cast<hipStream_t>(stream)));
+}
+
+// ------------------------------------------------------------------- backward
+}  // extern "C"
+
+namespace {
+
+// Workspace of the backward pass: the forward workspace, then float32 buffers
+// (see kda_layout.h), each 256-byte aligned.
+struct BwdLayout {
+  size_t tT, y, gam, beta, ckS, ckdS, dU, dQL, dW, dKt, dP, dLC, dBk, dBv, dA, dy, dbp, dcp;
+  size_t bytes;
+  size_t nfront;  // front-end workgroups per (b, h)
+};
+
+BwdLayout bwd_layout(const kda_backward_args* a) {
+  const kda_prefill_args* f = &a->fwd;
+  BwdLayout L{};
+  PrefillSizes sz;
+  prefill_sizes(f, sz);
+  const size_t nrec = (size_t)f->B * f->H * sz.NT;
+  const size_t C = (size_t)f->chunk, D = (size_t)f->D;
+  const size_t x = (size_t)f->B * f->T * f->H * D;  // elements of one [B][T][H][D] tensor
+  const size_t bth = (size_t)f->B * f->T * f->H;
+  size_t off = kda::round_up(ws_layout(f).bytes, 256);
+  auto take = [&](size_t floats) {
+    const size_t o = off;
+    off = kda::round_up(off + floats * 4, 256);
+    return o;
+  };
+  L.tT = take(nrec * C * C);
+  L.y = take(3 * x);
+  L.gam = take(x);
+  L.beta = take(bth);
+  L.ckS = take(nrec * D * D);
+  L.ckdS = take(nrec * D * D);
+  L.dU = take(nrec * D * C);
+  L.dQL = take(nrec * C * D);
+  L.dW = take(nrec * C * D);
+  L.dKt = take(nrec * C * D);
+  L.dP = take(nrec * C * C);
+  L.dLC = take(nrec * D);
+  L.dBk = take(nrec * C * D);
+  L.dBv = take(nrec * C * D);
+  L.dA = take(nrec * C * C);
+  L.dy = take(3 * x);
+  L.dbp = take((D < 32 ? 1 : D / 32) * bth);
+  L.nfront = kda::bwd_front_blocks(f->T, f->D);
+  L.dcp = take(f->conv_k > 0 ? (size_t)f->B * L.nfront * 3 * f->H * D * 4 : 0);
+  L.bytes = off;
+  return L;
+}
+
+// Every buffer of a backward call with its byte size: 13 inputs (and forward
+// outputs), 8 gradient outputs.
+void bwd_spans(const kda_backward_args* a, Span (&ins)[13], Span (&outs)[8]) {
+  const kda_prefill_args* f = &a->fwd;
+  PrefillSizes s;
+  prefill_sizes(f, s);
+  const size_t g = (size_t)f->B * f->T * f->H * f->D * 4, gb = (size_t)f->B * f->T * f->H * 4;
+  const size_t ck = f->conv_k > 0 ? (size_t)f->conv_k - 1 : 0;
+  const size_t dcs = (size_t)f->B * 3 * ck * f->H * f->D * 4;
+  const Span i[13] = {span(f->q, s.x), span(f->k, s.x), span(f->v, s.x), span(f->g, s.x),
+                      span(f->beta, s.bta), span(f->conv_w, s.cw), span(f->conv_state_in, s.cst),
+                      span(f->S0, s.state), span(f->o, s.x), span(f->S_T, s.state),
+                      span(f->conv_state_out, s.cst), span(a->dO, s.x), span(a->dS_T, s.state)};
+  const Span o[8] = {span(a->dq, g), span(a->dk, g), span(a->dv, g), span(a->dg, g),
+                     span(a->dbeta, gb), span(a->dS0, s.state), span(a->dconv_w, s.cw),
+                     span(a->dconv_state, dcs)};
+  for (int k = 0; k < 13; ++k) ins[k] = i[k];
+  for (int k = 0; k < 8; ++k) outs[k] = o[k];
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_validate_backward(const kda_backward_args* a) {
+  if (a == nullptr) return KDA_ERR_NULL;
+  const kda_prefill_args* f = &a->fwd;
+  if (kda_status e = kda_validate_prefill(f); e != KDA_OK) return e;
+  if (f->cu_seqlens != nullptr || f->A_log != nullptr || f->o_norm_w != nullptr ||
+      f->o_gate != nullptr || (f->flags & KDA_FLAG_BETA_LOGITS) != 0)
+    return KDA_ERR_UNSUPPORTED;
+  if (f->io == KDA_FP32 && f->D == 128) return KDA_ERR_UNSUPPORTED;
+  const bool need = f->T > 0;
+  if (need && (!a->dO || !a->dq || !a->dk || !a->dv || !a->dg || !a->dbeta)) return KDA_ERR_NULL;
+  if (f->conv_k > 0 && !a->dconv_w) return KDA_ERR_NULL;
+  if (f->conv_k == 0 && (a->dconv_w || a->dconv_state)) return KDA_ERR_NULL;
+  for (const void* p : std::initializer_list<const void*>{a->dO, a->dS_T, a->dq, a->dk, a->dv, a->dg,
+                                                          a->dbeta, a->dS0, a->dconv_w, a->dconv_state})
+    if (p && !aligned16(p)) return KDA_ERR_ALIGN;
+  Span ins[13], outs[8];
+  bwd_spans(a, ins, outs);
+  for (int i = 0; i < 8; ++i) {
+    for (int j = 0; j < 13; ++j)
+      if (overlaps(outs[i], ins[j])) return KDA_ERR_ALIAS;
+    for (int j = 0; j < 8; ++j)
+      if (i != j && overlaps(outs[i], outs[j])) return KDA_ERR_ALIAS;
+  }
+  return KDA_OK;
+}
+
+size_t kda_backward_workspace_bytes(const kda_backward_args* a) {
+  if (kda_validate_backward(a) != KDA_OK) return 0;
+  if (a->fwd.T == 0) return 0;
+  return bwd_layout(a).bytes;
+}
+
+kda_status kda_prefill_backward(const kda_backward_args* a, void* ws, size_t ws_bytes, void* stream) {
+  if (kda_status e = kda_validate_backward(a); e != KDA_OK) return e;
+  const kda_prefill_args* f = &a->fwd;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool fp32 = f->io == KDA_FP32;
+  PrefillSizes sz;
+  prefill_sizes(f, sz);
+  if (f->T == 0) {
+    // nothing flows: dS0 = dS_T; the filter and history gradients are zero
+    if (a->dS0 != nullptr &&
+        kda::launch_copy_state(a->dS_T, a->dS0, (size_t)f->B * f->H * f->D * f->D, st) != hipSuccess)
+      return KDA_ERR_HIP;
+    if (a->dconv_w != nullptr &&
+        kda::launch_copy_state(nullptr, a->dconv_w, (size_t)3 * f->H * f->D * f->conv_k, st) != hipSuccess)
+      return KDA_ERR_HIP;
+    if (a->dconv_state != nullptr &&
+        kda::launch_copy_state(nullptr, a->dconv_state, (size_t)f->B * 3 * 3 * f->H * f->D, st) != hipSuccess)
+      return KDA_ERR_HIP;
+    // the run_stage calls below still hand S_T and the conv state through
+    for (int stage = KDA_STAGE_PREP; stage <= KDA_STAGE_OUTPUT; ++stage)
+      if (kda_status e = run_stage(f, ws, stage, st); e != KDA_OK) return e;
+    return KDA_OK;
+  }
+  const BwdLayout L = bwd_layout(a);
+  if (ws == nullptr || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0 || ws_bytes < L.bytes)
+    return KDA_ERR_WORKSPACE;
+  {
+    const Span w = span(ws, L.bytes);
+    Span ins[13], outs[8];
+    bwd_spans(a, ins, outs);
+    for (const Span& x : ins)
+      if (overlaps(w, x)) return KDA_ERR_ALIAS;
+    for (const Span& x : outs)
+      if (overlaps(w, x)) return KDA_ERR_ALIAS;
+  }
+  char* wsb = static_cast<char*>(ws);
+  auto F = [&](size_t off) { return reinterpret_cast<float*>(wsb + off); };
+  // forward in backward mode
+  BwdFwdOut bo{F(L.y), F(L.gam), F(L.beta), F(L.tT), F(L.ckS)};
+  for (int stage = KDA_STAGE_PREP; stage <= KDA_STAGE_OUTPUT; ++stage)
+    if (kda_status e = run_stage(f, ws, stage, st, &bo); e != KDA_OK) return e;
+  // backward
+  kda::BwdLaunch B{};
+  const char* recs = wsb + ws_layout(f).records;
+  B.walk.ws = recs;
+  B.walk.dO = a->dO;
+  B.walk.dS_T = a->dS_T;
+  B.walk.dS0 = a->dS0;
+  B.walk.dU = F(L.dU);
+  B.walk.ckdS = F(L.ckdS);
+  B.walk.B = f->B; B.walk.T = f->T; B.walk.H = f->H; B.walk.NT = sz.NT;
+  B.prod.ws = recs;
+  B.prod.dO = a->dO;
+  B.prod.ckS = F(L.ckS);
+  B.prod.ckdS = F(L.ckdS);
+  B.prod.dU = F(L.dU);
+  B.prod.dQL = F(L.dQL); B.prod.dW = F(L.dW); B.prod.dKt = F(L.dKt); B.prod.dP = F(L.dP);
+  B.prod.dLC = F(L.dLC);
+  B.prod.B = f->B; B.prod.T = f->T; B.prod.H = f->H; B.prod.NT = sz.NT;
+  B.tside.tT = F(L.tT);
+  B.tside.y = F(L.y); B.tside.gam = F(L.gam); B.tside.beta = F(L.beta);
+  B.tside.dW = F(L.dW); B.tside.dU = F(L.dU);
+  B.tside.dBk = F(L.dBk); B.tside.dBv = F(L.dBv); B.tside.dA = F(L.dA);
+  B.tside.B = f->B; B.tside.T = f->T; B.tside.H = f->H; B.tside.NT = sz.NT;
+  B.pair.y = F(L.y); B.pair.gam = F(L.gam); B.pair.beta = F(L.beta);
+  B.pair.dA = F(L.dA); B.pair.dP = F(L.dP); B.pair.dQL = F(L.dQL); B.pair.dKt = F(L.dKt);
+  B.pair.dLC = F(L.dLC); B.pair.dBk = F(L.dBk); B.pair.dBv = F(L.dBv);
+  B.pair.dy = F(L.dy); B.pair.dg = a->dg; B.pair.dbeta_part = F(L.dbp);
+  B.pair.B = f->B; B.pair.T = f->T; B.pair.H = f->H; B.pair.NT = sz.NT;
+  B.front.q = f->q; B.front.k = f->k; B.front.v = f->v;
+  B.front.conv_w = f->conv_k > 0 ? f->conv_w : nullptr;
+  B.front.conv_state_in = f->conv_k > 0 ? f->conv_state_in : nullptr;
+  B.front.dy = F(L.dy);
+  B.front.dq = a->dq; B.front.dk = a->dk; B.front.dv = a->dv;
+  B.front.dconv_part = f->conv_k > 0 ? F(L.dcp) : nullptr;
+  B.front.dconv_state = a->dconv_state;
+  B.front.B = f->B; B.front.T = f->T; B.front.H = f->H;
+  B.front.l2 = (f->flags & KDA_FLAG_L2NORM_QK) ? 1 : 0;
+  B.front.eps = f->l2_eps;
+  B.front.scale = f->scale;
+  B.dbeta = a->dbeta;
+  B.dconv_w = a->dconv_w;
+  return hip_status(kda::launch_backward(B, f->D, f->chunk, fp32, st));
 }
 
 }  // extern "C"

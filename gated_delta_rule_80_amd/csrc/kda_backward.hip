@@ -1,0 +1,969 @@
+// Backward pass of the KDA prefill: the gradients of L = <o, dO> + <S_T, dS_T>
+// with respect to the raw q, k, v, the log-decay g, beta, S0 and the conv filters
+// and history.
+//
+// The forward is recomputed by the forward kernels in backward mode (chunk
+// records, the front end's outputs, T^T per chunk, and the state at every chunk
+// start).  With, per chunk (Gamma the chunk-local cumulative log-decay, Lambda =
+// exp(Gamma), C tokens):
+//   A_ij = beta_i sum_c k_ic k_jc exp(Gamma_ic - Gamma_jc) (j < i),  T = (I + A)^-1
+//   Bk = diag(beta) (K * Lambda),  Bv = diag(beta) V,  W = T Bk,  U~ = T Bv
+//   QL = Q' * Lambda (Q' = scale * q_hat),  P_ij = sum_c Q'_ic k_jc exp(Gamma_ic - Gamma_jc) (j <= i)
+//   Ktil = K * exp(Gamma_C - Gamma),  LC = exp(Gamma_C)
+//   U = U~ - W S,  O = QL S + P U,  S' = Diag(LC) S + Ktil^T U
+// the backward is
+//   reverse walk:  dU = P^T dO + Ktil dS',   dS = Diag(LC) dS' + QL^T dO - W^T dU
+//   per chunk:     dQL = dO S^T,  dW = -dU S^T,  dKtil = U dS'^T,  dP = (dO U^T) on j <= i,
+//                  dLC = rowsum(dS' * S),  dT = dW Bk^T + dU Bv^T,  dA = -T^T dT T^T (j < i),
+//                  dBk = T^T dW,  dBv = T^T dU
+// then the element terms and the pair terms of A and P (exp(Gamma_i - Gamma_j)
+// evaluated per pair, never split), dGamma to dg by a reverse running sum over the
+// chunk, and finally the front end in reverse (L2 norm, SiLU, convolution).
+#include "kda_convnorm.h"
+#include "kda_device.h"
+#include "kda_launch.h"
+#include "kda_layout.h"
+
+namespace kda {
+
+// ----------------------------------------------------------------- reverse walk
+// The part of a forward record the reverse walk reads, as an LDS image (byte
+// offsets): W [C][D], QL [C][D], KT [D][C], P [C][C] (swizzled as in the
+// forward walk), LC [D] float.
+template <int D, int C, typename E>
+struct BwdImage {
+  static constexpr int ES = (int)sizeof(E);
+  static constexpr int W = 0;
+  static constexpr int QL = W + C * D * ES;
+  static constexpr int KT = QL + C * D * ES;
+  static constexpr int P = KT + D * C * ES;
+  static constexpr int LC = P + C * C * ES;
+  static constexpr int BYTES = LC + D * 4;
+  static constexpr int CHUNKS = BYTES / 16;
+  static_assert(BYTES % 16 == 0, "whole 16-byte chunks");
+};
+
+// One workgroup per (b, h, block of VB value columns); the D x VB block of dS
+// stays in matrix-core accumulators, walking the chunks from the last to the
+// first.  Per chunk, in the NT products C[i][j] = sum_k A[i][k] B[j][k]:
+//   dU (t, v):  A = P^T rows t (P's column t, k = j >= t), B = dO^T rows v;
+//               + A = Ktil rows t (KT's column t, k = c),  B = dS'^T rows v
+//   dS (c, v):  A = QL^T rows c (QL's column c, k = t),   B = dO^T rows v;
+//               - A = W^T rows c,                         B = dU^T rows v
+template <int D, int C, int VB, typename IO, typename E, int NT>
+__global__ __launch_bounds__(NT, 1) void kda_bwd_walk_kernel(BwdWalkParams p) {
+  constexpr int NW = NT / 64;
+  constexpr int PE = 16 / (int)sizeof(E);
+  constexpr int ES = (int)sizeof(E);
+  constexpr int LS = D + PE;  // sS rows: value column v, k = key channel c
+  constexpr int LU = C + PE;  // sDU / sDO rows: value column v, k = token t
+  constexpr int NV = D / VB;
+  constexpr int VT = VB / 16;
+  constexpr int RT = C / 16;
+  constexpr int CT = D / 16;
+  static_assert(NW % RT == 0, "every unit of a wave has the same t-tile");
+  static_assert(CT <= NW || CT % NW == 0, "every unit of a wave has one of NCTW c-tiles");
+  constexpr int NU = (RT * VT + NW - 1) / NW;
+  constexpr int NS = (CT * VT + NW - 1) / NW;
+  constexpr int CTW = CT < NW ? CT : NW;
+  constexpr int NCTW = CT > NW ? CT / NW : 1;
+  constexpr bool FULL_U = (RT * VT) % NW == 0;
+  constexpr bool FULL_S = (CT * VT) % NW == 0;
+  constexpr RecordLayout RL = record_layout(C, D, sizeof(E));
+  using IMG = BwdImage<D, C, E>;
+  __shared__ __attribute__((aligned(16))) char img[IMG::BYTES];
+  __shared__ __attribute__((aligned(16))) E sS[VB * LS];
+  __shared__ __attribute__((aligned(16))) E sDU[VB * LU];
+  __shared__ __attribute__((aligned(16))) E sDO[2][VB * LU];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, g4 = lane >> 4;
+  const int vblk = blockIdx.x % NV;
+  const int bh = blockIdx.x / NV;
+  const int h = bh % p.H, b = bh / p.H;
+  const int vb0 = vblk * VB;
+  const size_t rec0 = (size_t)bh * p.NT;
+  const size_t HD = (size_t)p.H * D;
+
+  const int R = wave % RT;
+  const bool has_u = FULL_U || wave < RT * VT;
+  const int t_row = 16 * R + r;  // row of dU (token) this lane's A fragments hold
+
+  // ---- copy of a record's image (the same source offsets for every chunk)
+  constexpr int ITERS = (IMG::CHUNKS + NT - 1) / NT;
+  uint32_t src_off[ITERS];
+#pragma unroll
+  for (int it = 0; it < ITERS; ++it) {
+    constexpr int RCD = D * ES / 16;
+    constexpr int RCC = C * ES / 16;
+    const int idx = it * NT + tid;
+    const int byte = idx * 16;
+    size_t off;
+    if (byte < IMG::KT) {
+      const bool isql = byte >= IMG::QL;
+      const int ci = idx - (isql ? IMG::QL / 16 : 0);
+      const int row = ci / RCD, cs = ci % RCD;
+      off = (size_t)(isql ? RL.ql : RL.w) * ES + (size_t)(row * RCD + (cs ^ (row & (RCD - 1)))) * 16;
+    } else if (byte < IMG::LC) {
+      const bool isp = byte >= IMG::P;
+      const int ci = idx - (isp ? IMG::P : IMG::KT) / 16;
+      const int row = ci / RCC, cs = ci % RCC;
+      off = (size_t)(isp ? RL.p : RL.kt) * ES + (size_t)(row * RCC + (cs ^ (row & (RCC - 1)))) * 16;
+    } else {
+      off = RL.lc_bytes + (size_t)(idx - IMG::LC / 16) * 16;
+    }
+    src_off[it] = (uint32_t)off;
+  }
+  auto issue_copy = [&](int n) {
+    const char* recp = p.ws + (rec0 + n) * RL.bytes;
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+      if (it * NT + tid < IMG::CHUNKS)
+        __builtin_amdgcn_global_load_lds(
+            (const glb_void_t*)(recp + src_off[it]),
+            (lds_void_t*)(img + (size_t)(it * NT + 64 * wave) * 16), 16, 0, 0);
+    }
+  };
+
+  // ---- dO of a chunk: 8 consecutive value columns of one token per piece
+  constexpr int DOP = C * VB / 8;                // pieces per chunk
+  constexpr int DOIT = (DOP + NT - 1) / NT;
+  Raw8<IO> dor[DOIT];
+  auto load_do = [&](int n) {
+#pragma unroll
+    for (int it = 0; it < DOIT; ++it) {
+      const int idx = it * NT + tid;
+      const int tt = idx / (VB / 8), v8 = idx % (VB / 8);
+      const int t = n * C + tt;
+      if (idx < DOP && t < p.T)
+        dor[it].load(static_cast<const IO*>(p.dO) + ((size_t)b * p.T + t) * HD + (size_t)h * D + vb0 +
+                     8 * v8);
+      else
+        dor[it] = Raw8<IO>{};
+    }
+  };
+  auto stage_do = [&](int n) {
+    E* dst = sDO[n & 1];
+#pragma unroll
+    for (int it = 0; it < DOIT; ++it) {
+      const int idx = it * NT + tid;
+      if (idx < DOP) {
+        const int tt = idx / (VB / 8), v8 = idx % (VB / 8);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) dst[(8 * v8 + m) * LU + tt] = from_f32<E>(dor[it][m]);
+      }
+    }
+  };
+
+  // ---- dS: initial value dS_T (or zero), staged to LDS as the B operand
+  f32x4 accS[NS];
+  const size_t sbase = (size_t)bh * D * D;
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const int u = wave + NW * i;
+    accS[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if ((FULL_S || u < CT * VT) && p.dS_T != nullptr) {
+      const int Ct = u % CT, Vt = u / CT;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        accS[i][e] = p.dS_T[sbase + (size_t)(16 * Ct + 4 * g4 + e) * D + vb0 + 16 * Vt + r];
+    }
+  }
+  auto stage_state = [&]() {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int u = wave + NW * i;
+      if (FULL_S || u < CT * VT) {
+        const int Ct = u % CT, Vt = u / CT;
+        store4(&sS[(16 * Vt + r) * LS + 16 * Ct + 4 * g4], accS[i][0], accS[i][1], accS[i][2],
+               accS[i][3]);
+      }
+    }
+  };
+  stage_state();
+
+  const E* iW = reinterpret_cast<const E*>(img + IMG::W);
+  const E* iQL = reinterpret_cast<const E*>(img + IMG::QL);
+  const E* iKT = reinterpret_cast<const E*>(img + IMG::KT);
+  const E* iP = reinterpret_cast<const E*>(img + IMG::P);
+  const float* iLC = reinterpret_cast<const float*>(img + IMG::LC);
+
+  if (p.NT > 0) {
+    issue_copy(p.NT - 1);
+    load_do(p.NT - 1);
+  }
+  for (int n = p.NT - 1; n >= 0; --n) {
+    __builtin_amdgcn_s_waitcnt(0);  // image and dO of chunk n
+    stage_do(n);
+    lds_barrier();
+    // the gradient of this chunk's end state, for the per-chunk products
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int u = wave + NW * i;
+      if (FULL_S || u < CT * VT) {
+        const int Ct = u % CT, Vt = u / CT;
+        *reinterpret_cast<f32x4*>(p.ckdS + (rec0 + n) * D * D + (size_t)(vb0 + 16 * Vt + r) * D +
+                                  16 * Ct + 4 * g4) = accS[i];
+      }
+    }
+    // ---- fragments of this chunk
+    RowFrag<E, C> fpt;   // P^T row t_row
+    RowFrag<E, D> fkt;   // Ktil row t_row
+    RowFrag<E, C> fqlt[NCTW], fwt[NCTW];
+    f32x4 flc[NCTW];
+    if (has_u) {
+      load_swz_t<C, C>(fpt, iP, t_row, g4);
+      fpt.mask_below(t_row, g4);  // P[j][t] vanishes for j < t
+      load_swz_t<D, C>(fkt, iKT, t_row, g4);
+    }
+#pragma unroll
+    for (int jj = 0; jj < NCTW; ++jj) {
+      const int Ct = (wave % CTW) + CTW * jj;
+      load_swz_t<C, D>(fqlt[jj], iQL, 16 * Ct + r, g4);
+      load_swz_t<C, D>(fwt[jj], iW, 16 * Ct + r, g4);
+      flc[jj] = *reinterpret_cast<const f32x4*>(iLC + 16 * Ct + 4 * g4);
+    }
+    lds_barrier();  // every wave holds its fragments: the image may be overwritten
+    if (n > 0) {
+      issue_copy(n - 1);
+      load_do(n - 1);
+    }
+    const E* sdo = sDO[n & 1];
+    // ---- dU = P^T dO + Ktil dS'
+#pragma unroll
+    for (int i = 0; i < NU; ++i) {
+      const int u = wave + NW * i;
+      if (FULL_U || u < RT * VT) {
+        const int Vt = u / RT;
+        RowFrag<E, C> fo;
+        fo.load(sdo + (16 * Vt + r) * LU, g4);
+        RowFrag<E, D> fs;
+        fs.load(sS + (16 * Vt + r) * LS, g4);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        mma<C>(acc, fpt, fo);
+        mma<D>(acc, fkt, fs);
+        store4(&sDU[(16 * Vt + r) * LU + 16 * R + 4 * g4], acc[0], acc[1], acc[2], acc[3]);
+        *reinterpret_cast<f32x4*>(p.dU + (rec0 + n) * D * C + (size_t)(vb0 + 16 * Vt + r) * C +
+                                  16 * R + 4 * g4) = acc;
+      }
+    }
+    lds_barrier();  // sDU complete; every read of sS for this chunk is done
+    // ---- dS = Diag(LC) dS' + QL^T dO - W^T dU
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int u = wave + NW * i;
+      if (FULL_S || u < CT * VT) {
+        const int Vt = u / CT;
+        const int jj = i % NCTW;
+        RowFrag<E, C> fo, fu;
+        fo.load(sdo + (16 * Vt + r) * LU, g4);
+        fu.load(sDU + (16 * Vt + r) * LU, g4);
+        f32x4 neg = {0.f, 0.f, 0.f, 0.f};
+        mma<C>(neg, fwt[jj], fu);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) accS[i][e] = accS[i][e] * flc[jj][e] - neg[e];
+        mma<C>(accS[i], fqlt[jj], fo);
+      }
+    }
+    stage_state();
+  }
+  if (p.dS0 != nullptr) {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int u = wave + NW * i;
+      if (FULL_S || u < CT * VT) {
+        const int Ct = u % CT, Vt = u / CT;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          p.dS0[sbase + (size_t)(16 * Ct + 4 * g4 + e) * D + vb0 + 16 * Vt + r] = accS[i][e];
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------- per-chunk state products
+// One 256-thread workgroup per chunk record.  In the NT products
+// C[i][j] = sum_k A[i][k] B[j][k] (both operands k-contiguous in LDS, bf16, float
+// accumulation):
+//   U    = U~ - W S:   A = W rows t (record),   B = S^T rows v
+//   dQL  = dO S^T:     A = dO rows t,           B = S rows c
+//   dW   = -dU S^T:    A = dU rows t,           B = S rows c
+//   dKt  = U dS'^T:    A = U rows t,            B = dS' rows c
+//   dP   = dO U^T:     A = dO rows i,           B = U rows j      (j <= i)
+//   dLC  = rowsum(dS' * S)  in float32 from the checkpoints.
+template <int D, int C, typename IO, typename E>
+__global__ __launch_bounds__(256) void kda_bwd_prod_kernel(BwdProdParams p) {
+  constexpr int PE = 16 / (int)sizeof(E);
+  constexpr int LD = D + PE;  // rows of D elements
+  constexpr int CT = D / 16, RT = C / 16;
+  constexpr RecordLayout RL = record_layout(C, D, sizeof(E));
+  __shared__ __attribute__((aligned(16))) E sS[D * LD];   // S rows c, k = v
+  __shared__ __attribute__((aligned(16))) E sX[D * LD];   // S^T rows v, k = c; later dS' rows c
+  __shared__ __attribute__((aligned(16))) E sU[C * LD];   // U rows t, k = v
+  __shared__ __attribute__((aligned(16))) E sDO[C * LD];  // dO rows t
+  __shared__ __attribute__((aligned(16))) E sDU[C * LD];  // dU rows t
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, g4 = lane >> 4;
+  const int rec = blockIdx.x;
+  const int n = rec % p.NT;
+  const int bh = rec / p.NT;
+  const int h = bh % p.H, b = bh / p.H;
+  const size_t HD = (size_t)p.H * D;
+  const float* ckS = p.ckS + (size_t)rec * D * D;    // [v][c]
+  const float* ckdS = p.ckdS + (size_t)rec * D * D;  // [v][c]
+  const float* dUt = p.dU + (size_t)rec * D * C;     // [v][t]
+  const char* recp = p.ws + (size_t)rec * RL.bytes;
+  const E* gW = reinterpret_cast<const E*>(recp) + RL.w;
+  const E* gU = reinterpret_cast<const E*>(recp) + RL.u;
+
+  // ---- staging: S^T as is, S transposed, dO, dU transposed
+  for (int it = tid; it < D * D / 4; it += 256) {
+    const int v = it / (D / 4), c4 = 4 * (it % (D / 4));
+    const f32x4 x = *reinterpret_cast<const f32x4*>(ckS + (size_t)v * D + c4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sX[v * LD + c4 + e] = from_f32<E>(x[e]);
+      sS[(c4 + e) * LD + v] = from_f32<E>(x[e]);
+    }
+  }
+  for (int it = tid; it < C * D / 8; it += 256) {
+    const int t = it / (D / 8), c8 = 8 * (it % (D / 8));
+    const int tg = n * C + t;
+    float x[8];
+    if (tg < p.T)
+      load8(static_cast<const IO*>(p.dO) + ((size_t)b * p.T + tg) * HD + (size_t)h * D + c8, x);
+    else
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sDO[t * LD + c8 + e] = from_f32<E>(x[e]);
+  }
+  for (int it = tid; it < D * C / 4; it += 256) {
+    const int v = it / (C / 4), t4 = 4 * (it % (C / 4));
+    const f32x4 x = *reinterpret_cast<const f32x4*>(dUt + (size_t)v * C + t4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sDU[(t4 + e) * LD + v] = from_f32<E>(x[e]);
+  }
+  __syncthreads();
+
+  // ---- U = U~ - W S  (tiles (t, v))
+  for (int tile = wave; tile < RT * CT; tile += 4) {
+    const int Rt = tile / CT, Vt = tile % CT;
+    RowFrag<E, D> fa, fb;
+    fa.load(gW + (size_t)(16 * Rt + r) * D, g4);
+    fb.load(sX + (16 * Vt + r) * LD, g4);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    mma<D>(acc, fa, fb);
+    // U~ in fragment order: tile (t-tile, v-tile) of 64 lanes x 4 values
+    const E* up = gU + ((size_t)(Rt * CT + Vt) * 64 + lane) * 4;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      sU[(16 * Rt + 4 * g4 + e) * LD + 16 * Vt + r] = from_f32<E>(to_f32(up[e]) - acc[e]);
+  }
+  __syncthreads();  // U complete; S^T no longer needed
+  for (int it = tid; it < D * D / 4; it += 256) {
+    const int v = it / (D / 4), c4 = 4 * (it % (D / 4));
+    const f32x4 x = *reinterpret_cast<const f32x4*>(ckdS + (size_t)v * D + c4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sX[(c4 + e) * LD + v] = from_f32<E>(x[e]);
+  }
+  if (tid < D) {
+    float acc = 0.f;
+    for (int v = 0; v < D; ++v) acc = fmaf(ckdS[(size_t)v * D + tid], ckS[(size_t)v * D + tid], acc);
+    p.dLC[(size_t)rec * D + tid] = acc;
+  }
+  __syncthreads();
+
+  // ---- dQL, dW, dKt: tiles (t, c); dP: tiles (i, j) with j <= i
+  float* dQL = p.dQL + (size_t)rec * C * D;
+  float* dW = p.dW + (size_t)rec * C * D;
+  float* dKt = p.dKt + (size_t)rec * C * D;
+  float* dP = p.dP + (size_t)rec * C * C;
+  for (int tile = wave; tile < RT * CT; tile += 4) {
+    const int Rt = tile / CT, Ct = tile % CT;
+    RowFrag<E, D> fdo, fdu, fu, fs, fds;
+    fdo.load(sDO + (16 * Rt + r) * LD, g4);
+    fdu.load(sDU + (16 * Rt + r) * LD, g4);
+    fu.load(sU + (16 * Rt + r) * LD, g4);
+    fs.load(sS + (16 * Ct + r) * LD, g4);
+    fds.load(sX + (16 * Ct + r) * LD, g4);
+    f32x4 aq = {0.f, 0.f, 0.f, 0.f}, aw = aq, ak = aq;
+    mma<D>(aq, fdo, fs);
+    mma<D>(aw, fdu, fs);
+    mma<D>(ak, fu, fds);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const size_t o = (size_t)(16 * Rt + 4 * g4 + e) * D + 16 * Ct + r;
+      dQL[o] = aq[e];
+      dW[o] = -aw[e];
+      dKt[o] = ak[e];
+    }
+  }
+  for (int tile = wave; tile < RT * RT; tile += 4) {
+    const int It = tile / RT, Jt = tile % RT;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (Jt <= It) {
+      RowFrag<E, D> fa, fb;
+      fa.load(sDO + (16 * It + r) * LD, g4);
+      fb.load(sU + (16 * Jt + r) * LD, g4);
+      mma<D>(acc, fa, fb);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 16 * It + 4 * g4 + e, j = 16 * Jt + r;
+      dP[(size_t)i * C + j] = j <= i ? acc[e] : 0.f;
+    }
+  }
+}
+
+// ------------------------------------------------------------ T-side products
+// One 256-thread workgroup per chunk record, float32 matrix-core products
+// (16x16x4, one element per lane and step, so operands read along either index):
+//   dT = dW Bk^T + dU Bv^T   (j <= i),   Y = dT T^T,   dA = -T^T Y   (j < i)
+//   dBk = T^T dW,   dBv = T^T dU
+// Bk = beta K Lambda and Bv = beta V are rebuilt from the front end's outputs.
+template <int D, int C, typename E>
+__global__ __launch_bounds__(256) void kda_bwd_t_kernel(BwdTParams p) {
+  constexpr int LD = D + 4;                  // float rows of D
+  constexpr int LC = C + 4;                  // float rows of C
+  constexpr int LB = D + 16 / (int)sizeof(E);  // E rows of D
+  constexpr int CT = D / 16, RT = C / 16;
+  constexpr int BKY = (C * LB * (int)sizeof(E) > C * LC * 4) ? C * LB * (int)sizeof(E) : C * LC * 4;
+  __shared__ __attribute__((aligned(16))) float sdW[C * LD];
+  __shared__ __attribute__((aligned(16))) float sdU[C * LD];
+  __shared__ __attribute__((aligned(16))) float sTt[C * LC];
+  __shared__ __attribute__((aligned(16))) float sdT[C * LC];
+  __shared__ __attribute__((aligned(16))) char sBkY[BKY];  // Bk [C][LB] E, later Y [C][LC] float
+  __shared__ __attribute__((aligned(16))) E sBv[C * LB];
+  E* sBk = reinterpret_cast<E*>(sBkY);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, g4 = lane >> 4;
+  const int rec = blockIdx.x;
+  const int n = rec % p.NT;
+  const int bh = rec / p.NT;
+  const int h = bh % p.H, b = bh / p.H;
+  const size_t HD = (size_t)p.H * D;
+  const size_t plane = (size_t)p.B * p.T * HD;
+
+  const float* gdW = p.dW + (size_t)rec * C * D;
+  const float* gdUt = p.dU + (size_t)rec * D * C;  // [v][t]
+  const float* gTt = p.tT + (size_t)rec * C * C;
+  for (int it = tid; it < C * D / 4; it += 256) {
+    const int t = it / (D / 4), c4 = 4 * (it % (D / 4));
+    *reinterpret_cast<f32x4*>(&sdW[t * LD + c4]) = *reinterpret_cast<const f32x4*>(gdW + (size_t)t * D + c4);
+  }
+  for (int it = tid; it < D * C / 4; it += 256) {
+    const int v = it / (C / 4), t4 = 4 * (it % (C / 4));
+    const f32x4 x = *reinterpret_cast<const f32x4*>(gdUt + (size_t)v * C + t4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sdU[(t4 + e) * LD + v] = x[e];
+  }
+  for (int it = tid; it < C * C / 4; it += 256) {
+    const int j = it / (C / 4), i4 = 4 * (it % (C / 4));
+    *reinterpret_cast<f32x4*>(&sTt[j * LC + i4]) = *reinterpret_cast<const f32x4*>(gTt + (size_t)j * C + i4);
+  }
+  // Bk = beta k exp(Gamma), Bv = beta v (zero past the end of the sequence)
+  for (int it = tid; it < C * D / 8; it += 256) {
+    const int t = it / (D / 8), c8 = 8 * (it % (D / 8));
+    const int tg = n * C + t;
+    float kk[8], vv[8], gg[8];
+    float bt = 0.f;
+    if (tg < p.T) {
+      const size_t row = ((size_t)b * p.T + tg) * HD + (size_t)h * D + c8;
+      load8(p.y + plane + row, kk);
+      load8(p.y + 2 * plane + row, vv);
+      load8(p.gam + row, gg);
+      bt = p.beta[((size_t)b * p.T + tg) * p.H + h];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kk[e] = vv[e] = gg[e] = 0.f;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      sBk[t * LB + c8 + e] = from_f32<E>(bt * kk[e] * __builtin_amdgcn_exp2f(gg[e]));
+      sBv[t * LB + c8 + e] = from_f32<E>(bt * vv[e]);
+    }
+  }
+  __syncthreads();
+
+  // ---- dT (i, j) for j <= i
+  for (int tile = wave; tile < RT * RT; tile += 4) {
+    const int It = tile / RT, Jt = tile % RT;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (Jt <= It) {
+      for (int k = 0; k < D; k += 4) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sdW[(16 * It + r) * LD + k + g4],
+                                                   to_f32(sBk[(16 * Jt + r) * LB + k + g4]), acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sdU[(16 * It + r) * LD + k + g4],
+                                                   to_f32(sBv[(16 * Jt + r) * LB + k + g4]), acc, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 16 * It + 4 * g4 + e, j = 16 * Jt + r;
+      sdT[i * LC + j] = j <= i ? acc[e] : 0.f;
+    }
+  }
+  __syncthreads();  // dT complete; Bk, Bv dead
+  float* sY = reinterpret_cast<float*>(sBkY);
+  // ---- Y = dT T^T:  Y[i][j] = sum_m dT[i][m] T^T[m][j]
+  for (int tile = wave; tile < RT * RT; tile += 4) {
+    const int It = tile / RT, Jt = tile % RT;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < C; k += 4)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sdT[(16 * It + r) * LC + k + g4],
+                                                 sTt[(k + g4) * LC + 16 * Jt + r], acc, 0, 0, 0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sY[(16 * It + 4 * g4 + e) * LC + 16 * Jt + r] = acc[e];
+  }
+  __syncthreads();
+  // ---- dA = -T^T Y  (j < i)
+  float* gdA = p.dA + (size_t)rec * C * C;
+  for (int tile = wave; tile < RT * RT; tile += 4) {
+    const int It = tile / RT, Jt = tile % RT;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (Jt <= It)
+      for (int k = 0; k < C; k += 4)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sTt[(16 * It + r) * LC + k + g4],
+                                                   sY[(k + g4) * LC + 16 * Jt + r], acc, 0, 0, 0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 16 * It + 4 * g4 + e, j = 16 * Jt + r;
+      gdA[(size_t)i * C + j] = j < i ? -acc[e] : 0.f;
+    }
+  }
+  // ---- dBk = T^T dW,  dBv = T^T dU  (tiles (j, c))
+  float* gdBk = p.dBk + (size_t)rec * C * D;
+  float* gdBv = p.dBv + (size_t)rec * C * D;
+  for (int tile = wave; tile < RT * CT; tile += 4) {
+    const int Jt = tile / CT, Ct = tile % CT;
+    f32x4 ak = {0.f, 0.f, 0.f, 0.f}, av = ak;
+    for (int k = 0; k < C; k += 4) {
+      const float a = sTt[(16 * Jt + r) * LC + k + g4];
+      ak = __builtin_amdgcn_mfma_f32_16x16x4f32(a, sdW[(k + g4) * LD + 16 * Ct + r], ak, 0, 0, 0);
+      av = __builtin_amdgcn_mfma_f32_16x16x4f32(a, sdU[(k + g4) * LD + 16 * Ct + r], av, 0, 0, 0);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const size_t o = (size_t)(16 * Jt + 4 * g4 + e) * D + 16 * Ct + r;
+      gdBk[o] = ak[e];
+      gdBv[o] = av[e];
+    }
+  }
+}
+
+// ------------------------------------------------- pair and element terms, dg
+// One 256-thread workgroup per (chunk record, block of CB channels).  Per channel
+// c, with E_ij = exp(Gamma_ic - Gamma_jc) for j <= i (at most 1, evaluated per
+// pair):
+//   row i:    rK_i = sum_{j<i} dA_ij k_jc E_ij,   rQ_i = sum_{j<=i} dP_ij k_jc E_ij
+//   column j: cK_j = sum_{i>j} beta_i dA_ij k_ic E_ij + sum_{i>=j} dP_ij q'_ic E_ij
+// and then, per token t,
+//   dq'  = Lambda dQL + rQ
+//   dk   = beta Lambda dBk + exp(Gamma_C - Gamma) dKt + beta rK + cK
+//   dv   = beta dBv
+//   dGam = dBk Bk + dQL QL - dKt Ktil + beta k rK + q' rQ - k cK   (+ dGamma_C on the last row)
+//   dbeta (this block's channels) = sum_c (dBv v + dBk k Lambda + k rK)
+// with dGamma_C = sum_t dKt Ktil + dLC LC, and dg = the reverse running sum of dGam.
+// Half the threads take rows (i = q mod 4), half columns (j = q mod 4).
+template <int D, int C>
+__global__ __launch_bounds__(256) void kda_bwd_pair_kernel(BwdPairParams p) {
+  constexpr int CB = D < 32 ? D : 32;  // channels per workgroup
+  constexpr int NBLK = D / CB;
+  constexpr int LA = C + 1;
+  __shared__ float sdA[C * LA];
+  __shared__ float sdP[C * LA];
+  __shared__ float sK[C * CB], sQ[C * CB], sG[C * CB];
+  __shared__ float rK[C * CB], rQ[C * CB], cK[C * CB];
+  __shared__ float sB[C];
+  __shared__ float sPart[256];
+
+  const int tid = threadIdx.x;
+  const int rec = blockIdx.x / NBLK;
+  const int blk = blockIdx.x % NBLK;
+  const int cb0 = blk * CB;
+  const int n = rec % p.NT;
+  const int bh = rec / p.NT;
+  const int h = bh % p.H, b = bh / p.H;
+  const size_t HD = (size_t)p.H * D;
+  const size_t plane = (size_t)p.B * p.T * HD;
+  const int nval = p.T - n * C < C ? p.T - n * C : C;  // tokens of the sequence in this chunk
+  auto row_of = [&](int t) { return ((size_t)b * p.T + (size_t)n * C + t) * HD + (size_t)h * D + cb0; };
+
+  const float* gdA = p.dA + (size_t)rec * C * C;
+  const float* gdP = p.dP + (size_t)rec * C * C;
+  for (int it = tid; it < C * C; it += 256) {
+    const int i = it / C, j = it % C;
+    sdA[i * LA + j] = gdA[it];
+    sdP[i * LA + j] = gdP[it];
+  }
+  for (int it = tid; it < C * CB; it += 256) {
+    const int t = it / CB, c = it % CB;
+    float kk = 0.f, qq = 0.f, gg = 0.f;
+    if (t < nval) {
+      const size_t o = row_of(t) + c;
+      qq = p.y[o];
+      kk = p.y[plane + o];
+      gg = p.gam[o];
+    } else if (nval > 0) {
+      gg = p.gam[row_of(nval - 1) + c];  // past the end g = 0: Gamma stays at its last value
+    }
+    sK[it] = kk;
+    sQ[it] = qq;
+    sG[it] = gg;
+  }
+  for (int t = tid; t < C; t += 256)
+    sB[t] = t < nval ? p.beta[((size_t)b * p.T + (size_t)n * C + t) * p.H + h] : 0.f;
+  __syncthreads();
+
+  // ---- pair terms
+  {
+    const int c = tid % CB, q = tid / CB;  // q in [0, 256 / CB)
+    constexpr int NQ = 256 / CB;           // 8 (CB = 32) or 16 (CB = 16)
+    constexpr int NR = NQ / 2;             // row threads per channel
+    if (q < NR) {
+      for (int i = q; i < C; i += NR) {
+        const float gi = sG[i * CB + c];
+        float ak = 0.f, aq = 0.f;
+        for (int j = 0; j <= i; ++j) {
+          const float kE = sK[j * CB + c] * __builtin_amdgcn_exp2f(gi - sG[j * CB + c]);
+          ak = fmaf(sdA[i * LA + j], kE, ak);  // dA_ii = 0
+          aq = fmaf(sdP[i * LA + j], kE, aq);
+        }
+        rK[i * CB + c] = ak;
+        rQ[i * CB + c] = aq;
+      }
+    } else {
+      for (int j = q - NR; j < C; j += NR) {
+        const float gj = sG[j * CB + c];
+        float acc = 0.f;
+        for (int i = j; i < C; ++i) {
+          const float E = __builtin_amdgcn_exp2f(sG[i * CB + c] - gj);
+          acc = fmaf(sB[i] * sdA[i * LA + j], sK[i * CB + c] * E, acc);
+          acc = fmaf(sdP[i * LA + j], sQ[i * CB + c] * E, acc);
+        }
+        cK[j * CB + c] = acc;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- element terms: thread (t0 = tid / CB, c), tokens t = t0, t0 + NQ, ...
+  const int c = tid % CB;
+  constexpr int NQ = 256 / CB;
+  const float gC = sG[(C - 1) * CB + c];
+  const float* gdQL = p.dQL + (size_t)rec * C * D;
+  const float* gdKt = p.dKt + (size_t)rec * C * D;
+  const float* gdBk = p.dBk + (size_t)rec * C * D;
+  const float* gdBv = p.dBv + (size_t)rec * C * D;
+  float colsum = 0.f;  // sum over this thread's tokens of dKt Ktil
+  for (int t = tid / CB; t < C; t += NQ) {
+    const size_t lo = (size_t)t * D + cb0 + c;
+    const float dql = gdQL[lo], dkt = gdKt[lo], dbk = gdBk[lo], dbv = gdBv[lo];
+    const float kk = sK[t * CB + c], qq = sQ[t * CB + c], bt = sB[t];
+    const float lam = __builtin_amdgcn_exp2f(sG[t * CB + c]);
+    const float ec = __builtin_amdgcn_exp2f(gC - sG[t * CB + c]);
+    const float rk = rK[t * CB + c], rq = rQ[t * CB + c], ck = cK[t * CB + c];
+    const float ktil = kk * ec;
+    colsum = fmaf(dkt, ktil, colsum);
+    const float dgam = dbk * bt * kk * lam + dql * qq * lam - dkt * ktil + bt * kk * rk + qq * rq - kk * ck;
+    float vv = 0.f;
+    if (t < nval) {
+      const size_t o = row_of(t) + c;
+      vv = p.y[2 * plane + o];
+      p.dy[o] = lam * dql + rq;
+      p.dy[plane + o] = bt * lam * dbk + ec * dkt + bt * rk + ck;
+      p.dy[2 * plane + o] = bt * dbv;
+    }
+    rK[t * CB + c] = dgam;                      // reused: dGamma
+    rQ[t * CB + c] = dbv * vv + dbk * kk * lam + kk * rk;  // reused: beta partial
+  }
+  sPart[(tid / CB) * CB + c] = colsum;
+  __syncthreads();
+  if (tid < CB) {
+    // dGamma_C, then dg = reverse running sum over the chunk
+    float dgc = p.dLC[(size_t)rec * D + cb0 + tid] * __builtin_amdgcn_exp2f(sG[(C - 1) * CB + tid]);
+    for (int q = 0; q < NQ; ++q) dgc += sPart[q * CB + tid];
+    float acc = dgc;
+    for (int t = C - 1; t >= 0; --t) {
+      acc += rK[t * CB + tid];
+      if (t < nval) p.dg[row_of(t) + tid] = acc;
+    }
+  }
+  if (tid < C && tid < nval) {
+    float acc = 0.f;
+    for (int cc = 0; cc < CB; ++cc) acc += rQ[tid * CB + cc];
+    p.dbeta_part[(size_t)blk * p.B * p.T * p.H + ((size_t)b * p.T + (size_t)n * C + tid) * p.H + h] = acc;
+  }
+}
+
+// ------------------------------------------------------- front end in reverse
+// One 256-thread workgroup per (b, h, block of 4 * 256 / (D / 8) tokens); a thread
+// owns 4 tokens x 8 channels, the D / 8 lanes of a token row reduce the L2 sums
+// together.  For each of q, k, v, with pre the conv output, y = SiLU(pre) and
+// z = y / n, n = sqrt(|y|^2 + eps) (q and k):
+//   dy = dz / n - y (y . dz) / n^3,   dpre = dy sigmoid(pre) (1 + pre (1 - sigmoid(pre)))
+//   dx_t = sum_tau w_tau dpre_{t + 3 - tau},   dw_tau = sum_t dpre_t x_{t - 3 + tau}
+// so a thread also forms dpre for the 3 tokens after its own.  Tokens before the
+// sequence take their raw values from the conv history (their gradient goes to
+// dconv_state).  dbeta is summed from the per-channel-block partials here.
+template <int D, typename IO>
+__global__ __launch_bounds__(256) void kda_bwd_front_kernel(BwdFrontParams p, const float* dbeta_part,
+                                                            int nparts, float* dbeta) {
+  constexpr int NOCT = D / 8;
+  constexpr int SEG = 256 / NOCT;
+  constexpr int TOKB = 4 * SEG;  // tokens per workgroup
+  constexpr int NR = 10;         // raw rows: t_first - 3 .. t_first + 6
+  constexpr int NU = 7;          // tokens whose dpre a thread forms
+  __shared__ float sw[3 * 4 * D];      // filters [x][tap][c]
+  __shared__ float red[SEG * 8 * NOCT];  // per-segment partials of one (x, tap)
+
+  const int tid = threadIdx.x;
+  const int nblk = (p.T + TOKB - 1) / TOKB;
+  const int blk = blockIdx.x % nblk;
+  const int bh = blockIdx.x / nblk;
+  const int h = bh % p.H, b = bh / p.H;
+  const int s = tid / NOCT, j = tid % NOCT;
+  const int ch = 8 * j;
+  const int tf = blk * TOKB + 4 * s;
+  const size_t HD = (size_t)p.H * D;
+  const size_t plane = (size_t)p.B * p.T * HD;
+  const bool conv = p.conv_w != nullptr;
+  if (conv)
+    for (int it = tid; it < 3 * D; it += 256) {
+      const int x = it / D, c = it % D;
+      const f32x4 w = *reinterpret_cast<const f32x4*>(p.conv_w + ((size_t)x * HD + (size_t)h * D + c) * 4);
+#pragma unroll
+      for (int tau = 0; tau < 4; ++tau) sw[(x * 4 + tau) * D + c] = w[tau];
+    }
+  __syncthreads();
+
+  const IO* src[3] = {static_cast<const IO*>(p.q), static_cast<const IO*>(p.k),
+                      static_cast<const IO*>(p.v)};
+  float* dst[3] = {p.dq, p.dk, p.dv};
+  for (int x = 0; x < 3; ++x) {
+    // raw rows (token t_first - 3 + m), from the history before the sequence
+    float raw[NR][8];
+#pragma unroll
+    for (int m = 0; m < NR; ++m) {
+      const int t = tf - 3 + m;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) raw[m][c] = 0.f;
+      if (t >= 0 && t < p.T) {
+        load8(src[x] + ((size_t)b * p.T + t) * HD + (size_t)h * D + ch, raw[m]);
+      } else if (t < 0 && t >= -3 && conv && p.conv_state_in != nullptr) {
+        load8(static_cast<const IO*>(p.conv_state_in) + (((size_t)b * 3 + x) * 3 + (3 + t)) * HD +
+                  (size_t)h * D + ch,
+              raw[m]);
+      }
+    }
+    float w[4][8];
+    if (conv) {
+#pragma unroll
+      for (int tau = 0; tau < 4; ++tau)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) w[tau][c] = sw[(x * 4 + tau) * D + ch + c];
+    }
+    // dpre for tokens t_first .. t_first + 6
+    float dpre[NU][8];
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+      const int t = tf + u;
+      float pre[8], y[8], dz[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        if (conv) {
+          float acc = w[0][c] * raw[u][c];
+          acc = fmaf(w[1][c], raw[u + 1][c], acc);
+          acc = fmaf(w[2][c], raw[u + 2][c], acc);
+          acc = fmaf(w[3][c], raw[u + 3][c], acc);
+          pre[c] = acc;
+          y[c] = silu(acc);
+        } else {
+          pre[c] = 0.f;
+          y[c] = raw[u + 3][c];
+        }
+        dz[c] = 0.f;
+      }
+      if (t < p.T) {
+        load8(p.dy + x * plane + ((size_t)b * p.T + t) * HD + (size_t)h * D + ch, dz);
+        if (x == 0)
+#pragma unroll
+          for (int c = 0; c < 8; ++c) dz[c] *= p.scale;
+      }
+      float dyv[8];
+      if (x < 2 && p.l2) {
+        float yy = 0.f, yd = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          yy = fmaf(y[c], y[c], yy);
+          yd = fmaf(y[c], dz[c], yd);
+        }
+        yy = group_sum<NOCT>(yy);
+        yd = group_sum<NOCT>(yd);
+        const float rn = 1.0f / sqrtf(yy + p.eps);
+        const float k3 = yd * rn * rn * rn;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) dyv[c] = dz[c] * rn - y[c] * k3;
+      } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) dyv[c] = dz[c];
+      }
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        if (conv) {
+          const float sg = sigmoid(pre[c]);
+          dpre[u][c] = dyv[c] * sg * (1.0f + pre[c] * (1.0f - sg));
+        } else {
+          dpre[u][c] = dyv[c];
+        }
+      }
+    }
+    // dx of the own tokens
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int t = tf + m;
+      if (t < p.T) {
+        float dx[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          if (conv)
+            dx[c] = w[3][c] * dpre[m][c] + w[2][c] * dpre[m + 1][c] + w[1][c] * dpre[m + 2][c] +
+                    w[0][c] * dpre[m + 3][c];
+          else
+            dx[c] = dpre[m][c];
+        }
+        store8(dst[x] + ((size_t)b * p.T + t) * HD + (size_t)h * D + ch, dx);
+      }
+    }
+    if (!conv) continue;
+    // gradient of the conv history (tokens -3 .. -1) from the first segment
+    if (tf == 0 && p.dconv_state != nullptr) {
+#pragma unroll
+      for (int u = -3; u < 0; ++u) {
+        float dx[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          float acc = 0.f;
+#pragma unroll
+          for (int tau = 0; tau < 4; ++tau) {
+            const int tt = u + 3 - tau;  // token whose window holds token u at tap tau
+            if (tt >= 0 && tt < p.T) acc = fmaf(w[tau][c], dpre[tt][c], acc);
+          }
+          dx[c] = acc;
+        }
+        store8(p.dconv_state + (((size_t)b * 3 + x) * 3 + (3 + u)) * HD + (size_t)h * D + ch, dx);
+      }
+    }
+    // filter gradient partials of this workgroup: tap by tap, reduced over segments
+    for (int tau = 0; tau < 4; ++tau) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        float acc = 0.f;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          if (tf + m < p.T) acc = fmaf(dpre[m][c], raw[m + tau][c], acc);
+        red[(s * NOCT + j) * 8 + c] = acc;
+      }
+      __syncthreads();
+      if (tid < D) {
+        float acc = 0.f;
+        for (int s2 = 0; s2 < SEG; ++s2) acc += red[(s2 * NOCT + tid / 8) * 8 + tid % 8];
+        p.dconv_part[(((size_t)b * nblk + blk) * 3 + x) * HD * 4 + ((size_t)h * D + tid) * 4 + tau] = acc;
+      }
+      __syncthreads();
+    }
+  }
+  if (dbeta != nullptr && j == 0) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int t = tf + m;
+      if (t < p.T) {
+        const size_t o = ((size_t)b * p.T + t) * p.H + h;
+        float acc = 0.f;
+        for (int q = 0; q < nparts; ++q) acc += dbeta_part[(size_t)q * p.B * p.T * p.H + o];
+        dbeta[o] = acc;
+      }
+    }
+  }
+}
+
+// dconv_w = the sum of the workgroups' partials (fixed order: deterministic)
+__global__ __launch_bounds__(256) void kda_bwd_conv_reduce_kernel(const float* part, float* out,
+                                                                  size_t n, int nparts) {
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= n) return;
+  float acc = 0.f;
+  for (int q = 0; q < nparts; ++q) acc += part[(size_t)q * n + idx];
+  out[idx] = acc;
+}
+
+// ------------------------------------------------------------------ launchers
+template <int D, int C, typename IO, typename E>
+static hipError_t launch_bwd_t(const BwdLaunch& L, hipStream_t st) {
+  const size_t nrec = (size_t)L.walk.B * L.walk.H * L.walk.NT;
+  const size_t BH = (size_t)L.walk.B * L.walk.H;
+  // reverse walk: the forward walk's value blocks
+  if constexpr (D == 128 && sizeof(E) == 2) {
+    hipLaunchKernelGGL((kda_bwd_walk_kernel<D, C, 64, IO, E, 512>), dim3((unsigned)(BH * 2)), dim3(512),
+                       0, st, L.walk);
+  } else {
+    constexpr int VB = D >= 64 ? 64 : D;
+    hipLaunchKernelGGL((kda_bwd_walk_kernel<D, C, VB, IO, E, 256>), dim3((unsigned)(BH * (D / VB))),
+                       dim3(256), 0, st, L.walk);
+  }
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  hipLaunchKernelGGL((kda_bwd_prod_kernel<D, C, IO, E>), dim3((unsigned)nrec), dim3(256), 0, st, L.prod);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  hipLaunchKernelGGL((kda_bwd_t_kernel<D, C, E>), dim3((unsigned)nrec), dim3(256), 0, st, L.tside);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  constexpr int NBLK = D < 32 ? 1 : D / 32;
+  hipLaunchKernelGGL((kda_bwd_pair_kernel<D, C>), dim3((unsigned)(nrec * NBLK)), dim3(256), 0, st, L.pair);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  constexpr int TOKB = 4 * (256 / (D / 8));
+  const size_t nblk = ((size_t)L.front.T + TOKB - 1) / TOKB;
+  hipLaunchKernelGGL((kda_bwd_front_kernel<D, IO>), dim3((unsigned)(BH * nblk)), dim3(256), 0, st, L.front,
+                     L.pair.dbeta_part, NBLK, L.dbeta);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  if (L.front.conv_w != nullptr) {
+    const size_t n = (size_t)3 * L.front.H * D * 4;
+    hipLaunchKernelGGL(kda_bwd_conv_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                       L.front.dconv_part, L.dconv_w, n, (int)(L.front.B * nblk));
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <int D, typename IO, typename E>
+static hipError_t launch_bwd_c(const BwdLaunch& L, int C, hipStream_t st) {
+  switch (C) {
+    case 16: return launch_bwd_t<D, 16, IO, E>(L, st);
+    case 32: return launch_bwd_t<D, 32, IO, E>(L, st);
+    case 64: return launch_bwd_t<D, 64, IO, E>(L, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+size_t bwd_front_blocks(int T, int D) { return ((size_t)T + 4 * (256 / (D / 8)) - 1) / (4 * (256 / (D / 8))); }
+
+hipError_t launch_backward(const BwdLaunch& L, int D, int C, bool fp32, hipStream_t st) {
+  if (fp32) {
+    switch (D) {
+      case 16: return launch_bwd_c<16, float, float>(L, C, st);
+      case 32: return launch_bwd_c<32, float, float>(L, C, st);
+      case 64: return launch_bwd_c<64, float, float>(L, C, st);
+    }
+  } else {
+    switch (D) {
+      case 16: return launch_bwd_c<16, __bf16, __bf16>(L, C, st);
+      case 32: return launch_bwd_c<32, __bf16, __bf16>(L, C, st);
+      case 64: return launch_bwd_c<64, __bf16, __bf16>(L, C, st);
+      case 128: return launch_bwd_c<128, __bf16, __bf16>(L, C, st);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kda

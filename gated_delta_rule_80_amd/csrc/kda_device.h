@@ -204,6 +204,14 @@ template <int K> struct RowFrag<__bf16, K> {
       for (int e = 0; e < PER; ++e)
         if (i * STEP + PER * g + e > kmax) v[i][e] = (__bf16)0.f;
   }
+  // zero every element whose k index is below kmin
+  __device__ __forceinline__ void mask_below(int kmin, int g) {
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+#pragma unroll
+      for (int e = 0; e < PER; ++e)
+        if (i * STEP + PER * g + e < kmin) v[i][e] = (__bf16)0.f;
+  }
 };
 
 template <int K> struct RowFrag<float, K> {
@@ -219,6 +227,11 @@ template <int K> struct RowFrag<float, K> {
 #pragma unroll
     for (int i = 0; i < N; ++i)
       if (4 * i + g > kmax) v[i] = 0.f;
+  }
+  __device__ __forceinline__ void mask_below(int kmin, int g) {
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if (4 * i + g < kmin) v[i] = 0.f;
   }
 };
 
@@ -273,6 +286,23 @@ template <int K>
 __device__ __forceinline__ void load_swz(RowFrag<float, K>& f, const float* img, int row, int g) {
 #pragma unroll
   for (int i = 0; i < RowFrag<float, K>::N; ++i) f.v[i] = img[Swz<float, K>::at(row, 4 * i + g)];
+}
+
+// Transposed fragment: this lane's fragment of column j of a swizzled image with
+// KM elements per row (the fragment's k runs over the image's rows, KF of them).
+template <int KF, int KM>
+__device__ __forceinline__ void load_swz_t(RowFrag<__bf16, KF>& f, const __bf16* img, int j, int g) {
+  using FR = RowFrag<__bf16, KF>;
+#pragma unroll
+  for (int i = 0; i < FR::N; ++i)
+#pragma unroll
+    for (int e = 0; e < FR::PER; ++e)
+      f.v[i][e] = img[Swz<__bf16, KM>::at(i * FR::STEP + FR::PER * g + e, j)];
+}
+template <int KF, int KM>
+__device__ __forceinline__ void load_swz_t(RowFrag<float, KF>& f, const float* img, int j, int g) {
+#pragma unroll
+  for (int i = 0; i < RowFrag<float, KF>::N; ++i) f.v[i] = img[Swz<float, KM>::at(4 * i + g, j)];
 }
 
 // Instruction depth along k for an element type (used for causal bounds).

@@ -16,6 +16,8 @@ hipError_t launch_conv_norm(const ConvNormParams& p, int D, bool fp32, hipStream
 hipError_t launch_conv_tail(const TailParams& p, bool fp32, hipStream_t st);
 hipError_t launch_seq_index(const IndexParams& p, hipStream_t st);
 hipError_t launch_copy_state(const float* src, float* dst, size_t n, hipStream_t st);
+hipError_t launch_backward(const BwdLaunch& L, int D, int C, bool fp32, hipStream_t st);
+size_t bwd_front_blocks(int T, int D);
 hipError_t launch_decode(const DecodeParams& p, int D, bool fp32, hipStream_t st);
 
 }  // namespace kda

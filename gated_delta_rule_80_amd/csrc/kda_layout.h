@@ -96,6 +96,14 @@ struct PrepParams {
   const float* dt_bias;  // [H*D]
   int beta_logits;       // beta holds logits
   SeqTables seqs;        // packed sequences (then B = 1 and NT = chunk slots per head)
+  // backward mode (all NULL otherwise): the front end's outputs in float32 --
+  // y = (scale * q_hat, k_hat, v_hat) [3][B*T*H*D], gam = the chunk-local
+  // cumulative log2-decay [B*T*H*D], beta [B*T*H] -- and T^T = ((I + A)^-1)^T
+  // per record [C][C]
+  float* y_out;
+  float* gam_out;
+  float* beta_out;
+  float* t_out;
 };
 
 struct StateParams {
@@ -109,6 +117,7 @@ struct StateParams {
   const float* o_norm_w;  // [D] or NULL
   float o_norm_eps;
   SeqTables seqs;         // packed sequences (then B = n_seqs, NT = chunk slots per head)
+  float* ckpt;            // backward mode: the state at each chunk start, S^T [rec][D][D], or NULL
 };
 
 // The output stage on its own, in place on o: RMSNorm with gain and/or the
@@ -119,6 +128,97 @@ struct OutStageParams {
   const float* o_norm_w;  // or NULL
   float o_norm_eps;
   long rows;
+};
+
+// ------------------------------------------------------------------ backward
+// Workspace buffers of the backward pass, per record rec = (b * H + h) * NT + n:
+//   ckS  [rec][D][D]  S_n^T (state at the chunk start, row = value column)
+//   ckdS [rec][D][D]  dS_{n+1}^T (gradient of the chunk's end state)
+//   dU   [rec][D][C]  dU_n^T
+//   dQL, dW, dKt [rec][C][D], dP [rec][C][C], dLC [rec][D]: gradients of the
+//   record's quantities;  dBk, dBv [rec][C][D], dA [rec][C][C]
+struct BwdWalkParams {
+  const char* ws;      // forward records
+  const void* dO;      // [B][T][H][D]
+  const float* dS_T;   // [B][H][D][D] or NULL
+  float* dS0;          // [B][H][D][D] or NULL
+  float* dU;
+  float* ckdS;
+  int B, T, H, NT;
+};
+
+struct BwdProdParams {
+  const char* ws;      // forward records (W, U~)
+  const void* dO;
+  const float* ckS;
+  const float* ckdS;
+  const float* dU;
+  float* dQL;
+  float* dW;
+  float* dKt;
+  float* dP;
+  float* dLC;
+  int B, T, H, NT;
+};
+
+struct BwdTParams {
+  const float* tT;     // T^T per record
+  const float* y;      // front end outputs [3][B*T*H*D]
+  const float* gam;
+  const float* beta;
+  const float* dW;
+  const float* dU;
+  float* dBk;
+  float* dBv;
+  float* dA;
+  int B, T, H, NT;
+};
+
+struct BwdPairParams {
+  const float* y;
+  const float* gam;
+  const float* beta;
+  const float* dA;
+  const float* dP;
+  const float* dQL;
+  const float* dKt;
+  const float* dLC;
+  const float* dBk;
+  const float* dBv;
+  float* dy;           // [3][B*T*H*D]: gradients of (scale * q_hat, k_hat, v_hat)
+  float* dg;           // [B*T*H*D]
+  float* dbeta_part;   // [D / 32][B*T*H]: per block of 32 channels
+  int B, T, H, NT;
+};
+
+struct BwdFrontParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* conv_w;        // NULL: no convolution
+  const void* conv_state_in;  // may be NULL
+  const float* dy;            // [3][B*T*H*D]
+  float* dq;
+  float* dk;
+  float* dv;
+  float* dconv_part;          // [B * nblk][3][H*D][4] or NULL
+  float* dconv_state;         // [B][3][3][H*D] or NULL
+  int B, T, H;
+  int l2;
+  float eps;
+  float scale;
+};
+
+// Everything one backward launch sequence needs (the forward part is launched
+// separately, in backward mode).
+struct BwdLaunch {
+  BwdWalkParams walk;
+  BwdProdParams prod;
+  BwdTParams tside;
+  BwdPairParams pair;
+  BwdFrontParams front;
+  float* dbeta;    // [B*T*H]
+  float* dconv_w;  // [3][H*D][4] or NULL
 };
 
 struct ConvNormParams {

@@ -324,6 +324,28 @@ __global__ __launch_bounds__(fast_threads<E>()) void kda_chunk_prep_kernel(PrepP
     if (fatal) atomicOr(&sm.fatal, 1);
   }
   __syncthreads();
+  if (p.y_out != nullptr && active) {
+    // backward mode: the front end's outputs and the cumulative decay, in float32
+    float pre[8];
+    load8(&sm.tot[s * D + ch], pre);
+    const long HD = (long)p.H * D;
+    const long plane = (long)p.B * p.T * HD;
+#pragma unroll
+    for (int m = 0; m < TOK; ++m) {
+      const int t = tf + m;
+      if (t < Tq) {
+        const long row = (tok0 + t) * HD + (long)h * D + ch;
+        store8(p.y_out + row, yq[m]);
+        store8(p.y_out + plane + row, yk[m]);
+        store8(p.y_out + 2 * plane + row, yv[m]);
+        float gam[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) gam[c] = gc[m][c] + pre[c];
+        store8(p.gam_out + row, gam);
+        if (j == 0) p.beta_out[(tok0 + t) * p.H + h] = bt[m];
+      }
+    }
+  }
   if (sm.fatal) {
     // decays too strong for the factoring: the exact preparation redoes this chunk
     if (tid == 0) {
@@ -488,6 +510,14 @@ __global__ __launch_bounds__(fast_threads<E>()) void kda_chunk_prep_kernel(PrepP
       for (int e = 0; e < 4; ++e) sT[(16 * pr + 4 * g4 + e) * LA + 16 * qb + r] = -acc[e];
     }
     __syncthreads();
+  }
+  if (p.t_out != nullptr) {
+    // backward mode: T^T in float32 (the upper triangle of T is not computed here)
+    float* to = p.t_out + (size_t)rec * C * C;
+    for (int it = tid; it < C * C; it += NTH) {
+      const int jj = it / C, i = it % C;  // to[jj][i] = T[i][jj]
+      to[it] = jj <= i ? sT[i * LA + jj] : 0.f;
+    }
   }
   // T in the matrix-core element type, after A / T / scratch
   E* tb = reinterpret_cast<E*>(sm.r1 + SM::TB_OFF);

@@ -373,6 +373,14 @@ __global__ __launch_bounds__(kPrepThreads) void kda_chunk_prep_exact_kernel(Prep
     }
     __syncthreads();
   }
+  if (p.t_out != nullptr) {
+    // backward mode: T^T in float32
+    float* to = p.t_out + (size_t)rec * C * C;
+    for (int it = tid; it < C * C; it += kPrepThreads) {
+      const int jj = it / C, i = it % C;  // to[jj][i] = T[i][jj]
+      to[it] = jj <= i ? sT[i * LA + jj] : 0.f;
+    }
+  }
   // T in the matrix-core element type
   const E* Tb;
   int LTB;

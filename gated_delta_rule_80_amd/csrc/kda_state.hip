@@ -334,6 +334,18 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void kda_chunk_state_kernel(
     if (n + 1 < nch) issue_copy(n + 1);
     load_gate(n);  // buffer n % 2: chunk n - 2's, stored during step n - 1
     if (n > 0) store_out(n - 1);
+    if (p.ckpt != nullptr) {
+      // backward mode: S_n^T, four consecutive key channels per lane
+#pragma unroll
+      for (int i = 0; i < NS; ++i) {
+        const int u = wave + NW * i;
+        if (FULL_S || u < CT * VT) {
+          const int Ct = u % CT, Vt = u / CT;
+          *reinterpret_cast<f32x4*>(p.ckpt + (rec0 + n) * D * D + (size_t)(vb0 + 16 * Vt + r) * D +
+                                    16 * Ct + 4 * g4) = accS[i];
+        }
+      }
+    }
     if (has_u) fp.mask_above(i_row, g4);
 
     // ---- U = U~ - W S  and  O^T = S^T QL^T

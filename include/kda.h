@@ -229,6 +229,37 @@ typedef struct kda_decode_args {
 kda_status kda_validate_decode(const kda_decode_args* a);
 kda_status kda_decode_step(const kda_decode_args* a, void* stream);
 
+/* --------------------------------------------------------------- backward */
+/* Gradients of the prefill: with do and dS_T the gradients of a loss with
+ * respect to o and S_T, the gradients of L = <o, do> + <S_T, dS_T> with respect
+ * to the raw q, k, v, g, beta, S0, the conv filters and the conv history.  The
+ * forward is recomputed (the arguments' o, S_T and conv_state_out are written
+ * again with the same values), then walked back chunk by chunk: the reverse of
+ * the chunked form, with the pairs' relative decays exp(Gamma_i - Gamma_j)
+ * evaluated per pair.  Supported: the plain mixer over B equal-length sequences
+ * (no packed sequences, no optional stages); fp32 I/O up to D = 64, bf16 I/O up
+ * to D = 128.  All gradients are float32. */
+typedef struct kda_backward_args {
+  kda_prefill_args fwd; /* the forward call; its rules apply */
+  const void* dO;       /* device [B][T][H][D] io dtype: gradient of o */
+  const float* dS_T;    /* device [B][H][D][D] or NULL (= zeros): gradient of S_T */
+  float* dq;            /* device [B][T][H][D]: gradient of the raw q */
+  float* dk;            /* device [B][T][H][D] */
+  float* dv;            /* device [B][T][H][D] */
+  float* dg;            /* device [B][T][H][D] */
+  float* dbeta;         /* device [B][T][H] */
+  float* dS0;           /* device [B][H][D][D] or NULL (not written) */
+  float* dconv_w;       /* device [3][H*D][conv_k]; required iff conv_k > 0 */
+  float* dconv_state;   /* device [B][3][conv_k-1][H*D] or NULL (not written) */
+} kda_backward_args;
+
+kda_status kda_validate_backward(const kda_backward_args* a);
+/* Bytes of device workspace kda_prefill_backward needs (0 if invalid or T = 0). */
+size_t kda_backward_workspace_bytes(const kda_backward_args* a);
+/* Enqueue the recomputed forward and the backward on `stream`.  No output may
+ * overlap an input or another output; the workspace overlaps nothing. */
+kda_status kda_prefill_backward(const kda_backward_args* a, void* ws, size_t ws_bytes, void* stream);
+
 /* ------------------------------------------------------------------- misc */
 const char* kda_status_str(int status);
 int kda_abi_version(void);

@@ -1,0 +1,84 @@
+"""Gradients of the prefill on the GPU against the fp64 oracle's reverse-mode
+gradients (kda_reference_backward, itself pinned by finite differences).
+
+Loss L = <o, do> + <S_T, dS_T> with random do, dS_T.  Tolerance: relative L2 per
+gradient tensor, 2e-2 for bf16 inputs and 1e-4 for fp32 inputs (the same bar as
+the forward), over dq, dk, dv, dg, dbeta, dS0, dconv_w and dconv_state."""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_80_amd as kda
+from kda_inputs import to_numpy
+from kda_testutil import TOL, cuda, make, rel_l2, small
+from oracle import kda_reference_backward
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dS0", "dconv_w", "dconv_state")
+
+
+def check_backward(w, chunk, seed=0, conv=True, l2=True, scale=1.0, with_dST=True):
+    inp = make(w, seed)
+    if not conv:
+        inp = dict(inp, conv_w=None, conv_state=None)
+    gen = torch.Generator().manual_seed(seed + 1000)
+    do = torch.randn(w.B, w.T, w.H, w.D, generator=gen).to(inp["q"].dtype)
+    dST = torch.randn(w.B, w.H, w.D, w.D, generator=gen) if with_dST else None
+    c = cuda(inp)
+    grads, o, S_T = kda.kda_prefill_backward(c["q"], c["k"], c["v"], c["g"], c["beta"], c["conv_w"],
+                                             c["conv_state"], c["S0"], do=do.cuda(),
+                                             dS_T=None if dST is None else dST.cuda(), chunk=chunk,
+                                             scale=scale, l2norm_qk=l2)
+    torch.cuda.synchronize()
+    n = {k: to_numpy(v) for k, v in inp.items()}
+    ref = kda_reference_backward(n["q"], n["k"], n["v"], n["g"], n["beta"], to_numpy(do),
+                                 None if dST is None else to_numpy(dST), conv_w=n["conv_w"],
+                                 conv_state=n["conv_state"], S0=n["S0"], scale=scale, l2norm_qk=l2)
+    tol = TOL[w.io]
+    errs = {}
+    for name in NAMES:
+        if ref.get(name) is None:
+            continue
+        got = grads[name].cpu().numpy()
+        assert np.isfinite(got).all(), name
+        errs[name] = rel_l2(got, ref[name])
+    print(f"{w.name} C={chunk} conv={conv} l2={l2}: " +
+          " ".join(f"{k}={v:.1e}" for k, v in errs.items()), flush=True)
+    for name, e in errs.items():
+        assert e <= tol, (name, e)
+
+
+def test_backward_tiny_fp32():
+    w = small(B=1, T=64, H=2, D=16, io="fp32", chunk=16, s0=True, conv_state=True)
+    check_backward(w, 16)
+
+
+@pytest.mark.parametrize("io,D,chunk", [("fp32", 16, 16), ("fp32", 32, 32), ("fp32", 64, 64),
+                                        ("bf16", 32, 16), ("bf16", 64, 32), ("bf16", 128, 64),
+                                        ("bf16", 128, 32), ("bf16", 128, 16)])
+def test_backward_dims_and_chunks(io, D, chunk):
+    w = small(B=2, T=77, H=2, D=D, io=io, chunk=chunk, s0=True, conv_state=True)
+    check_backward(w, chunk, seed=D + chunk)
+
+
+@pytest.mark.parametrize("T", [1, 3, 16, 17, 64, 65, 130])
+def test_backward_lengths(T):
+    w = small(B=1, T=T, H=2, D=64, io="fp32", chunk=32, s0=True, conv_state=True)
+    check_backward(w, 32, seed=T)
+
+
+@pytest.mark.parametrize("conv,l2", [(False, True), (True, False), (False, False)])
+def test_backward_front_end_modes(conv, l2):
+    w = small(B=1, T=50, H=2, D=32, io="fp32", chunk=16, s0=True, conv_state=True)
+    check_backward(w, 16, seed=3, conv=conv, l2=l2, scale=0.5 if not l2 else 1.0)
+
+
+def test_backward_strong_decay_bf16():
+    w = small(B=1, T=200, H=2, D=128, io="bf16", chunk=64, strong=True, s0=True, conv_state=True)
+    check_backward(w, 64, seed=7)
+
+
+def test_backward_without_state_gradients():
+    w = small(B=2, T=40, H=2, D=64, io="bf16", chunk=32)
+    check_backward(w, 32, seed=8, with_dST=False)
