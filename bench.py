@@ -7,8 +7,8 @@ state walk with output, conv-state hand-over), inputs resident in HBM.  The
 decode step (B=256 sequences, in-place state) is timed in the same run and
 reported beside it.  A second leg ("stages") times the same prefill and decode
 steps with the optional stages on (decay and write strength from raw
-projections, output RMSNorm and sigmoid gate) and the prefill's tokens packed as
-sequences of mixed length.  Prints one JSON line.
+projections, output RMSNorm and sigmoid gate), the prefill's tokens packed as
+sequences of mixed length, and the backward pass.  Prints one JSON line.
 
 Roofline figures use algorithmic bytes (each tensor the kernel must read or
 write, once) divided by the kernel's mean duration from HIP events recorded on
@@ -34,6 +34,7 @@ BF16_PEAK = 2.5e15         # flop/s, dense
 STAGE_NAMES = ["kda_chunk_prep_kernel", "kda_chunk_state_kernel", "kda_conv_tail_kernel",
                "kda_out_stage_kernel"]
 KERNEL_SOURCES = ["gated_delta_rule_80_amd/csrc/kda_prep.hip",
+                  "gated_delta_rule_80_amd/csrc/kda_backward.hip",
                   "gated_delta_rule_80_amd/csrc/kda_prep_exact.hip",
                   "gated_delta_rule_80_amd/csrc/kda_state.hip",
                   "gated_delta_rule_80_amd/csrc/kda_decode.hip",
@@ -264,6 +265,45 @@ def stages_leg(kda, torch, w, wd, args, stream, dev, plain_ms, plain_dms):
             "prefill": prefill, "decode": decode}
 
 
+def backward_leg(kda, torch, w, args, stream, dev, plain_ms):
+    """kda_prefill_backward on the same workload (forward recomputed inside)."""
+    from kda_inputs import make_inputs
+    inp = make_inputs(w, seed=args.seed, device=dev)
+    gen = torch.Generator(device=dev).manual_seed(args.seed + 7)
+    do = torch.randn(w.B, w.T, w.H, w.D, generator=gen, device=dev).to(inp["q"].dtype)
+    f32 = dict(dtype=torch.float32, device=dev)
+    o = torch.empty_like(inp["q"])
+    S_T = torch.empty(w.B, w.H, w.D, w.D, **f32)
+    cso = torch.empty(w.B, 3, 3, w.H * w.D, dtype=inp["q"].dtype, device=dev)
+    fwd = kda.prefill_args(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["conv_w"],
+                           inp["conv_state"], inp["S0"], o, S_T, cso, chunk=w.chunk)
+    shape = (w.B, w.T, w.H, w.D)
+    grads = dict(dq=torch.empty(*shape, **f32), dk=torch.empty(*shape, **f32),
+                 dv=torch.empty(*shape, **f32), dg=torch.empty(*shape, **f32),
+                 dbeta=torch.empty(w.B, w.T, w.H, **f32), dS0=torch.empty(w.B, w.H, w.D, w.D, **f32),
+                 dconv_w=torch.empty(3, w.H * w.D, 4, **f32),
+                 dconv_state=torch.empty(w.B, 3, 3, w.H * w.D, **f32))
+    a = kda.backward_args(fwd, do, None, grads)
+    ws = torch.empty(kda.kda_backward_workspace_bytes(a), dtype=torch.uint8, device=dev)
+    for _ in range(args.warmup):
+        kda.kda_prefill_backward_raw(a, ws, stream)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        kda.kda_prefill_backward_raw(a, ws, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    out = {"workload": w.name, "ms_per_step": ms, "tokens_per_s": w.B * w.T / (ms / 1e3),
+           "ratio_to_forward": ms / plain_ms, "workspace_bytes": ws.numel(),
+           "includes": "recomputed forward + reverse walk + per-chunk gradient kernels + front end"}
+    del ws, inp, grads, o, S_T, cso, do
+    torch.cuda.empty_cache()
+    return out
+
+
 # The 4096 tokens of the 4k workload as 8 packed sequences of mixed length.
 PACKED_LENGTHS = [1024, 512, 700, 300, 1000, 60, 400, 100]
 
@@ -304,7 +344,7 @@ def main(argv=None) -> int:
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-stages", action="store_true",
                     help="skip the legs with the optional stages (raw projections, output norm + "
-                         "gate) and with packed sequences")
+                         "gate), packed sequences and the backward pass")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run the library's plain state-copy kernel (kda_prefill with T=0) "
                          "on this many MiB, to calibrate HBM byte counters")
@@ -386,6 +426,7 @@ def main(argv=None) -> int:
     if not args.no_stages:
         stages = stages_leg(kda, torch, w, wd, args, stream, dev, plain_ms, dms)
         stages["packed"] = packed_leg(kda, torch, w, args, stream, dev, plain_ms)
+        stages["backward"] = backward_leg(kda, torch, w, args, stream, dev, plain_ms)
 
     if args.calib_copy_mib > 0:
         # kda_prefill with T = 0 copies S0 to S_T with one plain copy kernel

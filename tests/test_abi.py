@@ -330,3 +330,67 @@ def test_packed_state_sizes_follow_n_seqs(lib):
     assert vp(a) == OK
     a.S_T = a.S0 + state - 256
     assert vp(a) == ALIAS
+
+
+# -------------------------------------------------------------------- backward
+def backward(**kw):
+    f = Fake()
+    f.next = 0x7B0000000000
+    a = _lib.BackwardArgs()
+    a.fwd = prefill()
+    for n in ("dO", "dS_T", "dq", "dk", "dv", "dg", "dbeta", "dS0", "dconv_w", "dconv_state"):
+        setattr(a, n, f())
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_backward_validation(lib):
+    vb = kda.kda_validate_backward
+    assert vb(backward()) == OK
+    assert kda.kda_backward_workspace_bytes(backward()) > kda.kda_prefill_workspace_bytes(prefill())
+    for n in ("dO", "dq", "dk", "dv", "dg", "dbeta", "dconv_w"):
+        assert vb(backward(**{n: None})) == NULL, n
+    assert vb(backward(dS_T=None, dS0=None, dconv_state=None)) == OK  # optional ones
+    a = backward()
+    a.dk = a.dq  # outputs may not overlap each other
+    assert vb(a) == ALIAS
+    a = backward()
+    a.dg = a.fwd.g  # nor an input
+    assert vb(a) == ALIAS
+    a = backward()
+    a.dq = a.fwd.o  # nor a forward output
+    assert vb(a) == ALIAS
+    a = backward()
+    a.dbeta += 4
+    assert vb(a) == ALIGN
+    # unsupported modes
+    f = Fake()
+    f.next = 0x7A0000000000
+    a = backward()
+    a.fwd.A_log, a.fwd.dt_bias = f(), f()
+    assert vb(a) == UNSUP
+    a = backward()
+    a.fwd.o_gate = f()
+    assert vb(a) == UNSUP
+    a = backward()
+    a.fwd.flags = 3
+    assert vb(a) == UNSUP
+    a = backward()
+    a.fwd.B, a.fwd.cu_seqlens, a.fwd.n_seqs = 1, f(), 2
+    assert vb(a) == UNSUP
+    a = backward()
+    a.fwd.io, a.fwd.chunk = _lib.KDA_FP32, 32
+    assert vb(a) == UNSUP  # fp32 with D = 128
+    a.fwd.D = 64
+    assert vb(a) == OK
+    # the forward's own rules still apply
+    a = backward()
+    a.fwd.D = 96
+    assert vb(a) == UNSUP
+    # conv_k = 0: no filter or history gradients
+    a = backward(dconv_w=None, dconv_state=None)
+    a.fwd.conv_k, a.fwd.conv_w, a.fwd.conv_state_in, a.fwd.conv_state_out = 0, None, None, None
+    assert vb(a) == OK
+    a.dconv_w = f()
+    assert vb(a) == NULL

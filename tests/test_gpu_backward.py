@@ -82,3 +82,36 @@ def test_backward_strong_decay_bf16():
 def test_backward_without_state_gradients():
     w = small(B=2, T=40, H=2, D=64, io="bf16", chunk=32)
     check_backward(w, 32, seed=8, with_dST=False)
+
+
+def test_backward_repeated_calls_are_bit_identical():
+    w = small(B=1, T=150, H=3, D=128, io="bf16", chunk=64, s0=True, conv_state=True)
+    inp = cuda(make(w, 9))
+    do = torch.randn(w.B, w.T, w.H, w.D, generator=torch.Generator().manual_seed(3)).to(torch.bfloat16).cuda()
+    first = None
+    for _ in range(5):
+        grads, _, _ = kda.kda_prefill_backward(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                               inp["conv_w"], inp["conv_state"], inp["S0"], do=do,
+                                               chunk=64)
+        torch.cuda.synchronize()
+        if first is None:
+            first = {k: v.clone() for k, v in grads.items()}
+        else:
+            for k, v in grads.items():
+                assert torch.equal(v, first[k]), k
+
+
+def test_backward_empty_sequence():
+    """T = 0: dS0 = dS_T, the filter and history gradients are zero."""
+    w = small(B=2, T=0, H=2, D=32, io="fp32", chunk=16, s0=True, conv_state=True)
+    inp = cuda(make(w, 1))
+    dST = torch.randn(2, 2, 32, 32, device="cuda")
+    do = torch.empty(2, 0, 2, 32, device="cuda")
+    grads, o, S_T = kda.kda_prefill_backward(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                             inp["conv_w"], inp["conv_state"], inp["S0"], do=do,
+                                             dS_T=dST, chunk=16)
+    torch.cuda.synchronize()
+    assert torch.equal(grads["dS0"], dST)
+    assert torch.equal(S_T, inp["S0"])
+    assert float(grads["dconv_w"].abs().max()) == 0.0
+    assert float(grads["dconv_state"].abs().max()) == 0.0

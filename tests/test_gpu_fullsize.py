@@ -17,7 +17,7 @@ import torch
 import gated_delta_rule_80_amd as kda
 from kda_inputs import WORKLOADS, make_inputs, to_numpy
 from kda_testutil import TOL, oracle_heads, rel_l2
-from oracle import kda_reference_decode_step
+from oracle import kda_reference_backward, kda_reference_decode_step
 
 pytestmark = pytest.mark.gpu
 
@@ -91,3 +91,36 @@ def test_full_size_decode_sampled_pairs():
         print(f"  (b={b}, h={h}): rel_l2 o={eo:.2e} S={eS:.2e}", flush=True)
         assert eo <= tol and eS <= tol, (b, h, eo, eS)
         np.testing.assert_array_equal(cs[b:b + 1, :, :, ch].float().cpu().numpy(), rcs)
+
+
+def test_full_size_backward_sampled_head():
+    """The backward at the 4k workload's full size (every head and chunk on the
+    GPU), checked on one sampled head against the oracle's reverse-mode gradients
+    of that head (heads are independent; the conv filter gradient of the head's
+    channels comes from that head alone)."""
+    w = WORKLOADS["prefill-4k"]
+    inp = make_inputs(w, seed=0, device="cuda")
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    do = torch.randn(w.B, w.T, w.H, w.D, generator=gen, device="cuda").to(torch.bfloat16)
+    grads, o, S_T = kda.kda_prefill_backward(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                             inp["conv_w"], inp["conv_state"], inp["S0"], do=do,
+                                             chunk=w.chunk)
+    torch.cuda.synchronize()
+    for n, t in grads.items():
+        assert bool(torch.isfinite(t).all()), n
+    b, h = 0, 37
+    D = w.D
+    ch = slice(h * D, (h + 1) * D)
+    one = lambda x: to_numpy(x[b:b + 1, :, h:h + 1])
+    ref = kda_reference_backward(one(inp["q"]), one(inp["k"]), one(inp["v"]), one(inp["g"]),
+                                 to_numpy(inp["beta"][b:b + 1, :, h:h + 1]), one(do),
+                                 conv_w=to_numpy(inp["conv_w"][:, ch]))
+    tol = TOL[w.io]
+    pairs = {"dq": grads["dq"][b:b + 1, :, h:h + 1], "dk": grads["dk"][b:b + 1, :, h:h + 1],
+             "dv": grads["dv"][b:b + 1, :, h:h + 1], "dg": grads["dg"][b:b + 1, :, h:h + 1],
+             "dbeta": grads["dbeta"][b:b + 1, :, h:h + 1], "dS0": grads["dS0"][b:b + 1, h:h + 1],
+             "dconv_w": grads["dconv_w"][:, ch], "dconv_state": grads["dconv_state"][b:b + 1, :, :, ch]}
+    for n, t in pairs.items():
+        e = rel_l2(t.cpu().numpy(), ref[n])
+        print(f"  backward (b={b}, h={h}) {n}: rel_l2 {e:.2e}", flush=True)
+        assert e <= tol, (n, e)
