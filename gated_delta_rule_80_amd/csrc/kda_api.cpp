@@ -516,7 +516,7 @@ BwdLayout bwd_layout(const kda_backward_args* a) {
   L.dBv = take(nrec * C * D);
   L.dA = take(nrec * C * C);
   L.dy = take(3 * x);
-  L.dbp = take((D < 32 ? 1 : D / 32) * bth);
+  L.dbp = take(bth);
   L.nfront = kda::bwd_front_blocks(f->T, f->D);
   L.dcp = take(f->conv_k > 0 ? (size_t)f->B * L.nfront * 3 * f->H * D * 4 : 0);
   L.bytes = off;

@@ -555,147 +555,195 @@ __global__ __launch_bounds__(256) void kda_bwd_t_kernel(BwdTParams p) {
 }
 
 // ------------------------------------------------- pair and element terms, dg
-// One 256-thread workgroup per (chunk record, block of CB channels).  Per channel
-// c, with E_ij = exp(Gamma_ic - Gamma_jc) for j <= i (at most 1, evaluated per
-// pair):
+// One workgroup per chunk record, TPC = C / 16 threads per channel (adjacent
+// lanes) and all D channels.  Per channel c, with E_ij = exp(Gamma_ic - Gamma_jc)
+// for j <= i (at most 1, evaluated once per pair):
 //   row i:    rK_i = sum_{j<i} dA_ij k_jc E_ij,   rQ_i = sum_{j<=i} dP_ij k_jc E_ij
-//   column j: cK_j = sum_{i>j} beta_i dA_ij k_ic E_ij + sum_{i>=j} dP_ij q'_ic E_ij
-// and then, per token t,
+//   column j: cK_j = sum_{i>=j} E_ij (beta_i dA_ij k_ic + dP_ij q'_ic)
+// The C rows come in chunks of 4; thread t of a channel takes chunks t, 2 TPC - 1 - t,
+// 2 TPC + t, 4 TPC - 1 - t (equal work), keeps its rows' sums and its share of
+// every column sum in registers, and the column shares are added across the
+// channel's lanes.  Then, per token t,
 //   dq'  = Lambda dQL + rQ
 //   dk   = beta Lambda dBk + exp(Gamma_C - Gamma) dKt + beta rK + cK
 //   dv   = beta dBv
 //   dGam = dBk Bk + dQL QL - dKt Ktil + beta k rK + q' rQ - k cK   (+ dGamma_C on the last row)
-//   dbeta (this block's channels) = sum_c (dBv v + dBk k Lambda + k rK)
+//   dbeta = sum_c (dBv v + dBk k Lambda + k rK)
 // with dGamma_C = sum_t dKt Ktil + dLC LC, and dg = the reverse running sum of dGam.
-// Half the threads take rows (i = q mod 4), half columns (j = q mod 4).
 template <int D, int C>
-__global__ __launch_bounds__(256) void kda_bwd_pair_kernel(BwdPairParams p) {
-  constexpr int CB = D < 32 ? D : 32;  // channels per workgroup
-  constexpr int NBLK = D / CB;
-  constexpr int LA = C + 1;
-  __shared__ float sdA[C * LA];
-  __shared__ float sdP[C * LA];
-  __shared__ float sK[C * CB], sQ[C * CB], sG[C * CB];
-  __shared__ float rK[C * CB], rQ[C * CB], cK[C * CB];
+struct PairShape {
+  static constexpr int TPC = C / 16;  // threads per channel (4 row chunks each)
+  static constexpr int NTH = D * TPC;
+};
+
+template <int D, int C>
+__global__ __launch_bounds__(D * (C / 16)) void kda_bwd_pair_kernel(BwdPairParams p) {
+  constexpr int TPC = PairShape<D, C>::TPC;
+  constexpr int NTH = PairShape<D, C>::NTH;
+  constexpr int LA = C + 4;
+  constexpr int LD = D + 4;
+  constexpr int AP = 2 * C * LA > C * LD ? 2 * C * LA : C * LD;
+  __shared__ __attribute__((aligned(16))) float sAP[AP];  // dA, dP; then cK, dbeta parts [C][LD]
+  __shared__ __attribute__((aligned(16))) float sK[C * LD];
+  __shared__ __attribute__((aligned(16))) float sQ[C * LD];  // later dGamma [C][LD]
+  __shared__ __attribute__((aligned(16))) float sG[C * LD];
   __shared__ float sB[C];
-  __shared__ float sPart[256];
+  __shared__ float sGC[D];
+  float* sdA = sAP;
+  float* sdP = sAP + C * LA;
 
   const int tid = threadIdx.x;
-  const int rec = blockIdx.x / NBLK;
-  const int blk = blockIdx.x % NBLK;
-  const int cb0 = blk * CB;
+  const int rec = blockIdx.x;
   const int n = rec % p.NT;
   const int bh = rec / p.NT;
   const int h = bh % p.H, b = bh / p.H;
   const size_t HD = (size_t)p.H * D;
   const size_t plane = (size_t)p.B * p.T * HD;
   const int nval = p.T - n * C < C ? p.T - n * C : C;  // tokens of the sequence in this chunk
-  auto row_of = [&](int t) { return ((size_t)b * p.T + (size_t)n * C + t) * HD + (size_t)h * D + cb0; };
+  auto row_of = [&](int t) { return ((size_t)b * p.T + (size_t)n * C + t) * HD + (size_t)h * D; };
 
   const float* gdA = p.dA + (size_t)rec * C * C;
   const float* gdP = p.dP + (size_t)rec * C * C;
-  for (int it = tid; it < C * C; it += 256) {
-    const int i = it / C, j = it % C;
-    sdA[i * LA + j] = gdA[it];
-    sdP[i * LA + j] = gdP[it];
+  for (int it = tid; it < C * C / 4; it += NTH) {
+    const int i = it / (C / 4), j4 = 4 * (it % (C / 4));
+    *reinterpret_cast<f32x4*>(&sdA[i * LA + j4]) = *reinterpret_cast<const f32x4*>(gdA + (size_t)i * C + j4);
+    *reinterpret_cast<f32x4*>(&sdP[i * LA + j4]) = *reinterpret_cast<const f32x4*>(gdP + (size_t)i * C + j4);
   }
-  for (int it = tid; it < C * CB; it += 256) {
-    const int t = it / CB, c = it % CB;
-    float kk = 0.f, qq = 0.f, gg = 0.f;
+  for (int it = tid; it < C * D / 4; it += NTH) {
+    const int t = it / (D / 4), c4 = 4 * (it % (D / 4));
+    f32x4 kk = {0.f, 0.f, 0.f, 0.f}, qq = kk, gg = kk;
     if (t < nval) {
-      const size_t o = row_of(t) + c;
-      qq = p.y[o];
-      kk = p.y[plane + o];
-      gg = p.gam[o];
+      const size_t o = row_of(t) + c4;
+      qq = *reinterpret_cast<const f32x4*>(p.y + o);
+      kk = *reinterpret_cast<const f32x4*>(p.y + plane + o);
+      gg = *reinterpret_cast<const f32x4*>(p.gam + o);
     } else if (nval > 0) {
-      gg = p.gam[row_of(nval - 1) + c];  // past the end g = 0: Gamma stays at its last value
+      // past the end g = 0: Gamma keeps its last value
+      gg = *reinterpret_cast<const f32x4*>(p.gam + row_of(nval - 1) + c4);
     }
-    sK[it] = kk;
-    sQ[it] = qq;
-    sG[it] = gg;
+    *reinterpret_cast<f32x4*>(&sK[t * LD + c4]) = kk;
+    *reinterpret_cast<f32x4*>(&sQ[t * LD + c4]) = qq;
+    *reinterpret_cast<f32x4*>(&sG[t * LD + c4]) = gg;
   }
-  for (int t = tid; t < C; t += 256)
+  for (int t = tid; t < C; t += NTH)
     sB[t] = t < nval ? p.beta[((size_t)b * p.T + (size_t)n * C + t) * p.H + h] : 0.f;
   __syncthreads();
 
-  // ---- pair terms
-  {
-    const int c = tid % CB, q = tid / CB;  // q in [0, 256 / CB)
-    constexpr int NQ = 256 / CB;           // 8 (CB = 32) or 16 (CB = 16)
-    constexpr int NR = NQ / 2;             // row threads per channel
-    if (q < NR) {
-      for (int i = q; i < C; i += NR) {
-        const float gi = sG[i * CB + c];
-        float ak = 0.f, aq = 0.f;
-        for (int j = 0; j <= i; ++j) {
-          const float kE = sK[j * CB + c] * __builtin_amdgcn_exp2f(gi - sG[j * CB + c]);
-          ak = fmaf(sdA[i * LA + j], kE, ak);  // dA_ii = 0
-          aq = fmaf(sdP[i * LA + j], kE, aq);
+  const int c = tid / TPC, tq = tid % TPC;
+  // this thread's row chunks (4 rows each)
+  int ck[4];
+  ck[0] = tq;
+  ck[1] = 2 * TPC - 1 - tq;
+  ck[2] = 2 * TPC + tq;
+  ck[3] = 4 * TPC - 1 - tq;
+  float rK[4][4], rQ[4][4];
+  float cacc[C];
+#pragma unroll
+  for (int j = 0; j < C; ++j) cacc[j] = 0.f;
+  for (int m = 0; m < 4; ++m) {
+    const int i0 = 4 * ck[m];
+    float gi[4], ki[4], qi[4], bi[4], ak[4], aq[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      gi[r] = sG[(i0 + r) * LD + c];
+      ki[r] = sK[(i0 + r) * LD + c];
+      qi[r] = sQ[(i0 + r) * LD + c];
+      bi[r] = sB[i0 + r];
+      ak[r] = aq[r] = 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      if (j < i0 + 4) {
+        const float kj = sK[j * LD + c], gj = sG[j * LD + c];
+        float col = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          // pairs with j > i carry dA = dP = 0; the clamp keeps their E finite
+          const float e = __builtin_amdgcn_exp2f(fminf(gi[r] - gj, 0.f));
+          const float a = sdA[(i0 + r) * LA + j], pp = sdP[(i0 + r) * LA + j];
+          const float ke = kj * e;
+          ak[r] = fmaf(a, ke, ak[r]);
+          aq[r] = fmaf(pp, ke, aq[r]);
+          col = fmaf(e, fmaf(bi[r] * a, ki[r], pp * qi[r]), col);
         }
-        rK[i * CB + c] = ak;
-        rQ[i * CB + c] = aq;
-      }
-    } else {
-      for (int j = q - NR; j < C; j += NR) {
-        const float gj = sG[j * CB + c];
-        float acc = 0.f;
-        for (int i = j; i < C; ++i) {
-          const float E = __builtin_amdgcn_exp2f(sG[i * CB + c] - gj);
-          acc = fmaf(sB[i] * sdA[i * LA + j], sK[i * CB + c] * E, acc);
-          acc = fmaf(sdP[i * LA + j], sQ[i * CB + c] * E, acc);
-        }
-        cK[j * CB + c] = acc;
+        cacc[j] += col;
       }
     }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      rK[m][r] = ak[r];
+      rQ[m][r] = aq[r];
+    }
   }
+  // column sums: add the shares of the channel's TPC lanes, then to LDS
+#pragma unroll
+  for (int j = 0; j < C; ++j) cacc[j] = group_sum<TPC>(cacc[j]);
+  __syncthreads();  // every read of dA, dP is done
+  float* sCK = sAP;  // [C][LD]
+  if (tq == 0)
+#pragma unroll
+    for (int j = 0; j < C; ++j) sCK[j * LD + c] = cacc[j];
   __syncthreads();
 
-  // ---- element terms: thread (t0 = tid / CB, c), tokens t = t0, t0 + NQ, ...
-  const int c = tid % CB;
-  constexpr int NQ = 256 / CB;
-  const float gC = sG[(C - 1) * CB + c];
+  // ---- element terms for this thread's rows
+  const float gC = sG[(C - 1) * LD + c];
   const float* gdQL = p.dQL + (size_t)rec * C * D;
   const float* gdKt = p.dKt + (size_t)rec * C * D;
   const float* gdBk = p.dBk + (size_t)rec * C * D;
   const float* gdBv = p.dBv + (size_t)rec * C * D;
-  float colsum = 0.f;  // sum over this thread's tokens of dKt Ktil
-  for (int t = tid / CB; t < C; t += NQ) {
-    const size_t lo = (size_t)t * D + cb0 + c;
-    const float dql = gdQL[lo], dkt = gdKt[lo], dbk = gdBk[lo], dbv = gdBv[lo];
-    const float kk = sK[t * CB + c], qq = sQ[t * CB + c], bt = sB[t];
-    const float lam = __builtin_amdgcn_exp2f(sG[t * CB + c]);
-    const float ec = __builtin_amdgcn_exp2f(gC - sG[t * CB + c]);
-    const float rk = rK[t * CB + c], rq = rQ[t * CB + c], ck = cK[t * CB + c];
-    const float ktil = kk * ec;
-    colsum = fmaf(dkt, ktil, colsum);
-    const float dgam = dbk * bt * kk * lam + dql * qq * lam - dkt * ktil + bt * kk * rk + qq * rq - kk * ck;
-    float vv = 0.f;
-    if (t < nval) {
-      const size_t o = row_of(t) + c;
-      vv = p.y[2 * plane + o];
-      p.dy[o] = lam * dql + rq;
-      p.dy[plane + o] = bt * lam * dbk + ec * dkt + bt * rk + ck;
-      p.dy[2 * plane + o] = bt * dbv;
+  float colsum = 0.f;  // sum over this thread's rows of dKt Ktil
+  float dgam[4][4], dbp[4][4];
+  for (int m = 0; m < 4; ++m) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 4 * ck[m] + r;
+      const size_t lo = (size_t)t * D + c;
+      const float dql = gdQL[lo], dkt = gdKt[lo], dbk = gdBk[lo], dbv = gdBv[lo];
+      const float kk = sK[t * LD + c], qq = sQ[t * LD + c], bt = sB[t];
+      const float lam = __builtin_amdgcn_exp2f(sG[t * LD + c]);
+      const float ec = __builtin_amdgcn_exp2f(gC - sG[t * LD + c]);
+      const float ckt = sCK[t * LD + c];
+      const float ktil = kk * ec;
+      colsum = fmaf(dkt, ktil, colsum);
+      dgam[m][r] = dbk * bt * kk * lam + dql * qq * lam - dkt * ktil + bt * kk * rK[m][r] +
+                   qq * rQ[m][r] - kk * ckt;
+      float vv = 0.f;
+      if (t < nval) {
+        const size_t o = row_of(t) + c;
+        vv = p.y[2 * plane + o];
+        p.dy[o] = lam * dql + rQ[m][r];
+        p.dy[plane + o] = bt * lam * dbk + ec * dkt + bt * rK[m][r] + ckt;
+        p.dy[2 * plane + o] = bt * dbv;
+      }
+      dbp[m][r] = dbv * vv + dbk * kk * lam + kk * rK[m][r];
     }
-    rK[t * CB + c] = dgam;                      // reused: dGamma
-    rQ[t * CB + c] = dbv * vv + dbk * kk * lam + kk * rk;  // reused: beta partial
   }
-  sPart[(tid / CB) * CB + c] = colsum;
+  colsum = group_sum<TPC>(colsum);
+  __syncthreads();  // every read of cK and Q is done
+  float* sdG = sQ;   // [C][LD]
+  float* sdb = sAP;  // [C][LD]
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = 4 * ck[m] + r;
+      sdG[t * LD + c] = dgam[m][r];
+      sdb[t * LD + c] = dbp[m][r];
+    }
+  if (tq == 0) sGC[c] = colsum + p.dLC[(size_t)rec * D + c] * __builtin_amdgcn_exp2f(gC);
   __syncthreads();
-  if (tid < CB) {
-    // dGamma_C, then dg = reverse running sum over the chunk
-    float dgc = p.dLC[(size_t)rec * D + cb0 + tid] * __builtin_amdgcn_exp2f(sG[(C - 1) * CB + tid]);
-    for (int q = 0; q < NQ; ++q) dgc += sPart[q * CB + tid];
-    float acc = dgc;
+  // dg: reverse running sum over the chunk, one thread per channel
+  if (tid < D) {
+    float acc = sGC[tid];
     for (int t = C - 1; t >= 0; --t) {
-      acc += rK[t * CB + tid];
+      acc += sdG[t * LD + tid];
       if (t < nval) p.dg[row_of(t) + tid] = acc;
     }
   }
-  if (tid < C && tid < nval) {
+  // dbeta: sum over the channels, one thread per token
+  if (tid < nval) {
     float acc = 0.f;
-    for (int cc = 0; cc < CB; ++cc) acc += rQ[tid * CB + cc];
-    p.dbeta_part[(size_t)blk * p.B * p.T * p.H + ((size_t)b * p.T + (size_t)n * C + tid) * p.H + h] = acc;
+    for (int cc = 0; cc < D; ++cc) acc += sdb[tid * LD + cc];
+    p.dbeta_part[((size_t)b * p.T + (size_t)n * C + tid) * p.H + h] = acc;
   }
 }
 
@@ -919,8 +967,9 @@ static hipError_t launch_bwd_t(const BwdLaunch& L, hipStream_t st) {
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   hipLaunchKernelGGL((kda_bwd_t_kernel<D, C, E>), dim3((unsigned)nrec), dim3(256), 0, st, L.tside);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-  constexpr int NBLK = D < 32 ? 1 : D / 32;
-  hipLaunchKernelGGL((kda_bwd_pair_kernel<D, C>), dim3((unsigned)(nrec * NBLK)), dim3(256), 0, st, L.pair);
+  constexpr int NBLK = 1;  // the pair kernel sums dbeta over all channels itself
+  constexpr int PNTH = PairShape<D, C>::NTH;
+  hipLaunchKernelGGL((kda_bwd_pair_kernel<D, C>), dim3((unsigned)nrec), dim3(PNTH), 0, st, L.pair);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   constexpr int TOKB = 4 * (256 / (D / 8));
   const size_t nblk = ((size_t)L.front.T + TOKB - 1) / TOKB;

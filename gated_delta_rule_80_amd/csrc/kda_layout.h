@@ -187,7 +187,7 @@ struct BwdPairParams {
   const float* dBv;
   float* dy;           // [3][B*T*H*D]: gradients of (scale * q_hat, k_hat, v_hat)
   float* dg;           // [B*T*H*D]
-  float* dbeta_part;   // [D / 32][B*T*H]: per block of 32 channels
+  float* dbeta_part;   // [B*T*H]: dbeta
   int B, T, H, NT;
 };
 
