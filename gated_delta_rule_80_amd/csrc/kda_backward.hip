@@ -748,34 +748,39 @@ __global__ __launch_bounds__(D * (C / 16)) void kda_bwd_pair_kernel(BwdPairParam
 }
 
 // ------------------------------------------------------- front end in reverse
-// One 256-thread workgroup per (b, h, block of 4 * 256 / (D / 8) tokens); a thread
-// owns 4 tokens x 8 channels, the D / 8 lanes of a token row reduce the L2 sums
-// together.  For each of q, k, v, with pre the conv output, y = SiLU(pre) and
-// z = y / n, n = sqrt(|y|^2 + eps) (q and k):
+// One 256-thread workgroup per (b, h, block of TOKB = 4 * 256 / (D / 8) tokens);
+// a thread owns 4 tokens x 8 channels and the D / 8 lanes of a token row reduce
+// the L2 sums together.  For each of q, k, v, with pre the conv output, y =
+// SiLU(pre) and z = y / n, n = sqrt(|y|^2 + eps) (q and k):
 //   dy = dz / n - y (y . dz) / n^3,   dpre = dy sigmoid(pre) (1 + pre (1 - sigmoid(pre)))
 //   dx_t = sum_tau w_tau dpre_{t + 3 - tau},   dw_tau = sum_t dpre_t x_{t - 3 + tau}
-// so a thread also forms dpre for the 3 tokens after its own.  Tokens before the
-// sequence take their raw values from the conv history (their gradient goes to
-// dconv_state).  dbeta is summed from the per-channel-block partials here.
+// dpre of the block goes through LDS; the last segment also forms it for the 3
+// tokens after the block (the conv reaches them).  Tokens before the sequence
+// take their raw values from the conv history (their gradient goes to
+// dconv_state).  The filter partials are summed over the lanes of a wave, then
+// over the waves, in a fixed order.  dbeta (summed by the pair kernel) is copied.
 template <int D, typename IO>
-__global__ __launch_bounds__(256) void kda_bwd_front_kernel(BwdFrontParams p, const float* dbeta_part,
-                                                            int nparts, float* dbeta) {
+__global__ __launch_bounds__(256, 2) void kda_bwd_front_kernel(BwdFrontParams p, const float* dbeta_part,
+                                                               int nparts, float* dbeta) {
   constexpr int NOCT = D / 8;
   constexpr int SEG = 256 / NOCT;
   constexpr int TOKB = 4 * SEG;  // tokens per workgroup
-  constexpr int NR = 10;         // raw rows: t_first - 3 .. t_first + 6
-  constexpr int NU = 7;          // tokens whose dpre a thread forms
-  __shared__ float sw[3 * 4 * D];      // filters [x][tap][c]
-  __shared__ float red[SEG * 8 * NOCT];  // per-segment partials of one (x, tap)
+  constexpr int LDP = D + 4;
+  constexpr int SPW = 64 / NOCT;  // segments per wave
+  __shared__ float sw[3 * 4 * D];            // filters [x][tap][c]
+  __shared__ float sdp[(TOKB + 3) * LDP];    // dpre of the block and the 3 tokens after it
+  __shared__ float sred[4][3 * 4 * D];       // filter partials per wave [x][tap][c]
 
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nblk = (p.T + TOKB - 1) / TOKB;
   const int blk = blockIdx.x % nblk;
   const int bh = blockIdx.x / nblk;
   const int h = bh % p.H, b = bh / p.H;
   const int s = tid / NOCT, j = tid % NOCT;
   const int ch = 8 * j;
-  const int tf = blk * TOKB + 4 * s;
+  const int t0 = blk * TOKB;
+  const int tf = t0 + 4 * s;
+  const bool last = s == SEG - 1;
   const size_t HD = (size_t)p.H * D;
   const size_t plane = (size_t)p.B * p.T * HD;
   const bool conv = p.conv_w != nullptr;
@@ -788,19 +793,20 @@ __global__ __launch_bounds__(256) void kda_bwd_front_kernel(BwdFrontParams p, co
     }
   __syncthreads();
 
-  const IO* src[3] = {static_cast<const IO*>(p.q), static_cast<const IO*>(p.k),
-                      static_cast<const IO*>(p.v)};
-  float* dst[3] = {p.dq, p.dk, p.dv};
   for (int x = 0; x < 3; ++x) {
-    // raw rows (token t_first - 3 + m), from the history before the sequence
-    float raw[NR][8];
+    const IO* src = x == 0 ? static_cast<const IO*>(p.q) : (x == 1 ? static_cast<const IO*>(p.k)
+                                                                   : static_cast<const IO*>(p.v));
+    float* dst = x == 0 ? p.dq : (x == 1 ? p.dk : p.dv);
+    // raw rows t_first - 3 .. t_first + 6 (the last 3 only for the last segment)
+    float raw[10][8];
 #pragma unroll
-    for (int m = 0; m < NR; ++m) {
+    for (int m = 0; m < 10; ++m) {
       const int t = tf - 3 + m;
 #pragma unroll
       for (int c = 0; c < 8; ++c) raw[m][c] = 0.f;
+      if (m >= 7 && !last) continue;
       if (t >= 0 && t < p.T) {
-        load8(src[x] + ((size_t)b * p.T + t) * HD + (size_t)h * D + ch, raw[m]);
+        load8(src + ((size_t)b * p.T + t) * HD + (size_t)h * D + ch, raw[m]);
       } else if (t < 0 && t >= -3 && conv && p.conv_state_in != nullptr) {
         load8(static_cast<const IO*>(p.conv_state_in) + (((size_t)b * 3 + x) * 3 + (3 + t)) * HD +
                   (size_t)h * D + ch,
@@ -814,10 +820,10 @@ __global__ __launch_bounds__(256) void kda_bwd_front_kernel(BwdFrontParams p, co
 #pragma unroll
         for (int c = 0; c < 8; ++c) w[tau][c] = sw[(x * 4 + tau) * D + ch + c];
     }
-    // dpre for tokens t_first .. t_first + 6
-    float dpre[NU][8];
+    // dpre of tokens t_first .. t_first + 3 (+ 3 more for the last segment)
 #pragma unroll
-    for (int u = 0; u < NU; ++u) {
+    for (int u = 0; u < 7; ++u) {
+      if (u >= 4 && !last) continue;  // the whole row group takes the same branch
       const int t = tf + u;
       float pre[8], y[8], dz[8];
 #pragma unroll
@@ -859,17 +865,32 @@ __global__ __launch_bounds__(256) void kda_bwd_front_kernel(BwdFrontParams p, co
 #pragma unroll
         for (int c = 0; c < 8; ++c) dyv[c] = dz[c];
       }
+      float dp[8];
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         if (conv) {
           const float sg = sigmoid(pre[c]);
-          dpre[u][c] = dyv[c] * sg * (1.0f + pre[c] * (1.0f - sg));
+          dp[c] = dyv[c] * sg * (1.0f + pre[c] * (1.0f - sg));
         } else {
-          dpre[u][c] = dyv[c];
+          dp[c] = dyv[c];
         }
       }
+      *reinterpret_cast<f32x4*>(&sdp[(4 * s + u) * LDP + ch]) = f32x4{dp[0], dp[1], dp[2], dp[3]};
+      *reinterpret_cast<f32x4*>(&sdp[(4 * s + u) * LDP + ch + 4]) = f32x4{dp[4], dp[5], dp[6], dp[7]};
     }
+    __syncthreads();
     // dx of the own tokens
+    float dpo[7][8];
+#pragma unroll
+    for (int u = 0; u < 7; ++u) {
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(&sdp[(4 * s + u) * LDP + ch]);
+      const f32x4 hi = *reinterpret_cast<const f32x4*>(&sdp[(4 * s + u) * LDP + ch + 4]);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        dpo[u][c] = tf + u < p.T ? lo[c] : 0.f;
+        dpo[u][c + 4] = tf + u < p.T ? hi[c] : 0.f;
+      }
+    }
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int t = tf + m;
@@ -878,50 +899,53 @@ __global__ __launch_bounds__(256) void kda_bwd_front_kernel(BwdFrontParams p, co
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
           if (conv)
-            dx[c] = w[3][c] * dpre[m][c] + w[2][c] * dpre[m + 1][c] + w[1][c] * dpre[m + 2][c] +
-                    w[0][c] * dpre[m + 3][c];
+            dx[c] = w[3][c] * dpo[m][c] + w[2][c] * dpo[m + 1][c] + w[1][c] * dpo[m + 2][c] +
+                    w[0][c] * dpo[m + 3][c];
           else
-            dx[c] = dpre[m][c];
+            dx[c] = dpo[m][c];
         }
-        store8(dst[x] + ((size_t)b * p.T + t) * HD + (size_t)h * D + ch, dx);
+        store8(dst + ((size_t)b * p.T + t) * HD + (size_t)h * D + ch, dx);
       }
     }
-    if (!conv) continue;
-    // gradient of the conv history (tokens -3 .. -1) from the first segment
-    if (tf == 0 && p.dconv_state != nullptr) {
+    if (conv) {
+      // gradient of the conv history (tokens -3 .. -1) from the first segment
+      if (tf == 0 && p.dconv_state != nullptr) {
 #pragma unroll
-      for (int u = -3; u < 0; ++u) {
-        float dx[8];
+        for (int u = -3; u < 0; ++u) {
+          float dx[8];
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            float acc = 0.f;
+#pragma unroll
+            for (int tau = 0; tau < 4; ++tau) {
+              const int tt = u + 3 - tau;  // token whose window holds token u at tap tau
+              if (tt >= 0) acc = fmaf(w[tau][c], dpo[tt][c], acc);
+            }
+            dx[c] = acc;
+          }
+          store8(p.dconv_state + (((size_t)b * 3 + x) * 3 + (3 + u)) * HD + (size_t)h * D + ch, dx);
+        }
+      }
+      // filter partials of the own tokens, summed over the wave's segments
+#pragma unroll
+      for (int tau = 0; tau < 4; ++tau)
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
           float acc = 0.f;
 #pragma unroll
-          for (int tau = 0; tau < 4; ++tau) {
-            const int tt = u + 3 - tau;  // token whose window holds token u at tap tau
-            if (tt >= 0 && tt < p.T) acc = fmaf(w[tau][c], dpre[tt][c], acc);
-          }
-          dx[c] = acc;
+          for (int m = 0; m < 4; ++m) acc = fmaf(dpo[m][c], raw[m + tau][c], acc);
+#pragma unroll
+          for (int o = NOCT; o < 64; o <<= 1) acc += __shfl_xor(acc, o, 64);
+          if (lane < NOCT) sred[wave][(x * 4 + tau) * D + ch + c] = acc;
         }
-        store8(p.dconv_state + (((size_t)b * 3 + x) * 3 + (3 + u)) * HD + (size_t)h * D + ch, dx);
-      }
     }
-    // filter gradient partials of this workgroup: tap by tap, reduced over segments
-    for (int tau = 0; tau < 4; ++tau) {
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        float acc = 0.f;
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-          if (tf + m < p.T) acc = fmaf(dpre[m][c], raw[m + tau][c], acc);
-        red[(s * NOCT + j) * 8 + c] = acc;
-      }
-      __syncthreads();
-      if (tid < D) {
-        float acc = 0.f;
-        for (int s2 = 0; s2 < SEG; ++s2) acc += red[(s2 * NOCT + tid / 8) * 8 + tid % 8];
-        p.dconv_part[(((size_t)b * nblk + blk) * 3 + x) * HD * 4 + ((size_t)h * D + tid) * 4 + tau] = acc;
-      }
-      __syncthreads();
+    __syncthreads();  // sdp is rewritten by the next tensor
+  }
+  if (conv) {
+    for (int it = tid; it < 3 * 4 * D; it += 256) {
+      const int x = it / (4 * D), tau = (it / D) % 4, c = it % D;
+      const float acc = sred[0][it] + sred[1][it] + sred[2][it] + sred[3][it];
+      p.dconv_part[(((size_t)b * nblk + blk) * 3 + x) * HD * 4 + ((size_t)h * D + c) * 4 + tau] = acc;
     }
   }
   if (dbeta != nullptr && j == 0) {
@@ -936,6 +960,7 @@ __global__ __launch_bounds__(256) void kda_bwd_front_kernel(BwdFrontParams p, co
       }
     }
   }
+  (void)SPW;
 }
 
 // dconv_w = the sum of the workgroups' partials (fixed order: deterministic)
