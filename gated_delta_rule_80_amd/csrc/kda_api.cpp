@@ -239,7 +239,7 @@ struct BwdFwdOut {
   float* gam;
   float* beta;
   float* tT;
-  float* ckS;
+  void* ckS;
 };
 
 static kda_status run_stage(const kda_prefill_args* a, void* ws, int stage, hipStream_t st,
@@ -504,9 +504,10 @@ BwdLayout bwd_layout(const kda_backward_args* a) {
   L.y = take(3 * x);
   L.gam = take(x);
   L.beta = take(bth);
-  L.ckS = take(nrec * D * D);
-  L.ckdS = take(nrec * D * D);
-  L.dU = take(nrec * D * C);
+  const size_t ef = esize(f->io) == 2 ? 2 : 1;  // element-type buffers in float units (rounded up)
+  L.ckS = take(nrec * 2 * D * D / ef);
+  L.ckdS = take(nrec * D * D / ef);
+  L.dU = take(nrec * C * D / ef);
   L.dQL = take(nrec * C * D);
   L.dW = take(nrec * C * D);
   L.dKt = take(nrec * C * D);
@@ -617,7 +618,7 @@ kda_status kda_prefill_backward(const kda_backward_args* a, void* ws, size_t ws_
   char* wsb = static_cast<char*>(ws);
   auto F = [&](size_t off) { return reinterpret_cast<float*>(wsb + off); };
   // forward in backward mode
-  BwdFwdOut bo{F(L.y), F(L.gam), F(L.beta), F(L.tT), F(L.ckS)};
+  BwdFwdOut bo{F(L.y), F(L.gam), F(L.beta), F(L.tT), wsb + L.ckS};
   for (int stage = KDA_STAGE_PREP; stage <= KDA_STAGE_OUTPUT; ++stage)
     if (kda_status e = run_stage(f, ws, stage, st, &bo); e != KDA_OK) return e;
   // backward
@@ -627,20 +628,20 @@ kda_status kda_prefill_backward(const kda_backward_args* a, void* ws, size_t ws_
   B.walk.dO = a->dO;
   B.walk.dS_T = a->dS_T;
   B.walk.dS0 = a->dS0;
-  B.walk.dU = F(L.dU);
-  B.walk.ckdS = F(L.ckdS);
+  B.walk.dU = wsb + L.dU;
+  B.walk.ckdS = wsb + L.ckdS;
   B.walk.B = f->B; B.walk.T = f->T; B.walk.H = f->H; B.walk.NT = sz.NT;
   B.prod.ws = recs;
   B.prod.dO = a->dO;
-  B.prod.ckS = F(L.ckS);
-  B.prod.ckdS = F(L.ckdS);
-  B.prod.dU = F(L.dU);
+  B.prod.ckS = wsb + L.ckS;
+  B.prod.ckdS = wsb + L.ckdS;
+  B.prod.dU = wsb + L.dU;
   B.prod.dQL = F(L.dQL); B.prod.dW = F(L.dW); B.prod.dKt = F(L.dKt); B.prod.dP = F(L.dP);
   B.prod.dLC = F(L.dLC);
   B.prod.B = f->B; B.prod.T = f->T; B.prod.H = f->H; B.prod.NT = sz.NT;
   B.tside.tT = F(L.tT);
   B.tside.y = F(L.y); B.tside.gam = F(L.gam); B.tside.beta = F(L.beta);
-  B.tside.dW = F(L.dW); B.tside.dU = F(L.dU);
+  B.tside.dW = F(L.dW); B.tside.dU = wsb + L.dU;
   B.tside.dBk = F(L.dBk); B.tside.dBv = F(L.dBv); B.tside.dA = F(L.dA);
   B.tside.B = f->B; B.tside.T = f->T; B.tside.H = f->H; B.tside.NT = sz.NT;
   B.pair.y = F(L.y); B.pair.gam = F(L.gam); B.pair.beta = F(L.beta);

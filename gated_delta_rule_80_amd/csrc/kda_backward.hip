@@ -196,14 +196,15 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_walk_kernel(BwdWalkParams p) {
     __builtin_amdgcn_s_waitcnt(0);  // image and dO of chunk n
     stage_do(n);
     lds_barrier();
-    // the gradient of this chunk's end state, for the per-chunk products
+    // the gradient of this chunk's end state, for the per-chunk products: dS' [c][v]
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       const int u = wave + NW * i;
       if (FULL_S || u < CT * VT) {
         const int Ct = u % CT, Vt = u / CT;
-        *reinterpret_cast<f32x4*>(p.ckdS + (rec0 + n) * D * D + (size_t)(vb0 + 16 * Vt + r) * D +
-                                  16 * Ct + 4 * g4) = accS[i];
+        E* ck = static_cast<E*>(p.ckdS) + (rec0 + n) * D * D + vb0 + 16 * Vt + r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ck[(size_t)(16 * Ct + 4 * g4 + e) * D] = from_f32<E>(accS[i][e]);
       }
     }
     // ---- fragments of this chunk
@@ -243,8 +244,9 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_walk_kernel(BwdWalkParams p) {
         mma<C>(acc, fpt, fo);
         mma<D>(acc, fkt, fs);
         store4(&sDU[(16 * Vt + r) * LU + 16 * R + 4 * g4], acc[0], acc[1], acc[2], acc[3]);
-        *reinterpret_cast<f32x4*>(p.dU + (rec0 + n) * D * C + (size_t)(vb0 + 16 * Vt + r) * C +
-                                  16 * R + 4 * g4) = acc;
+        E* du = static_cast<E*>(p.dU) + (rec0 + n) * C * D + vb0 + 16 * Vt + r;  // dU [t][v]
+#pragma unroll
+        for (int e = 0; e < 4; ++e) du[(size_t)(16 * R + 4 * g4 + e) * D] = from_f32<E>(acc[e]);
       }
     }
     lds_barrier();  // sDU complete; every read of sS for this chunk is done
@@ -283,25 +285,22 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_walk_kernel(BwdWalkParams p) {
 
 // ------------------------------------------------------- per-chunk state products
 // One 256-thread workgroup per chunk record.  In the NT products
-// C[i][j] = sum_k A[i][k] B[j][k] (both operands k-contiguous in LDS, bf16, float
-// accumulation):
-//   U    = U~ - W S:   A = W rows t (record),   B = S^T rows v
+// C[i][j] = sum_k A[i][k] B[j][k] (operands k-contiguous, element type, float
+// accumulation), fragments loaded straight from the checkpoints, dO, dU and the
+// record (only U, formed here, goes through LDS):
+//   U    = U~ - W S:   A = W rows t (record),   B = S^T rows v (checkpoint)
 //   dQL  = dO S^T:     A = dO rows t,           B = S rows c
 //   dW   = -dU S^T:    A = dU rows t,           B = S rows c
 //   dKt  = U dS'^T:    A = U rows t,            B = dS' rows c
 //   dP   = dO U^T:     A = dO rows i,           B = U rows j      (j <= i)
-//   dLC  = rowsum(dS' * S)  in float32 from the checkpoints.
+//   dLC  = rowsum(dS' * S)
 template <int D, int C, typename IO, typename E>
 __global__ __launch_bounds__(256) void kda_bwd_prod_kernel(BwdProdParams p) {
   constexpr int PE = 16 / (int)sizeof(E);
-  constexpr int LD = D + PE;  // rows of D elements
+  constexpr int LD = D + PE;
   constexpr int CT = D / 16, RT = C / 16;
   constexpr RecordLayout RL = record_layout(C, D, sizeof(E));
-  __shared__ __attribute__((aligned(16))) E sS[D * LD];   // S rows c, k = v
-  __shared__ __attribute__((aligned(16))) E sX[D * LD];   // S^T rows v, k = c; later dS' rows c
-  __shared__ __attribute__((aligned(16))) E sU[C * LD];   // U rows t, k = v
-  __shared__ __attribute__((aligned(16))) E sDO[C * LD];  // dO rows t
-  __shared__ __attribute__((aligned(16))) E sDU[C * LD];  // dU rows t
+  __shared__ __attribute__((aligned(16))) E sU[C * LD];  // U rows t, k = v
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g4 = lane >> 4;
@@ -310,49 +309,33 @@ __global__ __launch_bounds__(256) void kda_bwd_prod_kernel(BwdProdParams p) {
   const int bh = rec / p.NT;
   const int h = bh % p.H, b = bh / p.H;
   const size_t HD = (size_t)p.H * D;
-  const float* ckS = p.ckS + (size_t)rec * D * D;    // [v][c]
-  const float* ckdS = p.ckdS + (size_t)rec * D * D;  // [v][c]
-  const float* dUt = p.dU + (size_t)rec * D * C;     // [v][t]
+  const E* ckSt = static_cast<const E*>(p.ckS) + (size_t)rec * 2 * D * D;  // [v][c]
+  const E* ckS = ckSt + (size_t)D * D;                                      // [c][v]
+  const E* ckdS = static_cast<const E*>(p.ckdS) + (size_t)rec * D * D;     // [c][v]
+  const E* gdU = static_cast<const E*>(p.dU) + (size_t)rec * C * D;         // [t][v]
   const char* recp = p.ws + (size_t)rec * RL.bytes;
   const E* gW = reinterpret_cast<const E*>(recp) + RL.w;
   const E* gU = reinterpret_cast<const E*>(recp) + RL.u;
+  const IO* gdO = static_cast<const IO*>(p.dO) + ((size_t)b * p.T + (size_t)n * C) * HD + (size_t)h * D;
+  const int nval = p.T - n * C < C ? p.T - n * C : C;
 
-  // ---- staging: S^T as is, S transposed, dO, dU transposed
-  for (int it = tid; it < D * D / 4; it += 256) {
-    const int v = it / (D / 4), c4 = 4 * (it % (D / 4));
-    const f32x4 x = *reinterpret_cast<const f32x4*>(ckS + (size_t)v * D + c4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      sX[v * LD + c4 + e] = from_f32<E>(x[e]);
-      sS[(c4 + e) * LD + v] = from_f32<E>(x[e]);
+  // dO fragment of row t (zero past the end of the sequence)
+  auto load_do = [&](RowFrag<E, D>& f, int t) {
+    if (t < nval) {
+      if constexpr (sizeof(IO) == sizeof(E)) {
+        f.load(reinterpret_cast<const E*>(gdO + (size_t)t * HD), g4);
+      }
+    } else {
+      f = RowFrag<E, D>{};
     }
-  }
-  for (int it = tid; it < C * D / 8; it += 256) {
-    const int t = it / (D / 8), c8 = 8 * (it % (D / 8));
-    const int tg = n * C + t;
-    float x[8];
-    if (tg < p.T)
-      load8(static_cast<const IO*>(p.dO) + ((size_t)b * p.T + tg) * HD + (size_t)h * D + c8, x);
-    else
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) sDO[t * LD + c8 + e] = from_f32<E>(x[e]);
-  }
-  for (int it = tid; it < D * C / 4; it += 256) {
-    const int v = it / (C / 4), t4 = 4 * (it % (C / 4));
-    const f32x4 x = *reinterpret_cast<const f32x4*>(dUt + (size_t)v * C + t4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sDU[(t4 + e) * LD + v] = from_f32<E>(x[e]);
-  }
-  __syncthreads();
+  };
 
   // ---- U = U~ - W S  (tiles (t, v))
   for (int tile = wave; tile < RT * CT; tile += 4) {
     const int Rt = tile / CT, Vt = tile % CT;
     RowFrag<E, D> fa, fb;
     fa.load(gW + (size_t)(16 * Rt + r) * D, g4);
-    fb.load(sX + (16 * Vt + r) * LD, g4);
+    fb.load(ckSt + (size_t)(16 * Vt + r) * D, g4);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     mma<D>(acc, fa, fb);
     // U~ in fragment order: tile (t-tile, v-tile) of 64 lanes x 4 values
@@ -361,17 +344,22 @@ __global__ __launch_bounds__(256) void kda_bwd_prod_kernel(BwdProdParams p) {
     for (int e = 0; e < 4; ++e)
       sU[(16 * Rt + 4 * g4 + e) * LD + 16 * Vt + r] = from_f32<E>(to_f32(up[e]) - acc[e]);
   }
-  __syncthreads();  // U complete; S^T no longer needed
-  for (int it = tid; it < D * D / 4; it += 256) {
-    const int v = it / (D / 4), c4 = 4 * (it % (D / 4));
-    const f32x4 x = *reinterpret_cast<const f32x4*>(ckdS + (size_t)v * D + c4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sX[(c4 + e) * LD + v] = from_f32<E>(x[e]);
-  }
-  if (tid < D) {
+  // dLC: rows c of dS' and S, 16-byte pieces, TPR threads per row (adjacent lanes)
+  {
+    constexpr int PPR = D / 8;                       // 8-element pieces per row
+    constexpr int TPR = 256 / D < PPR ? 256 / D : PPR;  // threads per row
+    const int c = tid / TPR, q = tid % TPR;
     float acc = 0.f;
-    for (int v = 0; v < D; ++v) acc = fmaf(ckdS[(size_t)v * D + tid], ckS[(size_t)v * D + tid], acc);
-    p.dLC[(size_t)rec * D + tid] = acc;
+    if (c < D)
+      for (int pc = q; pc < PPR; pc += TPR) {
+        float a8[8], b8[8];
+        load8(ckdS + (size_t)c * D + 8 * pc, a8);
+        load8(ckS + (size_t)c * D + 8 * pc, b8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc = fmaf(a8[e], b8[e], acc);
+      }
+    acc = group_sum<TPR>(acc);
+    if (c < D && q == 0) p.dLC[(size_t)rec * D + c] = acc;
   }
   __syncthreads();
 
@@ -383,11 +371,11 @@ __global__ __launch_bounds__(256) void kda_bwd_prod_kernel(BwdProdParams p) {
   for (int tile = wave; tile < RT * CT; tile += 4) {
     const int Rt = tile / CT, Ct = tile % CT;
     RowFrag<E, D> fdo, fdu, fu, fs, fds;
-    fdo.load(sDO + (16 * Rt + r) * LD, g4);
-    fdu.load(sDU + (16 * Rt + r) * LD, g4);
+    load_do(fdo, 16 * Rt + r);
+    fdu.load(gdU + (size_t)(16 * Rt + r) * D, g4);
     fu.load(sU + (16 * Rt + r) * LD, g4);
-    fs.load(sS + (16 * Ct + r) * LD, g4);
-    fds.load(sX + (16 * Ct + r) * LD, g4);
+    fs.load(ckS + (size_t)(16 * Ct + r) * D, g4);
+    fds.load(ckdS + (size_t)(16 * Ct + r) * D, g4);
     f32x4 aq = {0.f, 0.f, 0.f, 0.f}, aw = aq, ak = aq;
     mma<D>(aq, fdo, fs);
     mma<D>(aw, fdu, fs);
@@ -405,7 +393,7 @@ __global__ __launch_bounds__(256) void kda_bwd_prod_kernel(BwdProdParams p) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if (Jt <= It) {
       RowFrag<E, D> fa, fb;
-      fa.load(sDO + (16 * It + r) * LD, g4);
+      load_do(fa, 16 * It + r);
       fb.load(sU + (16 * Jt + r) * LD, g4);
       mma<D>(acc, fa, fb);
     }
@@ -448,17 +436,18 @@ __global__ __launch_bounds__(256) void kda_bwd_t_kernel(BwdTParams p) {
   const size_t plane = (size_t)p.B * p.T * HD;
 
   const float* gdW = p.dW + (size_t)rec * C * D;
-  const float* gdUt = p.dU + (size_t)rec * D * C;  // [v][t]
+  const E* gdU = static_cast<const E*>(p.dU) + (size_t)rec * C * D;  // [t][v]
   const float* gTt = p.tT + (size_t)rec * C * C;
   for (int it = tid; it < C * D / 4; it += 256) {
     const int t = it / (D / 4), c4 = 4 * (it % (D / 4));
     *reinterpret_cast<f32x4*>(&sdW[t * LD + c4]) = *reinterpret_cast<const f32x4*>(gdW + (size_t)t * D + c4);
   }
-  for (int it = tid; it < D * C / 4; it += 256) {
-    const int v = it / (C / 4), t4 = 4 * (it % (C / 4));
-    const f32x4 x = *reinterpret_cast<const f32x4*>(gdUt + (size_t)v * C + t4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sdU[(t4 + e) * LD + v] = x[e];
+  for (int it = tid; it < C * D / 8; it += 256) {
+    const int t = it / (D / 8), c8 = 8 * (it % (D / 8));
+    float x[8];
+    load8(gdU + (size_t)t * D + c8, x);
+    *reinterpret_cast<f32x4*>(&sdU[t * LD + c8]) = f32x4{x[0], x[1], x[2], x[3]};
+    *reinterpret_cast<f32x4*>(&sdU[t * LD + c8 + 4]) = f32x4{x[4], x[5], x[6], x[7]};
   }
   for (int it = tid; it < C * C / 4; it += 256) {
     const int j = it / (C / 4), i4 = 4 * (it % (C / 4));

@@ -117,7 +117,8 @@ struct StateParams {
   const float* o_norm_w;  // [D] or NULL
   float o_norm_eps;
   SeqTables seqs;         // packed sequences (then B = n_seqs, NT = chunk slots per head)
-  float* ckpt;            // backward mode: the state at each chunk start, S^T [rec][D][D], or NULL
+  void* ckpt;             // backward mode: the state at each chunk start in the element type,
+                          // S^T then S, [rec][2][D][D], or NULL
 };
 
 // The output stage on its own, in place on o: RMSNorm with gain and/or the
@@ -132,9 +133,9 @@ struct OutStageParams {
 
 // ------------------------------------------------------------------ backward
 // Workspace buffers of the backward pass, per record rec = (b * H + h) * NT + n:
-//   ckS  [rec][D][D]  S_n^T (state at the chunk start, row = value column)
-//   ckdS [rec][D][D]  dS_{n+1}^T (gradient of the chunk's end state)
-//   dU   [rec][D][C]  dU_n^T
+//   ckS  [rec][2][D][D]  S_n^T then S_n (the state at the chunk start), element type
+//   ckdS [rec][D][D]     dS_{n+1} (gradient of the chunk's end state), element type
+//   dU   [rec][C][D]     dU_n, element type
 //   dQL, dW, dKt [rec][C][D], dP [rec][C][C], dLC [rec][D]: gradients of the
 //   record's quantities;  dBk, dBv [rec][C][D], dA [rec][C][C]
 struct BwdWalkParams {
@@ -142,17 +143,17 @@ struct BwdWalkParams {
   const void* dO;      // [B][T][H][D]
   const float* dS_T;   // [B][H][D][D] or NULL
   float* dS0;          // [B][H][D][D] or NULL
-  float* dU;
-  float* ckdS;
+  void* dU;
+  void* ckdS;
   int B, T, H, NT;
 };
 
 struct BwdProdParams {
   const char* ws;      // forward records (W, U~)
   const void* dO;
-  const float* ckS;
-  const float* ckdS;
-  const float* dU;
+  const void* ckS;
+  const void* ckdS;
+  const void* dU;
   float* dQL;
   float* dW;
   float* dKt;
@@ -167,7 +168,7 @@ struct BwdTParams {
   const float* gam;
   const float* beta;
   const float* dW;
-  const float* dU;
+  const void* dU;
   float* dBk;
   float* dBv;
   float* dA;

@@ -335,14 +335,17 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void kda_chunk_state_kernel(
     load_gate(n);  // buffer n % 2: chunk n - 2's, stored during step n - 1
     if (n > 0) store_out(n - 1);
     if (p.ckpt != nullptr) {
-      // backward mode: S_n^T, four consecutive key channels per lane
+      // backward mode: S_n^T (four consecutive key channels per lane) and S_n
+      E* ck = static_cast<E*>(p.ckpt) + (rec0 + n) * 2 * D * D;
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
         const int u = wave + NW * i;
         if (FULL_S || u < CT * VT) {
           const int Ct = u % CT, Vt = u / CT;
-          *reinterpret_cast<f32x4*>(p.ckpt + (rec0 + n) * D * D + (size_t)(vb0 + 16 * Vt + r) * D +
-                                    16 * Ct + 4 * g4) = accS[i];
+          const int v = vb0 + 16 * Vt + r, c0 = 16 * Ct + 4 * g4;
+          store4(ck + (size_t)v * D + c0, accS[i][0], accS[i][1], accS[i][2], accS[i][3]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ck[(size_t)D * D + (size_t)(c0 + e) * D + v] = from_f32<E>(accS[i][e]);
         }
       }
     }
