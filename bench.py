@@ -89,6 +89,40 @@ def decode_bytes(w) -> int:
             + 2 * w.B * 3 * 3 * w.H * w.D * es + 3 * w.H * w.D * 16)
 
 
+def backward_bytes(w) -> dict:
+    """Algorithmic bytes per launch of each backward kernel (its inputs read once and
+    its outputs written once, with the intermediate buffers the kernels hand over:
+    records and checkpoints in the I/O type, per-chunk gradients in fp32) and of the
+    whole call ("path": raw inputs and dO in, every gradient and the recomputed
+    forward outputs out).  dS_T is not given in the benchmark."""
+    es = esize(w.io)
+    C, D = w.chunk, w.D
+    NT = -(-w.T // C)
+    nrec = w.B * w.H * NT
+    tok = w.B * w.T
+    xe, x4 = tok * w.H * D * es, tok * w.H * D * 4
+    bth4 = tok * w.H * 4
+    state = w.B * w.H * D * D * 4
+    cw = 3 * w.H * D * 4 * 4
+    cst_e = w.B * 3 * 3 * w.H * D * es if w.conv_state_std > 0 else 0
+    cst_4 = w.B * 3 * 3 * w.H * D * 4
+    s0 = state if w.s0_std > 0 else 0
+    cd, cc, dd = C * D, C * C, D * D
+    tokb = 4 * (256 // (D // 8))
+    nblk = -(-w.T // tokb)
+    return {
+        "walk": nrec * ((3 * cd + cc) * es + 4 * D) + xe + nrec * (cd + dd) * es + state,
+        "prod": nrec * (2 * cd + 3 * dd + cd) * es + xe + nrec * (3 * cd * 4 + cc * 4 + D * 4),
+        "t": nrec * (cc * 4 + cd * 4 + cd * es) + 3 * x4 + bth4 + nrec * (2 * cd + cc) * 4,
+        "pair": 4 * x4 + bth4 + nrec * (2 * cc + 4 * cd + D) * 4 + 4 * x4 + bth4,
+        "front": 3 * xe + cw + cst_e + 3 * x4 + bth4 + 3 * x4 + w.B * nblk * 3 * w.H * D * 16
+                 + cst_4 + bth4,
+        "path": 4 * xe + tok * w.H * es + cw + cst_e + s0 + xe  # q, k, v, g, beta, filters, history, S0, dO
+                + 4 * x4 + bth4 + state + cw + cst_4        # dq, dk, dv, dg, dbeta, dS0, dconv_w, dconv_state
+                + xe + state + cst_e,                       # o, S_T, conv hand-over recomputed
+    }
+
+
 def stage_bytes(w) -> dict:
     """Extra algorithmic bytes of the optional stages: the gate pre-activation read
     once in the fused minimum; the separate output pass reads o and the gate and
@@ -296,8 +330,11 @@ def backward_leg(kda, torch, w, args, stream, dev, plain_ms):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
+    nb = backward_bytes(w)["path"]
     out = {"workload": w.name, "ms_per_step": ms, "tokens_per_s": w.B * w.T / (ms / 1e3),
            "ratio_to_forward": ms / plain_ms, "workspace_bytes": ws.numel(),
+           "path_bytes": nb, "path_GBps": nb / (ms / 1e3) / 1e9,
+           "path_frac_hbm": nb / (ms / 1e3) / HBM_PEAK,
            "includes": "recomputed forward + reverse walk + per-chunk gradient kernels + front end"}
     del ws, inp, grads, o, S_T, cso, do
     torch.cuda.empty_cache()

@@ -58,7 +58,7 @@ struct RecImage {
 // GN: apply the output stage (RMSNorm with gain over the head's D values, sigmoid
 // gate) before storing o.  Only with VB == D, where one workgroup holds every
 // value column of its tokens.
-template <int D, int C, int VB, typename IO, typename E, int NT, bool GN>
+template <int D, int C, int VB, typename IO, typename E, int NT, bool GN, bool CK>
 __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void kda_chunk_state_kernel(StateParams p) {
   static_assert(!GN || VB == D, "the output stage needs whole rows");
   constexpr int NW = NT / 64;  // waves
@@ -334,7 +334,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void kda_chunk_state_kernel(
     if (n + 1 < nch) issue_copy(n + 1);
     load_gate(n);  // buffer n % 2: chunk n - 2's, stored during step n - 1
     if (n > 0) store_out(n - 1);
-    if (p.ckpt != nullptr) {
+    if constexpr (CK) {
       // backward mode: S_n^T (four consecutive key channels per lane) and S_n
       E* ck = static_cast<E*>(p.ckpt) + (rec0 + n) * 2 * D * D;
 #pragma unroll
@@ -418,6 +418,21 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void kda_chunk_state_kernel(
   }
 }
 
+// One instantiation; CK (the backward mode's checkpoints) follows p.ckpt, so the
+// forward walk carries no checkpoint code.
+template <int D, int C, int VB, typename IO, typename E, int NT, bool GN>
+static hipError_t launch_walk(const StateParams& p, size_t grid, hipStream_t st) {
+  if (p.ckpt != nullptr) {
+    if constexpr (GN) return hipErrorInvalidValue;  // no output stage in the backward mode
+    else hipLaunchKernelGGL((kda_chunk_state_kernel<D, C, VB, IO, E, NT, false, true>),
+                            dim3((unsigned)grid), dim3(NT), 0, st, p);
+  } else {
+    hipLaunchKernelGGL((kda_chunk_state_kernel<D, C, VB, IO, E, NT, GN, false>), dim3((unsigned)grid),
+                       dim3(NT), 0, st, p);
+  }
+  return hipGetLastError();
+}
+
 template <int D, int C, typename IO, typename E>
 static hipError_t launch_state_t(const StateParams& p, int vb, int threads, bool gn,
                                  hipStream_t st) {
@@ -426,32 +441,22 @@ static hipError_t launch_state_t(const StateParams& p, int vb, int threads, bool
   // threads, D <= 64.
   const size_t BH = (size_t)p.B * p.H;
   if constexpr (D == 128) {
-    if (!gn && vb == 64 && threads == 512) {
-      hipLaunchKernelGGL((kda_chunk_state_kernel<D, C, 64, IO, E, 512, false>),
-                         dim3((unsigned)(BH * 2)), dim3(512), 0, st, p);
-      return hipGetLastError();
-    }
+    if (!gn && vb == 64 && threads == 512) return launch_walk<D, C, 64, IO, E, 512, false>(p, BH * 2, st);
   }
   if (threads != 256) return hipErrorInvalidValue;
   if (gn) {
     if constexpr (D <= 64) {
       if (vb != D) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((kda_chunk_state_kernel<D, C, D, IO, E, 256, true>), dim3((unsigned)BH),
-                         dim3(256), 0, st, p);
-      return hipGetLastError();
+      return launch_walk<D, C, D, IO, E, 256, true>(p, BH, st);
     }
     return hipErrorInvalidValue;
   }
   constexpr int VBmax = D >= 64 ? 64 : D;
   if (vb == 32 && D >= 32) {
     constexpr int VB = D >= 32 ? 32 : D;
-    hipLaunchKernelGGL((kda_chunk_state_kernel<D, C, VB, IO, E, 256, false>),
-                       dim3((unsigned)(BH * (D / VB))), dim3(256), 0, st, p);
-  } else {
-    hipLaunchKernelGGL((kda_chunk_state_kernel<D, C, VBmax, IO, E, 256, false>),
-                       dim3((unsigned)(BH * (D / VBmax))), dim3(256), 0, st, p);
+    return launch_walk<D, C, VB, IO, E, 256, false>(p, BH * (D / VB), st);
   }
-  return hipGetLastError();
+  return launch_walk<D, C, VBmax, IO, E, 256, false>(p, BH * (D / VBmax), st);
 }
 
 template <int D, typename IO, typename E>
