@@ -438,9 +438,24 @@ __global__ __launch_bounds__(fast_threads<E>()) void kda_chunk_prep_kernel(PrepP
 
   // ---------------------------------------------------------------- phase 3
   float* sA = reinterpret_cast<float*>(sm.r1);  // [C][LA]
-  float* sT = sA + C * LA;                      // [C][LA]
+  float* sT = sA + C * LA;                      // [C][LA]: the lower block triangle of T
   float* scr = sT + C * LA;                     // [4][16][17]
-  for (int it = tid; it < C * LA; it += NTH) sT[it] = 0.f;
+  // T in the matrix-core element type, after A / T / scratch, written by the solve
+  // as it goes.  The causal k-steps of the W, U~ products read row tile It up to
+  // column ceil(16 (It + 1) / STEPC) STEPC: the part of that beyond the diagonal
+  // block is zero.
+  E* tb = reinterpret_cast<E*>(sm.r1 + SM::TB_OFF);
+  {
+    constexpr int STEPC = RowFrag<E, C>::STEP;
+    for (int It = 0; It < NB; ++It) {
+      const int c0 = 16 * (It + 1);
+      const int ce0 = (c0 + STEPC - 1) / STEPC * STEPC;
+      const int ce = ce0 < C ? ce0 : C;
+      const int w = ce - c0;  // columns to clear in each of the tile's 16 rows
+      for (int it = tid; it < 16 * w; it += NTH)
+        tb[(16 * It + it / w) * LT + c0 + it % w] = from_f32<E>(0.f);
+    }
+  }
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
     const int R = tR[i], Q = tQ[i];
@@ -475,7 +490,10 @@ __global__ __launch_bounds__(fast_threads<E>()) void kda_chunk_prep_kernel(PrepP
       x[i] = acc;
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sT[(16 * pq + i) * LA + 16 * pq + col] = x[i];
+    for (int i = 0; i < 16; ++i) {
+      sT[(16 * pq + i) * LA + 16 * pq + col] = x[i];
+      tb[(16 * pq + i) * LT + 16 * pq + col] = from_f32<E>(x[i]);
+    }
   }
   __syncthreads();
   // off-diagonal blocks, block row by block row (wave qb computes block column qb):
@@ -507,7 +525,10 @@ __global__ __launch_bounds__(fast_threads<E>()) void kda_chunk_prep_kernel(PrepP
         acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a, bv, acc, 0, 0, 0);
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) sT[(16 * pr + 4 * g4 + e) * LA + 16 * qb + r] = -acc[e];
+      for (int e = 0; e < 4; ++e) {
+        sT[(16 * pr + 4 * g4 + e) * LA + 16 * qb + r] = -acc[e];
+        tb[(16 * pr + 4 * g4 + e) * LT + 16 * qb + r] = from_f32<E>(-acc[e]);
+      }
     }
     __syncthreads();
   }
@@ -518,12 +539,6 @@ __global__ __launch_bounds__(fast_threads<E>()) void kda_chunk_prep_kernel(PrepP
       const int jj = it / C, i = it % C;  // to[jj][i] = T[i][jj]
       to[it] = jj <= i ? sT[i * LA + jj] : 0.f;
     }
-  }
-  // T in the matrix-core element type, after A / T / scratch
-  E* tb = reinterpret_cast<E*>(sm.r1 + SM::TB_OFF);
-  for (int it = tid; it < C * C; it += NTH) {
-    const int i = it / C, jj = it % C;
-    tb[i * LT + jj] = from_f32<E>(sT[i * LA + jj]);
   }
   __syncthreads();  // A and T (float) are dead
 
