@@ -121,15 +121,18 @@ __device__ __forceinline__ void store_filters(const FilterRegs<D, NT>& f, float*
 
 // Raw rows of q, k, v (x = 0, 1, 2) for one thread's tile of TOK tokens from
 // t_first, channels [ch, ch + 8) of head h.  The workgroup's threads together
-// cover tokens [t_base, t_base + n_tok) (the same values for all of them).  With the convolution, row m holds token
-// t_first - 3 + m (TOK + 3 rows); tokens < 0 read the carried state
-// ([B][3 tensors][3 taps][H*D], oldest tap first).  Without it, row 3 + m holds
-// token t_first + m.  Rows that read nothing (tokens >= T, or < 0 with no
-// state) read zeros: every row goes through a range-checked buffer load whose
-// range ends at the sequence's last row (or the state's last tap; the check is
-// on the per-lane offset, where rows before the range wrap to huge values), so
-// all loads are issued unconditionally with 32-bit offset arithmetic.  Needs
-// T > 0 and (n_tok + 3) * H * D * sizeof(IO) < 2 GiB.
+// cover tokens [t_base, t_base + n_tok) (the same values for all of them).  Row m
+// holds token t_first - 3 + m (TOK + 3 rows); with the convolution, tokens < 0
+// read the carried state ([B][3 tensors][3 taps][H*D], oldest tap first).
+// Without it rows 0..2 are not used (the range starts at t_base).  Rows that
+// read nothing (tokens >= T, before the range, or < 0 with no state) read
+// zeros: every row goes through a range-checked buffer load whose range ends at
+// the sequence's last row (or the state's last tap; the check is on the
+// per-lane offset, where rows before the range wrap to huge values), so all
+// loads are issued unconditionally, into the same rows in both modes (a branch
+// between the modes would make the compiler wait for the loads where it joins),
+// with 32-bit offset arithmetic.  Needs T > 0 and
+// (n_tok + 3) * H * D * sizeof(IO) < 2 GiB.
 template <int TOK, typename IO>
 __device__ __forceinline__ void front_load(const IO* q, const IO* k, const IO* v, const IO* state,
                                            bool conv, int b, int T, int H, int D, int h, int ch,
@@ -143,19 +146,13 @@ __device__ __forceinline__ void front_load(const IO* q, const IO* k, const IO* v
   const int r1 = t_base + n_tok < T ? t_base + n_tok : T;
   const unsigned bytes = (unsigned)(((long)(r1 - 1 - r0) * HD + D) * ES);
   const int row_b = (int)(HD * ES);
-  const int t0 = conv ? t_first - 3 : t_first;  // token of row (conv ? 0 : 3)
-  const int voff = (t0 - r0) * row_b + ch * ES;  // negative rows fall out of range
+  const int voff = (t_first - 3 - r0) * row_b + ch * ES;  // negative rows fall out of range
 #pragma unroll
   for (int x = 0; x < 3; ++x) {
     const IO* src = x == 0 ? q : (x == 1 ? k : v);
     const BufRes rx = make_buf(src + ((long)b * T + r0) * HD + (long)h * D, bytes);
-    if (conv) {
 #pragma unroll
-      for (int m = 0; m < TOK + 3; ++m) win[x][m].load(rx, voff + m * row_b, 0);
-    } else {
-#pragma unroll
-      for (int m = 0; m < TOK; ++m) win[x][3 + m].load(rx, voff + m * row_b, 0);
-    }
+    for (int m = 0; m < TOK + 3; ++m) win[x][m].load(rx, voff + m * row_b, 0);
   }
   if (conv && state != nullptr && t_base < 3) {
     // the first rows of the sequence: taps before token 0 come from the state,
