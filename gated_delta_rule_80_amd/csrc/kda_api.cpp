@@ -480,7 +480,7 @@ namespace {
 // Workspace of the backward pass: the forward workspace, then float32 buffers
 // (see kda_layout.h), each 256-byte aligned.
 struct BwdLayout {
-  size_t tT, y, gam, beta, ckS, ckdS, dU, dQL, dW, dKt, dP, dLC, dBk, dBv, dA, dy, dbp, dcp;
+  size_t tT, y, gam, beta, ckS, ckdS, dU, dQL, dW, dKt, dP, dLC, dBk, dBv, dA, dy, dbp, dcp, pl;
   size_t bytes;
   size_t nfront;  // front-end workgroups per (b, h)
 };
@@ -520,6 +520,7 @@ BwdLayout bwd_layout(const kda_backward_args* a) {
   L.dbp = take(bth);
   L.nfront = kda::bwd_front_blocks(f->T, f->D);
   L.dcp = take(f->conv_k > 0 ? (size_t)f->B * L.nfront * 3 * f->H * D * 4 : 0);
+  L.pl = take(64 + nrec);  // count (256-byte header), then the list of records
   L.bytes = off;
   return L;
 }
@@ -648,6 +649,8 @@ kda_status kda_prefill_backward(const kda_backward_args* a, void* ws, size_t ws_
   B.pair.dA = F(L.dA); B.pair.dP = F(L.dP); B.pair.dQL = F(L.dQL); B.pair.dKt = F(L.dKt);
   B.pair.dLC = F(L.dLC); B.pair.dBk = F(L.dBk); B.pair.dBv = F(L.dBv);
   B.pair.dy = F(L.dy); B.pair.dg = a->dg; B.pair.dbeta_part = F(L.dbp);
+  B.pair.ex_count = reinterpret_cast<unsigned*>(wsb + L.pl);
+  B.pair.ex_list = B.pair.ex_count + 64;
   B.pair.B = f->B; B.pair.T = f->T; B.pair.H = f->H; B.pair.NT = sz.NT;
   B.front.q = f->q; B.front.k = f->k; B.front.v = f->v;
   B.front.conv_w = f->conv_k > 0 ? f->conv_w : nullptr;

@@ -543,9 +543,228 @@ __global__ __launch_bounds__(256) void kda_bwd_t_kernel(BwdTParams p) {
   }
 }
 
+// ------------------------------------------ pair and element terms, factored
+// The pair terms of A and P,
+//   rK_i = sum_{j<i} dA_ij k_j E_ij,   rQ_i = sum_{j<=i} dP_ij k_j E_ij,
+//   cK_j = sum_{i>=j} E_ij (beta_i dA_ij k_i + dP_ij q'_i)          (per channel),
+// with E_ij = exp(Gamma_i - Gamma_j) factored as in the forward preparation:
+// for i in 16-token block p and j in block q, with m_p the middle of block p's
+// log-decay range,  E_ij = a_i F_pq b_j,  a_i = exp(Gamma_i - m_p),
+// b_j = exp(m_q - Gamma_j),  F_pq = exp(m_p - m_q) (1 for p = q).  Then per block
+// pair (p, q <= p) and channel tile, float32 matrix-core products:
+//   rK_p += F_pq (dA_pq (K b)_q),   rQ_p += F_pq (dP_pq (K b)_q),
+//   cK_q += F_pq (dA_pq^T (beta K a)_p + dP_pq^T (Q' a)_p),
+// and rK, rQ take the factor a, cK the factor b.  dA and dP are exactly zero above
+// their diagonals, so the pairs j > i (whose a_i b_j exceed 1) add nothing.  a and b
+// lie within exp(+-s/2) for a block span s: chunks with a span above kBwdSpan2
+// (log2 units) are listed for the exact kernel, which keeps the products' partial
+// sums (up to 16 |dA| 2^(s/2)) far from the float32 range.
+// One workgroup per chunk record; wave w owns channels [16 w, 16 w + 16).  Lane
+// (r, g4) holds the operands of rows 4 s + g4 (s < C / 4) of its channel 16 w + r
+// (the matrix-core B layout), and its results for rows 16 p + 4 g4 + e.  Row
+// block by row block: the products that finish rK, rQ and cK of the block, then
+// its element terms as in the exact kernel.
+constexpr float kBwdSpan2 = 128.f;
+
+template <int D, int C>
+__global__ __launch_bounds__(4 * D, D / 32 > 1 ? D / 32 : 1) void kda_bwd_pair_mma_kernel(BwdPairParams p) {
+  constexpr int NTH = 4 * D;
+  constexpr int NB = C / 16;
+  constexpr int NS = C / 4;     // rows per lane in the B layout
+  constexpr int LA = C + 2;     // dA, dP rows (row reads of 16 lanes x 4 columns spread over the banks)
+  constexpr int LD = D + 4;     // dGamma rows
+  __shared__ __attribute__((aligned(16))) float sreg[2 * C * LA];  // dA, dP
+  __shared__ __attribute__((aligned(16))) float sG[C * LD];         // dGamma
+  __shared__ float sdbw[(D / 16) * C];  // dbeta partial sums per wave
+  __shared__ float sGC[D];
+  __shared__ float sB[C];
+  __shared__ int sfat[D / 16];  // per wave: a block span of its channels is too wide
+  float* sdA = sreg;
+  float* sdP = sreg + C * LA;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, g4 = lane >> 4;
+  const int c = 16 * wave + r;  // this lane's channel
+  const int rec = blockIdx.x;
+  const int n = rec % p.NT;
+  const int bh = rec / p.NT;
+  const int h = bh % p.H, b = bh / p.H;
+  const size_t HD = (size_t)p.H * D;
+  const size_t plane = (size_t)p.B * p.T * HD;
+  const int nval = p.T - n * C < C ? p.T - n * C : C;  // tokens of the sequence in this chunk
+  auto row_of = [&](int t) { return ((size_t)b * p.T + (size_t)n * C + t) * HD + (size_t)h * D; };
+  // Gamma of row t (past the end of the sequence g = 0: Gamma keeps its last value)
+  auto gam_at = [&](int t) { return p.gam[row_of(t < nval ? t : nval - 1) + c]; };
+
+  // ---- B-layout operands of this lane: rows 4 s + g4
+  float gB[NS], kB[NS], qB[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const int t = 4 * s + g4;
+    const bool in = t < nval;
+    gB[s] = gam_at(t);
+    kB[s] = in ? p.y[plane + row_of(t) + c] : 0.f;
+    qB[s] = in ? p.y[row_of(t) + c] : 0.f;
+  }
+  if (tid < C) sB[tid] = tid < nval ? p.beta[((size_t)b * p.T + (size_t)n * C + tid) * p.H + h] : 0.f;
+  // block boundaries G_1 .. G_NB (Gamma at the last row of each block: lane
+  // (r, 3), s = 4 p + 3) and the midpoints m_p = (G_p + G_p+1) / 2, G_0 = 0
+  float mid[NB];
+  bool fatal = false;
+  {
+    float gprev = 0.f;
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      const float gend = __shfl(gB[4 * q + 3], 48 + r, 64);
+      mid[q] = 0.5f * (gprev + gend);
+      fatal |= gprev - gend > kBwdSpan2;
+      gprev = gend;
+    }
+  }
+  {
+    const bool wfat = __any(fatal);
+    if (lane == 0) sfat[wave] = wfat ? 1 : 0;
+  }
+  // dA and dP into LDS
+  const float* gdA = p.dA + (size_t)rec * C * C;
+  const float* gdP = p.dP + (size_t)rec * C * C;
+  for (int it = tid; it < C * C / 4; it += NTH) {
+    const int i = it / (C / 4), j4 = 4 * (it % (C / 4));
+    const f32x4 va = *reinterpret_cast<const f32x4*>(gdA + (size_t)i * C + j4);
+    const f32x4 vp = *reinterpret_cast<const f32x4*>(gdP + (size_t)i * C + j4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sdA[i * LA + j4 + e] = va[e];
+      sdP[i * LA + j4 + e] = vp[e];
+    }
+  }
+  __syncthreads();
+  bool anyfat = false;
+#pragma unroll
+  for (int w = 0; w < D / 16; ++w) anyfat |= sfat[w] != 0;
+  if (anyfat) {
+    if (tid == 0) {
+      const unsigned slot = atomicAdd(p.ex_count, 1u);
+      p.ex_list[slot] = (unsigned)rec;
+    }
+    return;
+  }
+  // K b, beta K a, Q' a
+  float kb[NS], bka[NS], qa[NS];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const float m = mid[s / 4];
+    const float a = __builtin_amdgcn_exp2f(gB[s] - m), bb = __builtin_amdgcn_exp2f(m - gB[s]);
+    kb[s] = kB[s] * bb;
+    bka[s] = sB[4 * s + g4] * kB[s] * a;
+    qa[s] = qB[s] * a;
+  }
+
+  // ---- per row block pb: the block-pair products, then its element terms
+  float* sdG = sG;  // [C][LD]
+  const float gC = gam_at(C - 1);
+  const float* gdQL = p.dQL + (size_t)rec * C * D;
+  const float* gdKt = p.dKt + (size_t)rec * C * D;
+  const float* gdBk = p.dBk + (size_t)rec * C * D;
+  const float* gdBv = p.dBv + (size_t)rec * C * D;
+  float colsum = 0.f;  // sum over this lane's rows of dKt Ktil
+#pragma unroll
+  for (int pb = 0; pb < NB; ++pb) {
+    f32x4 tK = {0.f, 0.f, 0.f, 0.f}, tQ = tK, tC = tK;
+    // rK, rQ of rows in block pb: column blocks qb <= pb
+#pragma unroll
+    for (int qb = 0; qb <= pb; ++qb) {
+      const float F = pb == qb ? 1.f : __builtin_amdgcn_exp2f(mid[pb] - mid[qb]);
+      f32x4 xk = {0.f, 0.f, 0.f, 0.f}, xq = xk;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        // rows (16 pb + r), columns (16 qb + 4 s + g4)
+        const float a_ = sdA[(16 * pb + r) * LA + 16 * qb + 4 * s + g4];
+        const float p_ = sdP[(16 * pb + r) * LA + 16 * qb + 4 * s + g4];
+        xk = __builtin_amdgcn_mfma_f32_16x16x4f32(a_, kb[4 * qb + s], xk, 0, 0, 0);
+        xq = __builtin_amdgcn_mfma_f32_16x16x4f32(p_, kb[4 * qb + s], xq, 0, 0, 0);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        tK[e] = fmaf(F, xk[e], tK[e]);
+        tQ[e] = fmaf(F, xq[e], tQ[e]);
+      }
+    }
+    // cK of columns in block pb: row blocks rb >= pb
+#pragma unroll
+    for (int rb = pb; rb < NB; ++rb) {
+      const float F = rb == pb ? 1.f : __builtin_amdgcn_exp2f(mid[rb] - mid[pb]);
+      f32x4 xc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        // transposed reads: rows (16 rb + 4 s + g4), columns (16 pb + r)
+        const float at = sdA[(16 * rb + 4 * s + g4) * LA + 16 * pb + r];
+        const float pt = sdP[(16 * rb + 4 * s + g4) * LA + 16 * pb + r];
+        xc = __builtin_amdgcn_mfma_f32_16x16x4f32(at, bka[4 * rb + s], xc, 0, 0, 0);
+        xc = __builtin_amdgcn_mfma_f32_16x16x4f32(pt, qa[4 * rb + s], xc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tC[e] = fmaf(F, xc[e], tC[e]);
+    }
+    // element terms for rows t = 16 pb + 4 g4 + e of channel c
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int t = 16 * pb + 4 * g4 + e;
+      const bool in = t < nval;
+      const size_t lo = (size_t)t * D + c;
+      const float dql = gdQL[lo], dkt = gdKt[lo], dbk = gdBk[lo], dbv = gdBv[lo];
+      const float gt = gam_at(t);
+      float kk = 0.f, qq = 0.f, vv = 0.f;
+      if (in) {
+        const size_t o = row_of(t) + c;
+        qq = p.y[o];
+        kk = p.y[plane + o];
+        vv = p.y[2 * plane + o];
+      }
+      const float bt = sB[t];
+      const float a = __builtin_amdgcn_exp2f(gt - mid[pb]), bb = __builtin_amdgcn_exp2f(mid[pb] - gt);
+      const float rK = a * tK[e], rQ = a * tQ[e], ckt = bb * tC[e];
+      const float lam = __builtin_amdgcn_exp2f(gt);
+      const float ec = __builtin_amdgcn_exp2f(gC - gt);
+      const float ktil = kk * ec;
+      colsum = fmaf(dkt, ktil, colsum);
+      sdG[t * LD + c] = dbk * bt * kk * lam + dql * qq * lam - dkt * ktil + bt * kk * rK + qq * rQ - kk * ckt;
+      if (in) {
+        const size_t o = row_of(t) + c;
+        p.dy[o] = lam * dql + rQ;
+        p.dy[plane + o] = bt * lam * dbk + ec * dkt + bt * rK + ckt;
+        p.dy[2 * plane + o] = bt * dbv;
+      }
+      // dbeta: this wave's 16 channels of row t
+      const float dbp = group_sum<16>(dbv * vv + dbk * kk * lam + kk * rK);
+      if (r == 0) sdbw[wave * C + t] = dbp;
+    }
+  }
+  colsum += __shfl_xor(colsum, 16, 64);
+  colsum += __shfl_xor(colsum, 32, 64);
+  if (g4 == 0) sGC[c] = colsum + p.dLC[(size_t)rec * D + c] * __builtin_amdgcn_exp2f(gC);
+  __syncthreads();
+  // dg: reverse running sum over the chunk, one thread per channel
+  if (tid < D) {
+    float acc = sGC[tid];
+    for (int t = C - 1; t >= 0; --t) {
+      acc += sdG[t * LD + tid];
+      if (t < nval) p.dg[row_of(t) + tid] = acc;
+    }
+  }
+  // dbeta: sum over the waves, one thread per token
+  if (tid < nval) {
+    float acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < D / 16; ++w) acc += sdbw[w * C + tid];
+    p.dbeta_part[((size_t)b * p.T + (size_t)n * C + tid) * p.H + h] = acc;
+  }
+}
+
 // ------------------------------------------------- pair and element terms, dg
-// One workgroup per chunk record, TPC = C / 16 threads per channel (adjacent
-// lanes) and all D channels.  Per channel c, with E_ij = exp(Gamma_ic - Gamma_jc)
+// Exact form, for the chunks the factored kernel above lists (decay spans too
+// wide to factor): workgroup i takes listed record i, TPC = C / 16 threads per
+// channel (adjacent lanes) and all D channels.  Per channel c, with E_ij = exp(Gamma_ic - Gamma_jc)
 // for j <= i (at most 1, evaluated once per pair):
 //   row i:    rK_i = sum_{j<i} dA_ij k_jc E_ij,   rQ_i = sum_{j<=i} dP_ij k_jc E_ij
 //   column j: cK_j = sum_{i>=j} E_ij (beta_i dA_ij k_ic + dP_ij q'_ic)
@@ -582,7 +801,10 @@ __global__ __launch_bounds__(D * (C / 16)) void kda_bwd_pair_kernel(BwdPairParam
   float* sdP = sAP + C * LA;
 
   const int tid = threadIdx.x;
-  const int rec = blockIdx.x;
+  // workgroup i takes listed record i (the grid covers every record; most exit here)
+  if (blockIdx.x >= *p.ex_count) return;
+  const int rec = (int)p.ex_list[blockIdx.x];
+  if (rec >= p.B * p.H * p.NT) return;  // (the list holds record indices only)
   const int n = rec % p.NT;
   const int bh = rec / p.NT;
   const int h = bh % p.H, b = bh / p.H;
@@ -952,6 +1174,11 @@ __global__ __launch_bounds__(256, 2) void kda_bwd_front_kernel(BwdFrontParams p,
   (void)SPW;
 }
 
+// Clears the count of chunks listed for the exact pair kernel.
+__global__ void kda_bwd_clear_kernel(unsigned* count) {
+  if (threadIdx.x == 0) *count = 0u;
+}
+
 // dconv_w = the sum of the workgroups' partials (fixed order: deterministic)
 __global__ __launch_bounds__(256) void kda_bwd_conv_reduce_kernel(const float* part, float* out,
                                                                   size_t n, int nparts) {
@@ -981,7 +1208,12 @@ static hipError_t launch_bwd_t(const BwdLaunch& L, hipStream_t st) {
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   hipLaunchKernelGGL((kda_bwd_t_kernel<D, C, E>), dim3((unsigned)nrec), dim3(256), 0, st, L.tside);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-  constexpr int NBLK = 1;  // the pair kernel sums dbeta over all channels itself
+  constexpr int NBLK = 1;  // the pair kernels sum dbeta over all channels themselves
+  // factored products for every chunk; the exact kernel takes the ones they list
+  hipLaunchKernelGGL(kda_bwd_clear_kernel, dim3(1), dim3(64), 0, st, L.pair.ex_count);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  hipLaunchKernelGGL((kda_bwd_pair_mma_kernel<D, C>), dim3((unsigned)nrec), dim3(4 * D), 0, st, L.pair);
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   constexpr int PNTH = PairShape<D, C>::NTH;
   hipLaunchKernelGGL((kda_bwd_pair_kernel<D, C>), dim3((unsigned)nrec), dim3(PNTH), 0, st, L.pair);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;

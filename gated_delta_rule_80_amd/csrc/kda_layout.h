@@ -189,6 +189,10 @@ struct BwdPairParams {
   float* dy;           // [3][B*T*H*D]: gradients of (scale * q_hat, k_hat, v_hat)
   float* dg;           // [B*T*H*D]
   float* dbeta_part;   // [B*T*H]: dbeta
+  // chunks whose decay spans are too wide for the factored products: a count
+  // (cleared before the factored kernel) and the list the per-pair kernel takes
+  unsigned* ex_count;
+  unsigned* ex_list;
   int B, T, H, NT;
 };
 

@@ -18,8 +18,14 @@ pytestmark = pytest.mark.gpu
 NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dS0", "dconv_w", "dconv_state")
 
 
-def check_backward(w, chunk, seed=0, conv=True, l2=True, scale=1.0, with_dST=True):
+def check_backward(w, chunk, seed=0, conv=True, l2=True, scale=1.0, with_dST=True, g_head=None):
     inp = make(w, seed)
+    if g_head is not None:
+        # constant log-decay per token on the given heads: {head: g}
+        g = inp["g"].clone()
+        for hh, val in g_head.items():
+            g[:, :, hh, :] = val
+        inp = dict(inp, g=g)
     if not conv:
         inp = dict(inp, conv_w=None, conv_state=None)
     gen = torch.Generator().manual_seed(seed + 1000)
@@ -77,6 +83,17 @@ def test_backward_front_end_modes(conv, l2):
 def test_backward_strong_decay_bf16():
     w = small(B=1, T=200, H=2, D=128, io="bf16", chunk=64, strong=True, s0=True, conv_state=True)
     check_backward(w, 64, seed=7)
+
+
+@pytest.mark.parametrize("io,D,chunk", [("bf16", 128, 64), ("fp32", 64, 32), ("bf16", 32, 16)])
+@pytest.mark.parametrize("g0", [-12.0, -5.2])
+def test_backward_factored_and_exact_pair_paths(io, D, chunk, g0):
+    """Head 0 decays by a constant g0 per token: -12 gives 16-token block spans of
+    about 277 log2 units, beyond the factored pair products' limit (the chunks go to
+    the exact per-pair kernel); -5.2 gives about 120, just inside it (the widest
+    factors the factored kernel meets).  Head 1 keeps its drawn decays."""
+    w = small(B=1, T=150, H=2, D=D, io=io, chunk=chunk, s0=True, conv_state=True)
+    check_backward(w, chunk, seed=17, g_head={0: g0})
 
 
 def test_backward_without_state_gradients():
