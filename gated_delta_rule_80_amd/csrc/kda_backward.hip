@@ -283,6 +283,24 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_walk_kernel(BwdWalkParams p) {
   }
 }
 
+// sum over a lane's elements of two fragments of the same rows
+template <int K>
+__device__ __forceinline__ float frag_dot(const RowFrag<__bf16, K>& a, const RowFrag<__bf16, K>& b) {
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < RowFrag<__bf16, K>::N; ++i)
+#pragma unroll
+    for (int e = 0; e < RowFrag<__bf16, K>::PER; ++e) acc = fmaf((float)a.v[i][e], (float)b.v[i][e], acc);
+  return acc;
+}
+template <int K>
+__device__ __forceinline__ float frag_dot(const RowFrag<float, K>& a, const RowFrag<float, K>& b) {
+  float acc = 0.f;
+#pragma unroll
+  for (int i = 0; i < RowFrag<float, K>::N; ++i) acc = fmaf(a.v[i], b.v[i], acc);
+  return acc;
+}
+
 // ------------------------------------------------------- per-chunk state products
 // One 256-thread workgroup per chunk record.  In the NT products
 // C[i][j] = sum_k A[i][k] B[j][k] (operands k-contiguous, element type, float
@@ -293,7 +311,7 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_walk_kernel(BwdWalkParams p) {
 //   dW   = -dU S^T:    A = dU rows t,           B = S rows c
 //   dKt  = U dS'^T:    A = U rows t,            B = dS' rows c
 //   dP   = dO U^T:     A = dO rows i,           B = U rows j      (j <= i)
-//   dLC  = rowsum(dS' * S)
+//   dLC  = rowsum(dS' * S), from the S and dS' fragments of the dQL, dKt tiles
 template <int D, int C, typename IO, typename E>
 __global__ __launch_bounds__(256) void kda_bwd_prod_kernel(BwdProdParams p) {
   constexpr int PE = 16 / (int)sizeof(E);
@@ -330,36 +348,26 @@ __global__ __launch_bounds__(256) void kda_bwd_prod_kernel(BwdProdParams p) {
     }
   };
 
+  // Wave w owns t-tile Rt = w % RT (its row strips of W, dO, dU and U are
+  // loaded once) and every WPR-th column tile from w / RT, so the four waves
+  // read each checkpoint strip at about the same time (once from memory).
+  constexpr int WPR = 4 / RT;  // waves per t-tile
+  const int Rt = wave % RT, sub = wave / RT;
   // ---- U = U~ - W S  (tiles (t, v))
-  for (int tile = wave; tile < RT * CT; tile += 4) {
-    const int Rt = tile / CT, Vt = tile % CT;
-    RowFrag<E, D> fa, fb;
-    fa.load(gW + (size_t)(16 * Rt + r) * D, g4);
-    fb.load(ckSt + (size_t)(16 * Vt + r) * D, g4);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    mma<D>(acc, fa, fb);
-    // U~ in fragment order: tile (t-tile, v-tile) of 64 lanes x 4 values
-    const E* up = gU + ((size_t)(Rt * CT + Vt) * 64 + lane) * 4;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      sU[(16 * Rt + 4 * g4 + e) * LD + 16 * Vt + r] = from_f32<E>(to_f32(up[e]) - acc[e]);
-  }
-  // dLC: rows c of dS' and S, 16-byte pieces, TPR threads per row (adjacent lanes)
   {
-    constexpr int PPR = D / 8;                       // 8-element pieces per row
-    constexpr int TPR = 256 / D < PPR ? 256 / D : PPR;  // threads per row
-    const int c = tid / TPR, q = tid % TPR;
-    float acc = 0.f;
-    if (c < D)
-      for (int pc = q; pc < PPR; pc += TPR) {
-        float a8[8], b8[8];
-        load8(ckdS + (size_t)c * D + 8 * pc, a8);
-        load8(ckS + (size_t)c * D + 8 * pc, b8);
+    RowFrag<E, D> fa;
+    fa.load(gW + (size_t)(16 * Rt + r) * D, g4);
+    for (int Vt = sub; Vt < CT; Vt += WPR) {
+      RowFrag<E, D> fb;
+      fb.load(ckSt + (size_t)(16 * Vt + r) * D, g4);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      mma<D>(acc, fa, fb);
+      // U~ in fragment order: tile (t-tile, v-tile) of 64 lanes x 4 values
+      const E* up = gU + ((size_t)(Rt * CT + Vt) * 64 + lane) * 4;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc = fmaf(a8[e], b8[e], acc);
-      }
-    acc = group_sum<TPR>(acc);
-    if (c < D && q == 0) p.dLC[(size_t)rec * D + c] = acc;
+      for (int e = 0; e < 4; ++e)
+        sU[(16 * Rt + 4 * g4 + e) * LD + 16 * Vt + r] = from_f32<E>(to_f32(up[e]) - acc[e]);
+    }
   }
   __syncthreads();
 
@@ -368,12 +376,12 @@ __global__ __launch_bounds__(256) void kda_bwd_prod_kernel(BwdProdParams p) {
   float* dW = p.dW + (size_t)rec * C * D;
   float* dKt = p.dKt + (size_t)rec * C * D;
   float* dP = p.dP + (size_t)rec * C * C;
-  for (int tile = wave; tile < RT * CT; tile += 4) {
-    const int Rt = tile / CT, Ct = tile % CT;
-    RowFrag<E, D> fdo, fdu, fu, fs, fds;
-    load_do(fdo, 16 * Rt + r);
-    fdu.load(gdU + (size_t)(16 * Rt + r) * D, g4);
-    fu.load(sU + (16 * Rt + r) * LD, g4);
+  RowFrag<E, D> fdo, fdu, fu;
+  load_do(fdo, 16 * Rt + r);
+  fdu.load(gdU + (size_t)(16 * Rt + r) * D, g4);
+  fu.load(sU + (16 * Rt + r) * LD, g4);
+  for (int Ct = sub; Ct < CT; Ct += WPR) {
+    RowFrag<E, D> fs, fds;
     fs.load(ckS + (size_t)(16 * Ct + r) * D, g4);
     fds.load(ckdS + (size_t)(16 * Ct + r) * D, g4);
     f32x4 aq = {0.f, 0.f, 0.f, 0.f}, aw = aq, ak = aq;
@@ -387,15 +395,22 @@ __global__ __launch_bounds__(256) void kda_bwd_prod_kernel(BwdProdParams p) {
       dW[o] = -aw[e];
       dKt[o] = ak[e];
     }
+    if (Rt == 0) {
+      // dLC of rows c = 16 Ct + r: this lane's pieces of the row are the same
+      // elements of fs and fds, the rest sit in the lanes of the other g4
+      const float sum = frag_dot(fs, fds);
+      float tot = sum + __shfl_xor(sum, 16, 64);
+      tot += __shfl_xor(tot, 32, 64);
+      if (g4 == 0) p.dLC[(size_t)rec * D + 16 * Ct + r] = tot;
+    }
   }
-  for (int tile = wave; tile < RT * RT; tile += 4) {
-    const int It = tile / RT, Jt = tile % RT;
+  for (int Jt = sub; Jt < RT; Jt += WPR) {
+    const int It = Rt;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if (Jt <= It) {
-      RowFrag<E, D> fa, fb;
-      load_do(fa, 16 * It + r);
+      RowFrag<E, D> fb;
       fb.load(sU + (16 * Jt + r) * LD, g4);
-      mma<D>(acc, fa, fb);
+      mma<D>(acc, fdo, fb);
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
