@@ -421,140 +421,199 @@ __global__ __launch_bounds__(256) void kda_bwd_prod_kernel(BwdProdParams p) {
 }
 
 // ------------------------------------------------------------ T-side products
-// One 256-thread workgroup per chunk record, float32 matrix-core products
-// (16x16x4, one element per lane and step, so operands read along either index):
+// Persistent: each 512-thread workgroup (two waves per SIMD, so one's LDS reads
+// and barriers overlap the other's products) takes records blockIdx.x,
+// blockIdx.x + gridDim.x, ...; the global loads of its next record go into
+// registers while the current one computes from LDS.  float32 matrix-core
+// products (16x16x4, one element per lane and step, so operands read along either
+// index):
 //   dT = dW Bk^T + dU Bv^T   (j <= i),   Y = dT T^T,   dA = -T^T Y   (j < i)
 //   dBk = T^T dW,   dBv = T^T dU
 // Bk = beta K Lambda and Bv = beta V are rebuilt from the front end's outputs.
 template <int D, int C, typename E>
-__global__ __launch_bounds__(256) void kda_bwd_t_kernel(BwdTParams p) {
+__global__ __launch_bounds__(512) void kda_bwd_t_kernel(BwdTParams p) {
+  constexpr int NT = 512, NW = NT / 64;
   constexpr int LD = D + 4;                  // float rows of D
   constexpr int LC = C + 4;                  // float rows of C
   constexpr int LB = D + 16 / (int)sizeof(E);  // E rows of D
   constexpr int CT = D / 16, RT = C / 16;
   constexpr int BKY = (C * LB * (int)sizeof(E) > C * LC * 4) ? C * LB * (int)sizeof(E) : C * LC * 4;
+  // per-thread shares of one record's inputs
+  constexpr int N4 = (C * D / 4 + NT - 1) / NT;  // dW in float4 pieces
+  constexpr int N8 = (C * D / 8 + NT - 1) / NT;  // dU, k, v, Gamma in 8-element pieces
+  constexpr int NC = (C * C / 4 + NT - 1) / NT;  // T^T in float4 pieces
   __shared__ __attribute__((aligned(16))) float sdW[C * LD];
-  __shared__ __attribute__((aligned(16))) float sdU[C * LD];
+  __shared__ __attribute__((aligned(16))) E sdU[C * LB];  // dU in its stored element type
   __shared__ __attribute__((aligned(16))) float sTt[C * LC];
   __shared__ __attribute__((aligned(16))) float sdT[C * LC];
   __shared__ __attribute__((aligned(16))) char sBkY[BKY];  // Bk [C][LB] E, later Y [C][LC] float
   __shared__ __attribute__((aligned(16))) E sBv[C * LB];
   E* sBk = reinterpret_cast<E*>(sBkY);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int r = lane & 15, g4 = lane >> 4;
-  const int rec = blockIdx.x;
-  const int n = rec % p.NT;
-  const int bh = rec / p.NT;
-  const int h = bh % p.H, b = bh / p.H;
   const size_t HD = (size_t)p.H * D;
   const size_t plane = (size_t)p.B * p.T * HD;
+  const int nrec = p.B * p.H * p.NT;
 
-  const float* gdW = p.dW + (size_t)rec * C * D;
-  const E* gdU = static_cast<const E*>(p.dU) + (size_t)rec * C * D;  // [t][v]
-  const float* gTt = p.tT + (size_t)rec * C * C;
-  for (int it = tid; it < C * D / 4; it += 256) {
-    const int t = it / (D / 4), c4 = 4 * (it % (D / 4));
-    *reinterpret_cast<f32x4*>(&sdW[t * LD + c4]) = *reinterpret_cast<const f32x4*>(gdW + (size_t)t * D + c4);
-  }
-  for (int it = tid; it < C * D / 8; it += 256) {
-    const int t = it / (D / 8), c8 = 8 * (it % (D / 8));
-    float x[8];
-    load8(gdU + (size_t)t * D + c8, x);
-    *reinterpret_cast<f32x4*>(&sdU[t * LD + c8]) = f32x4{x[0], x[1], x[2], x[3]};
-    *reinterpret_cast<f32x4*>(&sdU[t * LD + c8 + 4]) = f32x4{x[4], x[5], x[6], x[7]};
-  }
-  for (int it = tid; it < C * C / 4; it += 256) {
-    const int j = it / (C / 4), i4 = 4 * (it % (C / 4));
-    *reinterpret_cast<f32x4*>(&sTt[j * LC + i4]) = *reinterpret_cast<const f32x4*>(gTt + (size_t)j * C + i4);
-  }
-  // Bk = beta k exp(Gamma), Bv = beta v (zero past the end of the sequence)
-  for (int it = tid; it < C * D / 8; it += 256) {
-    const int t = it / (D / 8), c8 = 8 * (it % (D / 8));
-    const int tg = n * C + t;
-    float kk[8], vv[8], gg[8];
-    float bt = 0.f;
-    if (tg < p.T) {
-      const size_t row = ((size_t)b * p.T + tg) * HD + (size_t)h * D + c8;
-      load8(p.y + plane + row, kk);
-      load8(p.y + 2 * plane + row, vv);
-      load8(p.gam + row, gg);
-      bt = p.beta[((size_t)b * p.T + tg) * p.H + h];
-    } else {
+  struct Stage {
+    f32x4 dw[N4];
+    float du[N8][8], kk[N8][8], vv[N8][8], gg[N8][8];
+    float bt[N8];
+    f32x4 tt[NC];
+  };
+  auto load_stage = [&](int rec, int tid, Stage& S) {
+    const int n = rec % p.NT;
+    const int bh = rec / p.NT;
+    const int h = bh % p.H, b = bh / p.H;
+    const float* gdW = p.dW + (size_t)rec * C * D;
+    const E* gdU = static_cast<const E*>(p.dU) + (size_t)rec * C * D;  // [t][v]
+    const float* gTt = p.tT + (size_t)rec * C * C;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) kk[e] = vv[e] = gg[e] = 0.f;
+    for (int i = 0; i < N4; ++i) {
+      const int it = tid + NT * i;
+      if (it < C * D / 4) S.dw[i] = *reinterpret_cast<const f32x4*>(gdW + 4 * (size_t)it);
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      sBk[t * LB + c8 + e] = from_f32<E>(bt * kk[e] * __builtin_amdgcn_exp2f(gg[e]));
-      sBv[t * LB + c8 + e] = from_f32<E>(bt * vv[e]);
+    for (int i = 0; i < NC; ++i) {
+      const int it = tid + NT * i;
+      if (it < C * C / 4) S.tt[i] = *reinterpret_cast<const f32x4*>(gTt + 4 * (size_t)it);
     }
-  }
-  __syncthreads();
-
-  // ---- dT (i, j) for j <= i
-  for (int tile = wave; tile < RT * RT; tile += 4) {
-    const int It = tile / RT, Jt = tile % RT;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (Jt <= It) {
-      for (int k = 0; k < D; k += 4) {
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sdW[(16 * It + r) * LD + k + g4],
-                                                   to_f32(sBk[(16 * Jt + r) * LB + k + g4]), acc, 0, 0, 0);
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sdU[(16 * It + r) * LD + k + g4],
-                                                   to_f32(sBv[(16 * Jt + r) * LB + k + g4]), acc, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < N8; ++i) {
+      const int it = tid + NT * i;
+      if (it < C * D / 8) {
+        const int t = it / (D / 8), c8 = 8 * (it % (D / 8));
+        load8(gdU + (size_t)t * D + c8, S.du[i]);
+        const int tg = n * C + t;
+        S.bt[i] = 0.f;
+        if (tg < p.T) {
+          const size_t row = ((size_t)b * p.T + tg) * HD + (size_t)h * D + c8;
+          load8(p.y + plane + row, S.kk[i]);
+          load8(p.y + 2 * plane + row, S.vv[i]);
+          load8(p.gam + row, S.gg[i]);
+          S.bt[i] = p.beta[((size_t)b * p.T + tg) * p.H + h];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) S.kk[i][e] = S.vv[i][e] = S.gg[i][e] = 0.f;
+        }
+      }
+    }
+  };
+  // into LDS; Bk = beta k exp(Gamma), Bv = beta v (zero past the end of the sequence)
+  auto store_stage = [&](int tid, const Stage& S) {
+#pragma unroll
+    for (int i = 0; i < N4; ++i) {
+      const int it = tid + NT * i;
+      if (it < C * D / 4) {
+        const int t = it / (D / 4), c4 = 4 * (it % (D / 4));
+        *reinterpret_cast<f32x4*>(&sdW[t * LD + c4]) = S.dw[i];
       }
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = 16 * It + 4 * g4 + e, j = 16 * Jt + r;
-      sdT[i * LC + j] = j <= i ? acc[e] : 0.f;
+    for (int i = 0; i < NC; ++i) {
+      const int it = tid + NT * i;
+      if (it < C * C / 4) {
+        const int j = it / (C / 4), i4 = 4 * (it % (C / 4));
+        *reinterpret_cast<f32x4*>(&sTt[j * LC + i4]) = S.tt[i];
+      }
     }
-  }
-  __syncthreads();  // dT complete; Bk, Bv dead
-  float* sY = reinterpret_cast<float*>(sBkY);
-  // ---- Y = dT T^T:  Y[i][j] = sum_m dT[i][m] T^T[m][j]
-  for (int tile = wave; tile < RT * RT; tile += 4) {
-    const int It = tile / RT, Jt = tile % RT;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < C; k += 4)
-      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sdT[(16 * It + r) * LC + k + g4],
-                                                 sTt[(k + g4) * LC + 16 * Jt + r], acc, 0, 0, 0);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sY[(16 * It + 4 * g4 + e) * LC + 16 * Jt + r] = acc[e];
-  }
-  __syncthreads();
-  // ---- dA = -T^T Y  (j < i)
-  float* gdA = p.dA + (size_t)rec * C * C;
-  for (int tile = wave; tile < RT * RT; tile += 4) {
-    const int It = tile / RT, Jt = tile % RT;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (Jt <= It)
+    for (int i = 0; i < N8; ++i) {
+      const int it = tid + NT * i;
+      if (it < C * D / 8) {
+        const int t = it / (D / 8), c8 = 8 * (it % (D / 8));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          sdU[t * LB + c8 + e] = from_f32<E>(S.du[i][e]);
+          sBk[t * LB + c8 + e] = from_f32<E>(S.bt[i] * S.kk[i][e] * __builtin_amdgcn_exp2f(S.gg[i][e]));
+          sBv[t * LB + c8 + e] = from_f32<E>(S.bt[i] * S.vv[i][e]);
+        }
+      }
+    }
+  };
+
+  int rec = blockIdx.x;
+  Stage S;
+  if (rec < nrec) load_stage(rec, threadIdx.x, S);
+  while (rec < nrec) {
+    // the thread's indices, opaque per record so that their address arithmetic
+    // stays inside the loop
+    int tid = threadIdx.x;
+    asm volatile("" : "+v"(tid));
+    const int lane = tid & 63, wave = tid >> 6;
+    const int r = lane & 15, g4 = lane >> 4;
+    store_stage(tid, S);
+    __syncthreads();
+    const int next = rec + (int)gridDim.x;
+    if (next < nrec) load_stage(next, tid, S);
+
+    // ---- dT (i, j) for j <= i
+    for (int tile = wave; tile < RT * RT; tile += NW) {
+      const int It = tile / RT, Jt = tile % RT;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = acc;
+      if (Jt <= It) {
+        for (int k = 0; k < D; k += 4) {
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sdW[(16 * It + r) * LD + k + g4],
+                                                     to_f32(sBk[(16 * Jt + r) * LB + k + g4]), acc, 0, 0, 0);
+          acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(to_f32(sdU[(16 * It + r) * LB + k + g4]),
+                                                      to_f32(sBv[(16 * Jt + r) * LB + k + g4]), acc2, 0, 0, 0);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += acc2[e];
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * It + 4 * g4 + e, j = 16 * Jt + r;
+        sdT[i * LC + j] = j <= i ? acc[e] : 0.f;
+      }
+    }
+    __syncthreads();  // dT complete; Bk, Bv dead
+    float* sY = reinterpret_cast<float*>(sBkY);
+    // ---- Y = dT T^T:  Y[i][j] = sum_m dT[i][m] T^T[m][j]
+    for (int tile = wave; tile < RT * RT; tile += NW) {
+      const int It = tile / RT, Jt = tile % RT;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       for (int k = 0; k < C; k += 4)
-        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sTt[(16 * It + r) * LC + k + g4],
-                                                   sY[(k + g4) * LC + 16 * Jt + r], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sdT[(16 * It + r) * LC + k + g4],
+                                                   sTt[(k + g4) * LC + 16 * Jt + r], acc, 0, 0, 0);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = 16 * It + 4 * g4 + e, j = 16 * Jt + r;
-      gdA[(size_t)i * C + j] = j < i ? -acc[e] : 0.f;
+      for (int e = 0; e < 4; ++e) sY[(16 * It + 4 * g4 + e) * LC + 16 * Jt + r] = acc[e];
     }
-  }
-  // ---- dBk = T^T dW,  dBv = T^T dU  (tiles (j, c))
-  float* gdBk = p.dBk + (size_t)rec * C * D;
-  float* gdBv = p.dBv + (size_t)rec * C * D;
-  for (int tile = wave; tile < RT * CT; tile += 4) {
-    const int Jt = tile / CT, Ct = tile % CT;
-    f32x4 ak = {0.f, 0.f, 0.f, 0.f}, av = ak;
-    for (int k = 0; k < C; k += 4) {
-      const float a = sTt[(16 * Jt + r) * LC + k + g4];
-      ak = __builtin_amdgcn_mfma_f32_16x16x4f32(a, sdW[(k + g4) * LD + 16 * Ct + r], ak, 0, 0, 0);
-      av = __builtin_amdgcn_mfma_f32_16x16x4f32(a, sdU[(k + g4) * LD + 16 * Ct + r], av, 0, 0, 0);
-    }
+    __syncthreads();
+    // ---- dA = -T^T Y  (j < i)
+    float* gdA = p.dA + (size_t)rec * C * C;
+    for (int tile = wave; tile < RT * RT; tile += NW) {
+      const int It = tile / RT, Jt = tile % RT;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      if (Jt <= It)
+        for (int k = 0; k < C; k += 4)
+          acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sTt[(16 * It + r) * LC + k + g4],
+                                                     sY[(k + g4) * LC + 16 * Jt + r], acc, 0, 0, 0);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const size_t o = (size_t)(16 * Jt + 4 * g4 + e) * D + 16 * Ct + r;
-      gdBk[o] = ak[e];
-      gdBv[o] = av[e];
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * It + 4 * g4 + e, j = 16 * Jt + r;
+        gdA[(size_t)i * C + j] = j < i ? -acc[e] : 0.f;
+      }
     }
+    // ---- dBk = T^T dW,  dBv = T^T dU  (tiles (j, c))
+    float* gdBk = p.dBk + (size_t)rec * C * D;
+    float* gdBv = p.dBv + (size_t)rec * C * D;
+    for (int tile = wave; tile < RT * CT; tile += NW) {
+      const int Jt = tile / CT, Ct = tile % CT;
+      f32x4 ak = {0.f, 0.f, 0.f, 0.f}, av = ak;
+      for (int k = 0; k < C; k += 4) {
+        const float a = sTt[(16 * Jt + r) * LC + k + g4];
+        ak = __builtin_amdgcn_mfma_f32_16x16x4f32(a, sdW[(k + g4) * LD + 16 * Ct + r], ak, 0, 0, 0);
+        av = __builtin_amdgcn_mfma_f32_16x16x4f32(a, to_f32(sdU[(k + g4) * LB + 16 * Ct + r]), av, 0, 0, 0);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const size_t o = (size_t)(16 * Jt + 4 * g4 + e) * D + 16 * Ct + r;
+        gdBk[o] = ak[e];
+        gdBv[o] = av[e];
+      }
+    }
+    __syncthreads();  // LDS is reused by the next record
+    rec = next;
   }
 }
 
@@ -1221,7 +1280,17 @@ static hipError_t launch_bwd_t(const BwdLaunch& L, hipStream_t st) {
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   hipLaunchKernelGGL((kda_bwd_prod_kernel<D, C, IO, E>), dim3((unsigned)nrec), dim3(256), 0, st, L.prod);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-  hipLaunchKernelGGL((kda_bwd_t_kernel<D, C, E>), dim3((unsigned)nrec), dim3(256), 0, st, L.tside);
+  {
+    // persistent: as many workgroups as fit on the device at once
+    int dev = 0, cus = 0, per = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kda_bwd_t_kernel<D, C, E>, 512, 0) != hipSuccess)
+      return hipErrorInvalidValue;
+    const size_t fit = (size_t)(per > 0 ? per : 1) * (size_t)(cus > 0 ? cus : 1);
+    hipLaunchKernelGGL((kda_bwd_t_kernel<D, C, E>), dim3((unsigned)(nrec < fit ? nrec : fit)), dim3(512), 0,
+                       st, L.tside);
+  }
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   constexpr int NBLK = 1;  // the pair kernels sum dbeta over all channels themselves
   // factored products for every chunk; the exact kernel takes the ones they list
