@@ -1082,22 +1082,48 @@ __global__ __launch_bounds__(256, 2) void kda_bwd_front_kernel(BwdFrontParams p,
     const IO* src = x == 0 ? static_cast<const IO*>(p.q) : (x == 1 ? static_cast<const IO*>(p.k)
                                                                    : static_cast<const IO*>(p.v));
     float* dst = x == 0 ? p.dq : (x == 1 ? p.dk : p.dv);
-    // raw rows t_first - 3 .. t_first + 6 (the last 3 only for the last segment)
-    float raw[10][8];
+    // Every global load of this tensor is issued before the first use, as
+    // range-checked buffer loads (zeros outside the range, no branches between
+    // the loads): raw rows t_first - 3 .. t_first + 6 (row m = token
+    // t_first - 3 + m; tokens < 0 from the conv history) and the rows of dz for
+    // tokens t_first .. t_first + 6.  The workgroup's rows are
+    // [max(t0 - 3, 0), min(t0 + TOKB + 3, T)).
+    Raw8<IO> rw[10];
+    Raw8<float> dzr[7];
+    {
+      constexpr int ES = (int)sizeof(IO);
+      const int r0 = t0 - 3 > 0 ? t0 - 3 : 0;
+      const int r1 = t0 + TOKB + 3 < p.T ? t0 + TOKB + 3 : p.T;
+      const int row_b = (int)(HD * ES);
+      const BufRes rx = make_buf(src + ((size_t)b * p.T + r0) * HD + (size_t)h * D,
+                                 (unsigned)(((long)(r1 - 1 - r0) * HD + D) * ES));
+      const int voff = (tf - 3 - r0) * row_b + ch * ES;
 #pragma unroll
-    for (int m = 0; m < 10; ++m) {
-      const int t = tf - 3 + m;
+      for (int m = 0; m < 10; ++m) rw[m].load(rx, voff + m * row_b, 0);
+      const int rz1 = t0 + TOKB + 3 < p.T ? t0 + TOKB + 3 : p.T;
+      const BufRes rz = make_buf(p.dy + x * plane + ((size_t)b * p.T + t0) * HD + (size_t)h * D,
+                                 (unsigned)(((long)(rz1 - 1 - t0) * HD + D) * 4));
+      const int zoff = (tf - t0) * (int)(HD * 4) + ch * 4;
 #pragma unroll
-      for (int c = 0; c < 8; ++c) raw[m][c] = 0.f;
-      if (m >= 7 && !last) continue;
-      if (t >= 0 && t < p.T) {
-        load8(src + ((size_t)b * p.T + t) * HD + (size_t)h * D + ch, raw[m]);
-      } else if (t < 0 && t >= -3 && conv && p.conv_state_in != nullptr) {
-        load8(static_cast<const IO*>(p.conv_state_in) + (((size_t)b * 3 + x) * 3 + (3 + t)) * HD +
-                  (size_t)h * D + ch,
-              raw[m]);
+      for (int u = 0; u < 7; ++u) dzr[u].load(rz, zoff + u * (int)(HD * 4), 0);
+      if (conv && p.conv_state_in != nullptr && t0 == 0) {
+        // tokens -3 .. -1 sit in history rows 0 .. 2 (only the first segment reaches them)
+        const BufRes rs = make_buf(static_cast<const IO*>(p.conv_state_in) + ((size_t)b * 3 + x) * 3 * HD +
+                                       (size_t)h * D,
+                                   (unsigned)((2 * HD + D) * ES));
+#pragma unroll
+        for (int m = 0; m < 3; ++m) {
+          Raw8<IO> sv;
+          sv.load(rs, (tf + m) * row_b + ch * ES, 0);  // history row tf + m = token tf - 3 + m
+          rw[m].merge(sv);
+        }
       }
     }
+    float raw[10][8];
+#pragma unroll
+    for (int m = 0; m < 10; ++m)
+#pragma unroll
+      for (int c = 0; c < 8; ++c) raw[m][c] = rw[m][c];
     float w[4][8];
     if (conv) {
 #pragma unroll
@@ -1124,13 +1150,8 @@ __global__ __launch_bounds__(256, 2) void kda_bwd_front_kernel(BwdFrontParams p,
           pre[c] = 0.f;
           y[c] = raw[u + 3][c];
         }
-        dz[c] = 0.f;
-      }
-      if (t < p.T) {
-        load8(p.dy + x * plane + ((size_t)b * p.T + t) * HD + (size_t)h * D + ch, dz);
-        if (x == 0)
-#pragma unroll
-          for (int c = 0; c < 8; ++c) dz[c] *= p.scale;
+        dz[c] = dzr[u][c];  // zero past the end of the sequence
+        if (x == 0) dz[c] *= p.scale;
       }
       float dyv[8];
       if (x < 2 && p.l2) {
