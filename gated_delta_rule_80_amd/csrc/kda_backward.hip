@@ -483,18 +483,16 @@ __global__ __launch_bounds__(512) void kda_bwd_t_kernel(BwdTParams p) {
       if (it < C * D / 8) {
         const int t = it / (D / 8), c8 = 8 * (it % (D / 8));
         load8(gdU + (size_t)t * D + c8, S.du[i]);
+        // rows past the end of the sequence read the last row and take beta = 0
+        // (no branch around the loads, so they stay in flight)
         const int tg = n * C + t;
-        S.bt[i] = 0.f;
-        if (tg < p.T) {
-          const size_t row = ((size_t)b * p.T + tg) * HD + (size_t)h * D + c8;
-          load8(p.y + plane + row, S.kk[i]);
-          load8(p.y + 2 * plane + row, S.vv[i]);
-          load8(p.gam + row, S.gg[i]);
-          S.bt[i] = p.beta[((size_t)b * p.T + tg) * p.H + h];
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) S.kk[i][e] = S.vv[i][e] = S.gg[i][e] = 0.f;
-        }
+        const int tc = tg < p.T ? tg : p.T - 1;
+        const size_t row = ((size_t)b * p.T + tc) * HD + (size_t)h * D + c8;
+        load8(p.y + plane + row, S.kk[i]);
+        load8(p.y + 2 * plane + row, S.vv[i]);
+        load8(p.gam + row, S.gg[i]);
+        const float bv = p.beta[((size_t)b * p.T + tc) * p.H + h];
+        S.bt[i] = tg < p.T ? bv : 0.f;
       }
     }
   };
