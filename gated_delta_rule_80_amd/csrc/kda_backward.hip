@@ -615,6 +615,168 @@ __global__ __launch_bounds__(512) void kda_bwd_t_kernel(BwdTParams p) {
   }
 }
 
+// bf16 records: the same products as element-type matrix-core products
+// (16x16x32, operands k-contiguous from swizzled LDS images, float accumulation),
+// the float32 inputs rounded to bf16 as the forward rounds T and its operands.
+// One 512-thread workgroup per chunk record.  Images (rows, k):
+//   W [i][c] and W^T [c][i] of dW, U [i][c] and U^T [c][i] of dU, Bk [j][c],
+//   Bv [j][c], T [j][l], T^T [i][m], dT [m][l], Y^T [j][m]
+// and the products, in the NT form C[a][b] = sum_k A[a][k] B[b][k]:
+//   dT  = dW Bk^T + dU Bv^T   A = W, U rows i;     B = Bk, Bv rows j      (j <= i)
+//   Y^T = T dT^T              A = T rows j;        B = dT rows m
+//   dA  = -T^T Y              A = T^T rows i;      B = Y^T rows j         (j < i)
+//   dBk = T^T dW,  dBv = T^T dU   A = T^T rows j;  B = W^T, U^T rows c
+template <int D, int C>
+__global__ __launch_bounds__(512) void kda_bwd_t16_kernel(BwdTParams p) {
+  constexpr int NT = 512, NW = NT / 64;
+  constexpr int CT = D / 16, RT = C / 16;
+  using SD = Swz<__bf16, D>;
+  using SC = Swz<__bf16, C>;
+  __shared__ __attribute__((aligned(16))) __bf16 iW[C * D];
+  __shared__ __attribute__((aligned(16))) __bf16 iWt[D * C];
+  __shared__ __attribute__((aligned(16))) __bf16 iU[C * D];
+  __shared__ __attribute__((aligned(16))) __bf16 iUt[D * C];
+  __shared__ __attribute__((aligned(16))) __bf16 iBk[C * D];
+  __shared__ __attribute__((aligned(16))) __bf16 iBv[C * D];
+  __shared__ __attribute__((aligned(16))) __bf16 iT[C * C];
+  __shared__ __attribute__((aligned(16))) __bf16 iTt[C * C];
+  __shared__ __attribute__((aligned(16))) __bf16 idT[C * C];
+  __shared__ __attribute__((aligned(16))) __bf16 iYt[C * C];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, g4 = lane >> 4;
+  const int rec = blockIdx.x;
+  const int n = rec % p.NT;
+  const int bh = rec / p.NT;
+  const int h = bh % p.H, b = bh / p.H;
+  const size_t HD = (size_t)p.H * D;
+  const size_t plane = (size_t)p.B * p.T * HD;
+
+  // ---- images
+  const float* gdW = p.dW + (size_t)rec * C * D;
+  const __bf16* gdU = static_cast<const __bf16*>(p.dU) + (size_t)rec * C * D;  // [t][v]
+  const float* gTt = p.tT + (size_t)rec * C * C;                               // [j][i] = T[i][j]
+  for (int it = tid; it < C * D / 4; it += NT) {
+    const int t = it / (D / 4), c4 = 4 * (it % (D / 4));
+    const f32x4 w = *reinterpret_cast<const f32x4*>(gdW + (size_t)t * D + c4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const __bf16 x = (__bf16)w[e];
+      iW[SD::at(t, c4 + e)] = x;
+      iWt[SC::at(c4 + e, t)] = x;
+    }
+  }
+  for (int it = tid; it < C * D / 8; it += NT) {
+    const int t = it / (D / 8), c8 = 8 * (it % (D / 8));
+    const bf16x8 u = *reinterpret_cast<const bf16x8*>(gdU + (size_t)t * D + c8);
+    *reinterpret_cast<bf16x8*>(&iU[SD::at(t, c8)]) = u;  // 8 elements = one 16-byte chunk
+#pragma unroll
+    for (int e = 0; e < 8; ++e) iUt[SC::at(c8 + e, t)] = u[e];
+  }
+  for (int it = tid; it < C * C / 4; it += NT) {
+    const int a = it / (C / 4), b4 = 4 * (it % (C / 4));
+    const f32x4 x = *reinterpret_cast<const f32x4*>(gTt + (size_t)a * C + b4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const __bf16 y = (__bf16)x[e];
+      iTt[SC::at(a, b4 + e)] = y;  // T^T[a][b]
+      iT[SC::at(b4 + e, a)] = y;   // T[b][a]
+    }
+  }
+  // Bk = beta k exp(Gamma), Bv = beta v; rows past the end of the sequence read
+  // the last row and take beta = 0
+  for (int it = tid; it < C * D / 8; it += NT) {
+    const int t = it / (D / 8), c8 = 8 * (it % (D / 8));
+    const int tg = n * C + t;
+    const int tc = tg < p.T ? tg : p.T - 1;
+    const size_t row = ((size_t)b * p.T + tc) * HD + (size_t)h * D + c8;
+    float kk[8], vv[8], gg[8];
+    load8(p.y + plane + row, kk);
+    load8(p.y + 2 * plane + row, vv);
+    load8(p.gam + row, gg);
+    const float bv = p.beta[((size_t)b * p.T + tc) * p.H + h];
+    const float bt = tg < p.T ? bv : 0.f;
+    bf16x8 xk, xv;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      xk[e] = (__bf16)(bt * kk[e] * __builtin_amdgcn_exp2f(gg[e]));
+      xv[e] = (__bf16)(bt * vv[e]);
+    }
+    *reinterpret_cast<bf16x8*>(&iBk[SD::at(t, c8)]) = xk;
+    *reinterpret_cast<bf16x8*>(&iBv[SD::at(t, c8)]) = xv;
+  }
+  __syncthreads();
+
+  // ---- dT (i, j), zero above the diagonal
+  for (int tile = wave; tile < RT * RT; tile += NW) {
+    const int It = tile / RT, Jt = tile % RT;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (Jt <= It) {
+      RowFrag<__bf16, D> fa, fb;
+      load_swz<D>(fa, iW, 16 * It + r, g4);
+      load_swz<D>(fb, iBk, 16 * Jt + r, g4);
+      mma<D>(acc, fa, fb);
+      load_swz<D>(fa, iU, 16 * It + r, g4);
+      load_swz<D>(fb, iBv, 16 * Jt + r, g4);
+      mma<D>(acc, fa, fb);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 16 * It + 4 * g4 + e, j = 16 * Jt + r;
+      idT[SC::at(i, j)] = (__bf16)(j <= i ? acc[e] : 0.f);
+    }
+  }
+  __syncthreads();
+  // ---- Y^T (j, m) = sum_l T[j][l] dT[m][l]
+  for (int tile = wave; tile < RT * RT; tile += NW) {
+    const int Jt = tile / RT, Mt = tile % RT;
+    RowFrag<__bf16, C> fa, fb;
+    load_swz<C>(fa, iT, 16 * Jt + r, g4);
+    load_swz<C>(fb, idT, 16 * Mt + r, g4);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    mma<C>(acc, fa, fb);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) iYt[SC::at(16 * Jt + 4 * g4 + e, 16 * Mt + r)] = (__bf16)acc[e];
+  }
+  __syncthreads();
+  // ---- dA (i, j) = -sum_m T^T[i][m] Y^T[j][m]  (j < i)
+  float* gdA = p.dA + (size_t)rec * C * C;
+  for (int tile = wave; tile < RT * RT; tile += NW) {
+    const int It = tile / RT, Jt = tile % RT;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (Jt <= It) {
+      RowFrag<__bf16, C> fa, fb;
+      load_swz<C>(fa, iTt, 16 * It + r, g4);
+      load_swz<C>(fb, iYt, 16 * Jt + r, g4);
+      mma<C>(acc, fa, fb);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 16 * It + 4 * g4 + e, j = 16 * Jt + r;
+      gdA[(size_t)i * C + j] = j < i ? -acc[e] : 0.f;
+    }
+  }
+  // ---- dBk (j, c) = sum_i T^T[j][i] dW^T[c][i],  dBv likewise with dU
+  float* gdBk = p.dBk + (size_t)rec * C * D;
+  float* gdBv = p.dBv + (size_t)rec * C * D;
+  for (int tile = wave; tile < RT * CT; tile += NW) {
+    const int Jt = tile / CT, Ct = tile % CT;
+    RowFrag<__bf16, C> ft, fw, fu;
+    load_swz<C>(ft, iTt, 16 * Jt + r, g4);
+    load_swz<C>(fw, iWt, 16 * Ct + r, g4);
+    load_swz<C>(fu, iUt, 16 * Ct + r, g4);
+    f32x4 ak = {0.f, 0.f, 0.f, 0.f}, av = ak;
+    mma<C>(ak, ft, fw);
+    mma<C>(av, ft, fu);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const size_t o = (size_t)(16 * Jt + 4 * g4 + e) * D + 16 * Ct + r;
+      gdBk[o] = ak[e];
+      gdBv[o] = av[e];
+    }
+  }
+}
+
 // ------------------------------------------ pair and element terms, factored
 // The pair terms of A and P,
 //   rK_i = sum_{j<i} dA_ij k_j E_ij,   rQ_i = sum_{j<=i} dP_ij k_j E_ij,
@@ -1299,7 +1461,9 @@ static hipError_t launch_bwd_t(const BwdLaunch& L, hipStream_t st) {
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   hipLaunchKernelGGL((kda_bwd_prod_kernel<D, C, IO, E>), dim3((unsigned)nrec), dim3(256), 0, st, L.prod);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-  {
+  if constexpr (sizeof(E) == 2) {
+    hipLaunchKernelGGL((kda_bwd_t16_kernel<D, C>), dim3((unsigned)nrec), dim3(512), 0, st, L.tside);
+  } else {
     // persistent: as many workgroups as fit on the device at once
     int dev = 0, cus = 0, per = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
