@@ -113,8 +113,9 @@ def backward_bytes(w) -> dict:
     return {
         "walk": nrec * ((3 * cd + cc) * es + 4 * D) + xe + nrec * (cd + dd) * es + state,
         "prod": nrec * (2 * cd + 3 * dd + cd) * es + xe + nrec * (3 * cd * 4 + cc * 4 + D * 4),
-        "t": nrec * (cc * 4 + cd * 4 + cd * es) + 3 * x4 + bth4 + nrec * (2 * cd + cc) * 4,
-        "pair": 4 * x4 + bth4 + nrec * (2 * cc + 4 * cd + D) * 4 + 4 * x4 + bth4,
+        # the front end's outputs k, v (and q) in the I/O type, Gamma in float32
+        "t": nrec * (cc * 4 + cd * 4 + cd * es) + 2 * xe + x4 + bth4 + nrec * (2 * cd + cc) * 4,
+        "pair": 3 * xe + x4 + bth4 + nrec * (2 * cc + 4 * cd + D) * 4 + 4 * x4 + bth4,
         "front": 3 * xe + cw + cst_e + 3 * x4 + bth4 + 3 * x4 + w.B * nblk * 3 * w.H * D * 16
                  + cst_4 + bth4,
         "path": 4 * xe + tok * w.H * es + cw + cst_e + s0 + xe  # q, k, v, g, beta, filters, history, S0, dO

@@ -235,7 +235,7 @@ static kda::SeqTables seq_tables(const kda_prefill_args* a, void* ws) {
 
 // Extra outputs of the forward stages when they run for the backward pass.
 struct BwdFwdOut {
-  float* y;
+  void* y;
   float* gam;
   float* beta;
   float* tT;
@@ -500,11 +500,11 @@ BwdLayout bwd_layout(const kda_backward_args* a) {
     off = kda::round_up(off + floats * 4, 256);
     return o;
   };
+  const size_t ef = esize(f->io) == 2 ? 2 : 1;  // element-type buffers in float units (rounded up)
   L.tT = take(nrec * C * C);
-  L.y = take(3 * x);
+  L.y = take(3 * x / ef);  // front end outputs in the record element type
   L.gam = take(x);
   L.beta = take(bth);
-  const size_t ef = esize(f->io) == 2 ? 2 : 1;  // element-type buffers in float units (rounded up)
   L.ckS = take(nrec * 2 * D * D / ef);
   L.ckdS = take(nrec * D * D / ef);
   L.dU = take(nrec * C * D / ef);
@@ -619,7 +619,7 @@ kda_status kda_prefill_backward(const kda_backward_args* a, void* ws, size_t ws_
   char* wsb = static_cast<char*>(ws);
   auto F = [&](size_t off) { return reinterpret_cast<float*>(wsb + off); };
   // forward in backward mode
-  BwdFwdOut bo{F(L.y), F(L.gam), F(L.beta), F(L.tT), wsb + L.ckS};
+  BwdFwdOut bo{wsb + L.y, F(L.gam), F(L.beta), F(L.tT), wsb + L.ckS};
   for (int stage = KDA_STAGE_PREP; stage <= KDA_STAGE_OUTPUT; ++stage)
     if (kda_status e = run_stage(f, ws, stage, st, &bo); e != KDA_OK) return e;
   // backward
@@ -641,11 +641,11 @@ kda_status kda_prefill_backward(const kda_backward_args* a, void* ws, size_t ws_
   B.prod.dLC = F(L.dLC);
   B.prod.B = f->B; B.prod.T = f->T; B.prod.H = f->H; B.prod.NT = sz.NT;
   B.tside.tT = F(L.tT);
-  B.tside.y = F(L.y); B.tside.gam = F(L.gam); B.tside.beta = F(L.beta);
+  B.tside.y = wsb + L.y; B.tside.gam = F(L.gam); B.tside.beta = F(L.beta);
   B.tside.dW = F(L.dW); B.tside.dU = wsb + L.dU;
   B.tside.dBk = F(L.dBk); B.tside.dBv = F(L.dBv); B.tside.dA = F(L.dA);
   B.tside.B = f->B; B.tside.T = f->T; B.tside.H = f->H; B.tside.NT = sz.NT;
-  B.pair.y = F(L.y); B.pair.gam = F(L.gam); B.pair.beta = F(L.beta);
+  B.pair.y = wsb + L.y; B.pair.gam = F(L.gam); B.pair.beta = F(L.beta);
   B.pair.dA = F(L.dA); B.pair.dP = F(L.dP); B.pair.dQL = F(L.dQL); B.pair.dKt = F(L.dKt);
   B.pair.dLC = F(L.dLC); B.pair.dBk = F(L.dBk); B.pair.dBv = F(L.dBv);
   B.pair.dy = F(L.dy); B.pair.dg = a->dg; B.pair.dbeta_part = F(L.dbp);

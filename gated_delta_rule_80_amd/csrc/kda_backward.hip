@@ -488,8 +488,8 @@ __global__ __launch_bounds__(512) void kda_bwd_t_kernel(BwdTParams p) {
         const int tg = n * C + t;
         const int tc = tg < p.T ? tg : p.T - 1;
         const size_t row = ((size_t)b * p.T + tc) * HD + (size_t)h * D + c8;
-        load8(p.y + plane + row, S.kk[i]);
-        load8(p.y + 2 * plane + row, S.vv[i]);
+        load8(static_cast<const E*>(p.y) + plane + row, S.kk[i]);
+        load8(static_cast<const E*>(p.y) + 2 * plane + row, S.vv[i]);
         load8(p.gam + row, S.gg[i]);
         const float bv = p.beta[((size_t)b * p.T + tc) * p.H + h];
         S.bt[i] = tg < p.T ? bv : 0.f;
@@ -691,8 +691,8 @@ __global__ __launch_bounds__(512) void kda_bwd_t16_kernel(BwdTParams p) {
     const int tc = tg < p.T ? tg : p.T - 1;
     const size_t row = ((size_t)b * p.T + tc) * HD + (size_t)h * D + c8;
     float kk[8], vv[8], gg[8];
-    load8(p.y + plane + row, kk);
-    load8(p.y + 2 * plane + row, vv);
+    load8(static_cast<const __bf16*>(p.y) + plane + row, kk);
+    load8(static_cast<const __bf16*>(p.y) + 2 * plane + row, vv);
     load8(p.gam + row, gg);
     const float bv = p.beta[((size_t)b * p.T + tc) * p.H + h];
     const float bt = tg < p.T ? bv : 0.f;
@@ -800,7 +800,7 @@ __global__ __launch_bounds__(512) void kda_bwd_t16_kernel(BwdTParams p) {
 // its element terms as in the exact kernel.
 constexpr float kBwdSpan2 = 128.f;
 
-template <int D, int C>
+template <int D, int C, typename E>
 __global__ __launch_bounds__(4 * D, D / 32 > 1 ? D / 32 : 1) void kda_bwd_pair_mma_kernel(BwdPairParams p) {
   constexpr int NTH = 4 * D;
   constexpr int NB = C / 16;
@@ -829,6 +829,7 @@ __global__ __launch_bounds__(4 * D, D / 32 > 1 ? D / 32 : 1) void kda_bwd_pair_m
   auto row_of = [&](int t) { return ((size_t)b * p.T + (size_t)n * C + t) * HD + (size_t)h * D; };
   // Gamma of row t (past the end of the sequence g = 0: Gamma keeps its last value)
   auto gam_at = [&](int t) { return p.gam[row_of(t < nval ? t : nval - 1) + c]; };
+  const E* y = static_cast<const E*>(p.y);
 
   // ---- B-layout operands of this lane: rows 4 s + g4
   float gB[NS], kB[NS], qB[NS];
@@ -837,8 +838,8 @@ __global__ __launch_bounds__(4 * D, D / 32 > 1 ? D / 32 : 1) void kda_bwd_pair_m
     const int t = 4 * s + g4;
     const bool in = t < nval;
     gB[s] = gam_at(t);
-    kB[s] = in ? p.y[plane + row_of(t) + c] : 0.f;
-    qB[s] = in ? p.y[row_of(t) + c] : 0.f;
+    kB[s] = in ? to_f32(y[plane + row_of(t) + c]) : 0.f;
+    qB[s] = in ? to_f32(y[row_of(t) + c]) : 0.f;
   }
   if (tid < C) sB[tid] = tid < nval ? p.beta[((size_t)b * p.T + (size_t)n * C + tid) * p.H + h] : 0.f;
   // block boundaries G_1 .. G_NB (Gamma at the last row of each block: lane
@@ -951,9 +952,9 @@ __global__ __launch_bounds__(4 * D, D / 32 > 1 ? D / 32 : 1) void kda_bwd_pair_m
       float kk = 0.f, qq = 0.f, vv = 0.f;
       if (in) {
         const size_t o = row_of(t) + c;
-        qq = p.y[o];
-        kk = p.y[plane + o];
-        vv = p.y[2 * plane + o];
+        qq = to_f32(y[o]);
+        kk = to_f32(y[plane + o]);
+        vv = to_f32(y[2 * plane + o]);
       }
       const float bt = sB[t];
       const float a = __builtin_amdgcn_exp2f(gt - mid[pb]), bb = __builtin_amdgcn_exp2f(mid[pb] - gt);
@@ -1018,7 +1019,7 @@ struct PairShape {
   static constexpr int NTH = D * TPC;
 };
 
-template <int D, int C>
+template <int D, int C, typename E>
 __global__ __launch_bounds__(D * (C / 16)) void kda_bwd_pair_kernel(BwdPairParams p) {
   constexpr int TPC = PairShape<D, C>::TPC;
   constexpr int NTH = PairShape<D, C>::NTH;
@@ -1059,8 +1060,12 @@ __global__ __launch_bounds__(D * (C / 16)) void kda_bwd_pair_kernel(BwdPairParam
     f32x4 kk = {0.f, 0.f, 0.f, 0.f}, qq = kk, gg = kk;
     if (t < nval) {
       const size_t o = row_of(t) + c4;
-      qq = *reinterpret_cast<const f32x4*>(p.y + o);
-      kk = *reinterpret_cast<const f32x4*>(p.y + plane + o);
+      const E* y = static_cast<const E*>(p.y);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        qq[e] = to_f32(y[o + e]);
+        kk[e] = to_f32(y[plane + o + e]);
+      }
       gg = *reinterpret_cast<const f32x4*>(p.gam + o);
     } else if (nval > 0) {
       // past the end g = 0: Gamma keeps its last value
@@ -1155,7 +1160,7 @@ __global__ __launch_bounds__(D * (C / 16)) void kda_bwd_pair_kernel(BwdPairParam
       float vv = 0.f;
       if (t < nval) {
         const size_t o = row_of(t) + c;
-        vv = p.y[2 * plane + o];
+        vv = to_f32(static_cast<const E*>(p.y)[2 * plane + o]);
         p.dy[o] = lam * dql + rQ[m][r];
         p.dy[plane + o] = bt * lam * dbk + ec * dkt + bt * rK[m][r] + ckt;
         p.dy[2 * plane + o] = bt * dbv;
@@ -1479,10 +1484,10 @@ static hipError_t launch_bwd_t(const BwdLaunch& L, hipStream_t st) {
   // factored products for every chunk; the exact kernel takes the ones they list
   hipLaunchKernelGGL(kda_bwd_clear_kernel, dim3(1), dim3(64), 0, st, L.pair.ex_count);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-  hipLaunchKernelGGL((kda_bwd_pair_mma_kernel<D, C>), dim3((unsigned)nrec), dim3(4 * D), 0, st, L.pair);
+  hipLaunchKernelGGL((kda_bwd_pair_mma_kernel<D, C, E>), dim3((unsigned)nrec), dim3(4 * D), 0, st, L.pair);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   constexpr int PNTH = PairShape<D, C>::NTH;
-  hipLaunchKernelGGL((kda_bwd_pair_kernel<D, C>), dim3((unsigned)nrec), dim3(PNTH), 0, st, L.pair);
+  hipLaunchKernelGGL((kda_bwd_pair_kernel<D, C, E>), dim3((unsigned)nrec), dim3(PNTH), 0, st, L.pair);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   constexpr int TOKB = 4 * (256 / (D / 8));
   const size_t nblk = ((size_t)L.front.T + TOKB - 1) / TOKB;

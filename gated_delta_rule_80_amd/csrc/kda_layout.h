@@ -100,7 +100,7 @@ struct PrepParams {
   // y = (scale * q_hat, k_hat, v_hat) [3][B*T*H*D], gam = the chunk-local
   // cumulative log2-decay [B*T*H*D], beta [B*T*H] -- and T^T = ((I + A)^-1)^T
   // per record [C][C]
-  float* y_out;
+  void* y_out;
   float* gam_out;
   float* beta_out;
   float* t_out;
@@ -164,7 +164,7 @@ struct BwdProdParams {
 
 struct BwdTParams {
   const float* tT;     // T^T per record
-  const float* y;      // front end outputs [3][B*T*H*D]
+  const void* y;       // front end outputs [3][B*T*H*D], record element type
   const float* gam;
   const float* beta;
   const float* dW;
@@ -176,7 +176,7 @@ struct BwdTParams {
 };
 
 struct BwdPairParams {
-  const float* y;
+  const void* y;       // front end outputs [3][B*T*H*D], record element type
   const float* gam;
   const float* beta;
   const float* dA;

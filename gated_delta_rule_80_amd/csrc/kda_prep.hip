@@ -325,7 +325,8 @@ __global__ __launch_bounds__(fast_threads<E>()) void kda_chunk_prep_kernel(PrepP
   }
   __syncthreads();
   if (p.y_out != nullptr && active) {
-    // backward mode: the front end's outputs and the cumulative decay, in float32
+    // backward mode: the front end's outputs (record element type) and the
+    // cumulative decay (float32)
     float pre[8];
     load8(&sm.tot[s * D + ch], pre);
     const long HD = (long)p.H * D;
@@ -335,9 +336,9 @@ __global__ __launch_bounds__(fast_threads<E>()) void kda_chunk_prep_kernel(PrepP
       const int t = tf + m;
       if (t < Tq) {
         const long row = (tok0 + t) * HD + (long)h * D + ch;
-        store8(p.y_out + row, yq[m]);
-        store8(p.y_out + plane + row, yk[m]);
-        store8(p.y_out + 2 * plane + row, yv[m]);
+        store8(static_cast<E*>(p.y_out) + row, yq[m]);
+        store8(static_cast<E*>(p.y_out) + plane + row, yk[m]);
+        store8(static_cast<E*>(p.y_out) + 2 * plane + row, yv[m]);
         float gam[8];
 #pragma unroll
         for (int c = 0; c < 8; ++c) gam[c] = gc[m][c] + pre[c];
