@@ -903,6 +903,22 @@ __global__ __launch_bounds__(4 * D, D / 32 > 1 ? D / 32 : 1) void kda_bwd_pair_m
   const float* gdBk = p.dBk + (size_t)rec * C * D;
   const float* gdBv = p.dBv + (size_t)rec * C * D;
   float colsum = 0.f;  // sum over this lane's rows of dKt Ktil
+  // the element terms' inputs of row t: dQL, dKt, dBk, dBv, Gamma, q', k, v (rows
+  // past the end of the sequence read the last row; q', k, v are zeroed there)
+  auto load_row = [&](int t, float (&v)[8]) {
+    const size_t lo = (size_t)t * D + c;
+    v[0] = gdQL[lo];
+    v[1] = gdKt[lo];
+    v[2] = gdBk[lo];
+    v[3] = gdBv[lo];
+    const size_t o = row_of(t < nval ? t : nval - 1) + c;
+    v[4] = p.gam[o];
+    v[5] = to_f32(y[o]);
+    v[6] = to_f32(y[plane + o]);
+    v[7] = to_f32(y[2 * plane + o]);
+  };
+  float rowv[2][8];
+  load_row(4 * g4, rowv[0]);
 #pragma unroll
   for (int pb = 0; pb < NB; ++pb) {
     f32x4 tK = {0.f, 0.f, 0.f, 0.f}, tQ = tK, tC = tK;
@@ -941,21 +957,18 @@ __global__ __launch_bounds__(4 * D, D / 32 > 1 ? D / 32 : 1) void kda_bwd_pair_m
 #pragma unroll
       for (int e = 0; e < 4; ++e) tC[e] = fmaf(F, xc[e], tC[e]);
     }
-    // element terms for rows t = 16 pb + 4 g4 + e of channel c
+    // element terms for rows t = 16 pb + 4 g4 + e of channel c; each row's inputs
+    // were loaded one row ahead (the next row's loads go out before this row's
+    // arithmetic)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int t = 16 * pb + 4 * g4 + e;
       const bool in = t < nval;
-      const size_t lo = (size_t)t * D + c;
-      const float dql = gdQL[lo], dkt = gdKt[lo], dbk = gdBk[lo], dbv = gdBv[lo];
-      const float gt = gam_at(t);
-      float kk = 0.f, qq = 0.f, vv = 0.f;
-      if (in) {
-        const size_t o = row_of(t) + c;
-        qq = to_f32(y[o]);
-        kk = to_f32(y[plane + o]);
-        vv = to_f32(y[2 * plane + o]);
-      }
+      const int cur = (4 * pb + e) & 1;
+      if (4 * pb + e + 1 < 4 * NB) load_row(16 * ((4 * pb + e + 1) / 4) + 4 * g4 + (4 * pb + e + 1) % 4, rowv[cur ^ 1]);
+      const float dql = rowv[cur][0], dkt = rowv[cur][1], dbk = rowv[cur][2], dbv = rowv[cur][3];
+      const float gt = rowv[cur][4];
+      const float qq = in ? rowv[cur][5] : 0.f, kk = in ? rowv[cur][6] : 0.f, vv = in ? rowv[cur][7] : 0.f;
       const float bt = sB[t];
       const float a = __builtin_amdgcn_exp2f(gt - mid[pb]), bb = __builtin_amdgcn_exp2f(mid[pb] - gt);
       const float rK = a * tK[e], rQ = a * tQ[e], ckt = bb * tC[e];
