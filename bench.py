@@ -112,7 +112,7 @@ def backward_bytes(w) -> dict:
     nblk = -(-w.T // tokb)
     return {
         "walk": nrec * ((3 * cd + cc) * es + 4 * D) + xe + nrec * (cd + dd) * es + state,
-        "prod": nrec * (2 * cd + 3 * dd + cd) * es + xe + nrec * (3 * cd * 4 + cc * 4 + D * 4),
+        "prod": nrec * (2 * cd + 2 * dd) * es + xe + nrec * (3 * cd * 4 + cc * 4 + D * 4),
         # the front end's outputs k, v (and q) in the I/O type, Gamma in float32
         "t": nrec * (cc * 4 + cd * 4 + cd * es) + 2 * xe + x4 + bth4 + nrec * (2 * cd + cc) * 4,
         "pair": 3 * xe + x4 + bth4 + nrec * (2 * cc + 4 * cd + D) * 4 + 4 * x4 + bth4,

@@ -505,7 +505,7 @@ BwdLayout bwd_layout(const kda_backward_args* a) {
   L.y = take(3 * x / ef);  // front end outputs in the record element type
   L.gam = take(x);
   L.beta = take(bth);
-  L.ckS = take(nrec * 2 * D * D / ef);
+  L.ckS = take(nrec * (D * D + C * D) / ef);  // S_n [D][D] and U [C][D] per record
   L.ckdS = take(nrec * D * D / ef);
   L.dU = take(nrec * C * D / ef);
   L.dQL = take(nrec * C * D);

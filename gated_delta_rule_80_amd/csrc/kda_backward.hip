@@ -305,8 +305,7 @@ __device__ __forceinline__ float frag_dot(const RowFrag<float, K>& a, const RowF
 // One 256-thread workgroup per chunk record.  In the NT products
 // C[i][j] = sum_k A[i][k] B[j][k] (operands k-contiguous, element type, float
 // accumulation), fragments loaded straight from the checkpoints, dO, dU and the
-// record (only U, formed here, goes through LDS):
-//   U    = U~ - W S:   A = W rows t (record),   B = S^T rows v (checkpoint)
+// record; U, as the forward walk rounded it, is checkpointed and staged in LDS:
 //   dQL  = dO S^T:     A = dO rows t,           B = S rows c
 //   dW   = -dU S^T:    A = dU rows t,           B = S rows c
 //   dKt  = U dS'^T:    A = U rows t,            B = dS' rows c
@@ -317,7 +316,6 @@ __global__ __launch_bounds__(256) void kda_bwd_prod_kernel(BwdProdParams p) {
   constexpr int PE = 16 / (int)sizeof(E);
   constexpr int LD = D + PE;
   constexpr int CT = D / 16, RT = C / 16;
-  constexpr RecordLayout RL = record_layout(C, D, sizeof(E));
   __shared__ __attribute__((aligned(16))) E sU[C * LD];  // U rows t, k = v
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -327,13 +325,10 @@ __global__ __launch_bounds__(256) void kda_bwd_prod_kernel(BwdProdParams p) {
   const int bh = rec / p.NT;
   const int h = bh % p.H, b = bh / p.H;
   const size_t HD = (size_t)p.H * D;
-  const E* ckSt = static_cast<const E*>(p.ckS) + (size_t)rec * 2 * D * D;  // [v][c]
-  const E* ckS = ckSt + (size_t)D * D;                                      // [c][v]
+  const E* ckS = static_cast<const E*>(p.ckS) + (size_t)rec * ((size_t)D * D + (size_t)C * D);  // [c][v]
+  const E* ckU = ckS + (size_t)D * D;                                                         // [t][v]
   const E* ckdS = static_cast<const E*>(p.ckdS) + (size_t)rec * D * D;     // [c][v]
   const E* gdU = static_cast<const E*>(p.dU) + (size_t)rec * C * D;         // [t][v]
-  const char* recp = p.ws + (size_t)rec * RL.bytes;
-  const E* gW = reinterpret_cast<const E*>(recp) + RL.w;
-  const E* gU = reinterpret_cast<const E*>(recp) + RL.u;
   const IO* gdO = static_cast<const IO*>(p.dO) + ((size_t)b * p.T + (size_t)n * C) * HD + (size_t)h * D;
   const int nval = p.T - n * C < C ? p.T - n * C : C;
 
@@ -348,26 +343,15 @@ __global__ __launch_bounds__(256) void kda_bwd_prod_kernel(BwdProdParams p) {
     }
   };
 
-  // Wave w owns t-tile Rt = w % RT (its row strips of W, dO, dU and U are
+  // Wave w owns t-tile Rt = w % RT (its row strips of dO, dU and U are
   // loaded once) and every WPR-th column tile from w / RT, so the four waves
   // read each checkpoint strip at about the same time (once from memory).
   constexpr int WPR = 4 / RT;  // waves per t-tile
   const int Rt = wave % RT, sub = wave / RT;
-  // ---- U = U~ - W S  (tiles (t, v))
-  {
-    RowFrag<E, D> fa;
-    fa.load(gW + (size_t)(16 * Rt + r) * D, g4);
-    for (int Vt = sub; Vt < CT; Vt += WPR) {
-      RowFrag<E, D> fb;
-      fb.load(ckSt + (size_t)(16 * Vt + r) * D, g4);
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-      mma<D>(acc, fa, fb);
-      // U~ in fragment order: tile (t-tile, v-tile) of 64 lanes x 4 values
-      const E* up = gU + ((size_t)(Rt * CT + Vt) * 64 + lane) * 4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        sU[(16 * Rt + 4 * g4 + e) * LD + 16 * Vt + r] = from_f32<E>(to_f32(up[e]) - acc[e]);
-    }
+  // ---- U (as the forward walk rounded it) into LDS, 16-byte pieces
+  for (int it = tid; it < C * D / PE; it += 256) {
+    const int t = it / (D / PE), c0 = PE * (it % (D / PE));
+    *reinterpret_cast<u32x4*>(&sU[t * LD + c0]) = *reinterpret_cast<const u32x4*>(ckU + (size_t)t * D + c0);
   }
   __syncthreads();
 

@@ -133,7 +133,8 @@ struct OutStageParams {
 
 // ------------------------------------------------------------------ backward
 // Workspace buffers of the backward pass, per record rec = (b * H + h) * NT + n:
-//   ckS  [rec][2][D][D]  S_n^T then S_n (the state at the chunk start), element type
+//   ckS  [rec]: S_n [D][D] (the state at the chunk start, rows = key channel) then
+//        U [C][D] (the chunk's corrected values U~ - W S_n), element type
 //   ckdS [rec][D][D]     dS_{n+1} (gradient of the chunk's end state), element type
 //   dU   [rec][C][D]     dU_n, element type
 //   dQL, dW, dKt [rec][C][D], dP [rec][C][C], dLC [rec][D]: gradients of the

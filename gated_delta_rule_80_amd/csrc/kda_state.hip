@@ -334,18 +334,17 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void kda_chunk_state_kernel(
     if (n + 1 < nch) issue_copy(n + 1);
     load_gate(n);  // buffer n % 2: chunk n - 2's, stored during step n - 1
     if (n > 0) store_out(n - 1);
+    // backward mode: the record's checkpoint, S_n [c][v] then U [t][v]
+    E* ck = CK ? static_cast<E*>(p.ckpt) + (rec0 + n) * ((size_t)D * D + (size_t)C * D) : nullptr;
     if constexpr (CK) {
-      // backward mode: S_n^T (four consecutive key channels per lane) and S_n
-      E* ck = static_cast<E*>(p.ckpt) + (rec0 + n) * 2 * D * D;
 #pragma unroll
       for (int i = 0; i < NS; ++i) {
         const int u = wave + NW * i;
         if (FULL_S || u < CT * VT) {
           const int Ct = u % CT, Vt = u / CT;
           const int v = vb0 + 16 * Vt + r, c0 = 16 * Ct + 4 * g4;
-          store4(ck + (size_t)v * D + c0, accS[i][0], accS[i][1], accS[i][2], accS[i][3]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) ck[(size_t)D * D + (size_t)(c0 + e) * D + v] = from_f32<E>(accS[i][e]);
+          for (int e = 0; e < 4; ++e) ck[(size_t)(c0 + e) * D + v] = from_f32<E>(accS[i][e]);
         }
       }
     }
@@ -366,6 +365,13 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void kda_chunk_state_kernel(
         mma<D>(accO[i], sf, fql);  // (v, t) tile of S^T QL^T
         store4(&sU[(16 * Vt + r) * LU + 16 * R + 4 * g4], fu[i][0] - ws[0], fu[i][1] - ws[1],
                fu[i][2] - ws[2], fu[i][3] - ws[3]);
+        if constexpr (CK) {
+          // the same rounded U for the backward: rows t = 16 R + 4 g4 + e
+          E* cu = ck + (size_t)D * D;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            cu[(size_t)(16 * R + 4 * g4 + e) * D + vb0 + 16 * Vt + r] = from_f32<E>(fu[i][e] - ws[e]);
+        }
       }
     }
     lds_barrier();  // sU complete; every read of sS for this chunk is done
