@@ -211,13 +211,16 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void kda_chunk_state_kernel(
   const E* iU = reinterpret_cast<const E*>(img + IMG::U);
   const float* iLC = reinterpret_cast<const float*>(img + IMG::LC);
 
-  // The output of chunk n is stored during step n + 1, right after the copy of
-  // chunk n + 2 is issued, so the stores retire while step n + 1 computes instead
-  // of delaying the wait for the next copy.
+  // The output of chunk n is stored during step n + 1, after its U and S^T QL^T
+  // products: by then the wave has issued the copy of chunk n + 2, so the stores
+  // neither queue behind that copy nor delay the products, and they retire while
+  // the rest of step n + 1 computes.
   f32x4 pendO[NU];
   // Output stage (GN): lane (r, g4) of a unit holds token 16 R + r and value rows
-  // 16 Vt + 4 g4 + e.  Each wave leaves its per-token sums of squares in ored;
-  // the waves of one t-tile are those with wave % RT == R.  The gate rows of
+  // 16 Vt + 4 g4 + e.  Each wave leaves its per-token sums of squares of chunk n
+  // in buffer n % 2 of ored (a wave of step n + 1 may write its sums before a
+  // slower wave has read chunk n's); the waves of one t-tile are those with
+  // wave % RT == R.  The gate rows of
   // chunk n are copied into buffer n % 2 of sgate at the start of step n, with
   // the record copy of chunk n + 1 (the same wait covers both), and read at the
   // store of chunk n in step n + 1.  A buffer holds [C][D] in 16-byte pieces,
@@ -225,7 +228,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void kda_chunk_state_kernel(
   // column).
   constexpr int GRP = D * (int)sizeof(IO) / 16;  // 16-byte pieces per gate row
   constexpr int GCH = C * GRP;                   // pieces per chunk
-  __shared__ float ored[GN ? NW * 16 : 1];
+  __shared__ float ored[GN ? 2 * NW * 16 : 1];
   __shared__ __attribute__((aligned(16))) float onw[GN ? D : 1];  // norm gain (1 without norm)
   __shared__ __attribute__((aligned(16))) char sgate[GN ? 2 * GCH * 16 : 16];
   const bool has_norm = GN && p.o_norm_w != nullptr;
@@ -257,7 +260,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void kda_chunk_state_kernel(
     gv.load(reinterpret_cast<const IO*>(sgate + ((nn & 1) * GCH + tt * GRP + (piece ^ (tt % GRP))) * 16 + off));
     return gv;
   };
-  auto row_sums = [&]() {
+  auto row_sums = [&](int nn) {
     if constexpr (GN) {
       float ss = 0.f;
 #pragma unroll
@@ -267,7 +270,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void kda_chunk_state_kernel(
           for (int e = 0; e < 4; ++e) ss = fmaf(pendO[i][e], pendO[i][e], ss);
       ss += __shfl_xor(ss, 16, 64);
       ss += __shfl_xor(ss, 32, 64);
-      if (g4 == 0) ored[wave * 16 + r] = ss;
+      if (g4 == 0) ored[((nn & 1) * NW + wave) * 16 + r] = ss;
     }
   };
   auto store_out = [&](int nn) {
@@ -276,7 +279,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void kda_chunk_state_kernel(
       if (has_norm) {
         float tot = 0.f;
 #pragma unroll
-        for (int w = R; w < NW; w += RT) tot += ored[w * 16 + r];
+        for (int w = R; w < NW; w += RT) tot += ored[((nn & 1) * NW + w) * 16 + r];
         rs = 1.0f / sqrtf(tot * (1.0f / D) + p.o_norm_eps);
       }
     }
@@ -333,7 +336,6 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void kda_chunk_state_kernel(
     lds_barrier();  // every wave holds its fragments: the image may be overwritten
     if (n + 1 < nch) issue_copy(n + 1);
     load_gate(n);  // buffer n % 2: chunk n - 2's, stored during step n - 1
-    if (n > 0) store_out(n - 1);
     // backward mode: the record's checkpoint, S_n [c][v] then U [t][v]
     E* ck = CK ? static_cast<E*>(p.ckpt) + (rec0 + n) * ((size_t)D * D + (size_t)C * D) : nullptr;
     if constexpr (CK) {
@@ -375,6 +377,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void kda_chunk_state_kernel(
       }
     }
     lds_barrier();  // sU complete; every read of sS for this chunk is done
+    if (n > 0) store_out(n - 1);
     // ---- O^T += U^T P^T (j <= i), store O
 #pragma unroll
     for (int i = 0; i < NU; ++i) {
@@ -387,7 +390,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void kda_chunk_state_kernel(
         pendO[i] = accO[i];
       }
     }
-    row_sums();
+    row_sums(n);
     // ---- S = Diag(Lambda_C) S + Ktil^T U
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
