@@ -516,7 +516,7 @@ BwdLayout bwd_layout(const kda_backward_args* a) {
   L.dBk = take(nrec * C * D);
   L.dBv = take(nrec * C * D);
   L.dA = take(nrec * C * C);
-  L.dy = take(3 * x);
+  L.dy = take(3 * x / ef);  // record element type
   L.dbp = take(bth);
   L.nfront = kda::bwd_front_blocks(f->T, f->D);
   L.dcp = take(f->conv_k > 0 ? (size_t)f->B * L.nfront * 3 * f->H * D * 4 : 0);
@@ -648,14 +648,14 @@ kda_status kda_prefill_backward(const kda_backward_args* a, void* ws, size_t ws_
   B.pair.y = wsb + L.y; B.pair.gam = F(L.gam); B.pair.beta = F(L.beta);
   B.pair.dA = F(L.dA); B.pair.dP = F(L.dP); B.pair.dQL = F(L.dQL); B.pair.dKt = F(L.dKt);
   B.pair.dLC = F(L.dLC); B.pair.dBk = F(L.dBk); B.pair.dBv = F(L.dBv);
-  B.pair.dy = F(L.dy); B.pair.dg = a->dg; B.pair.dbeta_part = F(L.dbp);
+  B.pair.dy = wsb + L.dy; B.pair.dg = a->dg; B.pair.dbeta_part = F(L.dbp);
   B.pair.ex_count = reinterpret_cast<unsigned*>(wsb + L.pl);
   B.pair.ex_list = B.pair.ex_count + 64;
   B.pair.B = f->B; B.pair.T = f->T; B.pair.H = f->H; B.pair.NT = sz.NT;
   B.front.q = f->q; B.front.k = f->k; B.front.v = f->v;
   B.front.conv_w = f->conv_k > 0 ? f->conv_w : nullptr;
   B.front.conv_state_in = f->conv_k > 0 ? f->conv_state_in : nullptr;
-  B.front.dy = F(L.dy);
+  B.front.dy = wsb + L.dy;
   B.front.dq = a->dq; B.front.dk = a->dk; B.front.dv = a->dv;
   B.front.dconv_part = f->conv_k > 0 ? F(L.dcp) : nullptr;
   B.front.dconv_state = a->dconv_state;

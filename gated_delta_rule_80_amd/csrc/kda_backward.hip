@@ -963,9 +963,10 @@ __global__ __launch_bounds__(4 * D, D / 32 > 1 ? D / 32 : 1) void kda_bwd_pair_m
       sdG[t * LD + c] = dbk * bt * kk * lam + dql * qq * lam - dkt * ktil + bt * kk * rK + qq * rQ - kk * ckt;
       if (in) {
         const size_t o = row_of(t) + c;
-        p.dy[o] = lam * dql + rQ;
-        p.dy[plane + o] = bt * lam * dbk + ec * dkt + bt * rK + ckt;
-        p.dy[2 * plane + o] = bt * dbv;
+        E* dy = static_cast<E*>(p.dy);
+        dy[o] = from_f32<E>(lam * dql + rQ);
+        dy[plane + o] = from_f32<E>(bt * lam * dbk + ec * dkt + bt * rK + ckt);
+        dy[2 * plane + o] = from_f32<E>(bt * dbv);
       }
       // dbeta: this wave's 16 channels of row t
       const float dbp = group_sum<16>(dbv * vv + dbk * kk * lam + kk * rK);
@@ -1158,9 +1159,10 @@ __global__ __launch_bounds__(D * (C / 16)) void kda_bwd_pair_kernel(BwdPairParam
       if (t < nval) {
         const size_t o = row_of(t) + c;
         vv = to_f32(static_cast<const E*>(p.y)[2 * plane + o]);
-        p.dy[o] = lam * dql + rQ[m][r];
-        p.dy[plane + o] = bt * lam * dbk + ec * dkt + bt * rK[m][r] + ckt;
-        p.dy[2 * plane + o] = bt * dbv;
+        E* dy = static_cast<E*>(p.dy);
+        dy[o] = from_f32<E>(lam * dql + rQ[m][r]);
+        dy[plane + o] = from_f32<E>(bt * lam * dbk + ec * dkt + bt * rK[m][r] + ckt);
+        dy[2 * plane + o] = from_f32<E>(bt * dbv);
       }
       dbp[m][r] = dbv * vv + dbk * kk * lam + kk * rK[m][r];
     }
@@ -1251,7 +1253,7 @@ __global__ __launch_bounds__(256, 2) void kda_bwd_front_kernel(BwdFrontParams p,
     // tokens t_first .. t_first + 6.  The workgroup's rows are
     // [max(t0 - 3, 0), min(t0 + TOKB + 3, T)).
     Raw8<IO> rw[10];
-    Raw8<float> dzr[7];
+    Raw8<IO> dzr[7];
     {
       constexpr int ES = (int)sizeof(IO);
       const int r0 = t0 - 3 > 0 ? t0 - 3 : 0;
@@ -1263,11 +1265,12 @@ __global__ __launch_bounds__(256, 2) void kda_bwd_front_kernel(BwdFrontParams p,
 #pragma unroll
       for (int m = 0; m < 10; ++m) rw[m].load(rx, voff + m * row_b, 0);
       const int rz1 = t0 + TOKB + 3 < p.T ? t0 + TOKB + 3 : p.T;
-      const BufRes rz = make_buf(p.dy + x * plane + ((size_t)b * p.T + t0) * HD + (size_t)h * D,
-                                 (unsigned)(((long)(rz1 - 1 - t0) * HD + D) * 4));
-      const int zoff = (tf - t0) * (int)(HD * 4) + ch * 4;
+      const BufRes rz = make_buf(static_cast<const IO*>(p.dy) + x * plane + ((size_t)b * p.T + t0) * HD +
+                                     (size_t)h * D,
+                                 (unsigned)(((long)(rz1 - 1 - t0) * HD + D) * ES));
+      const int zoff = (tf - t0) * row_b + ch * ES;
 #pragma unroll
-      for (int u = 0; u < 7; ++u) dzr[u].load(rz, zoff + u * (int)(HD * 4), 0);
+      for (int u = 0; u < 7; ++u) dzr[u].load(rz, zoff + u * row_b, 0);
       if (conv && p.conv_state_in != nullptr && t0 == 0) {
         // tokens -3 .. -1 sit in history rows 0 .. 2 (only the first segment reaches them)
         const BufRes rs = make_buf(static_cast<const IO*>(p.conv_state_in) + ((size_t)b * 3 + x) * 3 * HD +

@@ -187,7 +187,7 @@ struct BwdPairParams {
   const float* dLC;
   const float* dBk;
   const float* dBv;
-  float* dy;           // [3][B*T*H*D]: gradients of (scale * q_hat, k_hat, v_hat)
+  void* dy;            // [3][B*T*H*D], record element type: gradients of (scale * q_hat, k_hat, v_hat)
   float* dg;           // [B*T*H*D]
   float* dbeta_part;   // [B*T*H]: dbeta
   // chunks whose decay spans are too wide for the factored products: a count
@@ -203,7 +203,7 @@ struct BwdFrontParams {
   const void* v;
   const float* conv_w;        // NULL: no convolution
   const void* conv_state_in;  // may be NULL
-  const float* dy;            // [3][B*T*H*D]
+  const void* dy;             // [3][B*T*H*D], the I/O type
   float* dq;
   float* dk;
   float* dv;
