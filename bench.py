@@ -92,7 +92,7 @@ def decode_bytes(w) -> int:
 def backward_bytes(w) -> dict:
     """Algorithmic bytes per launch of each backward kernel (its inputs read once and
     its outputs written once, with the intermediate buffers the kernels hand over:
-    records, checkpoints and dy in the I/O type, per-chunk gradients in fp32) and of the
+    records, checkpoints, per-chunk gradients and dy in the I/O type) and of the
     whole call ("path": raw inputs and dO in, every gradient and the recomputed
     forward outputs out).  dS_T is not given in the benchmark."""
     es = esize(w.io)
@@ -112,11 +112,11 @@ def backward_bytes(w) -> dict:
     nblk = -(-w.T // tokb)
     return {
         "walk": nrec * ((3 * cd + cc) * es + 4 * D) + xe + nrec * (cd + dd) * es + state,
-        "prod": nrec * (2 * cd + 2 * dd) * es + xe + nrec * (3 * cd * 4 + cc * 4 + D * 4),
+        "prod": nrec * (2 * cd + 2 * dd) * es + xe + nrec * ((3 * cd + cc) * es + D * 4),
         # the front end's outputs k, v (and q) in the I/O type, Gamma in float32
-        "t": nrec * (cc * 4 + cd * 4 + cd * es) + 2 * xe + x4 + bth4 + nrec * (2 * cd + cc) * 4,
+        "t": nrec * (cc + cd + cd) * es + 2 * xe + x4 + bth4 + nrec * (2 * cd + cc) * es,
         # the gradients of the front end's outputs (dy) in the I/O type
-        "pair": 3 * xe + x4 + bth4 + nrec * (2 * cc + 4 * cd + D) * 4 + 3 * xe + x4 + bth4,
+        "pair": 3 * xe + x4 + bth4 + nrec * ((2 * cc + 4 * cd) * es + D * 4) + 3 * xe + x4 + bth4,
         "front": 3 * xe + cw + cst_e + 3 * xe + bth4 + 3 * x4 + w.B * nblk * 3 * w.H * D * 16
                  + cst_4 + bth4,
         "path": 4 * xe + tok * w.H * es + cw + cst_e + s0 + xe  # q, k, v, g, beta, filters, history, S0, dO

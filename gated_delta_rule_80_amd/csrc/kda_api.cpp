@@ -238,7 +238,7 @@ struct BwdFwdOut {
   void* y;
   float* gam;
   float* beta;
-  float* tT;
+  void* tT;  // record element type
   void* ckS;
 };
 
@@ -501,21 +501,22 @@ BwdLayout bwd_layout(const kda_backward_args* a) {
     return o;
   };
   const size_t ef = esize(f->io) == 2 ? 2 : 1;  // element-type buffers in float units (rounded up)
-  L.tT = take(nrec * C * C);
+  L.tT = take(nrec * C * C / ef);  // T^T in the record element type
   L.y = take(3 * x / ef);  // front end outputs in the record element type
   L.gam = take(x);
   L.beta = take(bth);
   L.ckS = take(nrec * (D * D + C * D) / ef);  // S_n [D][D] and U [C][D] per record
   L.ckdS = take(nrec * D * D / ef);
   L.dU = take(nrec * C * D / ef);
-  L.dQL = take(nrec * C * D);
-  L.dW = take(nrec * C * D);
-  L.dKt = take(nrec * C * D);
-  L.dP = take(nrec * C * C);
+  // per-record gradients in the record element type (dLC in float)
+  L.dQL = take(nrec * C * D / ef);
+  L.dW = take(nrec * C * D / ef);
+  L.dKt = take(nrec * C * D / ef);
+  L.dP = take(nrec * C * C / ef);
   L.dLC = take(nrec * D);
-  L.dBk = take(nrec * C * D);
-  L.dBv = take(nrec * C * D);
-  L.dA = take(nrec * C * C);
+  L.dBk = take(nrec * C * D / ef);
+  L.dBv = take(nrec * C * D / ef);
+  L.dA = take(nrec * C * C / ef);
   L.dy = take(3 * x / ef);  // record element type
   L.dbp = take(bth);
   L.nfront = kda::bwd_front_blocks(f->T, f->D);

@@ -356,10 +356,10 @@ __global__ __launch_bounds__(256) void kda_bwd_prod_kernel(BwdProdParams p) {
   __syncthreads();
 
   // ---- dQL, dW, dKt: tiles (t, c); dP: tiles (i, j) with j <= i
-  float* dQL = p.dQL + (size_t)rec * C * D;
-  float* dW = p.dW + (size_t)rec * C * D;
-  float* dKt = p.dKt + (size_t)rec * C * D;
-  float* dP = p.dP + (size_t)rec * C * C;
+  E* dQL = static_cast<E*>(p.dQL) + (size_t)rec * C * D;
+  E* dW = static_cast<E*>(p.dW) + (size_t)rec * C * D;
+  E* dKt = static_cast<E*>(p.dKt) + (size_t)rec * C * D;
+  E* dP = static_cast<E*>(p.dP) + (size_t)rec * C * C;
   RowFrag<E, D> fdo, fdu, fu;
   load_do(fdo, 16 * Rt + r);
   fdu.load(gdU + (size_t)(16 * Rt + r) * D, g4);
@@ -375,9 +375,9 @@ __global__ __launch_bounds__(256) void kda_bwd_prod_kernel(BwdProdParams p) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const size_t o = (size_t)(16 * Rt + 4 * g4 + e) * D + 16 * Ct + r;
-      dQL[o] = aq[e];
-      dW[o] = -aw[e];
-      dKt[o] = ak[e];
+      dQL[o] = from_f32<E>(aq[e]);
+      dW[o] = from_f32<E>(-aw[e]);
+      dKt[o] = from_f32<E>(ak[e]);
     }
     if (Rt == 0) {
       // dLC of rows c = 16 Ct + r: this lane's pieces of the row are the same
@@ -399,7 +399,7 @@ __global__ __launch_bounds__(256) void kda_bwd_prod_kernel(BwdProdParams p) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = 16 * It + 4 * g4 + e, j = 16 * Jt + r;
-      dP[(size_t)i * C + j] = j <= i ? acc[e] : 0.f;
+      dP[(size_t)i * C + j] = from_f32<E>(j <= i ? acc[e] : 0.f);
     }
   }
 }
@@ -448,9 +448,9 @@ __global__ __launch_bounds__(512) void kda_bwd_t_kernel(BwdTParams p) {
     const int n = rec % p.NT;
     const int bh = rec / p.NT;
     const int h = bh % p.H, b = bh / p.H;
-    const float* gdW = p.dW + (size_t)rec * C * D;
+    const float* gdW = static_cast<const float*>(p.dW) + (size_t)rec * C * D;
     const E* gdU = static_cast<const E*>(p.dU) + (size_t)rec * C * D;  // [t][v]
-    const float* gTt = p.tT + (size_t)rec * C * C;
+    const float* gTt = static_cast<const float*>(p.tT) + (size_t)rec * C * C;
 #pragma unroll
     for (int i = 0; i < N4; ++i) {
       const int it = tid + NT * i;
@@ -562,7 +562,7 @@ __global__ __launch_bounds__(512) void kda_bwd_t_kernel(BwdTParams p) {
     }
     __syncthreads();
     // ---- dA = -T^T Y  (j < i)
-    float* gdA = p.dA + (size_t)rec * C * C;
+    float* gdA = static_cast<float*>(p.dA) + (size_t)rec * C * C;
     for (int tile = wave; tile < RT * RT; tile += NW) {
       const int It = tile / RT, Jt = tile % RT;
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -577,8 +577,8 @@ __global__ __launch_bounds__(512) void kda_bwd_t_kernel(BwdTParams p) {
       }
     }
     // ---- dBk = T^T dW,  dBv = T^T dU  (tiles (j, c))
-    float* gdBk = p.dBk + (size_t)rec * C * D;
-    float* gdBv = p.dBv + (size_t)rec * C * D;
+    float* gdBk = static_cast<float*>(p.dBk) + (size_t)rec * C * D;
+    float* gdBv = static_cast<float*>(p.dBv) + (size_t)rec * C * D;
     for (int tile = wave; tile < RT * CT; tile += NW) {
       const int Jt = tile / CT, Ct = tile % CT;
       f32x4 ak = {0.f, 0.f, 0.f, 0.f}, av = ak;
@@ -637,15 +637,15 @@ __global__ __launch_bounds__(512) void kda_bwd_t16_kernel(BwdTParams p) {
   const size_t plane = (size_t)p.B * p.T * HD;
 
   // ---- images
-  const float* gdW = p.dW + (size_t)rec * C * D;
+  const __bf16* gdW = static_cast<const __bf16*>(p.dW) + (size_t)rec * C * D;
   const __bf16* gdU = static_cast<const __bf16*>(p.dU) + (size_t)rec * C * D;  // [t][v]
-  const float* gTt = p.tT + (size_t)rec * C * C;                               // [j][i] = T[i][j]
+  const __bf16* gTt = static_cast<const __bf16*>(p.tT) + (size_t)rec * C * C;  // [j][i] = T[i][j]
   for (int it = tid; it < C * D / 4; it += NT) {
     const int t = it / (D / 4), c4 = 4 * (it % (D / 4));
-    const f32x4 w = *reinterpret_cast<const f32x4*>(gdW + (size_t)t * D + c4);
+    const bf16x4 w = *reinterpret_cast<const bf16x4*>(gdW + (size_t)t * D + c4);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const __bf16 x = (__bf16)w[e];
+      const __bf16 x = w[e];
       iW[SD::at(t, c4 + e)] = x;
       iWt[SC::at(c4 + e, t)] = x;
     }
@@ -659,10 +659,10 @@ __global__ __launch_bounds__(512) void kda_bwd_t16_kernel(BwdTParams p) {
   }
   for (int it = tid; it < C * C / 4; it += NT) {
     const int a = it / (C / 4), b4 = 4 * (it % (C / 4));
-    const f32x4 x = *reinterpret_cast<const f32x4*>(gTt + (size_t)a * C + b4);
+    const bf16x4 x = *reinterpret_cast<const bf16x4*>(gTt + (size_t)a * C + b4);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const __bf16 y = (__bf16)x[e];
+      const __bf16 y = x[e];
       iTt[SC::at(a, b4 + e)] = y;  // T^T[a][b]
       iT[SC::at(b4 + e, a)] = y;   // T[b][a]
     }
@@ -724,7 +724,7 @@ __global__ __launch_bounds__(512) void kda_bwd_t16_kernel(BwdTParams p) {
   }
   __syncthreads();
   // ---- dA (i, j) = -sum_m T^T[i][m] Y^T[j][m]  (j < i)
-  float* gdA = p.dA + (size_t)rec * C * C;
+  __bf16* gdA = static_cast<__bf16*>(p.dA) + (size_t)rec * C * C;
   for (int tile = wave; tile < RT * RT; tile += NW) {
     const int It = tile / RT, Jt = tile % RT;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -737,12 +737,12 @@ __global__ __launch_bounds__(512) void kda_bwd_t16_kernel(BwdTParams p) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int i = 16 * It + 4 * g4 + e, j = 16 * Jt + r;
-      gdA[(size_t)i * C + j] = j < i ? -acc[e] : 0.f;
+      gdA[(size_t)i * C + j] = (__bf16)(j < i ? -acc[e] : 0.f);
     }
   }
   // ---- dBk (j, c) = sum_i T^T[j][i] dW^T[c][i],  dBv likewise with dU
-  float* gdBk = p.dBk + (size_t)rec * C * D;
-  float* gdBv = p.dBv + (size_t)rec * C * D;
+  __bf16* gdBk = static_cast<__bf16*>(p.dBk) + (size_t)rec * C * D;
+  __bf16* gdBv = static_cast<__bf16*>(p.dBv) + (size_t)rec * C * D;
   for (int tile = wave; tile < RT * CT; tile += NW) {
     const int Jt = tile / CT, Ct = tile % CT;
     RowFrag<__bf16, C> ft, fw, fu;
@@ -755,8 +755,8 @@ __global__ __launch_bounds__(512) void kda_bwd_t16_kernel(BwdTParams p) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const size_t o = (size_t)(16 * Jt + 4 * g4 + e) * D + 16 * Ct + r;
-      gdBk[o] = ak[e];
-      gdBv[o] = av[e];
+      gdBk[o] = (__bf16)ak[e];
+      gdBv[o] = (__bf16)av[e];
     }
   }
 }
@@ -845,12 +845,12 @@ __global__ __launch_bounds__(4 * D, D / 32 > 1 ? D / 32 : 1) void kda_bwd_pair_m
     if (lane == 0) sfat[wave] = wfat ? 1 : 0;
   }
   // dA and dP into LDS
-  const float* gdA = p.dA + (size_t)rec * C * C;
-  const float* gdP = p.dP + (size_t)rec * C * C;
+  const E* gdA = static_cast<const E*>(p.dA) + (size_t)rec * C * C;
+  const E* gdP = static_cast<const E*>(p.dP) + (size_t)rec * C * C;
   for (int it = tid; it < C * C / 4; it += NTH) {
     const int i = it / (C / 4), j4 = 4 * (it % (C / 4));
-    const f32x4 va = *reinterpret_cast<const f32x4*>(gdA + (size_t)i * C + j4);
-    const f32x4 vp = *reinterpret_cast<const f32x4*>(gdP + (size_t)i * C + j4);
+    const f32x4 va = load4v(gdA + (size_t)i * C + j4);
+    const f32x4 vp = load4v(gdP + (size_t)i * C + j4);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       sdA[i * LA + j4 + e] = va[e];
@@ -882,19 +882,19 @@ __global__ __launch_bounds__(4 * D, D / 32 > 1 ? D / 32 : 1) void kda_bwd_pair_m
   // ---- per row block pb: the block-pair products, then its element terms
   float* sdG = sG;  // [C][LD]
   const float gC = gam_at(C - 1);
-  const float* gdQL = p.dQL + (size_t)rec * C * D;
-  const float* gdKt = p.dKt + (size_t)rec * C * D;
-  const float* gdBk = p.dBk + (size_t)rec * C * D;
-  const float* gdBv = p.dBv + (size_t)rec * C * D;
+  const E* gdQL = static_cast<const E*>(p.dQL) + (size_t)rec * C * D;
+  const E* gdKt = static_cast<const E*>(p.dKt) + (size_t)rec * C * D;
+  const E* gdBk = static_cast<const E*>(p.dBk) + (size_t)rec * C * D;
+  const E* gdBv = static_cast<const E*>(p.dBv) + (size_t)rec * C * D;
   float colsum = 0.f;  // sum over this lane's rows of dKt Ktil
   // the element terms' inputs of row t: dQL, dKt, dBk, dBv, Gamma, q', k, v (rows
   // past the end of the sequence read the last row; q', k, v are zeroed there)
   auto load_row = [&](int t, float (&v)[8]) {
     const size_t lo = (size_t)t * D + c;
-    v[0] = gdQL[lo];
-    v[1] = gdKt[lo];
-    v[2] = gdBk[lo];
-    v[3] = gdBv[lo];
+    v[0] = to_f32(gdQL[lo]);
+    v[1] = to_f32(gdKt[lo]);
+    v[2] = to_f32(gdBk[lo]);
+    v[3] = to_f32(gdBv[lo]);
     const size_t o = row_of(t < nval ? t : nval - 1) + c;
     v[4] = p.gam[o];
     v[5] = to_f32(y[o]);
@@ -1046,12 +1046,12 @@ __global__ __launch_bounds__(D * (C / 16)) void kda_bwd_pair_kernel(BwdPairParam
   const int nval = p.T - n * C < C ? p.T - n * C : C;  // tokens of the sequence in this chunk
   auto row_of = [&](int t) { return ((size_t)b * p.T + (size_t)n * C + t) * HD + (size_t)h * D; };
 
-  const float* gdA = p.dA + (size_t)rec * C * C;
-  const float* gdP = p.dP + (size_t)rec * C * C;
+  const E* gdA = static_cast<const E*>(p.dA) + (size_t)rec * C * C;
+  const E* gdP = static_cast<const E*>(p.dP) + (size_t)rec * C * C;
   for (int it = tid; it < C * C / 4; it += NTH) {
     const int i = it / (C / 4), j4 = 4 * (it % (C / 4));
-    *reinterpret_cast<f32x4*>(&sdA[i * LA + j4]) = *reinterpret_cast<const f32x4*>(gdA + (size_t)i * C + j4);
-    *reinterpret_cast<f32x4*>(&sdP[i * LA + j4]) = *reinterpret_cast<const f32x4*>(gdP + (size_t)i * C + j4);
+    *reinterpret_cast<f32x4*>(&sdA[i * LA + j4]) = load4v(gdA + (size_t)i * C + j4);
+    *reinterpret_cast<f32x4*>(&sdP[i * LA + j4]) = load4v(gdP + (size_t)i * C + j4);
   }
   for (int it = tid; it < C * D / 4; it += NTH) {
     const int t = it / (D / 4), c4 = 4 * (it % (D / 4));
@@ -1135,10 +1135,10 @@ __global__ __launch_bounds__(D * (C / 16)) void kda_bwd_pair_kernel(BwdPairParam
 
   // ---- element terms for this thread's rows
   const float gC = sG[(C - 1) * LD + c];
-  const float* gdQL = p.dQL + (size_t)rec * C * D;
-  const float* gdKt = p.dKt + (size_t)rec * C * D;
-  const float* gdBk = p.dBk + (size_t)rec * C * D;
-  const float* gdBv = p.dBv + (size_t)rec * C * D;
+  const E* gdQL = static_cast<const E*>(p.dQL) + (size_t)rec * C * D;
+  const E* gdKt = static_cast<const E*>(p.dKt) + (size_t)rec * C * D;
+  const E* gdBk = static_cast<const E*>(p.dBk) + (size_t)rec * C * D;
+  const E* gdBv = static_cast<const E*>(p.dBv) + (size_t)rec * C * D;
   float colsum = 0.f;  // sum over this thread's rows of dKt Ktil
   float dgam[4][4], dbp[4][4];
   for (int m = 0; m < 4; ++m) {
@@ -1146,7 +1146,8 @@ __global__ __launch_bounds__(D * (C / 16)) void kda_bwd_pair_kernel(BwdPairParam
     for (int r = 0; r < 4; ++r) {
       const int t = 4 * ck[m] + r;
       const size_t lo = (size_t)t * D + c;
-      const float dql = gdQL[lo], dkt = gdKt[lo], dbk = gdBk[lo], dbv = gdBv[lo];
+      const float dql = to_f32(gdQL[lo]), dkt = to_f32(gdKt[lo]), dbk = to_f32(gdBk[lo]),
+                  dbv = to_f32(gdBv[lo]);
       const float kk = sK[t * LD + c], qq = sQ[t * LD + c], bt = sB[t];
       const float lam = __builtin_amdgcn_exp2f(sG[t * LD + c]);
       const float ec = __builtin_amdgcn_exp2f(gC - sG[t * LD + c]);

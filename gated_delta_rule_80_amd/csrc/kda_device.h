@@ -61,6 +61,13 @@ __device__ __forceinline__ void store8(float* p, const float* in) {
   *reinterpret_cast<f32x4*>(p) = a;
   *reinterpret_cast<f32x4*>(p + 4) = b;
 }
+// 4 consecutive elements as float32 (8-byte aligned bf16 / 16-byte aligned fp32)
+__device__ __forceinline__ f32x4 load4v(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ f32x4 load4v(const __bf16* p) {
+  const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
+  return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+
 // 4 consecutive elements (8-byte aligned bf16 / 16-byte aligned fp32)
 __device__ __forceinline__ void store4(__bf16* p, float a, float b, float c, float d) {
   bf16x4 v;

@@ -99,11 +99,11 @@ struct PrepParams {
   // backward mode (all NULL otherwise): the front end's outputs in float32 --
   // y = (scale * q_hat, k_hat, v_hat) [3][B*T*H*D], gam = the chunk-local
   // cumulative log2-decay [B*T*H*D], beta [B*T*H] -- and T^T = ((I + A)^-1)^T
-  // per record [C][C]
+  // per record [C][C] in the record element type
   void* y_out;
   float* gam_out;
   float* beta_out;
-  float* t_out;
+  void* t_out;
 };
 
 struct StateParams {
@@ -138,7 +138,8 @@ struct OutStageParams {
 //   ckdS [rec][D][D]     dS_{n+1} (gradient of the chunk's end state), element type
 //   dU   [rec][C][D]     dU_n, element type
 //   dQL, dW, dKt [rec][C][D], dP [rec][C][C], dLC [rec][D]: gradients of the
-//   record's quantities;  dBk, dBv [rec][C][D], dA [rec][C][C]
+//   record's quantities;  dBk, dBv [rec][C][D], dA [rec][C][C]; all in the
+//   element type except dLC (float)
 struct BwdWalkParams {
   const char* ws;      // forward records
   const void* dO;      // [B][T][H][D]
@@ -155,24 +156,24 @@ struct BwdProdParams {
   const void* ckS;
   const void* ckdS;
   const void* dU;
-  float* dQL;
-  float* dW;
-  float* dKt;
-  float* dP;
+  void* dQL;
+  void* dW;
+  void* dKt;
+  void* dP;
   float* dLC;
   int B, T, H, NT;
 };
 
 struct BwdTParams {
-  const float* tT;     // T^T per record
+  const void* tT;      // T^T per record, element type
   const void* y;       // front end outputs [3][B*T*H*D], record element type
   const float* gam;
   const float* beta;
-  const float* dW;
+  const void* dW;
   const void* dU;
-  float* dBk;
-  float* dBv;
-  float* dA;
+  void* dBk;
+  void* dBv;
+  void* dA;
   int B, T, H, NT;
 };
 
@@ -180,13 +181,13 @@ struct BwdPairParams {
   const void* y;       // front end outputs [3][B*T*H*D], record element type
   const float* gam;
   const float* beta;
-  const float* dA;
-  const float* dP;
-  const float* dQL;
-  const float* dKt;
+  const void* dA;      // the per-record gradients in the element type (dLC float)
+  const void* dP;
+  const void* dQL;
+  const void* dKt;
   const float* dLC;
-  const float* dBk;
-  const float* dBv;
+  const void* dBk;
+  const void* dBv;
   void* dy;            // [3][B*T*H*D], record element type: gradients of (scale * q_hat, k_hat, v_hat)
   float* dg;           // [B*T*H*D]
   float* dbeta_part;   // [B*T*H]: dbeta

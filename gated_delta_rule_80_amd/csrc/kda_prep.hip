@@ -534,11 +534,12 @@ __global__ __launch_bounds__(fast_threads<E>()) void kda_chunk_prep_kernel(PrepP
     __syncthreads();
   }
   if (p.t_out != nullptr) {
-    // backward mode: T^T in float32 (the upper triangle of T is not computed here)
-    float* to = p.t_out + (size_t)rec * C * C;
+    // backward mode: T^T in the element type (the upper triangle of T is not
+    // computed here)
+    E* to = static_cast<E*>(p.t_out) + (size_t)rec * C * C;
     for (int it = tid; it < C * C; it += NTH) {
       const int jj = it / C, i = it % C;  // to[jj][i] = T[i][jj]
-      to[it] = jj <= i ? sT[i * LA + jj] : 0.f;
+      to[it] = from_f32<E>(jj <= i ? sT[i * LA + jj] : 0.f);
     }
   }
   __syncthreads();  // A and T (float) are dead

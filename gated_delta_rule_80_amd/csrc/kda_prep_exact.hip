@@ -374,11 +374,11 @@ __global__ __launch_bounds__(kPrepThreads) void kda_chunk_prep_exact_kernel(Prep
     __syncthreads();
   }
   if (p.t_out != nullptr) {
-    // backward mode: T^T in float32
-    float* to = p.t_out + (size_t)rec * C * C;
+    // backward mode: T^T in the element type
+    E* to = static_cast<E*>(p.t_out) + (size_t)rec * C * C;
     for (int it = tid; it < C * C; it += kPrepThreads) {
       const int jj = it / C, i = it % C;  // to[jj][i] = T[i][jj]
-      to[it] = jj <= i ? sT[i * LA + jj] : 0.f;
+      to[it] = from_f32<E>(jj <= i ? sT[i * LA + jj] : 0.f);
     }
   }
   // T in the matrix-core element type
