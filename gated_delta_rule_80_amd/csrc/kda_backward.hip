@@ -1302,7 +1302,10 @@ __global__ __launch_bounds__(256, 2) void kda_bwd_front_kernel(BwdFrontParams p,
     for (int u = 0; u < 7; ++u) {
       if (u >= 4 && !last) continue;  // the whole row group takes the same branch
       const int t = tf + u;
-      float pre[8], y[8], dz[8];
+      // sigmoid(pre) once per element, with the hardware exp2 and reciprocal as in
+      // the forward front end (so y is the forward's value), for y = pre sigmoid(pre)
+      // and for the SiLU derivative
+      float pre[8], sg[8], y[8], dz[8];
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         if (conv) {
@@ -1311,9 +1314,11 @@ __global__ __launch_bounds__(256, 2) void kda_bwd_front_kernel(BwdFrontParams p,
           acc = fmaf(w[2][c], raw[u + 2][c], acc);
           acc = fmaf(w[3][c], raw[u + 3][c], acc);
           pre[c] = acc;
-          y[c] = silu(acc);
+          sg[c] = sigmoid_fast(acc);
+          y[c] = acc * sg[c];
         } else {
           pre[c] = 0.f;
+          sg[c] = 1.f;
           y[c] = raw[u + 3][c];
         }
         dz[c] = dzr[u][c];  // zero past the end of the sequence
@@ -1329,7 +1334,7 @@ __global__ __launch_bounds__(256, 2) void kda_bwd_front_kernel(BwdFrontParams p,
         }
         yy = group_sum<NOCT>(yy);
         yd = group_sum<NOCT>(yd);
-        const float rn = 1.0f / sqrtf(yy + p.eps);
+        const float rn = __builtin_amdgcn_rsqf(yy + p.eps);  // as the forward normalises
         const float k3 = yd * rn * rn * rn;
 #pragma unroll
         for (int c = 0; c < 8; ++c) dyv[c] = dz[c] * rn - y[c] * k3;
@@ -1341,8 +1346,7 @@ __global__ __launch_bounds__(256, 2) void kda_bwd_front_kernel(BwdFrontParams p,
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         if (conv) {
-          const float sg = sigmoid(pre[c]);
-          dp[c] = dyv[c] * sg * (1.0f + pre[c] * (1.0f - sg));
+          dp[c] = dyv[c] * sg[c] * (1.0f + pre[c] * (1.0f - sg[c]));
         } else {
           dp[c] = dyv[c];
         }
