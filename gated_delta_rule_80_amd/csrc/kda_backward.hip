@@ -368,17 +368,16 @@ __global__ __launch_bounds__(256) void kda_bwd_prod_kernel(BwdProdParams p) {
     RowFrag<E, D> fs, fds;
     fs.load(ckS + (size_t)(16 * Ct + r) * D, g4);
     fds.load(ckdS + (size_t)(16 * Ct + r) * D, g4);
+    // tiles formed transposed, (c, t): lane (r, g4) holds columns 16 Ct + 4 g4 + e
+    // of row t = 16 Rt + r, stored as 4 contiguous elements
     f32x4 aq = {0.f, 0.f, 0.f, 0.f}, aw = aq, ak = aq;
-    mma<D>(aq, fdo, fs);
-    mma<D>(aw, fdu, fs);
-    mma<D>(ak, fu, fds);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const size_t o = (size_t)(16 * Rt + 4 * g4 + e) * D + 16 * Ct + r;
-      dQL[o] = from_f32<E>(aq[e]);
-      dW[o] = from_f32<E>(-aw[e]);
-      dKt[o] = from_f32<E>(ak[e]);
-    }
+    mma<D>(aq, fs, fdo);
+    mma<D>(aw, fs, fdu);
+    mma<D>(ak, fds, fu);
+    const size_t o = (size_t)(16 * Rt + r) * D + 16 * Ct + 4 * g4;
+    store4(dQL + o, aq[0], aq[1], aq[2], aq[3]);
+    store4(dW + o, -aw[0], -aw[1], -aw[2], -aw[3]);
+    store4(dKt + o, ak[0], ak[1], ak[2], ak[3]);
     if (Rt == 0) {
       // dLC of rows c = 16 Ct + r: this lane's pieces of the row are the same
       // elements of fs and fds, the rest sit in the lanes of the other g4
@@ -390,17 +389,17 @@ __global__ __launch_bounds__(256) void kda_bwd_prod_kernel(BwdProdParams p) {
   }
   for (int Jt = sub; Jt < RT; Jt += WPR) {
     const int It = Rt;
+    // transposed tile (j, i): lane (r, g4) holds columns j = 16 Jt + 4 g4 + e of
+    // row i = 16 It + r
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if (Jt <= It) {
       RowFrag<E, D> fb;
       fb.load(sU + (16 * Jt + r) * LD, g4);
-      mma<D>(acc, fdo, fb);
+      mma<D>(acc, fb, fdo);
     }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = 16 * It + 4 * g4 + e, j = 16 * Jt + r;
-      dP[(size_t)i * C + j] = from_f32<E>(j <= i ? acc[e] : 0.f);
-    }
+    const int i = 16 * It + r, j0 = 16 * Jt + 4 * g4;
+    store4(dP + (size_t)i * C + j0, j0 <= i ? acc[0] : 0.f, j0 + 1 <= i ? acc[1] : 0.f,
+           j0 + 2 <= i ? acc[2] : 0.f, j0 + 3 <= i ? acc[3] : 0.f);
   }
 }
 
