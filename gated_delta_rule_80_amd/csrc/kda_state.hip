@@ -336,17 +336,21 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void kda_chunk_state_kernel(
     lds_barrier();  // every wave holds its fragments: the image may be overwritten
     if (n + 1 < nch) issue_copy(n + 1);
     load_gate(n);  // buffer n % 2: chunk n - 2's, stored during step n - 1
-    // backward mode: the record's checkpoint, S_n [c][v] then U [t][v]
+    // backward mode: the record's checkpoint, S_n [c][v] then U [t][v].  Both are
+    // written from their LDS copies (sS holds S_n as staged for this step, sU the
+    // step's U after the next barrier): a lane reads 4 consecutive value columns of
+    // one row there and stores them as one 4-element piece (the accumulators hold 4
+    // rows of one column, which would take 4 scattered stores).
     E* ck = CK ? static_cast<E*>(p.ckpt) + (rec0 + n) * ((size_t)D * D + (size_t)C * D) : nullptr;
     if constexpr (CK) {
+      constexpr int V4 = VB / 4;  // 4-column pieces per row of the block
 #pragma unroll
-      for (int i = 0; i < NS; ++i) {
-        const int u = wave + NW * i;
-        if (FULL_S || u < CT * VT) {
-          const int Ct = u % CT, Vt = u / CT;
-          const int v = vb0 + 16 * Vt + r, c0 = 16 * Ct + 4 * g4;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) ck[(size_t)(c0 + e) * D + v] = from_f32<E>(accS[i][e]);
+      for (int k = 0; k < (D * V4 + NT - 1) / NT; ++k) {
+        const int idx = tid + NT * k;
+        if ((D * V4) % NT == 0 || idx < D * V4) {
+          const int c = idx / V4, v4 = 4 * (idx % V4);
+          store4(ck + (size_t)c * D + vb0 + v4, to_f32(sS[(v4) * LS + c]), to_f32(sS[(v4 + 1) * LS + c]),
+                 to_f32(sS[(v4 + 2) * LS + c]), to_f32(sS[(v4 + 3) * LS + c]));
         }
       }
     }
@@ -367,17 +371,24 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void kda_chunk_state_kernel(
         mma<D>(accO[i], sf, fql);  // (v, t) tile of S^T QL^T
         store4(&sU[(16 * Vt + r) * LU + 16 * R + 4 * g4], fu[i][0] - ws[0], fu[i][1] - ws[1],
                fu[i][2] - ws[2], fu[i][3] - ws[3]);
-        if constexpr (CK) {
-          // the same rounded U for the backward: rows t = 16 R + 4 g4 + e
-          E* cu = ck + (size_t)D * D;
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            cu[(size_t)(16 * R + 4 * g4 + e) * D + vb0 + 16 * Vt + r] = from_f32<E>(fu[i][e] - ws[e]);
-        }
       }
     }
     lds_barrier();  // sU complete; every read of sS for this chunk is done
     if (n > 0) store_out(n - 1);
+    if constexpr (CK) {
+      // the same rounded U for the backward, from sU
+      E* cu = ck + (size_t)D * D;
+      constexpr int V4 = VB / 4;
+#pragma unroll
+      for (int k = 0; k < (C * V4 + NT - 1) / NT; ++k) {
+        const int idx = tid + NT * k;
+        if ((C * V4) % NT == 0 || idx < C * V4) {
+          const int t = idx / V4, v4 = 4 * (idx % V4);
+          store4(cu + (size_t)t * D + vb0 + v4, to_f32(sU[(v4) * LU + t]), to_f32(sU[(v4 + 1) * LU + t]),
+                 to_f32(sU[(v4 + 2) * LU + t]), to_f32(sU[(v4 + 3) * LU + t]));
+        }
+      }
+    }
     // ---- O^T += U^T P^T (j <= i), store O
 #pragma unroll
     for (int i = 0; i < NU; ++i) {
