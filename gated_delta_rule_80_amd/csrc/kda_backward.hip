@@ -1216,6 +1216,8 @@ __global__ __launch_bounds__(256, 2) void kda_bwd_front_kernel(BwdFrontParams p,
   constexpr int TOKB = 4 * SEG;  // tokens per workgroup
   constexpr int LDP = D + 4;
   constexpr int SPW = 64 / NOCT;  // segments per wave
+  constexpr int NW = 4;           // waves
+  static_assert(SPW >= 3, "the last wave holds the 3 segments that take the rows past the block");
   __shared__ float sw[3 * 4 * D];            // filters [x][tap][c]
   __shared__ float sdp[(TOKB + 3) * LDP];    // dpre of the block and the 3 tokens after it
   __shared__ float sred[4][3 * 4 * D];       // filter partials per wave [x][tap][c]
@@ -1229,7 +1231,6 @@ __global__ __launch_bounds__(256, 2) void kda_bwd_front_kernel(BwdFrontParams p,
   const int ch = 8 * j;
   const int t0 = blk * TOKB;
   const int tf = t0 + 4 * s;
-  const bool last = s == SEG - 1;
   const size_t HD = (size_t)p.H * D;
   const size_t plane = (size_t)p.B * p.T * HD;
   const bool conv = p.conv_w != nullptr;
@@ -1248,12 +1249,18 @@ __global__ __launch_bounds__(256, 2) void kda_bwd_front_kernel(BwdFrontParams p,
     float* dst = x == 0 ? p.dq : (x == 1 ? p.dk : p.dv);
     // Every global load of this tensor is issued before the first use, as
     // range-checked buffer loads (zeros outside the range, no branches between
-    // the loads): raw rows t_first - 3 .. t_first + 6 (row m = token
-    // t_first - 3 + m; tokens < 0 from the conv history) and the rows of dz for
-    // tokens t_first .. t_first + 6.  The workgroup's rows are
-    // [max(t0 - 3, 0), min(t0 + TOKB + 3, T)).
-    Raw8<IO> rw[10];
-    Raw8<IO> dzr[7];
+    // the loads): raw rows t_first - 3 .. t_first + 3 (row m = token t_first - 3 + m;
+    // tokens < 0 from the conv history) and the rows of dz for tokens t_first ..
+    // t_first + 3.  The dx of the block's last tokens also needs the dpre of the 3
+    // tokens past the block: in the last wave, segment SEG - SPW + hh (hh < 3)
+    // computes token t0 + TOKB + hh for its channels, from raw rows of that token
+    // and 3 before it and its dz row (so no wave takes more than 5 rows).  The
+    // workgroup's rows are [max(t0 - 3, 0), min(t0 + TOKB + 3, T)).
+    const int hh = s - (SEG - SPW);                     // 0 .. SPW - 1 in the last wave
+    const bool halo = hh >= 0 && hh < 3;
+    const int hc = halo ? hh : 0;                       // a valid row for the others' loads
+    Raw8<IO> rw[7], hw[4];
+    Raw8<IO> dzr[4], hz;
     {
       constexpr int ES = (int)sizeof(IO);
       const int r0 = t0 - 3 > 0 ? t0 - 3 : 0;
@@ -1263,14 +1270,18 @@ __global__ __launch_bounds__(256, 2) void kda_bwd_front_kernel(BwdFrontParams p,
                                  (unsigned)(((long)(r1 - 1 - r0) * HD + D) * ES));
       const int voff = (tf - 3 - r0) * row_b + ch * ES;
 #pragma unroll
-      for (int m = 0; m < 10; ++m) rw[m].load(rx, voff + m * row_b, 0);
+      for (int m = 0; m < 7; ++m) rw[m].load(rx, voff + m * row_b, 0);
+      const int hoff = (t0 + TOKB + hc - 3 - r0) * row_b + ch * ES;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) hw[m].load(rx, hoff + m * row_b, 0);
       const int rz1 = t0 + TOKB + 3 < p.T ? t0 + TOKB + 3 : p.T;
       const BufRes rz = make_buf(static_cast<const IO*>(p.dy) + x * plane + ((size_t)b * p.T + t0) * HD +
                                      (size_t)h * D,
                                  (unsigned)(((long)(rz1 - 1 - t0) * HD + D) * ES));
       const int zoff = (tf - t0) * row_b + ch * ES;
 #pragma unroll
-      for (int u = 0; u < 7; ++u) dzr[u].load(rz, zoff + u * row_b, 0);
+      for (int u = 0; u < 4; ++u) dzr[u].load(rz, zoff + u * row_b, 0);
+      hz.load(rz, (TOKB + hc) * row_b + ch * ES, 0);
       if (conv && p.conv_state_in != nullptr && t0 == 0) {
         // tokens -3 .. -1 sit in history rows 0 .. 2 (only the first segment reaches them)
         const BufRes rs = make_buf(static_cast<const IO*>(p.conv_state_in) + ((size_t)b * 3 + x) * 3 * HD +
@@ -1284,9 +1295,9 @@ __global__ __launch_bounds__(256, 2) void kda_bwd_front_kernel(BwdFrontParams p,
         }
       }
     }
-    float raw[10][8];
+    float raw[7][8];
 #pragma unroll
-    for (int m = 0; m < 10; ++m)
+    for (int m = 0; m < 7; ++m)
 #pragma unroll
       for (int c = 0; c < 8; ++c) raw[m][c] = rw[m][c];
     float w[4][8];
@@ -1296,11 +1307,9 @@ __global__ __launch_bounds__(256, 2) void kda_bwd_front_kernel(BwdFrontParams p,
 #pragma unroll
         for (int c = 0; c < 8; ++c) w[tau][c] = sw[(x * 4 + tau) * D + ch + c];
     }
-    // dpre of tokens t_first .. t_first + 3 (+ 3 more for the last segment)
-#pragma unroll
-    for (int u = 0; u < 7; ++u) {
-      if (u >= 4 && !last) continue;  // the whole row group takes the same branch
-      const int t = tf + u;
+    // dpre of one token into sdp row srow, from the raw rows rr[u0 .. u0 + 3] (the
+    // token and the 3 before it) and its dz row
+    auto dpre_row = [&](const auto& rr, int u0, const Raw8<IO>& dzrow, int srow, bool st) {
       // sigmoid(pre) once per element, with the hardware exp2 and reciprocal as in
       // the forward front end (so y is the forward's value), for y = pre sigmoid(pre)
       // and for the SiLU derivative
@@ -1308,19 +1317,19 @@ __global__ __launch_bounds__(256, 2) void kda_bwd_front_kernel(BwdFrontParams p,
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
         if (conv) {
-          float acc = w[0][c] * raw[u][c];
-          acc = fmaf(w[1][c], raw[u + 1][c], acc);
-          acc = fmaf(w[2][c], raw[u + 2][c], acc);
-          acc = fmaf(w[3][c], raw[u + 3][c], acc);
+          float acc = w[0][c] * rr[u0][c];
+          acc = fmaf(w[1][c], rr[u0 + 1][c], acc);
+          acc = fmaf(w[2][c], rr[u0 + 2][c], acc);
+          acc = fmaf(w[3][c], rr[u0 + 3][c], acc);
           pre[c] = acc;
           sg[c] = sigmoid_fast(acc);
           y[c] = acc * sg[c];
         } else {
           pre[c] = 0.f;
           sg[c] = 1.f;
-          y[c] = raw[u + 3][c];
+          y[c] = rr[u0 + 3][c];
         }
-        dz[c] = dzr[u][c];  // zero past the end of the sequence
+        dz[c] = dzrow[c];  // zero past the end of the sequence
         if (x == 0) dz[c] *= p.scale;
       }
       float dyv[8];
@@ -1350,8 +1359,20 @@ __global__ __launch_bounds__(256, 2) void kda_bwd_front_kernel(BwdFrontParams p,
           dp[c] = dyv[c];
         }
       }
-      *reinterpret_cast<f32x4*>(&sdp[(4 * s + u) * LDP + ch]) = f32x4{dp[0], dp[1], dp[2], dp[3]};
-      *reinterpret_cast<f32x4*>(&sdp[(4 * s + u) * LDP + ch + 4]) = f32x4{dp[4], dp[5], dp[6], dp[7]};
+      if (st) {
+        *reinterpret_cast<f32x4*>(&sdp[srow * LDP + ch]) = f32x4{dp[0], dp[1], dp[2], dp[3]};
+        *reinterpret_cast<f32x4*>(&sdp[srow * LDP + ch + 4]) = f32x4{dp[4], dp[5], dp[6], dp[7]};
+      }
+    };
+#pragma unroll
+    for (int u = 0; u < 4; ++u) dpre_row(raw, u, dzr[u], 4 * s + u, true);
+    if (wave == NW - 1) {  // the whole wave takes this branch
+      float hraw[4][8];
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) hraw[m][c] = hw[m][c];
+      dpre_row(hraw, 0, hz, TOKB + hc, halo);
     }
     __syncthreads();
     // dx of the own tokens
@@ -1435,7 +1456,6 @@ __global__ __launch_bounds__(256, 2) void kda_bwd_front_kernel(BwdFrontParams p,
       }
     }
   }
-  (void)SPW;
 }
 
 // Clears the count of chunks listed for the exact pair kernel.
