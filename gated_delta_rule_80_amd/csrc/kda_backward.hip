@@ -317,6 +317,12 @@ __global__ __launch_bounds__(256) void kda_bwd_prod_kernel(BwdProdParams p) {
   constexpr int LD = D + PE;
   constexpr int CT = D / 16, RT = C / 16;
   __shared__ __attribute__((aligned(16))) E sU[C * LD];  // U rows t, k = v
+  // column tiles of S and dS' (16 rows each), two buffers (used when C = 64)
+  constexpr int STG = C == 64 ? 16 * D : 1;
+  __shared__ __attribute__((aligned(16))) E sSt0[STG];
+  __shared__ __attribute__((aligned(16))) E sDt0[STG];
+  __shared__ __attribute__((aligned(16))) E sSt1[STG];
+  __shared__ __attribute__((aligned(16))) E sDt1[STG];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g4 = lane >> 4;
@@ -364,10 +370,9 @@ __global__ __launch_bounds__(256) void kda_bwd_prod_kernel(BwdProdParams p) {
   load_do(fdo, 16 * Rt + r);
   fdu.load(gdU + (size_t)(16 * Rt + r) * D, g4);
   fu.load(sU + (16 * Rt + r) * LD, g4);
-  for (int Ct = sub; Ct < CT; Ct += WPR) {
-    RowFrag<E, D> fs, fds;
-    fs.load(ckS + (size_t)(16 * Ct + r) * D, g4);
-    fds.load(ckdS + (size_t)(16 * Ct + r) * D, g4);
+  // the products of column tile Ct, from this lane's fragments fs, fds of rows
+  // 16 Ct + r of S and dS'
+  auto col_tile = [&](int Ct, const RowFrag<E, D>& fs, const RowFrag<E, D>& fds) {
     // tiles formed transposed, (c, t): lane (r, g4) holds columns 16 Ct + 4 g4 + e
     // of row t = 16 Rt + r, stored as 4 contiguous elements
     f32x4 aq = {0.f, 0.f, 0.f, 0.f}, aw = aq, ak = aq;
@@ -385,6 +390,49 @@ __global__ __launch_bounds__(256) void kda_bwd_prod_kernel(BwdProdParams p) {
       float tot = sum + __shfl_xor(sum, 16, 64);
       tot += __shfl_xor(tot, 32, 64);
       if (g4 == 0) p.dLC[(size_t)rec * D + 16 * Ct + r] = tot;
+    }
+  };
+  if constexpr (WPR == 1) {
+    // Every wave sweeps every column tile at the same time: the 16 rows of S and dS'
+    // of tile Ct are copied once into LDS (asynchronous global-to-LDS loads, one
+    // 16-byte piece per thread and matrix, swizzled so the fragment reads spread
+    // over the banks), the copy of tile Ct + 1 running while tile Ct computes.
+    using SW = Swz<E, D>;
+    constexpr int NCH = 16 * D * (int)sizeof(E) / 16;  // pieces per matrix tile
+    static_assert(NCH <= 256, "one piece per thread and matrix");
+    auto stage = [&](int Ct, E* dstS, E* dstD) {
+      if (tid < NCH) {
+        constexpr int RC = SW::RC;
+        const int row = tid / RC, pos = tid % RC;
+        const size_t src = (size_t)(16 * Ct + row) * D + (size_t)((pos ^ (row & (RC - 1))) * SW::EPC);
+        __builtin_amdgcn_global_load_lds((const glb_void_t*)(ckS + src), (lds_void_t*)(dstS + 64 * wave * SW::EPC),
+                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const glb_void_t*)(ckdS + src), (lds_void_t*)(dstD + 64 * wave * SW::EPC),
+                                         16, 0, 0);
+      }
+    };
+    // two buffers at fixed offsets (the compiler keeps the copies in flight apart
+    // from the reads of the other buffer)
+    auto tile = [&](int Ct, E* curS, E* curD, E* nxtS, E* nxtD) {
+      __builtin_amdgcn_s_waitcnt(0);  // this thread's pieces of tile Ct (and older stores)
+      __syncthreads();                // tile Ct is in LDS; every read of the other buffer is done
+      if (Ct + 1 < CT) stage(Ct + 1, nxtS, nxtD);
+      RowFrag<E, D> fs, fds;
+      load_swz<D>(fs, curS, r, g4);
+      load_swz<D>(fds, curD, r, g4);
+      col_tile(Ct, fs, fds);
+    };
+    stage(0, sSt0, sDt0);
+    for (int Ct = 0; Ct < CT; Ct += 2) {
+      tile(Ct, sSt0, sDt0, sSt1, sDt1);
+      if (Ct + 1 < CT) tile(Ct + 1, sSt1, sDt1, sSt0, sDt0);
+    }
+  } else {
+    for (int Ct = sub; Ct < CT; Ct += WPR) {
+      RowFrag<E, D> fs, fds;
+      fs.load(ckS + (size_t)(16 * Ct + r) * D, g4);
+      fds.load(ckdS + (size_t)(16 * Ct + r) * D, g4);
+      col_tile(Ct, fs, fds);
     }
   }
   for (int Jt = sub; Jt < RT; Jt += WPR) {
