@@ -663,16 +663,21 @@ __global__ __launch_bounds__(512) void kda_bwd_t16_kernel(BwdTParams p) {
   constexpr int CT = D / 16, RT = C / 16;
   using SD = Swz<__bf16, D>;
   using SC = Swz<__bf16, C>;
-  __shared__ __attribute__((aligned(16))) __bf16 iW[C * D];
-  __shared__ __attribute__((aligned(16))) __bf16 iWt[D * C];
-  __shared__ __attribute__((aligned(16))) __bf16 iU[C * D];
-  __shared__ __attribute__((aligned(16))) __bf16 iUt[D * C];
-  __shared__ __attribute__((aligned(16))) __bf16 iBk[C * D];
-  __shared__ __attribute__((aligned(16))) __bf16 iBv[C * D];
-  __shared__ __attribute__((aligned(16))) __bf16 iT[C * C];
+  // One region holds the images of dW, dU, Bk, Bv for the dT products, then (after
+  // them) Y^T and the transposed images of dW and dU; T^T and dT sit beside it.
+  // T itself is read as transposed fragments of T^T.  80 KB at C = 64, D = 128,
+  // so two workgroups share a compute unit.
+  constexpr int REG = 4 * C * D > C * C + 2 * C * D ? 4 * C * D : C * C + 2 * C * D;
+  __shared__ __attribute__((aligned(16))) __bf16 reg[REG];
   __shared__ __attribute__((aligned(16))) __bf16 iTt[C * C];
   __shared__ __attribute__((aligned(16))) __bf16 idT[C * C];
-  __shared__ __attribute__((aligned(16))) __bf16 iYt[C * C];
+  __bf16* iW = reg;
+  __bf16* iU = reg + C * D;
+  __bf16* iBk = reg + 2 * C * D;
+  __bf16* iBv = reg + 3 * C * D;
+  __bf16* iYt = reg;  // after the dT products
+  __bf16* iWt = reg + C * C;
+  __bf16* iUt = reg + C * C + D * C;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g4 = lane >> 4;
@@ -691,28 +696,18 @@ __global__ __launch_bounds__(512) void kda_bwd_t16_kernel(BwdTParams p) {
     const int t = it / (D / 4), c4 = 4 * (it % (D / 4));
     const bf16x4 w = *reinterpret_cast<const bf16x4*>(gdW + (size_t)t * D + c4);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const __bf16 x = w[e];
-      iW[SD::at(t, c4 + e)] = x;
-      iWt[SC::at(c4 + e, t)] = x;
-    }
+    for (int e = 0; e < 4; ++e) iW[SD::at(t, c4 + e)] = w[e];
   }
   for (int it = tid; it < C * D / 8; it += NT) {
     const int t = it / (D / 8), c8 = 8 * (it % (D / 8));
     const bf16x8 u = *reinterpret_cast<const bf16x8*>(gdU + (size_t)t * D + c8);
     *reinterpret_cast<bf16x8*>(&iU[SD::at(t, c8)]) = u;  // 8 elements = one 16-byte chunk
-#pragma unroll
-    for (int e = 0; e < 8; ++e) iUt[SC::at(c8 + e, t)] = u[e];
   }
   for (int it = tid; it < C * C / 4; it += NT) {
     const int a = it / (C / 4), b4 = 4 * (it % (C / 4));
     const bf16x4 x = *reinterpret_cast<const bf16x4*>(gTt + (size_t)a * C + b4);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const __bf16 y = x[e];
-      iTt[SC::at(a, b4 + e)] = y;  // T^T[a][b]
-      iT[SC::at(b4 + e, a)] = y;   // T[b][a]
-    }
+    for (int e = 0; e < 4; ++e) iTt[SC::at(a, b4 + e)] = x[e];  // T^T[a][b]
   }
   // Bk = beta k exp(Gamma), Bv = beta v; rows past the end of the sequence read
   // the last row and take beta = 0
@@ -757,17 +752,52 @@ __global__ __launch_bounds__(512) void kda_bwd_t16_kernel(BwdTParams p) {
       idT[SC::at(i, j)] = (__bf16)(j <= i ? acc[e] : 0.f);
     }
   }
-  __syncthreads();
-  // ---- Y^T (j, m) = sum_l T[j][l] dT[m][l]
+  __syncthreads();  // the images of dW, dU, Bk, Bv are dead
+  // dW and dU again (from L2), for their transposed images: loaded into registers
+  // before the Y^T products, written after them
+  constexpr int NWL = (C * D / 4 + NT - 1) / NT, NUL = (C * D / 8 + NT - 1) / NT;
+  bf16x4 wl[NWL];
+  bf16x8 ul[NUL];
+#pragma unroll
+  for (int k = 0; k < NWL; ++k) {
+    const int it = tid + NT * k;
+    if (it < C * D / 4)
+      wl[k] = *reinterpret_cast<const bf16x4*>(gdW + (size_t)(it / (D / 4)) * D + 4 * (it % (D / 4)));
+  }
+#pragma unroll
+  for (int k = 0; k < NUL; ++k) {
+    const int it = tid + NT * k;
+    if (it < C * D / 8)
+      ul[k] = *reinterpret_cast<const bf16x8*>(gdU + (size_t)(it / (D / 8)) * D + 8 * (it % (D / 8)));
+  }
+  // ---- Y^T (j, m) = sum_l T[j][l] dT[m][l], T rows read down the columns of T^T
   for (int tile = wave; tile < RT * RT; tile += NW) {
     const int Jt = tile / RT, Mt = tile % RT;
     RowFrag<__bf16, C> fa, fb;
-    load_swz<C>(fa, iT, 16 * Jt + r, g4);
+    load_swz_t<C, C>(fa, iTt, 16 * Jt + r, g4);
     load_swz<C>(fb, idT, 16 * Mt + r, g4);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     mma<C>(acc, fa, fb);
 #pragma unroll
     for (int e = 0; e < 4; ++e) iYt[SC::at(16 * Jt + 4 * g4 + e, 16 * Mt + r)] = (__bf16)acc[e];
+  }
+#pragma unroll
+  for (int k = 0; k < NWL; ++k) {
+    const int it = tid + NT * k;
+    if (it < C * D / 4) {
+      const int t = it / (D / 4), c4 = 4 * (it % (D / 4));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) iWt[SC::at(c4 + e, t)] = wl[k][e];
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < NUL; ++k) {
+    const int it = tid + NT * k;
+    if (it < C * D / 8) {
+      const int t = it / (D / 8), c8 = 8 * (it % (D / 8));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) iUt[SC::at(c8 + e, t)] = ul[k][e];
+    }
   }
   __syncthreads();
   // ---- dA (i, j) = -sum_m T^T[i][m] Y^T[j][m]  (j < i)
