@@ -236,9 +236,13 @@ kda_status kda_decode_step(const kda_decode_args* a, void* stream);
  * forward is recomputed (the arguments' o, S_T and conv_state_out are written
  * again with the same values), then walked back chunk by chunk: the reverse of
  * the chunked form, with the pairs' relative decays exp(Gamma_i - Gamma_j)
- * evaluated per pair.  Supported: the plain mixer over B equal-length sequences
+ * factored per 16-token block (chunks whose decay spans are too wide for that are
+ * evaluated per pair).  Supported: the plain mixer over B equal-length sequences
  * (no packed sequences, no optional stages); fp32 I/O up to D = 64, bf16 I/O up
- * to D = 128.  All gradients are float32. */
+ * to D = 128.  All gradients are float32; with bf16 I/O the intermediate
+ * gradients pass between the kernels in bf16 (relative error of the returned
+ * gradients about 4e-3 against an exact computation, at T = 4096, H = 96,
+ * D = 128). */
 typedef struct kda_backward_args {
   kda_prefill_args fwd; /* the forward call; its rules apply */
   const void* dO;       /* device [B][T][H][D] io dtype: gradient of o */
