@@ -874,6 +874,9 @@ __global__ __launch_bounds__(4 * D, D / 32 > 1 ? D / 32 : 1) void kda_bwd_pair_m
   __shared__ float sGC[D];
   __shared__ float sB[C];
   __shared__ int sfat[D / 16];  // per wave: a block span of its channels is too wide
+  constexpr int NSG = NTH / D;  // token segments of the dg running sum
+  constexpr int SL = C / NSG;   // tokens per segment
+  __shared__ float sseg[NSG * D];  // segment totals of dGamma
   float* sdA = sreg;
   float* sdP = sreg + C * LA;
 
@@ -1054,20 +1057,30 @@ __global__ __launch_bounds__(4 * D, D / 32 > 1 ? D / 32 : 1) void kda_bwd_pair_m
   colsum += __shfl_xor(colsum, 32, 64);
   if (g4 == 0) sGC[c] = colsum + p.dLC[(size_t)rec * D + c] * __builtin_amdgcn_exp2f(gC);
   __syncthreads();
-  // dg: reverse running sum over the chunk, one thread per channel
-  if (tid < D) {
-    float acc = sGC[tid];
-    for (int t = C - 1; t >= 0; --t) {
-      acc += sdG[t * LD + tid];
-      if (t < nval) p.dg[row_of(t) + tid] = acc;
-    }
-  }
   // dbeta: sum over the waves, one thread per token
   if (tid < nval) {
     float acc = 0.f;
 #pragma unroll
     for (int w = 0; w < D / 16; ++w) acc += sdbw[w * C + tid];
     p.dbeta_part[((size_t)b * p.T + (size_t)n * C + tid) * p.H + h] = acc;
+  }
+  // dg: reverse running sum over the chunk.  Thread (channel cc, segment sg) takes
+  // the SL tokens of segment sg: the segment totals go through LDS, then each
+  // thread walks its segment backwards from the sum of the later segments.
+  {
+    const int cc = tid % D, sg = tid / D;
+    float tot = 0.f;
+#pragma unroll
+    for (int t = SL * sg; t < SL * (sg + 1); ++t) tot += sdG[t * LD + cc];
+    sseg[sg * D + cc] = tot;
+    __syncthreads();
+    float acc = sGC[cc];
+    for (int s2 = NSG - 1; s2 > sg; --s2) acc += sseg[s2 * D + cc];
+#pragma unroll
+    for (int t = SL * (sg + 1) - 1; t >= SL * sg; --t) {
+      acc += sdG[t * LD + cc];
+      if (t < nval) p.dg[row_of(t) + cc] = acc;
+    }
   }
 }
 
