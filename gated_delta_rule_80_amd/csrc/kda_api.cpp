@@ -242,8 +242,10 @@ struct BwdFwdOut {
   void* ckS;
 };
 
+// fuse_tail: the state walk (T > 0) also writes the conv-state hand-over, and
+// the hand-over stage does nothing then.
 static kda_status run_stage(const kda_prefill_args* a, void* ws, int stage, hipStream_t st,
-                            const BwdFwdOut* bo = nullptr) {
+                            const BwdFwdOut* bo = nullptr, bool fuse_tail = false) {
   const bool fp32 = a->io == KDA_FP32;
   PrefillSizes sz;
   prefill_sizes(a, sz);
@@ -304,6 +306,11 @@ static kda_status run_stage(const kda_prefill_args* a, void* ws, int stage, hipS
       p.o_norm_w = a->o_norm_w;
       p.o_norm_eps = a->o_norm_eps;
       p.ckpt = bo != nullptr ? bo->ckS : nullptr;
+      if (fuse_tail && a->conv_k > 0 && a->conv_state_out != nullptr) {
+        p.tail_x[0] = a->q; p.tail_x[1] = a->k; p.tail_x[2] = a->v;
+        p.tail_in = a->conv_state_in;
+        p.tail_out = a->conv_state_out;
+      }
       return hip_status(kda::launch_state(p, a->D, a->chunk, fp32, cfg.vb, cfg.threads, cfg.fused,
                                           st));
     }
@@ -319,7 +326,7 @@ static kda_status run_stage(const kda_prefill_args* a, void* ws, int stage, hipS
       return hip_status(kda::launch_out_stage(q, a->D, fp32, st));
     }
     case KDA_STAGE_CONV_TAIL: {
-      if (a->conv_k == 0 || a->conv_state_out == nullptr) return KDA_OK;
+      if (a->conv_k == 0 || a->conv_state_out == nullptr || (fuse_tail && a->T > 0)) return KDA_OK;
       kda::TailParams p{};
       p.x[0] = a->q; p.x[1] = a->k; p.x[2] = a->v;
       p.conv_state_in = a->conv_state_in;
@@ -345,7 +352,7 @@ kda_status kda_prefill(const kda_prefill_args* a, void* ws, size_t ws_bytes, voi
   if (kda_status e = check_workspace(a, ws, ws_bytes); e != KDA_OK) return e;
   hipStream_t st = static_cast<hipStream_t>(stream);
   for (int stage = KDA_STAGE_PREP; stage <= KDA_STAGE_OUTPUT; ++stage)
-    if (kda_status e = run_stage(a, ws, stage, st); e != KDA_OK) return e;
+    if (kda_status e = run_stage(a, ws, stage, st, nullptr, true); e != KDA_OK) return e;
   return KDA_OK;
 }
 

@@ -119,6 +119,12 @@ struct StateParams {
   SeqTables seqs;         // packed sequences (then B = n_seqs, NT = chunk slots per head)
   void* ckpt;             // backward mode: the state at each chunk start in the element type,
                           // S^T then S, [rec][2][D][D], or NULL
+  // conv-state hand-over by the workgroups of value block 0, or tail_out NULL: the
+  // raw q, k, v [B][T][H*D], the previous conv state (or NULL) and the new one,
+  // [B][3][3][H*D].  The caller launches the walk after every read of tail_in.
+  const void* tail_x[3];
+  const void* tail_in;
+  void* tail_out;
 };
 
 // The output stage on its own, in place on o: RMSNorm with gain and/or the

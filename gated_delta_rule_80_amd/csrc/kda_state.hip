@@ -121,6 +121,33 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void kda_chunk_state_kernel(
     nch = c1 - c0;
     rec0 = (size_t)h * p.NT + c0;
   }
+  // conv-state hand-over of (b, h): new state row tau = raw input at position
+  // Tq - 3 + tau, from the previous state where that position is < 0.  A thread
+  // reads the 3 values of its (tensor, channel) before writing them, so the new
+  // state may overwrite the previous one.
+  if (p.tail_out != nullptr && vblk == 0) {
+    const size_t HD = (size_t)p.H * D;
+    for (int it = tid; it < 3 * D; it += NT) {
+      const int i = it / D;
+      const size_t col = (size_t)h * D + it % D;
+      const IO* x = static_cast<const IO*>(i == 0 ? p.tail_x[0] : (i == 1 ? p.tail_x[1] : p.tail_x[2]));
+      const IO* in = static_cast<const IO*>(p.tail_in);
+      IO* out = static_cast<IO*>(p.tail_out) + ((size_t)b * 3 + i) * 3 * HD + col;
+      IO val[3];
+#pragma unroll
+      for (int tau = 0; tau < 3; ++tau) {
+        const int t = Tq - 3 + tau;
+        if (t >= 0)
+          val[tau] = x[((size_t)tok0 + t) * HD + col];
+        else if (in != nullptr)
+          val[tau] = in[((size_t)b * 3 + i) * 3 * HD + (size_t)(3 + t) * HD + col];
+        else
+          val[tau] = from_f32<IO>(0.f);
+      }
+#pragma unroll
+      for (int tau = 0; tau < 3; ++tau) out[(size_t)tau * HD] = val[tau];
+    }
+  }
 
   // this wave's tiles
   const int R = wave % RT;                      // t-tile of every (t, v) unit of this wave
