@@ -25,6 +25,7 @@ KDA_FLAG_L2NORM_QK = 1
 KDA_FLAG_BETA_LOGITS = 2
 ABI_VERSION = 2
 KDA_STAGE_PREP, KDA_STAGE_STATE, KDA_STAGE_CONV_TAIL, KDA_STAGE_OUTPUT = 0, 1, 2, 3
+KDA_STAGE_STATE_TAIL = 4  # stages 1 and 2 in one launch, as kda_prefill runs them
 NUM_STAGES = 4
 STATUS_NAMES = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE",
                 4: "KDA_ERR_ALIGN", 5: "KDA_ERR_ALIAS", 6: "KDA_ERR_UNSUPPORTED",

@@ -342,8 +342,10 @@ static kda_status run_stage(const kda_prefill_args* a, void* ws, int stage, hipS
 kda_status kda_prefill_stage(const kda_prefill_args* a, void* ws, size_t ws_bytes, int stage,
                              void* stream) {
   if (kda_status e = kda_validate_prefill(a); e != KDA_OK) return e;
-  if (stage < KDA_STAGE_PREP || stage > KDA_STAGE_OUTPUT) return KDA_ERR_VALUE;
+  if (stage < KDA_STAGE_PREP || stage > KDA_STAGE_STATE_TAIL) return KDA_ERR_VALUE;
   if (kda_status e = check_workspace(a, ws, ws_bytes); e != KDA_OK) return e;
+  if (stage == KDA_STAGE_STATE_TAIL)
+    return run_stage(a, ws, KDA_STAGE_STATE, static_cast<hipStream_t>(stream), nullptr, true);
   return run_stage(a, ws, stage, static_cast<hipStream_t>(stream));
 }
 
@@ -351,6 +353,8 @@ kda_status kda_prefill(const kda_prefill_args* a, void* ws, size_t ws_bytes, voi
   if (kda_status e = kda_validate_prefill(a); e != KDA_OK) return e;
   if (kda_status e = check_workspace(a, ws, ws_bytes); e != KDA_OK) return e;
   hipStream_t st = static_cast<hipStream_t>(stream);
+  // stages 0, 4, 3 (stage 4 is the walk with the hand-over; the hand-over stage is
+  // then empty, and so is the state stage when T = 0 leaves the hand-over to it)
   for (int stage = KDA_STAGE_PREP; stage <= KDA_STAGE_OUTPUT; ++stage)
     if (kda_status e = run_stage(a, ws, stage, st, nullptr, true); e != KDA_OK) return e;
   return KDA_OK;

@@ -166,14 +166,16 @@ kda_status kda_prefill(const kda_prefill_args* a, void* ws, size_t ws_bytes, voi
  *   2 = conv-state hand-over (writes conv_state_out),
  *   3 = the output norm and gate as a separate in-place pass over o, when stage 1
  *       did not apply them (nothing otherwise).
- * Running 0, 1, 2, 3 in order on one stream gives exactly kda_prefill's results
- * (T > 0); kda_prefill itself has stage 1's kernel write the conv-state hand-over
- * too (its first value block per head, once the preparation has read the previous
- * state), so it enqueues no separate stage 2. */
+ *   4 = stages 1 and 2 in one launch: the state walk's first value block per head
+ *       also writes the conv-state hand-over (the preparation has read the
+ *       previous state by then, so the new one may overwrite it).
+ * Running 0, 1, 2, 3 or 0, 4, 3 in order on one stream gives exactly kda_prefill's
+ * results (T > 0); kda_prefill itself enqueues 0, 4, 3. */
 #define KDA_STAGE_PREP 0
 #define KDA_STAGE_STATE 1
 #define KDA_STAGE_CONV_TAIL 2
 #define KDA_STAGE_OUTPUT 3
+#define KDA_STAGE_STATE_TAIL 4
 kda_status kda_prefill_stage(const kda_prefill_args* a, void* ws, size_t ws_bytes, int stage,
                              void* stream);
 

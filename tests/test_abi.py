@@ -168,7 +168,7 @@ def test_prefill_workspace_errors(lib):
     # workspace overlapping an output
     assert lib.kda_prefill(ctypes.byref(a), ctypes.c_void_p(a.o), need, None) == ALIAS
     # invalid stage number
-    assert lib.kda_prefill_stage(ctypes.byref(a), ctypes.c_void_p(0x100000000000), need, 4,
+    assert lib.kda_prefill_stage(ctypes.byref(a), ctypes.c_void_p(0x100000000000), need, 5,
                                  None) == VALUE
     assert lib.kda_prefill_stage(ctypes.byref(a), ctypes.c_void_p(0x100000000000), need, -1,
                                  None) == VALUE

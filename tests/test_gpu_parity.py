@@ -130,6 +130,15 @@ def test_stages_compose_to_prefill():
         kda.kda_prefill_stage(a, ws, stage)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(S1, S2) and torch.equal(t1, t2)
+    # the walk with the hand-over folded in, in place on the previous conv state
+    o3, S3 = torch.empty_like(o1), torch.empty_like(S1)
+    t3 = inp["conv_state"].clone()
+    a3 = kda.prefill_args(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["conv_w"],
+                          t3, inp["S0"], o3, S3, t3, chunk=64)
+    for stage in (0, kda.KDA_STAGE_STATE_TAIL, 3):
+        kda.kda_prefill_stage(a3, ws, stage)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o3) and torch.equal(S1, S3) and torch.equal(t1, t3)
 
 
 @pytest.mark.parametrize("t0", [1, 3, 64, 100])
