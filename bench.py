@@ -213,11 +213,11 @@ def _warm(_):
 def time_prefill(kda, torch, a, ws, stream, steps, warmup):
     """Mean ms per kda_prefill and per stage, from HIP events on the launch stream.
 
-    The step runs the stages kda_prefill enqueues (STAGE_IDS) back to back.  The
-    throughput pass brackets all `steps` steps with one pair of events; a second
-    pass of the same steps records an event after every stage for the per-kernel
-    durations (an event between two kernels costs the step several microseconds
-    of drain, so those events stay out of the throughput pass)."""
+    The throughput pass brackets `steps` kda_prefill calls with one pair of
+    events; a second pass of the same number of steps runs the stages kda_prefill
+    enqueues (STAGE_IDS) one call each, with an event after every stage, for the
+    per-kernel durations (an event between two kernels costs the step several
+    microseconds of drain, so those events stay out of the throughput pass)."""
     n = len(STAGE_NAMES)
 
     def step(ev=None):
@@ -235,7 +235,7 @@ def time_prefill(kda, torch, a, ws, stream, steps, warmup):
     t_end = torch.cuda.Event(enable_timing=True)
     t_start.record(stream)
     for i in range(steps):
-        step()
+        kda.kda_prefill_raw(a, ws, stream)
     t_end.record(stream)
     torch.cuda.synchronize()
     ms = t_start.elapsed_time(t_end) / steps
@@ -385,7 +385,7 @@ def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="prefill-4k")
     ap.add_argument("--decode-workload", default="decode-b256")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing (0 = skip)")
