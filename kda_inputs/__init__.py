@@ -173,3 +173,20 @@ def to_numpy(t):
     if t is None:
         return None
     return t.detach().to("cpu", torch.float64).numpy()
+
+
+def to_storage(t, head_major: bool = False):
+    """NumPy copy of a tensor as stored for the oracle's host-process pool: bf16 as
+    its raw 16-bit patterns (uint16), float32 as is; a [B, T, H, ...] tensor moved
+    to [B, H, T, ...] when head_major, so one (sequence, head) pair is contiguous.
+    None stays None."""
+    import numpy as np
+
+    if t is None:
+        return None
+    if head_major:
+        t = t.transpose(1, 2)
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()

@@ -65,3 +65,4 @@ def oracle_heads(inp: dict, heads):
 
 def make(w: Workload, seed=0):
     return make_inputs(w, seed=seed, device="cpu")
+

@@ -1,103 +1,114 @@
 """Parity at the workloads' full sizes, in the launch configuration the benchmark
-times (same entry points, same shapes, hence the same kernels and grids).
+times (same entry points, same shapes, hence the same kernels and grids), over
+EVERY (sequence, head) pair.
 
-The GPU runs the whole workload; the fp64 oracle then runs whole sequences of a
-few sampled (sequence, head) pairs -- every (b, h) pair is independent of the
-others, so a sampled pair is an exact check of that pair's outputs.  Everything
-else is checked through properties that hold at any size: finite outputs, the
-conv-state hand-over equal to the raw inputs it copies, and untouched pairs of
-the decode state staying finite.
+The GPU runs the whole workload; the fp64 oracle then runs every pair's whole
+sequence in a pool of host processes (pairs are independent: each has its own
+state, conv filters and channels), and each pair is compared on its own.  The
+conv-state hand-over is compared whole and exactly.
 
-Tolerance: relative L2 2e-2 for bf16 inputs (per sampled pair, separately for
-o and S_T)."""
+Tolerance: relative L2 2e-2 for bf16 inputs per (sequence, head) pair,
+separately for o and S_T (the decode state S); the worst pair is printed.  The
+worst 64-token block of o per pair must stay within 5e-2, so an error confined
+to a few tokens cannot hide under a whole sequence's norm."""
+import shutil
+
 import numpy as np
 import pytest
 import torch
 
 import gated_delta_rule_80_amd as kda
-from kda_inputs import WORKLOADS, make_inputs, to_numpy
-from kda_testutil import TOL, oracle_heads, rel_l2
-from oracle import kda_reference_backward, kda_reference_decode_step
+from kda_inputs import WORKLOADS, make_inputs, to_storage
+from kda_testutil import TOL
+from oracle.pool import (backward_pair, decode_seq, prefill_pair, run, save_array, save_meta,
+                         scratch_dir)
 
 pytestmark = pytest.mark.gpu
 
-# sampled (b, h) pairs per workload: first / middle / last heads, every sequence
-# of the batched case touched at least once
-SAMPLES = {
-    "prefill-4k": [(0, 0), (0, 57), (0, 95)],
-    "prefill-b4-8k-s0": [(0, 3), (1, 50), (3, 95)],
-    "prefill-64k": [(0, 41)],
-}
+BLOCK_TOL = 5e-2
+FULL = ["prefill-4k", "prefill-b4-8k-s0", "prefill-64k"]
 
 
-@pytest.mark.parametrize("name", list(SAMPLES))
-def test_full_size_prefill_sampled_pairs(name):
+def summarize(label, res, tol):
+    """res: (b, h, e_o, e_S, e_block, block) per pair."""
+    wo = max(res, key=lambda x: x[2])
+    wS = max(res, key=lambda x: x[3])
+    wb = max(res, key=lambda x: x[4])
+    print(f"{label}: {len(res)} pairs; worst o {wo[2]:.2e} at (b={wo[0]}, h={wo[1]}), "
+          f"worst S_T {wS[3]:.2e} at (b={wS[0]}, h={wS[1]}), worst 64-token block "
+          f"{wb[4]:.2e} at (b={wb[0]}, h={wb[1]}, block {wb[5]})", flush=True)
+    bad = [x for x in res if not (x[2] <= tol and x[3] <= tol and x[4] <= BLOCK_TOL)]
+    assert not bad, bad[:8]
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_prefill_every_pair(name):
     w = WORKLOADS[name]
     print(f"full-size prefill {name}: B={w.B} T={w.T} H={w.H} D={w.D}", flush=True)
     inp = make_inputs(w, seed=0, device="cuda")
-    o, S, _ = kda.kda_prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["conv_w"],
-                              inp["conv_state"], inp["S0"], chunk=w.chunk)
+    o, S, cs = kda.kda_prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["conv_w"],
+                               inp["conv_state"], inp["S0"], chunk=w.chunk)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(S).all())
-    tol = TOL[w.io]
-    pairs = SAMPLES[name]
-    for (b, h), (ro, rS) in zip(pairs, oracle_heads(inp, pairs)):
-        go = o[b, :, h].float().cpu().numpy()
-        gS = S[b, h].cpu().numpy()
-        eo, eS = rel_l2(go, ro), rel_l2(gS, rS)
-        print(f"  (b={b}, h={h}): rel_l2 o={eo:.2e} S_T={eS:.2e}", flush=True)
-        assert eo <= tol, (b, h, eo)
-        assert eS <= tol, (b, h, eS)
-
-
-def test_full_size_conv_state_handover():
-    """The conv state handed over at the end of the 4k prefill is exactly the last
-    three raw inputs of every channel (whole tensor, not sampled)."""
-    w = WORKLOADS["prefill-4k"]
-    inp = make_inputs(w, seed=0, device="cuda")
-    _, _, cs = kda.kda_prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
-                               inp["conv_w"], inp["conv_state"], inp["S0"], chunk=w.chunk)
-    torch.cuda.synchronize()
+    # the conv hand-over: the last three raw inputs of every channel, whole tensor
     HD = w.H * w.D
-    for x, name in enumerate(("q", "k", "v")):
-        want = inp[name][:, w.T - 3:].reshape(w.B, 3, HD)
-        assert torch.equal(cs[:, x], want), name
+    for x, t in enumerate(("q", "k", "v")):
+        assert torch.equal(cs[:, x], inp[t][:, w.T - 3:].reshape(w.B, 3, HD)), t
+    d = scratch_dir(6 * o.numel() * o.element_size())
+    try:
+        save_meta(d, w.io, w.D)
+        for t in ("q", "k", "v", "g", "beta"):
+            save_array(d, t, to_storage(inp[t], head_major=True))
+        save_array(d, "conv_w", to_storage(inp["conv_w"]))
+        save_array(d, "conv_state", to_storage(inp["conv_state"]))
+        save_array(d, "S0", to_storage(inp["S0"]))
+        save_array(d, "o", to_storage(o, head_major=True))
+        save_array(d, "S_T", to_storage(S))
+        del inp, o, S, cs
+        torch.cuda.empty_cache()
+        res = run(prefill_pair, d, [(b, h) for b in range(w.B) for h in range(w.H)], name)
+    finally:
+        shutil.rmtree(d, ignore_errors=True)
+    summarize(name, res, TOL[w.io])
 
 
-def test_full_size_decode_sampled_pairs():
+@pytest.mark.timeout(600)
+def test_full_size_decode_every_pair():
     w = WORKLOADS["decode-b256"]
     print(f"full-size decode: B={w.B} H={w.H} D={w.D}", flush=True)
     inp = make_inputs(w, seed=1, device="cuda")
-    pairs = [(0, 0), (17, 40), (128, 95), (255, 63)]
-    before = {p: to_numpy(inp["S0"][p[0], p[1]]) for p in pairs}
-    S = inp["S0"]
-    cs = inp["conv_state"]
-    cs0 = cs.clone()
+    S0 = inp["S0"].clone()
+    cs0 = inp["conv_state"].clone()
+    S, cs = inp["S0"], inp["conv_state"]
     o = kda.kda_decode_step(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], S,
                             inp["conv_w"], cs)
     torch.cuda.synchronize()
     assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(S).all())
-    tol = TOL[w.io]
-    D = w.D
-    for b, h in pairs:
-        ch = slice(h * D, (h + 1) * D)
-        one = lambda t: to_numpy(t[b:b + 1, h:h + 1])
-        ro, rS, rcs = kda_reference_decode_step(
-            one(inp["q"]), one(inp["k"]), one(inp["v"]), one(inp["g"]),
-            to_numpy(inp["beta"][b:b + 1, h:h + 1]), before[(b, h)][None, None],
-            conv_w=to_numpy(inp["conv_w"][:, ch]), conv_state=to_numpy(cs0[b:b + 1, :, :, ch]))
-        eo = rel_l2(o[b, h].float().cpu().numpy(), ro[0, 0])
-        eS = rel_l2(S[b, h].cpu().numpy(), rS[0, 0])
-        print(f"  (b={b}, h={h}): rel_l2 o={eo:.2e} S={eS:.2e}", flush=True)
-        assert eo <= tol and eS <= tol, (b, h, eo, eS)
-        np.testing.assert_array_equal(cs[b:b + 1, :, :, ch].float().cpu().numpy(), rcs)
+    d = scratch_dir(3 * S.numel() * 4)
+    try:
+        save_meta(d, w.io, w.D)
+        for t in ("q", "k", "v", "g", "beta", "conv_w"):
+            save_array(d, t, to_storage(inp[t]))
+        save_array(d, "S0", to_storage(S0))
+        save_array(d, "conv_state", to_storage(cs0))
+        save_array(d, "o", to_storage(o))
+        save_array(d, "S", to_storage(S))
+        save_array(d, "conv_state_out", to_storage(cs))
+        del inp, S0, cs0, S, cs, o
+        torch.cuda.empty_cache()
+        res = [x for part in run(decode_seq, d, [(b,) for b in range(w.B)], "decode") for x in part]
+    finally:
+        shutil.rmtree(d, ignore_errors=True)
+    assert all(x[4] for x in res), "conv state after the step differs from the oracle's"
+    summarize("decode-b256", [(b, h, eo, eS, 0.0, -1) for b, h, eo, eS, _ in res], TOL[w.io])
 
 
-def test_full_size_backward_sampled_head():
-    """The backward at the 4k workload's full size (every head and chunk on the
-    GPU), checked on one sampled head against the oracle's reverse-mode gradients
-    of that head (heads are independent; the conv filter gradient of the head's
-    channels comes from that head alone)."""
+@pytest.mark.timeout(600)
+def test_full_size_backward_every_head():
+    """The backward at the 4k workload's full size, every head against the oracle's
+    reverse-mode gradients of that head (heads are independent; the conv filter
+    gradient of a head's channels comes from that head alone)."""
     w = WORKLOADS["prefill-4k"]
     inp = make_inputs(w, seed=0, device="cuda")
     gen = torch.Generator(device="cuda").manual_seed(5)
@@ -108,19 +119,28 @@ def test_full_size_backward_sampled_head():
     torch.cuda.synchronize()
     for n, t in grads.items():
         assert bool(torch.isfinite(t).all()), n
-    b, h = 0, 37
-    D = w.D
-    ch = slice(h * D, (h + 1) * D)
-    one = lambda x: to_numpy(x[b:b + 1, :, h:h + 1])
-    ref = kda_reference_backward(one(inp["q"]), one(inp["k"]), one(inp["v"]), one(inp["g"]),
-                                 to_numpy(inp["beta"][b:b + 1, :, h:h + 1]), one(do),
-                                 conv_w=to_numpy(inp["conv_w"][:, ch]))
+    d = scratch_dir(12 * do.numel() * 4)
+    try:
+        save_meta(d, w.io, w.D)
+        for t in ("q", "k", "v", "g", "beta"):
+            save_array(d, t, to_storage(inp[t], head_major=True))
+        save_array(d, "do", to_storage(do, head_major=True))
+        save_array(d, "conv_w", to_storage(inp["conv_w"]))
+        save_array(d, "conv_state", to_storage(inp["conv_state"]))
+        save_array(d, "S0", to_storage(inp["S0"]))
+        for n in ("dq", "dk", "dv", "dg", "dbeta"):
+            save_array(d, n, to_storage(grads[n], head_major=True))
+        for n in ("dS0", "dconv_w", "dconv_state"):
+            save_array(d, n, to_storage(grads[n]))
+        del inp, do, grads, o, S_T
+        torch.cuda.empty_cache()
+        res = run(backward_pair, d, [(0, h) for h in range(w.H)], "backward")
+    finally:
+        shutil.rmtree(d, ignore_errors=True)
     tol = TOL[w.io]
-    pairs = {"dq": grads["dq"][b:b + 1, :, h:h + 1], "dk": grads["dk"][b:b + 1, :, h:h + 1],
-             "dv": grads["dv"][b:b + 1, :, h:h + 1], "dg": grads["dg"][b:b + 1, :, h:h + 1],
-             "dbeta": grads["dbeta"][b:b + 1, :, h:h + 1], "dS0": grads["dS0"][b:b + 1, h:h + 1],
-             "dconv_w": grads["dconv_w"][:, ch], "dconv_state": grads["dconv_state"][b:b + 1, :, :, ch]}
-    for n, t in pairs.items():
-        e = rel_l2(t.cpu().numpy(), ref[n])
-        print(f"  backward (b={b}, h={h}) {n}: rel_l2 {e:.2e}", flush=True)
-        assert e <= tol, (n, e)
+    names = sorted(res[0][2])
+    for n in names:
+        worst = max(res, key=lambda x: x[2][n])
+        print(f"  backward {n}: worst rel_l2 {worst[2][n]:.2e} at h={worst[1]}", flush=True)
+    bad = [(b, h, n, e) for b, h, errs in res for n, e in errs.items() if not e <= tol]
+    assert not bad, bad[:8]
