@@ -242,15 +242,28 @@ struct BwdFwdOut {
   void* ckS;
 };
 
+// A time slice of B equal-length sequences: chunks c0 .. c0 + cnt - 1 of every
+// sequence, whose records take cap slots per (sequence, head) of a workspace laid
+// out for B * H * cap records.  cap = 0: whole sequences.
+struct Slice {
+  int c0 = 0, cnt = 0, cap = 0;
+};
+
 // fuse_tail: the state walk (T > 0) also writes the conv-state hand-over, and
-// the hand-over stage does nothing then.
+// the hand-over stage does nothing then.  A slice (sl != NULL) prepares or walks
+// only its chunks; its walk starts from S0 when c0 = 0 and from S_T (the previous
+// slice's end state) otherwise.
 static kda_status run_stage(const kda_prefill_args* a, void* ws, int stage, hipStream_t st,
-                            const BwdFwdOut* bo = nullptr, bool fuse_tail = false) {
+                            const BwdFwdOut* bo = nullptr, bool fuse_tail = false,
+                            const Slice* sl = nullptr) {
   const bool fp32 = a->io == KDA_FP32;
   PrefillSizes sz;
   prefill_sizes(a, sz);
-  const int NT = sz.NT;
-  const kda::SeqTables seqs = seq_tables(a, ws);
+  const int NT = sl != nullptr ? sl->cap : sz.NT;
+  const kda::SeqTables seqs = sl != nullptr ? kda::SeqTables{} : seq_tables(a, ws);
+  const kda::WorkspaceLayout wl =
+      sl != nullptr ? kda::workspace_layout((size_t)a->B * a->H * sl->cap, a->chunk, a->D, esize(a->io))
+                    : ws_layout(a);
   switch (stage) {
     case KDA_STAGE_PREP: {
       if (a->T == 0) return KDA_OK;
@@ -268,11 +281,12 @@ static kda_status run_stage(const kda_prefill_args* a, void* ws, int stage, hipS
       p.q = a->q; p.k = a->k; p.v = a->v; p.g = a->g; p.beta = a->beta;
       p.conv_w = a->conv_k > 0 ? a->conv_w : nullptr;
       p.conv_state_in = a->conv_k > 0 ? a->conv_state_in : nullptr;
-      const kda::WorkspaceLayout wl = ws_layout(a);
       p.ws = static_cast<char*>(ws) + wl.records;
       p.fb_count = static_cast<unsigned*>(ws);
       p.fb_list = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + wl.list);
       p.B = a->B; p.T = a->T; p.H = a->H; p.NT = NT;
+      p.c0 = sl != nullptr ? sl->c0 : 0;
+      p.nchunk = sl != nullptr ? sl->cnt : NT;
       p.conv_k = a->conv_k;
       p.l2 = (a->flags & KDA_FLAG_L2NORM_QK) ? 1 : 0;
       p.eps = a->l2_eps;
@@ -298,15 +312,17 @@ static kda_status run_stage(const kda_prefill_args* a, void* ws, int stage, hipS
       const bool gn = a->o_norm_w != nullptr || a->o_gate != nullptr;
       const StateCfg cfg = state_config(sz.NS, a->H, a->D, fp32, gn);
       kda::StateParams p{};
-      p.ws = static_cast<const char*>(ws) + ws_layout(a).records;
-      p.S0 = a->S0; p.S_T = a->S_T; p.o = a->o;
+      p.ws = static_cast<const char*>(ws) + wl.records;
+      p.S0 = sl != nullptr && sl->c0 > 0 ? a->S_T : a->S0;
+      p.S_T = a->S_T; p.o = a->o;
       p.B = sz.NS; p.T = a->T; p.H = a->H; p.NT = NT;
+      p.c0 = sl != nullptr ? sl->c0 : 0;
       p.seqs = seqs;
       p.o_gate = a->o_gate;
       p.o_norm_w = a->o_norm_w;
       p.o_norm_eps = a->o_norm_eps;
       p.ckpt = bo != nullptr ? bo->ckS : nullptr;
-      if (fuse_tail && a->conv_k > 0 && a->conv_state_out != nullptr) {
+      if (fuse_tail && sl == nullptr && a->conv_k > 0 && a->conv_state_out != nullptr) {
         p.tail_x[0] = a->q; p.tail_x[1] = a->k; p.tail_x[2] = a->v;
         p.tail_in = a->conv_state_in;
         p.tail_out = a->conv_state_out;
@@ -326,7 +342,8 @@ static kda_status run_stage(const kda_prefill_args* a, void* ws, int stage, hipS
       return hip_status(kda::launch_out_stage(q, a->D, fp32, st));
     }
     case KDA_STAGE_CONV_TAIL: {
-      if (a->conv_k == 0 || a->conv_state_out == nullptr || (fuse_tail && a->T > 0)) return KDA_OK;
+      if (a->conv_k == 0 || a->conv_state_out == nullptr || (fuse_tail && sl == nullptr && a->T > 0))
+        return KDA_OK;
       kda::TailParams p{};
       p.x[0] = a->q; p.x[1] = a->k; p.x[2] = a->v;
       p.conv_state_in = a->conv_state_in;
@@ -630,9 +647,11 @@ kda_status kda_prefill_backward(const kda_backward_args* a, void* ws, size_t ws_
   }
   char* wsb = static_cast<char*>(ws);
   auto F = [&](size_t off) { return reinterpret_cast<float*>(wsb + off); };
-  // forward in backward mode
+  // forward in backward mode.  The conv-state hand-over comes last, after the
+  // backward front end has read the previous conv state: conv_state_out may be
+  // conv_state_in, and the hand-over overwrites it.
   BwdFwdOut bo{wsb + L.y, F(L.gam), F(L.beta), F(L.tT), wsb + L.ckS};
-  for (int stage = KDA_STAGE_PREP; stage <= KDA_STAGE_OUTPUT; ++stage)
+  for (int stage : {KDA_STAGE_PREP, KDA_STAGE_STATE, KDA_STAGE_OUTPUT})
     if (kda_status e = run_stage(f, ws, stage, st, &bo); e != KDA_OK) return e;
   // backward
   kda::BwdLaunch B{};
@@ -677,7 +696,9 @@ kda_status kda_prefill_backward(const kda_backward_args* a, void* ws, size_t ws_
   B.front.scale = f->scale;
   B.dbeta = a->dbeta;
   B.dconv_w = a->dconv_w;
-  return hip_status(kda::launch_backward(B, f->D, f->chunk, fp32, st));
+  if (kda_status e = hip_status(kda::launch_backward(B, f->D, f->chunk, fp32, st)); e != KDA_OK)
+    return e;
+  return run_stage(f, ws, KDA_STAGE_CONV_TAIL, st, &bo);
 }
 
 }  // extern "C"

@@ -850,8 +850,13 @@ __global__ __launch_bounds__(512) void kda_bwd_t16_kernel(BwdTParams p) {
 //   rK_p += F_pq (dA_pq (K b)_q),   rQ_p += F_pq (dP_pq (K b)_q),
 //   cK_q += F_pq (dA_pq^T (beta K a)_p + dP_pq^T (Q' a)_p),
 // and rK, rQ take the factor a, cK the factor b.  dA and dP are exactly zero above
-// their diagonals, so the pairs j > i (whose a_i b_j exceed 1) add nothing.  a and b
-// lie within exp(+-s/2) for a block span s: chunks with a span above kBwdSpan2
+// their diagonals, so the pairs j > i (whose a_i b_j exceed 1) add nothing.  The
+// pair factor F_pq = exp(m_p - m_q) (p > q) is exp(-(s_p + s_q)/2) or smaller and
+// may underflow where the products it scales do not, so it is applied in two
+// steps, exp(-s/2) of the block whose operand carries exp(+s/2) first (with G_q
+// the cumulative decay before block q):
+//   rK_p, rQ_p:  (. exp(-s_q/2)) exp(m_p - G_{q+1}),   cK_q:  (. exp(-s_p/2)) exp(G_p - m_q),
+// both factors <= 1.  a and b lie within exp(+-s/2) for a block span s: chunks with a span above kBwdSpan2
 // (log2 units) are listed for the exact kernel, which keeps the products' partial
 // sums (up to 16 |dA| 2^(s/2)) far from the float32 range.
 // One workgroup per chunk record; wave w owns channels [16 w, 16 w + 16).  Lane
@@ -908,14 +913,16 @@ __global__ __launch_bounds__(4 * D, D / 32 > 1 ? D / 32 : 1) void kda_bwd_pair_m
   if (tid < C) sB[tid] = tid < nval ? p.beta[((size_t)b * p.T + (size_t)n * C + tid) * p.H + h] : 0.f;
   // block boundaries G_1 .. G_NB (Gamma at the last row of each block: lane
   // (r, 3), s = 4 p + 3) and the midpoints m_p = (G_p + G_p+1) / 2, G_0 = 0
-  float mid[NB];
+  float mid[NB], gbd[NB + 1];  // midpoints, block boundaries G_0 = 0, G_1, ...
   bool fatal = false;
   {
     float gprev = 0.f;
+    gbd[0] = 0.f;
 #pragma unroll
     for (int q = 0; q < NB; ++q) {
       const float gend = __shfl(gB[4 * q + 3], 48 + r, 64);
       mid[q] = 0.5f * (gprev + gend);
+      gbd[q + 1] = gend;
       fatal |= gprev - gend > kBwdSpan2;
       gprev = gend;
     }
@@ -989,7 +996,9 @@ __global__ __launch_bounds__(4 * D, D / 32 > 1 ? D / 32 : 1) void kda_bwd_pair_m
     // rK, rQ of rows in block pb: column blocks qb <= pb
 #pragma unroll
     for (int qb = 0; qb <= pb; ++qb) {
-      const float F = pb == qb ? 1.f : __builtin_amdgcn_exp2f(mid[pb] - mid[qb]);
+      // F_pq = exp(-s_q/2) exp(m_p - G_{q+1}), applied one factor at a time
+      const float F1 = pb == qb ? 1.f : __builtin_amdgcn_exp2f(gbd[qb + 1] - mid[qb]);
+      const float F2 = pb == qb ? 1.f : __builtin_amdgcn_exp2f(mid[pb] - gbd[qb + 1]);
       f32x4 xk = {0.f, 0.f, 0.f, 0.f}, xq = xk;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
@@ -1001,14 +1010,16 @@ __global__ __launch_bounds__(4 * D, D / 32 > 1 ? D / 32 : 1) void kda_bwd_pair_m
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        tK[e] = fmaf(F, xk[e], tK[e]);
-        tQ[e] = fmaf(F, xq[e], tQ[e]);
+        tK[e] = fmaf(F2, xk[e] * F1, tK[e]);
+        tQ[e] = fmaf(F2, xq[e] * F1, tQ[e]);
       }
     }
     // cK of columns in block pb: row blocks rb >= pb
 #pragma unroll
     for (int rb = pb; rb < NB; ++rb) {
-      const float F = rb == pb ? 1.f : __builtin_amdgcn_exp2f(mid[rb] - mid[pb]);
+      // F_rp = exp(-s_r/2) exp(G_r - m_p), applied one factor at a time
+      const float F1 = rb == pb ? 1.f : __builtin_amdgcn_exp2f(mid[rb] - gbd[rb]);
+      const float F2 = rb == pb ? 1.f : __builtin_amdgcn_exp2f(gbd[rb] - mid[pb]);
       f32x4 xc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
@@ -1019,7 +1030,7 @@ __global__ __launch_bounds__(4 * D, D / 32 > 1 ? D / 32 : 1) void kda_bwd_pair_m
         xc = __builtin_amdgcn_mfma_f32_16x16x4f32(pt, qa[4 * rb + s], xc, 0, 0, 0);
       }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) tC[e] = fmaf(F, xc[e], tC[e]);
+      for (int e = 0; e < 4; ++e) tC[e] = fmaf(F2, xc[e] * F1, tC[e]);
     }
     // element terms for rows t = 16 pb + 4 g4 + e of channel c; each row's inputs
     // were loaded one row ahead (the next row's loads go out before this row's

@@ -88,6 +88,10 @@ struct PrepParams {
   unsigned* fb_count;       // chunks handed to the exact preparation
   unsigned* fb_list;        // their record indices
   int B, T, H, NT;
+  // time slices: the records hold chunks c0 .. c0 + NT - 1 of each sequence (NT
+  // record slots per (sequence, head)), and the launch covers the first nchunk of
+  // them; whole sequences: c0 = 0, nchunk = NT
+  int c0, nchunk;
   int conv_k;
   int l2;
   float eps;
@@ -108,10 +112,11 @@ struct PrepParams {
 
 struct StateParams {
   const char* ws;
-  const float* S0;  // may be NULL
+  const float* S0;  // may be NULL; may equal S_T
   float* S_T;
   void* o;
   int B, T, H, NT;
+  int c0;           // time slices: the walk takes chunks c0 .. of each sequence (0: whole)
   // output stage, applied in the walk only by the kernels built for it
   const void* o_gate;     // [B][T][H][D] or NULL
   const float* o_norm_w;  // [D] or NULL
@@ -121,7 +126,8 @@ struct StateParams {
                           // S^T then S, [rec][2][D][D], or NULL
   // conv-state hand-over by the workgroups of value block 0, or tail_out NULL: the
   // raw q, k, v [B][T][H*D], the previous conv state (or NULL) and the new one,
-  // [B][3][3][H*D].  The caller launches the walk after every read of tail_in.
+  // [B][3][3][H*D].  The caller launches the walk after every read of tail_in, and
+  // only with c0 = 0 (whole sequences).
   const void* tail_x[3];
   const void* tail_in;
   void* tail_out;

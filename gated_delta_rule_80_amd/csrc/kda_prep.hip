@@ -14,14 +14,18 @@
 // Householder factors (I - beta k k^T) that the delta rule composes.
 //
 // Step 3 as matrix products over 16-token blocks, per channel: with G_p the
-// cumulative decay just before block p and m_p = (G_p + G_{p+1}) / 2 the middle
-// of the block's range,
+// cumulative decay just before block p, s_p = G_p - G_{p+1} its span and
+// m_p = (G_p + G_{p+1}) / 2 the middle of the block's range,
 //   a_i = exp(Gamma_i - m_p) for i in block p,   b_j = exp(m_q - Gamma_j) for j in block q,
-//   exp(Gamma_i - Gamma_j) = a_i * exp(m_p - m_q) * b_j,
-// where the pair factor is 1 on the diagonal (p = q) and <= 1 below it.  a and b
-// lie within exp(+-s/2) for a block decay span s, so every factor is representable
-// in fp32/bf16 while s stays below ~166 nats; a chunk with a wider block span is
-// listed in the workspace and recomputed by the exact preparation kernel.
+//   exp(Gamma_i - Gamma_j) = a_i * exp(m_p - m_q) * b_j.
+// a and b lie within exp(+-s/2), so every operand is representable in fp32/bf16
+// while s stays below ~166 nats; a chunk with a wider block span is listed in the
+// workspace and recomputed by the exact preparation kernel.  The pair factor of
+// blocks p > q is exp(-(s_p + s_q)/2) or smaller and may underflow although the
+// products it scales do not, so it is applied to the b side in two steps whose
+// partial products stay representable:
+//   b_j exp(-s_q/2) = exp(G_{q+1} - Gamma_j) <= 1,  then times exp(m_p - G_{q+1}) <= 1
+// (both factors <= 1: a product underflows only where its true value does).
 #include "kda_convnorm.h"
 #include "kda_device.h"
 #include "kda_launch.h"
@@ -77,7 +81,8 @@ struct FastSmem {
   alignas(16) float mid[NB * D];       // m_p
   alignas(16) float emid[NB * D];      // exp(m_p)
   alignas(16) float ecm[NB * D];       // exp(Gamma_C - m_p)
-  alignas(16) float mpq[NPAIR * D];    // exp(m_R - m_Q) for blocks R > Q
+  alignas(16) float hs[NB * D];        // exp(-s_p / 2) = exp(G_{p+1} - m_p)
+  alignas(16) float xf[NPAIR * D];     // exp(m_R - G_{Q+1}) for blocks R > Q
   alignas(16) float filt[3 * 4 * D];   // the head's conv filters [q, k, v][tap][D]
   int fatal;
 };
@@ -101,6 +106,28 @@ template <int K>
 __device__ __forceinline__ void scale_k(RowFrag<float, K>& fr, const float* f, int g) {
 #pragma unroll
   for (int i = 0; i < RowFrag<float, K>::N; ++i) fr.v[i] *= f[4 * i + g];
+}
+
+// Multiply the operand fragment element-wise by f1[k], then by f2[k] (two
+// roundings in fp32, so a product of two tiny factors cannot underflow where the
+// operand times f1 stays representable).
+template <int K>
+__device__ __forceinline__ void scale_k2(RowFrag<__bf16, K>& fr, const float* f1, const float* f2,
+                                         int g) {
+  using FR = RowFrag<__bf16, K>;
+#pragma unroll
+  for (int i = 0; i < FR::N; ++i)
+#pragma unroll
+    for (int e = 0; e < FR::PER; ++e) {
+      const int k = i * FR::STEP + FR::PER * g + e;
+      fr.v[i][e] = (__bf16)(((float)fr.v[i][e] * f1[k]) * f2[k]);
+    }
+}
+template <int K>
+__device__ __forceinline__ void scale_k2(RowFrag<float, K>& fr, const float* f1, const float* f2,
+                                         int g) {
+#pragma unroll
+  for (int i = 0; i < RowFrag<float, K>::N; ++i) fr.v[i] = (fr.v[i] * f1[4 * i + g]) * f2[4 * i + g];
 }
 
 // Swizzled image of a [rows][C] matrix used as a matrix-core operand along its
@@ -194,7 +221,7 @@ __global__ __launch_bounds__(fast_threads<E>()) void kda_chunk_prep_kernel(PrepP
     rec = h * p.NT + gc;
     if (n < 0 || (long)n * C >= Tq) return;  // inconsistent tables: touch nothing
   }
-  const int t0 = n * C;
+  const int t0 = (p.c0 + n) * C;  // first token of the chunk in its sequence
   char* recp = p.ws + (size_t)rec * RL.bytes;
   E* gW = reinterpret_cast<E*>(recp) + RL.w;
   E* gQL = reinterpret_cast<E*>(recp) + RL.ql;
@@ -314,13 +341,14 @@ __global__ __launch_bounds__(fast_threads<E>()) void kda_chunk_prep_kernel(PrepP
       sm.mid[q * D + c] = md[q];
       sm.emid[q * D + c] = __builtin_amdgcn_exp2f(md[q]);
       sm.ecm[q * D + c] = __builtin_amdgcn_exp2f(acc - md[q]);
+      sm.hs[q * D + c] = __builtin_amdgcn_exp2f(gbl[q + 1] - md[q]);
       fatal |= gbl[q] - gbl[q + 1] > kFatalSpan2;
     }
 #pragma unroll
     for (int R = 1; R < NB; ++R)
 #pragma unroll
       for (int Q = 0; Q < R; ++Q)
-        sm.mpq[pair_index(R, Q) * D + c] = __builtin_amdgcn_exp2f(md[R] - md[Q]);
+        sm.xf[pair_index(R, Q) * D + c] = __builtin_amdgcn_exp2f(md[R] - gbl[Q + 1]);
     if (fatal) atomicOr(&sm.fatal, 1);
   }
   __syncthreads();
@@ -428,7 +456,7 @@ __global__ __launch_bounds__(fast_threads<E>()) void kda_chunk_prep_kernel(PrepP
     for (int kc = 0; kc < D; kc += KC) {
       RowFrag<E, KC> cf, fa, fp;
       cf.load(CB + (16 * Q0 + r) * LQ + kc, g4);
-      if (R0 != Q0) scale_k<KC>(cf, &sm.mpq[pair_index(R0, Q0) * D + kc], g4);
+      if (R0 != Q0) scale_k2<KC>(cf, &sm.hs[Q0 * D + kc], &sm.xf[pair_index(R0, Q0) * D + kc], g4);
       fa.load(RA + (16 * R0 + r) * LQ + kc, g4);
       fp.load(RP + (16 * R0 + r) * LQ + kc, g4);
       mma<KC>(accA[i], cf, fa);
@@ -762,7 +790,7 @@ __global__ void kda_reset_count_kernel(unsigned* count) {
 // ------------------------------------------------------------------ launchers
 template <int D, int C, typename IO, typename E>
 static hipError_t launch_prep_t(const PrepParams& p, hipStream_t st) {
-  const unsigned grid = (unsigned)((size_t)p.B * p.H * p.NT);
+  const unsigned grid = (unsigned)((size_t)p.B * p.H * p.nchunk);
   hipLaunchKernelGGL((kda_chunk_prep_kernel<D, C, IO, E>), dim3(grid), dim3(fast_threads<E>()), 0,
                      st, p);
   return hipGetLastError();

@@ -105,7 +105,7 @@ __global__ __launch_bounds__(kPrepThreads) void kda_chunk_prep_exact_kernel(Prep
     Tq = p.seqs.bounds[b + 1] - p.seqs.bounds[b];
     if (n < 0 || (long)n * C >= Tq) continue;  // inconsistent tables: touch nothing
   }
-  const int t0 = n * C;
+  const int t0 = (p.c0 + n) * C;  // first token of the chunk in its sequence
   char* recp = p.ws + (size_t)rec * RL.bytes;
   E* gW = reinterpret_cast<E*>(recp) + RL.w;
   E* gQL = reinterpret_cast<E*>(recp) + RL.ql;

@@ -107,9 +107,10 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void kda_chunk_state_kernel(
   int Tq, nch;
   size_t rec0;
   if (p.seqs.bounds == nullptr) {
-    tok0 = (long)b * p.T;
-    Tq = p.T;
-    nch = p.NT;
+    // chunks c0 .. of sequence b: tokens from c0 C on, at most NT chunks
+    tok0 = (long)b * p.T + (long)p.c0 * C;
+    Tq = p.T - p.c0 * C;
+    nch = (Tq + C - 1) / C < p.NT ? (Tq + C - 1) / C : p.NT;
     rec0 = (size_t)bh * p.NT;
   } else {
     tok0 = p.seqs.bounds[b];

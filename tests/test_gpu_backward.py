@@ -19,7 +19,11 @@ NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dS0", "dconv_w", "dconv_state")
 
 
 def check_backward(w, chunk, seed=0, conv=True, l2=True, scale=1.0, with_dST=True, g_head=None):
-    inp = make(w, seed)
+    check_backward_inputs(w, chunk, make(w, seed), seed, conv, l2, scale, with_dST, g_head)
+
+
+def check_backward_inputs(w, chunk, inp, seed=0, conv=True, l2=True, scale=1.0, with_dST=True,
+                          g_head=None):
     if g_head is not None:
         # constant log-decay per token on the given heads: {head: g}
         g = inp["g"].clone()
@@ -97,6 +101,23 @@ def test_backward_factored_and_exact_pair_paths(io, D, chunk, g0):
     check_backward(w, chunk, seed=17, g_head={0: g0})
 
 
+@pytest.mark.parametrize("io,D,chunk", [("fp32", 64, 32), ("bf16", 128, 64)])
+def test_backward_wide_spans_with_free_block_boundaries(io, D, chunk):
+    """Head 0 decays by 5.88 nats per token inside every 16-token block but not at
+    the first token of a block: each block spans 127.3 log2 units (inside the
+    factored pair products' limit), so the pair factor of two adjacent blocks,
+    exp(-(s_p + s_q)/2), is a float32 denormal while the products it scales are
+    O(1)."""
+    w = small(B=1, T=150, H=2, D=D, io=io, chunk=chunk, s0=True, conv_state=True)
+    inp = make(w, 19)
+    g = inp["g"].float()
+    t = torch.arange(w.T)
+    g[0, :, 0, :] = torch.where(t % 16 == 0, 0.0, -5.88)[:, None]
+    inp["g"] = g.to(inp["g"].dtype)
+    w2 = w
+    check_backward_inputs(w2, chunk, inp, seed=19)
+
+
 def test_backward_without_state_gradients():
     w = small(B=2, T=40, H=2, D=64, io="bf16", chunk=32)
     check_backward(w, 32, seed=8, with_dST=False)
@@ -133,3 +154,45 @@ def test_backward_empty_sequence():
     assert torch.equal(S_T, inp["S0"])
     assert float(grads["dconv_w"].abs().max()) == 0.0
     assert float(grads["dconv_state"].abs().max()) == 0.0
+
+
+@pytest.mark.parametrize("io,D,chunk", [("bf16", 128, 64), ("fp32", 32, 16)])
+def test_backward_in_place_states(io, D, chunk):
+    """The forward rules allow S_T == S0 and conv_state_out == conv_state_in; the
+    backward recomputes the forward, so the hand-over must not overwrite the conv
+    history before the gradients have read it.  Called through the C ABI with both
+    states in place, the gradients equal those of a call with separate outputs
+    (bit for bit), and the recomputed S_T and conv hand-over land in place."""
+    w = small(B=2, T=70, H=2, D=D, io=io, chunk=chunk, s0=True, conv_state=True)
+    inp = cuda(make(w, 21))
+    do = torch.randn(w.B, w.T, w.H, w.D, generator=torch.Generator().manual_seed(4)).to(
+        inp["q"].dtype).cuda()
+    ref, o_ref, S_ref = kda.kda_prefill_backward(inp["q"], inp["k"], inp["v"], inp["g"],
+                                                 inp["beta"], inp["conv_w"], inp["conv_state"],
+                                                 inp["S0"], do=do, chunk=chunk)
+    torch.cuda.synchronize()
+    _, _, tail_ref = kda.kda_prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                     inp["conv_w"], inp["conv_state"], inp["S0"], chunk=chunk)
+    torch.cuda.synchronize()
+    S = inp["S0"].clone()
+    cs = inp["conv_state"].clone()
+    o = torch.empty_like(inp["q"])
+    fwd = kda.prefill_args(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["conv_w"],
+                           cs, S, o, S, cs, chunk=chunk)
+    f32 = dict(dtype=torch.float32, device="cuda")
+    shape = (w.B, w.T, w.H, w.D)
+    grads = dict(dq=torch.empty(*shape, **f32), dk=torch.empty(*shape, **f32),
+                 dv=torch.empty(*shape, **f32), dg=torch.empty(*shape, **f32),
+                 dbeta=torch.empty(w.B, w.T, w.H, **f32), dS0=torch.empty(w.B, w.H, w.D, w.D, **f32),
+                 dconv_w=torch.empty(3, w.H * w.D, 4, **f32),
+                 dconv_state=torch.empty(w.B, 3, 3, w.H * w.D, **f32))
+    a = kda.backward_args(fwd, do, None, grads)
+    assert kda.kda_validate_backward(a) == kda.KDA_OK
+    ws = torch.empty(kda.kda_backward_workspace_bytes(a), dtype=torch.uint8, device="cuda")
+    kda.kda_prefill_backward_raw(a, ws)
+    torch.cuda.synchronize()
+    for name, t in ref.items():
+        assert torch.equal(grads[name], t), name
+    assert torch.equal(o, o_ref)
+    assert torch.equal(S, S_ref)
+    assert torch.equal(cs, tail_ref)

@@ -302,6 +302,60 @@ def test_fallback_all_chunks_fp32():
     assert rel_l2(o, ro) <= 1e-4 and rel_l2(S, rS) <= 1e-4
 
 
+@pytest.mark.parametrize("io,D,chunk", [("fp32", 32, 64), ("fp32", 64, 32), ("bf16", 128, 64)])
+def test_wide_block_spans_with_free_block_boundaries(io, D, chunk):
+    """Head 0 decays by 10 nats per token inside every 16-token block but not at
+    the first token of a block: each block spans 150 nats (216 log2 units, inside
+    the fast preparation's factoring), while the pair formed by the last token of
+    a block and the first of the next has no decay at all.  The pair factor of two
+    adjacent blocks, exp(-(s_p + s_q)/2), lies far below the float32 range here, so
+    it must not be formed on its own (the products it scales are O(1))."""
+    w = small(B=1, T=150, H=2, D=D, io=io, chunk=chunk, s0=True, conv_state=True)
+    inp = make(w, 31)
+    g = inp["g"].float()
+    t = torch.arange(w.T)
+    g[0, :, 0, :] = torch.where(t % 16 == 0, 0.0, -10.0)[:, None]
+    inp["g"] = g.to(inp["g"].dtype)
+    o, S, _ = gpu_prefill(inp, chunk)
+    ro, rS, _ = oracle_prefill(inp)
+    tol = TOL[io]
+    for h in range(w.H):
+        eo, eS = rel_l2(o[0, :, h], ro[0, :, h]), rel_l2(S[0, h], rS[0, h])
+        print(f"{io} D={D} C={chunk} head {h}: o={eo:.2e} S={eS:.2e}", flush=True)
+        assert eo <= tol and eS <= tol, (h, eo, eS)
+
+
+@pytest.mark.parametrize("io", ["fp32", "bf16"])
+def test_fallback_more_chunks_than_exact_grid(io):
+    """768 chunks (B=1, T=1024, H=24, C=32), every one too strong for the factoring
+    (g = -15 per token: a 16-token block spans 240 nats), so all of them go to the
+    exact preparation, whose grid holds at most 512 workgroups: workgroups take a
+    second listed chunk after reusing their LDS.  The workspace header counts the
+    listed chunks."""
+    w = small(B=1, T=1024, H=24, D=16, io=io, chunk=32, s0=True, conv_state=True)
+    inp = make(w, 23)
+    inp["g"] = torch.full_like(inp["g"], -15.0)
+    c = cuda(inp)
+    o = torch.empty_like(c["q"])
+    S_T = torch.empty(w.B, w.H, w.D, w.D, dtype=torch.float32, device="cuda")
+    cso = torch.empty_like(c["conv_state"])
+    a = kda.prefill_args(c["q"], c["k"], c["v"], c["g"], c["beta"], c["conv_w"], c["conv_state"],
+                         c["S0"], o, S_T, cso, chunk=32)
+    ws = torch.empty(kda.kda_prefill_workspace_bytes(a), dtype=torch.uint8, device="cuda")
+    kda.kda_prefill_raw(a, ws)
+    torch.cuda.synchronize()
+    listed = int(ws[:4].view(torch.int32).item())
+    assert listed == w.H * (w.T // 32) == 768, listed
+    ro, rS, rtail = oracle_prefill(inp)
+    tol = TOL[io]
+    eo, eS = rel_l2(o.float().cpu().numpy(), ro), rel_l2(S_T.cpu().numpy(), rS)
+    print(f"exact preparation, {listed} listed chunks, {io}: o={eo:.2e} S={eS:.2e}", flush=True)
+    assert eo <= tol and eS <= tol
+    for h in range(w.H):
+        assert rel_l2(o[0, :, h].float().cpu().numpy(), ro[0, :, h]) <= tol, h
+    np.testing.assert_array_equal(cso.float().cpu().numpy(), rtail)
+
+
 @pytest.mark.parametrize("io,D,chunk", [("bf16", 16, 64), ("bf16", 16, 32), ("bf16", 128, 64),
                                         ("fp32", 64, 32), ("fp32", 16, 16), ("bf16", 64, 16)])
 def test_outputs_do_not_depend_on_prior_buffer_contents(io, D, chunk):
