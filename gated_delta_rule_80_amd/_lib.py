@@ -23,13 +23,15 @@ KDA_BF16 = 0
 KDA_FP32 = 1
 KDA_FLAG_L2NORM_QK = 1
 KDA_FLAG_BETA_LOGITS = 2
-ABI_VERSION = 2
+ABI_VERSION = 3
 KDA_STAGE_PREP, KDA_STAGE_STATE, KDA_STAGE_CONV_TAIL, KDA_STAGE_OUTPUT = 0, 1, 2, 3
 KDA_STAGE_STATE_TAIL = 4  # stages 1 and 2 in one launch, as kda_prefill runs them
 NUM_STAGES = 4
 STATUS_NAMES = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE",
                 4: "KDA_ERR_ALIGN", 5: "KDA_ERR_ALIAS", 6: "KDA_ERR_UNSUPPORTED",
-                7: "KDA_ERR_WORKSPACE", 8: "KDA_ERR_HIP", 9: "KDA_ERR_VALUE"}
+                7: "KDA_ERR_WORKSPACE", 8: "KDA_ERR_HIP", 9: "KDA_ERR_VALUE",
+                10: "KDA_ERR_SCRATCH"}
+KDA_ERR_SCRATCH = 10
 
 _vp = ctypes.c_void_p
 
@@ -107,6 +109,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.kda_prefill_workspace_bytes.argtypes = [P(PrefillArgs)]
     lib.kda_prefill.restype = ctypes.c_int
     lib.kda_prefill.argtypes = [P(PrefillArgs), _vp, ctypes.c_size_t, _vp]
+    lib.kda_prefill_static.restype = ctypes.c_int
+    lib.kda_prefill_static.argtypes = [P(PrefillArgs), _vp]
     lib.kda_prefill_stage.restype = ctypes.c_int
     lib.kda_prefill_stage.argtypes = [P(PrefillArgs), _vp, ctypes.c_size_t, ctypes.c_int, _vp]
     lib.kda_validate_conv_norm.restype = ctypes.c_int
@@ -286,6 +290,13 @@ def kda_prefill_raw(args: PrefillArgs, workspace, stream=None):
     ws = _ptr(workspace) if workspace is not None else None
     nbytes = workspace.numel() if workspace is not None else 0
     _check(load().kda_prefill(ctypes.byref(args), ws, nbytes, _stream(stream)), "kda_prefill")
+
+
+def kda_prefill_static_raw(args: PrefillArgs, stream=None) -> int:
+    """kda_prefill_static on a pre-filled argument struct: the library's static
+    per-GPU scratch is the workspace (nothing is allocated).  Returns the status
+    (KDA_OK, or KDA_ERR_SCRATCH when the request does not fit)."""
+    return int(load().kda_prefill_static(ctypes.byref(args), _stream(stream)))
 
 
 def conv_norm_args(q, k, v, conv_w, conv_state_in=None, q_out=None, k_out=None, v_out=None,

@@ -146,6 +146,7 @@ const char* kda_status_str(int status) {
     case KDA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case KDA_ERR_HIP: return "HIP runtime error";
     case KDA_ERR_VALUE: return "scalar argument out of range";
+    case KDA_ERR_SCRATCH: return "request needs more than the static scratch buffer";
   }
   return "unknown status";
 }
@@ -355,6 +356,56 @@ static kda_status run_stage(const kda_prefill_args* a, void* ws, int stage, hipS
   }
   return KDA_ERR_VALUE;
 }
+
+// Largest number of chunk slots per (sequence, head) whose workspace fits `bytes`
+// (at most the sequence's chunk count), or 0 when not even one fits.
+static int slice_capacity(const kda_prefill_args* a, size_t bytes) {
+  const int nt = (a->T + a->chunk - 1) / a->chunk;
+  const size_t bh = (size_t)a->B * a->H;
+  int lo = 0, hi = nt;  // workspace_layout grows with the slot count
+  while (lo < hi) {
+    const int mid = lo + (hi - lo + 1) / 2;
+    if (kda::workspace_layout(bh * mid, a->chunk, a->D, esize(a->io)).bytes <= bytes)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
+}  // extern "C"
+
+namespace kda {
+
+// The whole forward in a caller-sized workspace (validated arguments): as
+// kda_prefill when its workspace fits `bytes`; otherwise B equal-length
+// sequences are run in time slices (preparation and walk of as many chunks per
+// (sequence, head) as fit, the state carried from one slice to the next in S_T),
+// then the conv hand-over and the separate output pass over whole sequences.
+kda_status prefill_in_workspace(const kda_prefill_args* a, void* ws, size_t bytes, hipStream_t st) {
+  if (a->T > 0 && ws_layout(a).bytes > bytes) {
+    if (packed(a)) return KDA_ERR_SCRATCH;
+    const int cap = slice_capacity(a, bytes);
+    if (cap < 1) return KDA_ERR_SCRATCH;
+    const int nt = (a->T + a->chunk - 1) / a->chunk;
+    for (int c0 = 0; c0 < nt; c0 += cap) {
+      const Slice sl{c0, nt - c0 < cap ? nt - c0 : cap, cap};
+      if (kda_status e = run_stage(a, ws, KDA_STAGE_PREP, st, nullptr, false, &sl); e != KDA_OK)
+        return e;
+      if (kda_status e = run_stage(a, ws, KDA_STAGE_STATE, st, nullptr, false, &sl); e != KDA_OK)
+        return e;
+    }
+    if (kda_status e = run_stage(a, ws, KDA_STAGE_CONV_TAIL, st); e != KDA_OK) return e;
+    return run_stage(a, ws, KDA_STAGE_OUTPUT, st);
+  }
+  for (int stage = KDA_STAGE_PREP; stage <= KDA_STAGE_OUTPUT; ++stage)
+    if (kda_status e = run_stage(a, ws, stage, st, nullptr, true); e != KDA_OK) return e;
+  return KDA_OK;
+}
+
+}  // namespace kda
+
+extern "C" {
 
 kda_status kda_prefill_stage(const kda_prefill_args* a, void* ws, size_t ws_bytes, int stage,
                              void* stream) {

@@ -2,6 +2,7 @@
 #pragma once
 #include <hip/hip_runtime.h>
 
+#include "kda.h"
 #include "kda_layout.h"
 
 namespace kda {
@@ -19,5 +20,11 @@ hipError_t launch_copy_state(const float* src, float* dst, size_t n, hipStream_t
 hipError_t launch_backward(const BwdLaunch& L, int D, int C, bool fp32, hipStream_t st);
 size_t bwd_front_blocks(int T, int D);
 hipError_t launch_decode(const DecodeParams& p, int D, bool fp32, hipStream_t st);
+
+// The whole prefill (arguments already validated) in a workspace of `bytes`:
+// time slices when the whole-sequence workspace does not fit (B equal-length
+// sequences only; KDA_ERR_SCRATCH otherwise, or when one chunk per (sequence,
+// head) does not fit).  Defined with the host runtime.
+kda_status prefill_in_workspace(const kda_prefill_args* a, void* ws, size_t bytes, hipStream_t st);
 
 }  // namespace kda

@@ -36,7 +36,8 @@
  * Conventions for every entry point
  *   - Ownership: the caller owns every buffer.  The library never allocates or
  *     frees device memory and keeps no global mutable state (reentrant; any
- *     number of streams).  Scratch memory is the caller's workspace.
+ *     number of streams).  Scratch memory is the caller's workspace -- except
+ *     for kda_prefill_static, whose workspace is a static array per GPU.
  *   - Pointers named "device" are device (HBM) addresses; they must be 16-byte
  *     aligned.  Argument structs themselves live in host memory.
  *   - Asynchrony: compute entry points enqueue kernels on `stream` (a
@@ -72,7 +73,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 
 typedef enum kda_status {
   KDA_OK = 0,
@@ -84,7 +85,8 @@ typedef enum kda_status {
   KDA_ERR_UNSUPPORTED = 6, /* valid request outside what this build implements */
   KDA_ERR_WORKSPACE = 7,   /* workspace NULL or smaller than the query says */
   KDA_ERR_HIP = 8,         /* the HIP runtime refused a launch */
-  KDA_ERR_VALUE = 9        /* a scalar argument is out of range (eps, scale, flags, stage) */
+  KDA_ERR_VALUE = 9,       /* a scalar argument is out of range (eps, scale, flags, stage) */
+  KDA_ERR_SCRATCH = 10     /* kda_prefill_static: the request needs more than the static scratch */
 } kda_status;
 
 typedef enum kda_dtype {
@@ -178,6 +180,28 @@ kda_status kda_prefill(const kda_prefill_args* a, void* ws, size_t ws_bytes, voi
 #define KDA_STAGE_STATE_TAIL 4
 kda_status kda_prefill_stage(const kda_prefill_args* a, void* ws, size_t ws_bytes, int stage,
                              void* stream);
+
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: kda_prefill
+ * with its workspace taken from a static device array of
+ * KDA_STATIC_SCRATCH_BYTES that the library holds on every GPU it runs on (one
+ * array per GPU, from the first call there until the process ends).  It
+ * allocates nothing and takes no workspace argument; the caller still provides
+ * every input and output.  Same arguments, rules and results as kda_prefill.
+ *   - When the whole-sequence workspace (kda_prefill_workspace_bytes) fits the
+ *     array, the call runs exactly as kda_prefill.  Otherwise B equal-length
+ *     sequences are processed in time slices of as many chunks per (sequence,
+ *     head) as fit, the state handed from slice to slice through S_T; the
+ *     results are the same bit for bit.  Packed sequences that do not fit, and
+ *     any request of which not even one chunk per (sequence, head) fits (more
+ *     than about 1,800 sequence-heads at D = 128, chunk 64, bf16), return
+ *     KDA_ERR_SCRATCH before anything is enqueued.
+ *   - The stream must belong to the current device (hipSetDevice).
+ *   - Every call on one GPU shares that GPU's array: calls that may overlap on
+ *     one GPU (other streams, other host threads) race and must be serialised
+ *     by the caller.  Stream order serialises calls on one stream. */
+#define KDA_STATIC_SCRATCH_BYTES ((size_t)128 << 20)
+kda_status kda_prefill_static(const kda_prefill_args* a, void* stream);
 
 /* ---------------------------------------------------------------- conv_norm */
 /* Step 1 and 2 alone: writes the convolved, activated (and for q, k normalised)

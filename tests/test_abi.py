@@ -24,8 +24,8 @@ def test_exports_every_declared_symbol(lib):
             "kda_validate_conv_norm", "kda_status_str", "kda_abi_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.kda_abi_version() == 2
-    for s in range(10):
+    assert lib.kda_abi_version() == 3
+    for s in range(11):
         assert kda.kda_status_str(s) and kda.kda_status_str(s) != "unknown status"
 
 
