@@ -1,27 +1,37 @@
 """Benchmark of the KDA mixer on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill-4k]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill-64k]
+                    [--also prefill-4k,prefill-b4-8k-s0] [--no-stages] [--cpu-budget S]
+    python bench.py --profile-commands DIR        (print the rocprofv3 commands of a profile)
+    python bench.py --summarize-rocprof DIR       (turn their output into profiles/)
 
 A step is one kda_prefill over the workload (conv + SiLU + L2, chunk preparation,
 state walk with output, conv-state hand-over), inputs resident in HBM.  The
-decode step (B=256 sequences, in-place state) is timed in the same run and
-reported beside it.  A second leg ("stages") times the same prefill and decode
-steps with the optional stages on (decay and write strength from raw
-projections, output RMSNorm and sigmoid gate), the prefill's tokens packed as
-sequences of mixed length, and the backward pass.  Prints one JSON line.
+headline is the long-context layer (B=1, T=65536, H=96, D=128, bf16, chunk 64),
+the largest single-GPU prefill; the one-layer 4k prefill and the batched 8k
+prefill with an initial state are timed in the same run and reported beside it,
+as is the decode step (B=256 sequences, in-place state).  A further leg
+("stages", on the 4k prefill) times the optional stages (decay and write
+strength from raw projections, output RMSNorm and sigmoid gate), the 4k tokens
+packed as sequences of mixed length, and the backward pass.  Prints one JSON line.
 
-Roofline figures use algorithmic bytes (each tensor the kernel must read or
-write, once) divided by the kernel's mean duration from HIP events recorded on
-the launch stream; peaks are MI355X's published 8 TB/s HBM and 2.5 PFLOP/s dense
-bf16.  The CPU baseline runs the fp64 oracle on a bounded sample of heads in a
-process pool on the host cores.
+Rooflines use the fused minimum of HBM traffic of the whole mixer (raw q, k, v,
+g, beta read once, o written once: 5 H D + H elements per token; S_T written,
+S0 read when given, the conv filters read once) against MI355X's published
+8 TB/s.  `roofline` divides it by the dominant kernel's mean duration (HIP events
+on the launch stream), `path` by the whole step's; the bytes the kernels
+actually move are `traffic` (rocprofv3 counters, profiles/traffic.json).  The
+CPU baseline times the fp64 oracle on whole (sequence, head) pairs of the
+headline workload in a pool of host processes.
 """
 from __future__ import annotations
 
 import argparse
+import glob
 import hashlib
 import json
 import os
+import shutil
 import sys
 import time
 
@@ -43,6 +53,10 @@ KERNEL_SOURCES = ["gated_delta_rule_80_amd/csrc/kda_prep.hip",
                   "gated_delta_rule_80_amd/csrc/kda_convnorm.h",
                   "gated_delta_rule_80_amd/csrc/kda_device.h",
                   "gated_delta_rule_80_amd/csrc/kda_layout.h"]
+HEADLINE = "prefill-64k"
+ALSO = "prefill-4k,prefill-b4-8k-s0"
+STAGES_WORKLOAD = "prefill-4k"
+METRIC = "KDA tokens/s per GPU (prefill, H=96 d=128) + decode seq/s; % of roofline"
 
 
 def source_hash() -> str:
@@ -57,8 +71,23 @@ def esize(io: str) -> int:
     return 2 if io == "bf16" else 4
 
 
-def prefill_bytes(w) -> dict:
-    """Algorithmic bytes per launch of each prefill kernel and of the whole path."""
+def path_bytes(w) -> int:
+    """Fused minimum of HBM traffic of one prefill: raw q, k, v, g (H D elements
+    each per token), beta (H) read and o (H D) written once per token -- 123,072 B
+    per token at H = 96, D = 128, bf16 -- plus S_T written, S0 read when given,
+    the conv filters (and conv states, when given) once."""
+    es = esize(w.io)
+    tok = w.B * w.T
+    state = w.B * w.H * w.D * w.D * 4
+    cst = 2 * w.B * 3 * 3 * w.H * w.D * es if w.conv_state_std > 0 else 0
+    return (tok * (5 * w.H * w.D + w.H) * es + state + (state if w.s0_std > 0 else 0)
+            + 3 * w.H * w.D * 4 * 4 + cst)
+
+
+def design_bytes(w) -> dict:
+    """Bytes each prefill kernel of this design must move: the preparation reads
+    the raw inputs and writes one record per chunk (W, Q Lambda, Ktil^T, U~ in the
+    I/O type, P, Lambda_C); the walk reads the records and writes o and S_T."""
     es = esize(w.io)
     C, D = w.chunk, w.D
     NT = -(-w.T // C)
@@ -69,13 +98,9 @@ def prefill_bytes(w) -> dict:
     state = w.B * w.H * D * D * 4
     s0 = state if w.s0_std > 0 else 0
     cst = w.B * 3 * 3 * w.H * D * es if w.conv_state_std > 0 else 0
-    record = (4 * C * D + C * C) * es + 4 * D  # what the preparation hands over per chunk
-    records = w.B * w.H * NT * record
-    return {
-        "prep": 4 * x + beta + conv_w + cst + records,
-        "state": records + s0 + x + state,
-        "path": 4 * x + beta + conv_w + cst + s0 + x + state,  # fused minimum of the whole step
-    }
+    records = w.B * w.H * NT * ((4 * C * D + C * C) * es + 4 * D)
+    return {"kda_chunk_prep_kernel": 4 * x + beta + conv_w + cst + records,
+            "kda_chunk_state_kernel": records + s0 + x + state}
 
 
 def prefill_flops(w) -> float:
@@ -91,40 +116,21 @@ def decode_bytes(w) -> int:
             + 2 * w.B * 3 * 3 * w.H * w.D * es + 3 * w.H * w.D * 16)
 
 
-def backward_bytes(w) -> dict:
-    """Algorithmic bytes per launch of each backward kernel (its inputs read once and
-    its outputs written once, with the intermediate buffers the kernels hand over:
-    records, checkpoints, per-chunk gradients and dy in the I/O type) and of the
-    whole call ("path": raw inputs and dO in, every gradient and the recomputed
-    forward outputs out).  dS_T is not given in the benchmark."""
+def backward_bytes(w) -> int:
+    """Fused minimum of the backward call: raw inputs and dO in, every gradient and
+    the recomputed forward outputs out (dS_T not given in the benchmark)."""
     es = esize(w.io)
-    C, D = w.chunk, w.D
-    NT = -(-w.T // C)
-    nrec = w.B * w.H * NT
     tok = w.B * w.T
-    xe, x4 = tok * w.H * D * es, tok * w.H * D * 4
+    xe, x4 = tok * w.H * w.D * es, tok * w.H * w.D * 4
     bth4 = tok * w.H * 4
-    state = w.B * w.H * D * D * 4
-    cw = 3 * w.H * D * 4 * 4
-    cst_e = w.B * 3 * 3 * w.H * D * es if w.conv_state_std > 0 else 0
-    cst_4 = w.B * 3 * 3 * w.H * D * 4
+    state = w.B * w.H * w.D * w.D * 4
+    cw = 3 * w.H * w.D * 4 * 4
+    cst_e = w.B * 3 * 3 * w.H * w.D * es if w.conv_state_std > 0 else 0
+    cst_4 = w.B * 3 * 3 * w.H * w.D * 4
     s0 = state if w.s0_std > 0 else 0
-    cd, cc, dd = C * D, C * C, D * D
-    tokb = 4 * (256 // (D // 8))
-    nblk = -(-w.T // tokb)
-    return {
-        "walk": nrec * ((3 * cd + cc) * es + 4 * D) + xe + nrec * (cd + dd) * es + state,
-        "prod": nrec * (2 * cd + 2 * dd) * es + xe + nrec * ((3 * cd + cc) * es + D * 4),
-        # the front end's outputs k, v (and q) in the I/O type, Gamma in float32
-        "t": nrec * (cc + cd + cd) * es + 2 * xe + x4 + bth4 + nrec * (2 * cd + cc) * es,
-        # the gradients of the front end's outputs (dy) in the I/O type
-        "pair": 3 * xe + x4 + bth4 + nrec * ((2 * cc + 4 * cd) * es + D * 4) + 3 * xe + x4 + bth4,
-        "front": 3 * xe + cw + cst_e + 3 * xe + bth4 + 3 * x4 + w.B * nblk * 3 * w.H * D * 16
-                 + cst_4 + bth4,
-        "path": 4 * xe + tok * w.H * es + cw + cst_e + s0 + xe  # q, k, v, g, beta, filters, history, S0, dO
-                + 4 * x4 + bth4 + state + cw + cst_4        # dq, dk, dv, dg, dbeta, dS0, dconv_w, dconv_state
-                + xe + state + cst_e,                       # o, S_T, conv hand-over recomputed
-    }
+    return (4 * xe + tok * w.H * es + cw + cst_e + s0 + xe
+            + 4 * x4 + bth4 + state + cw + cst_4
+            + xe + state + cst_e)
 
 
 def stage_bytes(w) -> dict:
@@ -137,77 +143,58 @@ def stage_bytes(w) -> dict:
     return {"path_extra": x + params, "out_pass": 3 * x + w.D * 4}
 
 
-def traffic_for(kernel: str):
-    """Measured HBM bytes per launch from the committed counter summary, or None
-    when absent or taken on different kernel sources."""
-    p = os.path.join(ROOT, "profiles", "traffic.json")
+def traffic_for(workload: str, kernel: str):
+    """Measured HBM bytes per launch of a kernel at a workload, from the committed
+    counter summary, or None when absent or taken on other kernel sources."""
     try:
-        with open(p) as f:
+        with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
             d = json.load(f)
     except (OSError, ValueError):
         return None
-    if d.get("source_hash") != source_hash():
+    wl = d.get("workloads", {}).get(workload, {})
+    if wl.get("source_hash") != source_hash():
         return None
-    k = d.get("kernels", {}).get(kernel)
+    k = wl.get("kernels", {}).get(kernel)
     return None if k is None else k.get("bytes_per_launch")
 
 
-def cpu_baseline(w, inp, budget_s: float):
-    """Time the fp64 oracle on whole heads (full sequence) until ~budget_s elapsed."""
-    import multiprocessing as mp
-    from concurrent.futures import ProcessPoolExecutor
-
-    from kda_inputs import to_numpy
-    from oracle import kda_reference
-
+def host_cores() -> int:
     try:
-        ncpu = len(os.sched_getaffinity(0))
+        return len(os.sched_getaffinity(0))
     except AttributeError:  # pragma: no cover
-        ncpu = os.cpu_count() or 1
-    workers = max(1, min(16, ncpu))
-    for var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
-        os.environ[var] = "1"
-    D = w.D
-    heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+        return os.cpu_count() or 1
 
-    def job(b, h):
-        ch = slice(h * D, (h + 1) * D)
-        one = lambda x: to_numpy(x[b:b + 1, :, h:h + 1])
-        return (one(inp["q"]), one(inp["k"]), one(inp["v"]), one(inp["g"]),
-                to_numpy(inp["beta"][b:b + 1, :, h:h + 1]), to_numpy(inp["conv_w"][:, ch]),
-                None if inp["conv_state"] is None else to_numpy(inp["conv_state"][b:b + 1, :, :, ch]),
-                None if inp["S0"] is None else to_numpy(inp["S0"][b:b + 1, h:h + 1]))
 
-    done = 0
-    ctx = mp.get_context("spawn")
-    with ProcessPoolExecutor(max_workers=workers, mp_context=ctx) as ex:
-        # warm the workers (imports, first-call costs) outside the timed region
-        list(ex.map(_warm, range(workers)))
-        t0 = time.perf_counter()
-        i = 0
-        while i < len(heads):
-            batch = heads[i:i + workers]
-            futs = [ex.submit(kda_reference, *job(b, h)) for b, h in batch]
-            for f in futs:
-                f.result()
-            done += len(batch)
-            i += len(batch)
-            if time.perf_counter() - t0 >= budget_s:
-                break
-        elapsed = time.perf_counter() - t0
-    tokens_equiv = w.B * w.T * done / (w.B * w.H)
+def cpu_baseline(w, inp, budget_s: float):
+    """Time the fp64 oracle on whole (sequence, head) pairs (full sequence each) for
+    about budget_s seconds; the rate is scaled to the whole layer."""
+    from kda_inputs import to_storage
+    from oracle.pool import pool_workers, save_array, save_meta, scratch_dir, time_pairs
+
+    # the pairs a budget can reach: heads of the first sequence, a few per host process
+    nh = min(w.H, 4 * pool_workers())
+    sub = {t: inp[t][:1, :, :nh] for t in ("q", "k", "v", "g", "beta")}
+    sub["conv_w"] = inp["conv_w"][:, :nh * w.D]
+    sub["conv_state"] = None if inp["conv_state"] is None else inp["conv_state"][:1, :, :, :nh * w.D]
+    sub["S0"] = None if inp["S0"] is None else inp["S0"][:1, :nh]
+    d = scratch_dir(5 * sub["q"].numel() * sub["q"].element_size())
+    try:
+        save_meta(d, w.io, w.D)
+        for t in ("q", "k", "v", "g", "beta"):
+            save_array(d, t, to_storage(sub[t], head_major=True))
+        for t in ("conv_w", "conv_state", "S0"):
+            save_array(d, t, to_storage(sub[t]))
+        done, elapsed, workers = time_pairs(d, [(0, h) for h in range(nh)], budget_s)
+    finally:
+        shutil.rmtree(d, ignore_errors=True)
+    pairs = [(b, h) for b in range(w.B) for h in range(w.H)]
+    tokens_equiv = w.B * w.T * done / len(pairs)
     return {"value": tokens_equiv / elapsed, "unit": "tokens/s", "cores": workers, "kind": "oracle",
-            "sample": f"{done} of {w.B * w.H} heads, full T={w.T} each (fp64 sequential oracle, "
-                      f"{elapsed:.1f} s); rate scaled to the whole {w.H}-head layer"}
-
-
-def _warm(_):
-    import numpy as np
-
-    from oracle import kda_reference
-    x = np.zeros((1, 4, 1, 16))
-    kda_reference(x, x, x, -np.ones_like(x), np.zeros((1, 4, 1)))
-    return 0
+            "host_cores_visible": host_cores(),
+            "sample": f"{done} of {len(pairs)} (sequence, head) pairs of {w.name}, full T={w.T} "
+                      f"each (fp64 sequential oracle, {elapsed:.1f} s in {workers} host processes "
+                      f"of one thread; the pool is capped at 16, one GPU's share of the host); "
+                      f"rate scaled to the whole {w.H}-head layer"}
 
 
 def time_prefill(kda, torch, a, ws, stream, steps, warmup):
@@ -247,6 +234,46 @@ def time_prefill(kda, torch, a, ws, stream, steps, warmup):
     return ms, stage_ms
 
 
+def measure_prefill(kda, torch, w, args, stream, dev, keep_inputs=False):
+    """One workload's prefill: throughput, per-kernel times and rooflines."""
+    from kda_inputs import make_inputs
+    inp = make_inputs(w, seed=args.seed, device=dev)
+    o = torch.empty_like(inp["q"])
+    S_T = torch.empty(w.B, w.H, w.D, w.D, dtype=torch.float32, device=dev)
+    cso = torch.empty(w.B, 3, 3, w.H * w.D, dtype=inp["q"].dtype, device=dev)
+    a = kda.prefill_args(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["conv_w"],
+                         inp["conv_state"], inp["S0"], o, S_T, cso, chunk=w.chunk)
+    ws = torch.empty(kda.kda_prefill_workspace_bytes(a), dtype=torch.uint8, device=dev)
+    print(f"timing {w.name}: B={w.B} T={w.T} H={w.H} D={w.D} {w.io}", file=sys.stderr, flush=True)
+    ms, stage_ms = time_prefill(kda, torch, a, ws, stream, args.steps, args.warmup)
+    nb = path_bytes(w)
+    db = design_bytes(w)
+    flops = prefill_flops(w)
+    dom = 0 if stage_ms[0] >= stage_ms[1] else 1
+    kname = STAGE_NAMES[dom]
+    achieved = nb / (stage_ms[dom] / 1e3)
+    roofline = {"bound": "hbm", "kernel": kname,
+                "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK, "traffic": traffic_for(w.name, kname),
+                "algorithmic_bytes": nb, "mean_launch_ms": stage_ms[dom],
+                "design_bytes": db[kname],
+                "design_bytes_frac": db[kname] / (stage_ms[dom] / 1e3) / HBM_PEAK}
+    t = ms / 1e3
+    path = {"algorithmic_bytes": nb, "achieved_GBps": nb / t / 1e9, "hbm_frac": nb / t / HBM_PEAK,
+            "mfma_frac_useful": flops / t / BF16_PEAK,
+            "attainable_frac": max(flops / BF16_PEAK, nb / HBM_PEAK) / t,
+            "stage_ms": {STAGE_NAMES[i]: stage_ms[i] for i in range(2)}}
+    out = {"workload": w.name, "config": {"B": w.B, "T": w.T, "H": w.H, "D": w.D, "chunk": w.chunk,
+                                          "io": w.io, "state": "fp32", "S0": w.s0_std > 0},
+           "ms_per_step": ms, "tokens_per_s": w.B * w.T / t, "roofline": roofline, "path": path}
+    del ws, o, S_T, cso, a
+    if not keep_inputs:
+        del inp
+        inp = None
+    torch.cuda.empty_cache()
+    return out, inp
+
+
 def stages_leg(kda, torch, w, wd, args, stream, dev, plain_ms, plain_dms):
     """Prefill and decode with every optional stage on (same workloads and seeds)."""
     from kda_inputs import make_inputs, make_stage_inputs
@@ -262,19 +289,19 @@ def stages_leg(kda, torch, w, wd, args, stream, dev, plain_ms, plain_dms):
     ws = torch.empty(kda.kda_prefill_workspace_bytes(a), dtype=torch.uint8, device=dev)
     ms, stage_ms = time_prefill(kda, torch, a, ws, stream, args.steps, args.warmup)
     sb = stage_bytes(w)
-    path_bytes = prefill_bytes(w)["path"] + sb["path_extra"]
+    pb = path_bytes(w) + sb["path_extra"]
     out_ms = stage_ms[2]
     out = None
     if out_ms > 0.001:
         out = {"bound": "hbm", "kernel": STAGE_NAMES[2], "algorithmic_bytes": sb["out_pass"],
                "achieved": sb["out_pass"] / (out_ms / 1e3) / 1e9, "peak": HBM_PEAK / 1e9,
                "unit": "GB/s", "frac": sb["out_pass"] / (out_ms / 1e3) / HBM_PEAK,
-               "traffic": traffic_for(STAGE_NAMES[2]), "mean_launch_ms": out_ms}
+               "traffic": traffic_for(w.name, STAGE_NAMES[2]), "mean_launch_ms": out_ms}
     prefill = {"workload": w.name, "ms_per_step": ms, "tokens_per_s": w.B * w.T / (ms / 1e3),
                "extra_ms_vs_plain": ms - plain_ms,
                "output_stage_in_walk": out_ms <= 0.001,
                "stage_ms": {STAGE_NAMES[i]: stage_ms[i] for i in range(len(STAGE_NAMES))},
-               "path_hbm_frac": path_bytes / (ms / 1e3) / HBM_PEAK, "out_pass_roofline": out}
+               "path_hbm_frac": pb / (ms / 1e3) / HBM_PEAK, "out_pass_roofline": out}
     del ws, inp, st, o, S_T, cso
     torch.cuda.empty_cache()
 
@@ -286,17 +313,7 @@ def stages_leg(kda, torch, w, wd, args, stream, dev, plain_ms, plain_dms):
                          dinp["conv_w"], dinp["conv_state"], A_log=dst["A_log"],
                          dt_bias=dst["dt_bias"], beta_logits=True, o_norm_w=dst["o_norm_w"],
                          o_gate=dst["o_gate"])
-    for _ in range(args.warmup):
-        kda.kda_decode_raw(da, stream)
-    torch.cuda.synchronize()
-    d0 = torch.cuda.Event(enable_timing=True)
-    d1 = torch.cuda.Event(enable_timing=True)
-    d0.record(stream)
-    for _ in range(args.steps):
-        kda.kda_decode_raw(da, stream)
-    d1.record(stream)
-    torch.cuda.synchronize()
-    dms = d0.elapsed_time(d1) / args.steps
+    dms = time_decode(kda, torch, da, stream, args.steps, args.warmup)
     dbytes = decode_bytes(wd) + wd.B * wd.H * wd.D * esize(wd.io) + (wd.H + wd.H * wd.D + wd.D) * 4
     decode = {"workload": wd.name, "ms_per_step": dms, "seq_per_s": wd.B / (dms / 1e3),
               "extra_ms_vs_plain": dms - plain_dms,
@@ -308,6 +325,20 @@ def stages_leg(kda, torch, w, wd, args, stream, dev, plain_ms, plain_dms):
     torch.cuda.empty_cache()
     return {"what": "raw-projection decay and beta, output RMSNorm + sigmoid gate",
             "prefill": prefill, "decode": decode}
+
+
+def time_decode(kda, torch, da, stream, steps, warmup):
+    for _ in range(warmup):
+        kda.kda_decode_raw(da, stream)
+    torch.cuda.synchronize()
+    d0 = torch.cuda.Event(enable_timing=True)
+    d1 = torch.cuda.Event(enable_timing=True)
+    d0.record(stream)
+    for _ in range(steps):
+        kda.kda_decode_raw(da, stream)
+    d1.record(stream)
+    torch.cuda.synchronize()
+    return d0.elapsed_time(d1) / steps
 
 
 def backward_leg(kda, torch, w, args, stream, dev, plain_ms):
@@ -341,7 +372,7 @@ def backward_leg(kda, torch, w, args, stream, dev, plain_ms):
     e1.record(stream)
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
-    nb = backward_bytes(w)["path"]
+    nb = backward_bytes(w)
     out = {"workload": w.name, "ms_per_step": ms, "tokens_per_s": w.B * w.T / (ms / 1e3),
            "ratio_to_forward": ms / plain_ms, "workspace_bytes": ws.numel(),
            "path_bytes": nb, "path_GBps": nb / (ms / 1e3) / 1e9,
@@ -371,7 +402,7 @@ def packed_leg(kda, torch, w, args, stream, dev, plain_ms):
     ws = torch.empty(kda.kda_prefill_workspace_bytes(a), dtype=torch.uint8, device=dev)
     ms, stage_ms = time_prefill(kda, torch, a, ws, stream, args.steps, args.warmup)
     tokens = sum(lengths)
-    nb = prefill_bytes(w)["path"]
+    nb = path_bytes(w)
     out = {"workload": f"{w.name} packed as {N} sequences", "lengths": lengths, "ms_per_step": ms,
            "tokens_per_s": tokens / (ms / 1e3), "ms_vs_unpacked": ms - plain_ms,
            "stage_ms": {STAGE_NAMES[i]: stage_ms[i] for i in range(len(STAGE_NAMES))},
@@ -381,12 +412,156 @@ def packed_leg(kda, torch, w, args, stream, dev, plain_ms):
     return out
 
 
+# ---------------------------------------------------------------- profiles
+# One profile of a workload is four rocprofv3 runs of this script (the kernel
+# trace with per-kernel statistics, then one counter per run: HBM bytes fetched,
+# HBM bytes written, and the matrix-core / VALU counters); a plain copy kernel of
+# known size runs in each (kda_prefill with T = 0 copies S0 to S_T) to calibrate
+# the byte counters.
+CALIB_KERNEL = "kda_copy_state_kernel"
+CALIB_MIB = 1024
+SQ_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU",
+               "SQ_ACTIVE_INST_VALU", "SQ_BUSY_CYCLES", "SQ_WAVES", "GRBM_GUI_ACTIVE"]
+
+
+def profile_args(workload: str) -> str:
+    return (f"--workload {workload} --also none --no-stages --cpu-budget 0 --steps 5 "
+            f"--warmup 20 --calib-copy-mib {CALIB_MIB}")
+
+
+def profile_commands(d: str, workload: str) -> dict:
+    args = profile_args(workload)
+    run = f"python3 bench.py {args}"
+    return {
+        "trace": f"rocprofv3 --kernel-trace --stats -d {d}/trace -o trace -- {run}",
+        "fetch": f"rocprofv3 --pmc FETCH_SIZE -d {d}/fetch -o pmc -- {run}",
+        "write": f"rocprofv3 --pmc WRITE_SIZE -d {d}/write -o pmc -- {run}",
+        "sq": f"rocprofv3 --pmc {' '.join(SQ_COUNTERS)} -d {d}/sq -o pmc -- {run}",
+    }
+
+
+def _csv_rows(pattern: str):
+    import csv
+    rows = []
+    for p in sorted(glob.glob(pattern, recursive=True)):
+        with open(p, newline="") as f:
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+def _short(name: str) -> str:
+    """Kernel name without template arguments or parameters (kda_..._kernel)."""
+    import re
+    m = re.search(r"(kda_[a-z0-9_]+_kernel)", name)
+    return m.group(1) if m else name
+
+
+def summarize_rocprof(d: str, workload: str, out_dir: str) -> dict:
+    """Turn the four runs of profile_commands(d, workload) into one summary file
+    per kernel under out_dir (named for the kernel and the workload) and this
+    workload's entry of out_dir/traffic.json.  Returns the traffic entry."""
+    cmds = profile_commands(d, workload)
+    trace = _csv_rows(os.path.join(d, "trace", "**", "*kernel_trace.csv"))
+    stats = {}
+    for r in trace:
+        k = _short(r["Kernel_Name"])
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3  # us
+        s = stats.setdefault(k, {"full_name": r["Kernel_Name"], "durations": [],
+                                 "grid": int(r.get("Grid_Size_X", 0) or 0),
+                                 "wg": int(r.get("Workgroup_Size_X", 0) or 0),
+                                 "lds": int(r.get("Group_Segment_Size", r.get("LDS_Block_Size", 0)) or 0),
+                                 "scratch": int(r.get("Private_Segment_Size", 0) or 0)})
+        s["durations"].append(dur)
+
+    def counter(sub, name):
+        per = {}
+        for r in _csv_rows(os.path.join(d, sub, "**", "*counter_collection.csv")):
+            if r["Counter_Name"] != name:
+                continue
+            k = _short(r["Kernel_Name"])
+            per.setdefault(k, {}).setdefault(r["Dispatch_Id"], 0.0)
+            per[k][r["Dispatch_Id"]] += float(r["Counter_Value"])
+        return {k: sum(v.values()) / len(v) for k, v in per.items()}
+
+    fetch = counter("fetch", "FETCH_SIZE")
+    write = counter("write", "WRITE_SIZE")
+    sq = {c: counter("sq", c) for c in SQ_COUNTERS}
+    calib_bytes = (CALIB_MIB << 20) // (128 * 128 * 4) * (128 * 128 * 4)
+    ff = calib_bytes / (fetch[CALIB_KERNEL] * 1024) if fetch.get(CALIB_KERNEL) else None
+    wf = calib_bytes / (write[CALIB_KERNEL] * 1024) if write.get(CALIB_KERNEL) else None
+    shash = source_hash()
+    kernels = {}
+    os.makedirs(out_dir, exist_ok=True)
+    for k, s in sorted(stats.items()):
+        durs = s["durations"]
+        avg = sum(durs) / len(durs)
+        lines = [f"# {k} -- {workload}", "",
+                 f"kernel: {s['full_name']}",
+                 f"source hash of the kernel sources (bench.py KERNEL_SOURCES): {shash}", "",
+                 "## Kernel trace (rocprofv3 --kernel-trace --stats)",
+                 f"command: {cmds['trace']}",
+                 f"dispatches: {len(durs)}   grid: {s['grid']} work-items, workgroup {s['wg']}   "
+                 f"LDS: {s['lds']} B   scratch: {s['scratch']} B/lane",
+                 f"duration avg: {avg:.2f} us   min: {min(durs):.2f} us   max: {max(durs):.2f} us"]
+        entry = {"avg_us": avg, "dispatches": len(durs)}
+        if k in fetch and k in write and ff and wf:
+            nbytes = fetch[k] * 1024 * ff + write[k] * 1024 * wf
+            entry.update({"fetch_KiB": fetch[k], "write_KiB": write[k], "bytes_per_launch": nbytes})
+            lines += ["", "## HBM traffic (rocprofv3 --pmc, one counter per run)",
+                      f"commands: {cmds['fetch']}", f"          {cmds['write']}",
+                      f"FETCH_SIZE: {fetch[k]:.1f} KiB/dispatch   WRITE_SIZE: {write[k]:.1f} KiB/dispatch",
+                      f"calibration ({CALIB_KERNEL}, {calib_bytes} B read and {calib_bytes} B written "
+                      f"per launch): FETCH_SIZE x {ff:.3f}, WRITE_SIZE x {wf:.3f} give bytes",
+                      f"HBM bytes per launch: read {fetch[k] * 1024 * ff / 1e6:.1f} MB + written "
+                      f"{write[k] * 1024 * wf / 1e6:.1f} MB = {nbytes / 1e6:.1f} MB",
+                      f"achieved on those bytes: {nbytes / (avg * 1e-6) / 1e9:.0f} GB/s = "
+                      f"{nbytes / (avg * 1e-6) / HBM_PEAK * 100:.1f}% of 8 TB/s"]
+        if all(k in sq[c] for c in SQ_COUNTERS):
+            gui = sq["GRBM_GUI_ACTIVE"][k] / 8  # summed over the 8 XCDs
+            simd_cycles = gui * 1024
+            mfma_busy = sq["SQ_VALU_MFMA_BUSY_CYCLES"][k] / simd_cycles
+            bf16_flops = sq["SQ_INSTS_VALU_MFMA_MOPS_BF16"][k] * 512
+            waves = sq["SQ_WAVES"][k]
+            entry.update({"mfma_busy": mfma_busy, "bf16_tflops": bf16_flops / (avg * 1e-6) / 1e12,
+                          "valu_insts_per_wave": sq["SQ_INSTS_VALU"][k] / max(waves, 1),
+                          "valu_active_frac": sq["SQ_ACTIVE_INST_VALU"][k] * 4 / simd_cycles,
+                          "clock_GHz": gui / (avg * 1e-6) / 1e9})
+            lines += ["", "## Matrix-core and VALU counters (rocprofv3 --pmc)",
+                      f"command: {cmds['sq']}",
+                      "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); "
+                      "bf16 MFMA flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; VALU active = "
+                      "SQ_ACTIVE_INST_VALU x 4 / SIMD cycles",
+                      f"clock {entry['clock_GHz']:.2f} GHz   MFMA busy {mfma_busy * 100:.1f}%   "
+                      f"bf16 MFMA {entry['bf16_tflops']:.1f} TFLOP/s = "
+                      f"{entry['bf16_tflops'] * 1e12 / BF16_PEAK * 100:.2f}% of 2.5 PFLOP/s   "
+                      f"VALU instructions per wave {entry['valu_insts_per_wave']:.0f}   "
+                      f"VALU active {entry['valu_active_frac'] * 100:.1f}%"]
+        kernels[k] = entry
+        with open(os.path.join(out_dir, f"{k}.{workload}.txt"), "w") as f:
+            f.write("\n".join(lines) + "\n")
+    tpath = os.path.join(out_dir, "traffic.json")
+    try:
+        with open(tpath) as f:
+            tj = json.load(f)
+    except (OSError, ValueError):
+        tj = {}
+    tj.setdefault("workloads", {})
+    tj["calibration"] = {"kernel": CALIB_KERNEL, "bytes_read_and_written": calib_bytes}
+    tj["workloads"][workload] = {"source_hash": shash, "fetch_factor": ff, "write_factor": wf,
+                                 "commands": cmds, "kernels": kernels}
+    with open(tpath, "w") as f:
+        json.dump(tj, f, indent=1)
+    return tj["workloads"][workload]
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="prefill-4k")
+    ap.add_argument("--workload", default=HEADLINE)
+    ap.add_argument("--also", default=ALSO, help="comma-separated prefill workloads timed beside "
+                                                 "the headline ('none' for none)")
     ap.add_argument("--decode-workload", default="decode-b256")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle timing (0 = skip)")
     ap.add_argument("--seed", type=int, default=0)
@@ -396,7 +571,21 @@ def main(argv=None) -> int:
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run the library's plain state-copy kernel (kda_prefill with T=0) "
                          "on this many MiB, to calibrate HBM byte counters")
+    ap.add_argument("--profile-commands", metavar="DIR",
+                    help="print the rocprofv3 commands of a profile of --workload into DIR and exit")
+    ap.add_argument("--summarize-rocprof", metavar="DIR",
+                    help="summarize a profile of --workload taken by those commands into profiles/")
     args = ap.parse_args(argv)
+    if args.profile_commands:
+        for c in profile_commands(args.profile_commands.rstrip("/"), args.workload).values():
+            print(c)
+        return 0
+    if args.summarize_rocprof:
+        e = summarize_rocprof(args.summarize_rocprof.rstrip("/"), args.workload,
+                              os.path.join(ROOT, "profiles"))
+        print(json.dumps({k: {kk: vv for kk, vv in v.items()} for k, v in e["kernels"].items()},
+                         indent=1))
+        return 0
     if args.gpus != 1:
         print("bench.py measures one GPU: the KDA mixer shards over (sequence, head) with no "
               "collective, so only --gpus 1 is run here", file=sys.stderr)
@@ -409,36 +598,12 @@ def main(argv=None) -> int:
 
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
-    w = WORKLOADS[args.workload]
-    inp = make_inputs(w, seed=args.seed, device=dev)
-    o = torch.empty_like(inp["q"])
-    S_T = torch.empty(w.B, w.H, w.D, w.D, dtype=torch.float32, device=dev)
-    cso = torch.empty(w.B, 3, 3, w.H * w.D, dtype=inp["q"].dtype, device=dev)
-    a = kda.prefill_args(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["conv_w"],
-                         inp["conv_state"], inp["S0"], o, S_T, cso, chunk=w.chunk)
-    ws = torch.empty(kda.kda_prefill_workspace_bytes(a), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
-
-    ms, stage_ms = time_prefill(kda, torch, a, ws, stream, args.steps, args.warmup)
-    tokens_per_s = w.B * w.T / (ms / 1e3)
-
-    nb = prefill_bytes(w)
-    names = STAGE_NAMES
-    dom = 0 if stage_ms[0] >= stage_ms[1] else 1
-    dom_bytes = nb["prep"] if dom == 0 else nb["state"]
-    achieved = dom_bytes / (stage_ms[dom] / 1e3)
-    roofline = {"bound": "hbm", "kernel": names[dom], "achieved": achieved / 1e9,
-                "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": achieved / HBM_PEAK,
-                "traffic": traffic_for(names[dom]), "algorithmic_bytes": dom_bytes,
-                "mean_launch_ms": stage_ms[dom]}
-    flops = prefill_flops(w)
-    path = {"algorithmic_bytes": nb["path"], "achieved_GBps": nb["path"] / (ms / 1e3) / 1e9,
-            "hbm_frac": nb["path"] / (ms / 1e3) / HBM_PEAK,
-            "mfma_frac_useful": flops / (ms / 1e3) / BF16_PEAK,
-            "stage_ms": {names[i]: stage_ms[i] for i in range(2)}}
-    plain_ms = ms
-    del ws, inp, o, S_T, cso
-    torch.cuda.empty_cache()
+    w = WORKLOADS[args.workload]
+    head, _ = measure_prefill(kda, torch, w, args, stream, dev)
+    others = {}
+    for name in [x for x in args.also.split(",") if x and x != "none" and x != w.name]:
+        others[name] = measure_prefill(kda, torch, WORKLOADS[name], args, stream, dev)[0]
 
     # ---- decode leg
     wd = WORKLOADS[args.decode_workload]
@@ -448,33 +613,29 @@ def main(argv=None) -> int:
     od = torch.empty_like(dinp["q"])
     da = kda.decode_args(dinp["q"], dinp["k"], dinp["v"], dinp["g"], dinp["beta"], S, od,
                          dinp["conv_w"], cs)
-    for _ in range(args.warmup):
-        kda.kda_decode_raw(da, stream)
-    torch.cuda.synchronize()
-    d0 = torch.cuda.Event(enable_timing=True)
-    d1 = torch.cuda.Event(enable_timing=True)
-    d0.record(stream)
-    for _ in range(args.steps):
-        kda.kda_decode_raw(da, stream)
-    d1.record(stream)
-    torch.cuda.synchronize()
-    dms = d0.elapsed_time(d1) / args.steps
+    print(f"timing {wd.name}", file=sys.stderr, flush=True)
+    dms = time_decode(kda, torch, da, stream, args.steps, args.warmup)
     dbytes = decode_bytes(wd)
     decode = {"metric": "KDA decode seq/s", "value": wd.B / (dms / 1e3), "unit": "seq/s",
               "ms_per_step": dms, "config": {"workload": wd.name, "B": wd.B, "H": wd.H, "D": wd.D},
               "roofline": {"bound": "hbm", "kernel": "kda_decode_kernel",
                            "achieved": dbytes / (dms / 1e3) / 1e9, "peak": HBM_PEAK / 1e9,
                            "unit": "GB/s", "frac": dbytes / (dms / 1e3) / HBM_PEAK,
-                           "traffic": traffic_for("kda_decode_kernel"),
+                           "traffic": traffic_for(wd.name, "kda_decode_kernel"),
                            "algorithmic_bytes": dbytes}}
-    del dinp, S, cs, od
+    del dinp, S, cs, od, da
     torch.cuda.empty_cache()
 
     stages = None
     if not args.no_stages:
-        stages = stages_leg(kda, torch, w, wd, args, stream, dev, plain_ms, dms)
-        stages["packed"] = packed_leg(kda, torch, w, args, stream, dev, plain_ms)
-        stages["backward"] = backward_leg(kda, torch, w, args, stream, dev, plain_ms)
+        ws4 = WORKLOADS[STAGES_WORKLOAD]
+        base = others.get(ws4.name) or (head if w.name == ws4.name else None)
+        base_ms = base["ms_per_step"] if base else float("nan")
+        print("timing the optional stages, packed sequences and the backward", file=sys.stderr,
+              flush=True)
+        stages = stages_leg(kda, torch, ws4, wd, args, stream, dev, base_ms, dms)
+        stages["packed"] = packed_leg(kda, torch, ws4, args, stream, dev, base_ms)
+        stages["backward"] = backward_leg(kda, torch, ws4, args, stream, dev, base_ms)
 
     if args.calib_copy_mib > 0:
         # kda_prefill with T = 0 copies S0 to S_T with one plain copy kernel
@@ -494,18 +655,20 @@ def main(argv=None) -> int:
 
     cpu = None
     if args.cpu_budget > 0:
+        print(f"timing the oracle on the host (~{args.cpu_budget:.0f} s)", file=sys.stderr,
+              flush=True)
         cinp = make_inputs(w, seed=args.seed, device=dev)
         cpu = cpu_baseline(w, cinp, args.cpu_budget)
         del cinp
 
     line = {
-        "metric": "KDA tokens/s per GPU (prefill, H=96 d=128) + decode seq/s; % of roofline",
-        "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": w.io, "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "D": w.D, "chunk": w.chunk,
-                   "io": w.io, "state": "fp32"},
-        "roofline": roofline, "path": path, "decode": decode, "stages": stages,
+        "metric": METRIC,
+        "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": head["ms_per_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": w.io, "data": "synthetic",
+        "config": dict({"workload": w.name}, **head["config"]),
+        "roofline": head["roofline"], "path": head["path"],
+        "prefill_configs": others, "decode": decode, "stages": stages,
         "cpu_baseline": cpu,
         "source_hash": source_hash(),
     }
