@@ -424,6 +424,11 @@ SQ_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_I
                "SQ_ACTIVE_INST_VALU", "SQ_BUSY_CYCLES", "SQ_WAVES", "GRBM_GUI_ACTIVE"]
 
 
+# kernels that a profiled run also launches outside the prefill of its workload
+OTHER_LEG_WORKLOAD = {"kda_decode_kernel": "decode-b256",
+                      CALIB_KERNEL: f"calibration-copy-{CALIB_MIB}-MiB"}
+
+
 def profile_args(workload: str) -> str:
     return (f"--workload {workload} --also none --no-stages --cpu-budget 0 --steps 5 "
             f"--warmup 20 --calib-copy-mib {CALIB_MIB}")
@@ -433,10 +438,10 @@ def profile_commands(d: str, workload: str) -> dict:
     args = profile_args(workload)
     run = f"python3 bench.py {args}"
     return {
-        "trace": f"rocprofv3 --kernel-trace --stats -d {d}/trace -o trace -- {run}",
-        "fetch": f"rocprofv3 --pmc FETCH_SIZE -d {d}/fetch -o pmc -- {run}",
-        "write": f"rocprofv3 --pmc WRITE_SIZE -d {d}/write -o pmc -- {run}",
-        "sq": f"rocprofv3 --pmc {' '.join(SQ_COUNTERS)} -d {d}/sq -o pmc -- {run}",
+        "trace": f"rocprofv3 --kernel-trace --stats -f csv -d {d}/trace -o trace -- {run}",
+        "fetch": f"rocprofv3 --pmc FETCH_SIZE -f csv -d {d}/fetch -o pmc -- {run}",
+        "write": f"rocprofv3 --pmc WRITE_SIZE -f csv -d {d}/write -o pmc -- {run}",
+        "sq": f"rocprofv3 --pmc {' '.join(SQ_COUNTERS)} -f csv -d {d}/sq -o pmc -- {run}",
     }
 
 
@@ -465,12 +470,17 @@ def summarize_rocprof(d: str, workload: str, out_dir: str) -> dict:
     stats = {}
     for r in trace:
         k = _short(r["Kernel_Name"])
+        if not k.startswith("kda_"):
+            continue  # torch's input generation
         dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3  # us
+        col = lambda *names: next((int(float(r[n])) for n in names if r.get(n) not in (None, "")), 0)
         s = stats.setdefault(k, {"full_name": r["Kernel_Name"], "durations": [],
-                                 "grid": int(r.get("Grid_Size_X", 0) or 0),
-                                 "wg": int(r.get("Workgroup_Size_X", 0) or 0),
-                                 "lds": int(r.get("Group_Segment_Size", r.get("LDS_Block_Size", 0)) or 0),
-                                 "scratch": int(r.get("Private_Segment_Size", 0) or 0)})
+                                 "grid": col("Grid_Size_X", "Grid_Size"),
+                                 "wg": col("Workgroup_Size_X", "Workgroup_Size"),
+                                 "lds": col("LDS_Block_Size", "Group_Segment_Size"),
+                                 "scratch": col("Scratch_Size", "Private_Segment_Size"),
+                                 "vgpr": col("VGPR_Count", "Arch_VGPR_Count"),
+                                 "agpr": col("Accum_VGPR_Count")})
         s["durations"].append(dur)
 
     def counter(sub, name):
@@ -493,15 +503,18 @@ def summarize_rocprof(d: str, workload: str, out_dir: str) -> dict:
     kernels = {}
     os.makedirs(out_dir, exist_ok=True)
     for k, s in sorted(stats.items()):
+        # kernels of the other legs of the profiled run are filed under their own workload
+        wl = OTHER_LEG_WORKLOAD.get(k, workload)
         durs = s["durations"]
         avg = sum(durs) / len(durs)
-        lines = [f"# {k} -- {workload}", "",
+        lines = [f"# {k} -- {wl}", "",
                  f"kernel: {s['full_name']}",
                  f"source hash of the kernel sources (bench.py KERNEL_SOURCES): {shash}", "",
                  "## Kernel trace (rocprofv3 --kernel-trace --stats)",
                  f"command: {cmds['trace']}",
                  f"dispatches: {len(durs)}   grid: {s['grid']} work-items, workgroup {s['wg']}   "
-                 f"LDS: {s['lds']} B   scratch: {s['scratch']} B/lane",
+                 f"LDS: {s['lds']} B   scratch: {s['scratch']} B/lane   VGPRs: {s['vgpr']} "
+                 f"(+{s['agpr']} AGPRs)",
                  f"duration avg: {avg:.2f} us   min: {min(durs):.2f} us   max: {max(durs):.2f} us"]
         entry = {"avg_us": avg, "dispatches": len(durs)}
         if k in fetch and k in write and ff and wf:
@@ -536,8 +549,8 @@ def summarize_rocprof(d: str, workload: str, out_dir: str) -> dict:
                       f"{entry['bf16_tflops'] * 1e12 / BF16_PEAK * 100:.2f}% of 2.5 PFLOP/s   "
                       f"VALU instructions per wave {entry['valu_insts_per_wave']:.0f}   "
                       f"VALU active {entry['valu_active_frac'] * 100:.1f}%"]
-        kernels[k] = entry
-        with open(os.path.join(out_dir, f"{k}.{workload}.txt"), "w") as f:
+        kernels.setdefault(wl, {})[k] = entry
+        with open(os.path.join(out_dir, f"{k}.{wl}.txt"), "w") as f:
             f.write("\n".join(lines) + "\n")
     tpath = os.path.join(out_dir, "traffic.json")
     try:
@@ -547,8 +560,9 @@ def summarize_rocprof(d: str, workload: str, out_dir: str) -> dict:
         tj = {}
     tj.setdefault("workloads", {})
     tj["calibration"] = {"kernel": CALIB_KERNEL, "bytes_read_and_written": calib_bytes}
-    tj["workloads"][workload] = {"source_hash": shash, "fetch_factor": ff, "write_factor": wf,
-                                 "commands": cmds, "kernels": kernels}
+    for wl, ks in kernels.items():
+        tj["workloads"][wl] = {"source_hash": shash, "fetch_factor": ff, "write_factor": wf,
+                               "commands": cmds, "kernels": ks}
     with open(tpath, "w") as f:
         json.dump(tj, f, indent=1)
     return tj["workloads"][workload]
