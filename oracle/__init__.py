@@ -13,11 +13,13 @@ from .kda_oracle import (  # noqa: F401
     kda_gate,
     kda_reference,
     kda_reference_backward,
+    kda_reference_backward_packed,
     kda_reference_decode_step,
     kda_reference_heads,
     kda_reference_packed,
     l2_normalize,
     output_gate_norm,
+    output_gate_norm_backward,
     rms_norm,
     short_conv,
     sigmoid,

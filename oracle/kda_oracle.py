@@ -156,6 +156,43 @@ def output_gate_norm(o: np.ndarray, o_norm_w: np.ndarray | None = None,
     return y
 
 
+def output_gate_norm_backward(o: np.ndarray, dy: np.ndarray, o_norm_w: np.ndarray | None = None,
+                             gate: np.ndarray | None = None, eps: float = RMS_EPS):
+    """Reverse of ``output_gate_norm``: given the stage's input o [..., D] and the
+    gradient dy of its output, returns (do, do_norm_w [D] or None, dgate or None).
+
+    With r = 1 / sqrt(mean_c o_c^2 + eps), n = o r, a = n w (a = o without the
+    norm), s = sigmoid(gate), y = a s (y = a without the gate):
+        dgate = dy a s (1 - s),   da = dy s,
+        do_norm_w = sum over rows of da n,   dn = da w,
+        do = r (dn - n mean_c(dn n))   (the RMSNorm's Jacobian applied to dn).
+    """
+    o = np.asarray(o, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    if o_norm_w is not None:
+        w = np.asarray(o_norm_w, dtype=np.float64)
+        r = 1.0 / np.sqrt(np.mean(o * o, axis=-1, keepdims=True) + eps)
+        n = o * r
+        a = n * w
+    else:
+        a = o
+    dgate = None
+    if gate is not None:
+        s = sigmoid(gate)
+        dgate = dy * a * s * (1.0 - s)
+        da = dy * s
+    else:
+        da = dy
+    dw = None
+    if o_norm_w is not None:
+        dw = np.sum((da * n).reshape(-1, o.shape[-1]), axis=0)
+        dn = da * w
+        do = r * (dn - n * np.mean(dn * n, axis=-1, keepdims=True))
+    else:
+        do = da
+    return do, dw, dgate
+
+
 def softplus(x: np.ndarray) -> np.ndarray:
     """softplus(x) = ln(1 + e^x), elementwise, fp64 (as log(e^0 + e^x), which does
     not overflow for large x)."""
@@ -320,16 +357,20 @@ def conv_norm_reference(q, k, v, conv_w, conv_state=None, l2norm_qk=True, eps=L2
 
 
 def kda_reference_backward(q, k, v, g, beta, do, dS_T=None, conv_w=None, conv_state=None,
-                           S0=None, scale=1.0, l2norm_qk=True, eps=L2_EPS):
+                           S0=None, scale=1.0, l2norm_qk=True, eps=L2_EPS, o_norm_w=None,
+                           o_gate=None, o_norm_eps=RMS_EPS, A_log=None, dt_bias=None,
+                           beta_sigmoid=False):
     """Gradients of the mixer by reverse-mode differentiation of its sequential
     definition (``kda_reference``), fp64.
 
     The scalar differentiated is  L = sum(o * do) + sum(S_T * dS_T)  (dS_T None: 0),
     i.e. do and dS_T are the upstream gradients of o and S_T.  Inputs as
-    ``kda_reference``.  Returns a dict of gradients with the inputs' shapes: dq, dk,
-    dv (of the raw inputs), dg, dbeta, dS0 (zeros-shaped when S0 is None: the
-    gradient of a zero initial state), dconv_w and dconv_state (None without the
-    convolution).
+    ``kda_reference``, with its optional stages.  Returns a dict of gradients with the
+    inputs' shapes: dq, dk, dv (of the raw inputs), dg, dbeta (of g and beta as given:
+    of the gate projection f with A_log, of the logits with beta_sigmoid), dS0
+    (zeros-shaped when S0 is None: the gradient of a zero initial state), dconv_w and
+    dconv_state (None without the convolution), do_norm_w, do_gate, dA_log and
+    ddt_bias (None when their stage is off).
 
     Reverse of one step (S_bar = Diag(alpha) S, u = beta (v - S_bar^T k),
     S' = S_bar + k u^T, o = scale S'^T q), with G the gradient of S':
@@ -342,10 +383,20 @@ def kda_reference_backward(q, k, v, g, beta, do, dS_T=None, conv_w=None, conv_st
     dy = dz / n - y (y . dz) / n^3), SiLU (x sigmoid(x), derivative
     sigmoid(x) (1 + x (1 - sigmoid(x)))) and the convolution (a correlation, whose
     adjoint sends dy[t] back to the inputs t-3 .. t and to the filter taps).
+    The optional stages: the output stage first (``output_gate_norm_backward``, on
+    the mixer's output before it); the activations last, with g = -exp(A_log) sp,
+    sp = softplus(f + dt_bias): df = dg (-exp(A_log)) sigmoid(f + dt_bias),
+    dA_log = sum dg g, ddt_bias = sum df; and dbeta_logit = dbeta beta (1 - beta).
     """
     q, k, v, g, do = (np.asarray(a, dtype=np.float64) for a in (q, k, v, g, do))
     beta = np.asarray(beta, dtype=np.float64)
     B, T, H, D = q.shape
+    f = None
+    if A_log is not None:
+        f = g
+        g = kda_gate(f, A_log, dt_bias)
+    if beta_sigmoid:
+        beta = sigmoid(beta)
     _check_decay(g)
     HD = H * D
     raw = (q, k, v)
@@ -372,9 +423,13 @@ def kda_reference_backward(q, k, v, g, beta, do, dS_T=None, conv_w=None, conv_st
     # forward, keeping the state before each step
     S = np.zeros((B, H, D, D)) if S0 is None else np.array(S0, dtype=np.float64)
     S_prev = np.empty((T, B, H, D, D))
+    o_pre = np.empty((B, T, H, D))
     for t in range(T):
         S_prev[t] = S
-        S, _ = gated_delta_step(S, qh[:, t], kh[:, t], vh[:, t], g[:, t], beta[:, t], scale)
+        S, o_pre[:, t] = gated_delta_step(S, qh[:, t], kh[:, t], vh[:, t], g[:, t], beta[:, t], scale)
+    do_norm_w = do_gate = None
+    if o_norm_w is not None or o_gate is not None:
+        do, do_norm_w, do_gate = output_gate_norm_backward(o_pre, do, o_norm_w, o_gate, o_norm_eps)
     # reverse
     G = np.zeros((B, H, D, D)) if dS_T is None else np.array(dS_T, dtype=np.float64)
     dqh, dkh, dvh = np.zeros_like(qh), np.zeros_like(kh), np.zeros_like(vh)
@@ -409,10 +464,19 @@ def kda_reference_backward(q, k, v, g, beta, do, dS_T=None, conv_w=None, conv_st
     else:
         dyq, dyk = dqh, dkh
     dys = [dyq, dyk, dvh]
+    extra = dict(do_norm_w=do_norm_w, do_gate=do_gate, dA_log=None, ddt_bias=None)
+    if A_log is not None:
+        rate = np.exp(np.asarray(A_log, dtype=np.float64)).reshape(H, 1)
+        z = f + np.asarray(dt_bias, dtype=np.float64).reshape(H, D)
+        extra["dA_log"] = np.sum(dg * g, axis=(0, 1, 3))
+        dg = dg * (-rate) * sigmoid(z)
+        extra["ddt_bias"] = np.sum(dg, axis=(0, 1)).reshape(H * D)
+    if beta_sigmoid:
+        dbeta = dbeta * beta * (1.0 - beta)
     if conv_w is None:
         dq_, dk_, dv_ = dys
         return dict(dq=dq_, dk=dk_, dv=dv_, dg=dg, dbeta=dbeta, dS0=dS0, dconv_w=None,
-                    dconv_state=None)
+                    dconv_state=None, **extra)
     dconv_w = np.zeros_like(cw)
     dhist = np.zeros_like(hist)
     dx = []
@@ -431,7 +495,7 @@ def kda_reference_backward(q, k, v, g, beta, do, dS_T=None, conv_w=None, conv_st
             dxi[b] = dxe[K - 1:]
         dx.append(dxi.reshape(B, T, H, D))
     return dict(dq=dx[0], dk=dx[1], dv=dx[2], dg=dg, dbeta=dbeta, dS0=dS0, dconv_w=dconv_w,
-                dconv_state=dhist)
+                dconv_state=dhist, **extra)
 
 
 def kda_reference_packed(q, k, v, g, beta, cu_seqlens, conv_w=None, conv_state=None, S0=None,
@@ -475,6 +539,54 @@ def kda_reference_packed(q, k, v, g, beta, cu_seqlens, conv_w=None, conv_state=N
         if tails is not None:
             tails[i] = ti[0]
     return o, S_out, tails
+
+
+def kda_reference_backward_packed(q, k, v, g, beta, cu_seqlens, do, dS_T=None, conv_w=None,
+                                  conv_state=None, S0=None, **kw):
+    """Gradients of ``kda_reference_packed``: each sequence's part by
+    ``kda_reference_backward`` on its own tokens, conv history and initial state
+    (nothing crosses a boundary, so nothing flows across one backwards either).
+
+    Shapes as ``kda_reference_packed``; do [1, T, H, D], dS_T [N, H, D, D] or None.
+    Per-token gradients go to their tokens, dS0 [N, H, D, D] and dconv_state
+    [N, 3, K-1, H*D] to their sequences; the shared parameters' gradients (dconv_w,
+    do_norm_w, dA_log, ddt_bias) are the sums over the sequences.
+    """
+    cu = [int(c) for c in cu_seqlens]
+    N = len(cu) - 1
+    B, T, H, D = np.asarray(q).shape
+    if B != 1 or cu[0] != 0 or cu[-1] != T or any(b < a for a, b in zip(cu, cu[1:])):
+        raise ValueError("packed sequences: B = 1 and offsets from 0 to T without decreasing")
+    o_gate = kw.pop("o_gate", None)
+    tok = {n: np.zeros((1, T, H, D)) for n in ("dq", "dk", "dv", "dg")}
+    tok["dbeta"] = np.zeros((1, T, H))
+    if o_gate is not None:
+        tok["do_gate"] = np.zeros((1, T, H, D))
+    out = dict(tok)
+    out["dS0"] = np.zeros((N, H, D, D))
+    out["dconv_state"] = None
+    shared = {}
+    for i in range(N):
+        sl = slice(cu[i], cu[i + 1])
+        part = lambda x: None if x is None else np.asarray(x)[:, sl]
+        one = lambda x: None if x is None else np.asarray(x)[i:i + 1]
+        gi = kda_reference_backward(part(q), part(k), part(v), part(g), part(beta), part(do),
+                                    one(dS_T), conv_w=conv_w, conv_state=one(conv_state),
+                                    S0=one(S0), o_gate=part(o_gate), **kw)
+        for n in tok:
+            out[n][:, sl] = gi[n]
+        out["dS0"][i] = gi["dS0"][0]
+        if gi["dconv_state"] is not None:
+            if out["dconv_state"] is None:
+                out["dconv_state"] = np.zeros((N,) + gi["dconv_state"].shape[1:])
+            out["dconv_state"][i] = gi["dconv_state"][0]
+        for n in ("dconv_w", "do_norm_w", "dA_log", "ddt_bias"):
+            if gi[n] is not None:
+                shared[n] = shared.get(n, 0.0) + gi[n]
+    for n in ("dconv_w", "do_norm_w", "dA_log", "ddt_bias"):
+        out[n] = shared.get(n)
+    out.setdefault("do_gate", None)
+    return out
 
 
 def kda_reference_heads(q, k, v, g, beta, heads, conv_w=None, conv_state=None, S0=None,

@@ -15,7 +15,8 @@ import pytest
 from scipy.special import expit
 
 from oracle import (conv_norm_reference, conv_tail, gated_delta_step, kda_reference,
-                    kda_reference_backward, kda_reference_decode_step, kda_reference_heads, kda_reference_packed,
+                    kda_reference_backward, kda_reference_backward_packed, kda_reference_decode_step,
+                    kda_reference_heads, kda_reference_packed, output_gate_norm_backward,
                     l2_normalize,
                     kda_gate, output_gate_norm, rms_norm, short_conv, sigmoid, silu,
                     softplus)
@@ -649,3 +650,170 @@ def test_backward_closed_form_without_writes():
                                rtol=1e-13, atol=1e-14)
     np.testing.assert_array_equal(gr["dk"], 0.0)
     np.testing.assert_array_equal(gr["dv"], 0.0)
+
+
+# ------------------------------------------- backward: optional stages, packing
+STAGE_SETS = {
+    "norm": dict(norm=True),
+    "gate": dict(gate=True),
+    "norm+gate": dict(norm=True, gate=True),
+    "act": dict(act=True),
+    "logits": dict(logits=True),
+    "all": dict(norm=True, gate=True, act=True, logits=True),
+}
+
+
+def _stage_case(rng, B, T, H, D, norm=False, gate=False, act=False, logits=False):
+    """Inputs of a call with the chosen optional stages: with act, g holds the raw
+    gate projection; with logits, beta holds logits."""
+    q, k, v, g, beta, conv_w, S0 = rand_case(rng, B=B, T=T, H=H, D=D)
+    args = dict(q=q, k=k, v=v, g=g, beta=beta, S0=S0, conv_w=conv_w,
+                cs=rng.standard_normal((B, 3, 3, H * D)))
+    kw = {}
+    if norm:
+        args["o_norm_w"] = 1.0 + 0.3 * rng.standard_normal(D)
+    if gate:
+        args["o_gate"] = rng.standard_normal((B, T, H, D))
+    if act:
+        args["g"] = rng.standard_normal((B, T, H, D))
+        args["A_log"] = rng.uniform(-1.0, 1.0, H)
+        args["dt_bias"] = 0.5 * rng.standard_normal(H * D)
+    if logits:
+        args["beta"] = rng.standard_normal((B, T, H))
+        kw["beta_sigmoid"] = True
+    return args, kw
+
+
+GRAD_OF = dict(q="dq", k="dk", v="dv", g="dg", beta="dbeta", S0="dS0", conv_w="dconv_w",
+               cs="dconv_state", o_norm_w="do_norm_w", o_gate="do_gate", A_log="dA_log",
+               dt_bias="ddt_bias")
+
+
+def _check_fd(rng, L, gr, args, h=1e-6, tol=1e-7, reps=2):
+    for n, gn in GRAD_OF.items():
+        if args.get(n) is None:
+            assert gr.get(gn) is None, n
+            continue
+        for _ in range(reps):
+            d = rng.standard_normal(np.shape(args[n]))
+            a1, a2 = dict(args), dict(args)
+            a1[n] = args[n] + h * d
+            a2[n] = args[n] - h * d
+            fd = (L(**a1) - L(**a2)) / (2 * h)
+            an = np.sum(gr[gn] * d)
+            assert abs(fd - an) <= tol * max(1.0, abs(fd)), (n, fd, an)
+
+
+@pytest.mark.parametrize("stages", list(STAGE_SETS))
+def test_backward_stages_match_finite_differences(stages):
+    """The optional stages in the backward: directional derivatives of
+    L = sum(o * do) + sum(S_T * dS_T) by central differences of the forward oracle
+    with the stages on, for every input, the stage parameters included."""
+    rng = np.random.default_rng(40 + list(STAGE_SETS).index(stages))
+    B, T, H, D, scale = 2, 6, 2, 4, 0.8
+    args, kw = _stage_case(rng, B, T, H, D, **STAGE_SETS[stages])
+    do = rng.standard_normal((B, T, H, D))
+    dST = rng.standard_normal((B, H, D, D))
+
+    def L(q, k, v, g, beta, S0, conv_w, cs, o_norm_w=None, o_gate=None, A_log=None, dt_bias=None):
+        o, S, _ = kda_reference(q, k, v, g, beta, conv_w=conv_w, conv_state=cs, S0=S0, scale=scale,
+                                o_norm_w=o_norm_w, o_gate=o_gate, A_log=A_log, dt_bias=dt_bias, **kw)
+        return np.sum(o * do) + np.sum(S * dST)
+
+    a = dict(args)
+    gr = kda_reference_backward(a.pop("q"), a.pop("k"), a.pop("v"), a.pop("g"), a.pop("beta"), do, dST,
+                                conv_w=a.pop("conv_w"), conv_state=a.pop("cs"), S0=a.pop("S0"),
+                                scale=scale, **a, **kw)
+    _check_fd(rng, L, gr, args)
+
+
+def test_output_stage_backward_elementwise():
+    """Every element of the output stage's three gradients, one central difference
+    each of output_gate_norm (norm and gate on, eps 1e-6)."""
+    rng = np.random.default_rng(50)
+    o = rng.standard_normal((3, 5))
+    w = 1.0 + 0.3 * rng.standard_normal(5)
+    z = rng.standard_normal((3, 5))
+    dy = rng.standard_normal((3, 5))
+    do, dw, dz = output_gate_norm_backward(o, dy, w, z)
+    L = lambda o, w, z: np.sum(output_gate_norm(o, w, z) * dy)
+    h = 1e-6
+    for name, x, gx in (("o", o, do), ("w", w, dw), ("z", z, dz)):
+        for idx in np.ndindex(x.shape):
+            x1, x2 = x.copy(), x.copy()
+            x1[idx] += h
+            x2[idx] -= h
+            a1 = dict(o=o, w=w, z=z); a2 = dict(o=o, w=w, z=z)
+            a1[name], a2[name] = x1, x2
+            fd = (L(**a1) - L(**a2)) / (2 * h)
+            assert abs(fd - gx[idx]) <= 1e-8 * max(1.0, abs(fd)), (name, idx, fd, gx[idx])
+
+
+def test_output_stage_backward_closed_forms():
+    """A zero gate halves everything that flows through it (sigmoid(0) = 1/2, slope
+    1/4); the norm's input gradient is orthogonal to its input at eps = 0 (the
+    normalised row does not change when o is scaled)."""
+    rng = np.random.default_rng(51)
+    o = rng.standard_normal((4, 6))
+    dy = rng.standard_normal((4, 6))
+    do, dw, dz = output_gate_norm_backward(o, dy, None, np.zeros((4, 6)))
+    np.testing.assert_allclose(do, dy / 2, rtol=1e-15, atol=0)
+    np.testing.assert_allclose(dz, dy * o / 4, rtol=1e-15, atol=0)
+    assert dw is None
+    w = rng.standard_normal(6)
+    do, dw, dz = output_gate_norm_backward(o, dy, w, None, eps=0.0)
+    np.testing.assert_allclose(np.sum(do * o, axis=-1), 0.0, atol=1e-12)
+    n = o / np.sqrt(np.mean(o * o, axis=-1, keepdims=True))
+    np.testing.assert_allclose(dw, np.sum(dy * n, axis=0), rtol=1e-13)
+    assert dz is None
+
+
+def test_activation_backward_closed_form():
+    """With A_log = 0 and dt_bias = 0 the decay is g = -softplus(f), whose derivative
+    is -sigmoid(f): the gate projection's gradient is the decay's times that, and
+    dA_log is sum(dg * g); beta logits scale dbeta by sigmoid'(b)."""
+    rng = np.random.default_rng(52)
+    B, T, H, D = 1, 4, 2, 3
+    q, k, v, f = (rng.standard_normal((B, T, H, D)) for _ in range(4))
+    b = rng.standard_normal((B, T, H))
+    do = rng.standard_normal((B, T, H, D))
+    ref = kda_reference_backward(q, k, v, -softplus(f), sigmoid(b), do)
+    gr = kda_reference_backward(q, k, v, f, b, do, A_log=np.zeros(H), dt_bias=np.zeros(H * D),
+                                beta_sigmoid=True)
+    np.testing.assert_allclose(gr["dg"], -ref["dg"] * sigmoid(f), rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(gr["dA_log"], np.sum(ref["dg"] * -softplus(f), axis=(0, 1, 3)),
+                               rtol=1e-13)
+    np.testing.assert_allclose(gr["ddt_bias"], np.sum(gr["dg"], axis=(0, 1)).reshape(-1), rtol=1e-13)
+    np.testing.assert_allclose(gr["dbeta"], ref["dbeta"] * sigmoid(b) * (1 - sigmoid(b)), rtol=1e-13,
+                               atol=1e-15)
+    for n in ("dq", "dk", "dv", "dS0"):
+        np.testing.assert_allclose(gr[n], ref[n], rtol=1e-13, atol=1e-15)
+
+
+@pytest.mark.parametrize("stages", ["none", "all"])
+def test_backward_packed_matches_finite_differences(stages):
+    """Packed sequences (an empty one, one shorter than the conv window, longer
+    ones): directional derivatives of the packed forward oracle for every input."""
+    rng = np.random.default_rng(60 + (stages == "all"))
+    cu = [0, 5, 5, 7, 13]
+    N, T, H, D, scale = 4, 13, 2, 4, 0.9
+    args, kw = _stage_case(rng, 1, T, H, D, **(STAGE_SETS["all"] if stages == "all" else {}))
+    args["S0"] = 0.1 * rng.standard_normal((N, H, D, D))
+    args["cs"] = rng.standard_normal((N, 3, 3, H * D))
+    do = rng.standard_normal((1, T, H, D))
+    dST = rng.standard_normal((N, H, D, D))
+
+    def L(q, k, v, g, beta, S0, conv_w, cs, o_norm_w=None, o_gate=None, A_log=None, dt_bias=None):
+        o, S, _ = kda_reference_packed(q, k, v, g, beta, cu, conv_w=conv_w, conv_state=cs, S0=S0,
+                                       scale=scale, o_norm_w=o_norm_w, o_gate=o_gate, A_log=A_log,
+                                       dt_bias=dt_bias, **kw)
+        return np.sum(o * do) + np.sum(S * dST)
+
+    a = dict(args)
+    gr = kda_reference_backward_packed(a.pop("q"), a.pop("k"), a.pop("v"), a.pop("g"), a.pop("beta"),
+                                       cu, do, dST, conv_w=a.pop("conv_w"), conv_state=a.pop("cs"),
+                                       S0=a.pop("S0"), scale=scale, **a, **kw)
+    _check_fd(rng, L, gr, args)
+    # the empty sequence passes its end-state gradient straight through
+    np.testing.assert_array_equal(gr["dS0"][1], dST[1])
+    np.testing.assert_array_equal(gr["dconv_state"][1], 0.0)
