@@ -23,7 +23,7 @@ KDA_BF16 = 0
 KDA_FP32 = 1
 KDA_FLAG_L2NORM_QK = 1
 KDA_FLAG_BETA_LOGITS = 2
-ABI_VERSION = 3
+ABI_VERSION = 4
 KDA_STAGE_PREP, KDA_STAGE_STATE, KDA_STAGE_CONV_TAIL, KDA_STAGE_OUTPUT = 0, 1, 2, 3
 KDA_STAGE_STATE_TAIL = 4  # stages 1 and 2 in one launch, as kda_prefill runs them
 NUM_STAGES = 4
@@ -69,7 +69,8 @@ class DecodeArgs(ctypes.Structure):
 class BackwardArgs(ctypes.Structure):
     _fields_ = [("fwd", PrefillArgs), ("dO", _vp), ("dS_T", _vp), ("dq", _vp), ("dk", _vp),
                 ("dv", _vp), ("dg", _vp), ("dbeta", _vp), ("dS0", _vp), ("dconv_w", _vp),
-                ("dconv_state", _vp)]
+                ("dconv_state", _vp), ("dA_log", _vp), ("ddt_bias", _vp), ("do_norm_w", _vp),
+                ("do_gate", _vp)]
 
 
 class KdaError(RuntimeError):
@@ -377,7 +378,8 @@ def backward_args(fwd: PrefillArgs, do, dS_T, grads: dict) -> BackwardArgs:
     a = BackwardArgs()
     a.fwd = fwd
     a.dO, a.dS_T = _ptr(do), _ptr(dS_T)
-    for n in ("dq", "dk", "dv", "dg", "dbeta", "dS0", "dconv_w", "dconv_state"):
+    for n in ("dq", "dk", "dv", "dg", "dbeta", "dS0", "dconv_w", "dconv_state", "dA_log", "ddt_bias",
+              "do_norm_w", "do_gate"):
         setattr(a, n, _ptr(grads.get(n)))
     return a
 
@@ -392,12 +394,16 @@ def kda_backward_workspace_bytes(args: BackwardArgs) -> int:
 
 def kda_prefill_backward(q, k, v, g, beta, conv_w=None, conv_state=None, S0=None, *, do,
                          dS_T=None, chunk=64, scale=1.0, l2norm_qk=True, eps=1e-6, workspace=None,
-                         stream=None):
+                         stream=None, A_log=None, dt_bias=None, beta_logits=False, o_norm_w=None,
+                         o_norm_eps=1e-6, o_gate=None):
     """Gradients of L = <o, do> + <S_T, dS_T> (the forward is recomputed).
 
     Returns (grads, o, S_T): grads is a dict of float32 tensors dq, dk, dv, dg
-    [B, T, H, D], dbeta [B, T, H], dS0 [B, H, D, D], and with the convolution
-    dconv_w [3, H*D, 4] and dconv_state [B, 3, 3, H*D].
+    [B, T, H, D], dbeta [B, T, H], dS0 [B, H, D, D], with the convolution
+    dconv_w [3, H*D, 4] and dconv_state [B, 3, 3, H*D], and with the optional
+    stages (arguments as kda_prefill) dA_log [H] and ddt_bias [H*D] (dg is then
+    the gradient of the raw gate projection), do_norm_w [D], do_gate [B, T, H, D];
+    with beta_logits dbeta is the gradient of the logits.
     """
     B, T, H, D = q.shape
     dev = q.device
@@ -406,13 +412,22 @@ def kda_prefill_backward(q, k, v, g, beta, conv_w=None, conv_state=None, S0=None
     S_T = torch.empty(B, H, D, D, **f32)
     cso = torch.empty(B, 3, 3, H * D, dtype=q.dtype, device=dev) if conv_w is not None else None
     fwd = prefill_args(q, k, v, g, beta, conv_w, conv_state, S0, o, S_T, cso, chunk=chunk,
-                       scale=scale, l2norm_qk=l2norm_qk, eps=eps)
+                       scale=scale, l2norm_qk=l2norm_qk, eps=eps, A_log=A_log, dt_bias=dt_bias,
+                       beta_logits=beta_logits, o_norm_w=o_norm_w, o_norm_eps=o_norm_eps,
+                       o_gate=o_gate)
     grads = dict(dq=torch.empty(B, T, H, D, **f32), dk=torch.empty(B, T, H, D, **f32),
                  dv=torch.empty(B, T, H, D, **f32), dg=torch.empty(B, T, H, D, **f32),
                  dbeta=torch.empty(B, T, H, **f32), dS0=torch.empty(B, H, D, D, **f32))
     if conv_w is not None:
         grads["dconv_w"] = torch.empty(3, H * D, 4, **f32)
         grads["dconv_state"] = torch.empty(B, 3, 3, H * D, **f32)
+    if A_log is not None:
+        grads["dA_log"] = torch.empty(H, **f32)
+        grads["ddt_bias"] = torch.empty(H * D, **f32)
+    if o_norm_w is not None:
+        grads["do_norm_w"] = torch.empty(D, **f32)
+    if o_gate is not None:
+        grads["do_gate"] = torch.empty(B, T, H, D, **f32)
     a = backward_args(fwd, do, dS_T, grads)
     _check(kda_validate_backward(a), "kda_prefill_backward")
     need = kda_backward_workspace_bytes(a)

@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdint>
 #include <initializer_list>
+#include <utility>
 
 #include "kda_launch.h"
 #include "kda_layout.h"
@@ -560,6 +561,7 @@ namespace {
 // (see kda_layout.h), each 256-byte aligned.
 struct BwdLayout {
   size_t tT, y, gam, beta, ckS, ckdS, dU, dQL, dW, dKt, dP, dLC, dBk, dBv, dA, dy, dbp, dcp, pl;
+  size_t dOp, dwp, ddp, dap;  // the optional stages: dO before the output stage, partial sums
   size_t bytes;
   size_t nfront;  // front-end workgroups per (b, h)
 };
@@ -601,28 +603,39 @@ BwdLayout bwd_layout(const kda_backward_args* a) {
   L.nfront = kda::bwd_front_blocks(f->T, f->D);
   L.dcp = take(f->conv_k > 0 ? (size_t)f->B * L.nfront * 3 * f->H * D * 4 : 0);
   L.pl = take(64 + nrec);  // count (256-byte header), then the list of records
+  const bool gn = f->o_norm_w != nullptr || f->o_gate != nullptr;
+  L.dOp = take(gn ? x / ef : 0);  // gradient of the mixer's output (before the stage), I/O type
+  L.dwp = take(f->o_norm_w != nullptr ? (size_t)kda::bwd_out_groups((long)bth, f->D) * D : 0);
+  const size_t nact = f->A_log != nullptr ? (size_t)kda::bwd_act_groups((long)f->B * f->T, f->D) : 0;
+  L.ddp = take(nact * f->H * D);
+  L.dap = take(nact * f->H);
   L.bytes = off;
   return L;
 }
 
-// Every buffer of a backward call with its byte size: 13 inputs (and forward
-// outputs), 8 gradient outputs.
-void bwd_spans(const kda_backward_args* a, Span (&ins)[13], Span (&outs)[8]) {
+// Every buffer of a backward call with its byte size: 17 inputs (and forward
+// outputs), 12 gradient outputs.
+constexpr int kBwdIns = 17, kBwdOuts = 12;
+void bwd_spans(const kda_backward_args* a, Span (&ins)[kBwdIns], Span (&outs)[kBwdOuts]) {
   const kda_prefill_args* f = &a->fwd;
   PrefillSizes s;
   prefill_sizes(f, s);
   const size_t g = (size_t)f->B * f->T * f->H * f->D * 4, gb = (size_t)f->B * f->T * f->H * 4;
   const size_t ck = f->conv_k > 0 ? (size_t)f->conv_k - 1 : 0;
   const size_t dcs = (size_t)f->B * 3 * ck * f->H * f->D * 4;
-  const Span i[13] = {span(f->q, s.x), span(f->k, s.x), span(f->v, s.x), span(f->g, s.x),
-                      span(f->beta, s.bta), span(f->conv_w, s.cw), span(f->conv_state_in, s.cst),
-                      span(f->S0, s.state), span(f->o, s.x), span(f->S_T, s.state),
-                      span(f->conv_state_out, s.cst), span(a->dO, s.x), span(a->dS_T, s.state)};
-  const Span o[8] = {span(a->dq, g), span(a->dk, g), span(a->dv, g), span(a->dg, g),
-                     span(a->dbeta, gb), span(a->dS0, s.state), span(a->dconv_w, s.cw),
-                     span(a->dconv_state, dcs)};
-  for (int k = 0; k < 13; ++k) ins[k] = i[k];
-  for (int k = 0; k < 8; ++k) outs[k] = o[k];
+  const size_t H4 = (size_t)f->H * 4, HD4 = (size_t)f->H * f->D * 4, D4 = (size_t)f->D * 4;
+  const Span i[kBwdIns] = {span(f->q, s.x), span(f->k, s.x), span(f->v, s.x), span(f->g, s.x),
+                           span(f->beta, s.bta), span(f->conv_w, s.cw), span(f->conv_state_in, s.cst),
+                           span(f->S0, s.state), span(f->o, s.x), span(f->S_T, s.state),
+                           span(f->conv_state_out, s.cst), span(a->dO, s.x), span(a->dS_T, s.state),
+                           span(f->A_log, H4), span(f->dt_bias, HD4), span(f->o_norm_w, D4),
+                           span(f->o_gate, s.x)};
+  const Span o[kBwdOuts] = {span(a->dq, g), span(a->dk, g), span(a->dv, g), span(a->dg, g),
+                            span(a->dbeta, gb), span(a->dS0, s.state), span(a->dconv_w, s.cw),
+                            span(a->dconv_state, dcs), span(a->dA_log, H4), span(a->ddt_bias, HD4),
+                            span(a->do_norm_w, D4), span(a->do_gate, g)};
+  for (int k = 0; k < kBwdIns; ++k) ins[k] = i[k];
+  for (int k = 0; k < kBwdOuts; ++k) outs[k] = o[k];
 }
 
 }  // namespace
@@ -633,23 +646,26 @@ kda_status kda_validate_backward(const kda_backward_args* a) {
   if (a == nullptr) return KDA_ERR_NULL;
   const kda_prefill_args* f = &a->fwd;
   if (kda_status e = kda_validate_prefill(f); e != KDA_OK) return e;
-  if (f->cu_seqlens != nullptr || f->A_log != nullptr || f->o_norm_w != nullptr ||
-      f->o_gate != nullptr || (f->flags & KDA_FLAG_BETA_LOGITS) != 0)
-    return KDA_ERR_UNSUPPORTED;
+  if (f->cu_seqlens != nullptr) return KDA_ERR_UNSUPPORTED;
+  if ((a->dA_log || a->ddt_bias) && f->A_log == nullptr) return KDA_ERR_NULL;
+  if (a->do_norm_w && f->o_norm_w == nullptr) return KDA_ERR_NULL;
+  if (a->do_gate && f->o_gate == nullptr) return KDA_ERR_NULL;
   if (f->io == KDA_FP32 && f->D == 128) return KDA_ERR_UNSUPPORTED;
   const bool need = f->T > 0;
   if (need && (!a->dO || !a->dq || !a->dk || !a->dv || !a->dg || !a->dbeta)) return KDA_ERR_NULL;
   if (f->conv_k > 0 && !a->dconv_w) return KDA_ERR_NULL;
   if (f->conv_k == 0 && (a->dconv_w || a->dconv_state)) return KDA_ERR_NULL;
   for (const void* p : std::initializer_list<const void*>{a->dO, a->dS_T, a->dq, a->dk, a->dv, a->dg,
-                                                          a->dbeta, a->dS0, a->dconv_w, a->dconv_state})
+                                                          a->dbeta, a->dS0, a->dconv_w, a->dconv_state,
+                                                          a->dA_log, a->ddt_bias, a->do_norm_w,
+                                                          a->do_gate})
     if (p && !aligned16(p)) return KDA_ERR_ALIGN;
-  Span ins[13], outs[8];
+  Span ins[kBwdIns], outs[kBwdOuts];
   bwd_spans(a, ins, outs);
-  for (int i = 0; i < 8; ++i) {
-    for (int j = 0; j < 13; ++j)
+  for (int i = 0; i < kBwdOuts; ++i) {
+    for (int j = 0; j < kBwdIns; ++j)
       if (overlaps(outs[i], ins[j])) return KDA_ERR_ALIAS;
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < kBwdOuts; ++j)
       if (i != j && overlaps(outs[i], outs[j])) return KDA_ERR_ALIAS;
   }
   return KDA_OK;
@@ -679,6 +695,10 @@ kda_status kda_prefill_backward(const kda_backward_args* a, void* ws, size_t ws_
     if (a->dconv_state != nullptr &&
         kda::launch_copy_state(nullptr, a->dconv_state, (size_t)f->B * 3 * 3 * f->H * f->D, st) != hipSuccess)
       return KDA_ERR_HIP;
+    // sums over no tokens
+    for (auto [p, n] : {std::pair<float*, size_t>{a->dA_log, (size_t)f->H},
+                        {a->ddt_bias, (size_t)f->H * f->D}, {a->do_norm_w, (size_t)f->D}})
+      if (p != nullptr && kda::launch_copy_state(nullptr, p, n, st) != hipSuccess) return KDA_ERR_HIP;
     // the run_stage calls below still hand S_T and the conv state through
     for (int stage = KDA_STAGE_PREP; stage <= KDA_STAGE_OUTPUT; ++stage)
       if (kda_status e = run_stage(f, ws, stage, st); e != KDA_OK) return e;
@@ -689,7 +709,7 @@ kda_status kda_prefill_backward(const kda_backward_args* a, void* ws, size_t ws_
     return KDA_ERR_WORKSPACE;
   {
     const Span w = span(ws, L.bytes);
-    Span ins[13], outs[8];
+    Span ins[kBwdIns], outs[kBwdOuts];
     bwd_spans(a, ins, outs);
     for (const Span& x : ins)
       if (overlaps(w, x)) return KDA_ERR_ALIAS;
@@ -700,22 +720,51 @@ kda_status kda_prefill_backward(const kda_backward_args* a, void* ws, size_t ws_
   auto F = [&](size_t off) { return reinterpret_cast<float*>(wsb + off); };
   // forward in backward mode.  The conv-state hand-over comes last, after the
   // backward front end has read the previous conv state: conv_state_out may be
-  // conv_state_in, and the hand-over overwrites it.
+  // conv_state_in, and the hand-over overwrites it.  With the output stage the
+  // walk leaves the mixer's output in o; the stage's backward reads it, then the
+  // stage finishes o in place.
+  const bool gn = f->o_norm_w != nullptr || f->o_gate != nullptr;
+  kda_prefill_args f0 = *f;
+  f0.o_norm_w = nullptr;
+  f0.o_gate = nullptr;
   BwdFwdOut bo{wsb + L.y, F(L.gam), F(L.beta), F(L.tT), wsb + L.ckS};
-  for (int stage : {KDA_STAGE_PREP, KDA_STAGE_STATE, KDA_STAGE_OUTPUT})
-    if (kda_status e = run_stage(f, ws, stage, st, &bo); e != KDA_OK) return e;
+  for (int stage : {KDA_STAGE_PREP, KDA_STAGE_STATE})
+    if (kda_status e = run_stage(&f0, ws, stage, st, &bo); e != KDA_OK) return e;
+  const void* dO = a->dO;
+  if (gn) {
+    kda::BwdOutParams q{};
+    q.x = f->o;
+    q.z = f->o_gate;
+    q.dy = a->dO;
+    q.w = f->o_norm_w;
+    q.eps = f->o_norm_eps;
+    q.dx = wsb + L.dOp;
+    q.dz = a->do_gate;
+    q.dw_part = F(L.dwp);
+    q.rows = (long)f->B * f->T * f->H;
+    if (kda_status e = hip_status(kda::launch_bwd_out_stage(q, a->do_norm_w, f->D, fp32, st)); e != KDA_OK)
+      return e;
+    kda::OutStageParams os{};
+    os.o = f->o;
+    os.o_gate = f->o_gate;
+    os.o_norm_w = f->o_norm_w;
+    os.o_norm_eps = f->o_norm_eps;
+    os.rows = q.rows;
+    if (kda_status e = hip_status(kda::launch_out_stage(os, f->D, fp32, st)); e != KDA_OK) return e;
+    dO = wsb + L.dOp;
+  }
   // backward
   kda::BwdLaunch B{};
   const char* recs = wsb + ws_layout(f).records;
   B.walk.ws = recs;
-  B.walk.dO = a->dO;
+  B.walk.dO = dO;
   B.walk.dS_T = a->dS_T;
   B.walk.dS0 = a->dS0;
   B.walk.dU = wsb + L.dU;
   B.walk.ckdS = wsb + L.ckdS;
   B.walk.B = f->B; B.walk.T = f->T; B.walk.H = f->H; B.walk.NT = sz.NT;
   B.prod.ws = recs;
-  B.prod.dO = a->dO;
+  B.prod.dO = dO;
   B.prod.ckS = wsb + L.ckS;
   B.prod.ckdS = wsb + L.ckdS;
   B.prod.dU = wsb + L.dU;
@@ -749,6 +798,23 @@ kda_status kda_prefill_backward(const kda_backward_args* a, void* ws, size_t ws_
   B.dconv_w = a->dconv_w;
   if (kda_status e = hip_status(kda::launch_backward(B, f->D, f->chunk, fp32, st)); e != KDA_OK)
     return e;
+  const bool logits = (f->flags & KDA_FLAG_BETA_LOGITS) != 0;
+  if (f->A_log != nullptr || logits) {
+    kda::BwdActParams q{};
+    q.f = f->A_log != nullptr ? f->g : nullptr;
+    q.A_log = f->A_log;
+    q.dt_bias = f->dt_bias;
+    q.dg = a->dg;
+    q.ddt_part = F(L.ddp);
+    q.dA_part = F(L.dap);
+    q.beta = logits ? F(L.beta) : nullptr;
+    q.dbeta = a->dbeta;
+    q.tokens = (long)f->B * f->T;
+    q.H = f->H;
+    if (kda_status e = hip_status(kda::launch_bwd_act(q, a->dA_log, a->ddt_bias, f->D, fp32, st));
+        e != KDA_OK)
+      return e;
+  }
   return run_stage(f, ws, KDA_STAGE_CONV_TAIL, st, &bo);
 }
 

@@ -19,6 +19,12 @@ hipError_t launch_seq_index(const IndexParams& p, hipStream_t st);
 hipError_t launch_copy_state(const float* src, float* dst, size_t n, hipStream_t st);
 hipError_t launch_backward(const BwdLaunch& L, int D, int C, bool fp32, hipStream_t st);
 size_t bwd_front_blocks(int T, int D);
+// the optional stages' backward; dw, dA_log, ddt_bias may be NULL (not written)
+hipError_t launch_bwd_out_stage(const BwdOutParams& p, float* dw, int D, bool fp32, hipStream_t st);
+hipError_t launch_bwd_act(const BwdActParams& p, float* dA_log, float* ddt_bias, int D, bool fp32,
+                          hipStream_t st);
+int bwd_out_groups(long rows, int D);   // workgroups (= partials) of the two
+int bwd_act_groups(long tokens, int D);
 hipError_t launch_decode(const DecodeParams& p, int D, bool fp32, hipStream_t st);
 
 // The whole prefill (arguments already validated) in a workspace of `bytes`:

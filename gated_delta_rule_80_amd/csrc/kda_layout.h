@@ -240,6 +240,38 @@ struct BwdLaunch {
   float* dconv_w;  // [3][H*D][4] or NULL
 };
 
+// Backward of the output stage (RMSNorm with gain w, then the sigmoid gate), per
+// (token, head) row of D values.
+struct BwdOutParams {
+  const void* x;    // [rows][D] the mixer's output before the stage (I/O type)
+  const void* z;    // [rows][D] gate pre-activation (I/O type) or NULL
+  const void* dy;   // [rows][D] gradient of the stage's output (I/O type)
+  const float* w;   // [D] gain or NULL (no norm)
+  float eps;
+  void* dx;         // [rows][D] gradient of x (I/O type)
+  float* dz;        // [rows][D] gradient of z, or NULL
+  float* dw_part;   // [groups][D] partial sums of dw (with the norm)
+  long rows;
+};
+
+// Backward of the activations from raw projections, per token and head.
+struct BwdActParams {
+  const void* f;          // [tokens][H][D] raw gate projection (I/O type), or NULL
+  const float* A_log;     // [H]
+  const float* dt_bias;   // [H*D]
+  float* dg;              // [tokens][H][D] in: gradient of the decay; out: of f
+  float* ddt_part;        // [groups][H*D]
+  float* dA_part;         // [groups][H]
+  const float* beta;      // [tokens][H] activated beta, or NULL (no logits)
+  float* dbeta;           // [tokens][H] in: gradient of beta; out: of the logits
+  long tokens;
+  int H;
+};
+
+// Most workgroups of the output-stage backward (and 1/8 of that per head for the
+// activations'); their partial sums are added in a fixed order.
+constexpr int kBwdStageGroups = 1024;
+
 struct ConvNormParams {
   const void* q;
   const void* k;

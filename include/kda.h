@@ -73,7 +73,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 3
+#define KDA_ABI_VERSION 4
 
 typedef enum kda_status {
   KDA_OK = 0,
@@ -266,9 +266,13 @@ kda_status kda_decode_step(const kda_decode_args* a, void* stream);
  * again with the same values), then walked back chunk by chunk: the reverse of
  * the chunked form, with the pairs' relative decays exp(Gamma_i - Gamma_j)
  * factored per 16-token block (chunks whose decay spans are too wide for that are
- * evaluated per pair).  Supported: the plain mixer over B equal-length sequences
- * (no packed sequences, no optional stages); fp32 I/O up to D = 64, bf16 I/O up
- * to D = 128.  All gradients are float32; with bf16 I/O the intermediate
+ * evaluated per pair).  The optional stages are differentiated too: the
+ * gradient passes back through the output stage first (o is then finished by the
+ * stage in place, as kda_prefill's separate output pass does); with the
+ * activations, dg and dbeta are the gradients of g and beta as given (the raw
+ * gate projection, the logits).  Supported: B equal-length sequences (no packed
+ * sequences), fp32 I/O up to D = 64, bf16 I/O up to D = 128.  All gradients are
+ * float32; with bf16 I/O the intermediate
  * gradients pass between the kernels in bf16 (relative error of the returned
  * gradients about 4e-3 against an exact computation, at T = 4096, H = 96,
  * D = 128). */
@@ -284,6 +288,12 @@ typedef struct kda_backward_args {
   float* dS0;           /* device [B][H][D][D] or NULL (not written) */
   float* dconv_w;       /* device [3][H*D][conv_k]; required iff conv_k > 0 */
   float* dconv_state;   /* device [B][3][conv_k-1][H*D] or NULL (not written) */
+  /* gradients of the optional stages' parameters (ABI 4): each NULL = not written,
+     and must be NULL when its stage is off */
+  float* dA_log;        /* device [H]; with A_log */
+  float* ddt_bias;      /* device [H*D]; with A_log */
+  float* do_norm_w;     /* device [D]; with o_norm_w */
+  float* do_gate;       /* device [B][T][H][D]: gradient of o_gate; with o_gate */
 } kda_backward_args;
 
 kda_status kda_validate_backward(const kda_backward_args* a);

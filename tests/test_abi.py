@@ -24,7 +24,7 @@ def test_exports_every_declared_symbol(lib):
             "kda_validate_conv_norm", "kda_status_str", "kda_abi_version"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.kda_abi_version() == 3
+    assert lib.kda_abi_version() == 4
     for s in range(11):
         assert kda.kda_status_str(s) and kda.kda_status_str(s) != "unknown status"
 
@@ -364,18 +364,32 @@ def test_backward_validation(lib):
     a = backward()
     a.dbeta += 4
     assert vb(a) == ALIGN
-    # unsupported modes
+    # the optional stages: their parameters' gradients only with the stage on
     f = Fake()
     f.next = 0x7A0000000000
     a = backward()
     a.fwd.A_log, a.fwd.dt_bias = f(), f()
-    assert vb(a) == UNSUP
+    assert vb(a) == OK
+    a.dA_log, a.ddt_bias = f(), f()
+    assert vb(a) == OK
+    a.ddt_bias = a.fwd.dt_bias  # may not overlap its parameter
+    assert vb(a) == ALIAS
     a = backward()
-    a.fwd.o_gate = f()
-    assert vb(a) == UNSUP
+    a.fwd.o_gate, a.fwd.o_norm_w = f(), f()
+    a.do_gate, a.do_norm_w = f(), f()
+    assert vb(a) == OK
+    a.do_gate = a.dq  # nor another gradient
+    assert vb(a) == ALIAS
     a = backward()
     a.fwd.flags = 3
-    assert vb(a) == UNSUP
+    assert vb(a) == OK
+    for n in ("dA_log", "ddt_bias", "do_norm_w", "do_gate"):
+        assert vb(backward(**{n: f()})) == NULL, n  # stage off
+    a = backward()
+    a.fwd.o_gate = f()
+    a.do_gate = f() + 4
+    assert vb(a) == ALIGN
+    # unsupported modes
     a = backward()
     a.fwd.B, a.fwd.cu_seqlens, a.fwd.n_seqs = 1, f(), 2
     assert vb(a) == UNSUP

@@ -9,9 +9,9 @@ import pytest
 import torch
 
 import gated_delta_rule_80_amd as kda
-from kda_inputs import to_numpy
+from kda_inputs import make_stage_inputs, to_numpy
 from kda_testutil import TOL, cuda, make, rel_l2, small
-from oracle import kda_reference_backward
+from oracle import kda_reference, kda_reference_backward, output_gate_norm_backward
 
 pytestmark = pytest.mark.gpu
 
@@ -196,3 +196,120 @@ def test_backward_in_place_states(io, D, chunk):
     assert torch.equal(o, o_ref)
     assert torch.equal(S, S_ref)
     assert torch.equal(cs, tail_ref)
+
+
+# ----------------------------------------------------------- optional stages
+STAGES = {
+    "norm": dict(norm=True),
+    "gate": dict(gate=True),
+    "norm+gate": dict(norm=True, gate=True),
+    "act": dict(act=True),
+    "logits": dict(logits=True),
+    "all": dict(norm=True, gate=True, act=True, logits=True),
+}
+STAGE_GRADS = NAMES + ("dA_log", "ddt_bias", "do_norm_w", "do_gate")
+
+
+def check_backward_stages(w, chunk, seed, norm=False, gate=False, act=False, logits=False):
+    """The backward with optional stages against the oracle's; the recomputed o
+    against kda_prefill's with the same stages (bit for bit where both finish o
+    with the same separate pass, D = 128; otherwise to the tolerance, since the
+    fused walk of D <= 64 keeps the mixer's output in fp32 into the stage)."""
+    inp = make(w, seed)
+    st = make_stage_inputs(w, seed)
+    kw = {}
+    if norm:
+        kw["o_norm_w"] = st["o_norm_w"]
+    if gate:
+        kw["o_gate"] = st["o_gate"]
+    if act:
+        inp = dict(inp, g=st["f"])
+        kw["A_log"], kw["dt_bias"] = st["A_log"], st["dt_bias"]
+    if logits:
+        inp = dict(inp, beta=st["b_logit"])
+        kw["beta_logits"] = True
+    gen = torch.Generator().manual_seed(seed + 1000)
+    do = torch.randn(w.B, w.T, w.H, w.D, generator=gen).to(inp["q"].dtype)
+    dST = torch.randn(w.B, w.H, w.D, w.D, generator=gen)
+    c = cuda(inp)
+    ck = {k: (v.cuda() if torch.is_tensor(v) else v) for k, v in kw.items()}
+    grads, o, S_T = kda.kda_prefill_backward(c["q"], c["k"], c["v"], c["g"], c["beta"], c["conv_w"],
+                                             c["conv_state"], c["S0"], do=do.cuda(), dS_T=dST.cuda(),
+                                             chunk=chunk, **ck)
+    torch.cuda.synchronize()
+    o_f, S_f, _ = kda.kda_prefill(c["q"], c["k"], c["v"], c["g"], c["beta"], c["conv_w"],
+                                  c["conv_state"], c["S0"], chunk=chunk, **ck)
+    torch.cuda.synchronize()
+    assert torch.equal(S_T, S_f)
+    if w.D == 128 or not (norm or gate):
+        assert torch.equal(o, o_f)
+    else:
+        assert rel_l2(o.float().cpu().numpy(), o_f.float().cpu().numpy()) <= TOL[w.io]
+    n = {k: to_numpy(v) for k, v in inp.items()}
+    nk = {k: (to_numpy(v) if torch.is_tensor(v) else v) for k, v in kw.items()}
+    if "beta_logits" in nk:
+        nk["beta_sigmoid"] = nk.pop("beta_logits")
+    ref = kda_reference_backward(n["q"], n["k"], n["v"], n["g"], n["beta"], to_numpy(do),
+                                 to_numpy(dST), conv_w=n["conv_w"], conv_state=n["conv_state"],
+                                 S0=n["S0"], **nk)
+    tol = {name: TOL[w.io] for name in STAGE_GRADS}
+    if norm and w.io == "bf16":
+        # The output norm's backward divides by each row's rms: a row whose mixer
+        # output is much smaller than the others passes the forward's own error
+        # into the gradients magnified by that ratio.  The bf16 forward's error in
+        # the mixer output does not shrink with a row's magnitude (it comes from
+        # the rounding of the terms that sum to it), so it is modelled as seeded
+        # normal noise of 4e-3 times the output's rms over the call (the forward's
+        # measured relative error).  The bar adds twice the change that noise
+        # makes in the exact computation's gradients to the plain bar.
+        akw = {k: v for k, v in nk.items() if k in ("A_log", "dt_bias", "beta_sigmoid")}
+        base = dict(conv_w=n["conv_w"], conv_state=n["conv_state"], S0=n["S0"], **akw)
+        o_pre = kda_reference(n["q"], n["k"], n["v"], n["g"], n["beta"], **base)[0]
+        noise = np.random.default_rng(seed + 7).standard_normal(o_pre.shape)
+        d_pert = output_gate_norm_backward(o_pre + 4e-3 * np.sqrt(np.mean(o_pre ** 2)) * noise,
+                                           to_numpy(do), nk.get("o_norm_w"), nk.get("o_gate"))[0]
+        pert = kda_reference_backward(n["q"], n["k"], n["v"], n["g"], n["beta"], d_pert,
+                                      to_numpy(dST), **base)
+        for name in NAMES:
+            if ref.get(name) is not None:
+                tol[name] += 2.0 * rel_l2(pert[name], ref[name])
+    errs = {}
+    for name in STAGE_GRADS:
+        if ref.get(name) is None:
+            assert name not in grads or name in NAMES, name
+            continue
+        got = grads[name].cpu().numpy()
+        assert np.isfinite(got).all(), name
+        errs[name] = rel_l2(got, ref[name])
+    print(f"{w.name} D={w.D} C={chunk} stages={norm, gate, act, logits}: " +
+          " ".join(f"{k}={v:.1e}" for k, v in errs.items()), flush=True)
+    for name, e in errs.items():
+        assert e <= tol[name], (name, e, tol[name])
+
+
+@pytest.mark.parametrize("stages", list(STAGES))
+@pytest.mark.parametrize("io,D,chunk", [("bf16", 128, 64), ("fp32", 32, 16), ("bf16", 64, 32)])
+def test_backward_optional_stages(stages, io, D, chunk):
+    w = small(B=2, T=90, H=3, D=D, io=io, chunk=chunk, s0=True, conv_state=True)
+    check_backward_stages(w, chunk, seed=31 + D, **STAGES[stages])
+
+
+def test_backward_stages_repeated_calls_are_bit_identical():
+    """The parameter gradients are sums over tokens in a fixed order."""
+    w = small(B=2, T=300, H=4, D=128, io="bf16", chunk=64, s0=True, conv_state=True)
+    inp = cuda(make(w, 12))
+    st = {k: v.cuda() for k, v in make_stage_inputs(w, 12).items()}
+    do = torch.randn(w.B, w.T, w.H, w.D, generator=torch.Generator().manual_seed(5)).to(torch.bfloat16).cuda()
+    first = None
+    for _ in range(4):
+        grads, _, _ = kda.kda_prefill_backward(inp["q"], inp["k"], inp["v"], st["f"], st["b_logit"],
+                                               inp["conv_w"], inp["conv_state"], inp["S0"], do=do,
+                                               chunk=64, A_log=st["A_log"], dt_bias=st["dt_bias"],
+                                               beta_logits=True, o_norm_w=st["o_norm_w"],
+                                               o_gate=st["o_gate"])
+        torch.cuda.synchronize()
+        if first is None:
+            first = {k: v.clone() for k, v in grads.items()}
+        else:
+            for k, v in grads.items():
+                assert torch.equal(v, first[k]), k
