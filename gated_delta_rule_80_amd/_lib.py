@@ -395,7 +395,7 @@ def kda_backward_workspace_bytes(args: BackwardArgs) -> int:
 def kda_prefill_backward(q, k, v, g, beta, conv_w=None, conv_state=None, S0=None, *, do,
                          dS_T=None, chunk=64, scale=1.0, l2norm_qk=True, eps=1e-6, workspace=None,
                          stream=None, A_log=None, dt_bias=None, beta_logits=False, o_norm_w=None,
-                         o_norm_eps=1e-6, o_gate=None):
+                         o_norm_eps=1e-6, o_gate=None, cu_seqlens=None):
     """Gradients of L = <o, do> + <S_T, dS_T> (the forward is recomputed).
 
     Returns (grads, o, S_T): grads is a dict of float32 tensors dq, dk, dv, dg
@@ -403,24 +403,26 @@ def kda_prefill_backward(q, k, v, g, beta, conv_w=None, conv_state=None, S0=None
     dconv_w [3, H*D, 4] and dconv_state [B, 3, 3, H*D], and with the optional
     stages (arguments as kda_prefill) dA_log [H] and ddt_bias [H*D] (dg is then
     the gradient of the raw gate projection), do_norm_w [D], do_gate [B, T, H, D];
-    with beta_logits dbeta is the gradient of the logits.
+    with beta_logits dbeta is the gradient of the logits.  Packed sequences
+    (cu_seqlens as kda_prefill): dS_T, dS0 [N, H, D, D], dconv_state [N, 3, 3, H*D].
     """
     B, T, H, D = q.shape
     dev = q.device
+    NS = B if cu_seqlens is None else cu_seqlens.numel() - 1
     f32 = dict(dtype=torch.float32, device=dev)
     o = torch.empty_like(q)
-    S_T = torch.empty(B, H, D, D, **f32)
-    cso = torch.empty(B, 3, 3, H * D, dtype=q.dtype, device=dev) if conv_w is not None else None
+    S_T = torch.empty(NS, H, D, D, **f32)
+    cso = torch.empty(NS, 3, 3, H * D, dtype=q.dtype, device=dev) if conv_w is not None else None
     fwd = prefill_args(q, k, v, g, beta, conv_w, conv_state, S0, o, S_T, cso, chunk=chunk,
                        scale=scale, l2norm_qk=l2norm_qk, eps=eps, A_log=A_log, dt_bias=dt_bias,
                        beta_logits=beta_logits, o_norm_w=o_norm_w, o_norm_eps=o_norm_eps,
-                       o_gate=o_gate)
+                       o_gate=o_gate, cu_seqlens=cu_seqlens)
     grads = dict(dq=torch.empty(B, T, H, D, **f32), dk=torch.empty(B, T, H, D, **f32),
                  dv=torch.empty(B, T, H, D, **f32), dg=torch.empty(B, T, H, D, **f32),
-                 dbeta=torch.empty(B, T, H, **f32), dS0=torch.empty(B, H, D, D, **f32))
+                 dbeta=torch.empty(B, T, H, **f32), dS0=torch.empty(NS, H, D, D, **f32))
     if conv_w is not None:
         grads["dconv_w"] = torch.empty(3, H * D, 4, **f32)
-        grads["dconv_state"] = torch.empty(B, 3, 3, H * D, **f32)
+        grads["dconv_state"] = torch.empty(NS, 3, 3, H * D, **f32)
     if A_log is not None:
         grads["dA_log"] = torch.empty(H, **f32)
         grads["ddt_bias"] = torch.empty(H * D, **f32)

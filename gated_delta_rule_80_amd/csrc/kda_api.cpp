@@ -562,8 +562,9 @@ namespace {
 struct BwdLayout {
   size_t tT, y, gam, beta, ckS, ckdS, dU, dQL, dW, dKt, dP, dLC, dBk, dBv, dA, dy, dbp, dcp, pl;
   size_t dOp, dwp, ddp, dap;  // the optional stages: dO before the output stage, partial sums
+  size_t fst;                 // packed: first front-end block slot per sequence [n_seqs + 1]
   size_t bytes;
-  size_t nfront;  // front-end workgroups per (b, h)
+  size_t nfront;  // front-end block slots per head (filter partials)
 };
 
 BwdLayout bwd_layout(const kda_backward_args* a) {
@@ -600,8 +601,12 @@ BwdLayout bwd_layout(const kda_backward_args* a) {
   L.dA = take(nrec * C * C / ef);
   L.dy = take(3 * x / ef);  // record element type
   L.dbp = take(bth);
-  L.nfront = kda::bwd_front_blocks(f->T, f->D);
-  L.dcp = take(f->conv_k > 0 ? (size_t)f->B * L.nfront * 3 * f->H * D * 4 : 0);
+  // front-end block slots: per (sequence, block of the sequence) for packed
+  // batches, ceil(T / TOKB) + n_seqs of them (a sequence wastes at most one block)
+  L.nfront = packed(f) ? kda::bwd_front_blocks(f->T, f->D) + (size_t)f->n_seqs
+                       : (size_t)f->B * kda::bwd_front_blocks(f->T, f->D);
+  L.dcp = take(f->conv_k > 0 ? L.nfront * 3 * f->H * D * 4 : 0);
+  L.fst = take(packed(f) ? (size_t)f->n_seqs + 1 : 0);
   L.pl = take(64 + nrec);  // count (256-byte header), then the list of records
   const bool gn = f->o_norm_w != nullptr || f->o_gate != nullptr;
   L.dOp = take(gn ? x / ef : 0);  // gradient of the mixer's output (before the stage), I/O type
@@ -622,7 +627,7 @@ void bwd_spans(const kda_backward_args* a, Span (&ins)[kBwdIns], Span (&outs)[kB
   prefill_sizes(f, s);
   const size_t g = (size_t)f->B * f->T * f->H * f->D * 4, gb = (size_t)f->B * f->T * f->H * 4;
   const size_t ck = f->conv_k > 0 ? (size_t)f->conv_k - 1 : 0;
-  const size_t dcs = (size_t)f->B * 3 * ck * f->H * f->D * 4;
+  const size_t dcs = (size_t)s.NS * 3 * ck * f->H * f->D * 4;
   const size_t H4 = (size_t)f->H * 4, HD4 = (size_t)f->H * f->D * 4, D4 = (size_t)f->D * 4;
   const Span i[kBwdIns] = {span(f->q, s.x), span(f->k, s.x), span(f->v, s.x), span(f->g, s.x),
                            span(f->beta, s.bta), span(f->conv_w, s.cw), span(f->conv_state_in, s.cst),
@@ -646,7 +651,6 @@ kda_status kda_validate_backward(const kda_backward_args* a) {
   if (a == nullptr) return KDA_ERR_NULL;
   const kda_prefill_args* f = &a->fwd;
   if (kda_status e = kda_validate_prefill(f); e != KDA_OK) return e;
-  if (f->cu_seqlens != nullptr) return KDA_ERR_UNSUPPORTED;
   if ((a->dA_log || a->ddt_bias) && f->A_log == nullptr) return KDA_ERR_NULL;
   if (a->do_norm_w && f->o_norm_w == nullptr) return KDA_ERR_NULL;
   if (a->do_gate && f->o_gate == nullptr) return KDA_ERR_NULL;
@@ -687,13 +691,13 @@ kda_status kda_prefill_backward(const kda_backward_args* a, void* ws, size_t ws_
   if (f->T == 0) {
     // nothing flows: dS0 = dS_T; the filter and history gradients are zero
     if (a->dS0 != nullptr &&
-        kda::launch_copy_state(a->dS_T, a->dS0, (size_t)f->B * f->H * f->D * f->D, st) != hipSuccess)
+        kda::launch_copy_state(a->dS_T, a->dS0, (size_t)sz.NS * f->H * f->D * f->D, st) != hipSuccess)
       return KDA_ERR_HIP;
     if (a->dconv_w != nullptr &&
         kda::launch_copy_state(nullptr, a->dconv_w, (size_t)3 * f->H * f->D * f->conv_k, st) != hipSuccess)
       return KDA_ERR_HIP;
     if (a->dconv_state != nullptr &&
-        kda::launch_copy_state(nullptr, a->dconv_state, (size_t)f->B * 3 * 3 * f->H * f->D, st) != hipSuccess)
+        kda::launch_copy_state(nullptr, a->dconv_state, (size_t)sz.NS * 3 * 3 * f->H * f->D, st) != hipSuccess)
       return KDA_ERR_HIP;
     // sums over no tokens
     for (auto [p, n] : {std::pair<float*, size_t>{a->dA_log, (size_t)f->H},
@@ -742,6 +746,8 @@ kda_status kda_prefill_backward(const kda_backward_args* a, void* ws, size_t ws_
     q.dz = a->do_gate;
     q.dw_part = F(L.dwp);
     q.rows = (long)f->B * f->T * f->H;
+    q.H = f->H;
+    q.seqs = seq_tables(f, ws);
     if (kda_status e = hip_status(kda::launch_bwd_out_stage(q, a->do_norm_w, f->D, fp32, st)); e != KDA_OK)
       return e;
     kda::OutStageParams os{};
@@ -754,6 +760,22 @@ kda_status kda_prefill_backward(const kda_backward_args* a, void* ws, size_t ws_
     dO = wsb + L.dOp;
   }
   // backward
+  const kda::SeqTables seqs = seq_tables(f, ws);  // packed: written by the preparation above
+  int* fstart = nullptr;
+  if (packed(f)) {
+    // the same bounds and chunk slots again, plus each sequence's first block slot
+    // of the backward front end
+    kda::IndexParams ip{};
+    ip.cu_seqlens = f->cu_seqlens;
+    ip.bounds = const_cast<int*>(seqs.bounds);
+    ip.cstart = const_cast<int*>(seqs.cstart);
+    ip.n_seqs = f->n_seqs;
+    ip.T = f->T;
+    ip.C = f->chunk;
+    ip.fstart = fstart = reinterpret_cast<int*>(wsb + L.fst);
+    ip.FB = kda::bwd_front_tokens(f->D);
+    if (kda_status e = hip_status(kda::launch_seq_index(ip, st)); e != KDA_OK) return e;
+  }
   kda::BwdLaunch B{};
   const char* recs = wsb + ws_layout(f).records;
   B.walk.ws = recs;
@@ -762,7 +784,8 @@ kda_status kda_prefill_backward(const kda_backward_args* a, void* ws, size_t ws_
   B.walk.dS0 = a->dS0;
   B.walk.dU = wsb + L.dU;
   B.walk.ckdS = wsb + L.ckdS;
-  B.walk.B = f->B; B.walk.T = f->T; B.walk.H = f->H; B.walk.NT = sz.NT;
+  B.walk.B = sz.NS; B.walk.T = f->T; B.walk.H = f->H; B.walk.NT = sz.NT;  // one walk per sequence
+  B.walk.seqs = seqs;
   B.prod.ws = recs;
   B.prod.dO = dO;
   B.prod.ckS = wsb + L.ckS;
@@ -771,11 +794,13 @@ kda_status kda_prefill_backward(const kda_backward_args* a, void* ws, size_t ws_
   B.prod.dQL = F(L.dQL); B.prod.dW = F(L.dW); B.prod.dKt = F(L.dKt); B.prod.dP = F(L.dP);
   B.prod.dLC = F(L.dLC);
   B.prod.B = f->B; B.prod.T = f->T; B.prod.H = f->H; B.prod.NT = sz.NT;
+  B.prod.seqs = seqs;
   B.tside.tT = F(L.tT);
   B.tside.y = wsb + L.y; B.tside.gam = F(L.gam); B.tside.beta = F(L.beta);
   B.tside.dW = F(L.dW); B.tside.dU = wsb + L.dU;
   B.tside.dBk = F(L.dBk); B.tside.dBv = F(L.dBv); B.tside.dA = F(L.dA);
   B.tside.B = f->B; B.tside.T = f->T; B.tside.H = f->H; B.tside.NT = sz.NT;
+  B.tside.seqs = seqs;
   B.pair.y = wsb + L.y; B.pair.gam = F(L.gam); B.pair.beta = F(L.beta);
   B.pair.dA = F(L.dA); B.pair.dP = F(L.dP); B.pair.dQL = F(L.dQL); B.pair.dKt = F(L.dKt);
   B.pair.dLC = F(L.dLC); B.pair.dBk = F(L.dBk); B.pair.dBv = F(L.dBv);
@@ -783,6 +808,7 @@ kda_status kda_prefill_backward(const kda_backward_args* a, void* ws, size_t ws_
   B.pair.ex_count = reinterpret_cast<unsigned*>(wsb + L.pl);
   B.pair.ex_list = B.pair.ex_count + 64;
   B.pair.B = f->B; B.pair.T = f->T; B.pair.H = f->H; B.pair.NT = sz.NT;
+  B.pair.seqs = seqs;
   B.front.q = f->q; B.front.k = f->k; B.front.v = f->v;
   B.front.conv_w = f->conv_k > 0 ? f->conv_w : nullptr;
   B.front.conv_state_in = f->conv_k > 0 ? f->conv_state_in : nullptr;
@@ -794,10 +820,17 @@ kda_status kda_prefill_backward(const kda_backward_args* a, void* ws, size_t ws_
   B.front.l2 = (f->flags & KDA_FLAG_L2NORM_QK) ? 1 : 0;
   B.front.eps = f->l2_eps;
   B.front.scale = f->scale;
+  B.front.seqs = seqs;
+  B.front.fstart = fstart;
+  B.front.nfslots = packed(f) ? (int)L.nfront : 0;
   B.dbeta = a->dbeta;
   B.dconv_w = a->dconv_w;
   if (kda_status e = hip_status(kda::launch_backward(B, f->D, f->chunk, fp32, st)); e != KDA_OK)
     return e;
+  if (packed(f) && f->conv_k > 0 &&
+      hip_status(kda::launch_bwd_empty_history(a->dconv_state, seqs.bounds, f->n_seqs,
+                                               (long)3 * (f->conv_k - 1) * f->H * f->D, st)) != KDA_OK)
+    return KDA_ERR_HIP;
   const bool logits = (f->flags & KDA_FLAG_BETA_LOGITS) != 0;
   if (f->A_log != nullptr || logits) {
     kda::BwdActParams q{};
@@ -811,6 +844,7 @@ kda_status kda_prefill_backward(const kda_backward_args* a, void* ws, size_t ws_
     q.dbeta = a->dbeta;
     q.tokens = (long)f->B * f->T;
     q.H = f->H;
+    q.seqs = seqs;
     if (kda_status e = hip_status(kda::launch_bwd_act(q, a->dA_log, a->ddt_bias, f->D, fp32, st));
         e != KDA_OK)
       return e;

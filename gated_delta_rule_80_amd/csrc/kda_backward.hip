@@ -26,6 +26,39 @@
 
 namespace kda {
 
+// Tokens of record `rec`: `tok` is the token row of its first token (rows of the
+// [rows of tokens][H][D] tensors are tok + t), `nval` how many of its C tokens
+// exist (0 for an unused slot of a packed batch), h its head.  B equal-length
+// sequences: rec = (b H + h) NT + n.  Packed: rec = h NT + slot, the slot a
+// chunk of the sequence that owns it (the workspace tables).
+struct RecTok {
+  long tok;
+  int nval, h;
+};
+__device__ __forceinline__ RecTok rec_tokens(int rec, int T, int H, int NT, int C, const SeqTables& sq) {
+  RecTok g;
+  if (sq.bounds == nullptr) {
+    const int n = rec % NT, bh = rec / NT;
+    g.h = bh % H;
+    g.tok = (long)(bh / H) * T + (long)n * C;
+    const int rem = T - n * C;
+    g.nval = rem < C ? (rem > 0 ? rem : 0) : C;
+  } else {
+    const int slot = rec % NT;
+    g.h = rec / NT;
+    g.tok = 0;
+    g.nval = 0;
+    if (slot < sq.cstart[sq.n_seqs]) {
+      const int sq_i = seq_of_slot(sq.cstart, sq.n_seqs, slot);
+      const int n = slot - sq.cstart[sq_i];
+      const int rem = sq.bounds[sq_i + 1] - sq.bounds[sq_i] - n * C;
+      g.tok = sq.bounds[sq_i] + (long)n * C;
+      g.nval = rem < C ? (rem > 0 ? rem : 0) : C;
+    }
+  }
+  return g;
+}
+
 // ----------------------------------------------------------------- reverse walk
 // The part of a forward record the reverse walk reads, as an LDS image (byte
 // offsets): W [C][D], QL [C][D], KT [D][C], P [C][C] (swizzled as in the
@@ -43,9 +76,9 @@ struct BwdImage {
   static_assert(BYTES % 16 == 0, "whole 16-byte chunks");
 };
 
-// One workgroup per (b, h, block of VB value columns); the D x VB block of dS
-// stays in matrix-core accumulators, walking the chunks from the last to the
-// first.  Per chunk, in the NT products C[i][j] = sum_k A[i][k] B[j][k]:
+// One workgroup per (sequence b, h, block of VB value columns); the D x VB block
+// of dS stays in matrix-core accumulators, walking the sequence's chunks from the
+// last to the first.  Per chunk, in the NT products C[i][j] = sum_k A[i][k] B[j][k]:
 //   dU (t, v):  A = P^T rows t (P's column t, k = j >= t), B = dO^T rows v;
 //               + A = Ktil rows t (KT's column t, k = c),  B = dS'^T rows v
 //   dS (c, v):  A = QL^T rows c (QL's column c, k = t),   B = dO^T rows v;
@@ -82,8 +115,19 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_walk_kernel(BwdWalkParams p) {
   const int bh = blockIdx.x / NV;
   const int h = bh % p.H, b = bh / p.H;
   const int vb0 = vblk * VB;
-  const size_t rec0 = (size_t)bh * p.NT;
   const size_t HD = (size_t)p.H * D;
+  // the sequence's records, first token row and length
+  size_t rec0 = (size_t)bh * p.NT;
+  long tok0 = (long)b * p.T;
+  int Tq = p.T, nch = p.NT;
+  if (p.seqs.bounds != nullptr) {
+    const int c0 = p.seqs.cstart[b];
+    tok0 = p.seqs.bounds[b];
+    Tq = p.seqs.bounds[b + 1] - p.seqs.bounds[b];
+    nch = (Tq + C - 1) / C;
+    if (c0 + nch > p.NT) nch = c0 < p.NT ? p.NT - c0 : 0;  // inconsistent tables: stay in the head's slots
+    rec0 = (size_t)h * p.NT + c0;
+  }
 
   const int R = wave % RT;
   const bool has_u = FULL_U || wave < RT * VT;
@@ -135,8 +179,8 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_walk_kernel(BwdWalkParams p) {
       const int idx = it * NT + tid;
       const int tt = idx / (VB / 8), v8 = idx % (VB / 8);
       const int t = n * C + tt;
-      if (idx < DOP && t < p.T)
-        dor[it].load(static_cast<const IO*>(p.dO) + ((size_t)b * p.T + t) * HD + (size_t)h * D + vb0 +
+      if (idx < DOP && t < Tq)
+        dor[it].load(static_cast<const IO*>(p.dO) + ((size_t)tok0 + t) * HD + (size_t)h * D + vb0 +
                      8 * v8);
       else
         dor[it] = Raw8<IO>{};
@@ -188,11 +232,11 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_walk_kernel(BwdWalkParams p) {
   const E* iP = reinterpret_cast<const E*>(img + IMG::P);
   const float* iLC = reinterpret_cast<const float*>(img + IMG::LC);
 
-  if (p.NT > 0) {
-    issue_copy(p.NT - 1);
-    load_do(p.NT - 1);
+  if (nch > 0) {
+    issue_copy(nch - 1);
+    load_do(nch - 1);
   }
-  for (int n = p.NT - 1; n >= 0; --n) {
+  for (int n = nch - 1; n >= 0; --n) {
     __builtin_amdgcn_s_waitcnt(0);  // image and dO of chunk n
     stage_do(n);
     lds_barrier();
@@ -327,16 +371,16 @@ __global__ __launch_bounds__(256) void kda_bwd_prod_kernel(BwdProdParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g4 = lane >> 4;
   const int rec = blockIdx.x;
-  const int n = rec % p.NT;
-  const int bh = rec / p.NT;
-  const int h = bh % p.H, b = bh / p.H;
+  const RecTok rt = rec_tokens(rec, p.T, p.H, p.NT, C, p.seqs);
+  if (rt.nval == 0) return;  // an unused slot: nothing reads its products
+  const int h = rt.h;
   const size_t HD = (size_t)p.H * D;
   const E* ckS = static_cast<const E*>(p.ckS) + (size_t)rec * ((size_t)D * D + (size_t)C * D);  // [c][v]
   const E* ckU = ckS + (size_t)D * D;                                                         // [t][v]
   const E* ckdS = static_cast<const E*>(p.ckdS) + (size_t)rec * D * D;     // [c][v]
   const E* gdU = static_cast<const E*>(p.dU) + (size_t)rec * C * D;         // [t][v]
-  const IO* gdO = static_cast<const IO*>(p.dO) + ((size_t)b * p.T + (size_t)n * C) * HD + (size_t)h * D;
-  const int nval = p.T - n * C < C ? p.T - n * C : C;
+  const IO* gdO = static_cast<const IO*>(p.dO) + (size_t)rt.tok * HD + (size_t)h * D;
+  const int nval = rt.nval;
 
   // dO fragment of row t (zero past the end of the sequence)
   auto load_do = [&](RowFrag<E, D>& f, int t) {
@@ -492,9 +536,10 @@ __global__ __launch_bounds__(512) void kda_bwd_t_kernel(BwdTParams p) {
     f32x4 tt[NC];
   };
   auto load_stage = [&](int rec, int tid, Stage& S) {
-    const int n = rec % p.NT;
-    const int bh = rec / p.NT;
-    const int h = bh % p.H, b = bh / p.H;
+    // (an unused slot of a packed batch reads token row 0 with beta = 0; nothing
+    // reads what it produces)
+    const RecTok rt = rec_tokens(rec, p.T, p.H, p.NT, C, p.seqs);
+    const int h = rt.h;
     const float* gdW = static_cast<const float*>(p.dW) + (size_t)rec * C * D;
     const E* gdU = static_cast<const E*>(p.dU) + (size_t)rec * C * D;  // [t][v]
     const float* gTt = static_cast<const float*>(p.tT) + (size_t)rec * C * C;
@@ -516,14 +561,13 @@ __global__ __launch_bounds__(512) void kda_bwd_t_kernel(BwdTParams p) {
         load8(gdU + (size_t)t * D + c8, S.du[i]);
         // rows past the end of the sequence read the last row and take beta = 0
         // (no branch around the loads, so they stay in flight)
-        const int tg = n * C + t;
-        const int tc = tg < p.T ? tg : p.T - 1;
-        const size_t row = ((size_t)b * p.T + tc) * HD + (size_t)h * D + c8;
+        const int tc = t < rt.nval ? t : (rt.nval > 0 ? rt.nval - 1 : 0);
+        const size_t row = ((size_t)rt.tok + tc) * HD + (size_t)h * D + c8;
         load8(static_cast<const E*>(p.y) + plane + row, S.kk[i]);
         load8(static_cast<const E*>(p.y) + 2 * plane + row, S.vv[i]);
         load8(p.gam + row, S.gg[i]);
-        const float bv = p.beta[((size_t)b * p.T + tc) * p.H + h];
-        S.bt[i] = tg < p.T ? bv : 0.f;
+        const float bv = p.beta[((size_t)rt.tok + tc) * p.H + h];
+        S.bt[i] = t < rt.nval ? bv : 0.f;
       }
     }
   };
@@ -682,9 +726,9 @@ __global__ __launch_bounds__(512) void kda_bwd_t16_kernel(BwdTParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g4 = lane >> 4;
   const int rec = blockIdx.x;
-  const int n = rec % p.NT;
-  const int bh = rec / p.NT;
-  const int h = bh % p.H, b = bh / p.H;
+  const RecTok rt = rec_tokens(rec, p.T, p.H, p.NT, C, p.seqs);
+  if (rt.nval == 0) return;  // an unused slot: nothing reads its products
+  const int h = rt.h;
   const size_t HD = (size_t)p.H * D;
   const size_t plane = (size_t)p.B * p.T * HD;
 
@@ -713,15 +757,14 @@ __global__ __launch_bounds__(512) void kda_bwd_t16_kernel(BwdTParams p) {
   // the last row and take beta = 0
   for (int it = tid; it < C * D / 8; it += NT) {
     const int t = it / (D / 8), c8 = 8 * (it % (D / 8));
-    const int tg = n * C + t;
-    const int tc = tg < p.T ? tg : p.T - 1;
-    const size_t row = ((size_t)b * p.T + tc) * HD + (size_t)h * D + c8;
+    const int tc = t < rt.nval ? t : rt.nval - 1;
+    const size_t row = ((size_t)rt.tok + tc) * HD + (size_t)h * D + c8;
     float kk[8], vv[8], gg[8];
     load8(static_cast<const __bf16*>(p.y) + plane + row, kk);
     load8(static_cast<const __bf16*>(p.y) + 2 * plane + row, vv);
     load8(p.gam + row, gg);
-    const float bv = p.beta[((size_t)b * p.T + tc) * p.H + h];
-    const float bt = tg < p.T ? bv : 0.f;
+    const float bv = p.beta[((size_t)rt.tok + tc) * p.H + h];
+    const float bt = t < rt.nval ? bv : 0.f;
     bf16x8 xk, xv;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -889,13 +932,13 @@ __global__ __launch_bounds__(4 * D, D / 32 > 1 ? D / 32 : 1) void kda_bwd_pair_m
   const int r = lane & 15, g4 = lane >> 4;
   const int c = 16 * wave + r;  // this lane's channel
   const int rec = blockIdx.x;
-  const int n = rec % p.NT;
-  const int bh = rec / p.NT;
-  const int h = bh % p.H, b = bh / p.H;
+  const RecTok rt = rec_tokens(rec, p.T, p.H, p.NT, C, p.seqs);
+  if (rt.nval == 0) return;  // an unused slot of a packed batch
+  const int h = rt.h;
   const size_t HD = (size_t)p.H * D;
   const size_t plane = (size_t)p.B * p.T * HD;
-  const int nval = p.T - n * C < C ? p.T - n * C : C;  // tokens of the sequence in this chunk
-  auto row_of = [&](int t) { return ((size_t)b * p.T + (size_t)n * C + t) * HD + (size_t)h * D; };
+  const int nval = rt.nval;  // tokens of the sequence in this chunk
+  auto row_of = [&](int t) { return ((size_t)rt.tok + t) * HD + (size_t)h * D; };
   // Gamma of row t (past the end of the sequence g = 0: Gamma keeps its last value)
   auto gam_at = [&](int t) { return p.gam[row_of(t < nval ? t : nval - 1) + c]; };
   const E* y = static_cast<const E*>(p.y);
@@ -910,7 +953,7 @@ __global__ __launch_bounds__(4 * D, D / 32 > 1 ? D / 32 : 1) void kda_bwd_pair_m
     kB[s] = in ? to_f32(y[plane + row_of(t) + c]) : 0.f;
     qB[s] = in ? to_f32(y[row_of(t) + c]) : 0.f;
   }
-  if (tid < C) sB[tid] = tid < nval ? p.beta[((size_t)b * p.T + (size_t)n * C + tid) * p.H + h] : 0.f;
+  if (tid < C) sB[tid] = tid < nval ? p.beta[((size_t)rt.tok + tid) * p.H + h] : 0.f;
   // block boundaries G_1 .. G_NB (Gamma at the last row of each block: lane
   // (r, 3), s = 4 p + 3) and the midpoints m_p = (G_p + G_p+1) / 2, G_0 = 0
   float mid[NB], gbd[NB + 1];  // midpoints, block boundaries G_0 = 0, G_1, ...
@@ -1073,7 +1116,7 @@ __global__ __launch_bounds__(4 * D, D / 32 > 1 ? D / 32 : 1) void kda_bwd_pair_m
     float acc = 0.f;
 #pragma unroll
     for (int w = 0; w < D / 16; ++w) acc += sdbw[w * C + tid];
-    p.dbeta_part[((size_t)b * p.T + (size_t)n * C + tid) * p.H + h] = acc;
+    p.dbeta_part[((size_t)rt.tok + tid) * p.H + h] = acc;
   }
   // dg: reverse running sum over the chunk.  Thread (channel cc, segment sg) takes
   // the SL tokens of segment sg: the segment totals go through LDS, then each
@@ -1139,13 +1182,13 @@ __global__ __launch_bounds__(D * (C / 16)) void kda_bwd_pair_kernel(BwdPairParam
   if (blockIdx.x >= *p.ex_count) return;
   const int rec = (int)p.ex_list[blockIdx.x];
   if (rec >= p.B * p.H * p.NT) return;  // (the list holds record indices only)
-  const int n = rec % p.NT;
-  const int bh = rec / p.NT;
-  const int h = bh % p.H, b = bh / p.H;
+  const RecTok rt = rec_tokens(rec, p.T, p.H, p.NT, C, p.seqs);
+  if (rt.nval == 0) return;
+  const int h = rt.h;
   const size_t HD = (size_t)p.H * D;
   const size_t plane = (size_t)p.B * p.T * HD;
-  const int nval = p.T - n * C < C ? p.T - n * C : C;  // tokens of the sequence in this chunk
-  auto row_of = [&](int t) { return ((size_t)b * p.T + (size_t)n * C + t) * HD + (size_t)h * D; };
+  const int nval = rt.nval;  // tokens of the sequence in this chunk
+  auto row_of = [&](int t) { return ((size_t)rt.tok + t) * HD + (size_t)h * D; };
 
   const E* gdA = static_cast<const E*>(p.dA) + (size_t)rec * C * C;
   const E* gdP = static_cast<const E*>(p.dP) + (size_t)rec * C * C;
@@ -1175,7 +1218,7 @@ __global__ __launch_bounds__(D * (C / 16)) void kda_bwd_pair_kernel(BwdPairParam
     *reinterpret_cast<f32x4*>(&sG[t * LD + c4]) = gg;
   }
   for (int t = tid; t < C; t += NTH)
-    sB[t] = t < nval ? p.beta[((size_t)b * p.T + (size_t)n * C + t) * p.H + h] : 0.f;
+    sB[t] = t < nval ? p.beta[((size_t)rt.tok + t) * p.H + h] : 0.f;
   __syncthreads();
 
   const int c = tid / TPC, tq = tid % TPC;
@@ -1294,7 +1337,7 @@ __global__ __launch_bounds__(D * (C / 16)) void kda_bwd_pair_kernel(BwdPairParam
   if (tid < nval) {
     float acc = 0.f;
     for (int cc = 0; cc < D; ++cc) acc += sdb[tid * LD + cc];
-    p.dbeta_part[((size_t)b * p.T + (size_t)n * C + tid) * p.H + h] = acc;
+    p.dbeta_part[((size_t)rt.tok + tid) * p.H + h] = acc;
   }
 }
 
@@ -1325,15 +1368,42 @@ __global__ __launch_bounds__(256, 2) void kda_bwd_front_kernel(BwdFrontParams p,
   __shared__ float sred[4][3 * 4 * D];       // filter partials per wave [x][tap][c]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nblk = (p.T + TOKB - 1) / TOKB;
-  const int blk = blockIdx.x % nblk;
-  const int bh = blockIdx.x / nblk;
-  const int h = bh % p.H, b = bh / p.H;
+  const size_t HD = (size_t)p.H * D;
+  // the workgroup's sequence b, head h, block of the sequence, the sequence's
+  // first token row and length, and the slot of its filter partial
+  int h, b, blk, Tq, part;
+  long tok0;
+  if (p.seqs.bounds == nullptr) {
+    const int nblk = (p.T + TOKB - 1) / TOKB;
+    blk = blockIdx.x % nblk;
+    const int bh = blockIdx.x / nblk;
+    h = bh % p.H;
+    b = bh / p.H;
+    Tq = p.T;
+    tok0 = (long)b * p.T;
+    part = b * nblk + blk;
+  } else {
+    part = blockIdx.x % p.nfslots;
+    h = blockIdx.x / p.nfslots;
+    const bool used = part < p.fstart[p.seqs.n_seqs];
+    b = used ? seq_of_slot(p.fstart, p.seqs.n_seqs, part) : 0;
+    blk = used ? part - p.fstart[b] : 0;
+    tok0 = used ? p.seqs.bounds[b] : 0;
+    Tq = used ? p.seqs.bounds[b + 1] - p.seqs.bounds[b] : 0;
+    if (!used || blk * TOKB >= Tq) {
+      // a slot no sequence uses: its filter partial is zero
+      if (p.conv_w != nullptr)
+        for (int it = tid; it < 3 * 4 * D; it += 256) {
+          const int x = it / (4 * D), tau = (it / D) % 4, c = it % D;
+          p.dconv_part[((size_t)part * 3 + x) * HD * 4 + ((size_t)h * D + c) * 4 + tau] = 0.f;
+        }
+      return;
+    }
+  }
   const int s = tid / NOCT, j = tid % NOCT;
   const int ch = 8 * j;
   const int t0 = blk * TOKB;
   const int tf = t0 + 4 * s;
-  const size_t HD = (size_t)p.H * D;
   const size_t plane = (size_t)p.B * p.T * HD;
   const bool conv = p.conv_w != nullptr;
   if (conv)
@@ -1366,9 +1436,9 @@ __global__ __launch_bounds__(256, 2) void kda_bwd_front_kernel(BwdFrontParams p,
     {
       constexpr int ES = (int)sizeof(IO);
       const int r0 = t0 - 3 > 0 ? t0 - 3 : 0;
-      const int r1 = t0 + TOKB + 3 < p.T ? t0 + TOKB + 3 : p.T;
+      const int r1 = t0 + TOKB + 3 < Tq ? t0 + TOKB + 3 : Tq;
       const int row_b = (int)(HD * ES);
-      const BufRes rx = make_buf(src + ((size_t)b * p.T + r0) * HD + (size_t)h * D,
+      const BufRes rx = make_buf(src + ((size_t)tok0 + r0) * HD + (size_t)h * D,
                                  (unsigned)(((long)(r1 - 1 - r0) * HD + D) * ES));
       const int voff = (tf - 3 - r0) * row_b + ch * ES;
 #pragma unroll
@@ -1376,8 +1446,8 @@ __global__ __launch_bounds__(256, 2) void kda_bwd_front_kernel(BwdFrontParams p,
       const int hoff = (t0 + TOKB + hc - 3 - r0) * row_b + ch * ES;
 #pragma unroll
       for (int m = 0; m < 4; ++m) hw[m].load(rx, hoff + m * row_b, 0);
-      const int rz1 = t0 + TOKB + 3 < p.T ? t0 + TOKB + 3 : p.T;
-      const BufRes rz = make_buf(static_cast<const IO*>(p.dy) + x * plane + ((size_t)b * p.T + t0) * HD +
+      const int rz1 = t0 + TOKB + 3 < Tq ? t0 + TOKB + 3 : Tq;
+      const BufRes rz = make_buf(static_cast<const IO*>(p.dy) + x * plane + ((size_t)tok0 + t0) * HD +
                                      (size_t)h * D,
                                  (unsigned)(((long)(rz1 - 1 - t0) * HD + D) * ES));
       const int zoff = (tf - t0) * row_b + ch * ES;
@@ -1485,14 +1555,14 @@ __global__ __launch_bounds__(256, 2) void kda_bwd_front_kernel(BwdFrontParams p,
       const f32x4 hi = *reinterpret_cast<const f32x4*>(&sdp[(4 * s + u) * LDP + ch + 4]);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        dpo[u][c] = tf + u < p.T ? lo[c] : 0.f;
-        dpo[u][c + 4] = tf + u < p.T ? hi[c] : 0.f;
+        dpo[u][c] = tf + u < Tq ? lo[c] : 0.f;
+        dpo[u][c + 4] = tf + u < Tq ? hi[c] : 0.f;
       }
     }
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int t = tf + m;
-      if (t < p.T) {
+      if (t < Tq) {
         float dx[8];
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
@@ -1502,7 +1572,7 @@ __global__ __launch_bounds__(256, 2) void kda_bwd_front_kernel(BwdFrontParams p,
           else
             dx[c] = dpo[m][c];
         }
-        store8(dst + ((size_t)b * p.T + t) * HD + (size_t)h * D + ch, dx);
+        store8(dst + ((size_t)tok0 + t) * HD + (size_t)h * D + ch, dx);
       }
     }
     if (conv) {
@@ -1543,15 +1613,15 @@ __global__ __launch_bounds__(256, 2) void kda_bwd_front_kernel(BwdFrontParams p,
     for (int it = tid; it < 3 * 4 * D; it += 256) {
       const int x = it / (4 * D), tau = (it / D) % 4, c = it % D;
       const float acc = sred[0][it] + sred[1][it] + sred[2][it] + sred[3][it];
-      p.dconv_part[(((size_t)b * nblk + blk) * 3 + x) * HD * 4 + ((size_t)h * D + c) * 4 + tau] = acc;
+      p.dconv_part[((size_t)part * 3 + x) * HD * 4 + ((size_t)h * D + c) * 4 + tau] = acc;
     }
   }
   if (dbeta != nullptr && j == 0) {
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int t = tf + m;
-      if (t < p.T) {
-        const size_t o = ((size_t)b * p.T + t) * p.H + h;
+      if (t < Tq) {
+        const size_t o = ((size_t)tok0 + t) * p.H + h;
         float acc = 0.f;
         for (int q = 0; q < nparts; ++q) acc += dbeta_part[(size_t)q * p.B * p.T * p.H + o];
         dbeta[o] = acc;
@@ -1578,7 +1648,8 @@ __global__ __launch_bounds__(256) void kda_bwd_conv_reduce_kernel(const float* p
 // ------------------------------------------------------------------ launchers
 template <int D, int C, typename IO, typename E>
 static hipError_t launch_bwd_t(const BwdLaunch& L, hipStream_t st) {
-  const size_t nrec = (size_t)L.walk.B * L.walk.H * L.walk.NT;
+  // records (packed: one row of tokens, H * NT slots); walks per (sequence, head)
+  const size_t nrec = (size_t)L.prod.B * L.prod.H * L.prod.NT;
   const size_t BH = (size_t)L.walk.B * L.walk.H;
   // reverse walk: the forward walk's value blocks
   if constexpr (D == 128 && sizeof(E) == 2) {
@@ -1617,13 +1688,15 @@ static hipError_t launch_bwd_t(const BwdLaunch& L, hipStream_t st) {
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   constexpr int TOKB = 4 * (256 / (D / 8));
   const size_t nblk = ((size_t)L.front.T + TOKB - 1) / TOKB;
-  hipLaunchKernelGGL((kda_bwd_front_kernel<D, IO>), dim3((unsigned)(BH * nblk)), dim3(256), 0, st, L.front,
-                     L.pair.dbeta_part, NBLK, L.dbeta);
+  // filter partials: one per (sequence, block) slot
+  const size_t nparts = L.front.seqs.bounds != nullptr ? (size_t)L.front.nfslots : (size_t)L.front.B * nblk;
+  hipLaunchKernelGGL((kda_bwd_front_kernel<D, IO>), dim3((unsigned)(L.front.H * nparts)), dim3(256), 0, st,
+                     L.front, L.pair.dbeta_part, NBLK, L.dbeta);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   if (L.front.conv_w != nullptr) {
     const size_t n = (size_t)3 * L.front.H * D * 4;
     hipLaunchKernelGGL(kda_bwd_conv_reduce_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                       L.front.dconv_part, L.dconv_w, n, (int)(L.front.B * nblk));
+                       L.front.dconv_part, L.dconv_w, n, (int)nparts);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   }
   return hipSuccess;
@@ -1640,6 +1713,7 @@ static hipError_t launch_bwd_c(const BwdLaunch& L, int C, hipStream_t st) {
 }
 
 size_t bwd_front_blocks(int T, int D) { return ((size_t)T + 4 * (256 / (D / 8)) - 1) / (4 * (256 / (D / 8))); }
+int bwd_front_tokens(int D) { return 4 * (256 / (D / 8)); }
 
 hipError_t launch_backward(const BwdLaunch& L, int D, int C, bool fp32, hipStream_t st) {
   if (fp32) {

@@ -20,6 +20,12 @@
 
 namespace kda {
 
+// Whether token t belongs to a sequence (packed batches: the clamped bounds are
+// non-decreasing, so the sequences cover [bounds[0], bounds[n_seqs]) exactly).
+__device__ __forceinline__ bool token_in_seqs(long t, const SeqTables& sq) {
+  return sq.bounds == nullptr || (t >= sq.bounds[0] && t < sq.bounds[sq.n_seqs]);
+}
+
 // One pass over the rows: D / 8 threads per row, each with 8 consecutive
 // channels; a workgroup takes RPW rows at a time and strides over the rows
 // with the grid.
@@ -39,7 +45,7 @@ __global__ __launch_bounds__(256) void kda_bwd_out_kernel(BwdOutParams p) {
   // every thread runs the same number of passes (the group sums need the whole row)
   for (long base = (long)blockIdx.x * RPW; base < p.rows; base += (long)gridDim.x * RPW) {
     const long row = base + rr;
-    const bool ok = row < p.rows;
+    const bool ok = row < p.rows && token_in_seqs(row / p.H, p.seqs);
     float x[8], z[8], dy[8];
 #pragma unroll
     for (int c = 0; c < 8; ++c) x[c] = z[c] = dy[c] = 0.f;
@@ -124,7 +130,7 @@ __global__ __launch_bounds__(256) void kda_bwd_act_kernel(BwdActParams p) {
   }
   for (long base = (long)blockIdx.x * TPW; base < p.tokens; base += (long)gridDim.x * TPW) {
     const long t = base + tt;
-    if (t >= p.tokens) continue;  // no cross-lane work in this loop
+    if (t >= p.tokens || !token_in_seqs(t, p.seqs)) continue;  // no cross-lane work in this loop
     const size_t row = ((size_t)t * H + h) * D + 8 * j;
     if (act) {
       float f[8], dg[8];
@@ -162,6 +168,28 @@ __global__ __launch_bounds__(256) void kda_bwd_act_kernel(BwdActParams p) {
     for (int q = 0; q < 256; ++q) acc += sda[q];
     p.dA_part[(size_t)blockIdx.x * H + h] = acc;
   }
+}
+
+// Packed batches: the conv-history gradient of every empty sequence is zero (no
+// front-end workgroup covers such a sequence); the others' entries are left alone.
+__global__ __launch_bounds__(256) void kda_bwd_empty_history_kernel(float* dconv_state, const int* bounds,
+                                                                    int n_seqs, long per_seq) {
+  const long total = (long)n_seqs * per_seq;
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < total; i += (long)gridDim.x * 256) {
+    const long s = i / per_seq;
+    if (bounds[s + 1] == bounds[s]) dconv_state[i] = 0.f;
+  }
+}
+
+hipError_t launch_bwd_empty_history(float* dconv_state, const int* bounds, int n_seqs, long per_seq,
+                                    hipStream_t st) {
+  if (dconv_state == nullptr || n_seqs <= 0 || per_seq <= 0) return hipSuccess;
+  const long total = (long)n_seqs * per_seq;
+  const long want = (total + 255) / 256;
+  const unsigned grid = (unsigned)(want < 4096 ? want : 4096);
+  hipLaunchKernelGGL(kda_bwd_empty_history_kernel, dim3(grid), dim3(256), 0, st, dconv_state, bounds, n_seqs,
+                     per_seq);
+  return hipGetLastError();
 }
 
 // out[i] = sum over q = 0 .. nparts - 1 of part[q * n + i], one wave per output:

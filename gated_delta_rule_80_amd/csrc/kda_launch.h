@@ -19,10 +19,14 @@ hipError_t launch_seq_index(const IndexParams& p, hipStream_t st);
 hipError_t launch_copy_state(const float* src, float* dst, size_t n, hipStream_t st);
 hipError_t launch_backward(const BwdLaunch& L, int D, int C, bool fp32, hipStream_t st);
 size_t bwd_front_blocks(int T, int D);
+int bwd_front_tokens(int D);  // tokens per front-end workgroup of the backward
 // the optional stages' backward; dw, dA_log, ddt_bias may be NULL (not written)
 hipError_t launch_bwd_out_stage(const BwdOutParams& p, float* dw, int D, bool fp32, hipStream_t st);
 hipError_t launch_bwd_act(const BwdActParams& p, float* dA_log, float* ddt_bias, int D, bool fp32,
                           hipStream_t st);
+// packed batches: zero the conv-history gradient of the empty sequences
+hipError_t launch_bwd_empty_history(float* dconv_state, const int* bounds, int n_seqs, long per_seq,
+                                    hipStream_t st);
 int bwd_out_groups(long rows, int D);   // workgroups (= partials) of the two
 int bwd_act_groups(long tokens, int D);
 hipError_t launch_decode(const DecodeParams& p, int D, bool fp32, hipStream_t st);

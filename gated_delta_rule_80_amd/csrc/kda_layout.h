@@ -74,6 +74,8 @@ struct IndexParams {
   int n_seqs;
   int T;
   int C;
+  int* fstart;            // or NULL: first block slot per sequence for blocks of FB tokens
+  int FB;
 };
 
 struct PrepParams {
@@ -159,7 +161,8 @@ struct BwdWalkParams {
   float* dS0;          // [B][H][D][D] or NULL
   void* dU;
   void* ckdS;
-  int B, T, H, NT;
+  int B, T, H, NT;   // B: sequences (packed: n_seqs)
+  SeqTables seqs;    // packed sequences, or bounds NULL
 };
 
 struct BwdProdParams {
@@ -173,7 +176,8 @@ struct BwdProdParams {
   void* dKt;
   void* dP;
   float* dLC;
-  int B, T, H, NT;
+  int B, T, H, NT;   // B: rows of tokens (packed: 1)
+  SeqTables seqs;
 };
 
 struct BwdTParams {
@@ -187,6 +191,7 @@ struct BwdTParams {
   void* dBv;
   void* dA;
   int B, T, H, NT;
+  SeqTables seqs;
 };
 
 struct BwdPairParams {
@@ -208,6 +213,7 @@ struct BwdPairParams {
   unsigned* ex_count;
   unsigned* ex_list;
   int B, T, H, NT;
+  SeqTables seqs;
 };
 
 struct BwdFrontParams {
@@ -220,12 +226,17 @@ struct BwdFrontParams {
   float* dq;
   float* dk;
   float* dv;
-  float* dconv_part;          // [B * nblk][3][H*D][4] or NULL
-  float* dconv_state;         // [B][3][3][H*D] or NULL
+  float* dconv_part;          // [blocks][3][H*D][4] or NULL
+  float* dconv_state;         // [sequences][3][3][H*D] or NULL
   int B, T, H;
   int l2;
   float eps;
   float scale;
+  // packed sequences: per sequence its first block slot (exclusive running sum
+  // of its blocks of TOKB tokens); nfslots block slots per head
+  SeqTables seqs;
+  const int* fstart;
+  int nfslots;
 };
 
 // Everything one backward launch sequence needs (the forward part is launched
@@ -251,7 +262,9 @@ struct BwdOutParams {
   void* dx;         // [rows][D] gradient of x (I/O type)
   float* dz;        // [rows][D] gradient of z, or NULL
   float* dw_part;   // [groups][D] partial sums of dw (with the norm)
-  long rows;
+  long rows;        // (token, head) rows
+  int H;
+  SeqTables seqs;   // packed: only tokens [bounds[0], bounds[n_seqs]) count
 };
 
 // Backward of the activations from raw projections, per token and head.
@@ -266,6 +279,7 @@ struct BwdActParams {
   float* dbeta;           // [tokens][H] in: gradient of beta; out: of the logits
   long tokens;
   int H;
+  SeqTables seqs;         // packed: only tokens [bounds[0], bounds[n_seqs]) count
 };
 
 // Most workgroups of the output-stage backward (and 1/8 of that per head for the

@@ -740,7 +740,8 @@ __device__ __forceinline__ int block_scan(int x, int* red) {
 // offsets clamped to [0, T] (so malformed offsets can only give empty or
 // shortened sequences, never an access outside the tensors), and each sequence's
 // first chunk slot, the exclusive running sum of its chunk count (cstart[n_seqs]
-// = slots in use).  One workgroup of 1024 threads, n_seqs + 1 entries in blocks.
+// = slots in use); optionally the same for blocks of FB tokens (fstart).  One
+// workgroup of 1024 threads, n_seqs + 1 entries in blocks.
 __global__ __launch_bounds__(1024) void kda_seq_index_kernel(IndexParams p) {
   __shared__ int red[16];
   __shared__ int carry;
@@ -769,6 +770,19 @@ __global__ __launch_bounds__(1024) void kda_seq_index_kernel(IndexParams p) {
     const int cnt = i < p.n_seqs ? (p.bounds[i + 1] - p.bounds[i] + p.C - 1) / p.C : 0;
     const int incl = block_scan<true>(cnt, red) + carry;
     if (i <= p.n_seqs) p.cstart[i] = incl - cnt;
+    __syncthreads();
+    if (tid == 1023) carry = incl;
+    __syncthreads();
+  }
+  if (p.fstart == nullptr) return;
+  // the same for blocks of FB tokens
+  if (tid == 0) carry = 0;
+  __syncthreads();
+  for (int base = 0; base <= p.n_seqs; base += 1024) {
+    const int i = base + tid;
+    const int cnt = i < p.n_seqs ? (p.bounds[i + 1] - p.bounds[i] + p.FB - 1) / p.FB : 0;
+    const int incl = block_scan<true>(cnt, red) + carry;
+    if (i <= p.n_seqs) p.fstart[i] = incl - cnt;
     __syncthreads();
     if (tid == 1023) carry = incl;
     __syncthreads();

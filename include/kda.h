@@ -270,16 +270,18 @@ kda_status kda_decode_step(const kda_decode_args* a, void* stream);
  * gradient passes back through the output stage first (o is then finished by the
  * stage in place, as kda_prefill's separate output pass does); with the
  * activations, dg and dbeta are the gradients of g and beta as given (the raw
- * gate projection, the logits).  Supported: B equal-length sequences (no packed
- * sequences), fp32 I/O up to D = 64, bf16 I/O up to D = 128.  All gradients are
- * float32; with bf16 I/O the intermediate
+ * gate projection, the logits).  Packed sequences too: dS_T, dS0 and
+ * dconv_state are then per sequence ([n_seqs][...]); the gradients of tokens
+ * outside every sequence (malformed offsets) are left undefined.  Supported:
+ * fp32 I/O up to D = 64, bf16 I/O up to D = 128.  All gradients are float32;
+ * with bf16 I/O the intermediate
  * gradients pass between the kernels in bf16 (relative error of the returned
  * gradients about 4e-3 against an exact computation, at T = 4096, H = 96,
  * D = 128). */
 typedef struct kda_backward_args {
   kda_prefill_args fwd; /* the forward call; its rules apply */
   const void* dO;       /* device [B][T][H][D] io dtype: gradient of o */
-  const float* dS_T;    /* device [B][H][D][D] or NULL (= zeros): gradient of S_T */
+  const float* dS_T;    /* device [B][H][D][D] ([n_seqs][H][D][D] packed) or NULL (= zeros): gradient of S_T */
   float* dq;            /* device [B][T][H][D]: gradient of the raw q */
   float* dk;            /* device [B][T][H][D] */
   float* dv;            /* device [B][T][H][D] */

@@ -389,10 +389,14 @@ def test_backward_validation(lib):
     a.fwd.o_gate = f()
     a.do_gate = f() + 4
     assert vb(a) == ALIGN
-    # unsupported modes
+    # packed sequences: B = 1 and per-sequence states (the forward's rules)
     a = backward()
     a.fwd.B, a.fwd.cu_seqlens, a.fwd.n_seqs = 1, f(), 2
-    assert vb(a) == UNSUP
+    assert vb(a) == OK
+    assert kda.kda_backward_workspace_bytes(a) > 0
+    a.fwd.B = 2
+    assert vb(a) == SHAPE
+    # unsupported modes
     a = backward()
     a.fwd.io, a.fwd.chunk = _lib.KDA_FP32, 32
     assert vb(a) == UNSUP  # fp32 with D = 128
