@@ -13,6 +13,7 @@
 namespace kda {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 // SiLU(x) = x * sigmoid(x) with the hardware exp2 and reciprocal (about 1 ulp each).
 __device__ __forceinline__ float silu_fast(float x) {
@@ -106,15 +107,17 @@ __device__ __forceinline__ void load_filters(const float* conv_w, int H, int h, 
       f.w[i] = *reinterpret_cast<const f32x4*>(conv_w + ((size_t)x * H * D + (size_t)h * D + c) * 4);
   }
 }
+// `mul` scales every tap (kLog2e for front_compute's PRE mode).
 template <int D, int NT>
-__device__ __forceinline__ void store_filters(const FilterRegs<D, NT>& f, float* dst, int tid) {
+__device__ __forceinline__ void store_filters(const FilterRegs<D, NT>& f, float* dst, int tid,
+                                              float mul = 1.0f) {
 #pragma unroll
   for (int i = 0; i < FilterRegs<D, NT>::N; ++i) {
     const int e = tid + NT * i;
     const int x = e / D, c = e % D;
     if (e < 3 * D) {
 #pragma unroll
-      for (int tau = 0; tau < 4; ++tau) dst[(x * 4 + tau) * D + c] = f.w[i][tau];
+      for (int tau = 0; tau < 4; ++tau) dst[(x * 4 + tau) * D + c] = f.w[i][tau] * mul;
     }
   }
 }
@@ -174,19 +177,27 @@ __device__ __forceinline__ void front_load(const IO* q, const IO* k, const IO* v
 
 // conv + SiLU + L2 norm of the rows front_load fetched.  `filt` is the head's
 // [3][4][D] filter block written by store_filters (unused without the
-// convolution).  All
+// convolution).  PRE: the filters were stored times log2(e), so the convolution
+// gives u = log2(e) pre and SiLU(pre) = u sigmoid(pre) / log2(e) with
+// sigmoid(pre) = 1 / (1 + 2^-u): no multiply before the exponential.  The values
+// returned for q and k are exact all the same (the L2 norm divides the factor
+// out, its eps scaled by log2(e)^2; without the norm the factor is folded into
+// the scales), but v is returned times log2(e) (multiply by kLn2) when conv.  All
 // lanes of a group of D/8 consecutive lanes (the channels of one token row) must
 // call this together: the L2 sums are reduced across that group.  On return q is
 // normalised and multiplied by `scale`, k normalised, v convolved; qk[m] =
 // <q_m, k_m> of the returned values (0 unless WANT_QK).  With MASK, tokens >= T
 // and inactive lanes give zeros; without it their outputs are left as computed
 // (finite).
-template <int TOK, int D, typename IO, bool WANT_QK = true, bool MASK = true>
+template <int TOK, int D, typename IO, bool WANT_QK = true, bool MASK = true, bool PRE = false>
 __device__ __forceinline__ void front_compute(const Raw8<IO> (&win)[3][TOK + 3], const float* filt,
                                               bool conv, int ch, int t_first,
                                               int T, bool active, bool l2, float eps, float scale,
                                               float (&yq)[TOK][8], float (&yk)[TOK][8],
                                               float (&yv)[TOK][8], float (&qk)[TOK]) {
+  const bool pre = PRE && conv;                    // q, k, v come out times log2(e)
+  const float unit = pre ? kLn2 : 1.0f;            // undoes that without the norm
+  const float eps_n = pre ? eps * (kLog2e * kLog2e) : eps;
   float (*y[3])[8] = {yq, yk, yv};
 #pragma unroll
   for (int x = 0; x < 3; ++x) {
@@ -216,7 +227,9 @@ __device__ __forceinline__ void front_compute(const Raw8<IO> (&win)[3][TOK + 3],
           acc = fmaf(w[1][c], rows[m + 1][c], acc);
           acc = fmaf(w[2][c], rows[m + 2][c], acc);
           acc = fmaf(w[3][c], rows[m + 3][c], acc);
-          y[x][m][c] = (!MASK || (active && t_first + m < T)) ? silu_fast(acc) : 0.f;
+          const float sv = PRE ? acc * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-acc))
+                               : silu_fast(acc);
+          y[x][m][c] = (!MASK || (active && t_first + m < T)) ? sv : 0.f;
         }
       }
     } else {
@@ -238,8 +251,8 @@ __device__ __forceinline__ void front_compute(const Raw8<IO> (&win)[3][TOK + 3],
     }
     sq = group_sum<G>(sq);
     sk = group_sum<G>(sk);
-    const float rq = (l2 ? __builtin_amdgcn_rsqf(sq + eps) : 1.0f) * scale;
-    const float rk = l2 ? __builtin_amdgcn_rsqf(sk + eps) : 1.0f;
+    const float rq = (l2 ? __builtin_amdgcn_rsqf(sq + eps_n) : unit) * scale;
+    const float rk = l2 ? __builtin_amdgcn_rsqf(sk + eps_n) : unit;
     float d = 0.f;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {

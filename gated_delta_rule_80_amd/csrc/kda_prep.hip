@@ -33,7 +33,7 @@
 
 namespace kda {
 
-constexpr float kFatalSpan2 = 240.f;  // log2 units (~166 nats): widest block span factored
+constexpr float kFatalSpan = 240.f * kLn2;  // widest block span factored (240 log2 units, ~166 nats)
 
 // Threads per workgroup: 256 for bf16 (two workgroups share a compute unit, so
 // one's loads overlap the other's arithmetic), 512 for fp32 (whose rows take
@@ -76,9 +76,9 @@ struct FastSmem {
   static constexpr int R1 = OPS > LAST ? OPS : LAST;
   alignas(16) char r1[R1];
   alignas(16) float tot[NSEG * D];     // segment totals, then exclusive prefixes
-  // per block p and channel, with G_p the cumulative decay before block p and
+  // per block p and channel, with G_p the cumulative decay (nats) before block p and
   // m_p = (G_p + G_{p+1}) / 2:
-  alignas(16) float mid[NB * D];       // m_p
+  alignas(16) float mid[NB * D];       // m_p times log2(e)
   alignas(16) float emid[NB * D];      // exp(m_p)
   alignas(16) float ecm[NB * D];       // exp(Gamma_C - m_p)
   alignas(16) float hs[NB * D];        // exp(-s_p / 2) = exp(G_{p+1} - m_p)
@@ -267,7 +267,7 @@ __global__ __launch_bounds__(fast_threads<E>()) void kda_chunk_prep_kernel(PrepP
     const f32x4* bp = reinterpret_cast<const f32x4*>(p.dt_bias + (size_t)h * D + ch);
     gb0 = bp[0];
     gb1 = bp[1];
-    gneg = -__expf(p.A_log[h]);
+    gneg = -__expf(p.A_log[h]) * kLn2;  // softplus_log2 gives log2 units; the decay is kept in nats
   }
   {
     constexpr int ES = (int)sizeof(IO);
@@ -291,12 +291,14 @@ __global__ __launch_bounds__(fast_threads<E>()) void kda_chunk_prep_kernel(PrepP
   }
   if (tid == 0) sm.fatal = 0;
   __builtin_amdgcn_sched_barrier(0);  // the loads above are all issued first
-  if (conv) store_filters<D, NTH>(fr, sm.filt, tid);
+  if (conv) store_filters<D, NTH>(fr, sm.filt, tid, kLog2e);
   __syncthreads();  // filters are in LDS
+  // filters times log2(e): q and k come out as they are, v times log2(e)
   float yq[TOK][8], yk[TOK][8], yv[TOK][8], qk[TOK];
-  front_compute<TOK, D, IO, false, false>(win, sm.filt, conv, ch, tf, Tq, active, p.l2 != 0,
-                                          p.eps, p.scale, yq, yk, yv, qk);
-  // cumulative log2-decay within the segment.  Past the end of the sequence g
+  front_compute<TOK, D, IO, false, false, true>(win, sm.filt, conv, ch, tf, Tq, active, p.l2 != 0,
+                                                p.eps, p.scale, yq, yk, yv, qk);
+  const float vunit = conv ? kLn2 : 1.0f;
+  // cumulative decay (nats) within the segment.  Past the end of the sequence g
   // and beta are 0 (the range-checked loads give zeros; the activations of raw
   // projections are masked there), which is all the later phases need of those
   // tokens.
@@ -307,11 +309,11 @@ __global__ __launch_bounds__(fast_threads<E>()) void kda_chunk_prep_kernel(PrepP
     bt[m] = p.beta_logits ? (in_seq ? sigmoid_fast(braw[m]) : 0.f) : braw[m];
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      float gv;  // log2 units
+      float gv;  // nats
       if (gact)
         gv = in_seq ? gneg * softplus_log2(graw[m][c] + (c < 4 ? gb0[c] : gb1[c - 4])) : 0.f;
       else
-        gv = graw[m][c] * kLog2e;
+        gv = graw[m][c];
       gc[m][c] = m == 0 ? gv : gc[m - 1][c] + gv;
     }
   }
@@ -332,23 +334,24 @@ __global__ __launch_bounds__(fast_threads<E>()) void kda_chunk_prep_kernel(PrepP
       acc += v;
       if ((s2 + 1) % SPB == 0) gbl[(s2 + 1) / SPB] = acc;
     }
-    gLC[c] = __builtin_amdgcn_exp2f(acc);
+    // exponentials in base 2 of log2(e) times the decays
+    gLC[c] = __builtin_amdgcn_exp2f(acc * kLog2e);
     bool fatal = false;
     float md[NB];
 #pragma unroll
     for (int q = 0; q < NB; ++q) {
       md[q] = 0.5f * (gbl[q] + gbl[q + 1]);
-      sm.mid[q * D + c] = md[q];
-      sm.emid[q * D + c] = __builtin_amdgcn_exp2f(md[q]);
-      sm.ecm[q * D + c] = __builtin_amdgcn_exp2f(acc - md[q]);
-      sm.hs[q * D + c] = __builtin_amdgcn_exp2f(gbl[q + 1] - md[q]);
-      fatal |= gbl[q] - gbl[q + 1] > kFatalSpan2;
+      sm.mid[q * D + c] = md[q] * kLog2e;  // the operands use it in log2 units
+      sm.emid[q * D + c] = __builtin_amdgcn_exp2f(md[q] * kLog2e);
+      sm.ecm[q * D + c] = __builtin_amdgcn_exp2f((acc - md[q]) * kLog2e);
+      sm.hs[q * D + c] = __builtin_amdgcn_exp2f((gbl[q + 1] - md[q]) * kLog2e);
+      fatal |= gbl[q] - gbl[q + 1] > kFatalSpan;
     }
 #pragma unroll
     for (int R = 1; R < NB; ++R)
 #pragma unroll
       for (int Q = 0; Q < R; ++Q)
-        sm.xf[pair_index(R, Q) * D + c] = __builtin_amdgcn_exp2f(md[R] - gbl[Q + 1]);
+        sm.xf[pair_index(R, Q) * D + c] = __builtin_amdgcn_exp2f((md[R] - gbl[Q + 1]) * kLog2e);
     if (fatal) atomicOr(&sm.fatal, 1);
   }
   __syncthreads();
@@ -366,10 +369,13 @@ __global__ __launch_bounds__(fast_threads<E>()) void kda_chunk_prep_kernel(PrepP
         const long row = (tok0 + t) * HD + (long)h * D + ch;
         store8(static_cast<E*>(p.y_out) + row, yq[m]);
         store8(static_cast<E*>(p.y_out) + plane + row, yk[m]);
-        store8(static_cast<E*>(p.y_out) + 2 * plane + row, yv[m]);
-        float gam[8];
+        float vv[8], gam[8];  // v as it is; the cumulative decay in log2 units
 #pragma unroll
-        for (int c = 0; c < 8; ++c) gam[c] = gc[m][c] + pre[c];
+        for (int c = 0; c < 8; ++c) {
+          vv[c] = yv[m][c] * vunit;
+          gam[c] = (gc[m][c] + pre[c]) * kLog2e;
+        }
+        store8(static_cast<E*>(p.y_out) + 2 * plane + row, vv);
         store8(p.gam_out + row, gam);
         if (j == 0) p.beta_out[(tok0 + t) * p.H + h] = bt[m];
       }
@@ -399,12 +405,13 @@ __global__ __launch_bounds__(fast_threads<E>()) void kda_chunk_prep_kernel(PrepP
 #pragma unroll
     for (int m = 0; m < TOK; ++m) {
       const int tl = TOK * s + m;
+      const float btv = bt[m] * vunit;
       float ra[8], rp[8], cb[8], ql[8];
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        const float gam = gc[m][c] + pre[c];
-        const float a = __builtin_amdgcn_exp2f(gam - md[c]);
-        const float bb = __builtin_amdgcn_exp2f(md[c] - gam);
+        const float gam = gc[m][c] + pre[c];  // nats; md is in log2 units
+        const float a = __builtin_amdgcn_exp2f(fmaf(gam, kLog2e, -md[c]));
+        const float bb = __builtin_amdgcn_exp2f(fmaf(-gam, kLog2e, md[c]));
         const float lam = a * em[c];
         const float bk = bt[m] * yk[m][c];
         ra[c] = bk * a;
@@ -413,7 +420,7 @@ __global__ __launch_bounds__(fast_threads<E>()) void kda_chunk_prep_kernel(PrepP
         ql[c] = yq[m][c] * lam;
         kt[c][m] = yk[m][c] * (bb * ec[c]);
         kv[0][c][m] = from_f32<E>(bk * lam);
-        kv[1][c][m] = from_f32<E>(bt[m] * yv[m][c]);
+        kv[1][c][m] = from_f32<E>(btv * yv[m][c]);
       }
       store8(RA + tl * LQ + ch, ra);
       store8(RP + tl * LQ + ch, rp);
