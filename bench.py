@@ -47,6 +47,7 @@ STAGE_IDS = [0, 4, 3]
 STAGE_NAMES = ["kda_chunk_prep_kernel", "kda_chunk_state_kernel", "kda_out_stage_kernel"]
 KERNEL_SOURCES = ["gated_delta_rule_80_amd/csrc/kda_prep.hip",
                   "gated_delta_rule_80_amd/csrc/kda_backward.hip",
+                  "gated_delta_rule_80_amd/csrc/kda_bwd_stages.hip",
                   "gated_delta_rule_80_amd/csrc/kda_prep_exact.hip",
                   "gated_delta_rule_80_amd/csrc/kda_state.hip",
                   "gated_delta_rule_80_amd/csrc/kda_decode.hip",
@@ -374,7 +375,8 @@ def backward_leg(kda, torch, w, args, stream, dev, plain_ms):
     ms = e0.elapsed_time(e1) / args.steps
     nb = backward_bytes(w)
     out = {"workload": w.name, "ms_per_step": ms, "tokens_per_s": w.B * w.T / (ms / 1e3),
-           "ratio_to_forward": ms / plain_ms, "workspace_bytes": ws.numel(),
+           "ratio_to_forward": ms / plain_ms if plain_ms == plain_ms else None,
+           "workspace_bytes": ws.numel(),
            "path_bytes": nb, "path_GBps": nb / (ms / 1e3) / 1e9,
            "path_frac_hbm": nb / (ms / 1e3) / HBM_PEAK,
            "includes": "recomputed forward + reverse walk + per-chunk gradient kernels + front end"}
@@ -429,13 +431,19 @@ OTHER_LEG_WORKLOAD = {"kda_decode_kernel": "decode-b256",
                       CALIB_KERNEL: f"calibration-copy-{CALIB_MIB}-MiB"}
 
 
-def profile_args(workload: str) -> str:
+def profile_args(workload: str, backward: bool = False) -> str:
     return (f"--workload {workload} --also none --no-stages --cpu-budget 0 --steps 5 "
-            f"--warmup 20 --calib-copy-mib {CALIB_MIB}")
+            f"--warmup 20 --calib-copy-mib {CALIB_MIB}" + (" --backward-only" if backward else ""))
 
 
-def profile_commands(d: str, workload: str) -> dict:
-    args = profile_args(workload)
+def profile_label(workload: str, backward: bool = False) -> str:
+    """Name under which a profile's kernels are filed (the backward's own kernels and
+    its recomputed forward under <workload>-backward)."""
+    return f"{workload}-backward" if backward else workload
+
+
+def profile_commands(d: str, workload: str, backward: bool = False) -> dict:
+    args = profile_args(workload, backward)
     run = f"python3 bench.py {args}"
     return {
         "trace": f"rocprofv3 --kernel-trace --stats -f csv -d {d}/trace -o trace -- {run}",
@@ -461,11 +469,13 @@ def _short(name: str) -> str:
     return m.group(1) if m else name
 
 
-def summarize_rocprof(d: str, workload: str, out_dir: str) -> dict:
-    """Turn the four runs of profile_commands(d, workload) into one summary file
-    per kernel under out_dir (named for the kernel and the workload) and this
-    workload's entry of out_dir/traffic.json.  Returns the traffic entry."""
-    cmds = profile_commands(d, workload)
+def summarize_rocprof(d: str, workload: str, out_dir: str, backward: bool = False) -> dict:
+    """Turn the four runs of profile_commands(d, workload, backward) into one
+    summary file per kernel under out_dir (named for the kernel and the workload's
+    profile label) and this label's entry of out_dir/traffic.json.  Returns the
+    traffic entry."""
+    cmds = profile_commands(d, workload, backward)
+    label = profile_label(workload, backward)
     trace = _csv_rows(os.path.join(d, "trace", "**", "*kernel_trace.csv"))
     stats = {}
     for r in trace:
@@ -504,7 +514,7 @@ def summarize_rocprof(d: str, workload: str, out_dir: str) -> dict:
     os.makedirs(out_dir, exist_ok=True)
     for k, s in sorted(stats.items()):
         # kernels of the other legs of the profiled run are filed under their own workload
-        wl = OTHER_LEG_WORKLOAD.get(k, workload)
+        wl = OTHER_LEG_WORKLOAD.get(k, label)
         durs = s["durations"]
         avg = sum(durs) / len(durs)
         lines = [f"# {k} -- {wl}", "",
@@ -565,7 +575,24 @@ def summarize_rocprof(d: str, workload: str, out_dir: str) -> dict:
                                "commands": cmds, "kernels": ks}
     with open(tpath, "w") as f:
         json.dump(tj, f, indent=1)
-    return tj["workloads"][workload]
+    return tj["workloads"][label]
+
+
+def calibration_copy(kda, torch, mib, stream, dev):
+    """kda_prefill with T = 0 copies S0 to S_T with one plain copy kernel
+    (kda_copy_state_kernel): exactly n bytes read and n bytes written."""
+    nb_state = 128 * 128 * 4
+    nbh = max(1, mib * (1 << 20) // nb_state)
+    src = torch.randn(nbh, 1, 128, 128, device=dev)
+    dst = torch.empty_like(src)
+    z = torch.empty(nbh, 0, 1, 128, dtype=torch.bfloat16, device=dev)
+    ca = kda.prefill_args(z, z, z, z, z[..., 0], None, None, src, None, dst, None, chunk=64)
+    for _ in range(3):
+        kda.kda_prefill_raw(ca, None, stream)
+    torch.cuda.synchronize()
+    print(f"calibration copy: {nbh * nb_state} bytes read and written per launch",
+          file=sys.stderr, flush=True)
+    del src, dst
 
 
 def main(argv=None) -> int:
@@ -585,18 +612,21 @@ def main(argv=None) -> int:
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run the library's plain state-copy kernel (kda_prefill with T=0) "
                          "on this many MiB, to calibrate HBM byte counters")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="time only kda_prefill_backward on --workload (the profile of the backward)")
     ap.add_argument("--profile-commands", metavar="DIR",
                     help="print the rocprofv3 commands of a profile of --workload into DIR and exit")
     ap.add_argument("--summarize-rocprof", metavar="DIR",
                     help="summarize a profile of --workload taken by those commands into profiles/")
     args = ap.parse_args(argv)
     if args.profile_commands:
-        for c in profile_commands(args.profile_commands.rstrip("/"), args.workload).values():
+        for c in profile_commands(args.profile_commands.rstrip("/"), args.workload,
+                                  args.backward_only).values():
             print(c)
         return 0
     if args.summarize_rocprof:
         e = summarize_rocprof(args.summarize_rocprof.rstrip("/"), args.workload,
-                              os.path.join(ROOT, "profiles"))
+                              os.path.join(ROOT, "profiles"), args.backward_only)
         print(json.dumps({k: {kk: vv for kk, vv in v.items()} for k, v in e["kernels"].items()},
                          indent=1))
         return 0
@@ -614,6 +644,18 @@ def main(argv=None) -> int:
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     w = WORKLOADS[args.workload]
+    if args.backward_only:
+        print(f"timing the backward of {w.name}", file=sys.stderr, flush=True)
+        bw = backward_leg(kda, torch, w, args, stream, dev, float("nan"))
+        if args.calib_copy_mib > 0:
+            calibration_copy(kda, torch, args.calib_copy_mib, stream, dev)
+        print(json.dumps({"metric": "KDA backward tokens/s", "value": bw["tokens_per_s"],
+                          "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+                          "warmup": args.warmup, "ms_per_step": bw["ms_per_step"],
+                          "higher_is_better": True, "dtype": w.io, "data": "synthetic",
+                          "config": {"workload": w.name}, "backward": bw,
+                          "source_hash": source_hash()}), flush=True)
+        return 0
     head, _ = measure_prefill(kda, torch, w, args, stream, dev)
     others = {}
     for name in [x for x in args.also.split(",") if x and x != "none" and x != w.name]:
@@ -652,20 +694,7 @@ def main(argv=None) -> int:
         stages["backward"] = backward_leg(kda, torch, ws4, args, stream, dev, base_ms)
 
     if args.calib_copy_mib > 0:
-        # kda_prefill with T = 0 copies S0 to S_T with one plain copy kernel
-        # (kda_copy_state_kernel): exactly n bytes read and n bytes written.
-        nb_state = 128 * 128 * 4
-        nbh = max(1, args.calib_copy_mib * (1 << 20) // nb_state)
-        src = torch.randn(nbh, 1, 128, 128, device=dev)
-        dst = torch.empty_like(src)
-        z = torch.empty(nbh, 0, 1, 128, dtype=torch.bfloat16, device=dev)
-        ca = kda.prefill_args(z, z, z, z, z[..., 0], None, None, src, None, dst, None, chunk=64)
-        for _ in range(3):
-            kda.kda_prefill_raw(ca, None, stream)
-        torch.cuda.synchronize()
-        print(f"calibration copy: {nbh * nb_state} bytes read and written per launch",
-              file=sys.stderr, flush=True)
-        del src, dst
+        calibration_copy(kda, torch, args.calib_copy_mib, stream, dev)
 
     cpu = None
     if args.cpu_budget > 0:

@@ -111,8 +111,19 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_walk_kernel(BwdWalkParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g4 = lane >> 4;
-  const int vblk = blockIdx.x % NV;
-  const int bh = blockIdx.x / NV;
+  // The value blocks of one (sequence, head) read the same records: they go to
+  // the same XCD (workgroups are dealt round robin over the 8 XCDs), so the
+  // second read of a record is served by that XCD's L2.
+  const int total = p.B * p.H * NV;
+  int bh, vblk;
+  if (total % (8 * NV) == 0) {
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+    vblk = slot % NV;
+    bh = (slot / NV) * 8 + xcd;
+  } else {
+    vblk = blockIdx.x % NV;
+    bh = blockIdx.x / NV;
+  }
   const int h = bh % p.H, b = bh / p.H;
   const int vb0 = vblk * VB;
   const size_t HD = (size_t)p.H * D;
