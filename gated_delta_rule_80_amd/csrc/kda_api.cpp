@@ -654,7 +654,6 @@ kda_status kda_validate_backward(const kda_backward_args* a) {
   if ((a->dA_log || a->ddt_bias) && f->A_log == nullptr) return KDA_ERR_NULL;
   if (a->do_norm_w && f->o_norm_w == nullptr) return KDA_ERR_NULL;
   if (a->do_gate && f->o_gate == nullptr) return KDA_ERR_NULL;
-  if (f->io == KDA_FP32 && f->D == 128) return KDA_ERR_UNSUPPORTED;
   const bool need = f->T > 0;
   if (need && (!a->dO || !a->dq || !a->dk || !a->dv || !a->dg || !a->dbeta)) return KDA_ERR_NULL;
   if (f->conv_k > 0 && !a->dconv_w) return KDA_ERR_NULL;

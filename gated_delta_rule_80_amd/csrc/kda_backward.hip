@@ -1718,7 +1718,11 @@ static hipError_t launch_bwd_c(const BwdLaunch& L, int C, hipStream_t st) {
   switch (C) {
     case 16: return launch_bwd_t<D, 16, IO, E>(L, st);
     case 32: return launch_bwd_t<D, 32, IO, E>(L, st);
-    case 64: return launch_bwd_t<D, 64, IO, E>(L, st);
+    case 64:
+      // fp32 at D = 128 takes C <= 32 (the product kernel's staged tiles need more
+      // threads than it has at C = 64; the forward rejects that chunk size too)
+      if constexpr (D == 128 && sizeof(E) == 4) return hipErrorInvalidValue;
+      else return launch_bwd_t<D, 64, IO, E>(L, st);
   }
   return hipErrorInvalidValue;
 }
@@ -1732,6 +1736,7 @@ hipError_t launch_backward(const BwdLaunch& L, int D, int C, bool fp32, hipStrea
       case 16: return launch_bwd_c<16, float, float>(L, C, st);
       case 32: return launch_bwd_c<32, float, float>(L, C, st);
       case 64: return launch_bwd_c<64, float, float>(L, C, st);
+      case 128: return launch_bwd_c<128, float, float>(L, C, st);
     }
   } else {
     switch (D) {

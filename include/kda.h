@@ -272,8 +272,8 @@ kda_status kda_decode_step(const kda_decode_args* a, void* stream);
  * activations, dg and dbeta are the gradients of g and beta as given (the raw
  * gate projection, the logits).  Packed sequences too: dS_T, dS0 and
  * dconv_state are then per sequence ([n_seqs][...]); the gradients of tokens
- * outside every sequence (malformed offsets) are left undefined.  Supported:
- * fp32 I/O up to D = 64, bf16 I/O up to D = 128.  All gradients are float32;
+ * outside every sequence (malformed offsets) are left undefined.  Supported: every
+ * D and chunk size the forward supports.  All gradients are float32;
  * with bf16 I/O the intermediate
  * gradients pass between the kernels in bf16 (relative error of the returned
  * gradients about 4e-3 against an exact computation, at T = 4096, H = 96,

@@ -399,7 +399,9 @@ def test_backward_validation(lib):
     # unsupported modes
     a = backward()
     a.fwd.io, a.fwd.chunk = _lib.KDA_FP32, 32
-    assert vb(a) == UNSUP  # fp32 with D = 128
+    assert vb(a) == OK  # fp32 with D = 128 takes C <= 32
+    a.fwd.chunk = 64
+    assert vb(a) == UNSUP  # as in the forward
     a.fwd.D = 64
     assert vb(a) == OK
     # the forward's own rules still apply

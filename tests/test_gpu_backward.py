@@ -68,7 +68,8 @@ def test_backward_tiny_fp32():
 @pytest.mark.parametrize("io,D,chunk", [("fp32", 16, 16), ("fp32", 32, 32), ("fp32", 64, 64),
                                         ("bf16", 32, 16), ("bf16", 64, 32), ("bf16", 128, 64),
                                         ("bf16", 128, 32), ("bf16", 128, 16), ("bf16", 16, 64),
-                                        ("bf16", 32, 64), ("bf16", 64, 64), ("bf16", 16, 16)])
+                                        ("bf16", 32, 64), ("bf16", 64, 64), ("bf16", 16, 16),
+                                        ("fp32", 128, 32), ("fp32", 128, 16)])
 def test_backward_dims_and_chunks(io, D, chunk):
     w = small(B=2, T=77, H=2, D=D, io=io, chunk=chunk, s0=True, conv_state=True)
     check_backward(w, chunk, seed=D + chunk)
