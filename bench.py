@@ -342,24 +342,41 @@ def time_decode(kda, torch, da, stream, steps, warmup):
     return d0.elapsed_time(d1) / steps
 
 
-def backward_leg(kda, torch, w, args, stream, dev, plain_ms):
-    """kda_prefill_backward on the same workload (forward recomputed inside)."""
-    from kda_inputs import make_inputs
-    inp = make_inputs(w, seed=args.seed, device=dev)
+def backward_leg(kda, torch, w, args, stream, dev, plain_ms, stages=False, packed=False):
+    """kda_prefill_backward on the same workload (forward recomputed inside); with
+    every optional stage on, or the tokens packed as sequences of mixed length."""
+    from kda_inputs import make_inputs, make_packed_inputs, make_stage_inputs
+    if packed:
+        lengths = PACKED_LENGTHS if sum(PACKED_LENGTHS) == w.B * w.T else [w.T] * w.B
+        inp = make_packed_inputs(w, lengths, seed=args.seed, device=dev)
+        B, T, NS = 1, sum(lengths), len(lengths)
+    else:
+        inp = make_inputs(w, seed=args.seed, device=dev)
+        B, T, NS = w.B, w.T, w.B
+    skw, g, beta = {}, inp["g"], inp["beta"]
+    if stages:
+        st = make_stage_inputs(w, seed=args.seed, device=dev)
+        g, beta = st["f"], st["b_logit"]
+        skw = dict(A_log=st["A_log"], dt_bias=st["dt_bias"], beta_logits=True,
+                   o_norm_w=st["o_norm_w"], o_gate=st["o_gate"])
     gen = torch.Generator(device=dev).manual_seed(args.seed + 7)
-    do = torch.randn(w.B, w.T, w.H, w.D, generator=gen, device=dev).to(inp["q"].dtype)
+    do = torch.randn(B, T, w.H, w.D, generator=gen, device=dev).to(inp["q"].dtype)
     f32 = dict(dtype=torch.float32, device=dev)
     o = torch.empty_like(inp["q"])
-    S_T = torch.empty(w.B, w.H, w.D, w.D, **f32)
-    cso = torch.empty(w.B, 3, 3, w.H * w.D, dtype=inp["q"].dtype, device=dev)
-    fwd = kda.prefill_args(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["conv_w"],
-                           inp["conv_state"], inp["S0"], o, S_T, cso, chunk=w.chunk)
-    shape = (w.B, w.T, w.H, w.D)
+    S_T = torch.empty(NS, w.H, w.D, w.D, **f32)
+    cso = torch.empty(NS, 3, 3, w.H * w.D, dtype=inp["q"].dtype, device=dev)
+    fwd = kda.prefill_args(inp["q"], inp["k"], inp["v"], g, beta, inp["conv_w"],
+                           inp["conv_state"], inp["S0"], o, S_T, cso, chunk=w.chunk,
+                           cu_seqlens=inp.get("cu_seqlens"), **skw)
+    shape = (B, T, w.H, w.D)
     grads = dict(dq=torch.empty(*shape, **f32), dk=torch.empty(*shape, **f32),
                  dv=torch.empty(*shape, **f32), dg=torch.empty(*shape, **f32),
-                 dbeta=torch.empty(w.B, w.T, w.H, **f32), dS0=torch.empty(w.B, w.H, w.D, w.D, **f32),
+                 dbeta=torch.empty(B, T, w.H, **f32), dS0=torch.empty(NS, w.H, w.D, w.D, **f32),
                  dconv_w=torch.empty(3, w.H * w.D, 4, **f32),
-                 dconv_state=torch.empty(w.B, 3, 3, w.H * w.D, **f32))
+                 dconv_state=torch.empty(NS, 3, 3, w.H * w.D, **f32))
+    if stages:
+        grads.update(dA_log=torch.empty(w.H, **f32), ddt_bias=torch.empty(w.H * w.D, **f32),
+                     do_norm_w=torch.empty(w.D, **f32), do_gate=torch.empty(*shape, **f32))
     a = kda.backward_args(fwd, do, None, grads)
     ws = torch.empty(kda.kda_backward_workspace_bytes(a), dtype=torch.uint8, device=dev)
     for _ in range(args.warmup):
@@ -374,13 +391,17 @@ def backward_leg(kda, torch, w, args, stream, dev, plain_ms):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / args.steps
     nb = backward_bytes(w)
-    out = {"workload": w.name, "ms_per_step": ms, "tokens_per_s": w.B * w.T / (ms / 1e3),
+    what = "recomputed forward + reverse walk + per-chunk gradient kernels + front end"
+    if stages:
+        what += "; every optional stage on (their backward included)"
+    if packed:
+        what += f"; {NS} packed sequences of lengths {lengths}"
+    out = {"workload": w.name, "ms_per_step": ms, "tokens_per_s": B * T / (ms / 1e3),
            "ratio_to_forward": ms / plain_ms if plain_ms == plain_ms else None,
            "workspace_bytes": ws.numel(),
            "path_bytes": nb, "path_GBps": nb / (ms / 1e3) / 1e9,
-           "path_frac_hbm": nb / (ms / 1e3) / HBM_PEAK,
-           "includes": "recomputed forward + reverse walk + per-chunk gradient kernels + front end"}
-    del ws, inp, grads, o, S_T, cso, do
+           "path_frac_hbm": nb / (ms / 1e3) / HBM_PEAK, "includes": what}
+    del ws, inp, grads, o, S_T, cso, do, a, fwd
     torch.cuda.empty_cache()
     return out
 
@@ -692,6 +713,10 @@ def main(argv=None) -> int:
         stages = stages_leg(kda, torch, ws4, wd, args, stream, dev, base_ms, dms)
         stages["packed"] = packed_leg(kda, torch, ws4, args, stream, dev, base_ms)
         stages["backward"] = backward_leg(kda, torch, ws4, args, stream, dev, base_ms)
+        stages["backward_every_stage"] = backward_leg(kda, torch, ws4, args, stream, dev, base_ms,
+                                                      stages=True)
+        stages["backward_packed"] = backward_leg(kda, torch, ws4, args, stream, dev, base_ms,
+                                                 packed=True)
 
     if args.calib_copy_mib > 0:
         calibration_copy(kda, torch, args.calib_copy_mib, stream, dev)

@@ -1652,6 +1652,8 @@ __global__ __launch_bounds__(256) void kda_bwd_conv_reduce_kernel(const float* p
   const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= n) return;
   float acc = 0.f;
+  // eight loads in flight ahead of their (in-order) adds
+#pragma unroll 8
   for (int q = 0; q < nparts; ++q) acc += part[(size_t)q * n + idx];
   out[idx] = acc;
 }
