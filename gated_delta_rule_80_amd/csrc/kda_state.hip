@@ -337,8 +337,16 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void kda_chunk_state_kernel(
 
   if (nch > 0) issue_copy(0);
   for (int n = 0; n < nch; ++n) {
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of chunk n (and older stores) are done
-    lds_barrier();                  // the whole image of chunk n and the state are in LDS
+    // this wave's copies of chunk n are done.  From step 2 on, the last vector
+    // memory operations it issued are the NU output stores of chunk n - 2 (one per
+    // unit, every token of a full chunk), issued after that copy: they may stay in
+    // flight, as nothing in this kernel reads o.  (The output stage and the
+    // checkpoints issue further operations, so those walks wait for everything.)
+    if (!GN && !CK && n >= 2)
+      wait_vmcnt<NU>();
+    else
+      __builtin_amdgcn_s_waitcnt(0);
+    lds_barrier();  // the whole image of chunk n and the state are in LDS
     // ---- this chunk's fragments, from the image into registers
     RowFrag<E, D> fw, fql;
     RowFrag<E, C> fp;
