@@ -48,6 +48,7 @@ STAGE_NAMES = ["kda_chunk_prep_kernel", "kda_chunk_state_kernel", "kda_out_stage
 KERNEL_SOURCES = ["gated_delta_rule_80_amd/csrc/kda_prep.hip",
                   "gated_delta_rule_80_amd/csrc/kda_backward.hip",
                   "gated_delta_rule_80_amd/csrc/kda_bwd_stages.hip",
+                  "gated_delta_rule_80_amd/csrc/kda_split.hip",
                   "gated_delta_rule_80_amd/csrc/kda_prep_exact.hip",
                   "gated_delta_rule_80_amd/csrc/kda_state.hip",
                   "gated_delta_rule_80_amd/csrc/kda_decode.hip",
@@ -55,7 +56,7 @@ KERNEL_SOURCES = ["gated_delta_rule_80_amd/csrc/kda_prep.hip",
                   "gated_delta_rule_80_amd/csrc/kda_device.h",
                   "gated_delta_rule_80_amd/csrc/kda_layout.h"]
 HEADLINE = "prefill-64k"
-ALSO = "prefill-4k,prefill-b4-8k-s0"
+ALSO = "prefill-4k,prefill-b4-8k-s0,prefill-64k-h12"
 STAGES_WORKLOAD = "prefill-4k"
 METRIC = "KDA tokens/s per GPU (prefill, H=96 d=128) + decode seq/s; % of roofline"
 

@@ -23,7 +23,7 @@ KDA_BF16 = 0
 KDA_FP32 = 1
 KDA_FLAG_L2NORM_QK = 1
 KDA_FLAG_BETA_LOGITS = 2
-ABI_VERSION = 4
+ABI_VERSION = 5
 KDA_STAGE_PREP, KDA_STAGE_STATE, KDA_STAGE_CONV_TAIL, KDA_STAGE_OUTPUT = 0, 1, 2, 3
 KDA_STAGE_STATE_TAIL = 4  # stages 1 and 2 in one launch, as kda_prefill runs them
 NUM_STAGES = 4
@@ -114,6 +114,8 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.kda_prefill_static.argtypes = [P(PrefillArgs), _vp]
     lib.kda_prefill_stage.restype = ctypes.c_int
     lib.kda_prefill_stage.argtypes = [P(PrefillArgs), _vp, ctypes.c_size_t, ctypes.c_int, _vp]
+    lib.kda_prefill_walk_segments.restype = ctypes.c_int
+    lib.kda_prefill_walk_segments.argtypes = [P(PrefillArgs)]
     lib.kda_validate_conv_norm.restype = ctypes.c_int
     lib.kda_validate_conv_norm.argtypes = [P(ConvNormArgs)]
     lib.kda_conv_norm.restype = ctypes.c_int
@@ -275,6 +277,12 @@ def kda_prefill(q, k, v, g, beta, conv_w=None, conv_state=None, S0=None, *, chun
                               workspace is None else workspace.numel(), _stream(stream)),
            "kda_prefill")
     return o, S_T, conv_state_out
+
+
+def kda_prefill_walk_segments(args: PrefillArgs) -> int:
+    """Segments the state walk of kda_prefill(args) is split into (1: not split;
+    0: invalid arguments).  Host only."""
+    return int(load().kda_prefill_walk_segments(ctypes.byref(args)))
 
 
 def kda_prefill_stage(args: PrefillArgs, workspace, stage: int, stream=None):

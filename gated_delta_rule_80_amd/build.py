@@ -23,7 +23,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkda.so")
 
 SOURCES = ["kda_api.cpp", "kda_noalloc.hip", "kda_prep.hip", "kda_prep_exact.hip", "kda_state.hip",
-           "kda_decode.hip", "kda_backward.hip", "kda_bwd_stages.hip"]
+           "kda_decode.hip", "kda_backward.hip", "kda_bwd_stages.hip", "kda_split.hip"]
 ARCH = "gfx950"
 
 

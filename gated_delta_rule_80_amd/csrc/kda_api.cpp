@@ -87,12 +87,6 @@ kda_status prefill_sizes(const kda_prefill_args* a, PrefillSizes& s) {
   return KDA_OK;
 }
 
-kda::WorkspaceLayout ws_layout(const kda_prefill_args* a) {
-  PrefillSizes s;
-  prefill_sizes(a, s);
-  return kda::workspace_layout((size_t)a->B * a->H * s.NT, a->chunk, a->D, esize(a->io),
-                               packed(a) ? (size_t)a->n_seqs : 0);
-}
 
 // Value columns per state-walk workgroup and its thread count.  Every workgroup
 // streams the chunk's W, Q Lambda, Ktil^T and P whatever its value block, so
@@ -114,6 +108,50 @@ StateCfg state_config(int B, int H, int D, bool fp32, bool gn) {
   if (D == 128 && !fp32) return {64, 512, false};
   const long walks64 = (long)B * H * (D / 64);
   return {walks64 < 240 ? 32 : 64, 256, false};
+}
+
+// Split state walk (kda_split.hip): segments per (sequence, head) and their
+// length in chunks.  Only whole-sequence walks of B equal-length sequences
+// split (not time slices, packed sequences, the backward's checkpointing walk
+// or a walk that applies the output stage itself).  Splitting adds the segment
+// maps (the N and M walks of every segment but the last, about as many products
+// again as the plain walk's) and a short composition in exchange for a chain of
+// seg_len instead of all chunk steps, which pays while the walks leave CUs idle:
+// at most kSplitWalks workgroups in the split walk, segments of at least
+// kMinSegChunks chunks, and at most kMaxSegments segments (the composition is a
+// chain of nseg - 2 D x D products).
+struct SplitPlan {
+  int nseg = 1, seg_len = 0;
+};
+constexpr long kSplitWalks = 256;
+constexpr int kMinSegChunks = 16;
+constexpr long kMaxSegments = 32;
+
+SplitPlan split_plan(const kda_prefill_args* a) {
+  SplitPlan sp;
+  if (packed(a) || a->T <= 0 || a->chunk <= 0) return sp;
+  const bool gn = a->o_norm_w != nullptr || a->o_gate != nullptr;
+  const StateCfg cfg = state_config(a->B, a->H, a->D, a->io == KDA_FP32, gn);
+  if (cfg.fused) return sp;
+  const long walks = (long)a->B * a->H * (a->D / cfg.vb);
+  const long nch = ((long)a->T + a->chunk - 1) / a->chunk;
+  long P = kSplitWalks / walks;
+  if (nch / kMinSegChunks < P) P = nch / kMinSegChunks;
+  if (kMaxSegments < P) P = kMaxSegments;
+  if (P < 2) return sp;
+  sp.seg_len = (int)((nch + P - 1) / P);
+  sp.nseg = (int)((nch + sp.seg_len - 1) / sp.seg_len);
+  if (sp.nseg < 2) sp = SplitPlan{};
+  return sp;
+}
+
+kda::WorkspaceLayout ws_layout(const kda_prefill_args* a) {
+  PrefillSizes s;
+  prefill_sizes(a, s);
+  const SplitPlan sp = split_plan(a);
+  return kda::workspace_layout((size_t)a->B * a->H * s.NT, a->chunk, a->D, esize(a->io),
+                               packed(a) ? (size_t)a->n_seqs : 0,
+                               kda::split_bytes((size_t)a->B * a->H, sp.nseg, a->D));
 }
 
 constexpr uint32_t kKnownFlags = KDA_FLAG_L2NORM_QK | KDA_FLAG_BETA_LOGITS;
@@ -324,6 +362,24 @@ static kda_status run_stage(const kda_prefill_args* a, void* ws, int stage, hipS
       p.o_norm_w = a->o_norm_w;
       p.o_norm_eps = a->o_norm_eps;
       p.ckpt = bo != nullptr ? bo->ckS : nullptr;
+      const SplitPlan sp = sl == nullptr && bo == nullptr ? split_plan(a) : SplitPlan{};
+      if (sp.nseg > 1) {
+        kda::SplitParams q{};
+        q.ws = p.ws;
+        q.S0 = a->S0;
+        q.maps = reinterpret_cast<float*>(static_cast<char*>(ws) + wl.split);
+        q.starts = q.maps + (size_t)a->B * a->H * (sp.nseg - 1) * 2 * a->D * a->D;
+        q.B = a->B; q.H = a->H; q.NT = NT;
+        q.nseg = sp.nseg; q.seg_len = sp.seg_len;
+        if (kda_status e = hip_status(kda::launch_split_maps(q, a->D, a->chunk, fp32, cfg.vb,
+                                                             cfg.threads, st));
+            e != KDA_OK)
+          return e;
+        if (kda_status e = hip_status(kda::launch_split_combine(q, a->D, st)); e != KDA_OK) return e;
+        p.nseg = sp.nseg;
+        p.seg_len = sp.seg_len;
+        p.seg_start = q.starts;
+      }
       if (fuse_tail && sl == nullptr && a->conv_k > 0 && a->conv_state_out != nullptr) {
         p.tail_x[0] = a->q; p.tail_x[1] = a->k; p.tail_x[2] = a->v;
         p.tail_in = a->conv_state_in;
@@ -416,6 +472,11 @@ kda_status kda_prefill_stage(const kda_prefill_args* a, void* ws, size_t ws_byte
   if (stage == KDA_STAGE_STATE_TAIL)
     return run_stage(a, ws, KDA_STAGE_STATE, static_cast<hipStream_t>(stream), nullptr, true);
   return run_stage(a, ws, stage, static_cast<hipStream_t>(stream));
+}
+
+int kda_prefill_walk_segments(const kda_prefill_args* a) {
+  if (kda_validate_prefill(a) != KDA_OK) return 0;
+  return split_plan(a).nseg;
 }
 
 kda_status kda_prefill(const kda_prefill_args* a, void* ws, size_t ws_bytes, void* stream) {

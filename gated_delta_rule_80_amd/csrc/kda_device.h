@@ -333,6 +333,15 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Position of workgroup blk of an n-workgroup grid in the order that lists the
+// workgroups XCD by XCD.  Dispatch places workgroup blk on XCD blk % 8, so the
+// positions [x (n / 8) + min(x, n % 8), ...) all run on XCD x and consecutive
+// positions share that XCD's L2 (up to the 7 boundaries between XCDs).
+__device__ __forceinline__ int xcd_major(int blk, int n) {
+  const int x = blk & 7, i = blk >> 3, q = n >> 3, rem = n & 7;
+  return x * q + (x < rem ? x : rem) + i;
+}
+
 // ------------------------------------------------------------ packed sequences
 // The sequence that owns chunk slot gc: the largest i < n_seqs with cstart[i] <=
 // gc (an empty sequence owns no slot, so it is skipped).  gc < cstart[n_seqs].

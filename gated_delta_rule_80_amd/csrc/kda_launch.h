@@ -12,6 +12,10 @@ hipError_t launch_prep_exact(const PrepParams& p, int D, int C, bool fp32, unsig
                              hipStream_t st);
 hipError_t launch_state(const StateParams& p, int D, int C, bool fp32, int vb, int threads, bool gn,
                         hipStream_t st);
+// split state walk: the segments' maps, then their start states (SplitParams)
+hipError_t launch_split_maps(const SplitParams& p, int D, int C, bool fp32, int vb, int threads,
+                             hipStream_t st);
+hipError_t launch_split_combine(const SplitParams& p, int D, hipStream_t st);
 hipError_t launch_out_stage(const OutStageParams& p, int D, bool fp32, hipStream_t st);
 hipError_t launch_conv_norm(const ConvNormParams& p, int D, bool fp32, hipStream_t st);
 hipError_t launch_conv_tail(const TailParams& p, bool fp32, hipStream_t st);

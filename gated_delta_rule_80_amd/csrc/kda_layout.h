@@ -41,21 +41,50 @@ constexpr RecordLayout record_layout(int C, int D, size_t esize) {
 // packed sequences their clamped token bounds and first chunk indices (int32,
 // n_seqs + 1 each), then one record per (sequence, head, chunk) -- for packed
 // sequences per (head, chunk slot), n_slots = ceil(T / C) + n_seqs slots a head.
+// When the state walk is split into segments (below), their maps and start
+// states follow the records.
 struct WorkspaceLayout {
   size_t list;     // byte offset of the fallback list (uint32 per chunk)
   size_t seq;      // byte offset of the sequence tables (packed sequences)
   size_t records;  // byte offset of the first record
+  size_t split;    // byte offset of the segment maps and start states
   size_t bytes;    // total
 };
 
 constexpr WorkspaceLayout workspace_layout(size_t nrec, int C, int D, size_t esize,
-                                           size_t n_seqs = 0) {
+                                           size_t n_seqs = 0, size_t split_sz = 0) {
   WorkspaceLayout w{};
   w.list = 256;
   w.seq = round_up(w.list + 4 * nrec, 256);
   w.records = round_up(w.seq + (n_seqs > 0 ? 8 * (n_seqs + 1) : 0), 256);
-  w.bytes = w.records + nrec * record_layout(C, D, esize).bytes;
+  w.split = w.records + nrec * record_layout(C, D, esize).bytes;
+  w.bytes = w.split + split_sz;
   return w;
+}
+
+// Split state walk.  The state after a run of chunks is affine in the state
+// before it: S_end = M S_start + N, with M (D x D, acting on the key index) the
+// product of the chunks' homogeneous maps S -> Diag(Lambda_C) S - Ktil^T W S and
+// N the end state from zero.  The chunks of every (sequence, head) are cut into
+// nseg segments of seg_len chunks (the last one shorter); each segment's N and M
+// are walked in parallel, the segment start states are composed from them in
+// order, and then every segment is walked with its outputs from its own start.
+//   maps   [B*H][nseg - 1][2][D][D] float32, for segments s < nseg - 1: N row-major
+//          [key][value] (for s = 0 walked from S0 itself, so it is the state at
+//          the start of segment 1), then M transposed, Mt[j][c] = M[c][j]
+//          (not written for s = 0);
+//   starts [B*H][nseg][D][D] float32: the state at each segment's start.
+struct SplitParams {
+  const char* ws;     // first record
+  const float* S0;    // [B][H][D][D] or NULL (zeros)
+  float* maps;
+  float* starts;
+  int B, H, NT;       // NT: chunk records per (sequence, head)
+  int nseg, seg_len;
+};
+
+constexpr size_t split_bytes(size_t BH, int nseg, int D) {
+  return nseg > 1 ? BH * (size_t)(3 * nseg - 2) * D * D * 4 : 0;
 }
 
 // Packed sequences: sequence i is tokens [bounds[i], bounds[i + 1]) and owns
@@ -124,6 +153,12 @@ struct StateParams {
   const float* o_norm_w;  // [D] or NULL
   float o_norm_eps;
   SeqTables seqs;         // packed sequences (then B = n_seqs, NT = chunk slots per head)
+  // split walk (nseg > 1; equal-length sequences, c0 = 0): one workgroup per
+  // (sequence, head, segment, value block), walking chunks seg * seg_len .. of
+  // its sequence from seg_start [B*H][nseg][D][D] (S0 is not read); only the
+  // last segment writes S_T
+  int nseg, seg_len;
+  const float* seg_start;
   void* ckpt;             // backward mode: the state at each chunk start in the element type,
                           // S^T then S, [rec][2][D][D], or NULL
   // conv-state hand-over by the workgroups of value block 0, or tail_out NULL: the

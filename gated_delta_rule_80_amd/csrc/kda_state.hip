@@ -88,9 +88,14 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void kda_chunk_state_kernel(
   const int r = lane & 15, g4 = lane >> 4;
   // Workgroups of one head's value blocks are placed on the same XCD (dispatch
   // is round robin over the 8 XCDs), so they share the chunk records in L2.
-  const int total = p.B * p.H * NV;
-  int bh, vblk;
-  if (total % (8 * NV) == 0) {
+  int bh, vblk, seg = 0;
+  if (p.nseg > 1) {
+    // split walk: (head, segment) groups of NV workgroups, numbered XCD by XCD
+    const int grp = xcd_major(blockIdx.x, gridDim.x);
+    vblk = grp % NV;
+    bh = grp / NV % (p.B * p.H);
+    seg = grp / NV / (p.B * p.H);
+  } else if ((p.B * p.H * NV) % (8 * NV) == 0) {
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
     vblk = slot % NV;
     bh = (slot / NV) * 8 + xcd;
@@ -107,11 +112,15 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void kda_chunk_state_kernel(
   int Tq, nch;
   size_t rec0;
   if (p.seqs.bounds == nullptr) {
-    // chunks c0 .. of sequence b: tokens from c0 C on, at most NT chunks
-    tok0 = (long)b * p.T + (long)p.c0 * C;
-    Tq = p.T - p.c0 * C;
-    nch = (Tq + C - 1) / C < p.NT ? (Tq + C - 1) / C : p.NT;
-    rec0 = (size_t)bh * p.NT;
+    // chunks c0 .. of sequence b: tokens from c0 C on, at most cap chunks (a
+    // time slice's records fill the workspace from slot 0; a segment's are
+    // slots c0 .. of the sequence's)
+    const int c0 = p.nseg > 1 ? seg * p.seg_len : p.c0;
+    const int cap = p.nseg > 1 ? p.seg_len : p.NT;
+    tok0 = (long)b * p.T + (long)c0 * C;
+    Tq = p.T - c0 * C;
+    nch = (Tq + C - 1) / C < cap ? (Tq + C - 1) / C : cap;
+    rec0 = (size_t)bh * p.NT + (p.nseg > 1 ? c0 : 0);
   } else {
     tok0 = p.seqs.bounds[b];
     Tq = p.seqs.bounds[b + 1] - p.seqs.bounds[b];
@@ -126,7 +135,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void kda_chunk_state_kernel(
   // Tq - 3 + tau, from the previous state where that position is < 0.  A thread
   // reads the 3 values of its (tensor, channel) before writing them, so the new
   // state may overwrite the previous one.
-  if (p.tail_out != nullptr && vblk == 0) {
+  if (p.tail_out != nullptr && vblk == 0 && seg == 0) {
     const size_t HD = (size_t)p.H * D;
     for (int it = tid; it < 3 * D; it += NT) {
       const int i = it / D;
@@ -203,18 +212,23 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void kda_chunk_state_kernel(
     }
   };
 
-  // ---- initial state
+  // ---- initial state (a segment's from the composed start states; S_T, which
+  // may be S0, is written by the last segment only)
   f32x4 accS[NS];
   const size_t sbase = (size_t)bh * D * D;
+  const float* s_in = p.nseg > 1 ? p.seg_start + ((size_t)bh * p.nseg + seg) * D * D
+                                 : (p.S0 != nullptr ? p.S0 + sbase : nullptr);
+  float* s_out = p.nseg > 1 && seg != p.nseg - 1 ? nullptr
+                 : (p.S_T != nullptr ? p.S_T + sbase : nullptr);
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
     const int u = wave + NW * i;
     accS[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if ((FULL_S || u < CT * VT) && p.S0 != nullptr) {
+    if ((FULL_S || u < CT * VT) && s_in != nullptr) {
       const int Ct = u % CT, Vt = u / CT;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        accS[i][e] = p.S0[sbase + (size_t)(16 * Ct + 4 * g4 + e) * D + vb0 + 16 * Vt + r];
+        accS[i][e] = s_in[(size_t)(16 * Ct + 4 * g4 + e) * D + vb0 + 16 * Vt + r];
     }
   }
   auto stage_state = [&]() {
@@ -460,7 +474,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void kda_chunk_state_kernel(
   }
   if (nch > 0) store_out(nch - 1);
   // ---- final state
-  if (p.S_T != nullptr) {
+  if (s_out != nullptr) {
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       const int u = wave + NW * i;
@@ -468,7 +482,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void kda_chunk_state_kernel(
         const int Ct = u % CT, Vt = u / CT;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          p.S_T[sbase + (size_t)(16 * Ct + 4 * g4 + e) * D + vb0 + 16 * Vt + r] = accS[i][e];
+          s_out[(size_t)(16 * Ct + 4 * g4 + e) * D + vb0 + 16 * Vt + r] = accS[i][e];
       }
     }
   }
@@ -478,6 +492,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void kda_chunk_state_kernel(
 // forward walk carries no checkpoint code.
 template <int D, int C, int VB, typename IO, typename E, int NT, bool GN>
 static hipError_t launch_walk(const StateParams& p, size_t grid, hipStream_t st) {
+  if (p.nseg > 1) grid *= (size_t)p.nseg;
   if (p.ckpt != nullptr) {
     if constexpr (GN) return hipErrorInvalidValue;  // no output stage in the backward mode
     else hipLaunchKernelGGL((kda_chunk_state_kernel<D, C, VB, IO, E, NT, false, true>),

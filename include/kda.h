@@ -73,7 +73,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 4
+#define KDA_ABI_VERSION 5
 
 typedef enum kda_status {
   KDA_OK = 0,
@@ -181,6 +181,22 @@ kda_status kda_prefill(const kda_prefill_args* a, void* ws, size_t ws_bytes, voi
 kda_status kda_prefill_stage(const kda_prefill_args* a, void* ws, size_t ws_bytes, int stage,
                              void* stream);
 
+/* Host-only: the number of segments the state walk of kda_prefill(a) is split
+ * into, 1 when it is not split, 0 when the arguments are invalid.  The state
+ * after a run of tokens is affine in the state before it (S_end = M S_start + N,
+ * M acting on the key index: each step of the update in item 3 above maps S
+ * linearly, by (I - beta k k^T) Diag(exp(g)), and adds beta k v^T).
+ * When the walks of a call are too few to fill the GPU while each is a long
+ * chain of chunk steps (few sequence-heads, long T: a tensor-parallel share of
+ * heads at long context), every (sequence, head) is cut into segments: each
+ * segment's N and M are walked in parallel, the start states composed in order,
+ * then each segment walked with its outputs from its start.  Only B equal-length
+ * sequences with T > 0 split, and never a walk that applies the output stage
+ * itself.  The results agree with the unsplit walk's to rounding (the same sums
+ * in another order); the workspace includes the segments' maps and start states
+ * (3 nseg - 2 float32 D x D matrices per (sequence, head)). */
+int kda_prefill_walk_segments(const kda_prefill_args* a);
+
 /* For callers that cannot allocate device memory -- code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc: kda_prefill
  * with its workspace taken from a static device array of
@@ -192,7 +208,9 @@ kda_status kda_prefill_stage(const kda_prefill_args* a, void* ws, size_t ws_byte
  *     array, the call runs exactly as kda_prefill.  Otherwise B equal-length
  *     sequences are processed in time slices of as many chunks per (sequence,
  *     head) as fit, the state handed from slice to slice through S_T; the
- *     results are the same bit for bit.  Packed sequences that do not fit, and
+ *     results are the same bit for bit, except where kda_prefill would split
+ *     its state walk (kda_prefill_walk_segments > 1: slices walk unsplit, so
+ *     the two agree to rounding).  Packed sequences that do not fit, and
  *     any request of which not even one chunk per (sequence, head) fits (more
  *     than about 1,800 sequence-heads at D = 128, chunk 64, bf16), return
  *     KDA_ERR_SCRATCH before anything is enqueued.

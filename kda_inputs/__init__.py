@@ -74,6 +74,9 @@ WORKLOADS = {
                             conv_state_std=1.0),
     "prefill-64k": Workload("prefill-64k", B=1, T=65536, H=96, D=128, io="bf16", chunk=64,
                             a_lo=-3.0, a_hi=2.0, b_std=math.sqrt(2.0), s0_std=0.1),
+    # one GPU's share of the 64k layer under 8-way tensor parallelism over heads
+    "prefill-64k-h12": Workload("prefill-64k-h12", B=1, T=65536, H=12, D=128, io="bf16",
+                                chunk=64, a_lo=-3.0, a_hi=2.0, b_std=math.sqrt(2.0), s0_std=0.1),
 }
 # The same five workloads by position (0: tiny parity case ... 4: long context).
 ORDER = ["tiny-fp32", "prefill-4k", "prefill-b4-8k-s0", "decode-b256", "prefill-64k"]

@@ -21,10 +21,11 @@ def test_exports_every_declared_symbol(lib):
     names = kda.declared_functions()
     assert {"kda_prefill", "kda_decode_step", "kda_conv_norm", "kda_prefill_stage",
             "kda_prefill_workspace_bytes", "kda_validate_prefill", "kda_validate_decode",
-            "kda_validate_conv_norm", "kda_status_str", "kda_abi_version"} <= set(names)
+            "kda_validate_conv_norm", "kda_status_str", "kda_abi_version",
+            "kda_prefill_walk_segments"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.kda_abi_version() == 4
+    assert lib.kda_abi_version() == 5
     for s in range(11):
         assert kda.kda_status_str(s) and kda.kda_status_str(s) != "unknown status"
 
@@ -91,6 +92,32 @@ def test_prefill_valid_and_workspace(lib):
     a.chunk = 32
     assert vp(a) == OK
     assert kda.kda_prefill_workspace_bytes(prefill(B=0)) == 0
+
+
+def test_walk_segments_plan(lib):
+    """Host-only plan of the split state walk: few long walks are cut into
+    segments, walks that fill the GPU are not; the workspace grows by the
+    segments' maps and start states."""
+    def segs(**kw):
+        return lib.kda_prefill_walk_segments(ctypes.byref(prefill(**kw)))
+    # 12 heads x 2 value blocks = 24 walks of 1,024 chunks: 10 segments of 103
+    assert segs(B=1, T=65536, H=12) == 10
+    assert segs(B=1, T=4096, H=12) == 4      # segments of at least 16 chunks
+    assert segs(B=1, T=65536, H=96) == 1     # 192 walks
+    assert segs(B=1, T=4096, H=96) == 1
+    assert segs(B=1, T=1000, H=2) == 1       # 16 chunks
+    assert segs(B=1, T=65536, H=2, D=64) == 32
+    assert segs(B=1, T=0, H=12) == 1
+    assert segs(B=0) == 0
+    # packed sequences, and a walk that applies the output stage itself, never split
+    f = Fake()
+    assert segs(B=1, T=65536, H=12, cu_seqlens=f(), n_seqs=1) == 1
+    assert segs(B=1, T=65536, H=2, D=64, o_norm_w=f()) == 1
+    nrec = 12 * 1024
+    rec = 74240  # one chunk record at C = 64, D = 128, bf16
+    head = (256 + 4 * nrec + 255) // 256 * 256
+    assert kda.kda_prefill_workspace_bytes(prefill(B=1, T=65536, H=12)) == \
+        head + nrec * rec + 12 * (3 * 10 - 2) * 128 * 128 * 4
 
 
 @pytest.mark.parametrize("field,value,code", [

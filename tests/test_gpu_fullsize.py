@@ -26,7 +26,7 @@ from oracle.pool import (backward_pair, decode_seq, prefill_pair, run, save_arra
 pytestmark = pytest.mark.gpu
 
 BLOCK_TOL = 5e-2
-FULL = ["prefill-4k", "prefill-b4-8k-s0", "prefill-64k"]
+FULL = ["prefill-4k", "prefill-b4-8k-s0", "prefill-64k", "prefill-64k-h12"]
 
 
 def summarize(label, res, tol):
