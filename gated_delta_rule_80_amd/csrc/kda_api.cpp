@@ -112,8 +112,9 @@ StateCfg state_config(int B, int H, int D, bool fp32, bool gn) {
 
 // Split state walk (kda_split.hip): segments per (sequence, head) and their
 // length in chunks.  Only whole-sequence walks of B equal-length sequences
-// split (not time slices, packed sequences, the backward's checkpointing walk
-// or a walk that applies the output stage itself).  Splitting adds the segment
+// split (not time slices, packed sequences or a walk that applies the output
+// stage itself); the backward's walks, forward and reverse, split as the
+// forward it runs does.  Splitting adds the segment
 // maps (the N and M walks of every segment but the last, about as many products
 // again as the plain walk's) and a short composition in exchange for a chain of
 // seg_len instead of all chunk steps, which pays while the walks leave CUs idle:
@@ -362,13 +363,13 @@ static kda_status run_stage(const kda_prefill_args* a, void* ws, int stage, hipS
       p.o_norm_w = a->o_norm_w;
       p.o_norm_eps = a->o_norm_eps;
       p.ckpt = bo != nullptr ? bo->ckS : nullptr;
-      const SplitPlan sp = sl == nullptr && bo == nullptr ? split_plan(a) : SplitPlan{};
+      const SplitPlan sp = sl == nullptr ? split_plan(a) : SplitPlan{};
       if (sp.nseg > 1) {
         kda::SplitParams q{};
         q.ws = p.ws;
         q.S0 = a->S0;
         q.maps = reinterpret_cast<float*>(static_cast<char*>(ws) + wl.split);
-        q.starts = q.maps + (size_t)a->B * a->H * (sp.nseg - 1) * 2 * a->D * a->D;
+        q.starts = q.maps + (size_t)a->B * a->H * (sp.nseg - 1) * 3 * a->D * a->D;
         q.B = a->B; q.H = a->H; q.NT = NT;
         q.nseg = sp.nseg; q.seg_len = sp.seg_len;
         if (kda_status e = hip_status(kda::launch_split_maps(q, a->D, a->chunk, fp32, cfg.vb,
@@ -628,8 +629,19 @@ struct BwdLayout {
   size_t nfront;  // front-end block slots per head (filter partials)
 };
 
+// The forward that the backward runs: the mixer without the output stage (the
+// stage is differentiated and applied separately).  Its workspace layout, split
+// walk included, is the base of the backward's.
+kda_prefill_args forward_of_backward(const kda_prefill_args* f) {
+  kda_prefill_args f0 = *f;
+  f0.o_norm_w = nullptr;
+  f0.o_gate = nullptr;
+  return f0;
+}
+
 BwdLayout bwd_layout(const kda_backward_args* a) {
   const kda_prefill_args* f = &a->fwd;
+  const kda_prefill_args f0 = forward_of_backward(f);
   BwdLayout L{};
   PrefillSizes sz;
   prefill_sizes(f, sz);
@@ -637,7 +649,7 @@ BwdLayout bwd_layout(const kda_backward_args* a) {
   const size_t C = (size_t)f->chunk, D = (size_t)f->D;
   const size_t x = (size_t)f->B * f->T * f->H * D;  // elements of one [B][T][H][D] tensor
   const size_t bth = (size_t)f->B * f->T * f->H;
-  size_t off = kda::round_up(ws_layout(f).bytes, 256);
+  size_t off = kda::round_up(ws_layout(&f0).bytes, 256);
   auto take = [&](size_t floats) {
     const size_t o = off;
     off = kda::round_up(off + floats * 4, 256);
@@ -788,9 +800,7 @@ kda_status kda_prefill_backward(const kda_backward_args* a, void* ws, size_t ws_
   // walk leaves the mixer's output in o; the stage's backward reads it, then the
   // stage finishes o in place.
   const bool gn = f->o_norm_w != nullptr || f->o_gate != nullptr;
-  kda_prefill_args f0 = *f;
-  f0.o_norm_w = nullptr;
-  f0.o_gate = nullptr;
+  const kda_prefill_args f0 = forward_of_backward(f);
   BwdFwdOut bo{wsb + L.y, F(L.gam), F(L.beta), F(L.tT), wsb + L.ckS};
   for (int stage : {KDA_STAGE_PREP, KDA_STAGE_STATE})
     if (kda_status e = run_stage(&f0, ws, stage, st, &bo); e != KDA_OK) return e;
@@ -837,7 +847,7 @@ kda_status kda_prefill_backward(const kda_backward_args* a, void* ws, size_t ws_
     if (kda_status e = hip_status(kda::launch_seq_index(ip, st)); e != KDA_OK) return e;
   }
   kda::BwdLaunch B{};
-  const char* recs = wsb + ws_layout(f).records;
+  const char* recs = wsb + ws_layout(&f0).records;
   B.walk.ws = recs;
   B.walk.dO = dO;
   B.walk.dS_T = a->dS_T;
@@ -846,6 +856,13 @@ kda_status kda_prefill_backward(const kda_backward_args* a, void* ws, size_t ws_
   B.walk.ckdS = wsb + L.ckdS;
   B.walk.B = sz.NS; B.walk.T = f->T; B.walk.H = f->H; B.walk.NT = sz.NT;  // one walk per sequence
   B.walk.seqs = seqs;
+  // split as the forward walk above was: its maps M are the reverse walk's too
+  if (const SplitPlan sp = split_plan(&f0); sp.nseg > 1) {
+    B.walk.nseg = sp.nseg;
+    B.walk.seg_len = sp.seg_len;
+    B.walk.maps = reinterpret_cast<float*>(wsb + ws_layout(&f0).split);
+    B.walk.starts = B.walk.maps + (size_t)f->B * f->H * (sp.nseg - 1) * 3 * f->D * f->D;
+  }
   B.prod.ws = recs;
   B.prod.dO = dO;
   B.prod.ckS = wsb + L.ckS;

@@ -83,7 +83,13 @@ struct BwdImage {
 //               + A = Ktil rows t (KT's column t, k = c),  B = dS'^T rows v
 //   dS (c, v):  A = QL^T rows c (QL's column c, k = t),   B = dO^T rows v;
 //               - A = W^T rows c,                         B = dU^T rows v
-template <int D, int C, int VB, typename IO, typename E, int NT>
+// Split walk (p.nseg > 1): one workgroup per (sequence, head, segment, value
+// block) walking the segment's chunks from the gradient of its end state in
+// p.starts; only segment 0 writes dS0.  MAPW: the segments' reverse maps
+// instead, for segments 1 .. nseg - 1: the walk from a zero end gradient (from
+// dS_T for the last segment) with nothing stored per chunk, its result (the
+// gradient of the segment's start state) written to the N slot of segment s - 1.
+template <int D, int C, int VB, typename IO, typename E, int NT, bool MAPW>
 __global__ __launch_bounds__(NT, 1) void kda_bwd_walk_kernel(BwdWalkParams p) {
   constexpr int NW = NT / 64;
   constexpr int PE = 16 / (int)sizeof(E);
@@ -115,8 +121,14 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_walk_kernel(BwdWalkParams p) {
   // the same XCD (workgroups are dealt round robin over the 8 XCDs), so the
   // second read of a record is served by that XCD's L2.
   const int total = p.B * p.H * NV;
-  int bh, vblk;
-  if (total % (8 * NV) == 0) {
+  int bh, vblk, seg = 0;
+  if (p.nseg > 1) {
+    // (head, segment) groups of NV workgroups, numbered XCD by XCD
+    const int grp = xcd_major(blockIdx.x, gridDim.x);
+    vblk = grp % NV;
+    bh = grp / NV % (p.B * p.H);
+    seg = grp / NV / (p.B * p.H) + (MAPW ? 1 : 0);
+  } else if (total % (8 * NV) == 0) {
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
     vblk = slot % NV;
     bh = (slot / NV) * 8 + xcd;
@@ -138,6 +150,12 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_walk_kernel(BwdWalkParams p) {
     nch = (Tq + C - 1) / C;
     if (c0 + nch > p.NT) nch = c0 < p.NT ? p.NT - c0 : 0;  // inconsistent tables: stay in the head's slots
     rec0 = (size_t)h * p.NT + c0;
+  }
+  // this workgroup's chunks [n_lo, n_hi) of the sequence
+  int n_lo = 0, n_hi = nch;
+  if (p.nseg > 1) {
+    n_lo = seg * p.seg_len;
+    n_hi = n_lo + p.seg_len < nch ? n_lo + p.seg_len : nch;
   }
 
   const int R = wave % RT;
@@ -210,18 +228,24 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_walk_kernel(BwdWalkParams p) {
     }
   };
 
-  // ---- dS: initial value dS_T (or zero), staged to LDS as the B operand
+  // ---- dS: initial value dS_T (or zero; a segment's from the composed
+  // gradients), staged to LDS as the B operand
   f32x4 accS[NS];
   const size_t sbase = (size_t)bh * D * D;
+  const float* g_in = p.dS_T != nullptr ? p.dS_T + sbase : nullptr;
+  if (p.nseg > 1) {
+    if constexpr (MAPW) g_in = seg == p.nseg - 1 ? g_in : nullptr;
+    else g_in = p.starts + ((size_t)bh * p.nseg + seg) * D * D;
+  }
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
     const int u = wave + NW * i;
     accS[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if ((FULL_S || u < CT * VT) && p.dS_T != nullptr) {
+    if ((FULL_S || u < CT * VT) && g_in != nullptr) {
       const int Ct = u % CT, Vt = u / CT;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        accS[i][e] = p.dS_T[sbase + (size_t)(16 * Ct + 4 * g4 + e) * D + vb0 + 16 * Vt + r];
+        accS[i][e] = g_in[(size_t)(16 * Ct + 4 * g4 + e) * D + vb0 + 16 * Vt + r];
     }
   }
   auto stage_state = [&]() {
@@ -243,11 +267,11 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_walk_kernel(BwdWalkParams p) {
   const E* iP = reinterpret_cast<const E*>(img + IMG::P);
   const float* iLC = reinterpret_cast<const float*>(img + IMG::LC);
 
-  if (nch > 0) {
-    issue_copy(nch - 1);
-    load_do(nch - 1);
+  if (n_hi > n_lo) {
+    issue_copy(n_hi - 1);
+    load_do(n_hi - 1);
   }
-  for (int n = nch - 1; n >= 0; --n) {
+  for (int n = n_hi - 1; n >= n_lo; --n) {
     __builtin_amdgcn_s_waitcnt(0);  // image and dO of chunk n
     stage_do(n);
     lds_barrier();
@@ -255,7 +279,7 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_walk_kernel(BwdWalkParams p) {
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       const int u = wave + NW * i;
-      if (FULL_S || u < CT * VT) {
+      if (!MAPW && (FULL_S || u < CT * VT)) {
         const int Ct = u % CT, Vt = u / CT;
         E* ck = static_cast<E*>(p.ckdS) + (rec0 + n) * D * D + vb0 + 16 * Vt + r;
 #pragma unroll
@@ -280,7 +304,7 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_walk_kernel(BwdWalkParams p) {
       flc[jj] = *reinterpret_cast<const f32x4*>(iLC + 16 * Ct + 4 * g4);
     }
     lds_barrier();  // every wave holds its fragments: the image may be overwritten
-    if (n > 0) {
+    if (n > n_lo) {
       issue_copy(n - 1);
       load_do(n - 1);
     }
@@ -299,9 +323,11 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_walk_kernel(BwdWalkParams p) {
         mma<C>(acc, fpt, fo);
         mma<D>(acc, fkt, fs);
         store4(&sDU[(16 * Vt + r) * LU + 16 * R + 4 * g4], acc[0], acc[1], acc[2], acc[3]);
-        E* du = static_cast<E*>(p.dU) + (rec0 + n) * C * D + vb0 + 16 * Vt + r;  // dU [t][v]
+        if constexpr (!MAPW) {
+          E* du = static_cast<E*>(p.dU) + (rec0 + n) * C * D + vb0 + 16 * Vt + r;  // dU [t][v]
 #pragma unroll
-        for (int e = 0; e < 4; ++e) du[(size_t)(16 * R + 4 * g4 + e) * D] = from_f32<E>(acc[e]);
+          for (int e = 0; e < 4; ++e) du[(size_t)(16 * R + 4 * g4 + e) * D] = from_f32<E>(acc[e]);
+        }
       }
     }
     lds_barrier();  // sDU complete; every read of sS for this chunk is done
@@ -324,7 +350,11 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_walk_kernel(BwdWalkParams p) {
     }
     stage_state();
   }
-  if (p.dS0 != nullptr) {
+  // the gradient of the start state: dS0, or a segment's reverse map
+  float* g_out = seg == 0 && p.dS0 != nullptr ? p.dS0 + sbase : nullptr;
+  if constexpr (MAPW)
+    g_out = p.maps + ((size_t)bh * (p.nseg - 1) + (seg - 1)) * 3 * D * D;
+  if (g_out != nullptr) {
 #pragma unroll
     for (int i = 0; i < NS; ++i) {
       const int u = wave + NW * i;
@@ -332,7 +362,7 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_walk_kernel(BwdWalkParams p) {
         const int Ct = u % CT, Vt = u / CT;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          p.dS0[sbase + (size_t)(16 * Ct + 4 * g4 + e) * D + vb0 + 16 * Vt + r] = accS[i][e];
+          g_out[(size_t)(16 * Ct + 4 * g4 + e) * D + vb0 + 16 * Vt + r] = accS[i][e];
       }
     }
   }
@@ -1664,15 +1694,28 @@ static hipError_t launch_bwd_t(const BwdLaunch& L, hipStream_t st) {
   // records (packed: one row of tokens, H * NT slots); walks per (sequence, head)
   const size_t nrec = (size_t)L.prod.B * L.prod.H * L.prod.NT;
   const size_t BH = (size_t)L.walk.B * L.walk.H;
-  // reverse walk: the forward walk's value blocks
-  if constexpr (D == 128 && sizeof(E) == 2) {
-    hipLaunchKernelGGL((kda_bwd_walk_kernel<D, C, 64, IO, E, 512>), dim3((unsigned)(BH * 2)), dim3(512),
-                       0, st, L.walk);
-  } else {
-    constexpr int VB = D >= 64 ? 64 : D;
-    hipLaunchKernelGGL((kda_bwd_walk_kernel<D, C, VB, IO, E, 256>), dim3((unsigned)(BH * (D / VB))),
-                       dim3(256), 0, st, L.walk);
+  // reverse walk, one workgroup per value block of 64 columns (of D when D < 64);
+  // split: the segments' reverse maps, their composition, the segment walks
+  constexpr bool WIDE = D == 128 && sizeof(E) == 2;
+  constexpr int WVB = WIDE ? 64 : (D >= 64 ? 64 : D);
+  constexpr int WNT = WIDE ? 512 : 256;
+  const size_t walks = BH * (D / WVB);
+  if (L.walk.nseg > 1) {
+    hipLaunchKernelGGL((kda_bwd_walk_kernel<D, C, WVB, IO, E, WNT, true>),
+                       dim3((unsigned)(walks * (L.walk.nseg - 1))), dim3(WNT), 0, st, L.walk);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    SplitParams q{};
+    q.S0 = L.walk.dS_T;
+    q.maps = L.walk.maps;
+    q.starts = L.walk.starts;
+    q.B = L.walk.B; q.H = L.walk.H; q.NT = L.walk.NT;
+    q.nseg = L.walk.nseg; q.seg_len = L.walk.seg_len;
+    q.reverse = 1;
+    if (hipError_t e = launch_split_combine(q, D, st); e != hipSuccess) return e;
   }
+  hipLaunchKernelGGL((kda_bwd_walk_kernel<D, C, WVB, IO, E, WNT, false>),
+                     dim3((unsigned)(walks * (L.walk.nseg > 1 ? L.walk.nseg : 1))), dim3(WNT), 0, st,
+                     L.walk);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   hipLaunchKernelGGL((kda_bwd_prod_kernel<D, C, IO, E>), dim3((unsigned)nrec), dim3(256), 0, st, L.prod);
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;

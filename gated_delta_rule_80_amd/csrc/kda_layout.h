@@ -67,24 +67,31 @@ constexpr WorkspaceLayout workspace_layout(size_t nrec, int C, int D, size_t esi
 // product of the chunks' homogeneous maps S -> Diag(Lambda_C) S - Ktil^T W S and
 // N the end state from zero.  The chunks of every (sequence, head) are cut into
 // nseg segments of seg_len chunks (the last one shorter); each segment's N and M
-// are walked in parallel, the segment start states are composed from them in
-// order, and then every segment is walked with its outputs from its own start.
-//   maps   [B*H][nseg - 1][2][D][D] float32, for segments s < nseg - 1: N row-major
-//          [key][value] (for s = 0 walked from S0 itself, so it is the state at
-//          the start of segment 1), then M transposed, Mt[j][c] = M[c][j]
-//          (not written for s = 0);
+// are walked in parallel, the segment start states are composed in order, and
+// then every segment is walked with its outputs from its own start.
+//   maps   [B*H][nseg - 1][3][D][D] float32, for segments s < nseg - 1: N
+//          row-major [key][value] (for s = 0 walked from S0 itself, so it is the
+//          state at the start of segment 1), then M transposed, Mt[j][c] =
+//          M[c][j], then M row-major (the two M slots not written for s = 0);
 //   starts [B*H][nseg][D][D] float32: the state at each segment's start.
+// The reverse walk of the backward is affine in the same way: the gradient of a
+// segment's start state is M^T (the gradient of its end state) + N', with N'
+// the reverse walk of the segment from a zero end gradient (from dS_T for the
+// last segment).  It reuses both buffers once the forward walk is done: N'_s in
+// the N slot of segment s - 1 (s >= 1), and in starts[s] the gradient of the
+// state at the end of segment s; reverse = 1 composes these from dS_T down.
 struct SplitParams {
   const char* ws;     // first record
-  const float* S0;    // [B][H][D][D] or NULL (zeros)
+  const float* S0;    // [B][H][D][D] or NULL (zeros); reverse: dS_T
   float* maps;
   float* starts;
   int B, H, NT;       // NT: chunk records per (sequence, head)
   int nseg, seg_len;
+  int reverse;
 };
 
 constexpr size_t split_bytes(size_t BH, int nseg, int D) {
-  return nseg > 1 ? BH * (size_t)(3 * nseg - 2) * D * D * 4 : 0;
+  return nseg > 1 ? BH * (size_t)(4 * nseg - 3) * D * D * 4 : 0;
 }
 
 // Packed sequences: sequence i is tokens [bounds[i], bounds[i + 1]) and owns
@@ -198,6 +205,11 @@ struct BwdWalkParams {
   void* ckdS;
   int B, T, H, NT;   // B: sequences (packed: n_seqs)
   SeqTables seqs;    // packed sequences, or bounds NULL
+  // split walk (nseg > 1, equal-length sequences; SplitParams): the segments'
+  // reverse maps N' go to maps, the composed end gradients come from starts
+  int nseg, seg_len;
+  float* maps;
+  float* starts;
 };
 
 struct BwdProdParams {

@@ -10,7 +10,9 @@
 // states are composed in order (one D x D product per segment), and every
 // segment is then walked with its outputs from its own start.  The composition
 // is exact in exact arithmetic; only the rounding order differs from one long
-// walk.
+// walk.  The backward's reverse walk composes the gradients of the segments'
+// end states the same way with the transposed maps (its map walks live with
+// the reverse walk kernel; the composition is the kernel below, reversed).
 #include "kda_device.h"
 #include "kda_launch.h"
 #include "kda_layout.h"
@@ -214,28 +216,33 @@ __global__ __launch_bounds__(NT, 2) void kda_seg_map_kernel(SplitParams p) {
     }
     stage_state();
   }
-  // ---- N row-major, or the rows vb0 .. of Mt (4 consecutive key channels a lane)
-  float* out = p.maps + ((size_t)grp * 2 + kind) * D * D;
+  // ---- N or M row-major, and the rows vb0 .. of Mt (4 consecutive key channels
+  // a lane)
+  float* slots = p.maps + (size_t)grp * 3 * D * D;
+  float* out = slots + (kind == 1 ? 2 : 0) * (size_t)D * D;
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
     const int u = wave + NW * i;
     if (FULL_S || u < CT * VT) {
       const int Ct = u % CT, Vt = u / CT;
       const int c = 16 * Ct + 4 * g4, v = vb0 + 16 * Vt + r;
-      if (kind == 1) {
-        store4(out + (size_t)v * D + c, accS[i][0], accS[i][1], accS[i][2], accS[i][3]);
-      } else {
+      if (kind == 1)
+        store4(slots + (size_t)D * D + (size_t)v * D + c, accS[i][0], accS[i][1], accS[i][2],
+               accS[i][3]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) out[(size_t)(c + e) * D + v] = accS[i][e];
-      }
+      for (int e = 0; e < 4; ++e) out[(size_t)(c + e) * D + v] = accS[i][e];
     }
   }
 }
 
-// Segment start states in order: starts[0] = S0 (or zeros), starts[1] = N_0,
-// starts[s + 1] = M_s starts[s] + N_s, in float32.  One workgroup per (sequence,
-// head, block of CW value columns); thread (row group rg, column col) holds rows
-// rg RPT .. rg RPT + RPT - 1 of its column.  Mt_s is copied into LDS whole.
+// Segment start states in order, in float32.  Forward: starts[0] = S0 (or
+// zeros), starts[1] = N_0, starts[s + 1] = M_s starts[s] + N_s.  Reverse (the
+// gradients of the segments' end states): starts[nseg - 1] = dS_T (or zeros),
+// starts[nseg - 2] = N'_{nseg-1}, starts[s - 1] = M_s^T starts[s] + N'_s.  Both
+// are X_next = A X + N with A held as sA[k][row]: Mt_s for M_s, M_s row-major for
+// M_s^T.  One workgroup per (sequence, head, block of CW value columns); thread
+// (row group rg, column col) holds rows rg RPT .. rg RPT + RPT - 1 of its
+// column.  A is copied into LDS whole.
 template <int D>
 __global__ __launch_bounds__(256) void kda_seg_combine_kernel(SplitParams p) {
   constexpr int CW = D >= 64 ? 8 : 16;  // columns per workgroup
@@ -243,58 +250,64 @@ __global__ __launch_bounds__(256) void kda_seg_combine_kernel(SplitParams p) {
   constexpr int RG = 256 / CW;          // row groups
   constexpr int RPT = D / RG;           // rows per thread
   static_assert(RPT >= 1 && RPT * RG == D, "rows split evenly");
-  __shared__ __attribute__((aligned(16))) float sM[D * D];
+  __shared__ __attribute__((aligned(16))) float sA[D * D];
   __shared__ float sX[D * CW];
   const int tid = threadIdx.x, wave = tid >> 6;
   const int bh = blockIdx.x / NCB, cb = blockIdx.x % NCB;
   const int col = tid % CW, rg = tid / CW;
   const int v = cb * CW + col, c0 = rg * RPT;
-  const int nseg1 = p.nseg - 1;
+  const int nseg = p.nseg;
+  const bool rev = p.reverse != 0;
   const size_t DD = (size_t)D * D;
-  float* st = p.starts + (size_t)bh * p.nseg * DD;
-  const float* mp = p.maps + (size_t)bh * nseg1 * 2 * DD;
+  float* st = p.starts + (size_t)bh * nseg * DD;
+  const float* mp = p.maps + (size_t)bh * (nseg - 1) * 3 * DD;
+  auto slot = [&](int s, int k) { return mp + ((size_t)s * 3 + k) * DD; };
+  const int first = rev ? nseg - 1 : 0, second = rev ? nseg - 2 : 1;
+  const float* n1 = slot(rev ? nseg - 2 : 0, 0);
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const size_t e = (size_t)(c0 + i) * D + v;
-    st[e] = p.S0 != nullptr ? p.S0[(size_t)bh * DD + e] : 0.f;
-    const float x = mp[e];  // N_0
-    st[DD + e] = x;
+    st[first * DD + e] = p.S0 != nullptr ? p.S0[(size_t)bh * DD + e] : 0.f;
+    const float x = n1[e];
+    st[second * DD + e] = x;
     sX[(c0 + i) * CW + col] = x;
   }
-  for (int s = 1; s < nseg1; ++s) {
-    const float* Mt = mp + ((size_t)s * 2 + 1) * DD;
-    const float* N = mp + (size_t)s * 2 * DD;
+  for (int k = 1; k < nseg - 1; ++k) {
+    const int s = rev ? nseg - 1 - k : k;
+    const float* A = slot(s, rev ? 2 : 1);
+    const float* N = rev ? slot(s - 1, 0) : slot(s, 0);
+    float* out = st + (size_t)(rev ? s - 1 : s + 1) * DD;
     // 16 bytes a lane; the lanes of a wave fill 64 consecutive pieces
-    for (int k = 0; k < (int)(DD / 4); k += 256)
-      if (k + tid < (int)(DD / 4))
-        __builtin_amdgcn_global_load_lds((const glb_void_t*)(Mt + 4 * (size_t)(k + tid)),
-                                         (lds_void_t*)(sM + 4 * (k + 64 * wave)), 16, 0, 0);
+    for (int q = 0; q < (int)(DD / 4); q += 256)
+      if (q + tid < (int)(DD / 4))
+        __builtin_amdgcn_global_load_lds((const glb_void_t*)(A + 4 * (size_t)(q + tid)),
+                                         (lds_void_t*)(sA + 4 * (q + 64 * wave)), 16, 0, 0);
     float acc[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) acc[i] = N[(size_t)(c0 + i) * D + v];
     __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();  // Mt_s and starts[s] are in LDS
+    __syncthreads();  // A and the previous X are in LDS
 #pragma unroll 4
     for (int j = 0; j < D; ++j) {
       const float xj = sX[j * CW + col];
-      const float* mrow = sM + j * D + c0;
+      const float* arow = sA + j * D + c0;
       if constexpr (RPT % 4 == 0) {
 #pragma unroll
         for (int q = 0; q < RPT / 4; ++q) {
-          const f32x4 m = *reinterpret_cast<const f32x4*>(mrow + 4 * q);
+          const f32x4 m = *reinterpret_cast<const f32x4*>(arow + 4 * q);
 #pragma unroll
           for (int e = 0; e < 4; ++e) acc[4 * q + e] = fmaf(m[e], xj, acc[4 * q + e]);
         }
       } else {
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) acc[i] = fmaf(mrow[i], xj, acc[i]);
+        for (int i = 0; i < RPT; ++i) acc[i] = fmaf(arow[i], xj, acc[i]);
       }
     }
-    __syncthreads();  // every read of sM and sX for this segment is done
+    __syncthreads();  // every read of sA and sX for this step is done
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       sX[(c0 + i) * CW + col] = acc[i];
-      st[(size_t)(s + 1) * DD + (size_t)(c0 + i) * D + v] = acc[i];
+      out[(size_t)(c0 + i) * D + v] = acc[i];
     }
   }
 }
@@ -302,6 +315,7 @@ __global__ __launch_bounds__(256) void kda_seg_combine_kernel(SplitParams p) {
 template <int D, int C, typename E>
 static hipError_t launch_maps_t(const SplitParams& p, int vb, int threads, hipStream_t st) {
   const size_t groups = (size_t)p.B * p.H * (p.nseg - 1);
+  if (p.reverse != 0) return hipErrorInvalidValue;
   if constexpr (D == 128) {
     if (vb == 64 && threads == 512) {
       hipLaunchKernelGGL((kda_seg_map_kernel<D, C, 64, E, 512>), dim3((unsigned)(groups * 2 * 2)),

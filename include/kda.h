@@ -194,7 +194,9 @@ kda_status kda_prefill_stage(const kda_prefill_args* a, void* ws, size_t ws_byte
  * sequences with T > 0 split, and never a walk that applies the output stage
  * itself.  The results agree with the unsplit walk's to rounding (the same sums
  * in another order); the workspace includes the segments' maps and start states
- * (3 nseg - 2 float32 D x D matrices per (sequence, head)). */
+ * (4 nseg - 3 float32 D x D matrices per (sequence, head)).  kda_prefill_backward
+ * splits both of its walks the same way: the reverse walk is affine in the
+ * gradient of the end state with the transposed maps M^T of the forward. */
 int kda_prefill_walk_segments(const kda_prefill_args* a);
 
 /* For callers that cannot allocate device memory -- code under HIP graph

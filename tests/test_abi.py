@@ -117,7 +117,7 @@ def test_walk_segments_plan(lib):
     rec = 74240  # one chunk record at C = 64, D = 128, bf16
     head = (256 + 4 * nrec + 255) // 256 * 256
     assert kda.kda_prefill_workspace_bytes(prefill(B=1, T=65536, H=12)) == \
-        head + nrec * rec + 12 * (3 * 10 - 2) * 128 * 128 * 4
+        head + nrec * rec + 12 * (4 * 10 - 3) * 128 * 128 * 4
 
 
 @pytest.mark.parametrize("field,value,code", [
@@ -370,6 +370,16 @@ def backward(**kw):
     for k, v in kw.items():
         setattr(a, k, v)
     return a
+
+
+def test_backward_workspace_holds_the_forward(lib):
+    """The backward's workspace starts with its forward's (records and, when the
+    walk splits, the segment maps that the reverse walk reuses) and stays within
+    a bounded multiple of it."""
+    for kw in (dict(B=1, T=100, H=4), dict(B=1, T=65536, H=12), dict(B=2, T=4096, H=96)):
+        fwd = kda.kda_prefill_workspace_bytes(prefill(**kw))
+        bwd = kda.kda_backward_workspace_bytes(backward(fwd=prefill(**kw)))
+        assert fwd > 0 and fwd < bwd < 40 * fwd, (kw, fwd, bwd)
 
 
 def test_backward_validation(lib):

@@ -1,4 +1,4 @@
-"""The split state walk against the fp64 oracle.
+"""The split state walk against the fp64 oracle, forward and backward.
 
 When a call has few (sequence, head) walks and long sequences, the library cuts
 each walk into segments: every segment's affine map (S_end = M S_start + N) is
@@ -103,11 +103,7 @@ def test_split_walk_long_memory(io, D, chunk, T):
     with the initial state removed, the outputs of the last segment change by
     far more than the tolerance, and with it they match the oracle."""
     w = small(B=1, T=T, H=1, D=D, io=io, chunk=chunk, s0=True, conv_state=True)
-    inp = make(w, seed=T)
-    dt = inp["g"].dtype
-    inp["g"] = (inp["g"].float() * 1e-3).to(dt)
-    inp["beta"] = (inp["beta"].float() * 0.05).to(dt)
-    inp["S0"] = inp["S0"] * 20.0
+    inp = long_memory(make(w, seed=T))
     nseg = kda.kda_prefill_walk_segments(args_of(inp, chunk))
     assert nseg >= 3
     o, S, _ = gpu_prefill(inp, chunk)
@@ -122,3 +118,30 @@ def test_split_walk_long_memory(io, D, chunk, T):
           f"initial state's share of the last segment's output {reach:.2e}", flush=True)
     assert reach > 20 * tol
     assert eo <= tol and eS <= tol and el <= tol, (eo, eS, el)
+
+
+def long_memory(inp):
+    """Slow decay, small write strengths, a large initial state: the state and
+    its gradient carry across every segment boundary."""
+    dt = inp["g"].dtype
+    return dict(inp, g=(inp["g"].float() * 1e-3).to(dt), beta=(inp["beta"].float() * 0.05).to(dt),
+                S0=inp["S0"] * 20.0)
+
+
+@pytest.mark.parametrize("io,D,chunk,B,H,T,slow", [
+    ("bf16", 128, 64, 1, 1, 64 * 70 + 5, False),
+    ("bf16", 128, 64, 1, 1, 64 * 70 + 5, True),
+    ("fp32", 64, 32, 1, 1, 32 * 96 + 7, True),
+    ("fp32", 128, 16, 1, 1, 16 * 130, True),
+    ("bf16", 32, 32, 2, 1, 32 * 70 + 1, False),
+])
+def test_split_backward_matches_oracle(io, D, chunk, B, H, T, slow):
+    """kda_prefill_backward splits its forward and reverse walks as the forward
+    does; every gradient against the oracle's reverse-mode gradients."""
+    from test_gpu_backward import check_backward_inputs
+    w = small(B=B, T=T, H=H, D=D, io=io, chunk=chunk, s0=True, conv_state=True)
+    inp = make(w, seed=T + D)
+    if slow:
+        inp = long_memory(inp)
+    assert kda.kda_prefill_walk_segments(args_of(inp, chunk)) >= 2
+    check_backward_inputs(w, chunk, inp, seed=T)
