@@ -58,6 +58,7 @@ KERNEL_SOURCES = ["gated_delta_rule_80_amd/csrc/kda_prep.hip",
 HEADLINE = "prefill-64k"
 ALSO = "prefill-4k,prefill-b4-8k-s0,prefill-64k-h12"
 STAGES_WORKLOAD = "prefill-4k"
+TP_SHARE_WORKLOAD = "prefill-64k-h12"
 METRIC = "KDA tokens/s per GPU (prefill, H=96 d=128) + decode seq/s; % of roofline"
 
 
@@ -254,7 +255,12 @@ def measure_prefill(kda, torch, w, args, stream, dev, keep_inputs=False):
     dom = 0 if stage_ms[0] >= stage_ms[1] else 1
     kname = STAGE_NAMES[dom]
     achieved = nb / (stage_ms[dom] / 1e3)
-    roofline = {"bound": "hbm", "kernel": kname,
+    nseg = kda.kda_prefill_walk_segments(a)
+    label = kname
+    if dom == 1 and nseg > 1:
+        label = (f"{kname} (walk split into {nseg} segments: kda_seg_map_kernel, "
+                 f"kda_seg_combine_kernel, then {kname})")
+    roofline = {"bound": "hbm", "kernel": label,
                 "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK, "traffic": traffic_for(w.name, kname),
                 "algorithmic_bytes": nb, "mean_launch_ms": stage_ms[dom],
@@ -266,7 +272,8 @@ def measure_prefill(kda, torch, w, args, stream, dev, keep_inputs=False):
             "attainable_frac": max(flops / BF16_PEAK, nb / HBM_PEAK) / t,
             "stage_ms": {STAGE_NAMES[i]: stage_ms[i] for i in range(2)}}
     out = {"workload": w.name, "config": {"B": w.B, "T": w.T, "H": w.H, "D": w.D, "chunk": w.chunk,
-                                          "io": w.io, "state": "fp32", "S0": w.s0_std > 0},
+                                          "io": w.io, "state": "fp32", "S0": w.s0_std > 0,
+                                          "walk_segments": nseg},
            "ms_per_step": ms, "tokens_per_s": w.B * w.T / t, "roofline": roofline, "path": path}
     del ws, o, S_T, cso, a
     if not keep_inputs:
@@ -718,6 +725,11 @@ def main(argv=None) -> int:
                                                       stages=True)
         stages["backward_packed"] = backward_leg(kda, torch, ws4, args, stream, dev, base_ms,
                                                  packed=True)
+        # the backward of one GPU's share of the heads at long context (split walks)
+        wtp = WORKLOADS[TP_SHARE_WORKLOAD]
+        tp = others.get(wtp.name) or (head if w.name == wtp.name else None)
+        stages["backward_tp_share"] = backward_leg(kda, torch, wtp, args, stream, dev,
+                                                   tp["ms_per_step"] if tp else float("nan"))
 
     if args.calib_copy_mib > 0:
         calibration_copy(kda, torch, args.calib_copy_mib, stream, dev)
