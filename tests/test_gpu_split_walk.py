@@ -145,3 +145,53 @@ def test_split_backward_matches_oracle(io, D, chunk, B, H, T, slow):
         inp = long_memory(inp)
     assert kda.kda_prefill_walk_segments(args_of(inp, chunk)) >= 2
     check_backward_inputs(w, chunk, inp, seed=T)
+
+
+def test_split_walk_stages_static_entry_and_optional_stages():
+    """With every optional stage on (decay and beta from raw projections, the
+    output norm and gate), a split call's stages (0, 1, 2, 3 and 0, 4, 3) and the
+    entry point without a workspace argument (whose scratch holds this call's whole
+    workspace, so it splits the same way) give kda_prefill's results bit for bit,
+    and kda_prefill matches the oracle."""
+    from kda_inputs import make_stage_inputs, to_numpy
+    from oracle import kda_reference
+    w = small(B=1, T=64 * 70 + 9, H=2, D=128, io="bf16", chunk=64, s0=True, conv_state=True)
+    inp = cuda(make(w, seed=21))
+    st = make_stage_inputs(w, seed=21, device="cuda")
+    kw = dict(A_log=st["A_log"], dt_bias=st["dt_bias"], beta_logits=True,
+              o_norm_w=st["o_norm_w"], o_gate=st["o_gate"])
+
+    def call(run):
+        o = torch.empty_like(inp["q"])
+        S_T = torch.empty(w.B, w.H, w.D, w.D, device="cuda")
+        cso = torch.empty(w.B, 3, 3, w.H * w.D, dtype=inp["q"].dtype, device="cuda")
+        a = kda.prefill_args(inp["q"], inp["k"], inp["v"], st["f"], st["b_logit"], inp["conv_w"],
+                             inp["conv_state"], inp["S0"], o, S_T, cso, chunk=64, **kw)
+        assert kda.kda_prefill_walk_segments(a) == 4
+        run(a)
+        torch.cuda.synchronize()
+        return o, S_T, cso
+
+    def with_ws(stages):
+        def run(a):
+            ws = torch.empty(kda.kda_prefill_workspace_bytes(a), dtype=torch.uint8, device="cuda")
+            if stages is None:
+                kda.kda_prefill_raw(a, ws)
+            else:
+                for s in stages:
+                    kda.kda_prefill_stage(a, ws, s)
+        return run
+
+    ref = call(with_ws(None))
+    for got in (call(with_ws((0, 1, 2, 3))), call(with_ws((0, kda.KDA_STAGE_STATE_TAIL, 3))),
+                call(lambda a: kda.kda_prefill_static_raw(a))):
+        for x, y in zip(ref, got):
+            assert torch.equal(x, y)
+    n = {k: to_numpy(v) for k, v in inp.items()}
+    ns = {k: to_numpy(v) for k, v in st.items()}
+    ro, rS, _ = kda_reference(n["q"], n["k"], n["v"], ns["f"], ns["b_logit"], conv_w=n["conv_w"],
+                              conv_state=n["conv_state"], S0=n["S0"], A_log=ns["A_log"],
+                              dt_bias=ns["dt_bias"], beta_sigmoid=True, o_norm_w=ns["o_norm_w"],
+                              o_gate=ns["o_gate"])
+    o = ref[0].float().cpu().numpy()
+    assert rel_l2(o, ro) <= TOL["bf16"] and rel_l2(ref[1].cpu().numpy(), rS) <= TOL["bf16"]
