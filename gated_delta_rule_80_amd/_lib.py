@@ -23,7 +23,7 @@ KDA_BF16 = 0
 KDA_FP32 = 1
 KDA_FLAG_L2NORM_QK = 1
 KDA_FLAG_BETA_LOGITS = 2
-ABI_VERSION = 5
+ABI_VERSION = 6
 KDA_STAGE_PREP, KDA_STAGE_STATE, KDA_STAGE_CONV_TAIL, KDA_STAGE_OUTPUT = 0, 1, 2, 3
 KDA_STAGE_STATE_TAIL = 4  # stages 1 and 2 in one launch, as kda_prefill runs them
 NUM_STAGES = 4
@@ -116,6 +116,10 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.kda_prefill_stage.argtypes = [P(PrefillArgs), _vp, ctypes.c_size_t, ctypes.c_int, _vp]
     lib.kda_prefill_walk_segments.restype = ctypes.c_int
     lib.kda_prefill_walk_segments.argtypes = [P(PrefillArgs)]
+    lib.kda_prefill_state_map_workspace_bytes.restype = ctypes.c_size_t
+    lib.kda_prefill_state_map_workspace_bytes.argtypes = [P(PrefillArgs)]
+    lib.kda_prefill_state_map.restype = ctypes.c_int
+    lib.kda_prefill_state_map.argtypes = [P(PrefillArgs), _vp, ctypes.c_size_t, _vp, _vp, _vp]
     lib.kda_validate_conv_norm.restype = ctypes.c_int
     lib.kda_validate_conv_norm.argtypes = [P(ConvNormArgs)]
     lib.kda_conv_norm.restype = ctypes.c_int
@@ -283,6 +287,44 @@ def kda_prefill_walk_segments(args: PrefillArgs) -> int:
     """Segments the state walk of kda_prefill(args) is split into (1: not split;
     0: invalid arguments).  Host only."""
     return int(load().kda_prefill_walk_segments(ctypes.byref(args)))
+
+
+def kda_prefill_state_map_workspace_bytes(args: PrefillArgs) -> int:
+    return int(load().kda_prefill_state_map_workspace_bytes(ctypes.byref(args)))
+
+
+def kda_prefill_state_map_raw(args: PrefillArgs, workspace, M, N, stream=None):
+    """kda_prefill_state_map on a pre-filled argument struct whose preparation
+    stage has run on `workspace` (no allocation)."""
+    ws = _ptr(workspace) if workspace is not None else None
+    nbytes = workspace.numel() if workspace is not None else 0
+    _check(load().kda_prefill_state_map(ctypes.byref(args), ws, nbytes, _ptr(M), _ptr(N),
+                                        _stream(stream)), "kda_prefill_state_map")
+
+
+def kda_prefill_state_map(q, k, v, g, beta, conv_w=None, conv_state=None, *, chunk=64, scale=1.0,
+                          l2norm_qk=True, eps=1e-6, A_log=None, dt_bias=None, beta_logits=False,
+                          stream=None):
+    """The affine state map of a prefill over these tokens: (M, N), each
+    [B, H, D, D] fp32, with S_T = M S_start + N for any start state.  Runs the
+    preparation stage, then the map (o and S_T of the arguments are allocated for
+    the call but not written)."""
+    B, T, H, D = q.shape
+    dev = q.device
+    o = torch.empty_like(q)
+    S_T = torch.empty(B, H, D, D, dtype=torch.float32, device=dev)
+    a = prefill_args(q, k, v, g, beta, conv_w, conv_state, None, o, S_T, None, chunk=chunk,
+                     scale=scale, l2norm_qk=l2norm_qk, eps=eps, A_log=A_log, dt_bias=dt_bias,
+                     beta_logits=beta_logits)
+    _check(kda_validate_prefill(a), "kda_prefill_state_map")
+    M = torch.empty(B, H, D, D, dtype=torch.float32, device=dev)
+    N = torch.empty_like(M)
+    need = kda_prefill_state_map_workspace_bytes(a)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev) if need > 0 else None
+    if T > 0:
+        kda_prefill_stage(a, ws, 0, stream)
+    kda_prefill_state_map_raw(a, ws, M, N, stream)
+    return M, N
 
 
 def kda_prefill_stage(args: PrefillArgs, workspace, stage: int, stream=None):

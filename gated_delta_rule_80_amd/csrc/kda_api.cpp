@@ -146,6 +146,23 @@ SplitPlan split_plan(const kda_prefill_args* a) {
   return sp;
 }
 
+// The state map of a whole call (kda_prefill_state_map) cuts the walks as the
+// split walk would, but into at least one segment, and maps every segment.
+SplitPlan map_plan(const kda_prefill_args* a) {
+  SplitPlan sp;
+  if (a->T <= 0 || a->chunk <= 0) return sp;
+  const StateCfg cfg = state_config(a->B, a->H, a->D, a->io == KDA_FP32, false);
+  const long walks = (long)a->B * a->H * (a->D / cfg.vb);
+  const long nch = ((long)a->T + a->chunk - 1) / a->chunk;
+  long P = kSplitWalks / walks;
+  if (nch / kMinSegChunks < P) P = nch / kMinSegChunks;
+  if (kMaxSegments < P) P = kMaxSegments;
+  if (P < 1) P = 1;
+  sp.seg_len = (int)((nch + P - 1) / P);
+  sp.nseg = (int)((nch + sp.seg_len - 1) / sp.seg_len);
+  return sp;
+}
+
 kda::WorkspaceLayout ws_layout(const kda_prefill_args* a) {
   PrefillSizes s;
   prefill_sizes(a, s);
@@ -473,6 +490,54 @@ kda_status kda_prefill_stage(const kda_prefill_args* a, void* ws, size_t ws_byte
   if (stage == KDA_STAGE_STATE_TAIL)
     return run_stage(a, ws, KDA_STAGE_STATE, static_cast<hipStream_t>(stream), nullptr, true);
   return run_stage(a, ws, stage, static_cast<hipStream_t>(stream));
+}
+
+size_t kda_prefill_state_map_workspace_bytes(const kda_prefill_args* a) {
+  if (kda_validate_prefill(a) != KDA_OK || packed(a) || a->T == 0) return 0;
+  const kda::WorkspaceLayout wl = ws_layout(a);
+  const SplitPlan sp = map_plan(a);
+  const size_t maps = (size_t)a->B * a->H * sp.nseg * 3 * a->D * a->D * 4;
+  return wl.split + maps > wl.bytes ? wl.split + maps : wl.bytes;
+}
+
+kda_status kda_prefill_state_map(const kda_prefill_args* a, void* ws, size_t ws_bytes, float* M,
+                                 float* N, void* stream) {
+  if (kda_status e = kda_validate_prefill(a); e != KDA_OK) return e;
+  if (packed(a)) return KDA_ERR_UNSUPPORTED;
+  if (M == nullptr || N == nullptr) return KDA_ERR_NULL;
+  if (!aligned16(M) || !aligned16(N)) return KDA_ERR_ALIGN;
+  PrefillSizes sz;
+  prefill_sizes(a, sz);
+  const Span m = span(M, sz.state), n = span(N, sz.state);
+  if (overlaps(m, n)) return KDA_ERR_ALIAS;
+  for (Span x : {span(a->q, sz.x), span(a->k, sz.x), span(a->v, sz.x), span(a->g, sz.x),
+                 span(a->beta, sz.bta), span(a->conv_w, sz.cw), span(a->conv_state_in, sz.cst),
+                 span(a->S0, sz.state), span(a->o, sz.x), span(a->S_T, sz.state),
+                 span(a->conv_state_out, sz.cst), span(a->A_log, (size_t)a->H * 4),
+                 span(a->dt_bias, (size_t)a->H * a->D * 4), span(a->o_norm_w, (size_t)a->D * 4),
+                 span(a->o_gate, sz.x)})
+    if (overlaps(m, x) || overlaps(n, x)) return KDA_ERR_ALIAS;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (a->T == 0)
+    return hip_status(kda::launch_state_map_identity(M, N, (size_t)a->B * a->H * a->D * a->D, a->D, st));
+  const size_t need = kda_prefill_state_map_workspace_bytes(a);
+  if (ws == nullptr || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0 || ws_bytes < need)
+    return KDA_ERR_WORKSPACE;
+  const Span w = span(ws, need);
+  if (overlaps(w, m) || overlaps(w, n)) return KDA_ERR_ALIAS;
+  const kda::WorkspaceLayout wl = ws_layout(a);
+  const SplitPlan sp = map_plan(a);
+  const StateCfg cfg = state_config(a->B, a->H, a->D, a->io == KDA_FP32, false);
+  kda::SplitParams q{};
+  q.ws = static_cast<const char*>(ws) + wl.records;
+  q.maps = reinterpret_cast<float*>(static_cast<char*>(ws) + wl.split);
+  q.B = a->B; q.H = a->H; q.NT = sz.NT;
+  q.nseg = sp.nseg; q.seg_len = sp.seg_len;
+  q.whole = 1;
+  q.nch = (a->T + a->chunk - 1) / a->chunk;
+  q.M_out = M;
+  q.N_out = N;
+  return hip_status(kda::launch_state_map(q, a->D, a->chunk, a->io == KDA_FP32, cfg.vb, cfg.threads, st));
 }
 
 int kda_prefill_walk_segments(const kda_prefill_args* a) {

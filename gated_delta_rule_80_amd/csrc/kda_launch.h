@@ -16,6 +16,11 @@ hipError_t launch_state(const StateParams& p, int D, int C, bool fp32, int vb, i
 hipError_t launch_split_maps(const SplitParams& p, int D, int C, bool fp32, int vb, int threads,
                              hipStream_t st);
 hipError_t launch_split_combine(const SplitParams& p, int D, hipStream_t st);
+// the state map of a whole call (SplitParams.whole): segment maps, then their
+// composition into M_out, N_out; and M = I, N = 0 for n matrices of D x D
+hipError_t launch_state_map(const SplitParams& p, int D, int C, bool fp32, int vb, int threads,
+                            hipStream_t st);
+hipError_t launch_state_map_identity(float* M, float* N, size_t n, int D, hipStream_t st);
 hipError_t launch_out_stage(const OutStageParams& p, int D, bool fp32, hipStream_t st);
 hipError_t launch_conv_norm(const ConvNormParams& p, int D, bool fp32, hipStream_t st);
 hipError_t launch_conv_tail(const TailParams& p, bool fp32, hipStream_t st);

@@ -80,6 +80,10 @@ constexpr WorkspaceLayout workspace_layout(size_t nrec, int C, int D, size_t esi
 // last segment).  It reuses both buffers once the forward walk is done: N'_s in
 // the N slot of segment s - 1 (s >= 1), and in starts[s] the gradient of the
 // state at the end of segment s; reverse = 1 composes these from dS_T down.
+// whole = 1 (the state map of a call): every segment's N (from zero, also for
+// the first) and M, maps [B*H][nseg][3][D][D], the last segment nch - (nseg - 1)
+// seg_len chunks long; the composition writes M and N of the whole call to
+// M_out and N_out [B][H][D][D].
 struct SplitParams {
   const char* ws;     // first record
   const float* S0;    // [B][H][D][D] or NULL (zeros); reverse: dS_T
@@ -88,6 +92,9 @@ struct SplitParams {
   int B, H, NT;       // NT: chunk records per (sequence, head)
   int nseg, seg_len;
   int reverse;
+  int whole, nch;     // state map of the whole call; chunks per sequence
+  float* M_out;
+  float* N_out;
 };
 
 constexpr size_t split_bytes(size_t BH, int nseg, int D) {

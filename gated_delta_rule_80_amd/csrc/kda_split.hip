@@ -68,15 +68,16 @@ __global__ __launch_bounds__(NT, 2) void kda_seg_map_kernel(SplitParams p) {
   const int r = lane & 15, g4 = lane >> 4;
   // (head, segment) groups of 2 NV workgroups, numbered XCD by XCD: the
   // workgroups of one group read the same records
-  const int nseg1 = p.nseg - 1;
+  const int nmap = p.whole ? p.nseg : p.nseg - 1;  // segments with maps
   const int pos = xcd_major(blockIdx.x, gridDim.x);
   const int job = pos % (2 * NV), grp = pos / (2 * NV);
   const int kind = job / NV, vblk = job % NV;
-  const int bh = grp / nseg1, s = grp % nseg1;
-  if (kind == 1 && s == 0) return;  // the first segment's M is never used
+  const int bh = grp / nmap, s = grp % nmap;
+  if (kind == 1 && s == 0 && !p.whole) return;  // the walk's first segment needs no M
   const int vb0 = vblk * VB;
-  // every segment but the last has seg_len whole chunks
-  const int nch = p.seg_len;
+  // every segment but the last has seg_len whole chunks; the last (only mapped
+  // for a whole call) has the rest, its last chunk possibly partial
+  const int nch = p.whole && s == nmap - 1 ? p.nch - s * p.seg_len : p.seg_len;
   const size_t rec0 = (size_t)bh * p.NT + (size_t)s * p.seg_len;
 
   const int R = wave % RT;
@@ -138,7 +139,7 @@ __global__ __launch_bounds__(NT, 2) void kda_seg_map_kernel(SplitParams p) {
         const int c = 16 * Ct + 4 * g4 + e;
         if (kind == 1)
           accS[i][e] = c == v ? 1.f : 0.f;
-        else if (s == 0 && p.S0 != nullptr)
+        else if (s == 0 && !p.whole && p.S0 != nullptr)
           accS[i][e] = p.S0[(size_t)bh * D * D + (size_t)c * D + v];
       }
     }
@@ -161,7 +162,7 @@ __global__ __launch_bounds__(NT, 2) void kda_seg_map_kernel(SplitParams p) {
   const E* iU = reinterpret_cast<const E*>(img + IMG::U);
   const float* iLC = reinterpret_cast<const float*>(img + IMG::LC);
 
-  issue_copy(0);
+  if (nch > 0) issue_copy(0);
   for (int n = 0; n < nch; ++n) {
     __builtin_amdgcn_s_waitcnt(0);  // this wave's copies of chunk n
     lds_barrier();                  // the whole image of chunk n and the state are in LDS
@@ -235,24 +236,69 @@ __global__ __launch_bounds__(NT, 2) void kda_seg_map_kernel(SplitParams p) {
   }
 }
 
+// The composition kernels' layout: one workgroup per (sequence, head, block of
+// CW columns); thread (row group rg, column col) holds rows rg RPT .. rg RPT +
+// RPT - 1 of its column.
+template <int D>
+struct ComposeShape {
+  static constexpr int CW = D >= 64 ? 8 : 16;  // columns per workgroup
+  static constexpr int NCB = D / CW;
+  static constexpr int RG = 256 / CW;          // row groups
+  static constexpr int RPT = D / RG;           // rows per thread
+  static_assert(RPT >= 1 && RPT * RG == D, "rows split evenly");
+};
+
+// acc += (A X)[rows c0 .., column col], A held as A[k][row] (D x D float32 in
+// global memory, copied into sA whole), X the workgroup's D x CW column block in
+// sX.  Every thread calls it; it ends with the barrier after the last read of sA
+// and sX.
+template <int D>
+__device__ __forceinline__ void apply_map(const float* A, float* sA, const float* sX,
+                                          float (&acc)[ComposeShape<D>::RPT], int tid, int col,
+                                          int c0) {
+  using SH = ComposeShape<D>;
+  constexpr int CW = SH::CW, RPT = SH::RPT;
+  constexpr int DD = D * D;
+  const int wave = tid >> 6;
+  // 16 bytes a lane; the lanes of a wave fill 64 consecutive pieces
+  for (int q = 0; q < DD / 4; q += 256)
+    if (q + tid < DD / 4)
+      __builtin_amdgcn_global_load_lds((const glb_void_t*)(A + 4 * (size_t)(q + tid)),
+                                       (lds_void_t*)(sA + 4 * (q + 64 * wave)), 16, 0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();  // A and X are in LDS
+#pragma unroll 4
+  for (int j = 0; j < D; ++j) {
+    const float xj = sX[j * CW + col];
+    const float* arow = sA + j * D + c0;
+    if constexpr (RPT % 4 == 0) {
+#pragma unroll
+      for (int q = 0; q < RPT / 4; ++q) {
+        const f32x4 m = *reinterpret_cast<const f32x4*>(arow + 4 * q);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[4 * q + e] = fmaf(m[e], xj, acc[4 * q + e]);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) acc[i] = fmaf(arow[i], xj, acc[i]);
+    }
+  }
+  __syncthreads();  // every read of sA and sX for this step is done
+}
+
 // Segment start states in order, in float32.  Forward: starts[0] = S0 (or
 // zeros), starts[1] = N_0, starts[s + 1] = M_s starts[s] + N_s.  Reverse (the
 // gradients of the segments' end states): starts[nseg - 1] = dS_T (or zeros),
 // starts[nseg - 2] = N'_{nseg-1}, starts[s - 1] = M_s^T starts[s] + N'_s.  Both
-// are X_next = A X + N with A held as sA[k][row]: Mt_s for M_s, M_s row-major for
-// M_s^T.  One workgroup per (sequence, head, block of CW value columns); thread
-// (row group rg, column col) holds rows rg RPT .. rg RPT + RPT - 1 of its
-// column.  A is copied into LDS whole.
+// are X_next = A X + N with A held as A[k][row]: Mt_s for M_s, M_s row-major for
+// M_s^T.
 template <int D>
 __global__ __launch_bounds__(256) void kda_seg_combine_kernel(SplitParams p) {
-  constexpr int CW = D >= 64 ? 8 : 16;  // columns per workgroup
-  constexpr int NCB = D / CW;
-  constexpr int RG = 256 / CW;          // row groups
-  constexpr int RPT = D / RG;           // rows per thread
-  static_assert(RPT >= 1 && RPT * RG == D, "rows split evenly");
+  using SH = ComposeShape<D>;
+  constexpr int CW = SH::CW, NCB = SH::NCB, RPT = SH::RPT;
   __shared__ __attribute__((aligned(16))) float sA[D * D];
   __shared__ float sX[D * CW];
-  const int tid = threadIdx.x, wave = tid >> 6;
+  const int tid = threadIdx.x;
   const int bh = blockIdx.x / NCB, cb = blockIdx.x % NCB;
   const int col = tid % CW, rg = tid / CW;
   const int v = cb * CW + col, c0 = rg * RPT;
@@ -274,36 +320,12 @@ __global__ __launch_bounds__(256) void kda_seg_combine_kernel(SplitParams p) {
   }
   for (int k = 1; k < nseg - 1; ++k) {
     const int s = rev ? nseg - 1 - k : k;
-    const float* A = slot(s, rev ? 2 : 1);
     const float* N = rev ? slot(s - 1, 0) : slot(s, 0);
     float* out = st + (size_t)(rev ? s - 1 : s + 1) * DD;
-    // 16 bytes a lane; the lanes of a wave fill 64 consecutive pieces
-    for (int q = 0; q < (int)(DD / 4); q += 256)
-      if (q + tid < (int)(DD / 4))
-        __builtin_amdgcn_global_load_lds((const glb_void_t*)(A + 4 * (size_t)(q + tid)),
-                                         (lds_void_t*)(sA + 4 * (q + 64 * wave)), 16, 0, 0);
     float acc[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) acc[i] = N[(size_t)(c0 + i) * D + v];
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();  // A and the previous X are in LDS
-#pragma unroll 4
-    for (int j = 0; j < D; ++j) {
-      const float xj = sX[j * CW + col];
-      const float* arow = sA + j * D + c0;
-      if constexpr (RPT % 4 == 0) {
-#pragma unroll
-        for (int q = 0; q < RPT / 4; ++q) {
-          const f32x4 m = *reinterpret_cast<const f32x4*>(arow + 4 * q);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[4 * q + e] = fmaf(m[e], xj, acc[4 * q + e]);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < RPT; ++i) acc[i] = fmaf(arow[i], xj, acc[i]);
-      }
-    }
-    __syncthreads();  // every read of sA and sX for this step is done
+    apply_map<D>(slot(s, rev ? 2 : 1), sA, sX, acc, tid, col, c0);
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       sX[(c0 + i) * CW + col] = acc[i];
@@ -312,9 +334,56 @@ __global__ __launch_bounds__(256) void kda_seg_combine_kernel(SplitParams p) {
   }
 }
 
+// The state map of a whole call per (sequence, head), from the maps of its
+// segments in order: M = M_{P-1} ... M_1 M_0 and N = M_{P-1}(... (M_1 N_0 +
+// N_1) ...) + N_{P-1}, in float32.  The columns of [M | N] evolve independently
+// (X <- M_s X, plus N_s in the N columns), so workgroup (sequence, head, part,
+// column block) carries one CW-column block of M (part 0) or N (part 1).
+template <int D>
+__global__ __launch_bounds__(256) void kda_seg_compose_kernel(SplitParams p) {
+  using SH = ComposeShape<D>;
+  constexpr int CW = SH::CW, NCB = SH::NCB, RPT = SH::RPT;
+  __shared__ __attribute__((aligned(16))) float sA[D * D];
+  __shared__ float sX[D * CW];
+  const int tid = threadIdx.x;
+  const int bh = blockIdx.x / (2 * NCB), part = blockIdx.x / NCB % 2, cb = blockIdx.x % NCB;
+  const int col = tid % CW, rg = tid / CW;
+  const int v = cb * CW + col, c0 = rg * RPT;
+  const int nseg = p.nseg;
+  const size_t DD = (size_t)D * D;
+  const float* mp = p.maps + (size_t)bh * nseg * 3 * DD;
+  auto slot = [&](int s, int k) { return mp + ((size_t)s * 3 + k) * DD; };
+  const float* x0 = slot(0, part == 1 ? 0 : 2);  // N_0, or M_0 row-major
+  float acc[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    acc[i] = x0[(size_t)(c0 + i) * D + v];
+    sX[(c0 + i) * CW + col] = acc[i];
+  }
+  for (int s = 1; s < nseg; ++s) {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) acc[i] = part == 1 ? slot(s, 0)[(size_t)(c0 + i) * D + v] : 0.f;
+    apply_map<D>(slot(s, 1), sA, sX, acc, tid, col, c0);
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) sX[(c0 + i) * CW + col] = acc[i];
+  }
+  float* out = (part == 1 ? p.N_out : p.M_out) + (size_t)bh * DD;
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) out[(size_t)(c0 + i) * D + v] = acc[i];
+}
+
+// The state map of an empty call: M = I, N = 0, for n_mats (sequence, head) pairs.
+__global__ __launch_bounds__(256) void kda_state_map_identity_kernel(float* M, float* N, size_t n, int D) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+    const size_t e = i % ((size_t)D * D);
+    M[i] = e / D == e % D ? 1.f : 0.f;
+    N[i] = 0.f;
+  }
+}
+
 template <int D, int C, typename E>
 static hipError_t launch_maps_t(const SplitParams& p, int vb, int threads, hipStream_t st) {
-  const size_t groups = (size_t)p.B * p.H * (p.nseg - 1);
+  const size_t groups = (size_t)p.B * p.H * (p.whole ? p.nseg : p.nseg - 1);
   if (p.reverse != 0) return hipErrorInvalidValue;
   if constexpr (D == 128) {
     if (vb == 64 && threads == 512) {
@@ -361,7 +430,7 @@ static hipError_t launch_maps_d(const SplitParams& p, int D, int C, int vb, int 
 
 hipError_t launch_split_maps(const SplitParams& p, int D, int C, bool fp32, int vb, int threads,
                              hipStream_t st) {
-  if (p.nseg < 2) return hipErrorInvalidValue;
+  if (p.nseg < (p.whole ? 1 : 2)) return hipErrorInvalidValue;
   return fp32 ? launch_maps_d<float>(p, D, C, vb, threads, st)
               : launch_maps_d<__bf16>(p, D, C, vb, threads, st);
 }
@@ -370,12 +439,35 @@ hipError_t launch_split_combine(const SplitParams& p, int D, hipStream_t st) {
   if (p.nseg < 2) return hipErrorInvalidValue;
   const size_t bh = (size_t)p.B * p.H;
   switch (D) {
-    case 16: hipLaunchKernelGGL((kda_seg_combine_kernel<16>), dim3((unsigned)(bh * 1)), dim3(256), 0, st, p); break;
-    case 32: hipLaunchKernelGGL((kda_seg_combine_kernel<32>), dim3((unsigned)(bh * 2)), dim3(256), 0, st, p); break;
-    case 64: hipLaunchKernelGGL((kda_seg_combine_kernel<64>), dim3((unsigned)(bh * 8)), dim3(256), 0, st, p); break;
-    case 128: hipLaunchKernelGGL((kda_seg_combine_kernel<128>), dim3((unsigned)(bh * 16)), dim3(256), 0, st, p); break;
+    case 16: hipLaunchKernelGGL((kda_seg_combine_kernel<16>), dim3((unsigned)(bh * ComposeShape<16>::NCB)), dim3(256), 0, st, p); break;
+    case 32: hipLaunchKernelGGL((kda_seg_combine_kernel<32>), dim3((unsigned)(bh * ComposeShape<32>::NCB)), dim3(256), 0, st, p); break;
+    case 64: hipLaunchKernelGGL((kda_seg_combine_kernel<64>), dim3((unsigned)(bh * ComposeShape<64>::NCB)), dim3(256), 0, st, p); break;
+    case 128: hipLaunchKernelGGL((kda_seg_combine_kernel<128>), dim3((unsigned)(bh * ComposeShape<128>::NCB)), dim3(256), 0, st, p); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_state_map(const SplitParams& p, int D, int C, bool fp32, int vb, int threads,
+                            hipStream_t st) {
+  if (!p.whole || p.nseg < 1) return hipErrorInvalidValue;
+  if (hipError_t e = launch_split_maps(p, D, C, fp32, vb, threads, st); e != hipSuccess) return e;
+  const unsigned grid = (unsigned)((size_t)p.B * p.H * 2);
+  switch (D) {
+    case 16: hipLaunchKernelGGL((kda_seg_compose_kernel<16>), dim3(grid * ComposeShape<16>::NCB), dim3(256), 0, st, p); break;
+    case 32: hipLaunchKernelGGL((kda_seg_compose_kernel<32>), dim3(grid * ComposeShape<32>::NCB), dim3(256), 0, st, p); break;
+    case 64: hipLaunchKernelGGL((kda_seg_compose_kernel<64>), dim3(grid * ComposeShape<64>::NCB), dim3(256), 0, st, p); break;
+    case 128: hipLaunchKernelGGL((kda_seg_compose_kernel<128>), dim3(grid * ComposeShape<128>::NCB), dim3(256), 0, st, p); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_state_map_identity(float* M, float* N, size_t n, int D, hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  const size_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(kda_state_map_identity_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)),
+                     dim3(256), 0, st, M, N, n, D);
   return hipGetLastError();
 }
 

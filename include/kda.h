@@ -73,7 +73,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 5
+#define KDA_ABI_VERSION 6
 
 typedef enum kda_status {
   KDA_OK = 0,
@@ -198,6 +198,31 @@ kda_status kda_prefill_stage(const kda_prefill_args* a, void* ws, size_t ws_byte
  * splits both of its walks the same way: the reverse walk is affine in the
  * gradient of the end state with the transposed maps M^T of the forward. */
 int kda_prefill_walk_segments(const kda_prefill_args* a);
+
+/* The affine state map of a prefill call, for splitting one sequence over
+ * devices (each device its contiguous share of the tokens): per (sequence, head),
+ * the state after the call's tokens is S_T = M S_start + N for any state
+ * S_start before them, where N is the state reached from zero and M
+ * (D x D, acting on the key index) the product of the steps' linear parts
+ * (I - beta k k^T) Diag(exp(g)) (see kda_prefill_walk_segments).  A device
+ * holding the later tokens computes its (M, N) without knowing S_start; once
+ * the shares before it have handed over their maps (S_start = M' S' + N',
+ * composed in order; M and N are 64 KB each per head in float32 at D = 128),
+ * it runs stages 1 to 3 from S0 = S_start on the same workspace.
+ *   - Call after kda_prefill_stage(a, ws, ws_bytes, KDA_STAGE_PREP, stream) on
+ *     the same stream with the same arguments and workspace: the map is formed
+ *     from the chunk records that stage wrote.  ws_bytes must be at least
+ *     kda_prefill_state_map_workspace_bytes(a) (at least the prefill's); a later
+ *     stage 1 on the same workspace is unaffected.  a->S0 is not read.
+ *   - M, N: device [B][H][D][D] float32, row = key channel of S_T; written.  They
+ *     may not overlap each other, any buffer of a, or the workspace.
+ *   - B equal-length sequences only (packed: KDA_ERR_UNSUPPORTED).  T = 0 gives
+ *     M = I, N = 0 (no workspace needed).
+ *   - The maps of the call's segments (cut as the split walk cuts) are walked in
+ *     parallel and composed in float32; rounding as in the walk itself. */
+size_t kda_prefill_state_map_workspace_bytes(const kda_prefill_args* a);
+kda_status kda_prefill_state_map(const kda_prefill_args* a, void* ws, size_t ws_bytes, float* M,
+                                 float* N, void* stream);
 
 /* For callers that cannot allocate device memory -- code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc: kda_prefill

@@ -22,10 +22,11 @@ def test_exports_every_declared_symbol(lib):
     assert {"kda_prefill", "kda_decode_step", "kda_conv_norm", "kda_prefill_stage",
             "kda_prefill_workspace_bytes", "kda_validate_prefill", "kda_validate_decode",
             "kda_validate_conv_norm", "kda_status_str", "kda_abi_version",
-            "kda_prefill_walk_segments"} <= set(names)
+            "kda_prefill_walk_segments", "kda_prefill_state_map",
+            "kda_prefill_state_map_workspace_bytes"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.kda_abi_version() == 5
+    assert lib.kda_abi_version() == 6
     for s in range(11):
         assert kda.kda_status_str(s) and kda.kda_status_str(s) != "unknown status"
 
@@ -370,6 +371,28 @@ def backward(**kw):
     for k, v in kw.items():
         setattr(a, k, v)
     return a
+
+
+def test_state_map_arguments(lib):
+    """The state map's host-side checks: nothing is launched for any of these."""
+    f = Fake()
+    f.next = 0x7D0000000000  # clear of the argument buffers
+    a = prefill(B=1, T=65536, H=12)
+    need = kda.kda_prefill_state_map_workspace_bytes(a)
+    assert need >= kda.kda_prefill_workspace_bytes(a) > 0
+    M, N, ws = f(12 * 128 * 128 * 4), f(12 * 128 * 128 * 4), f(need)
+
+    def sm(args, m=M, n=N, w=ws, nbytes=need):
+        return lib.kda_prefill_state_map(ctypes.byref(args), ctypes.c_void_p(w), nbytes,
+                                         ctypes.c_void_p(m), ctypes.c_void_p(n), None)
+    assert sm(a, m=None) == NULL and sm(a, n=None) == NULL
+    assert sm(a, m=M + 4) == ALIGN
+    assert sm(a, n=M) == ALIAS and sm(a, m=a.q) == ALIAS and sm(a, n=a.S0) == ALIAS
+    assert sm(a, w=M - 256) == ALIAS
+    assert sm(a, nbytes=need - 1) == WS and sm(a, w=ws + 16) == WS and sm(a, w=None) == WS
+    assert sm(prefill(B=1, T=64, H=2, cu_seqlens=f(), n_seqs=1)) == UNSUP
+    assert sm(prefill(B=0)) == SHAPE
+    assert kda.kda_prefill_state_map_workspace_bytes(prefill(B=1, T=0, H=2)) == 0
 
 
 def test_backward_workspace_holds_the_forward(lib):
