@@ -730,6 +730,9 @@ def main(argv=None) -> int:
         tp = others.get(wtp.name) or (head if w.name == wtp.name else None)
         stages["backward_tp_share"] = backward_leg(kda, torch, wtp, args, stream, dev,
                                                    tp["ms_per_step"] if tp else float("nan"))
+        # the backward of the headline workload itself
+        stages["backward_headline"] = backward_leg(kda, torch, w, args, stream, dev,
+                                                   head["ms_per_step"])
 
     if args.calib_copy_mib > 0:
         calibration_copy(kda, torch, args.calib_copy_mib, stream, dev)
