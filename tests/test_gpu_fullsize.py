@@ -104,12 +104,20 @@ def test_full_size_decode_every_pair():
     summarize("decode-b256", [(b, h, eo, eS, 0.0, -1) for b, h, eo, eS, _ in res], TOL[w.io])
 
 
-@pytest.mark.timeout(600)
-def test_full_size_backward_every_head():
-    """The backward at the 4k workload's full size, every head against the oracle's
-    reverse-mode gradients of that head (heads are independent; the conv filter
-    gradient of a head's channels comes from that head alone)."""
-    w = WORKLOADS["prefill-4k"]
+# (workload, oracle processes): the oracle keeps every step's state of a head
+# (8.6 GB at T = 65536, D = 128), so the long case runs 6 heads at a time
+BACKWARD_FULL = [("prefill-4k", None), ("prefill-64k-h12", 6)]
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,workers", BACKWARD_FULL)
+def test_full_size_backward_every_head(name, workers):
+    """The backward at a workload's full size (at 12 heads and T = 65536 both of
+    its walks split into segments), every head against the oracle's reverse-mode
+    gradients of that head (heads are independent; the conv filter gradient of a
+    head's channels comes from that head alone)."""
+    w = WORKLOADS[name]
+    print(f"full-size backward {name}: B={w.B} T={w.T} H={w.H} D={w.D}", flush=True)
     inp = make_inputs(w, seed=0, device="cuda")
     gen = torch.Generator(device="cuda").manual_seed(5)
     do = torch.randn(w.B, w.T, w.H, w.D, generator=gen, device="cuda").to(torch.bfloat16)
@@ -134,7 +142,7 @@ def test_full_size_backward_every_head():
             save_array(d, n, to_storage(grads[n]))
         del inp, do, grads, o, S_T
         torch.cuda.empty_cache()
-        res = run(backward_pair, d, [(0, h) for h in range(w.H)], "backward")
+        res = run(backward_pair, d, [(0, h) for h in range(w.H)], "backward", workers=workers)
     finally:
         shutil.rmtree(d, ignore_errors=True)
     tol = TOL[w.io]
