@@ -336,6 +336,58 @@ def stages_leg(kda, torch, w, wd, args, stream, dev, plain_ms, plain_dms):
             "prefill": prefill, "decode": decode}
 
 
+def training_leg(kda, torch, w, args, stream, dev, plain_ms, backward_ms):
+    """A training step's mixer work with the forward kept for the backward
+    (kda_prefill_forward_saved, then kda_prefill_backward_saved), each timed on
+    its own, against kda_prefill plus the recomputing kda_prefill_backward."""
+    from kda_inputs import make_inputs
+    inp = make_inputs(w, seed=args.seed, device=dev)
+    gen = torch.Generator(device=dev).manual_seed(args.seed + 7)
+    do = torch.randn(w.B, w.T, w.H, w.D, generator=gen, device=dev).to(inp["q"].dtype)
+    f32 = dict(dtype=torch.float32, device=dev)
+    o = torch.empty_like(inp["q"])
+    S_T = torch.empty(w.B, w.H, w.D, w.D, **f32)
+    cso = torch.empty(w.B, 3, 3, w.H * w.D, dtype=inp["q"].dtype, device=dev)
+    fwd = kda.prefill_args(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["conv_w"],
+                           inp["conv_state"], inp["S0"], o, S_T, cso, chunk=w.chunk)
+    shape = (w.B, w.T, w.H, w.D)
+    grads = dict(dq=torch.empty(*shape, **f32), dk=torch.empty(*shape, **f32),
+                 dv=torch.empty(*shape, **f32), dg=torch.empty(*shape, **f32),
+                 dbeta=torch.empty(w.B, w.T, w.H, **f32), dS0=torch.empty(w.B, w.H, w.D, w.D, **f32),
+                 dconv_w=torch.empty(3, w.H * w.D, 4, **f32),
+                 dconv_state=torch.empty(w.B, 3, 3, w.H * w.D, **f32))
+    a = kda.backward_args(fwd, do, None, grads)
+    ws = torch.empty(kda.kda_training_workspace_bytes(fwd), dtype=torch.uint8, device=dev)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    f_ms = timed(lambda: kda.kda_prefill_forward_saved_raw(fwd, ws, stream))
+    # the saved part of the workspace is only read by the backward: repeated
+    # backward calls on one saved forward are the steady state
+    b_ms = timed(lambda: kda.kda_prefill_backward_saved_raw(a, ws, stream))
+    out = {"workload": w.name, "forward_saved_ms": f_ms, "backward_saved_ms": b_ms,
+           "step_ms": f_ms + b_ms,
+           "backward_ratio_to_forward": b_ms / plain_ms if plain_ms == plain_ms else None,
+           "step_ms_recomputing": (plain_ms + backward_ms) if plain_ms == plain_ms else None,
+           "workspace_bytes": ws.numel(),
+           "includes": "forward kept for the backward (records, front-end outputs, decay sums, "
+                       "chunk-start states) + backward without the forward recompute"}
+    del ws, inp, grads, o, S_T, cso, do, a, fwd
+    torch.cuda.empty_cache()
+    return out
+
+
 def time_decode(kda, torch, da, stream, steps, warmup):
     for _ in range(warmup):
         kda.kda_decode_raw(da, stream)
@@ -730,6 +782,8 @@ def main(argv=None) -> int:
         tp = others.get(wtp.name) or (head if w.name == wtp.name else None)
         stages["backward_tp_share"] = backward_leg(kda, torch, wtp, args, stream, dev,
                                                    tp["ms_per_step"] if tp else float("nan"))
+        stages["training"] = training_leg(kda, torch, ws4, args, stream, dev, base_ms,
+                                          stages["backward"]["ms_per_step"])
         # the backward of the headline workload itself
         stages["backward_headline"] = backward_leg(kda, torch, w, args, stream, dev,
                                                    head["ms_per_step"])

@@ -23,7 +23,7 @@ KDA_BF16 = 0
 KDA_FP32 = 1
 KDA_FLAG_L2NORM_QK = 1
 KDA_FLAG_BETA_LOGITS = 2
-ABI_VERSION = 6
+ABI_VERSION = 7
 KDA_STAGE_PREP, KDA_STAGE_STATE, KDA_STAGE_CONV_TAIL, KDA_STAGE_OUTPUT = 0, 1, 2, 3
 KDA_STAGE_STATE_TAIL = 4  # stages 1 and 2 in one launch, as kda_prefill runs them
 NUM_STAGES = 4
@@ -134,6 +134,12 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.kda_backward_workspace_bytes.argtypes = [P(BackwardArgs)]
     lib.kda_prefill_backward.restype = ctypes.c_int
     lib.kda_prefill_backward.argtypes = [P(BackwardArgs), _vp, ctypes.c_size_t, _vp]
+    lib.kda_training_workspace_bytes.restype = ctypes.c_size_t
+    lib.kda_training_workspace_bytes.argtypes = [P(PrefillArgs)]
+    lib.kda_prefill_forward_saved.restype = ctypes.c_int
+    lib.kda_prefill_forward_saved.argtypes = [P(PrefillArgs), _vp, ctypes.c_size_t, _vp]
+    lib.kda_prefill_backward_saved.restype = ctypes.c_int
+    lib.kda_prefill_backward_saved.argtypes = [P(BackwardArgs), _vp, ctypes.c_size_t, _vp]
     if lib.kda_abi_version() != ABI_VERSION:
         raise RuntimeError("libkda ABI version mismatch")
     if path is None:
@@ -490,6 +496,91 @@ def kda_prefill_backward(q, k, v, g, beta, conv_w=None, conv_state=None, S0=None
     _check(load().kda_prefill_backward(ctypes.byref(a), ws, nbytes, _stream(stream)),
            "kda_prefill_backward")
     return grads, o, S_T
+
+
+def _grads_for(q, NS, conv, A_log, o_norm_w, o_gate):
+    B, T, H, D = q.shape
+    f32 = dict(dtype=torch.float32, device=q.device)
+    grads = dict(dq=torch.empty(B, T, H, D, **f32), dk=torch.empty(B, T, H, D, **f32),
+                 dv=torch.empty(B, T, H, D, **f32), dg=torch.empty(B, T, H, D, **f32),
+                 dbeta=torch.empty(B, T, H, **f32), dS0=torch.empty(NS, H, D, D, **f32))
+    if conv:
+        grads["dconv_w"] = torch.empty(3, H * D, 4, **f32)
+        grads["dconv_state"] = torch.empty(NS, 3, 3, H * D, **f32)
+    if A_log is not None:
+        grads["dA_log"] = torch.empty(H, **f32)
+        grads["ddt_bias"] = torch.empty(H * D, **f32)
+    if o_norm_w is not None:
+        grads["do_norm_w"] = torch.empty(D, **f32)
+    if o_gate is not None:
+        grads["do_gate"] = torch.empty(B, T, H, D, **f32)
+    return grads
+
+
+def kda_training_workspace_bytes(args: PrefillArgs) -> int:
+    return int(load().kda_training_workspace_bytes(ctypes.byref(args)))
+
+
+def kda_prefill_forward_saved_raw(args: PrefillArgs, workspace, stream=None):
+    ws = _ptr(workspace) if workspace is not None else None
+    nbytes = workspace.numel() if workspace is not None else 0
+    _check(load().kda_prefill_forward_saved(ctypes.byref(args), ws, nbytes, _stream(stream)),
+           "kda_prefill_forward_saved")
+
+
+def kda_prefill_backward_saved_raw(args: BackwardArgs, workspace, stream=None):
+    ws = _ptr(workspace) if workspace is not None else None
+    nbytes = workspace.numel() if workspace is not None else 0
+    _check(load().kda_prefill_backward_saved(ctypes.byref(args), ws, nbytes, _stream(stream)),
+           "kda_prefill_backward_saved")
+
+
+class SavedForward:
+    """What kda_prefill_forward_saved hands to kda_prefill_backward_saved: the
+    forward's argument struct, its workspace, and the tensors both refer to."""
+
+    def __init__(self, args, workspace, keep, NS, conv, stages):
+        self.args, self.workspace, self.keep = args, workspace, keep
+        self.NS, self.conv, self.stages = NS, conv, stages
+
+
+def kda_prefill_forward_saved(q, k, v, g, beta, conv_w=None, conv_state=None, S0=None, *, chunk=64,
+                              scale=1.0, l2norm_qk=True, eps=1e-6, stream=None, A_log=None,
+                              dt_bias=None, beta_logits=False, o_norm_w=None, o_norm_eps=1e-6,
+                              o_gate=None, cu_seqlens=None):
+    """The forward of a training step, kept for its backward: returns (o, S_T,
+    conv_state_out, saved), the outputs as kda_prefill's and `saved` for
+    kda_prefill_backward_saved (the inputs must not change in between)."""
+    B, T, H, D = q.shape
+    dev = q.device
+    NS = B if cu_seqlens is None else cu_seqlens.numel() - 1
+    o = torch.empty_like(q)
+    S_T = torch.empty(NS, H, D, D, dtype=torch.float32, device=dev)
+    cso = torch.empty(NS, 3, 3, H * D, dtype=q.dtype, device=dev) if conv_w is not None else None
+    a = prefill_args(q, k, v, g, beta, conv_w, conv_state, S0, o, S_T, cso, chunk=chunk,
+                     scale=scale, l2norm_qk=l2norm_qk, eps=eps, A_log=A_log, dt_bias=dt_bias,
+                     beta_logits=beta_logits, o_norm_w=o_norm_w, o_norm_eps=o_norm_eps,
+                     o_gate=o_gate, cu_seqlens=cu_seqlens)
+    _check(kda_validate_prefill(a), "kda_prefill_forward_saved")
+    need = kda_training_workspace_bytes(a)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev) if need > 0 else None
+    kda_prefill_forward_saved_raw(a, ws, stream)
+    keep = (q, k, v, g, beta, conv_w, conv_state, S0, o, S_T, cso, A_log, dt_bias, o_norm_w, o_gate,
+            cu_seqlens)
+    saved = SavedForward(a, ws, keep, NS, conv_w is not None, (A_log, o_norm_w, o_gate))
+    return o, S_T, cso, saved
+
+
+def kda_prefill_backward_saved(saved: SavedForward, *, do, dS_T=None, stream=None) -> dict:
+    """The backward of a kda_prefill_forward_saved call, without recomputing the
+    forward.  Returns the gradients as kda_prefill_backward does."""
+    q = saved.keep[0]
+    A_log, o_norm_w, o_gate = saved.stages
+    grads = _grads_for(q, saved.NS, saved.conv, A_log, o_norm_w, o_gate)
+    a = backward_args(saved.args, do, dS_T, grads)
+    _check(kda_validate_backward(a), "kda_prefill_backward_saved")
+    kda_prefill_backward_saved_raw(a, saved.workspace, stream)
+    return grads
 
 
 def kda_prefill_backward_raw(args: BackwardArgs, workspace, stream=None):

@@ -690,6 +690,7 @@ struct BwdLayout {
   size_t tT, y, gam, beta, ckS, ckdS, dU, dQL, dW, dKt, dP, dLC, dBk, dBv, dA, dy, dbp, dcp, pl;
   size_t dOp, dwp, ddp, dap;  // the optional stages: dO before the output stage, partial sums
   size_t fst;                 // packed: first front-end block slot per sequence [n_seqs + 1]
+  size_t opre;                // saved forward with the output stage: the mixer's output
   size_t bytes;
   size_t nfront;  // front-end block slots per head (filter partials)
 };
@@ -704,7 +705,10 @@ kda_prefill_args forward_of_backward(const kda_prefill_args* f) {
   return f0;
 }
 
-BwdLayout bwd_layout(const kda_backward_args* a) {
+// saved: the workspace of kda_prefill_forward_saved / kda_prefill_backward_saved,
+// which also keeps the mixer's output before the output stage.  The layout
+// depends on the forward's arguments only.
+BwdLayout bwd_layout(const kda_backward_args* a, bool saved = false) {
   const kda_prefill_args* f = &a->fwd;
   const kda_prefill_args f0 = forward_of_backward(f);
   BwdLayout L{};
@@ -752,6 +756,7 @@ BwdLayout bwd_layout(const kda_backward_args* a) {
   const size_t nact = f->A_log != nullptr ? (size_t)kda::bwd_act_groups((long)f->B * f->T, f->D) : 0;
   L.ddp = take(nact * f->H * D);
   L.dap = take(nact * f->H);
+  L.opre = take(saved && gn ? x / ef : 0);  // I/O type
   L.bytes = off;
   return L;
 }
@@ -818,61 +823,75 @@ size_t kda_backward_workspace_bytes(const kda_backward_args* a) {
   return bwd_layout(a).bytes;
 }
 
-kda_status kda_prefill_backward(const kda_backward_args* a, void* ws, size_t ws_bytes, void* stream) {
-  if (kda_status e = kda_validate_backward(a); e != KDA_OK) return e;
+}  // extern "C"
+
+// The gradients when the call has no tokens: dS0 = dS_T, the filter, history and
+// stage-parameter gradients zero.
+static kda_status backward_no_tokens(const kda_backward_args* a, hipStream_t st) {
   const kda_prefill_args* f = &a->fwd;
-  hipStream_t st = static_cast<hipStream_t>(stream);
+  PrefillSizes sz;
+  prefill_sizes(f, sz);
+  if (a->dS0 != nullptr &&
+      kda::launch_copy_state(a->dS_T, a->dS0, (size_t)sz.NS * f->H * f->D * f->D, st) != hipSuccess)
+    return KDA_ERR_HIP;
+  if (a->dconv_w != nullptr &&
+      kda::launch_copy_state(nullptr, a->dconv_w, (size_t)3 * f->H * f->D * f->conv_k, st) != hipSuccess)
+    return KDA_ERR_HIP;
+  if (a->dconv_state != nullptr &&
+      kda::launch_copy_state(nullptr, a->dconv_state, (size_t)sz.NS * 3 * 3 * f->H * f->D, st) != hipSuccess)
+    return KDA_ERR_HIP;
+  // sums over no tokens
+  for (auto [p, n] : {std::pair<float*, size_t>{a->dA_log, (size_t)f->H},
+                      {a->ddt_bias, (size_t)f->H * f->D}, {a->do_norm_w, (size_t)f->D}})
+    if (p != nullptr && kda::launch_copy_state(nullptr, p, n, st) != hipSuccess) return KDA_ERR_HIP;
+  return KDA_OK;
+}
+
+// The workspace checks of a backward call with T > 0.
+static kda_status check_bwd_workspace(const kda_backward_args* a, void* ws, size_t ws_bytes,
+                                      const BwdLayout& L) {
+  if (ws == nullptr || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0 || ws_bytes < L.bytes)
+    return KDA_ERR_WORKSPACE;
+  const Span w = span(ws, L.bytes);
+  Span ins[kBwdIns], outs[kBwdOuts];
+  bwd_spans(a, ins, outs);
+  for (const Span& x : ins)
+    if (overlaps(w, x)) return KDA_ERR_ALIAS;
+  for (const Span& x : outs)
+    if (overlaps(w, x)) return KDA_ERR_ALIAS;
+  return KDA_OK;
+}
+
+// The forward in backward mode: the mixer without the output stage, keeping in
+// the workspace what the backward reads (records, front-end outputs, Gamma, beta,
+// T, the state at each chunk start and U).  o then holds the mixer's output.
+static kda_status forward_for_backward(const kda_prefill_args* f, char* wsb, const BwdLayout& L,
+                                       hipStream_t st, BwdFwdOut& bo) {
+  auto F = [&](size_t off) { return reinterpret_cast<float*>(wsb + off); };
+  const kda_prefill_args f0 = forward_of_backward(f);
+  bo = BwdFwdOut{wsb + L.y, F(L.gam), F(L.beta), F(L.tT), wsb + L.ckS};
+  for (int stage : {KDA_STAGE_PREP, KDA_STAGE_STATE})
+    if (kda_status e = run_stage(&f0, wsb, stage, st, &bo); e != KDA_OK) return e;
+  return KDA_OK;
+}
+
+// Everything after the forward: the output stage's backward (from the mixer's
+// output o_pre; finish_o: then the stage finishes o in place), the reverse walk
+// and the per-chunk gradient kernels, the front end, the activations' backward.
+static kda_status backward_core(const kda_backward_args* a, char* wsb, const BwdLayout& L,
+                                const void* o_pre, bool finish_o, hipStream_t st) {
+  const kda_prefill_args* f = &a->fwd;
+  void* ws = wsb;
   const bool fp32 = f->io == KDA_FP32;
   PrefillSizes sz;
   prefill_sizes(f, sz);
-  if (f->T == 0) {
-    // nothing flows: dS0 = dS_T; the filter and history gradients are zero
-    if (a->dS0 != nullptr &&
-        kda::launch_copy_state(a->dS_T, a->dS0, (size_t)sz.NS * f->H * f->D * f->D, st) != hipSuccess)
-      return KDA_ERR_HIP;
-    if (a->dconv_w != nullptr &&
-        kda::launch_copy_state(nullptr, a->dconv_w, (size_t)3 * f->H * f->D * f->conv_k, st) != hipSuccess)
-      return KDA_ERR_HIP;
-    if (a->dconv_state != nullptr &&
-        kda::launch_copy_state(nullptr, a->dconv_state, (size_t)sz.NS * 3 * 3 * f->H * f->D, st) != hipSuccess)
-      return KDA_ERR_HIP;
-    // sums over no tokens
-    for (auto [p, n] : {std::pair<float*, size_t>{a->dA_log, (size_t)f->H},
-                        {a->ddt_bias, (size_t)f->H * f->D}, {a->do_norm_w, (size_t)f->D}})
-      if (p != nullptr && kda::launch_copy_state(nullptr, p, n, st) != hipSuccess) return KDA_ERR_HIP;
-    // the run_stage calls below still hand S_T and the conv state through
-    for (int stage = KDA_STAGE_PREP; stage <= KDA_STAGE_OUTPUT; ++stage)
-      if (kda_status e = run_stage(f, ws, stage, st); e != KDA_OK) return e;
-    return KDA_OK;
-  }
-  const BwdLayout L = bwd_layout(a);
-  if (ws == nullptr || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0 || ws_bytes < L.bytes)
-    return KDA_ERR_WORKSPACE;
-  {
-    const Span w = span(ws, L.bytes);
-    Span ins[kBwdIns], outs[kBwdOuts];
-    bwd_spans(a, ins, outs);
-    for (const Span& x : ins)
-      if (overlaps(w, x)) return KDA_ERR_ALIAS;
-    for (const Span& x : outs)
-      if (overlaps(w, x)) return KDA_ERR_ALIAS;
-  }
-  char* wsb = static_cast<char*>(ws);
   auto F = [&](size_t off) { return reinterpret_cast<float*>(wsb + off); };
-  // forward in backward mode.  The conv-state hand-over comes last, after the
-  // backward front end has read the previous conv state: conv_state_out may be
-  // conv_state_in, and the hand-over overwrites it.  With the output stage the
-  // walk leaves the mixer's output in o; the stage's backward reads it, then the
-  // stage finishes o in place.
   const bool gn = f->o_norm_w != nullptr || f->o_gate != nullptr;
   const kda_prefill_args f0 = forward_of_backward(f);
-  BwdFwdOut bo{wsb + L.y, F(L.gam), F(L.beta), F(L.tT), wsb + L.ckS};
-  for (int stage : {KDA_STAGE_PREP, KDA_STAGE_STATE})
-    if (kda_status e = run_stage(&f0, ws, stage, st, &bo); e != KDA_OK) return e;
   const void* dO = a->dO;
   if (gn) {
     kda::BwdOutParams q{};
-    q.x = f->o;
+    q.x = o_pre;
     q.z = f->o_gate;
     q.dy = a->dO;
     q.w = f->o_norm_w;
@@ -885,13 +904,15 @@ kda_status kda_prefill_backward(const kda_backward_args* a, void* ws, size_t ws_
     q.seqs = seq_tables(f, ws);
     if (kda_status e = hip_status(kda::launch_bwd_out_stage(q, a->do_norm_w, f->D, fp32, st)); e != KDA_OK)
       return e;
-    kda::OutStageParams os{};
-    os.o = f->o;
-    os.o_gate = f->o_gate;
-    os.o_norm_w = f->o_norm_w;
-    os.o_norm_eps = f->o_norm_eps;
-    os.rows = q.rows;
-    if (kda_status e = hip_status(kda::launch_out_stage(os, f->D, fp32, st)); e != KDA_OK) return e;
+    if (finish_o) {
+      kda::OutStageParams os{};
+      os.o = f->o;
+      os.o_gate = f->o_gate;
+      os.o_norm_w = f->o_norm_w;
+      os.o_norm_eps = f->o_norm_eps;
+      os.rows = q.rows;
+      if (kda_status e = hip_status(kda::launch_out_stage(os, f->D, fp32, st)); e != KDA_OK) return e;
+    }
     dO = wsb + L.dOp;
   }
   // backward
@@ -991,7 +1012,107 @@ kda_status kda_prefill_backward(const kda_backward_args* a, void* ws, size_t ws_
         e != KDA_OK)
       return e;
   }
+  return KDA_OK;
+}
+
+extern "C" {
+
+kda_status kda_prefill_backward(const kda_backward_args* a, void* ws, size_t ws_bytes, void* stream) {
+  if (kda_status e = kda_validate_backward(a); e != KDA_OK) return e;
+  const kda_prefill_args* f = &a->fwd;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (f->T == 0) {
+    if (kda_status e = backward_no_tokens(a, st); e != KDA_OK) return e;
+    // the run_stage calls below still hand S_T and the conv state through
+    for (int stage = KDA_STAGE_PREP; stage <= KDA_STAGE_OUTPUT; ++stage)
+      if (kda_status e = run_stage(f, ws, stage, st); e != KDA_OK) return e;
+    return KDA_OK;
+  }
+  const BwdLayout L = bwd_layout(a);
+  if (kda_status e = check_bwd_workspace(a, ws, ws_bytes, L); e != KDA_OK) return e;
+  char* wsb = static_cast<char*>(ws);
+  // The conv-state hand-over comes last, after the backward front end has read the
+  // previous conv state: conv_state_out may be conv_state_in, and the hand-over
+  // overwrites it.  With the output stage the walk leaves the mixer's output in o;
+  // the stage's backward reads it, then the stage finishes o in place.
+  BwdFwdOut bo{};
+  if (kda_status e = forward_for_backward(f, wsb, L, st, bo); e != KDA_OK) return e;
+  if (kda_status e = backward_core(a, wsb, L, f->o, true, st); e != KDA_OK) return e;
   return run_stage(f, ws, KDA_STAGE_CONV_TAIL, st, &bo);
+}
+
+// The saved forward's workspace: the backward's, plus the mixer's output before
+// the output stage when there is one.
+static kda_backward_args backward_of_forward(const kda_prefill_args* f) {
+  kda_backward_args b{};
+  b.fwd = *f;
+  return b;
+}
+
+size_t kda_training_workspace_bytes(const kda_prefill_args* f) {
+  if (kda_validate_prefill(f) != KDA_OK || f->T == 0) return 0;
+  const kda_backward_args b = backward_of_forward(f);
+  return bwd_layout(&b, true).bytes;
+}
+
+kda_status kda_prefill_forward_saved(const kda_prefill_args* f, void* ws, size_t ws_bytes,
+                                     void* stream) {
+  if (kda_status e = kda_validate_prefill(f); e != KDA_OK) return e;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (f->T == 0) {
+    for (int stage = KDA_STAGE_PREP; stage <= KDA_STAGE_OUTPUT; ++stage)
+      if (kda_status e = run_stage(f, ws, stage, st); e != KDA_OK) return e;
+    return KDA_OK;
+  }
+  PrefillSizes sz;
+  prefill_sizes(f, sz);
+  // the backward reads the previous conv state after this call has written the new one
+  if (overlaps(span(f->conv_state_in, sz.cst), span(f->conv_state_out, sz.cst))) return KDA_ERR_ALIAS;
+  const kda_backward_args b = backward_of_forward(f);
+  const BwdLayout L = bwd_layout(&b, true);
+  if (ws == nullptr || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0 || ws_bytes < L.bytes)
+    return KDA_ERR_WORKSPACE;
+  const Span w = span(ws, L.bytes);
+  for (Span x : {span(f->q, sz.x), span(f->k, sz.x), span(f->v, sz.x), span(f->g, sz.x),
+                 span(f->beta, sz.bta), span(f->conv_w, sz.cw), span(f->conv_state_in, sz.cst),
+                 span(f->S0, sz.state), span(f->o, sz.x), span(f->S_T, sz.state),
+                 span(f->conv_state_out, sz.cst), span(f->A_log, (size_t)f->H * 4),
+                 span(f->dt_bias, (size_t)f->H * f->D * 4), span(f->o_norm_w, (size_t)f->D * 4),
+                 span(f->o_gate, sz.x), span(f->cu_seqlens, sz.cu)})
+    if (overlaps(w, x)) return KDA_ERR_ALIAS;
+  char* wsb = static_cast<char*>(ws);
+  BwdFwdOut bo{};
+  if (kda_status e = forward_for_backward(f, wsb, L, st, bo); e != KDA_OK) return e;
+  if (f->o_norm_w != nullptr || f->o_gate != nullptr) {
+    // keep the mixer's output for the output stage's backward, then finish o
+    if (kda::launch_copy_state(static_cast<const float*>(f->o), reinterpret_cast<float*>(wsb + L.opre),
+                               sz.x / 4, st) != hipSuccess)
+      return KDA_ERR_HIP;
+    kda::OutStageParams os{};
+    os.o = f->o;
+    os.o_gate = f->o_gate;
+    os.o_norm_w = f->o_norm_w;
+    os.o_norm_eps = f->o_norm_eps;
+    os.rows = (long)f->B * f->T * f->H;
+    if (kda_status e = hip_status(kda::launch_out_stage(os, f->D, f->io == KDA_FP32, st)); e != KDA_OK)
+      return e;
+  }
+  return run_stage(f, ws, KDA_STAGE_CONV_TAIL, st, &bo);
+}
+
+kda_status kda_prefill_backward_saved(const kda_backward_args* a, void* ws, size_t ws_bytes,
+                                      void* stream) {
+  if (kda_status e = kda_validate_backward(a); e != KDA_OK) return e;
+  const kda_prefill_args* f = &a->fwd;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (f->T == 0) return backward_no_tokens(a, st);
+  PrefillSizes sz;
+  prefill_sizes(f, sz);
+  if (overlaps(span(f->conv_state_in, sz.cst), span(f->conv_state_out, sz.cst))) return KDA_ERR_ALIAS;
+  const BwdLayout L = bwd_layout(a, true);
+  if (kda_status e = check_bwd_workspace(a, ws, ws_bytes, L); e != KDA_OK) return e;
+  char* wsb = static_cast<char*>(ws);
+  return backward_core(a, wsb, L, wsb + L.opre, false, st);
 }
 
 }  // extern "C"

@@ -73,7 +73,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 6
+#define KDA_ABI_VERSION 7
 
 typedef enum kda_status {
   KDA_OK = 0,
@@ -349,6 +349,27 @@ size_t kda_backward_workspace_bytes(const kda_backward_args* a);
 /* Enqueue the recomputed forward and the backward on `stream`.  No output may
  * overlap an input or another output; the workspace overlaps nothing. */
 kda_status kda_prefill_backward(const kda_backward_args* a, void* ws, size_t ws_bytes, void* stream);
+
+/* Training: the forward kept for its backward.  kda_prefill_forward_saved gives
+ * kda_prefill's results (o, S_T, conv_state_out; computed as kda_prefill_backward
+ * computes them) and keeps in the workspace everything the backward would
+ * otherwise recompute (the chunk records, the front end's outputs, the decay
+ * sums, the state at every chunk start, and with the output stage the mixer's
+ * output before it); kda_prefill_backward_saved then runs the backward alone, with
+ * results identical to kda_prefill_backward's.
+ *   - ws: kda_training_workspace_bytes(f) bytes, 256-byte aligned, handed from the
+ *     forward to the backward untouched; the forward's inputs (q, k, v, g, beta,
+ *     the filters, the previous conv state and the optional stages' parameters)
+ *     must not change in between, and the backward's args.fwd must equal f.
+ *   - conv_state_out may not overlap conv_state_in (KDA_ERR_ALIAS): the backward
+ *     reads the previous conv state after the forward has written the new one.
+ *   - T = 0: the forward hands S0 and the conv state through, the backward gives
+ *     dS0 = dS_T and zero filter, history and parameter gradients; no workspace. */
+size_t kda_training_workspace_bytes(const kda_prefill_args* f);
+kda_status kda_prefill_forward_saved(const kda_prefill_args* f, void* ws, size_t ws_bytes,
+                                     void* stream);
+kda_status kda_prefill_backward_saved(const kda_backward_args* a, void* ws, size_t ws_bytes,
+                                      void* stream);
 
 /* ------------------------------------------------------------------- misc */
 const char* kda_status_str(int status);

@@ -23,10 +23,11 @@ def test_exports_every_declared_symbol(lib):
             "kda_prefill_workspace_bytes", "kda_validate_prefill", "kda_validate_decode",
             "kda_validate_conv_norm", "kda_status_str", "kda_abi_version",
             "kda_prefill_walk_segments", "kda_prefill_state_map",
-            "kda_prefill_state_map_workspace_bytes"} <= set(names)
+            "kda_prefill_state_map_workspace_bytes", "kda_training_workspace_bytes",
+            "kda_prefill_forward_saved", "kda_prefill_backward_saved"} <= set(names)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.kda_abi_version() == 6
+    assert lib.kda_abi_version() == 7
     for s in range(11):
         assert kda.kda_status_str(s) and kda.kda_status_str(s) != "unknown status"
 
@@ -393,6 +394,30 @@ def test_state_map_arguments(lib):
     assert sm(prefill(B=1, T=64, H=2, cu_seqlens=f(), n_seqs=1)) == UNSUP
     assert sm(prefill(B=0)) == SHAPE
     assert kda.kda_prefill_state_map_workspace_bytes(prefill(B=1, T=0, H=2)) == 0
+
+
+def test_saved_forward_arguments(lib):
+    """Host-side checks of the training pair (nothing is launched)."""
+    a = prefill(B=1, T=4096, H=8)
+    need = kda.kda_training_workspace_bytes(a)
+    assert need >= kda.kda_backward_workspace_bytes(backward(fwd=prefill(B=1, T=4096, H=8))) > 0
+    f = Fake()
+    f.next = 0x7D0000000000
+    ws = f(need)
+
+    def fs(args, w=ws, nbytes=need):
+        return lib.kda_prefill_forward_saved(ctypes.byref(args), ctypes.c_void_p(w), nbytes, None)
+    assert fs(a, nbytes=need - 1) == WS and fs(a, w=ws + 64) == WS and fs(a, w=None) == WS
+    assert fs(a, w=a.q) == ALIAS
+    same = prefill(B=1, T=4096, H=8)
+    same.conv_state_out = same.conv_state_in
+    assert fs(same) == ALIAS
+    b = backward(fwd=prefill(B=1, T=4096, H=8))
+    b.fwd.conv_state_out = b.fwd.conv_state_in
+    assert lib.kda_prefill_backward_saved(ctypes.byref(b), ctypes.c_void_p(ws), need, None) == ALIAS
+    # the output stage adds the mixer's output to the workspace
+    g = f()
+    assert kda.kda_training_workspace_bytes(prefill(B=1, T=4096, H=8, o_gate=g)) > need
 
 
 def test_backward_workspace_holds_the_forward(lib):
