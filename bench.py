@@ -388,6 +388,29 @@ def training_leg(kda, torch, w, args, stream, dev, plain_ms, backward_ms):
     return out
 
 
+def hbm_probe(torch, dev, stream, steps):
+    """A practical ceiling for the decode step's access pattern: torch's in-place
+    multiply of 1.5 GiB of float32 (read once, written once, like the 256 x 96
+    decode states)."""
+    x = torch.zeros(1610612736 // 4, dtype=torch.float32, device=dev)
+    for _ in range(3):
+        x.mul_(1.0)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        x.mul_(1.0)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = 2 * x.numel() * 4
+    del x
+    torch.cuda.empty_cache()
+    return {"what": "torch in-place multiply of 1.5 GiB float32", "ms": ms,
+            "GBps": nbytes / (ms / 1e3) / 1e9, "frac": nbytes / (ms / 1e3) / HBM_PEAK}
+
+
 def time_decode(kda, torch, da, stream, steps, warmup):
     for _ in range(warmup):
         kda.kda_decode_raw(da, stream)
@@ -762,6 +785,7 @@ def main(argv=None) -> int:
                            "algorithmic_bytes": dbytes}}
     del dinp, S, cs, od, da
     torch.cuda.empty_cache()
+    decode["hbm_probe"] = hbm_probe(torch, dev, stream, args.steps)
 
     stages = None
     if not args.no_stages:
