@@ -71,6 +71,36 @@ def test_state_map_matches_oracle(io, D, chunk, B, H, T):
     assert eM <= TOL[io] and eN <= TOL[io], (eM, eN)
 
 
+def test_state_map_with_raw_projections():
+    """With the decay and beta computed from raw projections the map follows the
+    activated values."""
+    from kda_inputs import make_stage_inputs
+    w = small(B=1, T=64 * 40 + 3, H=2, D=128, io="bf16", chunk=64, conv_state=True)
+    inp = make(w, seed=31)
+    st = make_stage_inputs(w, seed=31)
+    # slow decay (A_log = -7) and small write strengths, so M stays far from zero
+    st["A_log"] = torch.full_like(st["A_log"], -7.0)
+    inp = dict(inp, g=st["f"], beta=(st["b_logit"].float() - 4.0).to(st["b_logit"].dtype))
+    c = cuda(inp)
+    M, N = kda.kda_prefill_state_map(c["q"], c["k"], c["v"], c["g"], c["beta"], c["conv_w"],
+                                     c["conv_state"], chunk=64, A_log=st["A_log"].cuda(),
+                                     dt_bias=st["dt_bias"].cuda(), beta_logits=True)
+    torch.cuda.synchronize()
+    n = {k: to_numpy(v) for k, v in inp.items()}
+    kw = dict(A_log=to_numpy(st["A_log"]), dt_bias=to_numpy(st["dt_bias"]), beta_sigmoid=True)
+    _, rN, _ = kda_reference(n["q"], n["k"], n["v"], n["g"], n["beta"], conv_w=n["conv_w"],
+                             conv_state=n["conv_state"], S0=None, **kw)
+    cs0 = n["conv_state"].copy()
+    cs0[:, 2] = 0.0
+    eye = np.broadcast_to(np.eye(128), (1, 2, 128, 128)).copy()
+    _, rM, _ = kda_reference(n["q"], n["k"], np.zeros_like(n["v"]), n["g"], n["beta"],
+                             conv_w=n["conv_w"], conv_state=cs0, S0=eye, **kw)
+    eM, eN = rel_l2(M.cpu().numpy(), rM), rel_l2(N.cpu().numpy(), rN)
+    print(f"raw projections: M {eM:.2e} (|M| {np.linalg.norm(rM):.1f}) N {eN:.2e}", flush=True)
+    assert np.linalg.norm(rM) > 1.0
+    assert eM <= TOL["bf16"] and eN <= TOL["bf16"]
+
+
 def test_state_map_of_no_tokens_is_the_identity():
     w = small(B=2, T=0, H=3, D=32, io="bf16", chunk=32, conv_state=True)
     M, N = gpu_map(make(w, seed=1), 32)
