@@ -262,8 +262,11 @@ size_t kda_prefill_workspace_bytes(const kda_prefill_args* a) {
   return ws_layout(a).bytes;
 }
 
-static kda_status check_workspace(const kda_prefill_args* a, void* ws, size_t ws_bytes) {
-  const size_t need = kda_prefill_workspace_bytes(a);
+// The workspace of a call: 256-byte aligned, at least `need` bytes (the
+// prefill's by default), and clear of every buffer of the call.
+static kda_status check_workspace(const kda_prefill_args* a, void* ws, size_t ws_bytes,
+                                  size_t need = 0) {
+  if (need == 0) need = kda_prefill_workspace_bytes(a);
   if (need == 0) return KDA_OK;
   if (ws == nullptr || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0 || ws_bytes < need)
     return KDA_ERR_WORKSPACE;
@@ -521,8 +524,7 @@ kda_status kda_prefill_state_map(const kda_prefill_args* a, void* ws, size_t ws_
   if (a->T == 0)
     return hip_status(kda::launch_state_map_identity(M, N, (size_t)a->B * a->H * a->D * a->D, a->D, st));
   const size_t need = kda_prefill_state_map_workspace_bytes(a);
-  if (ws == nullptr || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0 || ws_bytes < need)
-    return KDA_ERR_WORKSPACE;
+  if (kda_status e = check_workspace(a, ws, ws_bytes, need); e != KDA_OK) return e;
   const Span w = span(ws, need);
   if (overlaps(w, m) || overlaps(w, n)) return KDA_ERR_ALIAS;
   const kda::WorkspaceLayout wl = ws_layout(a);

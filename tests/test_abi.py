@@ -390,6 +390,10 @@ def test_state_map_arguments(lib):
     assert sm(a, m=M + 4) == ALIGN
     assert sm(a, n=M) == ALIAS and sm(a, m=a.q) == ALIAS and sm(a, n=a.S0) == ALIAS
     assert sm(a, w=M - 256) == ALIAS
+    # the workspace against the call's own buffers, over all of its bytes
+    assert sm(a, w=a.q) == ALIAS
+    tail = (a.S0 - need + 256) // 256 * 256  # only its last bytes reach S0
+    assert sm(a, w=tail) == ALIAS
     assert sm(a, nbytes=need - 1) == WS and sm(a, w=ws + 16) == WS and sm(a, w=None) == WS
     assert sm(prefill(B=1, T=64, H=2, cu_seqlens=f(), n_seqs=1)) == UNSUP
     assert sm(prefill(B=0)) == SHAPE
