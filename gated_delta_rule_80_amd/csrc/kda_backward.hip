@@ -940,15 +940,20 @@ __global__ __launch_bounds__(512) void kda_bwd_t16_kernel(BwdTParams p) {
 // steps, exp(-s/2) of the block whose operand carries exp(+s/2) first (with G_q
 // the cumulative decay before block q):
 //   rK_p, rQ_p:  (. exp(-s_q/2)) exp(m_p - G_{q+1}),   cK_q:  (. exp(-s_p/2)) exp(G_p - m_q),
-// both factors <= 1.  a and b lie within exp(+-s/2) for a block span s: chunks with a span above kBwdSpan2
-// (log2 units) are listed for the exact kernel, which keeps the products' partial
-// sums (up to 16 |dA| 2^(s/2)) far from the float32 range.
+// both factors <= 1.  a and b lie within 2^(+-s/2) for a block span s (log2
+// units), so every operand and partial sum of the products is bounded by
+//   C max(|dA| |k|, |dP| |k|, |beta| |dA| |k| + |dP| |q'|) 2^(s/2)
+// with each maximum taken over the chunk.  A chunk whose widest span or whose
+// bound exceeds what float32 holds with room to spare (span 240, bound 2^120) is
+// listed for the exact kernel; the bound comes from the chunk's own values, so
+// wide spans with ordinary gradients stay factored.
 // One workgroup per chunk record; wave w owns channels [16 w, 16 w + 16).  Lane
 // (r, g4) holds the operands of rows 4 s + g4 (s < C / 4) of its channel 16 w + r
 // (the matrix-core B layout), and its results for rows 16 p + 4 g4 + e.  Row
 // block by row block: the products that finish rK, rQ and cK of the block, then
 // its element terms as in the exact kernel.
-constexpr float kBwdSpan2 = 128.f;
+constexpr float kBwdSpan2 = 240.f;   // widest block span factored (log2 units)
+constexpr float kBwdBound2 = 120.f;  // log2 of the largest partial sum allowed
 
 template <int D, int C, typename E>
 __global__ __launch_bounds__(4 * D, D / 32 > 1 ? D / 32 : 1) void kda_bwd_pair_mma_kernel(BwdPairParams p) {
@@ -962,7 +967,10 @@ __global__ __launch_bounds__(4 * D, D / 32 > 1 ? D / 32 : 1) void kda_bwd_pair_m
   __shared__ float sdbw[(D / 16) * C];  // dbeta partial sums per wave
   __shared__ float sGC[D];
   __shared__ float sB[C];
-  __shared__ int sfat[D / 16];  // per wave: a block span of its channels is too wide
+  // per wave: the widest block span of its channels, the largest |k|, |q'|, |dA|,
+  // |dP| it holds; and the largest |beta| of the chunk
+  __shared__ float smax[5][D / 16];
+  __shared__ float smaxb;
   constexpr int NSG = NTH / D;  // token segments of the dg running sum
   constexpr int SL = C / NSG;   // tokens per segment
   __shared__ float sseg[NSG * D];  // segment totals of dGamma
@@ -998,7 +1006,7 @@ __global__ __launch_bounds__(4 * D, D / 32 > 1 ? D / 32 : 1) void kda_bwd_pair_m
   // block boundaries G_1 .. G_NB (Gamma at the last row of each block: lane
   // (r, 3), s = 4 p + 3) and the midpoints m_p = (G_p + G_p+1) / 2, G_0 = 0
   float mid[NB], gbd[NB + 1];  // midpoints, block boundaries G_0 = 0, G_1, ...
-  bool fatal = false;
+  float mx[5] = {0.f, 0.f, 0.f, 0.f, 0.f};  // span, |k|, |q'|, |dA|, |dP| seen by this lane
   {
     float gprev = 0.f;
     gbd[0] = 0.f;
@@ -1007,13 +1015,14 @@ __global__ __launch_bounds__(4 * D, D / 32 > 1 ? D / 32 : 1) void kda_bwd_pair_m
       const float gend = __shfl(gB[4 * q + 3], 48 + r, 64);
       mid[q] = 0.5f * (gprev + gend);
       gbd[q + 1] = gend;
-      fatal |= gprev - gend > kBwdSpan2;
+      mx[0] = fmaxf(mx[0], gprev - gend);
       gprev = gend;
     }
   }
-  {
-    const bool wfat = __any(fatal);
-    if (lane == 0) sfat[wave] = wfat ? 1 : 0;
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    mx[1] = fmaxf(mx[1], fabsf(kB[s]));
+    mx[2] = fmaxf(mx[2], fabsf(qB[s]));
   }
   // dA and dP into LDS
   const E* gdA = static_cast<const E*>(p.dA) + (size_t)rec * C * C;
@@ -1026,12 +1035,35 @@ __global__ __launch_bounds__(4 * D, D / 32 > 1 ? D / 32 : 1) void kda_bwd_pair_m
     for (int e = 0; e < 4; ++e) {
       sdA[i * LA + j4 + e] = va[e];
       sdP[i * LA + j4 + e] = vp[e];
+      mx[3] = fmaxf(mx[3], fabsf(va[e]));
+      mx[4] = fmaxf(mx[4], fabsf(vp[e]));
     }
   }
-  __syncthreads();
-  bool anyfat = false;
 #pragma unroll
-  for (int w = 0; w < D / 16; ++w) anyfat |= sfat[w] != 0;
+  for (int m = 0; m < 5; ++m) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) mx[m] = fmaxf(mx[m], __shfl_xor(mx[m], o, 64));
+    if (lane == 0) smax[m][wave] = mx[m];
+  }
+  if (wave == 0) {  // the beta loads above are lanes tid < C of wave 0
+    float mb = tid < C ? fabsf(sB[tid]) : 0.f;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) mb = fmaxf(mb, __shfl_xor(mb, o, 64));
+    if (lane == 0) smaxb = mb;
+  }
+  __syncthreads();
+  bool anyfat;
+  {
+    float m[5] = {0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < D / 16; ++w)
+#pragma unroll
+      for (int k = 0; k < 5; ++k) m[k] = fmaxf(m[k], smax[k][w]);
+    const float span = m[0], mk = m[1], mq = m[2], ma = m[3], mp = m[4];
+    const float bound = fmaxf(fmaxf(ma * mk, mp * mk), smaxb * ma * mk + mp * mq) * (float)C;
+    // (an infinite or NaN bound fails the comparison and lists the chunk)
+    anyfat = !(span <= kBwdSpan2 && bound <= __builtin_amdgcn_exp2f(kBwdBound2 - 0.5f * span));
+  }
   if (anyfat) {
     if (tid == 0) {
       const unsigned slot = atomicAdd(p.ex_count, 1u);

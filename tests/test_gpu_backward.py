@@ -19,12 +19,13 @@ pytestmark = pytest.mark.gpu
 NAMES = ("dq", "dk", "dv", "dg", "dbeta", "dS0", "dconv_w", "dconv_state")
 
 
-def check_backward(w, chunk, seed=0, conv=True, l2=True, scale=1.0, with_dST=True, g_head=None):
-    check_backward_inputs(w, chunk, make(w, seed), seed, conv, l2, scale, with_dST, g_head)
+def check_backward(w, chunk, seed=0, conv=True, l2=True, scale=1.0, with_dST=True, g_head=None,
+                   do_scale=1.0):
+    check_backward_inputs(w, chunk, make(w, seed), seed, conv, l2, scale, with_dST, g_head, do_scale)
 
 
 def check_backward_inputs(w, chunk, inp, seed=0, conv=True, l2=True, scale=1.0, with_dST=True,
-                          g_head=None):
+                          g_head=None, do_scale=1.0):
     if g_head is not None:
         # constant log-decay per token on the given heads: {head: g}
         g = inp["g"].clone()
@@ -34,8 +35,8 @@ def check_backward_inputs(w, chunk, inp, seed=0, conv=True, l2=True, scale=1.0, 
     if not conv:
         inp = dict(inp, conv_w=None, conv_state=None)
     gen = torch.Generator().manual_seed(seed + 1000)
-    do = torch.randn(w.B, w.T, w.H, w.D, generator=gen).to(inp["q"].dtype)
-    dST = torch.randn(w.B, w.H, w.D, w.D, generator=gen) if with_dST else None
+    do = (torch.randn(w.B, w.T, w.H, w.D, generator=gen) * do_scale).to(inp["q"].dtype)
+    dST = torch.randn(w.B, w.H, w.D, w.D, generator=gen) * do_scale if with_dST else None
     c = cuda(inp)
     grads, o, S_T = kda.kda_prefill_backward(c["q"], c["k"], c["v"], c["g"], c["beta"], c["conv_w"],
                                              c["conv_state"], c["S0"], do=do.cuda(),
@@ -93,14 +94,25 @@ def test_backward_strong_decay_bf16():
 
 
 @pytest.mark.parametrize("io,D,chunk", [("bf16", 128, 64), ("fp32", 64, 32), ("bf16", 32, 16)])
-@pytest.mark.parametrize("g0", [-12.0, -5.2])
+@pytest.mark.parametrize("g0", [-12.0, -8.0, -5.2])
 def test_backward_factored_and_exact_pair_paths(io, D, chunk, g0):
     """Head 0 decays by a constant g0 per token: -12 gives 16-token block spans of
-    about 277 log2 units, beyond the factored pair products' limit (the chunks go to
-    the exact per-pair kernel); -5.2 gives about 120, just inside it (the widest
-    factors the factored kernel meets).  Head 1 keeps its drawn decays."""
+    about 277 log2 units, beyond the factored pair products' span limit of 240 (the
+    chunks go to the exact per-pair kernel); -8 gives about 185 and -5.2 about 120,
+    both factored with gradients of ordinary size (factors up to 2^92 and 2^60).
+    Head 1 keeps its drawn decays."""
     w = small(B=1, T=150, H=2, D=D, io=io, chunk=chunk, s0=True, conv_state=True)
     check_backward(w, chunk, seed=17, g_head={0: g0})
+
+
+@pytest.mark.parametrize("io,D,chunk", [("bf16", 128, 64), ("fp32", 64, 32)])
+def test_backward_pair_path_follows_the_gradient_scale(io, D, chunk):
+    """Spans of about 185 log2 units with dO and dS_T scaled by 2^40: the chunk's
+    bound on the factored partial sums passes 2^120, so its pair terms go to the
+    exact kernel (with unit gradients the same chunks are factored); the
+    gradients, 2^40 times larger, still match the oracle."""
+    w = small(B=1, T=150, H=2, D=D, io=io, chunk=chunk, s0=True, conv_state=True)
+    check_backward(w, chunk, seed=17, g_head={0: -8.0}, do_scale=2.0 ** 40)
 
 
 @pytest.mark.parametrize("io,D,chunk", [("fp32", 64, 32), ("bf16", 128, 64)])

@@ -55,6 +55,8 @@ CASES = [
     ("fp32", 128, 32, 1, 1, 32 * 64 + 3),
     ("fp32", 64, 32, 2, 1, 32 * 48 + 31),
     ("bf16", 32, 16, 1, 2, 16 * 100 + 7),
+    ("fp32", 32, 32, 1, 2, 7),      # shorter than one chunk
+    ("bf16", 64, 64, 2, 1, 64),     # exactly one chunk
 ]
 
 
