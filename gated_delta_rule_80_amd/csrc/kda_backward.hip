@@ -292,15 +292,15 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_walk_kernel(BwdWalkParams p) {
     RowFrag<E, C> fqlt[NCTW], fwt[NCTW];
     f32x4 flc[NCTW];
     if (has_u) {
-      load_swz_t<C, C>(fpt, iP, t_row, g4);
+      load_frag_t<C, C>(fpt, iP, 16 * R, r, g4);
       fpt.mask_below(t_row, g4);  // P[j][t] vanishes for j < t
-      load_swz_t<D, C>(fkt, iKT, t_row, g4);
+      load_frag_t<D, C>(fkt, iKT, 16 * R, r, g4);
     }
 #pragma unroll
     for (int jj = 0; jj < NCTW; ++jj) {
       const int Ct = (wave % CTW) + CTW * jj;
-      load_swz_t<C, D>(fqlt[jj], iQL, 16 * Ct + r, g4);
-      load_swz_t<C, D>(fwt[jj], iW, 16 * Ct + r, g4);
+      load_frag_t<C, D>(fqlt[jj], iQL, 16 * Ct, r, g4);
+      load_frag_t<C, D>(fwt[jj], iW, 16 * Ct, r, g4);
       flc[jj] = *reinterpret_cast<const f32x4*>(iLC + 16 * Ct + 4 * g4);
     }
     lds_barrier();  // every wave holds its fragments: the image may be overwritten
@@ -858,7 +858,7 @@ __global__ __launch_bounds__(512) void kda_bwd_t16_kernel(BwdTParams p) {
   for (int tile = wave; tile < RT * RT; tile += NW) {
     const int Jt = tile / RT, Mt = tile % RT;
     RowFrag<__bf16, C> fa, fb;
-    load_swz_t<C, C>(fa, iTt, 16 * Jt + r, g4);
+    load_frag_t<C, C>(fa, iTt, 16 * Jt, r, g4);
     load_swz<C>(fb, idT, 16 * Mt + r, g4);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     mma<C>(acc, fa, fb);

@@ -312,6 +312,45 @@ __device__ __forceinline__ void load_swz_t(RowFrag<float, KF>& f, const float* i
   for (int i = 0; i < RowFrag<float, KF>::N; ++i) f.v[i] = img[Swz<float, KM>::at(4 * i + g, j)];
 }
 
+// The same transposed bf16 fragment with gfx950's transposing LDS read
+// (ds_read_b64_tr_b16).  Within each group of 16 lanes, output lane i element e is
+// element i % 4 of the 8 bytes lane 4 e + i / 4 addressed; so lane r of the group
+// addresses image row k0 + r / 4, columns m0 + 4 (r % 4) .. + 3, and receives
+// column m0 + r of rows k0 .. k0 + 3: four k-elements of its fragment in one read.
+// The lanes of a group share g (lanes 16 g .. 16 g + 15), m0 is the fragment's
+// 16-column block of the image, r the lane's index within its group.
+template <int KF, int KM>
+__device__ __forceinline__ void load_swz_tr(RowFrag<__bf16, KF>& f, const __bf16* img, int m0, int r,
+                                            int g) {
+  using FR = RowFrag<__bf16, KF>;
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  const int col = m0 + 4 * (r & 3);
+#pragma unroll
+  for (int i = 0; i < FR::N; ++i)
+#pragma unroll
+    for (int hh = 0; hh < FR::PER / 4; ++hh) {
+      const int row = i * FR::STEP + FR::PER * g + 4 * hh + (r >> 2);
+      // (the bf16 form of the builtin: the 16-bit integer form with each element
+      // cast to bf16 was compiled to use element 0 four times)
+      const bf16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (lds_bf16x4*)(img + Swz<__bf16, KM>::at(row, col)));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) f.v[i][4 * hh + e] = v[e];
+    }
+}
+// Transposed fragment of column m0 + r: the transposing read for bf16, element
+// reads for fp32 (which has no such read).
+template <int KF, int KM>
+__device__ __forceinline__ void load_frag_t(RowFrag<__bf16, KF>& f, const __bf16* img, int m0, int r,
+                                            int g) {
+  load_swz_tr<KF, KM>(f, img, m0, r, g);
+}
+template <int KF, int KM>
+__device__ __forceinline__ void load_frag_t(RowFrag<float, KF>& f, const float* img, int m0, int r,
+                                            int g) {
+  load_swz_t<KF, KM>(f, img, m0 + r, g);
+}
+
 // Instruction depth along k for an element type (used for causal bounds).
 template <typename E> struct KStep;
 template <> struct KStep<__bf16> { static constexpr int value = 32; };
