@@ -748,11 +748,12 @@ __global__ __launch_bounds__(512) void kda_bwd_t16_kernel(BwdTParams p) {
   constexpr int CT = D / 16, RT = C / 16;
   using SD = Swz<__bf16, D>;
   using SC = Swz<__bf16, C>;
-  // One region holds the images of dW, dU, Bk, Bv for the dT products, then (after
-  // them) Y^T and the transposed images of dW and dU; T^T and dT sit beside it.
-  // T itself is read as transposed fragments of T^T.  80 KB at C = 64, D = 128,
-  // so two workgroups share a compute unit.
-  constexpr int REG = 4 * C * D > C * C + 2 * C * D ? 4 * C * D : C * C + 2 * C * D;
+  // One region holds the images of dW, dU, Bk, Bv for the dT products; Y^T then
+  // takes the place of Bk (dW and dU stay for the dBk, dBv products, which read
+  // them as transposed fragments); T^T and dT sit beside it.  T itself is read as
+  // transposed fragments of T^T.  80 KB at C = 64, D = 128, so two workgroups
+  // share a compute unit.
+  constexpr int REG = 2 * C * D + (C * C > 2 * C * D ? C * C : 2 * C * D);
   __shared__ __attribute__((aligned(16))) __bf16 reg[REG];
   __shared__ __attribute__((aligned(16))) __bf16 iTt[C * C];
   __shared__ __attribute__((aligned(16))) __bf16 idT[C * C];
@@ -760,9 +761,7 @@ __global__ __launch_bounds__(512) void kda_bwd_t16_kernel(BwdTParams p) {
   __bf16* iU = reg + C * D;
   __bf16* iBk = reg + 2 * C * D;
   __bf16* iBv = reg + 3 * C * D;
-  __bf16* iYt = reg;  // after the dT products
-  __bf16* iWt = reg + C * C;
-  __bf16* iUt = reg + C * C + D * C;
+  __bf16* iYt = iBk;  // after the dT products
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g4 = lane >> 4;
@@ -779,9 +778,9 @@ __global__ __launch_bounds__(512) void kda_bwd_t16_kernel(BwdTParams p) {
   const __bf16* gTt = static_cast<const __bf16*>(p.tT) + (size_t)rec * C * C;  // [j][i] = T[i][j]
   for (int it = tid; it < C * D / 4; it += NT) {
     const int t = it / (D / 4), c4 = 4 * (it % (D / 4));
-    const bf16x4 w = *reinterpret_cast<const bf16x4*>(gdW + (size_t)t * D + c4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) iW[SD::at(t, c4 + e)] = w[e];
+    // 4 elements inside one 16-byte chunk of the image row
+    *reinterpret_cast<bf16x4*>(&iW[SD::at(t, c4)]) =
+        *reinterpret_cast<const bf16x4*>(gdW + (size_t)t * D + c4);
   }
   for (int it = tid; it < C * D / 8; it += NT) {
     const int t = it / (D / 8), c8 = 8 * (it % (D / 8));
@@ -836,24 +835,7 @@ __global__ __launch_bounds__(512) void kda_bwd_t16_kernel(BwdTParams p) {
       idT[SC::at(i, j)] = (__bf16)(j <= i ? acc[e] : 0.f);
     }
   }
-  __syncthreads();  // the images of dW, dU, Bk, Bv are dead
-  // dW and dU again (from L2), for their transposed images: loaded into registers
-  // before the Y^T products, written after them
-  constexpr int NWL = (C * D / 4 + NT - 1) / NT, NUL = (C * D / 8 + NT - 1) / NT;
-  bf16x4 wl[NWL];
-  bf16x8 ul[NUL];
-#pragma unroll
-  for (int k = 0; k < NWL; ++k) {
-    const int it = tid + NT * k;
-    if (it < C * D / 4)
-      wl[k] = *reinterpret_cast<const bf16x4*>(gdW + (size_t)(it / (D / 4)) * D + 4 * (it % (D / 4)));
-  }
-#pragma unroll
-  for (int k = 0; k < NUL; ++k) {
-    const int it = tid + NT * k;
-    if (it < C * D / 8)
-      ul[k] = *reinterpret_cast<const bf16x8*>(gdU + (size_t)(it / (D / 8)) * D + 8 * (it % (D / 8)));
-  }
+  __syncthreads();  // the images of Bk and Bv are dead
   // ---- Y^T (j, m) = sum_l T[j][l] dT[m][l], T rows read down the columns of T^T
   for (int tile = wave; tile < RT * RT; tile += NW) {
     const int Jt = tile / RT, Mt = tile % RT;
@@ -864,24 +846,6 @@ __global__ __launch_bounds__(512) void kda_bwd_t16_kernel(BwdTParams p) {
     mma<C>(acc, fa, fb);
 #pragma unroll
     for (int e = 0; e < 4; ++e) iYt[SC::at(16 * Jt + 4 * g4 + e, 16 * Mt + r)] = (__bf16)acc[e];
-  }
-#pragma unroll
-  for (int k = 0; k < NWL; ++k) {
-    const int it = tid + NT * k;
-    if (it < C * D / 4) {
-      const int t = it / (D / 4), c4 = 4 * (it % (D / 4));
-#pragma unroll
-      for (int e = 0; e < 4; ++e) iWt[SC::at(c4 + e, t)] = wl[k][e];
-    }
-  }
-#pragma unroll
-  for (int k = 0; k < NUL; ++k) {
-    const int it = tid + NT * k;
-    if (it < C * D / 8) {
-      const int t = it / (D / 8), c8 = 8 * (it % (D / 8));
-#pragma unroll
-      for (int e = 0; e < 8; ++e) iUt[SC::at(c8 + e, t)] = ul[k][e];
-    }
   }
   __syncthreads();
   // ---- dA (i, j) = -sum_m T^T[i][m] Y^T[j][m]  (j < i)
@@ -901,15 +865,16 @@ __global__ __launch_bounds__(512) void kda_bwd_t16_kernel(BwdTParams p) {
       gdA[(size_t)i * C + j] = (__bf16)(j < i ? -acc[e] : 0.f);
     }
   }
-  // ---- dBk (j, c) = sum_i T^T[j][i] dW^T[c][i],  dBv likewise with dU
+  // ---- dBk (j, c) = sum_i T^T[j][i] dW^T[c][i],  dBv likewise with dU (dW^T and
+  // dU^T rows read as transposed fragments of the dW, dU images)
   __bf16* gdBk = static_cast<__bf16*>(p.dBk) + (size_t)rec * C * D;
   __bf16* gdBv = static_cast<__bf16*>(p.dBv) + (size_t)rec * C * D;
   for (int tile = wave; tile < RT * CT; tile += NW) {
     const int Jt = tile / CT, Ct = tile % CT;
     RowFrag<__bf16, C> ft, fw, fu;
     load_swz<C>(ft, iTt, 16 * Jt + r, g4);
-    load_swz<C>(fw, iWt, 16 * Ct + r, g4);
-    load_swz<C>(fu, iUt, 16 * Ct + r, g4);
+    load_swz_tr<C, D>(fw, iW, 16 * Ct, r, g4);
+    load_swz_tr<C, D>(fu, iU, 16 * Ct, r, g4);
     f32x4 ak = {0.f, 0.f, 0.f, 0.f}, av = ak;
     mma<C>(ak, ft, fw);
     mma<C>(av, ft, fu);
