@@ -734,10 +734,11 @@ __global__ __launch_bounds__(512) void kda_bwd_t_kernel(BwdTParams p) {
 // bf16 records: the same products as element-type matrix-core products
 // (16x16x32, operands k-contiguous from swizzled LDS images, float accumulation),
 // the float32 inputs rounded to bf16 as the forward rounds T and its operands.
-// One 512-thread workgroup per chunk record.  Images (rows, k):
-//   W [i][c] and W^T [c][i] of dW, U [i][c] and U^T [c][i] of dU, Bk [j][c],
-//   Bv [j][c], T [j][l], T^T [i][m], dT [m][l], Y^T [j][m]
-// and the products, in the NT form C[a][b] = sum_k A[a][k] B[b][k]:
+// One 512-thread workgroup per chunk record.  LDS images (rows, k): W [i][c] of
+// dW, U [i][c] of dU, Bk [j][c], Bv [j][c], T^T [i][m], dT^T [l][m], Y [m][j]; the
+// rows of a transposed operand (T, dT, Y^T, W^T, U^T) are read down the columns of
+// the stored image with the transposing read.  The products, in the NT form
+// C[a][b] = sum_k A[a][k] B[b][k]:
 //   dT  = dW Bk^T + dU Bv^T   A = W, U rows i;     B = Bk, Bv rows j      (j <= i)
 //   Y^T = T dT^T              A = T rows j;        B = dT rows m
 //   dA  = -T^T Y              A = T^T rows i;      B = Y^T rows j         (j < i)
@@ -748,7 +749,7 @@ __global__ __launch_bounds__(512) void kda_bwd_t16_kernel(BwdTParams p) {
   constexpr int CT = D / 16, RT = C / 16;
   using SD = Swz<__bf16, D>;
   using SC = Swz<__bf16, C>;
-  // One region holds the images of dW, dU, Bk, Bv for the dT products; Y^T then
+  // One region holds the images of dW, dU, Bk, Bv for the dT products; Y then
   // takes the place of Bk (dW and dU stay for the dBk, dBv products, which read
   // them as transposed fragments); T^T and dT sit beside it.  T itself is read as
   // transposed fragments of T^T.  80 KB at C = 64, D = 128, so two workgroups
@@ -756,12 +757,12 @@ __global__ __launch_bounds__(512) void kda_bwd_t16_kernel(BwdTParams p) {
   constexpr int REG = 2 * C * D + (C * C > 2 * C * D ? C * C : 2 * C * D);
   __shared__ __attribute__((aligned(16))) __bf16 reg[REG];
   __shared__ __attribute__((aligned(16))) __bf16 iTt[C * C];
-  __shared__ __attribute__((aligned(16))) __bf16 idT[C * C];
+  __shared__ __attribute__((aligned(16))) __bf16 idTt[C * C];  // dT^T
   __bf16* iW = reg;
   __bf16* iU = reg + C * D;
   __bf16* iBk = reg + 2 * C * D;
   __bf16* iBv = reg + 3 * C * D;
-  __bf16* iYt = iBk;  // after the dT products
+  __bf16* iY = iBk;  // Y, after the dT products
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g4 = lane >> 4;
@@ -789,9 +790,9 @@ __global__ __launch_bounds__(512) void kda_bwd_t16_kernel(BwdTParams p) {
   }
   for (int it = tid; it < C * C / 4; it += NT) {
     const int a = it / (C / 4), b4 = 4 * (it % (C / 4));
-    const bf16x4 x = *reinterpret_cast<const bf16x4*>(gTt + (size_t)a * C + b4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) iTt[SC::at(a, b4 + e)] = x[e];  // T^T[a][b]
+    // T^T[a][b4 .. b4 + 3], inside one 16-byte chunk of the image row
+    *reinterpret_cast<bf16x4*>(&iTt[SC::at(a, b4)]) =
+        *reinterpret_cast<const bf16x4*>(gTt + (size_t)a * C + b4);
   }
   // Bk = beta k exp(Gamma), Bv = beta v; rows past the end of the sequence read
   // the last row and take beta = 0
@@ -829,11 +830,12 @@ __global__ __launch_bounds__(512) void kda_bwd_t16_kernel(BwdTParams p) {
       load_swz<D>(fb, iBv, 16 * Jt + r, g4);
       mma<D>(acc, fa, fb);
     }
+    // rows i .. i + 3 of column j: 4 consecutive elements of row j of dT^T
+    const int i0 = 16 * It + 4 * g4, j = 16 * Jt + r;
+    bf16x4 x;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = 16 * It + 4 * g4 + e, j = 16 * Jt + r;
-      idT[SC::at(i, j)] = (__bf16)(j <= i ? acc[e] : 0.f);
-    }
+    for (int e = 0; e < 4; ++e) x[e] = (__bf16)(j <= i0 + e ? acc[e] : 0.f);
+    *reinterpret_cast<bf16x4*>(&idTt[SC::at(j, i0)]) = x;
   }
   __syncthreads();  // the images of Bk and Bv are dead
   // ---- Y^T (j, m) = sum_l T[j][l] dT[m][l], T rows read down the columns of T^T
@@ -841,11 +843,14 @@ __global__ __launch_bounds__(512) void kda_bwd_t16_kernel(BwdTParams p) {
     const int Jt = tile / RT, Mt = tile % RT;
     RowFrag<__bf16, C> fa, fb;
     load_frag_t<C, C>(fa, iTt, 16 * Jt, r, g4);
-    load_swz<C>(fb, idT, 16 * Mt + r, g4);
+    load_swz_tr<C, C>(fb, idTt, 16 * Mt, r, g4);  // dT rows: columns of dT^T
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     mma<C>(acc, fa, fb);
+    // Y^T rows j .. j + 3 of column m: 4 consecutive elements of row m of Y
+    bf16x4 x;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) iYt[SC::at(16 * Jt + 4 * g4 + e, 16 * Mt + r)] = (__bf16)acc[e];
+    for (int e = 0; e < 4; ++e) x[e] = (__bf16)acc[e];
+    *reinterpret_cast<bf16x4*>(&iY[SC::at(16 * Mt + r, 16 * Jt + 4 * g4)]) = x;
   }
   __syncthreads();
   // ---- dA (i, j) = -sum_m T^T[i][m] Y^T[j][m]  (j < i)
@@ -856,7 +861,7 @@ __global__ __launch_bounds__(512) void kda_bwd_t16_kernel(BwdTParams p) {
     if (Jt <= It) {
       RowFrag<__bf16, C> fa, fb;
       load_swz<C>(fa, iTt, 16 * It + r, g4);
-      load_swz<C>(fb, iYt, 16 * Jt + r, g4);
+      load_swz_tr<C, C>(fb, iY, 16 * Jt, r, g4);  // Y^T rows: columns of Y
       mma<C>(acc, fa, fb);
     }
 #pragma unroll
