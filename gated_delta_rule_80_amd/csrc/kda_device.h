@@ -318,7 +318,9 @@ __device__ __forceinline__ void load_swz_t(RowFrag<float, KF>& f, const float* i
 // addresses image row k0 + r / 4, columns m0 + 4 (r % 4) .. + 3, and receives
 // column m0 + r of rows k0 .. k0 + 3: four k-elements of its fragment in one read.
 // The lanes of a group share g (lanes 16 g .. 16 g + 15), m0 is the fragment's
-// 16-column block of the image, r the lane's index within its group.
+// 16-column block of the image, r the lane's index within its group.  A lane's
+// result comes from the addresses of other lanes of its group, so all 16 must be
+// active: call it from wave-uniform control flow only.
 template <int KF, int KM>
 __device__ __forceinline__ void load_swz_tr(RowFrag<__bf16, KF>& f, const __bf16* img, int m0, int r,
                                             int g) {
