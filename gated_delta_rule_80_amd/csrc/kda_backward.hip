@@ -29,23 +29,23 @@ namespace kda {
 // Tokens of record `rec`: `tok` is the token row of its first token (rows of the
 // [rows of tokens][H][D] tensors are tok + t), `nval` how many of its C tokens
 // exist (0 for an unused slot of a packed batch), h its head.  B equal-length
-// sequences: rec = (b H + h) NT + n.  Packed: rec = h NT + slot, the slot a
-// chunk of the sequence that owns it (the workspace tables).
+// sequences: rec = rec_slot(n, b H + h, B H).  Packed: rec = rec_slot(slot, h,
+// H), the slot a chunk of the sequence that owns it (the workspace tables).
 struct RecTok {
   long tok;
   int nval, h;
 };
-__device__ __forceinline__ RecTok rec_tokens(int rec, int T, int H, int NT, int C, const SeqTables& sq) {
+__device__ __forceinline__ RecTok rec_tokens(int rec, int B, int T, int H, int C, const SeqTables& sq) {
   RecTok g;
   if (sq.bounds == nullptr) {
-    const int n = rec % NT, bh = rec / NT;
+    const int n = rec / (B * H), bh = rec % (B * H);
     g.h = bh % H;
     g.tok = (long)(bh / H) * T + (long)n * C;
     const int rem = T - n * C;
     g.nval = rem < C ? (rem > 0 ? rem : 0) : C;
   } else {
-    const int slot = rec % NT;
-    g.h = rec / NT;
+    const int slot = rec / H;
+    g.h = rec % H;
     g.tok = 0;
     g.nval = 0;
     if (slot < sq.cstart[sq.n_seqs]) {
@@ -139,8 +139,10 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_walk_kernel(BwdWalkParams p) {
   const int h = bh % p.H, b = bh / p.H;
   const int vb0 = vblk * VB;
   const size_t HD = (size_t)p.H * D;
-  // the sequence's records, first token row and length
-  size_t rec0 = (size_t)bh * p.NT;
+  // the sequence's records (chunk n is record rec0 + n rstride, rec_slot), first
+  // token row and length
+  size_t rstride = (size_t)p.B * p.H;
+  size_t rec0 = bh;
   long tok0 = (long)b * p.T;
   int Tq = p.T, nch = p.NT;
   if (p.seqs.bounds != nullptr) {
@@ -149,7 +151,8 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_walk_kernel(BwdWalkParams p) {
     Tq = p.seqs.bounds[b + 1] - p.seqs.bounds[b];
     nch = (Tq + C - 1) / C;
     if (c0 + nch > p.NT) nch = c0 < p.NT ? p.NT - c0 : 0;  // inconsistent tables: stay in the head's slots
-    rec0 = (size_t)h * p.NT + c0;
+    rstride = (size_t)p.H;
+    rec0 = rec_slot(c0, h, rstride);
   }
   // this workgroup's chunks [n_lo, n_hi) of the sequence
   int n_lo = 0, n_hi = nch;
@@ -188,7 +191,7 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_walk_kernel(BwdWalkParams p) {
     src_off[it] = (uint32_t)off;
   }
   auto issue_copy = [&](int n) {
-    const char* recp = p.ws + (rec0 + n) * RL.bytes;
+    const char* recp = p.ws + (rec0 + n * rstride) * RL.bytes;
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
       if (it * NT + tid < IMG::CHUNKS)
@@ -281,7 +284,7 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_walk_kernel(BwdWalkParams p) {
       const int u = wave + NW * i;
       if (!MAPW && (FULL_S || u < CT * VT)) {
         const int Ct = u % CT, Vt = u / CT;
-        E* ck = static_cast<E*>(p.ckdS) + (rec0 + n) * D * D + vb0 + 16 * Vt + r;
+        E* ck = static_cast<E*>(p.ckdS) + (rec0 + n * rstride) * D * D + vb0 + 16 * Vt + r;
 #pragma unroll
         for (int e = 0; e < 4; ++e) ck[(size_t)(16 * Ct + 4 * g4 + e) * D] = from_f32<E>(accS[i][e]);
       }
@@ -324,7 +327,7 @@ __global__ __launch_bounds__(NT, 1) void kda_bwd_walk_kernel(BwdWalkParams p) {
         mma<D>(acc, fkt, fs);
         store4(&sDU[(16 * Vt + r) * LU + 16 * R + 4 * g4], acc[0], acc[1], acc[2], acc[3]);
         if constexpr (!MAPW) {
-          E* du = static_cast<E*>(p.dU) + (rec0 + n) * C * D + vb0 + 16 * Vt + r;  // dU [t][v]
+          E* du = static_cast<E*>(p.dU) + (rec0 + n * rstride) * C * D + vb0 + 16 * Vt + r;  // dU [t][v]
 #pragma unroll
           for (int e = 0; e < 4; ++e) du[(size_t)(16 * R + 4 * g4 + e) * D] = from_f32<E>(acc[e]);
         }
@@ -412,7 +415,7 @@ __global__ __launch_bounds__(256) void kda_bwd_prod_kernel(BwdProdParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g4 = lane >> 4;
   const int rec = blockIdx.x;
-  const RecTok rt = rec_tokens(rec, p.T, p.H, p.NT, C, p.seqs);
+  const RecTok rt = rec_tokens(rec, p.B, p.T, p.H, C, p.seqs);
   if (rt.nval == 0) return;  // an unused slot: nothing reads its products
   const int h = rt.h;
   const size_t HD = (size_t)p.H * D;
@@ -579,7 +582,7 @@ __global__ __launch_bounds__(512) void kda_bwd_t_kernel(BwdTParams p) {
   auto load_stage = [&](int rec, int tid, Stage& S) {
     // (an unused slot of a packed batch reads token row 0 with beta = 0; nothing
     // reads what it produces)
-    const RecTok rt = rec_tokens(rec, p.T, p.H, p.NT, C, p.seqs);
+    const RecTok rt = rec_tokens(rec, p.B, p.T, p.H, C, p.seqs);
     const int h = rt.h;
     const float* gdW = static_cast<const float*>(p.dW) + (size_t)rec * C * D;
     const E* gdU = static_cast<const E*>(p.dU) + (size_t)rec * C * D;  // [t][v]
@@ -767,7 +770,7 @@ __global__ __launch_bounds__(512) void kda_bwd_t16_kernel(BwdTParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g4 = lane >> 4;
   const int rec = blockIdx.x;
-  const RecTok rt = rec_tokens(rec, p.T, p.H, p.NT, C, p.seqs);
+  const RecTok rt = rec_tokens(rec, p.B, p.T, p.H, C, p.seqs);
   if (rt.nval == 0) return;  // an unused slot: nothing reads its products
   const int h = rt.h;
   const size_t HD = (size_t)p.H * D;
@@ -951,7 +954,7 @@ __global__ __launch_bounds__(4 * D, D / 32 > 1 ? D / 32 : 1) void kda_bwd_pair_m
   const int r = lane & 15, g4 = lane >> 4;
   const int c = 16 * wave + r;  // this lane's channel
   const int rec = blockIdx.x;
-  const RecTok rt = rec_tokens(rec, p.T, p.H, p.NT, C, p.seqs);
+  const RecTok rt = rec_tokens(rec, p.B, p.T, p.H, C, p.seqs);
   if (rt.nval == 0) return;  // an unused slot of a packed batch
   const int h = rt.h;
   const size_t HD = (size_t)p.H * D;
@@ -1225,7 +1228,7 @@ __global__ __launch_bounds__(D * (C / 16)) void kda_bwd_pair_kernel(BwdPairParam
   if (blockIdx.x >= *p.ex_count) return;
   const int rec = (int)p.ex_list[blockIdx.x];
   if (rec >= p.B * p.H * p.NT) return;  // (the list holds record indices only)
-  const RecTok rt = rec_tokens(rec, p.T, p.H, p.NT, C, p.seqs);
+  const RecTok rt = rec_tokens(rec, p.B, p.T, p.H, C, p.seqs);
   if (rt.nval == 0) return;
   const int h = rt.h;
   const size_t HD = (size_t)p.H * D;

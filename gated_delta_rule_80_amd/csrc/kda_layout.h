@@ -43,6 +43,17 @@ constexpr RecordLayout record_layout(int C, int D, size_t esize) {
 // sequences per (head, chunk slot), n_slots = ceil(T / C) + n_seqs slots a head.
 // When the state walk is split into segments (below), their maps and start
 // states follow the records.
+//
+// Records are chunk-major (rec_slot): a walk is one (sequence, head) pair,
+// w = b H + h of NW = B H walks (packed sequences: w = h, NW = H, and the chunk
+// index is the head's slot), and chunk n of walk w sits at slot n NW + w.  The
+// walks step through their chunks together, so at any moment they read one
+// contiguous stretch of records instead of NW stretches a whole head's records
+// apart (equal low address bits, hence the same HBM channels); the preparation,
+// whose workgroups run chunk by chunk over all heads, writes them the same way.
+// Every per-record buffer of the backward uses the same slots.
+constexpr size_t rec_slot(size_t n, size_t w, size_t nw) { return n * nw + w; }
+
 struct WorkspaceLayout {
   size_t list;     // byte offset of the fallback list (uint32 per chunk)
   size_t seq;      // byte offset of the sequence tables (packed sequences)
@@ -195,7 +206,7 @@ struct OutStageParams {
 };
 
 // ------------------------------------------------------------------ backward
-// Workspace buffers of the backward pass, per record rec = (b * H + h) * NT + n:
+// Workspace buffers of the backward pass, per record slot rec (rec_slot):
 //   ckS  [rec]: S_n [D][D] (the state at the chunk start, rows = key channel) then
 //        U [C][D] (the chunk's corrected values U~ - W S_n), element type
 //   ckdS [rec][D][D]     dS_{n+1} (gradient of the chunk's end state), element type

@@ -194,11 +194,11 @@ __global__ __launch_bounds__(fast_threads<E>()) void kda_chunk_prep_kernel(PrepP
   const int r = lane & 15, g4 = lane >> 4;
   // Chunk-major order: the workgroups running at the same time cover every head
   // of a few consecutive chunks, so together they read whole token rows of q, k,
-  // v, g (all heads of a token are adjacent in memory).  Records stay in
-  // (sequence, head, chunk) order for the state walk.  Packed sequences: slot gc
-  // of head h, a chunk of the sequence owning that slot (slots past the last one
-  // in use have nothing to do).  b is the sequence (conv state), tok0 its first
-  // token row, Tq its length.
+  // v, g (all heads of a token are adjacent in memory), and write one
+  // contiguous stretch of records (rec_slot: workgroup i is record slot i).
+  // Packed sequences: slot gc of head h, a chunk of the sequence owning that
+  // slot (slots past the last one in use have nothing to do).  b is the
+  // sequence (conv state), tok0 its first token row, Tq its length.
   int n, h, b, rec, Tq;
   long tok0;
   if (p.seqs.bounds == nullptr) {
@@ -207,7 +207,7 @@ __global__ __launch_bounds__(fast_threads<E>()) void kda_chunk_prep_kernel(PrepP
     const int bh = blockIdx.x % BH;
     h = bh % p.H;
     b = bh / p.H;
-    rec = bh * p.NT + n;
+    rec = (int)rec_slot(n, bh, BH);
     tok0 = (long)b * p.T;
     Tq = p.T;
   } else {
@@ -218,7 +218,7 @@ __global__ __launch_bounds__(fast_threads<E>()) void kda_chunk_prep_kernel(PrepP
     n = gc - p.seqs.cstart[b];
     tok0 = p.seqs.bounds[b];
     Tq = p.seqs.bounds[b + 1] - p.seqs.bounds[b];
-    rec = h * p.NT + gc;
+    rec = (int)rec_slot(gc, h, p.H);
     if (n < 0 || (long)n * C >= Tq) return;  // inconsistent tables: touch nothing
   }
   const int t0 = (p.c0 + n) * C;  // first token of the chunk in its sequence

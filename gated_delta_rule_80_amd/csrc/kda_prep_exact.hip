@@ -89,16 +89,18 @@ __global__ __launch_bounds__(kPrepThreads) void kda_chunk_prep_exact_kernel(Prep
   int n, h, b, Tq;
   long tok0;
   if (p.seqs.bounds == nullptr) {
-    n = rec % p.NT;
-    const int bh = rec / p.NT;
+    // rec_slot(n, b H + h, B H)
+    const int BH = p.B * p.H;
+    n = rec / BH;
+    const int bh = rec % BH;
     h = bh % p.H;
     b = bh / p.H;
     tok0 = (long)b * p.T;
     Tq = p.T;
   } else {
-    // packed sequences: record = head * slots + slot
-    const int gc = rec % p.NT;
-    h = rec / p.NT;
+    // packed sequences: rec_slot(slot, h, H)
+    const int gc = rec / p.H;
+    h = rec % p.H;
     b = seq_of_slot(p.seqs.cstart, p.seqs.n_seqs, gc);
     n = gc - p.seqs.cstart[b];
     tok0 = p.seqs.bounds[b];

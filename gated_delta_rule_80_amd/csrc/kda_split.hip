@@ -78,7 +78,9 @@ __global__ __launch_bounds__(NT, 2) void kda_seg_map_kernel(SplitParams p) {
   // every segment but the last has seg_len whole chunks; the last (only mapped
   // for a whole call) has the rest, its last chunk possibly partial
   const int nch = p.whole && s == nmap - 1 ? p.nch - s * p.seg_len : p.seg_len;
-  const size_t rec0 = (size_t)bh * p.NT + (size_t)s * p.seg_len;
+  // chunk n of the segment is record rec0 + n rstride (rec_slot)
+  const size_t rstride = (size_t)p.B * p.H;
+  const size_t rec0 = rec_slot((size_t)s * p.seg_len, bh, rstride);
 
   const int R = wave % RT;
   const bool has_u = FULL_U || wave < RT * VT;
@@ -113,7 +115,7 @@ __global__ __launch_bounds__(NT, 2) void kda_seg_map_kernel(SplitParams p) {
   }
   const bool skip_u = kind == 1;  // no inputs: U~ is never read, so never copied
   auto issue_copy = [&](int n) {
-    const char* recp = p.ws + (rec0 + n) * RL.bytes;
+    const char* recp = p.ws + (rec0 + n * rstride) * RL.bytes;
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
       const int idx = it * NT + tid;

@@ -108,9 +108,10 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void kda_chunk_state_kernel(
   // This walk's tokens and records: sequence b of B equal-length ones, or packed
   // sequence b (tokens [bounds[b], bounds[b + 1]), chunk slots from cstart[b] of
   // head h).
+  // Chunk n of this walk is record rec0 + n rstride (rec_slot).
   long tok0;
   int Tq, nch;
-  size_t rec0;
+  size_t rec0, rstride;
   if (p.seqs.bounds == nullptr) {
     // chunks c0 .. of sequence b: tokens from c0 C on, at most cap chunks (a
     // time slice's records fill the workspace from slot 0; a segment's are
@@ -120,7 +121,8 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void kda_chunk_state_kernel(
     tok0 = (long)b * p.T + (long)c0 * C;
     Tq = p.T - c0 * C;
     nch = (Tq + C - 1) / C < cap ? (Tq + C - 1) / C : cap;
-    rec0 = (size_t)bh * p.NT + (p.nseg > 1 ? c0 : 0);
+    rstride = (size_t)p.B * p.H;
+    rec0 = rec_slot(p.nseg > 1 ? c0 : 0, bh, rstride);
   } else {
     tok0 = p.seqs.bounds[b];
     Tq = p.seqs.bounds[b + 1] - p.seqs.bounds[b];
@@ -129,7 +131,8 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void kda_chunk_state_kernel(
     c0 = c0 < 0 ? 0 : (c0 > p.NT ? p.NT : c0);
     c1 = c1 < c0 ? c0 : (c1 > p.NT ? p.NT : c1);
     nch = c1 - c0;
-    rec0 = (size_t)h * p.NT + c0;
+    rstride = (size_t)p.H;
+    rec0 = rec_slot(c0, h, rstride);
   }
   // conv-state hand-over of (b, h): new state row tau = raw input at position
   // Tq - 3 + tau, from the previous state where that position is < 0.  A thread
@@ -201,7 +204,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void kda_chunk_state_kernel(
     src_off[it] = (uint32_t)off;
   }
   auto issue_copy = [&](int n) {
-    const char* recp = p.ws + (rec0 + n) * RL.bytes;
+    const char* recp = p.ws + (rec0 + n * rstride) * RL.bytes;
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
       // this wave's 64 lanes fill img + (it * NT + 64 * wave) * 16 onwards, 16 bytes per lane
@@ -391,7 +394,7 @@ __global__ __launch_bounds__(NT, NT == 256 ? 2 : 1) void kda_chunk_state_kernel(
     // step's U after the next barrier): a lane reads 4 consecutive value columns of
     // one row there and stores them as one 4-element piece (the accumulators hold 4
     // rows of one column, which would take 4 scattered stores).
-    E* ck = CK ? static_cast<E*>(p.ckpt) + (rec0 + n) * ((size_t)D * D + (size_t)C * D) : nullptr;
+    E* ck = CK ? static_cast<E*>(p.ckpt) + (rec0 + n * rstride) * ((size_t)D * D + (size_t)C * D) : nullptr;
     if constexpr (CK) {
       constexpr int V4 = VB / 4;  // 4-column pieces per row of the block
 #pragma unroll
