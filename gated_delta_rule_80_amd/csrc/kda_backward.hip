@@ -923,8 +923,10 @@ __global__ __launch_bounds__(512) void kda_bwd_t16_kernel(BwdTParams p) {
 // One workgroup per chunk record; wave w owns channels [16 w, 16 w + 16).  Lane
 // (r, g4) holds the operands of rows 4 s + g4 (s < C / 4) of its channel 16 w + r
 // (the matrix-core B layout), and its results for rows 16 p + 4 g4 + e.  Row
-// block by row block: the products that finish rK, rQ and cK of the block, then
-// its element terms as in the exact kernel.
+// block by row block: the products that finish rK, rQ and cK of the block, which
+// go through LDS once, then its element terms as in the exact kernel with thread
+// (row, 4 adjacent channels) of the block, so that every input and output of
+// that phase moves as one vector access per tensor.
 constexpr float kBwdSpan2 = 240.f;   // widest block span factored (log2 units)
 constexpr float kBwdBound2 = 120.f;  // log2 of the largest partial sum allowed
 
@@ -935,9 +937,14 @@ __global__ __launch_bounds__(4 * D, D / 32 > 1 ? D / 32 : 1) void kda_bwd_pair_m
   constexpr int NS = C / 4;     // rows per lane in the B layout
   constexpr int LA = C + 2;     // dA, dP rows (row reads of 16 lanes x 4 columns spread over the banks)
   constexpr int LD = D + 4;     // dGamma rows
-  __shared__ __attribute__((aligned(16))) float sreg[2 * C * LA];  // dA, dP
+  constexpr int LT = D + 4;     // rows of the block's product results
+  constexpr int CPT = D / 4;    // threads per row in the element phase
+  // dA, dP in the record element type (they arrive in it, so bf16 is exact)
+  __shared__ __attribute__((aligned(16))) E sreg[2 * C * LA];
   __shared__ __attribute__((aligned(16))) float sG[C * LD];         // dGamma
-  __shared__ float sdbw[(D / 16) * C];  // dbeta partial sums per wave
+  // rK, rQ, cK sums of one row block [3][16][LT] (finally the dKt Ktil column partials)
+  __shared__ __attribute__((aligned(16))) float sT[3 * 16 * LT];
+  __shared__ float smid[NB * D];  // block midpoints per channel
   __shared__ float sGC[D];
   __shared__ float sB[C];
   // per wave: the widest block span of its channels, the largest |k|, |q'|, |dA|,
@@ -947,8 +954,8 @@ __global__ __launch_bounds__(4 * D, D / 32 > 1 ? D / 32 : 1) void kda_bwd_pair_m
   constexpr int NSG = NTH / D;  // token segments of the dg running sum
   constexpr int SL = C / NSG;   // tokens per segment
   __shared__ float sseg[NSG * D];  // segment totals of dGamma
-  float* sdA = sreg;
-  float* sdP = sreg + C * LA;
+  E* sdA = sreg;
+  E* sdP = sreg + C * LA;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g4 = lane >> 4;
@@ -1006,11 +1013,15 @@ __global__ __launch_bounds__(4 * D, D / 32 > 1 ? D / 32 : 1) void kda_bwd_pair_m
     const f32x4 vp = load4v(gdP + (size_t)i * C + j4);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      sdA[i * LA + j4 + e] = va[e];
-      sdP[i * LA + j4 + e] = vp[e];
+      sdA[i * LA + j4 + e] = from_f32<E>(va[e]);
+      sdP[i * LA + j4 + e] = from_f32<E>(vp[e]);
       mx[3] = fmaxf(mx[3], fabsf(va[e]));
       mx[4] = fmaxf(mx[4], fabsf(vp[e]));
     }
+  }
+  if (g4 == 0) {
+#pragma unroll
+    for (int q = 0; q < NB; ++q) smid[q * D + c] = mid[q];
   }
 #pragma unroll
   for (int m = 0; m < 5; ++m) {
@@ -1057,28 +1068,15 @@ __global__ __launch_bounds__(4 * D, D / 32 > 1 ? D / 32 : 1) void kda_bwd_pair_m
 
   // ---- per row block pb: the block-pair products, then its element terms
   float* sdG = sG;  // [C][LD]
-  const float gC = gam_at(C - 1);
   const E* gdQL = static_cast<const E*>(p.dQL) + (size_t)rec * C * D;
   const E* gdKt = static_cast<const E*>(p.dKt) + (size_t)rec * C * D;
   const E* gdBk = static_cast<const E*>(p.dBk) + (size_t)rec * C * D;
   const E* gdBv = static_cast<const E*>(p.dBv) + (size_t)rec * C * D;
-  float colsum = 0.f;  // sum over this lane's rows of dKt Ktil
-  // the element terms' inputs of row t: dQL, dKt, dBk, dBv, Gamma, q', k, v (rows
-  // past the end of the sequence read the last row; q', k, v are zeroed there)
-  auto load_row = [&](int t, float (&v)[8]) {
-    const size_t lo = (size_t)t * D + c;
-    v[0] = to_f32(gdQL[lo]);
-    v[1] = to_f32(gdKt[lo]);
-    v[2] = to_f32(gdBk[lo]);
-    v[3] = to_f32(gdBv[lo]);
-    const size_t o = row_of(t < nval ? t : nval - 1) + c;
-    v[4] = p.gam[o];
-    v[5] = to_f32(y[o]);
-    v[6] = to_f32(y[plane + o]);
-    v[7] = to_f32(y[2 * plane + o]);
-  };
-  float rowv[2][8];
-  load_row(4 * g4, rowv[0]);
+  // element phase: thread (row er of the block, channels c4 .. c4 + 3)
+  const int er = tid / CPT, c4 = 4 * (tid % CPT);
+  const size_t rowC = row_of(C - 1 < nval ? C - 1 : nval - 1);  // Gamma_C: the last row
+  const f32x4 gC4 = load4v(p.gam + rowC + c4);
+  f32x4 csum = {0.f, 0.f, 0.f, 0.f};  // sum over this thread's rows of dKt Ktil
 #pragma unroll
   for (int pb = 0; pb < NB; ++pb) {
     f32x4 tK = {0.f, 0.f, 0.f, 0.f}, tQ = tK, tC = tK;
@@ -1092,8 +1090,8 @@ __global__ __launch_bounds__(4 * D, D / 32 > 1 ? D / 32 : 1) void kda_bwd_pair_m
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         // rows (16 pb + r), columns (16 qb + 4 s + g4)
-        const float a_ = sdA[(16 * pb + r) * LA + 16 * qb + 4 * s + g4];
-        const float p_ = sdP[(16 * pb + r) * LA + 16 * qb + 4 * s + g4];
+        const float a_ = to_f32(sdA[(16 * pb + r) * LA + 16 * qb + 4 * s + g4]);
+        const float p_ = to_f32(sdP[(16 * pb + r) * LA + 16 * qb + 4 * s + g4]);
         xk = __builtin_amdgcn_mfma_f32_16x16x4f32(a_, kb[4 * qb + s], xk, 0, 0, 0);
         xq = __builtin_amdgcn_mfma_f32_16x16x4f32(p_, kb[4 * qb + s], xq, 0, 0, 0);
       }
@@ -1113,57 +1111,84 @@ __global__ __launch_bounds__(4 * D, D / 32 > 1 ? D / 32 : 1) void kda_bwd_pair_m
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
         // transposed reads: rows (16 rb + 4 s + g4), columns (16 pb + r)
-        const float at = sdA[(16 * rb + 4 * s + g4) * LA + 16 * pb + r];
-        const float pt = sdP[(16 * rb + 4 * s + g4) * LA + 16 * pb + r];
+        const float at = to_f32(sdA[(16 * rb + 4 * s + g4) * LA + 16 * pb + r]);
+        const float pt = to_f32(sdP[(16 * rb + 4 * s + g4) * LA + 16 * pb + r]);
         xc = __builtin_amdgcn_mfma_f32_16x16x4f32(at, bka[4 * rb + s], xc, 0, 0, 0);
         xc = __builtin_amdgcn_mfma_f32_16x16x4f32(pt, qa[4 * rb + s], xc, 0, 0, 0);
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) tC[e] = fmaf(F2, xc[e] * F1, tC[e]);
     }
-    // element terms for rows t = 16 pb + 4 g4 + e of channel c; each row's inputs
-    // were loaded one row ahead (the next row's loads go out before this row's
-    // arithmetic)
+    // the element terms' inputs of row t = 16 pb + er, issued before the
+    // block's sums go through LDS:
+    // dQL, dKt, dBk, dBv, Gamma, q', k, v (rows past the end of the sequence read
+    // the last row; q', k, v are zeroed there)
+    const int t = 16 * pb + er;
+    const bool in = t < nval;
+    const size_t lo = (size_t)t * D + c4;
+    const size_t o = row_of(in ? t : nval - 1) + c4;
+    // (held in the element type until used: half the registers for bf16)
+    using V4 = typename Vec4<E>::type;
+    const V4 dql = *reinterpret_cast<const V4*>(gdQL + lo), dkt = *reinterpret_cast<const V4*>(gdKt + lo);
+    const V4 dbk = *reinterpret_cast<const V4*>(gdBk + lo), dbv = *reinterpret_cast<const V4*>(gdBv + lo);
+    const f32x4 gt = load4v(p.gam + o);
+    const V4 qv = *reinterpret_cast<const V4*>(y + o), kv = *reinterpret_cast<const V4*>(y + plane + o),
+             vv = *reinterpret_cast<const V4*>(y + 2 * plane + o);
+    // the block's sums, rows 4 g4 + e of channel c, into LDS (the previous block's
+    // element phase has read them: barrier at the end of each block)
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int t = 16 * pb + 4 * g4 + e;
-      const bool in = t < nval;
-      const int cur = (4 * pb + e) & 1;
-      if (4 * pb + e + 1 < 4 * NB) load_row(16 * ((4 * pb + e + 1) / 4) + 4 * g4 + (4 * pb + e + 1) % 4, rowv[cur ^ 1]);
-      const float dql = rowv[cur][0], dkt = rowv[cur][1], dbk = rowv[cur][2], dbv = rowv[cur][3];
-      const float gt = rowv[cur][4];
-      const float qq = in ? rowv[cur][5] : 0.f, kk = in ? rowv[cur][6] : 0.f, vv = in ? rowv[cur][7] : 0.f;
-      const float bt = sB[t];
-      const float a = __builtin_amdgcn_exp2f(gt - mid[pb]), bb = __builtin_amdgcn_exp2f(mid[pb] - gt);
-      const float rK = a * tK[e], rQ = a * tQ[e], ckt = bb * tC[e];
-      const float lam = __builtin_amdgcn_exp2f(gt);
-      const float ec = __builtin_amdgcn_exp2f(gC - gt);
-      const float ktil = kk * ec;
-      colsum = fmaf(dkt, ktil, colsum);
-      sdG[t * LD + c] = dbk * bt * kk * lam + dql * qq * lam - dkt * ktil + bt * kk * rK + qq * rQ - kk * ckt;
-      if (in) {
-        const size_t o = row_of(t) + c;
-        E* dy = static_cast<E*>(p.dy);
-        dy[o] = from_f32<E>(lam * dql + rQ);
-        dy[plane + o] = from_f32<E>(bt * lam * dbk + ec * dkt + bt * rK + ckt);
-        dy[2 * plane + o] = from_f32<E>(bt * dbv);
-      }
-      // dbeta: this wave's 16 channels of row t
-      const float dbp = group_sum<16>(dbv * vv + dbk * kk * lam + kk * rK);
-      if (r == 0) sdbw[wave * C + t] = dbp;
+      sT[(0 * 16 + 4 * g4 + e) * LT + c] = tK[e];
+      sT[(1 * 16 + 4 * g4 + e) * LT + c] = tQ[e];
+      sT[(2 * 16 + 4 * g4 + e) * LT + c] = tC[e];
     }
+    __syncthreads();
+    // element terms of row t, channels c4 .. c4 + 3
+    const f32x4 sK = *reinterpret_cast<const f32x4*>(&sT[(0 * 16 + er) * LT + c4]);
+    const f32x4 sQ = *reinterpret_cast<const f32x4*>(&sT[(1 * 16 + er) * LT + c4]);
+    const f32x4 sC = *reinterpret_cast<const f32x4*>(&sT[(2 * 16 + er) * LT + c4]);
+    const f32x4 md = *reinterpret_cast<const f32x4*>(&smid[pb * D + c4]);
+    const float bt = sB[t];
+    float dg4[4], yq[4], yk[4], yv[4];
+    float dbp = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float qq = in ? (float)qv[e] : 0.f, kk = in ? (float)kv[e] : 0.f, vx = in ? (float)vv[e] : 0.f;
+      const float dqle = (float)dql[e], dkte = (float)dkt[e], dbke = (float)dbk[e], dbve = (float)dbv[e];
+      const float a = __builtin_amdgcn_exp2f(gt[e] - md[e]), bb = __builtin_amdgcn_exp2f(md[e] - gt[e]);
+      const float rK = a * sK[e], rQ = a * sQ[e], ckt = bb * sC[e];
+      const float lam = __builtin_amdgcn_exp2f(gt[e]);
+      const float ec = __builtin_amdgcn_exp2f(gC4[e] - gt[e]);
+      const float ktil = kk * ec;
+      csum[e] = fmaf(dkte, ktil, csum[e]);
+      dg4[e] = dbke * bt * kk * lam + dqle * qq * lam - dkte * ktil + bt * kk * rK + qq * rQ - kk * ckt;
+      yq[e] = lam * dqle + rQ;
+      yk[e] = bt * lam * dbke + ec * dkte + bt * rK + ckt;
+      yv[e] = bt * dbve;
+      dbp += dbve * vx + dbke * kk * lam + kk * rK;
+    }
+    store4(&sdG[t * LD + c4], dg4[0], dg4[1], dg4[2], dg4[3]);
+    if (in) {
+      E* dy = static_cast<E*>(p.dy) + row_of(t) + c4;
+      store4(dy, yq[0], yq[1], yq[2], yq[3]);
+      store4(dy + plane, yk[0], yk[1], yk[2], yk[3]);
+      store4(dy + 2 * plane, yv[0], yv[1], yv[2], yv[3]);
+    }
+    // dbeta of row t: the row's CPT threads are adjacent lanes of one wave
+    dbp = group_sum<CPT>(dbp);
+    if (c4 == 0 && in) p.dbeta_part[((size_t)rt.tok + t) * p.H + h] = dbp;
+    __syncthreads();  // the block's sums are read
   }
-  colsum += __shfl_xor(colsum, 16, 64);
-  colsum += __shfl_xor(colsum, 32, 64);
-  if (g4 == 0) sGC[c] = colsum + p.dLC[(size_t)rec * D + c] * __builtin_amdgcn_exp2f(gC);
+  // dGamma_C: the dKt Ktil column sums over the chunk's rows, plus dLC LC
+  store4(&sT[er * LT + c4], csum[0], csum[1], csum[2], csum[3]);
   __syncthreads();
-  // dbeta: sum over the waves, one thread per token
-  if (tid < nval) {
+  if (tid < D) {
     float acc = 0.f;
 #pragma unroll
-    for (int w = 0; w < D / 16; ++w) acc += sdbw[w * C + tid];
-    p.dbeta_part[((size_t)rt.tok + tid) * p.H + h] = acc;
+    for (int e2 = 0; e2 < 16; ++e2) acc += sT[e2 * LT + tid];
+    sGC[tid] = acc + p.dLC[(size_t)rec * D + tid] * __builtin_amdgcn_exp2f(p.gam[rowC + tid]);
   }
+  __syncthreads();
   // dg: reverse running sum over the chunk.  Thread (channel cc, segment sg) takes
   // the SL tokens of segment sg: the segment totals go through LDS, then each
   // thread walks its segment backwards from the sum of the later segments.

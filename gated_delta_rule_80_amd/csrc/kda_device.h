@@ -62,6 +62,11 @@ __device__ __forceinline__ void store8(float* p, const float* in) {
   *reinterpret_cast<f32x4*>(p + 4) = b;
 }
 // 4 consecutive elements as float32 (8-byte aligned bf16 / 16-byte aligned fp32)
+// 4 elements of type E as one vector (bf16x4 / f32x4)
+template <typename E> struct Vec4;
+template <> struct Vec4<__bf16> { using type = bf16x4; };
+template <> struct Vec4<float> { using type = f32x4; };
+
 __device__ __forceinline__ f32x4 load4v(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 __device__ __forceinline__ f32x4 load4v(const __bf16* p) {
   const bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
