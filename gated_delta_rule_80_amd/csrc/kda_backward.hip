@@ -1441,21 +1441,25 @@ __global__ __launch_bounds__(256, 2) void kda_bwd_front_kernel(BwdFrontParams p,
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const size_t HD = (size_t)p.H * D;
   // the workgroup's sequence b, head h, block of the sequence, the sequence's
-  // first token row and length, and the slot of its filter partial
+  // first token row and length, and the slot of its filter partial.  Block-major
+  // order: the workgroups running at the same time cover every head of a few
+  // token blocks, so together they read and write whole token rows (all heads of
+  // a token are adjacent in memory) instead of one head's slice of many rows.
   int h, b, blk, Tq, part;
   long tok0;
   if (p.seqs.bounds == nullptr) {
     const int nblk = (p.T + TOKB - 1) / TOKB;
-    blk = blockIdx.x % nblk;
-    const int bh = blockIdx.x / nblk;
+    const int BH = p.B * p.H;
+    blk = blockIdx.x / BH;
+    const int bh = blockIdx.x % BH;
     h = bh % p.H;
     b = bh / p.H;
     Tq = p.T;
     tok0 = (long)b * p.T;
     part = b * nblk + blk;
   } else {
-    part = blockIdx.x % p.nfslots;
-    h = blockIdx.x / p.nfslots;
+    part = blockIdx.x / p.H;
+    h = blockIdx.x % p.H;
     const bool used = part < p.fstart[p.seqs.n_seqs];
     b = used ? seq_of_slot(p.fstart, p.seqs.n_seqs, part) : 0;
     blk = used ? part - p.fstart[b] : 0;
